@@ -1,0 +1,17 @@
+"""Float64 CPU oracle for the RG-LRU scan and its block-diagonal gate projection.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg. The HIP library and its binding never import,
+call or link anything here.
+"""
+from .rglru import (  # noqa: F401
+    C_DEFAULT,
+    blockdiag_proj_backward,
+    blockdiag_proj_forward,
+    gates,
+    rglru_backward,
+    rglru_forward,
+    rglru_forward_chunked,
+    sigmoid,
+    softplus,
+)
