@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the RG-LRU scan hot path on one MI355X.
+
+One step = rglru_fwd (training mode: writes the float32 checkpoint) followed by
+rglru_bwd (reverse scan, pointwise gradients and the lambda-gradient
+reduction) over one batch of the workload, inputs already resident in HBM.
+The default workload is the pages' measured shape, B=4, L=2048, W=2048, bf16
+io with a float32 carry, zero initial state and no resets.
+
+Cache honesty: the step's working set (about 270 MB) would otherwise sit in
+the 256 MB Infinity Cache between steps, so the benchmark rotates through
+several copies of every buffer (more than twice the cache in total) and each
+step reads data last touched two steps earlier.
+
+Prints one JSON line (see the "fields" list in the docstring of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "RG-LRU fwd & fwd+bwd ms + % HBM peak, B=4 L=2048 W=2048 bf16"
+FWD_BYTES_PER_ELEM = {"bf16": 8, "f32": 16}    # read x, gate_x, gate_a; write h
+BWD_BYTES_PER_ELEM = {"bf16": 14, "f32": 28}   # read x, gate_x, gate_a, dh; write dx, dgate_x, dgate_a
+
+
+def cpu_baseline(wl, inp, seconds_target=12.0):
+    """The float64 oracle (untuned) on a bounded channel sample of the same workload.
+
+    Channels are independent, so the time for the whole workload is the sample
+    time scaled by W / sample_channels. numpy's elementwise loops run on one core.
+    """
+    import numpy as np
+
+    import oracle
+
+    n_ch = min(wl.width, 256)
+    sl = np.arange(n_ch)
+    x, gx, ga, dh = (s.value[:, :, sl] for s in (inp.x, inp.gx, inp.ga, inp.dh))
+    lam = inp.lam.astype(np.float64)[sl]
+    h0 = None if inp.h0 is None else inp.h0.astype(np.float64)[:, sl]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.rglru_forward(x, gx, ga, lam, inp.reset, h0)
+        oracle.rglru_backward(x, gx, ga, lam, dh, inp.reset, h0)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds_target or reps >= 50:
+            break
+    per_step_s = el / reps * (wl.width / n_ch)
+    return {
+        "value": per_step_s * 1e3,
+        "unit": "ms",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"B={wl.batch} L={wl.length}, {n_ch} of {wl.width} channels, fwd+bwd x{reps} "
+                  f"({el:.1f} s), scaled by {wl.width / n_ch:g} to the full width",
+    }
+
+
+def main():
+    """Fields: metric, value (fwd+bwd ms per step), unit, n_gpus, steps, warmup, ms_per_step,
+    higher_is_better, scaling, vs_baseline, dtype, data, config, fwd_ms, bwd_ms, elements_per_s,
+    hbm_frac_fwd, hbm_frac_fwd_bwd, roofline, cpu_baseline."""
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="synth workload id (1 = pages' shape)")
+    ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=3, help="rotating buffer copies (cache honesty)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan shards by channel or batch with no exchange in the forward; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_linear_recurrence_amd as glr
+    import synth
+
+    glr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    chunk = wl.chunk if args.chunk is None else args.chunk
+    inp = synth.make_inputs(wl)
+    B, L, W = wl.batch, wl.length, wl.width
+    N = B * L * W
+
+    def io_tensor(s):
+        if s.io == "f32":
+            return torch.from_numpy(np.ascontiguousarray(s.raw)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(s.raw).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = {k: io_tensor(getattr(inp, k)) for k in ("x", "gx", "ga", "dh")}
+    lam = torch.from_numpy(inp.lam).to(dev)
+    reset = None if inp.reset is None else torch.from_numpy(inp.reset).to(dev)
+    h0 = None if inp.h0 is None else torch.from_numpy(inp.h0).to(dev)
+    shape = glr.make_shape(B, L, W, base["x"].dtype, chunk)
+    n_ck = glr.rglru_ckpt_elems(shape)
+    sets = []
+    for s in range(args.sets):
+        d = {k: v.clone() for k, v in base.items()}
+        d["h"] = torch.empty_like(d["x"])
+        d["h_last"] = torch.empty((B, W), dtype=torch.float32, device=dev)
+        d["ckpt"] = torch.empty(n_ck, dtype=torch.float32, device=dev)
+        for k in ("dx", "dgx", "dga"):
+            d[k] = torch.empty_like(d["x"])
+        d["dlam"] = torch.empty(W, dtype=torch.float32, device=dev)
+        d["dh0"] = torch.empty((B, W), dtype=torch.float32, device=dev) if h0 is not None else None
+        d["ws"] = glr.Workspace(dev)
+        d["ws"].get(glr.rglru_workspace_bytes(shape))
+        sets.append(d)
+    del base
+    stream = torch.cuda.current_stream(dev)
+
+    def step(d, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        glr.rglru_fwd(d["x"], d["gx"], d["ga"], lam, reset, h0, chunk=chunk, h=d["h"], h_last=d["h_last"],
+                      ckpt=d["ckpt"], workspace=d["ws"])
+        if evs is not None:
+            evs[1].record(stream)
+        glr.rglru_bwd(d["x"], d["gx"], d["ga"], lam, reset, d["ckpt"], d["dh"], None, chunk=chunk,
+                      want_dh0=h0 is not None, dx=d["dx"], dgate_x=d["dgx"], dgate_a=d["dga"], dlam=d["dlam"],
+                      dh0=d["dh0"], workspace=d["ws"])
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    err = max(d["ws"].error_bits() for d in sets)
+    if err:
+        print(f"look-back spin limit reported (error bits {err}); timings invalid", file=sys.stderr)
+        sys.exit(3)
+
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_avg = float(np.mean(fwd_ms))
+    bwd_avg = float(np.mean(bwd_ms))
+    fb = FWD_BYTES_PER_ELEM[wl.io] * N
+    bb = BWD_BYTES_PER_ELEM[wl.io] * N
+    fwd_gbs = fb / (fwd_avg * 1e-3) / 1e9
+    bwd_gbs = bb / (bwd_avg * 1e-3) / 1e9
+    fb_gbs = (fb + bb) / (ms_per_step * 1e-3) / 1e9
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(prof):
+        with open(prof) as f:
+            tr = json.load(f).get(f"{wl.name}:bwd")
+        traffic = tr
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 5),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.io,
+        "data": "synthetic (seeded N(0,1) inputs and logits, decay U[0.9,0.999]; no datasets)",
+        "config": {"workload": wl.name, "batch": B, "length": L, "width": W, "io": wl.io,
+                   "chunk": chunk or 64, "resets": wl.doc_mean is not None, "h0": wl.h0,
+                   "step": "rglru_fwd + rglru_bwd"},
+        "fwd_ms": round(fwd_avg, 5),
+        "bwd_ms": round(bwd_avg, 5),
+        "elements_per_s": N / (ms_per_step * 1e-3),
+        "hbm_frac_fwd": round(fwd_gbs / HBM_PEAK_GBS, 4),
+        "hbm_frac_fwd_bwd": round(fb_gbs / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": "rglru_bwd (bwd_kernel + dlambda reduce)",
+            "bound": "hbm",
+            "achieved": round(bwd_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(bwd_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bb,
+            "fwd_achieved": round(fwd_gbs, 1),
+            "fwd_frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

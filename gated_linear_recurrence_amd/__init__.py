@@ -1,0 +1,21 @@
+"""MI355X (gfx950) RG-LRU: HIP kernels behind a C ABI (include/rglru.h) and this thin binding."""
+from . import _lib
+from ._lib import RglruError, header_symbols  # noqa: F401
+from .ops import (  # noqa: F401
+    Workspace,
+    make_shape,
+    rglru,
+    rglru_blockdiag_gate_proj_bwd,
+    rglru_blockdiag_gate_proj_fwd,
+    rglru_bwd,
+    rglru_bwd_workspace_bytes,
+    rglru_ckpt_elems,
+    rglru_fwd,
+    rglru_fwd_workspace_bytes,
+    rglru_workspace_bytes,
+)
+
+
+def load_library():
+    """Loads the in-tree librglru.so; raises if it is not built."""
+    return _lib.load()

@@ -1,0 +1,250 @@
+"""Python binding of the C ABI, with the same entry-point names.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs are allocated with torch when the caller passes none, and
+the raw pointers go to librglru. Every step of the computation runs in the
+HIP kernels; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_IO = {torch.float32: _lib.RGLRU_IO_F32, torch.bfloat16: _lib.RGLRU_IO_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name, shape, dtype, device):
+    return None if t is None else _need(t, name, shape, dtype, device)
+
+
+def make_shape(batch, length, width, io_dtype, chunk=0, c=8.0) -> _lib.rglru_shape_t:
+    io = _IO[io_dtype] if isinstance(io_dtype, torch.dtype) else int(io_dtype)
+    return _lib.rglru_shape_t(int(batch), int(length), int(width), io, int(chunk), float(c), 0)
+
+
+def rglru_ckpt_elems(shape: _lib.rglru_shape_t) -> int:
+    return int(_lib.load().rglru_ckpt_elems(ctypes.byref(shape)))
+
+
+def rglru_fwd_workspace_bytes(shape: _lib.rglru_shape_t) -> int:
+    return int(_lib.load().rglru_fwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def rglru_bwd_workspace_bytes(shape: _lib.rglru_shape_t) -> int:
+    return int(_lib.load().rglru_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def rglru_workspace_bytes(shape: _lib.rglru_shape_t) -> int:
+    return int(_lib.load().rglru_workspace_bytes(ctypes.byref(shape)))
+
+
+class Workspace:
+    """A zero-initialised device buffer reused by consecutive calls on one stream.
+
+    The library leaves it ready for the next call after each one, so it is
+    zero-filled only when (re)allocated. Calls sharing one Workspace must not
+    overlap in time.
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device(device if device is not None else "cuda")
+        self.buf = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+    def error_bits(self) -> int:
+        """Sticky error word of the header (bit 0: a look-back wait hit its spin limit)."""
+        if self.buf is None:
+            return 0
+        return int(self.buf[12:16].view(torch.int32).item())
+
+
+_default_ws = {}
+
+
+def default_workspace(device: torch.device) -> Workspace:
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(device)
+    return ws
+
+
+def rglru_fwd(x: torch.Tensor, gate_x: torch.Tensor, gate_a: torch.Tensor, lam: torch.Tensor,
+              reset: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None, *,
+              chunk: int = 0, c: float = 8.0, training: bool = True, want_h_last: bool = True,
+              h: Optional[torch.Tensor] = None, h_last: Optional[torch.Tensor] = None,
+              ckpt: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
+    """Forward scan. Returns (h, h_last or None, ckpt or None)."""
+    lib = _lib.load()
+    dev = x.device
+    if x.dim() != 3:
+        raise ValueError("x must be [B, L, W]")
+    B, L, W = x.shape
+    io = x.dtype
+    if io not in _IO:
+        raise ValueError(f"unsupported io dtype {io}")
+    _need(x, "x", (B, L, W), io, dev)
+    _need(gate_x, "gate_x", (B, L, W), io, dev)
+    _need(gate_a, "gate_a", (B, L, W), io, dev)
+    _need(lam, "lambda", (W,), torch.float32, dev)
+    _opt(reset, "reset", (B, L), torch.uint8, dev)
+    _opt(h0, "h0", (B, W), torch.float32, dev)
+    shape = make_shape(B, L, W, io, chunk, c)
+    if h is None:
+        h = torch.empty((B, L, W), dtype=io, device=dev)
+    _need(h, "h", (B, L, W), io, dev)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((B, W), dtype=torch.float32, device=dev)
+    _opt(h_last, "h_last", (B, W), torch.float32, dev)
+    if ckpt is None and training:
+        ckpt = torch.empty(rglru_ckpt_elems(shape), dtype=torch.float32, device=dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", (rglru_ckpt_elems(shape),), torch.float32, dev)
+    ws = workspace if workspace is not None else default_workspace(dev)
+    nbytes = rglru_workspace_bytes(shape)
+    buf = ws.get(nbytes)
+    st = lib.rglru_fwd(ctypes.byref(shape), _ptr(x), _ptr(gate_x), _ptr(gate_a), _ptr(lam), _ptr(reset),
+                       _ptr(h0), _ptr(h), _ptr(h_last), _ptr(ckpt), _ptr(buf), buf.numel(), _stream(dev))
+    _lib.check(st, "rglru_fwd")
+    return h, h_last, ckpt
+
+
+def rglru_bwd(x: torch.Tensor, gate_x: torch.Tensor, gate_a: torch.Tensor, lam: torch.Tensor,
+              reset: Optional[torch.Tensor], ckpt: torch.Tensor, dh: torch.Tensor,
+              dh_last: Optional[torch.Tensor] = None, *, chunk: int = 0, c: float = 8.0,
+              want_dh0: bool = True, dx: Optional[torch.Tensor] = None, dgate_x: Optional[torch.Tensor] = None,
+              dgate_a: Optional[torch.Tensor] = None, dlam: Optional[torch.Tensor] = None,
+              dh0: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
+    """Backward scan. Returns (dx, dgate_x, dgate_a, dlambda, dh0 or None)."""
+    lib = _lib.load()
+    dev = x.device
+    B, L, W = x.shape
+    io = x.dtype
+    if io not in _IO:
+        raise ValueError(f"unsupported io dtype {io}")
+    for t, n in ((x, "x"), (gate_x, "gate_x"), (gate_a, "gate_a"), (dh, "dh")):
+        _need(t, n, (B, L, W), io, dev)
+    _need(lam, "lambda", (W,), torch.float32, dev)
+    _opt(reset, "reset", (B, L), torch.uint8, dev)
+    _opt(dh_last, "dh_last", (B, W), torch.float32, dev)
+    shape = make_shape(B, L, W, io, chunk, c)
+    _need(ckpt, "ckpt", (rglru_ckpt_elems(shape),), torch.float32, dev)
+    dx = torch.empty_like(x) if dx is None else _need(dx, "dx", (B, L, W), io, dev)
+    dgate_x = torch.empty_like(x) if dgate_x is None else _need(dgate_x, "dgate_x", (B, L, W), io, dev)
+    dgate_a = torch.empty_like(x) if dgate_a is None else _need(dgate_a, "dgate_a", (B, L, W), io, dev)
+    dlam = torch.empty((W,), dtype=torch.float32, device=dev) if dlam is None else \
+        _need(dlam, "dlambda", (W,), torch.float32, dev)
+    if dh0 is None and want_dh0:
+        dh0 = torch.empty((B, W), dtype=torch.float32, device=dev)
+    _opt(dh0, "dh0", (B, W), torch.float32, dev)
+    ws = workspace if workspace is not None else default_workspace(dev)
+    nbytes = rglru_workspace_bytes(shape)
+    buf = ws.get(nbytes)
+    st = lib.rglru_bwd(ctypes.byref(shape), _ptr(x), _ptr(gate_x), _ptr(gate_a), _ptr(lam), _ptr(reset),
+                       _ptr(ckpt), _ptr(dh), _ptr(dh_last), _ptr(dx), _ptr(dgate_x), _ptr(dgate_a),
+                       _ptr(dlam), _ptr(dh0), _ptr(buf), buf.numel(), _stream(dev))
+    _lib.check(st, "rglru_bwd")
+    return dx, dgate_x, dgate_a, dlam, dh0
+
+
+def rglru_blockdiag_gate_proj_fwd(x: torch.Tensor, w_x: torch.Tensor, b_x: Optional[torch.Tensor],
+                                  w_a: torch.Tensor, b_a: Optional[torch.Tensor], *,
+                                  gate_x: Optional[torch.Tensor] = None, gate_a: Optional[torch.Tensor] = None):
+    """Both block-diagonal gate projections of x [T, W] (bf16). Returns (gate_x, gate_a)."""
+    lib = _lib.load()
+    dev = x.device
+    T, W = x.shape
+    nb, bs, _ = w_x.shape
+    _need(x, "x", (T, W), torch.bfloat16, dev)
+    _need(w_x, "w_x", (nb, bs, bs), torch.bfloat16, dev)
+    _need(w_a, "w_a", (nb, bs, bs), torch.bfloat16, dev)
+    _opt(b_x, "b_x", (W,), torch.bfloat16, dev)
+    _opt(b_a, "b_a", (W,), torch.bfloat16, dev)
+    gate_x = torch.empty_like(x) if gate_x is None else _need(gate_x, "gate_x", (T, W), torch.bfloat16, dev)
+    gate_a = torch.empty_like(x) if gate_a is None else _need(gate_a, "gate_a", (T, W), torch.bfloat16, dev)
+    st = lib.rglru_blockdiag_gate_proj_fwd(T, W, bs, _ptr(x), _ptr(w_x), _ptr(b_x), _ptr(w_a), _ptr(b_a),
+                                           _ptr(gate_x), _ptr(gate_a), _stream(dev))
+    _lib.check(st, "rglru_blockdiag_gate_proj_fwd")
+    return gate_x, gate_a
+
+
+def rglru_blockdiag_gate_proj_bwd(x: torch.Tensor, w_x: torch.Tensor, w_a: torch.Tensor,
+                                  dgate_x: torch.Tensor, dgate_a: torch.Tensor,
+                                  dx_in: Optional[torch.Tensor] = None, *, want_db: bool = True,
+                                  dx_out: Optional[torch.Tensor] = None):
+    """Backward of both projections. Returns (dx, dw_x, db_x, dw_a, db_a)."""
+    lib = _lib.load()
+    dev = x.device
+    T, W = x.shape
+    nb, bs, _ = w_x.shape
+    for t, n in ((x, "x"), (dgate_x, "dgate_x"), (dgate_a, "dgate_a")):
+        _need(t, n, (T, W), torch.bfloat16, dev)
+    _need(w_x, "w_x", (nb, bs, bs), torch.bfloat16, dev)
+    _need(w_a, "w_a", (nb, bs, bs), torch.bfloat16, dev)
+    _opt(dx_in, "dx_in", (T, W), torch.bfloat16, dev)
+    dx_out = torch.empty_like(x) if dx_out is None else _need(dx_out, "dx_out", (T, W), torch.bfloat16, dev)
+    dw_x = torch.empty((nb, bs, bs), dtype=torch.float32, device=dev)
+    dw_a = torch.empty((nb, bs, bs), dtype=torch.float32, device=dev)
+    db_x = torch.empty((W,), dtype=torch.float32, device=dev) if want_db else None
+    db_a = torch.empty((W,), dtype=torch.float32, device=dev) if want_db else None
+    nws = int(lib.rglru_blockdiag_gate_proj_bwd_workspace_bytes(T, W, bs))
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    st = lib.rglru_blockdiag_gate_proj_bwd(T, W, bs, _ptr(x), _ptr(w_x), _ptr(w_a), _ptr(dgate_x),
+                                           _ptr(dgate_a), _ptr(dx_in), _ptr(dx_out), _ptr(dw_x), _ptr(db_x),
+                                           _ptr(dw_a), _ptr(db_a), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(st, "rglru_blockdiag_gate_proj_bwd")
+    return dx_out, dw_x, db_x, dw_a, db_a
+
+
+class _RGLRU(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, gate_x, gate_a, lam, h0, reset, chunk, c):
+        h, h_last, ckpt = rglru_fwd(x, gate_x, gate_a, lam, reset, h0, chunk=chunk, c=c, training=True)
+        ctx.save_for_backward(x, gate_x, gate_a, lam, reset, ckpt)
+        ctx.has_h0 = h0 is not None
+        ctx.chunk, ctx.c = chunk, c
+        return h, h_last
+
+    @staticmethod
+    def backward(ctx, dh, dh_last):
+        x, gate_x, gate_a, lam, reset, ckpt = ctx.saved_tensors
+        dh = torch.zeros_like(x) if dh is None else dh.contiguous().to(x.dtype)
+        dh_last = None if dh_last is None else dh_last.contiguous().float()
+        dx, dgx, dga, dlam, dh0 = rglru_bwd(x, gate_x, gate_a, lam, reset, ckpt, dh, dh_last,
+                                            chunk=ctx.chunk, c=ctx.c, want_dh0=ctx.has_h0)
+        return dx, dgx, dga, dlam, (dh0 if ctx.has_h0 else None), None, None, None
+
+
+def rglru(x, gate_x, gate_a, lam, h0=None, reset=None, *, chunk: int = 0, c: float = 8.0):
+    """Differentiable RG-LRU scan: returns (h, h_last). Gradients flow to x, gate_x, gate_a, lambda and h0."""
+    return _RGLRU.apply(x, gate_x, gate_a, lam, h0, reset, chunk, c)

@@ -1,0 +1,194 @@
+/*
+ * rglru.h - C ABI of the MI355X (gfx950) RG-LRU library.
+ *
+ * The library computes the fused RG-LRU (Hawk) gated linear recurrence and its
+ * backward on one GPU, plus the block-diagonal gate projection that feeds it.
+ * The Fattori comparison page lists what the fused operator covers: both
+ * sigmoid gates, softplus(a_param) with a dynamic decay and the stationary
+ * square-root factor, the input-gated write, a sequential state-stationary
+ * recurrence, and a custom backward with the reverse recurrence and pointwise
+ * derivatives. Its "Semantic limits" list names what a canonical version adds
+ * (reset tokens, a nonzero initial state, any width, any length), and its
+ * closing paragraph names an exact parallel chunk forward and backward with
+ * partial chunks. Per batch row b, channel w and step t:
+ *
+ *   i = sigmoid(gate_x)   r = sigmoid(gate_a)   s = softplus(lambda[w])
+ *   a = exp(-c * s * r)   m = sqrt(1 - a^2)
+ *   h[t] = a * h[t-1] + m * i * x           (ordinary token)
+ *   h[t] = i * x                            (reset token: state cleared, multiplier 1)
+ *   h[-1] = h0 (or 0)
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are dense, row-major and owned by the caller. Sequence
+ *    tensors are [B, L, W] with channels contiguous; reset flags are uint8
+ *    [B, L] (nonzero = reset token, shared by all channels of that token).
+ *  - "io" tensors are float32 or bf16 (bit pattern, uint16) per
+ *    rglru_shape_t.io_dtype. lambda, h0, h_last, ckpt, dlambda and dh0 are
+ *    always float32. The carry is float32; bf16 outputs are rounded to nearest
+ *    even.
+ *  - Pointers are device pointers unless stated. Every pointer must be aligned
+ *    to its element size; wider alignment (and W a multiple of 4) selects
+ *    wider vector loads, it never changes results beyond rounding.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream). The library never allocates, frees or synchronises.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error the call returns a status and writes nothing.
+ *  - Outputs must not alias inputs unless an entry point says otherwise.
+ *  - Workspaces: a caller-owned device buffer of at least the queried size,
+ *    aligned to 256 bytes, ZERO-FILLED BEFORE ITS FIRST USE. Every completed
+ *    call leaves it ready for the next one; no clearing between calls is
+ *    needed. One workspace may serve forward and backward calls of any shape
+ *    (size it for the largest), but calls that use the same workspace must not
+ *    overlap in time (same stream, or ordered by events).
+ *    Layout of its first 16 bytes (read-only for callers): a 64-bit call
+ *    counter, a 32-bit counter, and a 32-bit sticky error word whose bit 0 is
+ *    set if a look-back wait ever exceeded its spin limit (the outputs of that
+ *    call are then invalid; it cannot happen while every launched workgroup
+ *    makes progress).
+ */
+#ifndef RGLRU_H_
+#define RGLRU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RGLRU_ABI_VERSION 1
+/* The forward checkpoints the float32 carry every RGLRU_CKPT_STEPS steps. */
+#define RGLRU_CKPT_STEPS 8
+
+typedef enum {
+  RGLRU_IO_F32 = 0,
+  RGLRU_IO_BF16 = 1
+} rglru_io_t;
+
+typedef enum {
+  RGLRU_OK = 0,
+  RGLRU_ERR_INVALID_ARGUMENT = 1,  /* bad shape, NULL required pointer, bad enum */
+  RGLRU_ERR_MISALIGNED = 2,        /* a pointer not aligned to its element size */
+  RGLRU_ERR_WORKSPACE_TOO_SMALL = 3,
+  RGLRU_ERR_UNSUPPORTED = 4,       /* a valid request this build does not implement */
+  RGLRU_ERR_HIP = 5                /* the HIP runtime refused a launch */
+} rglru_status_t;
+
+typedef struct {
+  int64_t batch;    /* B >= 1 */
+  int64_t length;   /* L >= 1 */
+  int64_t width;    /* W >= 1, any value */
+  int32_t io_dtype; /* rglru_io_t */
+  int32_t chunk;    /* time tile of the parallel scan: 0 = library default (64),
+                       or one of 8, 16, 32, 64, 128, 256. Results depend on it
+                       only through floating-point rounding. The backward uses
+                       min(chunk, 128). */
+  float c;          /* decay scale of a = exp(-c * softplus(lambda) * r); 8 in the method */
+  int32_t reserved; /* must be 0 */
+} rglru_shape_t;
+
+/* Number of float32 elements of the forward's carry checkpoint:
+ * B * ceil(L / RGLRU_CKPT_STEPS) * W. Element [b, k, w] holds the carry
+ * entering step k * RGLRU_CKPT_STEPS (so [b, 0, w] = h0 or 0). Returns 0 for
+ * an invalid shape. */
+size_t rglru_ckpt_elems(const rglru_shape_t* shape);
+
+/* Workspace bytes for rglru_fwd, rglru_bwd, and for either (the maximum).
+ * Return 0 for an invalid shape. */
+size_t rglru_fwd_workspace_bytes(const rglru_shape_t* shape);
+size_t rglru_bwd_workspace_bytes(const rglru_shape_t* shape);
+size_t rglru_workspace_bytes(const rglru_shape_t* shape);
+
+/* Forward scan (the operator of the Fattori comparison page: sigmoid gates,
+ * softplus dynamic decay, stationary square-root multiplier, input-gated write,
+ * state-stationary recurrence; canonical reset tokens and initial state as its
+ * "Semantic limits" list describes; an exact chunked parallel form).
+ *
+ *   x, gate_x, gate_a : [B, L, W] io, required.
+ *   lambda            : [W] float32, required (the per-channel a_param).
+ *   reset             : [B, L] uint8 or NULL (no reset tokens).
+ *   h0                : [B, W] float32 or NULL (zero initial state).
+ *   h                 : [B, L, W] io, required output: the state after every step.
+ *   h_last            : [B, W] float32 or NULL: the float32 state after step L-1.
+ *   ckpt              : rglru_ckpt_elems() float32 or NULL. Required if a
+ *                       backward will follow (training); NULL for inference.
+ *   workspace         : see Conventions.
+ */
+rglru_status_t rglru_fwd(const rglru_shape_t* shape,
+                         const void* x, const void* gate_x, const void* gate_a,
+                         const float* lambda, const uint8_t* reset, const float* h0,
+                         void* h, float* h_last, float* ckpt,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward scan (the custom backward of the same page: reverse recurrence,
+ * pointwise derivatives recomputed from the inputs instead of saved gates,
+ * a_param gradient reduced over batch and time). The loss is taken to be
+ * <dh, h> + <dh_last, h_last>.
+ *
+ *   x, gate_x, gate_a, lambda, reset : exactly as passed to rglru_fwd.
+ *   ckpt              : filled by rglru_fwd with the same shape, required.
+ *                       (It carries h0, so h0 is not passed again.)
+ *   dh                : [B, L, W] io, required: gradient on every h[t].
+ *   dh_last           : [B, W] float32 or NULL: gradient on h_last.
+ *   dx, dgate_x, dgate_a : [B, L, W] io, required outputs.
+ *   dlambda           : [W] float32, required output, overwritten (not accumulated).
+ *   dh0               : [B, W] float32 or NULL: gradient on h0 (0 where t = 0 is a reset).
+ *   workspace         : see Conventions.
+ */
+rglru_status_t rglru_bwd(const rglru_shape_t* shape,
+                         const void* x, const void* gate_x, const void* gate_a,
+                         const float* lambda, const uint8_t* reset, const float* ckpt,
+                         const void* dh, const float* dh_last,
+                         void* dx, void* dgate_x, void* dgate_a,
+                         float* dlambda, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Block-diagonal gate projections (the two BlockDiagonalLinear maps the
+ * Fattori comparison page says the caller computes before the operator):
+ *   gate_x[:, blk k] = x[:, blk k] @ w_x[k] + b_x[blk k]   (and likewise for gate_a)
+ * with blk k = columns [k*block, (k+1)*block).
+ *
+ *   tokens, width, block : T >= 1 rows; width = nblocks * block; block = 256 in this build.
+ *   x                 : [T, width] bf16, required.
+ *   w_x, w_a          : [width/block, block, block] bf16, read as [block, in, out], required.
+ *   b_x, b_a          : [width] bf16 or NULL (zero bias).
+ *   gate_x, gate_a    : [T, width] bf16 outputs (float32 accumulation, rounded once).
+ */
+rglru_status_t rglru_blockdiag_gate_proj_fwd(int64_t tokens, int64_t width, int64_t block,
+                                             const void* x,
+                                             const void* w_x, const void* b_x,
+                                             const void* w_a, const void* b_a,
+                                             void* gate_x, void* gate_a, void* stream);
+
+/* Backward of the projections:
+ *   dx_out = dx_in + dgate_x @ w_x^T + dgate_a @ w_a^T   (per block; dx_in may be NULL)
+ *   dw_x[k] = x_blk^T @ dgate_x_blk,  dw_a likewise     (float32, overwritten)
+ *   db_x = column sums of dgate_x,    db_a likewise     (float32, overwritten; NULL skips)
+ *
+ *   x, w_x, w_a       : as in the forward.
+ *   dgate_x, dgate_a  : [T, width] bf16, required.
+ *   dx_in             : [T, width] bf16 or NULL; dx_out may equal dx_in.
+ *   dx_out            : [T, width] bf16, required.
+ *   dw_x, dw_a        : [width/block, block, block] float32, required.
+ *   db_x, db_a        : [width] float32 or NULL.
+ *   workspace         : at least rglru_blockdiag_gate_proj_bwd_workspace_bytes(); any content.
+ */
+size_t rglru_blockdiag_gate_proj_bwd_workspace_bytes(int64_t tokens, int64_t width, int64_t block);
+rglru_status_t rglru_blockdiag_gate_proj_bwd(int64_t tokens, int64_t width, int64_t block,
+                                             const void* x, const void* w_x, const void* w_a,
+                                             const void* dgate_x, const void* dgate_a,
+                                             const void* dx_in, void* dx_out,
+                                             float* dw_x, float* db_x, float* dw_a, float* db_a,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status. Never NULL. */
+const char* rglru_status_string(rglru_status_t status);
+
+/* RGLRU_ABI_VERSION of the loaded library. */
+int rglru_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGLRU_H_ */

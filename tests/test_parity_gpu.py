@@ -1,0 +1,117 @@
+"""HIP path vs the float64 oracle, element by element, on seeded inputs.
+
+Sizes span several tiles and a ragged tail while the oracle still finishes in
+seconds; the full-size workloads are checked on sampled channels, which the
+oracle computes exactly because channels are independent.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _helpers import DevInputs, compare, host64, run_gpu, run_oracle, sample_channels
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+W = synth.WORKLOADS
+
+
+def _case(glr, wl, chunk=None, variant=0, chans=None, with_dh_last=False, force_reset0=False, label=""):
+    inp = synth.make_inputs(wl, variant=variant, with_dh_last=with_dh_last, force_reset0=force_reset0)
+    d = DevInputs(inp)
+    gpu = run_gpu(glr, d, chunk=chunk)
+    ref = run_oracle(inp, chans=chans)
+    return compare(wl.io, gpu, ref, chans=chans, label=label or wl.name)
+
+
+# ------------------------------------------------------------------ tiny f32 workload
+
+@pytest.mark.parametrize("chunk", [0, 8, 16, 32, 64, 128, 256])
+def test_tiny_f32_all_chunks(gpu_lib, chunk):
+    _case(gpu_lib, W[0], chunk=chunk)
+
+
+def test_tiny_f32_with_state_resets_and_final_grad(gpu_lib):
+    wl = W[0].resized(batch=3, length=77, width=64)
+    wl = synth.dataclasses.replace(wl, doc_mean=9.0, h0=True)
+    _case(gpu_lib, wl, chunk=16, with_dh_last=True)
+
+
+# ------------------------------------------------------------------ reduced bf16 workloads
+
+@pytest.mark.parametrize("chunk", [0, 32, 128])
+def test_restricted_reduced(gpu_lib, chunk):
+    # restricted protocol: zero initial state, no resets; ragged length
+    _case(gpu_lib, W[1].resized(batch=2, length=300, width=1024), chunk=chunk)
+
+
+@pytest.mark.parametrize("width", [1, 3, 63, 65, 100, 130, 2560])
+def test_ragged_widths(gpu_lib, width):
+    wl = synth.dataclasses.replace(W[2].resized(batch=2, length=45, width=width), doc_mean=11.0)
+    _case(gpu_lib, wl, chunk=16, with_dh_last=True)
+
+
+@pytest.mark.parametrize("length", [1, 2, 7, 8, 9, 63, 64, 65])
+def test_short_lengths(gpu_lib, length):
+    wl = synth.dataclasses.replace(W[2].resized(batch=3, length=length, width=256), doc_mean=5.0)
+    _case(gpu_lib, wl, chunk=32, with_dh_last=True)
+
+
+def test_canonical_reset_reduced(gpu_lib):
+    _case(gpu_lib, W[2].resized(batch=2, length=1500, width=512))
+
+
+def test_canonical_dense_resets(gpu_lib):
+    wl = synth.dataclasses.replace(W[2].resized(batch=4, length=600, width=256), doc_mean=20.0)
+    _case(gpu_lib, wl, chunk=64, with_dh_last=True)
+
+
+@pytest.mark.parametrize("length", [2048, 2048 + 37])
+def test_long_memory_reduced(gpu_lib, length):
+    # chunks of 256 with a partial last chunk, long-memory decay range
+    _case(gpu_lib, W[3].resized(length=length, width=256))
+
+
+def test_reset_at_t0_zeroes_dh0_and_ignores_h0(gpu_lib):
+    wl = W[2].resized(batch=2, length=100, width=256)
+    inp = synth.make_inputs(wl, force_reset0=True)
+    d = DevInputs(inp)
+    gpu = run_gpu(gpu_lib, d, chunk=16)
+    assert torch.all(gpu["dh0"] == 0)
+    d.h0 = d.h0 * 3.0 + 1.0
+    gpu2 = run_gpu(gpu_lib, d, chunk=16)
+    assert torch.equal(gpu["h"], gpu2["h"])
+    compare(wl.io, gpu, run_oracle(inp))
+
+
+# ------------------------------------------------------------------ full sizes, sampled channels
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_full_size_pages_shape(gpu_lib, wid):
+    wl = W[wid]
+    ch = sample_channels(wl.width)
+    _case(gpu_lib, wl, chans=ch)
+
+
+@pytest.mark.parametrize("length", [32768, 32768 + 37])
+def test_full_size_long_sequence(gpu_lib, length):
+    wl = W[3].resized(length=length)
+    ch = sample_channels(wl.width, n=24)
+    _case(gpu_lib, wl, chans=ch)
+
+
+def test_full_size_blockdiag_workload_scan(gpu_lib):
+    # the scan of the 8 x 4096 x 2560 workload, on its own inputs as logits
+    wl = W[4]
+    ch = sample_channels(wl.width, n=24)
+    _case(gpu_lib, wl, chans=ch)
