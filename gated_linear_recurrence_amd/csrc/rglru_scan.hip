@@ -54,6 +54,15 @@ constexpr unsigned kSpinLimit = 1u << 20;
 constexpr size_t kHeaderBytes = 256;
 constexpr int kMaxStrip = 512;   // widest channel strip of any variant (64 lanes * 8)
 
+// Widest vector (channels per lane) the forward and backward may use; the
+// host picks the widest one that divides W and matches the pointers' alignment.
+#ifndef RGLRU_FWD_VMAX
+#define RGLRU_FWD_VMAX 4
+#endif
+#ifndef RGLRU_BWD_VMAX
+#define RGLRU_BWD_VMAX 2
+#endif
+
 // ------------------------------------------------------------------ io access
 
 struct F32 {
@@ -205,77 +214,124 @@ struct Header {
   unsigned err;    // sticky error bits
 };
 
-// Carry entering a tile: walk back over the tiles of earlier (forward) or
-// later (backward) chunks of the same row, composing published maps until a
-// published carry, a reset, or the start of the sequence is reached.
-// `pred` is the slot index base of the nearest predecessor, `stride` the slot
-// distance between consecutive predecessors, `npred` how many exist, `init`
-// the carry before the first chunk.
-template <int V>
-__device__ __forceinline__ void look_back(const u64* slot_a, const u64* slot_b, const u64* slot_h,
-                                          long long pred, long long stride, int npred, unsigned tag,
-                                          const float (&init)[V], float (&carry)[V],
-                                          unsigned* err) {
-  float cA[V], cB[V];
-  bool cR = false;
+// LDS of the windowed look-back: one predecessor per wave and round.
+template <int V, int NW>
+struct LookSmem {
+  float a[NW][64 * V];
+  float b[NW][64 * V];
+  float h[NW][64 * V];
+  unsigned char st[NW][64];   // bit 0: map ready, bit 1: carry ready, bit 2: map has a reset
+  int done[64];
+  int pending;
+};
+
+// Carry entering a tile (valid in wave 0 on return). Called by every thread
+// of the workgroup. In each round wave w polls the predecessor at distance
+// w + 1 (tiles of earlier chunks of the same row in the forward, of later
+// chunks in the backward), so one memory round trip covers NW predecessors.
+// Wave 0 then looks for the nearest predecessor whose outgoing carry is
+// known (published, or fixed by a reset inside it) with every map between
+// published, and applies those maps oldest first with the very fma the
+// predecessors use for their own outgoing carries. The carry is therefore
+// bit-identical to the serial chain whatever the timing: results are
+// deterministic run to run.
+// `self` is the slot index of this lane's first channel in this tile,
+// `stride` the slot distance between consecutive predecessors, `npred` how
+// many exist, `init` the carry before the first chunk.
+template <int V, int NW>
+__device__ __forceinline__ void look_back(LookSmem<V, NW>& sm, const u64* slot_a, const u64* slot_b,
+                                          const u64* slot_h, long long self, long long stride, int npred,
+                                          unsigned tag, bool active, int wave, int lane,
+                                          const float (&init)[V], float (&carry)[V], unsigned* err) {
+  bool done = !active;
 #pragma unroll
-  for (int j = 0; j < V; ++j) {
-    cA[j] = 1.0f;
-    cB[j] = 0.0f;
-  }
-  unsigned spins = 0;
-  while (true) {
-    u64 wh[V];
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      wh[j] = poll(slot_h, pred + j);
-      ok = ok && tagged(wh[j], tag);
-    }
-    if (ok) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const float hv = __uint_as_float(static_cast<uint32_t>(wh[j]));
-        carry[j] = cR ? cB[j] : fmaf(cA[j], hv, cB[j]);
-      }
-      return;
-    }
-    u64 wa[V], wb[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      wa[j] = poll(slot_a, pred + j);
-      wb[j] = poll(slot_b, pred + j);
-      ok = ok && tagged(wa[j], tag) && tagged(wb[j], tag);
-    }
-    if (ok) {
-      const bool Rj = (static_cast<uint32_t>(wa[0]) >> 31) != 0;
+  for (int j = 0; j < V; ++j) carry[j] = 0.0f;
+  if (wave == 0) sm.done[lane] = done ? 1 : 0;
+  __syncthreads();
+  for (unsigned round = 0;; ++round) {
+    unsigned char st = 0;
+    if (sm.done[lane] == 0 && wave < npred) {
+      const long long q = self - static_cast<long long>(wave + 1) * stride;
+      u64 wh[V];
+      bool ok = true;
 #pragma unroll
       for (int j = 0; j < V; ++j) {
-        const float Aj = __uint_as_float(static_cast<uint32_t>(wa[j]) & 0x7FFFFFFFu);
-        const float Bj = __uint_as_float(static_cast<uint32_t>(wb[j]));
-        cB[j] = cR ? cB[j] : fmaf(cA[j], Bj, cB[j]);
-        cA[j] *= Aj;
+        wh[j] = poll(slot_h, q + j);
+        ok = ok && tagged(wh[j], tag);
       }
-      cR = cR || Rj;
-      if (cR) {
+      if (ok) {
+        st = 2;
 #pragma unroll
-        for (int j = 0; j < V; ++j) carry[j] = cB[j];
-        return;
-      }
-      pred -= stride;
-      if (--npred == 0) {
+        for (int j = 0; j < V; ++j) sm.h[wave][lane * V + j] = __uint_as_float(static_cast<uint32_t>(wh[j]));
+      } else {
+        u64 wa[V], wb[V];
+        ok = true;
 #pragma unroll
-        for (int j = 0; j < V; ++j) carry[j] = fmaf(cA[j], init[j], cB[j]);
-        return;
+        for (int j = 0; j < V; ++j) {
+          wa[j] = poll(slot_a, q + j);
+          wb[j] = poll(slot_b, q + j);
+          ok = ok && tagged(wa[j], tag) && tagged(wb[j], tag);
+        }
+        if (ok) {
+          st = ((static_cast<uint32_t>(wa[0]) >> 31) != 0) ? 5 : 1;
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            sm.a[wave][lane * V + j] = __uint_as_float(static_cast<uint32_t>(wa[j]) & 0x7FFFFFFFu);
+            sm.b[wave][lane * V + j] = __uint_as_float(static_cast<uint32_t>(wb[j]));
+          }
+        }
       }
-      continue;
     }
-    if (++spins > kSpinLimit) {
-      atomicOr(err, 1u);
+    sm.st[wave][lane] = st;
+    __syncthreads();
+    if (wave == 0) {
+      if (!done) {
+        // nearest resolvable start: a published carry, a reset map, or the sequence start
+        int start = -1;
+        int kind = 0;   // 1: published carry, 2: reset map, 3: initial carry
+        for (int w = 0; w < NW; ++w) {
+          if (w >= npred) {
+            start = w;
+            kind = 3;
+            break;
+          }
+          const unsigned char sw = sm.st[w][lane];
+          if (sw & 2) {
+            start = w;
+            kind = 1;
+            break;
+          }
+          if ((sw & 1) == 0) break;
+          if (sw & 4) {
+            start = w;
+            kind = 2;
+            break;
+          }
+        }
+        if (start >= 0) {
+          float hv[V];
 #pragma unroll
-      for (int j = 0; j < V; ++j) carry[j] = 0.0f;
-      return;
+          for (int j = 0; j < V; ++j) {
+            hv[j] = kind == 1 ? sm.h[start][lane * V + j] : (kind == 2 ? sm.b[start][lane * V + j] : init[j]);
+          }
+          for (int w = start - 1; w >= 0; --w) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) hv[j] = fmaf(sm.a[w][lane * V + j], hv[j], sm.b[w][lane * V + j]);
+          }
+#pragma unroll
+          for (int j = 0; j < V; ++j) carry[j] = hv[j];
+          done = true;
+        } else if (round >= kSpinLimit) {
+          atomicOr(err, 1u);
+          done = true;
+        }
+        sm.done[lane] = done ? 1 : 0;
+      }
+      const bool any = __ballot(!done) != 0ull;
+      if (lane == 0) sm.pending = any ? 1 : 0;
     }
+    __syncthreads();
+    if (sm.pending == 0) break;
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -288,6 +344,18 @@ __device__ __forceinline__ void finish_call(Header* hdr, unsigned n_tiles) {
     atomicExch(&hdr->done, 0u);
     atomicAdd(&hdr->counter, (1ull << 32) - static_cast<u64>(n_tiles));
   }
+}
+
+// Ticket of this workgroup: (tile index, slot tag), wave-uniform.
+__device__ __forceinline__ void take_ticket(Header* hdr, unsigned* s_ticket, unsigned& tile, unsigned& tag) {
+  if (threadIdx.x == 0) {
+    const u64 v = atomicAdd(&hdr->counter, 1ull);
+    s_ticket[0] = static_cast<unsigned>(v);
+    s_ticket[1] = static_cast<unsigned>(v >> 32) + 1u;
+  }
+  __syncthreads();
+  tile = __builtin_amdgcn_readfirstlane(s_ticket[0]);
+  tag = __builtin_amdgcn_readfirstlane(s_ticket[1]);
 }
 
 // ------------------------------------------------------------------ forward
@@ -316,8 +384,9 @@ struct FwdArgs {
   float c;
 };
 
-template <typename IO, int V, int TS, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs p) {
+template <typename IO, int V, int TS, int NW, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void fwd_kernel(FwdArgs p) {
   static_assert(TS % kCkpt == 0, "a wave's steps must cover whole checkpoint intervals");
   constexpr int SW = 64 * V;
   constexpr int T = TS * NW;
@@ -329,17 +398,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs p) {
   __shared__ float s_B[NW][SW];
   __shared__ unsigned s_R[NW];
   __shared__ float s_carry[SW];
+  __shared__ LookSmem<V, NW> s_look;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (threadIdx.x == 0) {
-    const u64 v = atomicAdd(&p.hdr->counter, 1ull);
-    s_ticket[0] = static_cast<unsigned>(v);
-    s_ticket[1] = static_cast<unsigned>(v >> 32) + 1u;
-  }
-  __syncthreads();
-  const unsigned tile = __builtin_amdgcn_readfirstlane(s_ticket[0]);
-  const unsigned tag = __builtin_amdgcn_readfirstlane(s_ticket[1]);
+  unsigned tile, tag;
+  take_ticket(p.hdr, s_ticket, tile, tag);
   const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
   const int chunk = static_cast<int>(tile / rows);
   const int row = static_cast<int>(tile - static_cast<unsigned>(chunk) * rows);
@@ -429,57 +493,56 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs p) {
   if (lane == 0) s_R[wave] = rmask != 0u ? 1u : 0u;
   __syncthreads();
 
-  if (wave == 0) {
-    float GA[V], GB[V];
-    bool GR = false;
+  // the tile's map (every wave computes it; wave 0 publishes it)
+  float GA[V], GB[V];
+  bool GR = false;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    GA[j] = 1.0f;
+    GB[j] = 0.0f;
+  }
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const bool Rw = s_R[w] != 0u;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      GA[j] = 1.0f;
-      GB[j] = 0.0f;
+      const float Aw = s_A[w][lane * V + j];
+      const float Bw = s_B[w][lane * V + j];
+      GB[j] = Rw ? Bw : fmaf(Aw, GB[j], Bw);
+      GA[j] *= Aw;
     }
+    GR = GR || Rw;
+  }
+  const size_t sbase = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
+  const bool has_succ = chunk < p.n_chunks - 1;
+  float init[V], carry[V];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const bool Rw = s_R[w] != 0u;
+  for (int j = 0; j < V; ++j) init[j] = (active && p.h0 != nullptr) ? p.h0[b * W + ch + j] : 0.0f;
+  if (chunk == 0) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = init[j];
+  } else {
+    if (wave == 0 && active && has_succ) {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
-        const float Aw = s_A[w][lane * V + j];
-        const float Bw = s_B[w][lane * V + j];
-        GB[j] = Rw ? Bw : fmaf(Aw, GB[j], Bw);
-        GA[j] *= Aw;
+        publish(p.slot_a, sbase + j, tag, encode_a(GA[j], GR));
+        publish(p.slot_b, sbase + j, tag, __float_as_uint(GB[j]));
       }
-      GR = GR || Rw;
     }
-    if (active) {
-      const size_t sbase = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
-      const bool has_succ = chunk < p.n_chunks - 1;
-      float init[V], carry[V];
+    look_back<V, NW>(s_look, p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(sbase),
+                     static_cast<long long>(rows) * SW, chunk, tag, active, wave, lane, init, carry,
+                     &p.hdr->err);
+  }
+  if (wave == 0 && active) {
+    if (has_succ) {
 #pragma unroll
-      for (int j = 0; j < V; ++j) init[j] = p.h0 != nullptr ? p.h0[b * W + ch + j] : 0.0f;
-      if (chunk == 0) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) carry[j] = init[j];
-      } else {
-        if (has_succ) {
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            publish(p.slot_a, sbase + j, tag, encode_a(GA[j], GR));
-            publish(p.slot_b, sbase + j, tag, __float_as_uint(GB[j]));
-          }
-        }
-        look_back<V>(p.slot_a, p.slot_b, p.slot_h,
-                     static_cast<long long>(sbase) - static_cast<long long>(rows) * SW,
-                     static_cast<long long>(rows) * SW, chunk, tag, init, carry, &p.hdr->err);
+      for (int j = 0; j < V; ++j) {
+        const float hout = GR ? GB[j] : fmaf(GA[j], carry[j], GB[j]);
+        publish(p.slot_h, sbase + j, tag, __float_as_uint(hout));
       }
-      if (has_succ) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const float hout = GR ? GB[j] : fmaf(GA[j], carry[j], GB[j]);
-          publish(p.slot_h, sbase + j, tag, __float_as_uint(hout));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < V; ++j) s_carry[lane * V + j] = carry[j];
     }
+#pragma unroll
+    for (int j = 0; j < V; ++j) s_carry[lane * V + j] = carry[j];
   }
   __syncthreads();
 
@@ -529,12 +592,13 @@ struct BwdArgs {
   void* dx;
   void* dgx;
   void* dga;
-  float* dlam_part;   // [n_chunks, B, W]
+  float* dlam;
   float* dh0;
   Header* hdr;
   u64* slot_a;
   u64* slot_b;
   u64* slot_h;
+  u64* slot_p;       // per-tile lambda-gradient partials
   long long L;
   long long n_ckpt;
   int B;
@@ -546,9 +610,10 @@ struct BwdArgs {
 };
 
 // Every wave covers exactly one checkpoint interval, whose entering carry the
-// forward stored.
-template <typename IO, int V, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs p) {
+// forward stored. Tiles are handed out from the last chunk backwards.
+template <typename IO, int V, int NW, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void bwd_kernel(BwdArgs p) {
   constexpr int TS = kCkpt;
   constexpr int SW = 64 * V;
   constexpr int T = TS * NW;
@@ -560,17 +625,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs p) {
   __shared__ float s_B[NW][SW];
   __shared__ unsigned s_R[NW];
   __shared__ float s_carry[SW];
+  __shared__ LookSmem<V, NW> s_look;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (threadIdx.x == 0) {
-    const u64 v = atomicAdd(&p.hdr->counter, 1ull);
-    s_ticket[0] = static_cast<unsigned>(v);
-    s_ticket[1] = static_cast<unsigned>(v >> 32) + 1u;
-  }
-  __syncthreads();
-  const unsigned tile = __builtin_amdgcn_readfirstlane(s_ticket[0]);
-  const unsigned tag = __builtin_amdgcn_readfirstlane(s_ticket[1]);
+  unsigned tile, tag;
+  take_ticket(p.hdr, s_ticket, tile, tag);
   const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
   const int crev = static_cast<int>(tile / rows);          // 0 = last chunk in time
   const int row = static_cast<int>(tile - static_cast<unsigned>(crev) * rows);
@@ -622,7 +682,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs p) {
   // Recompute the forward through this wave's steps and turn every step into
   // the coefficients the reverse pass needs:
   //   g = G + dh;  dx = g*cx;  dgate_x = g*cgx;  dgate_a = g*cga;
-  //   dlambda partial += g*cl;  G <- alpha*g  (0 after a reset token)
+  //   lambda-gradient partial += g*cl;  G <- alpha*g  (0 after a reset token)
   // with dl = g * a*(h_prev - a*i*x/m) off reset tokens (0 on them).
   float cx[TS][V], cgx[TS][V], cga[TS][V], cl[TS][V], al[TS][V], dhv[TS][V];
 #pragma unroll
@@ -683,57 +743,55 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs p) {
   if (lane == 0) s_R[wave] = rmask != 0u ? 1u : 0u;
   __syncthreads();
 
-  if (wave == 0) {
-    float GA[V], GB[V];
-    bool GR = false;
+  float GA[V], GB[V];
+  bool GR = false;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    GA[j] = 1.0f;
+    GB[j] = 0.0f;
+  }
+#pragma unroll
+  for (int w = NW - 1; w >= 0; --w) {
+    const bool Rw = s_R[w] != 0u;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      GA[j] = 1.0f;
-      GB[j] = 0.0f;
+      const float Aw = s_A[w][lane * V + j];
+      const float Bw = s_B[w][lane * V + j];
+      GB[j] = Rw ? Bw : fmaf(Aw, GB[j], Bw);
+      GA[j] *= Aw;
     }
+    GR = GR || Rw;
+  }
+  const size_t sbase = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
+  const bool has_succ = crev < p.n_chunks - 1;
+  float init[V], carry[V];
 #pragma unroll
-    for (int w = NW - 1; w >= 0; --w) {
-      const bool Rw = s_R[w] != 0u;
+  for (int j = 0; j < V; ++j) init[j] = (active && p.dh_last != nullptr) ? p.dh_last[b * W + ch + j] : 0.0f;
+  if (crev == 0) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = init[j];
+  } else {
+    if (wave == 0 && active && has_succ) {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
-        const float Aw = s_A[w][lane * V + j];
-        const float Bw = s_B[w][lane * V + j];
-        GB[j] = Rw ? Bw : fmaf(Aw, GB[j], Bw);
-        GA[j] *= Aw;
+        publish(p.slot_a, sbase + j, tag, encode_a(GA[j], GR));
+        publish(p.slot_b, sbase + j, tag, __float_as_uint(GB[j]));
       }
-      GR = GR || Rw;
     }
-    if (active) {
-      const size_t sbase = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
-      const bool has_succ = crev < p.n_chunks - 1;
-      float init[V], carry[V];
+    look_back<V, NW>(s_look, p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(sbase),
+                     static_cast<long long>(rows) * SW, crev, tag, active, wave, lane, init, carry,
+                     &p.hdr->err);
+  }
+  if (wave == 0 && active) {
+    if (has_succ) {
 #pragma unroll
-      for (int j = 0; j < V; ++j) init[j] = p.dh_last != nullptr ? p.dh_last[b * W + ch + j] : 0.0f;
-      if (crev == 0) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) carry[j] = init[j];
-      } else {
-        if (has_succ) {
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            publish(p.slot_a, sbase + j, tag, encode_a(GA[j], GR));
-            publish(p.slot_b, sbase + j, tag, __float_as_uint(GB[j]));
-          }
-        }
-        look_back<V>(p.slot_a, p.slot_b, p.slot_h,
-                     static_cast<long long>(sbase) - static_cast<long long>(rows) * SW,
-                     static_cast<long long>(rows) * SW, crev, tag, init, carry, &p.hdr->err);
+      for (int j = 0; j < V; ++j) {
+        const float gout = GR ? GB[j] : fmaf(GA[j], carry[j], GB[j]);
+        publish(p.slot_h, sbase + j, tag, __float_as_uint(gout));
       }
-      if (has_succ) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const float gout = GR ? GB[j] : fmaf(GA[j], carry[j], GB[j]);
-          publish(p.slot_h, sbase + j, tag, __float_as_uint(gout));
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < V; ++j) s_carry[lane * V + j] = carry[j];
     }
+#pragma unroll
+    for (int j = 0; j < V; ++j) s_carry[lane * V + j] = carry[j];
   }
   __syncthreads();
 
@@ -774,34 +832,76 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs p) {
     if (chunk == 0 && wave == 0 && p.dh0 != nullptr) store_f32v<V>(p.dh0 + b * W + ch, G);
   }
 
-  // fixed-order reduction of the lambda-gradient partial over the waves
+  // the tile's lambda-gradient partial: fixed-order sum over the waves, published tagged
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < V; ++j) s_A[wave][lane * V + j] = dl_acc[j];
   __syncthreads();
   if (wave == 0 && active) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      float s = 0.0f;
+      for (int w = 0; w < NW; ++w) s += s_A[w][lane * V + j];
+      publish(p.slot_p, sbase + j, tag, __float_as_uint(s));
+    }
+  }
+
+  // The tile with the largest ticket of its channel strip (chunk 0, last
+  // batch row) sums the strip's partials in a fixed order: waves take
+  // contiguous runs of (chunk, batch) pairs, then wave 0 adds the runs in
+  // wave order. Every partial it waits for belongs to a smaller ticket.
+  if (crev == p.n_chunks - 1 && b == p.B - 1) {
+    const int n_parts = p.n_chunks * p.B;
+    const int per = (n_parts + NW - 1) / NW;
+    const int k0 = wave * per;
+    const int k1 = k0 + per < n_parts ? k0 + per : n_parts;
     float s[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) s[j] = 0.0f;
-    for (int w = 0; w < NW; ++w) {
+    bool failed = false;
+    if (active) {
+      for (int k = k0; k < k1; ++k) {
+        const int cr = k / p.B;
+        const int bb = k - cr * p.B;
+        const long long q = (static_cast<long long>(cr) * rows + static_cast<long long>(bb) * p.n_strips + strip) * SW +
+                            static_cast<long long>(lane) * V;
+        u64 wv[V];
+        unsigned spins = 0;
+        while (true) {
+          bool ok = true;
 #pragma unroll
-      for (int j = 0; j < V; ++j) s[j] += s_A[w][lane * V + j];
+          for (int j = 0; j < V; ++j) {
+            wv[j] = poll(p.slot_p, q + j);
+            ok = ok && tagged(wv[j], tag);
+          }
+          if (ok) break;
+          if (++spins > kSpinLimit) {
+            failed = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+#pragma unroll
+        for (int j = 0; j < V; ++j) s[j] += __uint_as_float(static_cast<uint32_t>(wv[j]));
+      }
     }
-    store_f32v<V>(p.dlam_part + (static_cast<long long>(chunk) * p.B + b) * W + ch, s);
+    if (failed) atomicOr(&p.hdr->err, 1u);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < V; ++j) s_A[wave][lane * V + j] = s[j];
+    __syncthreads();
+    if (wave == 0 && active) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        float tot = 0.0f;
+        for (int w = 0; w < NW; ++w) tot += s_A[w][lane * V + j];
+        const float lm = p.lam[ch + j];
+        const float sig = 1.0f / (1.0f + expf(-lm));
+        p.dlam[ch + j] = -p.c * sig * tot;
+      }
+    }
   }
   if (threadIdx.x == 0) finish_call(p.hdr, p.n_tiles);
-}
-
-// dlambda[w] = -c * sigmoid(lambda[w]) * sum over (chunk, b) of the partials, in a fixed order.
-__global__ __launch_bounds__(256) void dlam_reduce_kernel(const float* part, const float* lam,
-                                                          float* dlam, int n_parts, int W, float c) {
-  const int w = blockIdx.x * 256 + threadIdx.x;
-  if (w >= W) return;
-  float s = 0.0f;
-  for (int k = 0; k < n_parts; ++k) s += part[static_cast<long long>(k) * W + w];
-  const float lm = lam[w];
-  const float sig = 1.0f / (1.0f + expf(-lm));
-  dlam[w] = -c * sig * s;
 }
 
 // ------------------------------------------------------------------ host side
@@ -850,27 +950,21 @@ size_t slot_words(const rglru_shape_t* s, int n_chunks) {
          round_up(static_cast<size_t>(s->width), kMaxStrip);
 }
 
-size_t fwd_ws(const rglru_shape_t* s) {
-  const Geometry g = geometry(s);
-  return kHeaderBytes + 3 * round_up(slot_words(s, g.n_chunks_f) * 8, 256);
+constexpr int kSlotKinds = 4;   // map A, map B, carry, lambda-gradient partial
+
+size_t ws_bytes(const rglru_shape_t* s, int n_chunks) {
+  return kHeaderBytes + kSlotKinds * round_up(slot_words(s, n_chunks) * 8, 256);
 }
 
-size_t bwd_part_offset(const rglru_shape_t* s) {
-  const Geometry g = geometry(s);
-  return kHeaderBytes + 3 * round_up(slot_words(s, g.n_chunks_b) * 8, 256);
-}
-
-size_t bwd_ws(const rglru_shape_t* s) {
-  const Geometry g = geometry(s);
-  return bwd_part_offset(s) +
-         round_up(static_cast<size_t>(g.n_chunks_b) * s->batch * s->width * sizeof(float), 256);
-}
+size_t fwd_ws(const rglru_shape_t* s) { return ws_bytes(s, geometry(s).n_chunks_f); }
+size_t bwd_ws(const rglru_shape_t* s) { return ws_bytes(s, geometry(s).n_chunks_b); }
 
 struct Slots {
   Header* hdr;
   u64* a;
   u64* b;
   u64* h;
+  u64* p;
 };
 
 Slots slots_in(void* ws, size_t words) {
@@ -881,6 +975,7 @@ Slots slots_in(void* ws, size_t words) {
   sl.a = reinterpret_cast<u64*>(base + kHeaderBytes);
   sl.b = reinterpret_cast<u64*>(base + kHeaderBytes + kind);
   sl.h = reinterpret_cast<u64*>(base + kHeaderBytes + 2 * kind);
+  sl.p = reinterpret_cast<u64*>(base + kHeaderBytes + 3 * kind);
   return sl;
 }
 
@@ -898,12 +993,15 @@ int pick_vec(int vmax, long long W, int io_bytes, std::initializer_list<const vo
   return 1;
 }
 
+// waves per SIMD the register budget is fitted to: two workgroups per CU
+constexpr int wpe_for(int nw) { return nw >= 16 ? 4 : (nw >= 2 ? nw / 2 : 1); }
+
 template <typename IO, int V, int TS, int NW>
 rglru_status_t launch_fwd(FwdArgs a, hipStream_t stream) {
   a.n_strips = static_cast<int>(ceil_div(a.W, 64 * V));
   a.n_chunks = static_cast<int>(ceil_div(a.L, TS * NW));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  hipLaunchKernelGGL((fwd_kernel<IO, V, TS, NW>), dim3(a.n_tiles), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<IO, V, TS, NW, wpe_for(NW)>), dim3(a.n_tiles), dim3(NW * 64), 0, stream, a);
   return launch_status();
 }
 
@@ -935,35 +1033,31 @@ rglru_status_t dispatch_fwd(int T, int V, FwdArgs a, hipStream_t stream) {
 }
 
 template <typename IO, int V, int NW>
-rglru_status_t launch_bwd(BwdArgs a, const float* lam, float* dlam, hipStream_t stream) {
+rglru_status_t launch_bwd(BwdArgs a, hipStream_t stream) {
   a.n_strips = static_cast<int>(ceil_div(a.W, 64 * V));
   a.n_chunks = static_cast<int>(ceil_div(a.L, kCkpt * NW));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  hipLaunchKernelGGL((bwd_kernel<IO, V, NW>), dim3(a.n_tiles), dim3(NW * 64), 0, stream, a);
-  rglru_status_t st = launch_status();
-  if (st != RGLRU_OK) return st;
-  hipLaunchKernelGGL(dlam_reduce_kernel, dim3(static_cast<unsigned>(ceil_div(a.W, 256))), dim3(256), 0, stream,
-                     static_cast<const float*>(a.dlam_part), lam, dlam, a.n_chunks * a.B, a.W, a.c);
+  hipLaunchKernelGGL((bwd_kernel<IO, V, NW, wpe_for(NW)>), dim3(a.n_tiles), dim3(NW * 64), 0, stream, a);
   return launch_status();
 }
 
 template <typename IO, int V>
-rglru_status_t dispatch_bwd_chunk(int Tb, BwdArgs a, const float* lam, float* dlam, hipStream_t stream) {
+rglru_status_t dispatch_bwd_chunk(int Tb, BwdArgs a, hipStream_t stream) {
   switch (Tb) {
-    case 8: return launch_bwd<IO, V, 1>(a, lam, dlam, stream);
-    case 16: return launch_bwd<IO, V, 2>(a, lam, dlam, stream);
-    case 32: return launch_bwd<IO, V, 4>(a, lam, dlam, stream);
-    case 64: return launch_bwd<IO, V, 8>(a, lam, dlam, stream);
-    case 128: return launch_bwd<IO, V, 16>(a, lam, dlam, stream);
+    case 8: return launch_bwd<IO, V, 1>(a, stream);
+    case 16: return launch_bwd<IO, V, 2>(a, stream);
+    case 32: return launch_bwd<IO, V, 4>(a, stream);
+    case 64: return launch_bwd<IO, V, 8>(a, stream);
+    case 128: return launch_bwd<IO, V, 16>(a, stream);
     default: break;
   }
   return RGLRU_ERR_UNSUPPORTED;
 }
 
 template <typename IO>
-rglru_status_t dispatch_bwd(int Tb, int V, BwdArgs a, const float* lam, float* dlam, hipStream_t stream) {
-  if (V >= 2) return dispatch_bwd_chunk<IO, 2>(Tb, a, lam, dlam, stream);
-  return dispatch_bwd_chunk<IO, 1>(Tb, a, lam, dlam, stream);
+rglru_status_t dispatch_bwd(int Tb, int V, BwdArgs a, hipStream_t stream) {
+  if (V >= 2) return dispatch_bwd_chunk<IO, 2>(Tb, a, stream);
+  return dispatch_bwd_chunk<IO, 1>(Tb, a, stream);
 }
 
 bool io_aligned(const void* p, int io_bytes) { return p == nullptr || aligned_to(p, io_bytes); }
@@ -1006,8 +1100,7 @@ rglru_status_t rglru_fwd(const rglru_shape_t* s, const void* x, const void* gate
   }
   if (workspace_bytes < fwd_ws(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
 
-  const int vmax = g.io_bytes == 4 ? 4 : 4;
-  const int V = pick_vec(vmax, s->width, g.io_bytes, {x, gate_x, gate_a, h}, {h0, h_last, ckpt});
+  const int V = pick_vec(RGLRU_FWD_VMAX, s->width, g.io_bytes, {x, gate_x, gate_a, h}, {h0, h_last, ckpt});
   const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_f));
   FwdArgs a;
   a.x = x;
@@ -1051,7 +1144,7 @@ rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate
   }
   if (workspace_bytes < bwd_ws(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
 
-  const int V = pick_vec(2, s->width, g.io_bytes, {x, gate_x, gate_a, dh, dx, dgate_x, dgate_a},
+  const int V = pick_vec(RGLRU_BWD_VMAX, s->width, g.io_bytes, {x, gate_x, gate_a, dh, dx, dgate_x, dgate_a},
                          {ckpt, dh_last, dh0});
   const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_b));
   BwdArgs a;
@@ -1066,20 +1159,21 @@ rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate
   a.dx = dx;
   a.dgx = dgate_x;
   a.dga = dgate_a;
-  a.dlam_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_part_offset(s));
+  a.dlam = dlambda;
   a.dh0 = dh0;
   a.hdr = sl.hdr;
   a.slot_a = sl.a;
   a.slot_b = sl.b;
   a.slot_h = sl.h;
+  a.slot_p = sl.p;
   a.L = s->length;
   a.n_ckpt = g.n_ckpt;
   a.B = static_cast<int>(s->batch);
   a.W = static_cast<int>(s->width);
   a.c = s->c;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (s->io_dtype == RGLRU_IO_F32) return dispatch_bwd<F32>(g.Tb, V, a, lambda, dlambda, st);
-  return dispatch_bwd<BF16>(g.Tb, V, a, lambda, dlambda, st);
+  if (s->io_dtype == RGLRU_IO_F32) return dispatch_bwd<F32>(g.Tb, V, a, st);
+  return dispatch_bwd<BF16>(g.Tb, V, a, st);
 }
 
 const char* rglru_status_string(rglru_status_t status) {
