@@ -111,6 +111,9 @@ def main():
     reset = None if inp.reset is None else torch.from_numpy(inp.reset).to(dev)
     h0 = None if inp.h0 is None else torch.from_numpy(inp.h0).to(dev)
     shape = glr.make_shape(B, L, W, base["x"].dtype, chunk)
+    proj = wl.proj_blocks > 0
+    if proj:
+        wx, wa, bx, ba = (io_tensor(getattr(inp, k)) for k in ("wx", "wa", "bx", "ba"))
     n_ck = glr.rglru_ckpt_elems(shape)
     sets = []
     for s in range(args.sets):
@@ -124,36 +127,56 @@ def main():
         d["dh0"] = torch.empty((B, W), dtype=torch.float32, device=dev) if h0 is not None else None
         d["ws"] = glr.Workspace(dev)
         d["ws"].get(glr.rglru_workspace_bytes(shape))
+        if proj:
+            d["gxp"] = torch.empty_like(d["x"])
+            d["gap"] = torch.empty_like(d["x"])
+            d["dxp"] = torch.empty_like(d["x"])
         sets.append(d)
     del base
     stream = torch.cuda.current_stream(dev)
 
     def step(d, evs=None):
-        if evs is not None:
-            evs[0].record(stream)
-        glr.rglru_fwd(d["x"], d["gx"], d["ga"], lam, reset, h0, chunk=chunk, h=d["h"], h_last=d["h_last"],
+        """One pass of the hot path; evs[k] brackets the k-th launch group."""
+        def mark(k):
+            if evs is not None:
+                evs[k].record(stream)
+        mark(0)
+        if proj:
+            x2 = d["x"].view(B * L, W)
+            glr.rglru_blockdiag_gate_proj_fwd(x2, wx, bx, wa, ba, gate_x=d["gxp"].view(B * L, W),
+                                              gate_a=d["gap"].view(B * L, W))
+            gx, ga = d["gxp"], d["gap"]
+        else:
+            gx, ga = d["gx"], d["ga"]
+        mark(1)
+        glr.rglru_fwd(d["x"], gx, ga, lam, reset, h0, chunk=chunk, h=d["h"], h_last=d["h_last"],
                       ckpt=d["ckpt"], workspace=d["ws"])
-        if evs is not None:
-            evs[1].record(stream)
-        glr.rglru_bwd(d["x"], d["gx"], d["ga"], lam, reset, d["ckpt"], d["dh"], None, chunk=chunk,
+        mark(2)
+        glr.rglru_bwd(d["x"], gx, ga, lam, reset, d["ckpt"], d["dh"], None, chunk=chunk,
                       want_dh0=h0 is not None, dx=d["dx"], dgate_x=d["dgx"], dgate_a=d["dga"], dlam=d["dlam"],
                       dh0=d["dh0"], workspace=d["ws"])
-        if evs is not None:
-            evs[2].record(stream)
+        mark(3)
+        if proj:
+            glr.rglru_blockdiag_gate_proj_bwd(d["x"].view(B * L, W), wx, wa, d["dgx"].view(B * L, W),
+                                              d["dga"].view(B * L, W), d["dx"].view(B * L, W),
+                                              dx_out=d["dxp"].view(B * L, W))
+        mark(4)
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pfwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    bwd_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    pbwd_ms = [e[3].elapsed_time(e[4]) for e in evs]
     err = max(d["ws"].error_bits() for d in sets)
     if err:
         print(f"look-back spin limit reported (error bits {err}); timings invalid", file=sys.stderr)
@@ -191,6 +214,7 @@ def main():
                    "step": "rglru_fwd + rglru_bwd"},
         "fwd_ms": round(fwd_avg, 5),
         "bwd_ms": round(bwd_avg, 5),
+        "fwd_plus_bwd_ms": round(fwd_avg + bwd_avg, 5),
         "elements_per_s": N / (ms_per_step * 1e-3),
         "hbm_frac_fwd": round(fwd_gbs / HBM_PEAK_GBS, 4),
         "hbm_frac_fwd_bwd": round(fb_gbs / HBM_PEAK_GBS, 4),
@@ -208,6 +232,21 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if proj:
+        # projection: x read once, both gates written; backward reads x, both gate
+        # gradients and the scan's dx, writes dx (weights and their gradients are small)
+        T = B * L
+        pf_bytes = 3 * 2 * N
+        pb_bytes = 5 * 2 * N
+        flops = 2 * 2 * T * W * wl.proj_block
+        pf = float(np.mean(pfwd_ms))
+        pbk = float(np.mean(pbwd_ms))
+        out["projection"] = {
+            "fwd_ms": round(pf, 5), "bwd_ms": round(pbk, 5),
+            "fwd_gbs": round(pf_bytes / (pf * 1e-3) / 1e9, 1), "bwd_gbs": round(pb_bytes / (pbk * 1e-3) / 1e9, 1),
+            "fwd_tflops": round(flops / (pf * 1e-3) / 1e12, 1), "bwd_tflops": round(2 * flops / (pbk * 1e-3) / 1e12, 1),
+            "mfma_peak_tflops": 2500.0,
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(out), flush=True)
