@@ -56,6 +56,15 @@ constexpr int kMaxStrip = 512;   // widest channel strip of any variant (64 lane
 
 // Widest vector (channels per lane) the forward and backward may use; the
 // host picks the widest one that divides W and matches the pointers' alignment.
+#ifndef RGLRU_FWD_DEPTH
+#define RGLRU_FWD_DEPTH 2
+#endif
+#ifndef RGLRU_FWD_GATE_GROUP
+#define RGLRU_FWD_GATE_GROUP 2
+#endif
+#ifndef RGLRU_FWD_LOOKBACK
+#define RGLRU_FWD_LOOKBACK 4
+#endif
 #ifndef RGLRU_FWD_VMAX
 #define RGLRU_FWD_VMAX 4
 #endif
@@ -81,6 +90,35 @@ template <> struct Raw<4> { using T = uint32_t; };
 template <> struct Raw<8> { using T = u32x2; };
 template <> struct Raw<16> { using T = u32x4; };
 
+// A wave-uniform pointer, forced into scalar registers and the global
+// address space, so that accesses at base + 32-bit per-lane byte offset use
+// the scalar-base address form (one VGPR per lane instead of a 64-bit pair).
+typedef __attribute__((address_space(1))) const char gbyte;
+typedef __attribute__((address_space(1))) char gbyte_w;
+
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ gbyte* uniform_gptr(const void* p) {
+  return reinterpret_cast<gbyte*>(uniform_u64(reinterpret_cast<uint64_t>(p)));
+}
+
+__device__ __forceinline__ gbyte_w* uniform_gptr_w(void* p) {
+  return reinterpret_cast<gbyte_w*>(uniform_u64(reinterpret_cast<uint64_t>(p)));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// dst + 16 * l. The 16-byte form exists only on gfx950, so the host pass
+// (which checks builtins against its own target) does not see it.
+__device__ __forceinline__ void lds_dma16(gbyte* src, void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(const_cast<gbyte_w*>(src), dst, 16, 0, 0);
+#endif
+}
+
 // V consecutive io elements of one row, moved as a single vector access.
 template <typename IO, int V>
 struct Io {
@@ -97,6 +135,24 @@ struct Io {
   }
   static __device__ __forceinline__ void store(void* base, long long off, R r) {
     *reinterpret_cast<R*>(reinterpret_cast<elem*>(base) + off) = r;
+  }
+  // streaming (read-once / write-once) accesses at a wave-uniform base plus a
+  // 32-bit per-lane element offset (selects the scalar-base address form)
+  static __device__ __forceinline__ R load_nt32(const elem* base, unsigned off) {
+    const gbyte* b = uniform_gptr(base);
+    return __builtin_nontemporal_load(
+        reinterpret_cast<__attribute__((address_space(1))) const R*>(b + off * static_cast<unsigned>(sizeof(elem))));
+  }
+  static __device__ __forceinline__ void store_nt32(elem* base, unsigned off, R r) {
+    gbyte_w* b = uniform_gptr_w(base);
+    __builtin_nontemporal_store(
+        r, reinterpret_cast<__attribute__((address_space(1))) R*>(b + off * static_cast<unsigned>(sizeof(elem))));
+  }
+  static __device__ __forceinline__ R load_nt(const void* base, long long off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const R*>(reinterpret_cast<const elem*>(base) + off));
+  }
+  static __device__ __forceinline__ void store_nt(void* base, long long off, R r) {
+    __builtin_nontemporal_store(r, reinterpret_cast<R*>(reinterpret_cast<elem*>(base) + off));
   }
   static __device__ __forceinline__ void unpack(R r, float (&v)[V]) {
     U u;
@@ -162,21 +218,19 @@ __device__ __forceinline__ float sigmoid_f(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * z));
 }
 
-// 1 - e^l for l <= 0, given a = e^l. Near 0 it is the Taylor series of
-// -expm1(l) through l^8 (relative truncation error below 1e-9 for
-// |l| < ln2/2), so the stationary factor sqrt(1 - a^2) keeps full float32
-// precision when a is close to 1; elsewhere 1 - a loses at most one bit.
+// 1 - e^l for l <= 0, given a = e^l. For l > ln 0.9 (a > 0.9, where 1 - a
+// would cancel) it is the Taylor series of -expm1(l) through l^5: the next
+// term is below 2e-8 relative for |l| < 0.106. Elsewhere 1 - a >= 0.1, so
+// the rounding of a costs at most about 1e-6 relative. The stationary factor
+// sqrt(1 - a^2) thus keeps float32 precision when a is close to 1.
 __device__ __forceinline__ float one_minus_exp(float l, float a) {
-  float q = 1.0f / 40320.0f;
-  q = fmaf(q, l, 1.0f / 5040.0f);
-  q = fmaf(q, l, 1.0f / 720.0f);
-  q = fmaf(q, l, 1.0f / 120.0f);
+  float q = 1.0f / 120.0f;
   q = fmaf(q, l, 1.0f / 24.0f);
   q = fmaf(q, l, 1.0f / 6.0f);
   q = fmaf(q, l, 0.5f);
   q = fmaf(q, l, 1.0f);
   const float near0 = -l * q;
-  return (l > -0.34657359f) ? near0 : 1.0f - a;
+  return (l > -0.10536052f) ? near0 : 1.0f - a;
 }
 
 // Per-channel decay constants: cs = -c * softplus(lambda), k2 = cs * log2 e.
@@ -195,6 +249,13 @@ __device__ __forceinline__ void publish(u64* slot, size_t idx, unsigned tag, uin
 
 __device__ __forceinline__ u64 poll(const u64* slot, size_t idx) {
   return __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// poll at a wave-uniform slot pointer plus a per-lane byte offset
+__device__ __forceinline__ u64 poll_at(const u64* uniform_slot, unsigned lane_bytes) {
+  gbyte* b = uniform_gptr(uniform_slot);
+  return __hip_atomic_load(reinterpret_cast<__attribute__((address_space(1))) const u64*>(b + lane_bytes),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ bool tagged(u64 w, unsigned tag) {
@@ -336,6 +397,94 @@ __device__ __forceinline__ void look_back(LookSmem<V, NW>& sm, const u64* slot_a
   }
 }
 
+// Carry entering a tile, computed by one wave (the workgroup's control
+// wave). Each round polls the published words of the K nearest predecessors
+// (tiles of earlier chunks of the same row in the forward, later chunks in the
+// backward) in one memory round trip, finds the nearest one whose outgoing
+// carry is known (published, fixed by a reset inside it, or the sequence
+// start) with every map between published, and applies those maps oldest
+// first with the very fma the predecessors use for their own outgoing
+// carries: the carry is bit-identical to the serial chain whatever the
+// timing. `self` is the slot index of this lane's first channel, `stride` the
+// slot distance between consecutive predecessors, `npred` how many exist.
+// `self` is split into a wave-uniform part and a per-lane part below 2^29 so
+// the polls address a scalar base plus one 32-bit lane offset.
+// Returns false if the spin limit was reached (the carry is then 0).
+template <int V, int K>
+__device__ __forceinline__ bool look_back_wave(const u64* slot_a, const u64* slot_b, const u64* slot_h,
+                                               long long self_uniform, unsigned self_lane, long long stride,
+                                               int npred, unsigned tag, const float (&init)[V],
+                                               float (&carry)[V]) {
+  const unsigned lane_bytes = self_lane * 8u;
+  for (unsigned round = 0; round < kSpinLimit; ++round) {
+    u64 wh[K][V], wa[K][V], wb[K][V];
+#pragma unroll
+    for (int d = 0; d < K; ++d) {
+      const long long q = self_uniform - static_cast<long long>(d + 1) * stride;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        wh[d][j] = d < npred ? poll_at(slot_h + q, lane_bytes + 8u * j) : 0ull;
+        wa[d][j] = d < npred ? poll_at(slot_a + q, lane_bytes + 8u * j) : 0ull;
+        wb[d][j] = d < npred ? poll_at(slot_b + q, lane_bytes + 8u * j) : 0ull;
+      }
+    }
+    int start = -1;
+    int kind = 0;     // 1: published carry, 2: map with a reset, 3: sequence start
+    bool open = true; // every nearer map is published
+#pragma unroll
+    for (int d = 0; d < K; ++d) {
+      if (open && start < 0) {
+        if (d >= npred) {
+          start = d;
+          kind = 3;
+        } else {
+          bool hr = true, ar = true;
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            hr = hr && tagged(wh[d][j], tag);
+            ar = ar && tagged(wa[d][j], tag) && tagged(wb[d][j], tag);
+          }
+          if (hr) {
+            start = d;
+            kind = 1;
+          } else if (!ar) {
+            open = false;
+          } else if ((static_cast<uint32_t>(wa[d][0]) >> 31) != 0) {
+            start = d;
+            kind = 2;
+          }
+        }
+      }
+    }
+    if (start >= 0) {
+      float hv[V];
+      bool have = false;
+#pragma unroll
+      for (int d = K - 1; d >= 0; --d) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const float hd = __uint_as_float(static_cast<uint32_t>(wh[d][j]));
+          const float ad = __uint_as_float(static_cast<uint32_t>(wa[d][j]) & 0x7FFFFFFFu);
+          const float bd = __uint_as_float(static_cast<uint32_t>(wb[d][j]));
+          if (d == start) {
+            hv[j] = kind == 1 ? hd : (kind == 2 ? bd : init[j]);
+          } else if (have) {
+            hv[j] = fmaf(ad, hv[j], bd);
+          }
+        }
+        if (d == start) have = true;
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) carry[j] = hv[j];
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) carry[j] = 0.0f;
+  return false;
+}
+
 // Called once per workgroup at its end: the last one re-arms the ticket
 // counter and advances the call counter (and with it the slot tag).
 __device__ __forceinline__ void finish_call(Header* hdr, unsigned n_tiles) {
@@ -384,198 +533,489 @@ struct FwdArgs {
   float c;
 };
 
-template <typename IO, int V, int TS, int NW, int WPE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
-void fwd_kernel(FwdArgs p) {
-  static_assert(TS % kCkpt == 0, "a wave's steps must cover whole checkpoint intervals");
-  constexpr int SW = 64 * V;
-  constexpr int T = TS * NW;
+// Flags in LDS between the waves of a workgroup. Workgroup-scope relaxed
+// atomics on the LDS variable itself compile to plain ds_write / ds_read:
+// no wait on the issuing wave's global memory traffic.
+__device__ __forceinline__ void lds_flag_set(int* flag, int v) {
+  __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_flag_wait(int* flag, int v) {
+  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != v) __builtin_amdgcn_s_sleep(1);
+}
+__device__ __forceinline__ void lds_count_add(int* count) {
+  __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_count_wait(int* count, int v) {
+  while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < v) __builtin_amdgcn_s_sleep(1);
+}
+
+// s_waitcnt immediates (gfx9 layout: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
+
+// Persistent, software-pipelined forward with a producer wave.
+//
+// Waves 0 .. NW-1 are data waves: each owns TS steps of a tile for 64*V
+// channels. Waves NW .. NW+V-1 are control waves, one per channel of a lane
+// (control wave j handles channel lane*V + j), and wave NW+V is the load wave.
+// One barrier per iteration. In iteration i, with t_i the i-th ticket of this
+// workgroup:
+//   control waves : run the look-back of t_{i-1}, whose map went out during
+//                   the previous iteration, publish its outgoing carry and hand
+//                   the incoming one to the data waves through LDS; take
+//                   ticket t_{i+2}; once every data wave has reduced its steps
+//                   of t_i, publish the map of t_i; evaluate the per-channel
+//                   decay constants of t_{i+1};
+//   load wave     : once the look-back polls are on their way, stream the raw
+//                   words (and reset flags) of t_{i+1} from HBM straight into
+//                   LDS (global_load_lds) and wait for them;
+//   data waves    : evaluate the gates of t_i from LDS into registers as
+//                   (alpha, write) pairs, reduce their steps to an affine map
+//                   and report it, then wait for the carry of t_{i-1} and replay
+//                   it from the pairs kept since the previous iteration,
+//                   storing h.
+// A map is published part-way through the iteration that evaluates it and
+// looked back from at the start of the next, so the predecessors' words are
+// mostly visible by then. The data waves issue no loads and the control waves
+// only their polls, so no wave waits on memory traffic it does not need (the
+// vector memory counter retires in order), and the polls are not queued
+// behind a tile of loads. The only waits between waves inside an iteration
+// are one-directional LDS flags (data -> control for the maps, control ->
+// data and load for the carry and the polls), so they cannot deadlock.
+//
+// A staged step row is 256 bytes (64 lanes, 4 bytes each). WIDE loads move 16
+// bytes per lane, so one instruction fills 4 step rows and a tile takes
+// 3 * TS * NW / 4 of them (a wave can have at most 63 in flight); otherwise
+// each instruction fills one row with 2 or 4 bytes per lane (every lane still
+// gets its own 4-byte slot, the value zero-extended).
+template <typename IO, int V, int TS, int NW, bool WIDE>
+__global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
+  static_assert((TS * NW) % kCkpt == 0 && (TS % kCkpt == 0 || kCkpt % TS == 0),
+                "checkpoint steps fall on wave boundaries");
+  static_assert(TS <= 32, "reset flags of a wave's steps fit one mask word");
   using io = Io<IO, V>;
   using R_t = typename io::R;
+  using elem = typename io::elem;
+  constexpr int SW = 64 * V;
+  constexpr int T = TS * NW;
+  constexpr int K = RGLRU_FWD_LOOKBACK;
+  constexpr int LOAD_BYTES = static_cast<int>(sizeof(R_t));
+  static_assert(LOAD_BYTES == 2 || LOAD_BYTES == 4, "one or two channels of 2 or 4 bytes per lane");
+  static_assert(!WIDE || (LOAD_BYTES == 4 && TS % 4 == 0), "wide loads fill 4 rows of 64 four-byte slots");
+  static_assert(!WIDE || 3 * T / 4 + (T + 63) / 64 <= 63, "a tile's wide loads fit the vector memory counter");
 
-  __shared__ unsigned s_ticket[2];
-  __shared__ float s_A[NW][SW];
-  __shared__ float s_B[NW][SW];
-  __shared__ unsigned s_R[NW];
-  __shared__ float s_carry[SW];
-  __shared__ LookSmem<V, NW> s_look;
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][3][NW][TS][256];
+  __shared__ __attribute__((aligned(16))) unsigned char s_flag[2][(T < 64 ? 64 : T) * 4];
+  __shared__ float s_A[2][NW][SW];
+  __shared__ float s_B[2][NW][SW];
+  __shared__ unsigned s_R[2][NW];
+  __shared__ unsigned s_rmask[2][NW];
+  __shared__ float s_cs[2][SW];
+  __shared__ float s_k2[2][SW];
+  __shared__ float s_carry[2][SW];
+  __shared__ unsigned s_tk[8];
+  __shared__ unsigned s_tag;
+  __shared__ int s_carry_ready[V];   // iteration whose carry (channel j) is in s_carry
+  __shared__ int s_polls_out;        // iteration whose look-back polls have been issued
+  __shared__ int s_maps_in;          // data-wave maps reported so far (NW per iteration)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  unsigned tile, tag;
-  take_ticket(p.hdr, s_ticket, tile, tag);
+  const bool ctrl = wave >= NW && wave < NW + V;
+  const int cj = ctrl ? wave - NW : 0;           // channel of a lane a control wave handles
+  const bool loader = wave == NW + V;
   const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
-  const int chunk = static_cast<int>(tile / rows);
-  const int row = static_cast<int>(tile - static_cast<unsigned>(chunk) * rows);
-  const int b = row / p.n_strips;
-  const int strip = row - b * p.n_strips;
-  const int ch = strip * SW + lane * V;
-  const bool active = ch < p.W;
-  const long long t0 = static_cast<long long>(chunk) * T + static_cast<long long>(wave) * TS;
-  const long long rem = p.L - t0;
-  const int nvalid = rem <= 0 ? 0 : (rem >= TS ? TS : static_cast<int>(rem));
-  const long long rowbase = static_cast<long long>(b) * p.L;
   const long long W = p.W;
+  // The control and load waves do little arithmetic but sit on the critical
+  // path (look-back, loads); each shares a SIMD with two data waves whose
+  // gate arithmetic would otherwise take nearly all of its issue slots.
+  if (ctrl || loader) __builtin_amdgcn_s_setprio(3);
 
-  // reset flags of this wave's steps as a wave-uniform bit mask
-  unsigned rmask = 0;
-  if (p.reset != nullptr) {
-    const bool f = lane < nvalid && p.reset[rowbase + t0 + lane] != 0;
-    rmask = static_cast<unsigned>(__ballot(f));
-  }
+  struct Tile {
+    int chunk, b, strip, ch, nvalid;
+    long long t0, rowbase;
+    bool valid, active;
+  };
+  // Lambdas capture by value: a by-reference capture of the kernel arguments
+  // takes their address and moves them to scratch memory.
+  auto tile_of = [=](unsigned tile, int w) {
+    Tile t;
+    t.valid = tile < p.n_tiles;
+    const unsigned tt = t.valid ? tile : 0u;
+    t.chunk = static_cast<int>(tt / rows);
+    const int row = static_cast<int>(tt - static_cast<unsigned>(t.chunk) * rows);
+    t.b = row / p.n_strips;
+    t.strip = row - t.b * p.n_strips;
+    t.ch = t.strip * SW + lane * V;
+    t.active = t.ch < p.W;
+    t.t0 = static_cast<long long>(t.chunk) * T + static_cast<long long>(w) * TS;
+    const long long rem = p.L - t.t0;
+    t.nvalid = rem <= 0 ? 0 : (rem >= TS ? TS : static_cast<int>(rem));
+    t.rowbase = static_cast<long long>(t.b) * p.L;
+    return t;
+  };
 
-  // phase 1: stream the steps in
-  R_t rx[TS], rgx[TS], rga[TS];
-#pragma unroll
-  for (int k = 0; k < TS; ++k) {
-    if (active && k < nvalid) {
-      const long long off = (rowbase + t0 + k) * W + ch;
-      rx[k] = io::load(p.x, off);
-      rgx[k] = io::load(p.gx, off);
-      rga[k] = io::load(p.ga, off);
-    } else {
-      rx[k] = R_t{};
-      rgx[k] = R_t{};
-      rga[k] = R_t{};
-    }
-  }
-  float cs[V], k2[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    cs[j] = 0.0f;
-    k2[j] = 0.0f;
-    if (active) channel_consts(p.lam[ch + j], p.c, cs[j], k2[j]);
-  }
+  // control wave cj: decay constants of channel lane*V + cj of a tile
+  auto tile_consts = [=](unsigned tile, int buf) {
+    const Tile t = tile_of(tile, 0);
+    if (!t.valid) return;
+    float cs = 0.0f, k2 = 0.0f;
+    if (t.active) channel_consts(p.lam[t.ch + cj], p.c, cs, k2);
+    s_cs[buf][lane * V + cj] = cs;
+    s_k2[buf][lane * V + cj] = k2;
+  };
 
-  float al[TS][V], u[TS][V];
+  // load wave: every data wave's raw words of a tile, and the tile's reset
+  // flags, into LDS buffer `buf`. Words past W (last strip only) re-read the
+  // strip's first word and steps past L re-read row L-1; those words are never
+  // used, so every source address stays in bounds.
+  auto load_tile = [=](unsigned tile, int buf) {
+    const Tile t = tile_of(tile, 0);
+    const unsigned char* src[3] = {static_cast<const unsigned char*>(p.x), static_cast<const unsigned char*>(p.gx),
+                                   static_cast<const unsigned char*>(p.ga)};
+    const long long row_bytes = W * static_cast<long long>(sizeof(elem));
+    const long long strip_b = static_cast<long long>(t.strip) * 256;
+    if constexpr (WIDE) {
+      // lane l: step row l / 16 of a group of 4, bytes (l % 16) * 16 .. +15 of
+      // it. The per-lane offset from the tile's first word is fixed; a group's
+      // row offset is wave-uniform and goes into the scalar base (the host
+      // keeps a tile's rows under 2 GiB).
+      const unsigned col = strip_b + (lane & 15) * 16 < row_bytes ? static_cast<unsigned>((lane & 15) * 16) : 0u;
+      const long long tile_off = (t.rowbase + t.t0) * row_bytes + strip_b;
+      if (t.t0 + T <= p.L) {
+        const unsigned lane_off = static_cast<unsigned>(lane >> 4) * static_cast<unsigned>(row_bytes) + col;
 #pragma unroll
-  for (int k = 0; k < TS; ++k) {
-    float xv[V], gxv[V], gav[V];
-    io::unpack(rx[k], xv);
-    io::unpack(rgx[k], gxv);
-    io::unpack(rga[k], gav);
-    const bool rs = (rmask >> k) & 1u;
+        for (int q = 0; q < 3; ++q) {
+          for (int w = 0; w < NW; ++w) {
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const float i = sigmoid_f(gxv[j]);
-      const float r = sigmoid_f(gav[j]);
-      const float l = cs[j] * r;
-      const float a = __builtin_amdgcn_exp2f(k2[j] * r);
-      const float m = __builtin_amdgcn_sqrtf(one_minus_exp(l, a) * (1.0f + a));
-      al[k][j] = rs ? 0.0f : a;
-      u[k][j] = (rs ? 1.0f : m) * i * xv[j];
-    }
-  }
-
-  // this wave's map
-  float A[V], Bv[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    A[j] = 1.0f;
-    Bv[j] = 0.0f;
-  }
-#pragma unroll
-  for (int k = 0; k < TS; ++k) {
-    if (k < nvalid) {
-      const bool rs = (rmask >> k) & 1u;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        Bv[j] = rs ? u[k][j] : fmaf(al[k][j], Bv[j], u[k][j]);
-        A[j] *= al[k][j];
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    s_A[wave][lane * V + j] = A[j];
-    s_B[wave][lane * V + j] = Bv[j];
-  }
-  if (lane == 0) s_R[wave] = rmask != 0u ? 1u : 0u;
-  __syncthreads();
-
-  // the tile's map (every wave computes it; wave 0 publishes it)
-  float GA[V], GB[V];
-  bool GR = false;
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    GA[j] = 1.0f;
-    GB[j] = 0.0f;
-  }
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const bool Rw = s_R[w] != 0u;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const float Aw = s_A[w][lane * V + j];
-      const float Bw = s_B[w][lane * V + j];
-      GB[j] = Rw ? Bw : fmaf(Aw, GB[j], Bw);
-      GA[j] *= Aw;
-    }
-    GR = GR || Rw;
-  }
-  const size_t sbase = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
-  const bool has_succ = chunk < p.n_chunks - 1;
-  float init[V], carry[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) init[j] = (active && p.h0 != nullptr) ? p.h0[b * W + ch + j] : 0.0f;
-  if (chunk == 0) {
-#pragma unroll
-    for (int j = 0; j < V; ++j) carry[j] = init[j];
-  } else {
-    if (wave == 0 && active && has_succ) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        publish(p.slot_a, sbase + j, tag, encode_a(GA[j], GR));
-        publish(p.slot_b, sbase + j, tag, __float_as_uint(GB[j]));
-      }
-    }
-    look_back<V, NW>(s_look, p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(sbase),
-                     static_cast<long long>(rows) * SW, chunk, tag, active, wave, lane, init, carry,
-                     &p.hdr->err);
-  }
-  if (wave == 0 && active) {
-    if (has_succ) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const float hout = GR ? GB[j] : fmaf(GA[j], carry[j], GB[j]);
-        publish(p.slot_h, sbase + j, tag, __float_as_uint(hout));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < V; ++j) s_carry[lane * V + j] = carry[j];
-  }
-  __syncthreads();
-
-  // phase 3: replay from the carry entering this wave
-  if (active) {
-    float hc[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) hc[j] = s_carry[lane * V + j];
-    for (int w = 0; w < wave; ++w) {
-      const bool Rw = s_R[w] != 0u;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        hc[j] = Rw ? s_B[w][lane * V + j] : fmaf(s_A[w][lane * V + j], hc[j], s_B[w][lane * V + j]);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < TS; ++k) {
-      if (k < nvalid) {
-        const long long t = t0 + k;
-        if (p.ckpt != nullptr && (k % kCkpt) == 0) {
-          store_f32v<V>(p.ckpt + (static_cast<long long>(b) * p.n_ckpt + t / kCkpt) * W + ch, hc);
+            for (int k = 0; k < TS; k += 4) {
+              const long long grp = tile_off + static_cast<long long>(w * TS + k) * row_bytes;
+              lds_dma16(uniform_gptr(src[q] + grp) + lane_off, &s_raw[buf][q][w][k][0]);
+            }
+          }
         }
-        const bool rs = (rmask >> k) & 1u;
+      } else {
+        const long long lim = p.L - 1 - t.t0;
 #pragma unroll
-        for (int j = 0; j < V; ++j) hc[j] = rs ? u[k][j] : fmaf(al[k][j], hc[j], u[k][j]);
-        io::store(p.h, (rowbase + t) * W + ch, io::pack(hc));
+        for (int q = 0; q < 3; ++q) {
+          gbyte* base = uniform_gptr(src[q] + tile_off);
+          for (int w = 0; w < NW; ++w) {
+#pragma unroll
+            for (int k = 0; k < TS; k += 4) {
+              const int sr = w * TS + k + (lane >> 4);
+              const unsigned off = static_cast<unsigned>(sr < lim ? sr : lim) * static_cast<unsigned>(row_bytes) + col;
+              lds_dma16(base + off, &s_raw[buf][q][w][k][0]);
+            }
+          }
+        }
+      }
+    } else {
+      const long long col = strip_b / (4 / LOAD_BYTES) + (t.active ? lane * LOAD_BYTES : 0);
+      for (int w = 0; w < NW; ++w) {
+#pragma unroll
+        for (int k = 0; k < TS; ++k) {
+          const long long st = t.t0 + w * TS + k;
+          const long long tk = st < p.L ? st : p.L - 1;
+          const long long off = (t.rowbase + tk) * row_bytes + col;
+#pragma unroll
+          for (int q = 0; q < 3; ++q) {
+            __builtin_amdgcn_global_load_lds(src[q] + off, &s_raw[buf][q][w][k][0], LOAD_BYTES, 0, 0);
+          }
+        }
       }
     }
-    if (p.h_last != nullptr && nvalid > 0 && t0 + nvalid == p.L) {
-      store_f32v<V>(p.h_last + b * W + ch, hc);
+    if (p.reset != nullptr) {
+#pragma unroll
+      for (int h = 0; h < (T + 63) / 64; ++h) {
+        const long long st = t.t0 + h * 64 + lane;
+        const long long tk = st < p.L ? st : p.L - 1;
+        __builtin_amdgcn_global_load_lds(p.reset + t.rowbase + tk, &s_flag[buf][h * 256], 1, 0, 0);
+      }
+    }
+  };
+
+  if (ctrl && cj == 0 && lane == 0) {
+    const u64 v0 = atomicAdd(&p.hdr->counter, 1ull);
+    const u64 v1 = atomicAdd(&p.hdr->counter, 1ull);
+    s_tk[0] = static_cast<unsigned>(v0);
+    s_tk[1] = static_cast<unsigned>(v1);
+#pragma unroll
+    for (int q = 2; q < 8; ++q) s_tk[q] = p.n_tiles;
+    s_tag = static_cast<unsigned>(v0 >> 32) + 1u;
+#pragma unroll
+    for (int j = 0; j < V; ++j) s_carry_ready[j] = -1;
+    s_polls_out = -1;
+    s_maps_in = 0;
+  }
+  __syncthreads();
+  const unsigned tag = __builtin_amdgcn_readfirstlane(s_tag);
+  {
+    const unsigned t0 = __builtin_amdgcn_readfirstlane(s_tk[0]);
+    if (ctrl) tile_consts(t0, 0);
+    if (loader) {
+      if (t0 < p.n_tiles) load_tile(t0, 0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
   }
-  if (threadIdx.x == 0) finish_call(p.hdr, p.n_tiles);
+  __syncthreads();
+
+  // One pipeline iteration. (cal, cu) receive t_i's (alpha, write) pairs,
+  // (pal, pu) hold t_{i-1}'s. Tickets of a workgroup increase, so once t_{i-1}
+  // is past the last tile every later one is too; t_{i+1} was taken in the
+  // previous iteration whenever t_i is a tile.
+  auto iteration = [=](int i, float (&cal)[TS][V], float (&cu)[TS][V], float (&pal)[TS][V],
+                       float (&pu)[TS][V]) -> bool {
+    const unsigned t_cur = __builtin_amdgcn_readfirstlane(s_tk[i & 7]);
+    const unsigned t_nxt = __builtin_amdgcn_readfirstlane(s_tk[(i + 1) & 7]);
+    const unsigned t_prv = i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i + 7) & 7]) : p.n_tiles;
+    const bool cur_ok = t_cur < p.n_tiles;
+    const bool prv_ok = t_prv < p.n_tiles;
+    if (!cur_ok && !prv_ok) return false;
+    const bool nxt_ok = cur_ok && t_nxt < p.n_tiles;
+    const int cb = i & 1;    // raw words, constants, maps and carry of t_i
+    const int pb = cb ^ 1;   // maps and carry of t_{i-1}; raw words and constants of t_{i+1}
+    // Waves that evaluate no gates still define (cal, cu): their previous
+    // contents are dead, and leaving them undefined on some paths would keep
+    // them alive and cost whole-array register copies.
+    auto clear = [&cal, &cu]() {
+#pragma unroll
+      for (int k = 0; k < TS; ++k) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          cal[k][j] = 0.0f;
+          cu[k][j] = 0.0f;
+        }
+      }
+    };
+    // composite map of a whole tile, channel lane*V + cj, from its waves' maps
+    auto tile_map = [=](int mb, float& GA, float& GB, bool& GR) {
+      GA = 1.0f;
+      GB = 0.0f;
+      GR = false;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const bool Rw = s_R[mb][w] != 0u;
+        const float Aw = s_A[mb][w][lane * V + cj];
+        const float Bw = s_B[mb][w][lane * V + cj];
+        GB = Rw ? Bw : fmaf(Aw, GB, Bw);
+        GA *= Aw;
+        GR = GR || Rw;
+      }
+    };
+
+    if (ctrl) {
+      clear();
+      // the carry entering t_{i-1}
+      {
+        const Tile t = tile_of(t_prv, 0);
+        if (prv_ok && t.active) {
+          const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch + cj] : 0.0f;
+          float carry = init;
+          if (t.chunk > 0) {
+            if (cj == 0 && lane == 0) lds_flag_set(&s_polls_out, i);
+            float in[1] = {init}, out[1];
+            if (!look_back_wave<1, K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(t_prv) * SW,
+                                      static_cast<unsigned>(lane * V + cj), static_cast<long long>(rows) * SW,
+                                      t.chunk, tag, in, out)) {
+              atomicOr(&p.hdr->err, 1u);
+            }
+            carry = out[0];
+            if (t.chunk < p.n_chunks - 1) {
+              float GA, GB;
+              bool GR;
+              tile_map(pb, GA, GB, GR);
+              const size_t sidx = static_cast<size_t>(t_prv) * SW + static_cast<size_t>(lane) * V + cj;
+              publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, carry, GB)));
+            }
+          }
+          s_carry[pb][lane * V + cj] = carry;
+        }
+      }
+      // the load wave starts once the polls are out (or there are none)
+      if (cj == 0 && lane == 0) lds_flag_set(&s_polls_out, i);
+      // s_carry is written before the flag that releases the data waves
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lane == 0) lds_flag_set(&s_carry_ready[cj], i);
+      // every slot read later is written: a ticket while this workgroup
+      // still draws them, past the last tile once it has stopped
+      if (cj == 0 && lane == 0) {
+        s_tk[(i + 2) & 7] = cur_ok ? static_cast<unsigned>(atomicAdd(&p.hdr->counter, 1ull)) : p.n_tiles;
+      }
+      // the map of t_i as soon as every data wave has reported its own (a
+      // first chunk publishes its outgoing carry instead)
+      {
+        const Tile t = tile_of(t_cur, 0);
+        if (cur_ok && t.active && t.chunk < p.n_chunks - 1) {
+          lds_count_wait(&s_maps_in, NW * (i + 1));
+          float GA, GB;
+          bool GR;
+          tile_map(cb, GA, GB, GR);
+          const size_t sidx = static_cast<size_t>(t_cur) * SW + static_cast<size_t>(lane) * V + cj;
+          if (t.chunk == 0) {
+            const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch + cj] : 0.0f;
+            publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, init, GB)));
+          } else {
+            publish(p.slot_a, sidx, tag, encode_a(GA, GR));
+            publish(p.slot_b, sidx, tag, __float_as_uint(GB));
+          }
+        }
+      }
+      if (nxt_ok) tile_consts(t_nxt, pb);
+    } else if (loader) {
+      clear();
+      if (nxt_ok) {
+        lds_flag_wait(&s_polls_out, i);
+        load_tile(t_nxt, pb);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    } else {
+      if (cur_ok) {
+        const Tile t = tile_of(t_cur, wave);
+        unsigned rmask = 0;
+        if (p.reset != nullptr) {
+          const unsigned* fl = reinterpret_cast<const unsigned*>(&s_flag[cb][wave * TS * 4]);
+#pragma unroll
+          for (int k = 0; k < TS; ++k) rmask |= (k < t.nvalid && fl[k] != 0u) ? (1u << k) : 0u;
+        }
+        float cs[V], k2[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          cs[j] = s_cs[cb][lane * V + j];
+          k2[j] = s_k2[cb][lane * V + j];
+        }
+        float A[V], Bv[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          A[j] = 1.0f;
+          Bv[j] = 0.0f;
+        }
+        // One step: (alpha, write) of both channels, and the wave's map
+        // extended by it. FULL: every step in range and no reset token, so
+        // no selects.
+        auto gate_step = [&](int k, bool FULL) {
+          float xv[V], gxv[V], gav[V];
+          io::unpack(*reinterpret_cast<const R_t*>(&s_raw[cb][0][wave][k][lane * 4]), xv);
+          io::unpack(*reinterpret_cast<const R_t*>(&s_raw[cb][1][wave][k][lane * 4]), gxv);
+          io::unpack(*reinterpret_cast<const R_t*>(&s_raw[cb][2][wave][k][lane * 4]), gav);
+          const bool rs = FULL ? false : ((rmask >> k) & 1u) != 0u;
+          const bool in = FULL ? true : k < t.nvalid;
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            const float ig = sigmoid_f(gxv[j]);
+            const float r = sigmoid_f(gav[j]);
+            const float a = __builtin_amdgcn_exp2f(k2[j] * r);
+            const float m = __builtin_amdgcn_sqrtf(one_minus_exp(cs[j] * r, a) * (1.0f + a));
+            if (FULL) {
+              cal[k][j] = a;
+              cu[k][j] = m * ig * xv[j];
+              Bv[j] = fmaf(a, Bv[j], cu[k][j]);
+              A[j] *= a;
+            } else {
+              cal[k][j] = rs ? 0.0f : a;
+              cu[k][j] = (rs ? 1.0f : m) * ig * xv[j];
+              if (in) {
+                Bv[j] = rs ? cu[k][j] : fmaf(cal[k][j], Bv[j], cu[k][j]);
+                A[j] *= cal[k][j];
+              }
+            }
+          }
+        };
+        if (rmask == 0u && t.nvalid == TS) {
+#pragma unroll
+          for (int k = 0; k < TS; ++k) gate_step(k, true);
+        } else {
+#pragma unroll
+          for (int k = 0; k < TS; ++k) gate_step(k, false);
+        }
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          s_A[cb][wave][lane * V + j] = A[j];
+          s_B[cb][wave][lane * V + j] = Bv[j];
+        }
+        if (lane == 0) {
+          s_R[cb][wave] = rmask != 0u ? 1u : 0u;
+          s_rmask[cb][wave] = rmask;
+        }
+      } else {
+        clear();
+      }
+      // report the map (every iteration, so the count stays NW per iteration)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lane == 0) lds_count_add(&s_maps_in);
+      if (prv_ok) {
+        // replay t_{i-1} from its carry and store h (and the checkpoint)
+        const Tile t = tile_of(t_prv, wave);
+        // the prefix of the earlier waves' maps does not need the carry
+        float PA[V], PB[V];
+        bool PR = false;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          PA[j] = 1.0f;
+          PB[j] = 0.0f;
+        }
+        for (int w = 0; w < wave; ++w) {
+          const bool Rw = s_R[pb][w] != 0u;
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            const float Aw = s_A[pb][w][lane * V + j];
+            const float Bw = s_B[pb][w][lane * V + j];
+            PB[j] = Rw ? Bw : fmaf(Aw, PB[j], Bw);
+            PA[j] *= Aw;
+          }
+          PR = PR || Rw;
+        }
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          lds_flag_wait(&s_carry_ready[j], i);
+        }
+        asm volatile("" ::: "memory");
+        if (t.active) {
+          float hc[V];
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            const float c0 = s_carry[pb][lane * V + j];
+            hc[j] = PR ? PB[j] : fmaf(PA[j], c0, PB[j]);
+          }
+          const unsigned rmask = s_rmask[pb][wave];
+          elem* hb = static_cast<elem*>(p.h) + (t.rowbase + t.t0) * W + static_cast<long long>(t.strip) * SW;
+#pragma unroll
+          for (int k = 0; k < TS; ++k) {
+            if (k < t.nvalid) {
+              const long long tk = t.t0 + k;
+              if (p.ckpt != nullptr && ((wave * TS + k) % kCkpt) == 0) {
+                store_f32v<V>(p.ckpt + (static_cast<long long>(t.b) * p.n_ckpt + tk / kCkpt) * W + t.ch, hc);
+              }
+              const bool rs = (rmask >> k) & 1u;
+#pragma unroll
+              for (int j = 0; j < V; ++j) hc[j] = rs ? pu[k][j] : fmaf(pal[k][j], hc[j], pu[k][j]);
+              io::store_nt32(hb + static_cast<long long>(k) * W, static_cast<unsigned>(lane * V), io::pack(hc));
+            }
+          }
+          if (p.h_last != nullptr && t.nvalid > 0 && t.t0 + t.nvalid == p.L) {
+            store_f32v<V>(p.h_last + t.b * W + t.ch, hc);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    return true;
+  };
+
+  // register ring: iteration i writes one set and replays the other
+  float al0[TS][V], u0[TS][V], al1[TS][V], u1[TS][V];
+  for (int i = 0;; i += 2) {
+    if (!iteration(i, al0, u0, al1, u1)) break;
+    if (!iteration(i + 1, al1, u1, al0, u0)) break;
+  }
+  if (ctrl && cj == 0 && lane == 0) {
+    // every workgroup took 2 tickets past the last tile; the last one to
+    // finish re-arms the counter and advances the call tag
+    const unsigned taken = p.n_tiles + 2u * gridDim.x;
+    const unsigned prev = atomicAdd(&p.hdr->done, 1u);
+    if (prev == gridDim.x - 1) {
+      atomicExch(&p.hdr->done, 0u);
+      atomicAdd(&p.hdr->counter, (1ull << 32) - static_cast<u64>(taken));
+    }
+  }
 }
 
 // ------------------------------------------------------------------ backward
@@ -926,7 +1366,7 @@ bool shape_ok(const rglru_shape_t* s) {
     default: return false;
   }
   // index arithmetic limits: batch and width fit int, tile counts fit 32 bits
-  if (s->batch > (1LL << 24) || s->width > (1LL << 30)) return false;
+  if (s->batch > (1LL << 24) || s->width > (1LL << 24)) return false;
   const long long strips = ceil_div(s->width, 64);
   const long long tiles = strips * s->batch * ceil_div(s->length, 8);
   if (tiles >= (1LL << 31)) return false;
@@ -936,8 +1376,9 @@ bool shape_ok(const rglru_shape_t* s) {
 Geometry geometry(const rglru_shape_t* s) {
   Geometry g;
   g.io_bytes = s->io_dtype == RGLRU_IO_F32 ? 4 : 2;
-  g.T = s->chunk == 0 ? 64 : s->chunk;
-  g.Tb = g.T > 128 ? 128 : g.T;
+  g.Tb = s->chunk == 0 ? 64 : (s->chunk > 128 ? 128 : s->chunk);
+  // the forward keeps the (alpha, write) pairs of two tiles in registers: at most 64 steps
+  g.T = g.Tb > 64 ? 64 : g.Tb;
   g.n_ckpt = ceil_div(s->length, kCkpt);
   g.n_chunks_f = static_cast<int>(ceil_div(s->length, g.T));
   g.n_chunks_b = static_cast<int>(ceil_div(s->length, g.Tb));
@@ -996,39 +1437,57 @@ int pick_vec(int vmax, long long W, int io_bytes, std::initializer_list<const vo
 // waves per SIMD the register budget is fitted to: two workgroups per CU
 constexpr int wpe_for(int nw) { return nw >= 16 ? 4 : (nw >= 2 ? nw / 2 : 1); }
 
-template <typename IO, int V, int TS, int NW>
+// Number of workgroups of a persistent kernel: as many as fit on the device at once.
+template <typename Kern>
+unsigned persistent_grid(Kern kernel, int threads, unsigned n_tiles) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  if (per_cu < 1) per_cu = 1;
+  const unsigned g = static_cast<unsigned>(cus) * static_cast<unsigned>(per_cu);
+  return g < n_tiles ? g : n_tiles;
+}
+
+template <typename IO, int V, int TS, int NW, bool WIDE>
 rglru_status_t launch_fwd(FwdArgs a, hipStream_t stream) {
   a.n_strips = static_cast<int>(ceil_div(a.W, 64 * V));
   a.n_chunks = static_cast<int>(ceil_div(a.L, TS * NW));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  hipLaunchKernelGGL((fwd_kernel<IO, V, TS, NW, wpe_for(NW)>), dim3(a.n_tiles), dim3(NW * 64), 0, stream, a);
+  auto kernel = fwd_kernel<IO, V, TS, NW, WIDE>;
+  constexpr int threads = (NW + V + 1) * 64;
+  const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
+  if (grid == 0) return RGLRU_ERR_HIP;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
   return launch_status();
 }
 
-template <typename IO, int V>
+template <typename IO, int V, bool WIDE>
 rglru_status_t dispatch_fwd_chunk(int T, FwdArgs a, hipStream_t stream) {
+  // up to 8 data waves (two per SIMD)
   switch (T) {
-    case 8: return launch_fwd<IO, V, 8, 1>(a, stream);
-    case 16: return launch_fwd<IO, V, 8, 2>(a, stream);
-    case 32: return launch_fwd<IO, V, 8, 4>(a, stream);
-    case 64: return launch_fwd<IO, V, 8, 8>(a, stream);
-    case 128: return launch_fwd<IO, V, 8, 16>(a, stream);
-    default: break;
+    case 8: return launch_fwd<IO, V, 8, 1, WIDE>(a, stream);
+    case 16: return launch_fwd<IO, V, 8, 2, WIDE>(a, stream);
+    case 32: return launch_fwd<IO, V, 8, 4, WIDE>(a, stream);
+    default: return launch_fwd<IO, V, 8, 8, WIDE>(a, stream);
   }
-  return RGLRU_ERR_UNSUPPORTED;
 }
 
+// One lane covers 4 bytes of a step row: two bf16 channels or one float32
+// channel (one bf16 channel where the width or alignment rules out pairs).
+// Rows of 16-byte aligned words are loaded 16 bytes per lane.
 template <typename IO>
-rglru_status_t dispatch_fwd(int T, int V, FwdArgs a, hipStream_t stream) {
-  if (T == 256) {
-    // 16 waves of 16 steps: keep the per-lane state within the register budget
-    if (V >= 2) return launch_fwd<IO, 2, 16, 16>(a, stream);
-    return launch_fwd<IO, 1, 16, 16>(a, stream);
-  }
-  switch (V) {
-    case 4: return dispatch_fwd_chunk<IO, 4>(T, a, stream);
-    case 2: return dispatch_fwd_chunk<IO, 2>(T, a, stream);
-    default: return dispatch_fwd_chunk<IO, 1>(T, a, stream);
+rglru_status_t dispatch_fwd(int T, int V, bool wide, FwdArgs a, hipStream_t stream) {
+  constexpr bool f32 = std::is_same<IO, F32>::value;
+  if constexpr (f32) {
+    return wide ? dispatch_fwd_chunk<IO, 1, true>(T, a, stream) : dispatch_fwd_chunk<IO, 1, false>(T, a, stream);
+  } else {
+    if (V >= 2) {
+      return wide ? dispatch_fwd_chunk<IO, 2, true>(T, a, stream) : dispatch_fwd_chunk<IO, 2, false>(T, a, stream);
+    }
+    return dispatch_fwd_chunk<IO, 1, false>(T, a, stream);
   }
 }
 
@@ -1121,9 +1580,13 @@ rglru_status_t rglru_fwd(const rglru_shape_t* s, const void* x, const void* gate
   a.B = static_cast<int>(s->batch);
   a.W = static_cast<int>(s->width);
   a.c = s->c;
+  // 16-byte loads: rows a multiple of 16 bytes, the three inputs 16-byte aligned
+  const bool wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(x, 16) && aligned_to(gate_x, 16) &&
+                    aligned_to(gate_a, 16) && (s->io_dtype == RGLRU_IO_F32 || V >= 2) &&
+                    static_cast<long long>(g.T) * s->width * g.io_bytes < (1ll << 31);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (s->io_dtype == RGLRU_IO_F32) return dispatch_fwd<F32>(g.T, V, a, st);
-  return dispatch_fwd<BF16>(g.T, V, a, st);
+  if (s->io_dtype == RGLRU_IO_F32) return dispatch_fwd<F32>(g.T, 1, wide, a, st);
+  return dispatch_fwd<BF16>(g.T, V, wide, a, st);
 }
 
 rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate_x, const void* gate_a,
