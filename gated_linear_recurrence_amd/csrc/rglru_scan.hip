@@ -612,6 +612,9 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
   __shared__ float s_cs[2][SW];
   __shared__ float s_k2[2][SW];
   __shared__ float s_carry[2][SW];
+  __shared__ float s_PA[2][NW][SW];  // composite of the maps of the waves before each wave
+  __shared__ float s_PB[2][NW][SW];
+  __shared__ unsigned s_PR[2][NW];
   __shared__ unsigned s_tk[8];
   __shared__ unsigned s_tag;
   __shared__ int s_carry_ready[V];   // iteration whose carry (channel j) is in s_carry
@@ -654,14 +657,19 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     return t;
   };
 
-  // control wave cj: decay constants of channel lane*V + cj of a tile
-  auto tile_consts = [=](unsigned tile, int buf) {
+  // control wave cj: decay constants of channel lane*V + cj of a tile, from
+  // the lambda value `lam` of that channel
+  auto tile_consts = [=](unsigned tile, int buf, float lam) {
     const Tile t = tile_of(tile, 0);
     if (!t.valid) return;
     float cs = 0.0f, k2 = 0.0f;
-    if (t.active) channel_consts(p.lam[t.ch + cj], p.c, cs, k2);
+    if (t.active) channel_consts(lam, p.c, cs, k2);
     s_cs[buf][lane * V + cj] = cs;
     s_k2[buf][lane * V + cj] = k2;
+  };
+  auto tile_lam = [=](unsigned tile) -> float {
+    const Tile t = tile_of(tile, 0);
+    return (t.valid && t.active) ? p.lam[t.ch + cj] : 0.0f;
   };
 
   // load wave: every data wave's raw words of a tile, and the tile's reset
@@ -750,7 +758,7 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
   const unsigned tag = __builtin_amdgcn_readfirstlane(s_tag);
   {
     const unsigned t0 = __builtin_amdgcn_readfirstlane(s_tk[0]);
-    if (ctrl) tile_consts(t0, 0);
+    if (ctrl) tile_consts(t0, 0, tile_lam(t0));
     if (loader) {
       if (t0 < p.n_tiles) load_tile(t0, 0);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -804,6 +812,11 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
 
     if (ctrl) {
       clear();
+      // Issued first, used after the look-back: the next ticket and the
+      // lambda values of t_{i+1} (their round trips overlap the polls').
+      unsigned long long ticket = 0;
+      if (cj == 0 && lane == 0 && cur_ok) ticket = atomicAdd(&p.hdr->counter, 1ull);
+      const float lam_nxt = nxt_ok ? tile_lam(t_nxt) : 0.0f;
       // the carry entering t_{i-1}
       {
         const Tile t = tile_of(t_prv, 0);
@@ -837,29 +850,41 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
       if (lane == 0) lds_flag_set(&s_carry_ready[cj], i);
       // every slot read later is written: a ticket while this workgroup
       // still draws them, past the last tile once it has stopped
-      if (cj == 0 && lane == 0) {
-        s_tk[(i + 2) & 7] = cur_ok ? static_cast<unsigned>(atomicAdd(&p.hdr->counter, 1ull)) : p.n_tiles;
-      }
-      // the map of t_i as soon as every data wave has reported its own (a
-      // first chunk publishes its outgoing carry instead)
+      if (cj == 0 && lane == 0) s_tk[(i + 2) & 7] = cur_ok ? static_cast<unsigned>(ticket) : p.n_tiles;
+      if (nxt_ok) tile_consts(t_nxt, pb, lam_nxt);
+      // once every data wave has reported its map of t_i: the prefixes the
+      // data waves replay from, and the published map (a first chunk
+      // publishes its outgoing carry instead)
       {
         const Tile t = tile_of(t_cur, 0);
-        if (cur_ok && t.active && t.chunk < p.n_chunks - 1) {
+        if (cur_ok) {
           lds_count_wait(&s_maps_in, NW * (i + 1));
-          float GA, GB;
-          bool GR;
-          tile_map(cb, GA, GB, GR);
-          const size_t sidx = static_cast<size_t>(t_cur) * SW + static_cast<size_t>(lane) * V + cj;
-          if (t.chunk == 0) {
-            const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch + cj] : 0.0f;
-            publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, init, GB)));
-          } else {
-            publish(p.slot_a, sidx, tag, encode_a(GA, GR));
-            publish(p.slot_b, sidx, tag, __float_as_uint(GB));
+          float GA = 1.0f, GB = 0.0f;
+          bool GR = false;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            s_PA[cb][w][lane * V + cj] = GA;
+            s_PB[cb][w][lane * V + cj] = GB;
+            if (cj == 0 && lane == 0) s_PR[cb][w] = GR ? 1u : 0u;
+            const bool Rw = s_R[cb][w] != 0u;
+            const float Aw = s_A[cb][w][lane * V + cj];
+            const float Bw = s_B[cb][w][lane * V + cj];
+            GB = Rw ? Bw : fmaf(Aw, GB, Bw);
+            GA *= Aw;
+            GR = GR || Rw;
+          }
+          if (t.active && t.chunk < p.n_chunks - 1) {
+            const size_t sidx = static_cast<size_t>(t_cur) * SW + static_cast<size_t>(lane) * V + cj;
+            if (t.chunk == 0) {
+              const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch + cj] : 0.0f;
+              publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, init, GB)));
+            } else {
+              publish(p.slot_a, sidx, tag, encode_a(GA, GR));
+              publish(p.slot_b, sidx, tag, __float_as_uint(GB));
+            }
           }
         }
       }
-      if (nxt_ok) tile_consts(t_nxt, pb);
     } else if (loader) {
       clear();
       if (nxt_ok) {
@@ -944,25 +969,14 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
       if (prv_ok) {
         // replay t_{i-1} from its carry and store h (and the checkpoint)
         const Tile t = tile_of(t_prv, wave);
-        // the prefix of the earlier waves' maps does not need the carry
+        // the composite of the earlier waves' maps, from the control waves
         float PA[V], PB[V];
-        bool PR = false;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-          PA[j] = 1.0f;
-          PB[j] = 0.0f;
+          PA[j] = s_PA[pb][wave][lane * V + j];
+          PB[j] = s_PB[pb][wave][lane * V + j];
         }
-        for (int w = 0; w < wave; ++w) {
-          const bool Rw = s_R[pb][w] != 0u;
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            const float Aw = s_A[pb][w][lane * V + j];
-            const float Bw = s_B[pb][w][lane * V + j];
-            PB[j] = Rw ? Bw : fmaf(Aw, PB[j], Bw);
-            PA[j] *= Aw;
-          }
-          PR = PR || Rw;
-        }
+        const bool PR = s_PR[pb][wave] != 0u;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
           lds_flag_wait(&s_carry_ready[j], i);
@@ -977,18 +991,25 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
           }
           const unsigned rmask = s_rmask[pb][wave];
           elem* hb = static_cast<elem*>(p.h) + (t.rowbase + t.t0) * W + static_cast<long long>(t.strip) * SW;
-#pragma unroll
-          for (int k = 0; k < TS; ++k) {
-            if (k < t.nvalid) {
+          // FULL: every step in range and no reset token, so no selects
+          auto replay_step = [&](int k, bool FULL) {
+            if (FULL || k < t.nvalid) {
               const long long tk = t.t0 + k;
               if (p.ckpt != nullptr && ((wave * TS + k) % kCkpt) == 0) {
                 store_f32v<V>(p.ckpt + (static_cast<long long>(t.b) * p.n_ckpt + tk / kCkpt) * W + t.ch, hc);
               }
-              const bool rs = (rmask >> k) & 1u;
+              const bool rs = FULL ? false : ((rmask >> k) & 1u) != 0u;
 #pragma unroll
               for (int j = 0; j < V; ++j) hc[j] = rs ? pu[k][j] : fmaf(pal[k][j], hc[j], pu[k][j]);
               io::store_nt32(hb + static_cast<long long>(k) * W, static_cast<unsigned>(lane * V), io::pack(hc));
             }
+          };
+          if (rmask == 0u && t.nvalid == TS) {
+#pragma unroll
+            for (int k = 0; k < TS; ++k) replay_step(k, true);
+          } else {
+#pragma unroll
+            for (int k = 0; k < TS; ++k) replay_step(k, false);
           }
           if (p.h_last != nullptr && t.nvalid > 0 && t.t0 + t.nvalid == p.L) {
             store_f32v<V>(p.h_last + t.b * W + t.ch, hc);
