@@ -275,128 +275,6 @@ struct Header {
   unsigned err;    // sticky error bits
 };
 
-// LDS of the windowed look-back: one predecessor per wave and round.
-template <int V, int NW>
-struct LookSmem {
-  float a[NW][64 * V];
-  float b[NW][64 * V];
-  float h[NW][64 * V];
-  unsigned char st[NW][64];   // bit 0: map ready, bit 1: carry ready, bit 2: map has a reset
-  int done[64];
-  int pending;
-};
-
-// Carry entering a tile (valid in wave 0 on return). Called by every thread
-// of the workgroup. In each round wave w polls the predecessor at distance
-// w + 1 (tiles of earlier chunks of the same row in the forward, of later
-// chunks in the backward), so one memory round trip covers NW predecessors.
-// Wave 0 then looks for the nearest predecessor whose outgoing carry is
-// known (published, or fixed by a reset inside it) with every map between
-// published, and applies those maps oldest first with the very fma the
-// predecessors use for their own outgoing carries. The carry is therefore
-// bit-identical to the serial chain whatever the timing: results are
-// deterministic run to run.
-// `self` is the slot index of this lane's first channel in this tile,
-// `stride` the slot distance between consecutive predecessors, `npred` how
-// many exist, `init` the carry before the first chunk.
-template <int V, int NW>
-__device__ __forceinline__ void look_back(LookSmem<V, NW>& sm, const u64* slot_a, const u64* slot_b,
-                                          const u64* slot_h, long long self, long long stride, int npred,
-                                          unsigned tag, bool active, int wave, int lane,
-                                          const float (&init)[V], float (&carry)[V], unsigned* err) {
-  bool done = !active;
-#pragma unroll
-  for (int j = 0; j < V; ++j) carry[j] = 0.0f;
-  if (wave == 0) sm.done[lane] = done ? 1 : 0;
-  __syncthreads();
-  for (unsigned round = 0;; ++round) {
-    unsigned char st = 0;
-    if (sm.done[lane] == 0 && wave < npred) {
-      const long long q = self - static_cast<long long>(wave + 1) * stride;
-      u64 wh[V];
-      bool ok = true;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        wh[j] = poll(slot_h, q + j);
-        ok = ok && tagged(wh[j], tag);
-      }
-      if (ok) {
-        st = 2;
-#pragma unroll
-        for (int j = 0; j < V; ++j) sm.h[wave][lane * V + j] = __uint_as_float(static_cast<uint32_t>(wh[j]));
-      } else {
-        u64 wa[V], wb[V];
-        ok = true;
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          wa[j] = poll(slot_a, q + j);
-          wb[j] = poll(slot_b, q + j);
-          ok = ok && tagged(wa[j], tag) && tagged(wb[j], tag);
-        }
-        if (ok) {
-          st = ((static_cast<uint32_t>(wa[0]) >> 31) != 0) ? 5 : 1;
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            sm.a[wave][lane * V + j] = __uint_as_float(static_cast<uint32_t>(wa[j]) & 0x7FFFFFFFu);
-            sm.b[wave][lane * V + j] = __uint_as_float(static_cast<uint32_t>(wb[j]));
-          }
-        }
-      }
-    }
-    sm.st[wave][lane] = st;
-    __syncthreads();
-    if (wave == 0) {
-      if (!done) {
-        // nearest resolvable start: a published carry, a reset map, or the sequence start
-        int start = -1;
-        int kind = 0;   // 1: published carry, 2: reset map, 3: initial carry
-        for (int w = 0; w < NW; ++w) {
-          if (w >= npred) {
-            start = w;
-            kind = 3;
-            break;
-          }
-          const unsigned char sw = sm.st[w][lane];
-          if (sw & 2) {
-            start = w;
-            kind = 1;
-            break;
-          }
-          if ((sw & 1) == 0) break;
-          if (sw & 4) {
-            start = w;
-            kind = 2;
-            break;
-          }
-        }
-        if (start >= 0) {
-          float hv[V];
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            hv[j] = kind == 1 ? sm.h[start][lane * V + j] : (kind == 2 ? sm.b[start][lane * V + j] : init[j]);
-          }
-          for (int w = start - 1; w >= 0; --w) {
-#pragma unroll
-            for (int j = 0; j < V; ++j) hv[j] = fmaf(sm.a[w][lane * V + j], hv[j], sm.b[w][lane * V + j]);
-          }
-#pragma unroll
-          for (int j = 0; j < V; ++j) carry[j] = hv[j];
-          done = true;
-        } else if (round >= kSpinLimit) {
-          atomicOr(err, 1u);
-          done = true;
-        }
-        sm.done[lane] = done ? 1 : 0;
-      }
-      const bool any = __ballot(!done) != 0ull;
-      if (lane == 0) sm.pending = any ? 1 : 0;
-    }
-    __syncthreads();
-    if (sm.pending == 0) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
 // Carry entering a tile, computed by one wave (the workgroup's control
 // wave). Each round polls the published words of the K nearest predecessors
 // (tiles of earlier chunks of the same row in the forward, later chunks in the
@@ -483,28 +361,6 @@ __device__ __forceinline__ bool look_back_wave(const u64* slot_a, const u64* slo
 #pragma unroll
   for (int j = 0; j < V; ++j) carry[j] = 0.0f;
   return false;
-}
-
-// Called once per workgroup at its end: the last one re-arms the ticket
-// counter and advances the call counter (and with it the slot tag).
-__device__ __forceinline__ void finish_call(Header* hdr, unsigned n_tiles) {
-  const unsigned prev = atomicAdd(&hdr->done, 1u);
-  if (prev == n_tiles - 1) {
-    atomicExch(&hdr->done, 0u);
-    atomicAdd(&hdr->counter, (1ull << 32) - static_cast<u64>(n_tiles));
-  }
-}
-
-// Ticket of this workgroup: (tile index, slot tag), wave-uniform.
-__device__ __forceinline__ void take_ticket(Header* hdr, unsigned* s_ticket, unsigned& tile, unsigned& tag) {
-  if (threadIdx.x == 0) {
-    const u64 v = atomicAdd(&hdr->counter, 1ull);
-    s_ticket[0] = static_cast<unsigned>(v);
-    s_ticket[1] = static_cast<unsigned>(v >> 32) + 1u;
-  }
-  __syncthreads();
-  tile = __builtin_amdgcn_readfirstlane(s_ticket[0]);
-  tag = __builtin_amdgcn_readfirstlane(s_ticket[1]);
 }
 
 // ------------------------------------------------------------------ forward
@@ -1040,6 +896,25 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
 }
 
 // ------------------------------------------------------------------ backward
+//
+// The reverse recurrence g_t = dh_t + alpha_{t+1} g_{t+1} needs only the
+// decays and dh, not x or gate_x, so the backward runs as three launches:
+//   bwd_map_kernel   : each tile's reverse map G_out = A*G_in + B (carry
+//                      entering its first step from the carry entering its
+//                      last), from gate_a, lambda, the reset flags and dh;
+//   bwd_carry_kernel : one thread per (batch row, channel) composes the maps
+//                      from the last chunk backwards and stores the carry
+//                      entering every tile;
+//   bwd_main_kernel  : every tile independently recomputes the forward from
+//                      its checkpoints, runs the reverse pass from its carry
+//                      and writes dx, dgate_x, dgate_a and its lambda-gradient
+//                      partial;
+//   bwd_dlam_kernel  : sums each channel's partials over (chunk, batch row)
+//                      in a fixed order.
+// No workgroup waits for another, so the main pass streams at full occupancy.
+// The maps, carries and partials are stored as 64-bit slot words whose high
+// half is 0, a tag the forward never uses, so a forward sharing the workspace
+// never mistakes them for its own published words.
 
 struct BwdArgs {
   const void* x;
@@ -1056,10 +931,10 @@ struct BwdArgs {
   float* dlam;
   float* dh0;
   Header* hdr;
-  u64* slot_a;
-  u64* slot_b;
-  u64* slot_h;
-  u64* slot_p;       // per-tile lambda-gradient partials
+  u64* map_a;            // per tile and channel: A of the reverse map (a reset in the sign bit)
+  u64* map_b;            // B of the reverse map
+  u64* carry;            // carry entering the tile's last step from the later chunks
+  u64* part;             // the tile's lambda-gradient partial
   long long L;
   long long n_ckpt;
   int B;
@@ -1070,74 +945,294 @@ struct BwdArgs {
   float c;
 };
 
-// Every wave covers exactly one checkpoint interval, whose entering carry the
-// forward stored. Tiles are handed out from the last chunk backwards.
-template <typename IO, int V, int NW, int WPE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
-void bwd_kernel(BwdArgs p) {
+__device__ __forceinline__ u64 untagged(float v) { return static_cast<u64>(__float_as_uint(v)); }
+__device__ __forceinline__ float word_value(u64 w) { return __uint_as_float(static_cast<uint32_t>(w)); }
+
+// Geometry of a backward tile: chunk-major tile index, TS = 8 steps per wave
+// (one checkpoint interval), NW waves, 64*V channels.
+struct BwdTile {
+  int chunk, b, strip, ch, nvalid;
+  long long t0, rowbase;
+  bool active;
+};
+template <int V, int NW>
+__device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& p, unsigned tile, int wave, int lane) {
+  const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
+  BwdTile t;
+  t.chunk = static_cast<int>(tile / rows);
+  const int row = static_cast<int>(tile - static_cast<unsigned>(t.chunk) * rows);
+  t.b = row / p.n_strips;
+  t.strip = row - t.b * p.n_strips;
+  t.ch = t.strip * 64 * V + lane * V;
+  t.active = t.ch < p.W;
+  t.t0 = static_cast<long long>(t.chunk) * (kCkpt * NW) + static_cast<long long>(wave) * kCkpt;
+  const long long rem = p.L - t.t0;
+  t.nvalid = rem <= 0 ? 0 : (rem >= kCkpt ? kCkpt : static_cast<int>(rem));
+  t.rowbase = static_cast<long long>(t.b) * p.L;
+  return t;
+}
+
+template <int NW>
+__device__ __forceinline__ unsigned reset_mask(const BwdArgs& p, long long rowbase, long long t0, int nvalid,
+                                               int lane) {
+  if (p.reset == nullptr) return 0u;
+  const bool f = lane < nvalid && p.reset[rowbase + t0 + lane] != 0;
+  return static_cast<unsigned>(__ballot(f));
+}
+
+// Reverse maps of all tiles. Workgroup (row, y) covers chunks
+// y*CPB .. y*CPB+CPB-1 of one row, so the decay constants are evaluated once.
+template <typename IO, int V, int NW, int CPB>
+__global__ __launch_bounds__(NW * 64) void bwd_map_kernel(BwdArgs p) {
   constexpr int TS = kCkpt;
   constexpr int SW = 64 * V;
-  constexpr int T = TS * NW;
   using io = Io<IO, V>;
   using R_t = typename io::R;
-
-  __shared__ unsigned s_ticket[2];
   __shared__ float s_A[NW][SW];
   __shared__ float s_B[NW][SW];
   __shared__ unsigned s_R[NW];
-  __shared__ float s_carry[SW];
-  __shared__ LookSmem<V, NW> s_look;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  unsigned tile, tag;
-  take_ticket(p.hdr, s_ticket, tile, tag);
   const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
-  const int crev = static_cast<int>(tile / rows);          // 0 = last chunk in time
-  const int row = static_cast<int>(tile - static_cast<unsigned>(crev) * rows);
-  const int chunk = p.n_chunks - 1 - crev;
-  const int b = row / p.n_strips;
-  const int strip = row - b * p.n_strips;
-  const int ch = strip * SW + lane * V;
-  const bool active = ch < p.W;
-  const long long t0 = static_cast<long long>(chunk) * T + static_cast<long long>(wave) * TS;
-  const long long rem = p.L - t0;
-  const int nvalid = rem <= 0 ? 0 : (rem >= TS ? TS : static_cast<int>(rem));
-  const long long rowbase = static_cast<long long>(b) * p.L;
   const long long W = p.W;
-
-  unsigned rmask = 0;
-  if (p.reset != nullptr) {
-    const bool f = lane < nvalid && p.reset[rowbase + t0 + lane] != 0;
-    rmask = static_cast<unsigned>(__ballot(f));
-  }
-
-  R_t rx[TS], rgx[TS], rga[TS], rdh[TS];
-#pragma unroll
-  for (int k = 0; k < TS; ++k) {
-    if (active && k < nvalid) {
-      const long long off = (rowbase + t0 + k) * W + ch;
-      rx[k] = io::load(p.x, off);
-      rgx[k] = io::load(p.gx, off);
-      rga[k] = io::load(p.ga, off);
-      rdh[k] = io::load(p.dh, off);
-    } else {
-      rx[k] = R_t{};
-      rgx[k] = R_t{};
-      rga[k] = R_t{};
-      rdh[k] = R_t{};
-    }
-  }
-  float h[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) h[j] = 0.0f;
-  if (active && nvalid > 0) load_f32v<V>(p.ckpt + (static_cast<long long>(b) * p.n_ckpt + t0 / kCkpt) * W + ch, h);
+  const int c_begin = blockIdx.y * CPB;
+  const int c_end = c_begin + CPB < p.n_chunks ? c_begin + CPB : p.n_chunks;
+  const BwdTile t0 = bwd_tile<V, NW>(p, static_cast<unsigned>(c_begin) * rows + blockIdx.x, wave, lane);
   float cs[V], k2[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     cs[j] = 0.0f;
     k2[j] = 0.0f;
-    if (active) channel_consts(p.lam[ch + j], p.c, cs[j], k2[j]);
+    if (t0.active) channel_consts(p.lam[t0.ch + j], p.c, cs[j], k2[j]);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const unsigned tile = static_cast<unsigned>(c) * rows + blockIdx.x;
+    const BwdTile t = bwd_tile<V, NW>(p, tile, wave, lane);
+    const unsigned rmask = reset_mask<NW>(p, t.rowbase, t.t0, t.nvalid, lane);
+    R_t rga[TS], rdh[TS];
+#pragma unroll
+    for (int k = 0; k < TS; ++k) {
+      rga[k] = R_t{};
+      rdh[k] = R_t{};
+      if (t.active && k < t.nvalid) {
+        const long long off = (t.rowbase + t.t0 + k) * W + t.ch;
+        rga[k] = io::load_nt(p.ga, off);
+        rdh[k] = io::load_nt(p.dh, off);
+      }
+    }
+    float A[V], Bv[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      A[j] = 1.0f;
+      Bv[j] = 0.0f;
+    }
+#pragma unroll
+    for (int k = TS - 1; k >= 0; --k) {
+      if (k < t.nvalid) {
+        const bool rs = (rmask >> k) & 1u;
+        float gav[V], dhv[V];
+        io::unpack(rga[k], gav);
+        io::unpack(rdh[k], dhv);
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const float a = __builtin_amdgcn_exp2f(k2[j] * sigmoid_f(gav[j]));
+          const float gB = Bv[j] + dhv[j];
+          Bv[j] = rs ? 0.0f : a * gB;
+          A[j] = rs ? 0.0f : a * A[j];
+        }
+      }
+    }
+    __syncthreads();   // the previous chunk's maps have been combined
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      s_A[wave][lane * V + j] = A[j];
+      s_B[wave][lane * V + j] = Bv[j];
+    }
+    if (lane == 0) s_R[wave] = rmask != 0u ? 1u : 0u;
+    __syncthreads();
+    if (wave == 0 && t.active) {
+      float GA[V], GB[V];
+      bool GR = false;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        GA[j] = 1.0f;
+        GB[j] = 0.0f;
+      }
+#pragma unroll
+      for (int w = NW - 1; w >= 0; --w) {
+        const bool Rw = s_R[w] != 0u;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const float Aw = s_A[w][lane * V + j];
+          const float Bw = s_B[w][lane * V + j];
+          GB[j] = Rw ? Bw : fmaf(Aw, GB[j], Bw);
+          GA[j] *= Aw;
+        }
+        GR = GR || Rw;
+      }
+      const size_t idx = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        p.map_a[idx + j] = static_cast<u64>(encode_a(GA[j], GR));
+        p.map_b[idx + j] = untagged(GB[j]);
+      }
+    }
+  }
+}
+
+// Carry entering every tile. Workgroup: 64 channels of one batch row, NWC
+// waves each covering a contiguous run of chunks. Each wave composes its
+// run's maps, the runs are combined from the last backwards through LDS, and
+// each wave then walks its run again from the carry entering it, storing the
+// carry entering every tile.
+template <int V>
+__global__ __launch_bounds__(1024) void bwd_carry_kernel(BwdArgs p) {
+  constexpr int SW = 64 * V;
+  constexpr int NWC = 16;
+  constexpr int U = 8;
+  __shared__ float s_a[NWC][64];
+  __shared__ float s_b[NWC][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int groups = (p.W + 63) / 64;
+  const int b = blockIdx.x / groups;
+  const int ch = (blockIdx.x - b * groups) * 64 + lane;
+  const bool active = ch < p.W;
+  const int strip = ch / SW;
+  const int cin = ch - strip * SW;
+  const size_t rows = static_cast<size_t>(p.B) * static_cast<size_t>(p.n_strips);
+  const size_t row = static_cast<size_t>(b) * p.n_strips + strip;
+  const int per = (p.n_chunks + NWC - 1) / NWC;
+  const int c_lo = wave * per;                                   // run: chunks [c_lo, c_hi)
+  const int c_hi = c_lo + per < p.n_chunks ? c_lo + per : p.n_chunks;
+  auto idx_of = [=](int c) { return (static_cast<size_t>(c) * rows + row) * SW + cin; };
+  // pass 1: the run's composite map, latest chunk first
+  float RA = 1.0f, RB = 0.0f;
+  bool RR = false;
+  for (int c0 = c_hi - 1; c0 >= c_lo; c0 -= U) {
+    u64 wa[U], wb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 - u;
+      const bool ok = active && c >= c_lo;
+      wa[u] = ok ? p.map_a[idx_of(c)] : 0ull;
+      wb[u] = ok ? p.map_b[idx_of(c)] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 - u >= c_lo) {
+        const uint32_t a = static_cast<uint32_t>(wa[u]);
+        const float Am = __uint_as_float(a & 0x7FFFFFFFu);
+        const float Bm = word_value(wb[u]);
+        const bool Rm = (a >> 31) != 0;
+        RB = Rm ? Bm : fmaf(Am, RB, Bm);
+        RA *= Am;
+        RR = RR || Rm;
+      }
+    }
+  }
+  // A >= 0, so a reset inside the run is kept in the sign of A
+  s_a[wave][lane] = RR ? -0.0f : RA;
+  s_b[wave][lane] = RB;
+  __syncthreads();
+  // carry entering this run: dh_last through the later runs, latest first
+  float G = (active && p.dh_last != nullptr) ? p.dh_last[static_cast<long long>(b) * p.W + ch] : 0.0f;
+  for (int w = NWC - 1; w > wave; --w) {
+    const float Am = s_a[w][lane];
+    const float Bm = s_b[w][lane];
+    G = signbit(Am) ? Bm : fmaf(Am, G, Bm);
+  }
+  // pass 2: store the carry entering each tile of the run
+  for (int c0 = c_hi - 1; c0 >= c_lo; c0 -= U) {
+    u64 wa[U], wb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 - u;
+      const bool ok = active && c >= c_lo;
+      wa[u] = ok ? p.map_a[idx_of(c)] : 0ull;
+      wb[u] = ok ? p.map_b[idx_of(c)] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 - u;
+      if (active && c >= c_lo) {
+        p.carry[idx_of(c)] = untagged(G);
+        const uint32_t a = static_cast<uint32_t>(wa[u]);
+        const float Bm = word_value(wb[u]);
+        G = (a >> 31) != 0 ? Bm : fmaf(__uint_as_float(a & 0x7FFFFFFFu), G, Bm);
+      }
+    }
+  }
+}
+
+// Every wave covers exactly one checkpoint interval, whose entering state the
+// forward stored; the tile's carry comes from bwd_carry_kernel. Workgroup
+// (row, y) covers chunks y*CPB .. y*CPB+CPB-1 of one row, so the decay
+// constants are evaluated once.
+template <typename IO, int V, int NW, int WPE, int CPB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void bwd_main_kernel(BwdArgs p) {
+  constexpr int TS = kCkpt;
+  constexpr int SW = 64 * V;
+  using io = Io<IO, V>;
+  using R_t = typename io::R;
+
+  __shared__ float s_A[NW][SW];
+  __shared__ float s_B[NW][SW];
+  __shared__ unsigned s_R[NW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
+  const long long W = p.W;
+  const int c_begin = blockIdx.y * CPB;
+  const int c_end = c_begin + CPB < p.n_chunks ? c_begin + CPB : p.n_chunks;
+  float cs[V], k2[V];
+  {
+    const BwdTile t0 = bwd_tile<V, NW>(p, static_cast<unsigned>(c_begin) * rows + blockIdx.x, wave, lane);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      cs[j] = 0.0f;
+      k2[j] = 0.0f;
+      if (t0.active) channel_consts(p.lam[t0.ch + j], p.c, cs[j], k2[j]);
+    }
+  }
+  for (int chunk = c_begin; chunk < c_end; ++chunk) {
+  const unsigned tile = static_cast<unsigned>(chunk) * rows + blockIdx.x;
+  const BwdTile t = bwd_tile<V, NW>(p, tile, wave, lane);
+  const bool active = t.active;
+  const int nvalid = t.nvalid;
+  const unsigned rmask = reset_mask<NW>(p, t.rowbase, t.t0, nvalid, lane);
+  const size_t idx = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
+
+  R_t rx[TS], rgx[TS], rga[TS], rdh[TS];
+#pragma unroll
+  for (int k = 0; k < TS; ++k) {
+    rx[k] = R_t{};
+    rgx[k] = R_t{};
+    rga[k] = R_t{};
+    rdh[k] = R_t{};
+    if (active && k < nvalid) {
+      const long long off = (t.rowbase + t.t0 + k) * W + t.ch;
+      rx[k] = io::load_nt(p.x, off);
+      rgx[k] = io::load_nt(p.gx, off);
+      rga[k] = io::load_nt(p.ga, off);
+      rdh[k] = io::load_nt(p.dh, off);
+    }
+  }
+  float h[V], cin[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    h[j] = 0.0f;
+    cin[j] = 0.0f;
+  }
+  if (active && nvalid > 0) {
+    load_f32v<V>(p.ckpt + (static_cast<long long>(t.b) * p.n_ckpt + t.t0 / kCkpt) * W + t.ch, h);
+  }
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) cin[j] = word_value(p.carry[idx + j]);
   }
 
   // Recompute the forward through this wave's steps and turn every step into
@@ -1177,7 +1272,7 @@ void bwd_kernel(BwdArgs p) {
     }
   }
 
-  // this wave's reverse map G_in -> G_out (G_out = carry handed to the step before the wave)
+  // this wave's reverse map G_in -> G_out
   float A[V], Bv[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
@@ -1196,6 +1291,7 @@ void bwd_kernel(BwdArgs p) {
       }
     }
   }
+  __syncthreads();   // the previous chunk's partials have been summed
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     s_A[wave][lane * V + j] = A[j];
@@ -1204,65 +1300,14 @@ void bwd_kernel(BwdArgs p) {
   if (lane == 0) s_R[wave] = rmask != 0u ? 1u : 0u;
   __syncthreads();
 
-  float GA[V], GB[V];
-  bool GR = false;
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    GA[j] = 1.0f;
-    GB[j] = 0.0f;
-  }
-#pragma unroll
-  for (int w = NW - 1; w >= 0; --w) {
-    const bool Rw = s_R[w] != 0u;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const float Aw = s_A[w][lane * V + j];
-      const float Bw = s_B[w][lane * V + j];
-      GB[j] = Rw ? Bw : fmaf(Aw, GB[j], Bw);
-      GA[j] *= Aw;
-    }
-    GR = GR || Rw;
-  }
-  const size_t sbase = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
-  const bool has_succ = crev < p.n_chunks - 1;
-  float init[V], carry[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) init[j] = (active && p.dh_last != nullptr) ? p.dh_last[b * W + ch + j] : 0.0f;
-  if (crev == 0) {
-#pragma unroll
-    for (int j = 0; j < V; ++j) carry[j] = init[j];
-  } else {
-    if (wave == 0 && active && has_succ) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        publish(p.slot_a, sbase + j, tag, encode_a(GA[j], GR));
-        publish(p.slot_b, sbase + j, tag, __float_as_uint(GB[j]));
-      }
-    }
-    look_back<V, NW>(s_look, p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(sbase),
-                     static_cast<long long>(rows) * SW, crev, tag, active, wave, lane, init, carry,
-                     &p.hdr->err);
-  }
-  if (wave == 0 && active) {
-    if (has_succ) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const float gout = GR ? GB[j] : fmaf(GA[j], carry[j], GB[j]);
-        publish(p.slot_h, sbase + j, tag, __float_as_uint(gout));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < V; ++j) s_carry[lane * V + j] = carry[j];
-  }
-  __syncthreads();
-
   float dl_acc[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) dl_acc[j] = 0.0f;
   if (active) {
+    // carry at this wave's last step: the tile's carry through the later waves
     float G[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) G[j] = s_carry[lane * V + j];
+    for (int j = 0; j < V; ++j) G[j] = cin[j];
     for (int w = NW - 1; w > wave; --w) {
       const bool Rw = s_R[w] != 0u;
 #pragma unroll
@@ -1284,16 +1329,16 @@ void bwd_kernel(BwdArgs p) {
           dl_acc[j] = fmaf(g, cl[k][j], dl_acc[j]);
           G[j] = rs ? 0.0f : al[k][j] * g;
         }
-        const long long off = (rowbase + t0 + k) * W + ch;
-        io::store(p.dx, off, io::pack(ox));
-        io::store(p.dgx, off, io::pack(ogx));
-        io::store(p.dga, off, io::pack(oga));
+        const long long off = (t.rowbase + t.t0 + k) * W + t.ch;
+        io::store_nt(p.dx, off, io::pack(ox));
+        io::store_nt(p.dgx, off, io::pack(ogx));
+        io::store_nt(p.dga, off, io::pack(oga));
       }
     }
-    if (chunk == 0 && wave == 0 && p.dh0 != nullptr) store_f32v<V>(p.dh0 + b * W + ch, G);
+    if (t.chunk == 0 && wave == 0 && p.dh0 != nullptr) store_f32v<V>(p.dh0 + t.b * W + t.ch, G);
   }
 
-  // the tile's lambda-gradient partial: fixed-order sum over the waves, published tagged
+  // the tile's lambda-gradient partial: fixed-order sum over the waves
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < V; ++j) s_A[wave][lane * V + j] = dl_acc[j];
@@ -1303,66 +1348,56 @@ void bwd_kernel(BwdArgs p) {
     for (int j = 0; j < V; ++j) {
       float s = 0.0f;
       for (int w = 0; w < NW; ++w) s += s_A[w][lane * V + j];
-      publish(p.slot_p, sbase + j, tag, __float_as_uint(s));
+      p.part[idx + j] = untagged(s);
     }
   }
+  }   // chunks
 
-  // The tile with the largest ticket of its channel strip (chunk 0, last
-  // batch row) sums the strip's partials in a fixed order: waves take
-  // contiguous runs of (chunk, batch) pairs, then wave 0 adds the runs in
-  // wave order. Every partial it waits for belongs to a smaller ticket.
-  if (crev == p.n_chunks - 1 && b == p.B - 1) {
-    const int n_parts = p.n_chunks * p.B;
-    const int per = (n_parts + NW - 1) / NW;
-    const int k0 = wave * per;
-    const int k1 = k0 + per < n_parts ? k0 + per : n_parts;
-    float s[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) s[j] = 0.0f;
-    bool failed = false;
-    if (active) {
-      for (int k = k0; k < k1; ++k) {
-        const int cr = k / p.B;
-        const int bb = k - cr * p.B;
-        const long long q = (static_cast<long long>(cr) * rows + static_cast<long long>(bb) * p.n_strips + strip) * SW +
-                            static_cast<long long>(lane) * V;
-        u64 wv[V];
-        unsigned spins = 0;
-        while (true) {
-          bool ok = true;
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            wv[j] = poll(p.slot_p, q + j);
-            ok = ok && tagged(wv[j], tag);
-          }
-          if (ok) break;
-          if (++spins > kSpinLimit) {
-            failed = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-#pragma unroll
-        for (int j = 0; j < V; ++j) s[j] += __uint_as_float(static_cast<uint32_t>(wv[j]));
-      }
-    }
-    if (failed) atomicOr(&p.hdr->err, 1u);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < V; ++j) s_A[wave][lane * V + j] = s[j];
-    __syncthreads();
-    if (wave == 0 && active) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        float tot = 0.0f;
-        for (int w = 0; w < NW; ++w) tot += s_A[w][lane * V + j];
-        const float lm = p.lam[ch + j];
-        const float sig = 1.0f / (1.0f + expf(-lm));
-        p.dlam[ch + j] = -p.c * sig * tot;
-      }
+  // the last workgroup of the call advances the call counter
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(&p.hdr->done, 1u);
+    if (prev == gridDim.x * gridDim.y - 1) {
+      atomicExch(&p.hdr->done, 0u);
+      atomicAdd(&p.hdr->counter, 1ull << 32);
     }
   }
-  if (threadIdx.x == 0) finish_call(p.hdr, p.n_tiles);
+}
+
+// Lambda gradient: 64 channels per workgroup, NWR waves each summing a
+// contiguous run of (chunk, batch row) partials, then the runs in wave order.
+template <int V>
+__global__ __launch_bounds__(1024) void bwd_dlam_kernel(BwdArgs p) {
+  constexpr int SW = 64 * V;
+  constexpr int NWR = 16;
+  __shared__ float s_sum[NWR][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ch = blockIdx.x * 64 + lane;
+  const bool active = ch < p.W;
+  const int strip = ch / SW;
+  const int cin = ch - strip * SW;
+  const int n_parts = p.n_chunks * p.B;
+  const int per = (n_parts + NWR - 1) / NWR;
+  const int k0 = wave * per;
+  const int k1 = k0 + per < n_parts ? k0 + per : n_parts;
+  float s = 0.0f;
+  if (active) {
+#pragma unroll 8
+    for (int k = k0; k < k1; ++k) {
+      // k = chunk * B + b: tile (chunk, b, strip)
+      const size_t q = (static_cast<size_t>(k) * p.n_strips + strip) * SW + cin;
+      s += word_value(p.part[q]);
+    }
+  }
+  s_sum[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && active) {
+    float tot = 0.0f;
+    for (int w = 0; w < NWR; ++w) tot += s_sum[w][lane];
+    const float lm = p.lam[ch];
+    const float sig = 1.0f / (1.0f + expf(-lm));
+    p.dlam[ch] = -p.c * sig * tot;
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -1397,9 +1432,11 @@ bool shape_ok(const rglru_shape_t* s) {
 Geometry geometry(const rglru_shape_t* s) {
   Geometry g;
   g.io_bytes = s->io_dtype == RGLRU_IO_F32 ? 4 : 2;
-  g.Tb = s->chunk == 0 ? 64 : (s->chunk > 128 ? 128 : s->chunk);
-  // the forward keeps the (alpha, write) pairs of two tiles in registers: at most 64 steps
-  g.T = g.Tb > 64 ? 64 : g.Tb;
+  const int req = s->chunk == 0 ? 64 : s->chunk;
+  // the forward keeps the (alpha, write) pairs of two tiles in registers: at
+  // most 64 steps; the backward keeps six coefficients per step: at most 32
+  g.T = req > 64 ? 64 : req;
+  g.Tb = req > 32 ? 32 : req;
   g.n_ckpt = ceil_div(s->length, kCkpt);
   g.n_chunks_f = static_cast<int>(ceil_div(s->length, g.T));
   g.n_chunks_b = static_cast<int>(ceil_div(s->length, g.Tb));
@@ -1412,7 +1449,7 @@ size_t slot_words(const rglru_shape_t* s, int n_chunks) {
          round_up(static_cast<size_t>(s->width), kMaxStrip);
 }
 
-constexpr int kSlotKinds = 4;   // map A, map B, carry, lambda-gradient partial
+constexpr int kSlotKinds = 4;   // forward: map A, map B, carry; backward: map A, map B, carry, partial
 
 size_t ws_bytes(const rglru_shape_t* s, int n_chunks) {
   return kHeaderBytes + kSlotKinds * round_up(slot_words(s, n_chunks) * 8, 256);
@@ -1455,8 +1492,6 @@ int pick_vec(int vmax, long long W, int io_bytes, std::initializer_list<const vo
   return 1;
 }
 
-// waves per SIMD the register budget is fitted to: two workgroups per CU
-constexpr int wpe_for(int nw) { return nw >= 16 ? 4 : (nw >= 2 ? nw / 2 : 1); }
 
 // Number of workgroups of a persistent kernel: as many as fit on the device at once.
 template <typename Kern>
@@ -1514,10 +1549,25 @@ rglru_status_t dispatch_fwd(int T, int V, bool wide, FwdArgs a, hipStream_t stre
 
 template <typename IO, int V, int NW>
 rglru_status_t launch_bwd(BwdArgs a, hipStream_t stream) {
+  constexpr int CPB = 4;   // chunks per workgroup in the map and main passes
   a.n_strips = static_cast<int>(ceil_div(a.W, 64 * V));
   a.n_chunks = static_cast<int>(ceil_div(a.L, kCkpt * NW));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  hipLaunchKernelGGL((bwd_kernel<IO, V, NW, wpe_for(NW)>), dim3(a.n_tiles), dim3(NW * 64), 0, stream, a);
+  const dim3 tiles_grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips),
+                        static_cast<unsigned>(ceil_div(a.n_chunks, CPB)));
+  hipLaunchKernelGGL((bwd_map_kernel<IO, V, NW, CPB>), tiles_grid, dim3(NW * 64), 0, stream, a);
+  rglru_status_t st = launch_status();
+  if (st != RGLRU_OK) return st;
+  const unsigned groups = static_cast<unsigned>(ceil_div(a.W, 64)) * static_cast<unsigned>(a.B);
+  hipLaunchKernelGGL((bwd_carry_kernel<V>), dim3(groups), dim3(1024), 0, stream, a);
+  st = launch_status();
+  if (st != RGLRU_OK) return st;
+  // three waves per SIMD: room for the per-step coefficients without spills
+  hipLaunchKernelGGL((bwd_main_kernel<IO, V, NW, 3, CPB>), tiles_grid, dim3(NW * 64), 0, stream, a);
+  st = launch_status();
+  if (st != RGLRU_OK) return st;
+  hipLaunchKernelGGL((bwd_dlam_kernel<V>), dim3(static_cast<unsigned>(ceil_div(a.W, 64))), dim3(1024), 0,
+                     stream, a);
   return launch_status();
 }
 
@@ -1527,8 +1577,6 @@ rglru_status_t dispatch_bwd_chunk(int Tb, BwdArgs a, hipStream_t stream) {
     case 8: return launch_bwd<IO, V, 1>(a, stream);
     case 16: return launch_bwd<IO, V, 2>(a, stream);
     case 32: return launch_bwd<IO, V, 4>(a, stream);
-    case 64: return launch_bwd<IO, V, 8>(a, stream);
-    case 128: return launch_bwd<IO, V, 16>(a, stream);
     default: break;
   }
   return RGLRU_ERR_UNSUPPORTED;
@@ -1646,10 +1694,10 @@ rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate
   a.dlam = dlambda;
   a.dh0 = dh0;
   a.hdr = sl.hdr;
-  a.slot_a = sl.a;
-  a.slot_b = sl.b;
-  a.slot_h = sl.h;
-  a.slot_p = sl.p;
+  a.map_a = sl.a;
+  a.map_b = sl.b;
+  a.carry = sl.h;
+  a.part = sl.p;
   a.L = s->length;
   a.n_ckpt = g.n_ckpt;
   a.B = static_cast<int>(s->batch);
