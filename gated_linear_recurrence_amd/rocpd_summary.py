@@ -1,0 +1,85 @@
+"""Summaries of rocprofv3 databases (rocpd SQLite) for this library's kernels.
+
+    python -m gated_linear_recurrence_amd.rocpd_summary kernels RUN_results.db
+        per-kernel calls and durations of a --kernel-trace run (markdown table)
+
+    python -m gated_linear_recurrence_amd.rocpd_summary traffic FETCH.db WRITE.db CALIB_MIB
+        per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of two --pmc runs,
+        each scaled by what the same counter read for the largest plain copy
+        (__amd_rocclr_copyBuffer) of CALIB_MIB MiB in the same run; prints a
+        markdown table and a JSON object of bytes per dispatch
+
+Only the standard library is used; nothing here runs on the GPU.
+"""
+from __future__ import annotations
+
+import json
+import sqlite3
+import sys
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _short(name: str) -> str:
+    s = name.replace("rglru::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    return s if len(s) <= 90 else s[:90] + "..."
+
+
+def kernels(db: str) -> str:
+    con = sqlite3.connect(db)
+    rows = con.execute("""select name, count(*), sum(duration), avg(duration), min(duration), max(duration)
+                          from kernels group by name order by sum(duration) desc""").fetchall()
+    out = ["| kernel | calls | total us | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for n, c, tot, avg, mn, mx in rows:
+        out.append(f"| `{_short(n)}` | {c} | {tot / 1e3:.1f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    return "\n".join(out)
+
+
+def _counter(db: str, counter: str):
+    con = sqlite3.connect(db)
+    rows = con.execute("""select kernel_name, count(*), avg(value) from counters_collection
+                          where counter_name = ? group by kernel_name""", (counter,)).fetchall()
+    copy_max = con.execute("""select max(value) from counters_collection
+                              where counter_name = ? and kernel_name = ?""", (counter, COPY_KERNEL)).fetchone()[0]
+    return {n: (c, v) for n, c, v in rows}, copy_max
+
+
+def traffic(fetch_db: str, write_db: str, calib_mib: float):
+    fetch, fcopy = _counter(fetch_db, "FETCH_SIZE")
+    write, wcopy = _counter(write_db, "WRITE_SIZE")
+    ref_kib = calib_mib * 1024.0
+    fscale = ref_kib / fcopy
+    wscale = ref_kib / wcopy
+    out = [f"calibration: {calib_mib:g} MiB copy read FETCH_SIZE {fcopy:.1f} KiB (scale {fscale:.4f}), "
+           f"WRITE_SIZE {wcopy:.1f} KiB (scale {wscale:.4f})", "",
+           "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
+           "|---|---|---|---|---|---|"]
+    per = {}
+    for name in sorted(set(fetch) | set(write), key=lambda n: -(fetch.get(n, (0, 0))[1] or 0)):
+        if name == COPY_KERNEL or not name.startswith("void rglru::"):
+            continue
+        fc, fv = fetch.get(name, (0, 0.0))
+        wc, wv = write.get(name, (0, 0.0))
+        rb = fv * fscale * 1024.0
+        wb = wv * wscale * 1024.0
+        per[_short(name)] = {"read_bytes": round(rb), "write_bytes": round(wb)}
+        out.append(f"| `{_short(name)}` | {fc} | {fv:.1f} | {wv:.1f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    return "\n".join(out), per
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "kernels":
+        print(kernels(argv[1]))
+    elif len(argv) >= 4 and argv[0] == "traffic":
+        table, per = traffic(argv[1], argv[2], float(argv[3]))
+        print(table)
+        print()
+        print(json.dumps(per, indent=1))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
