@@ -45,7 +45,7 @@ def test_projection_forward_small(gpu_lib, T, nb):
     assert out_err(host64(ga), ra) <= OUT_TOL["bf16"]
 
 
-@pytest.mark.parametrize("T,nb,with_dx_in", [(1, 1, True), (45, 1, False), (300, 2, True), (1000, 3, True)])
+@pytest.mark.parametrize("T,nb,with_dx_in", [(1, 1, True), (45, 1, False), (300, 2, True), (1000, 3, True), (5000, 2, False)])
 def test_projection_backward_small(gpu_lib, T, nb, with_dx_in):
     x, wx, wa, _, _, dgx, dga, dxi = _proj_inputs(T, nb)
     dx, dwx, dbx, dwa, dba = gpu_lib.rglru_blockdiag_gate_proj_bwd(
