@@ -12,11 +12,11 @@
 // B 32x16; lane l holds row/column l%16 and k = (l/16)*8 .. +7; D lane l holds
 // column l%16, rows (l/16)*4 .. +3).
 //
-// Forward and dx kernels: a workgroup (4 waves) owns one half (128 rows of
-// the MFMA M dimension) of one block for both gates, stages those weights in
-// LDS once (the forward stores them transposed so that every fragment is 16
-// contiguous bytes), and then walks token tiles of 128 (32 per wave),
-// prefetching the next tile's token fragments from HBM while it multiplies.
+// Forward and dx kernels: a workgroup of 8 waves owns one block and a
+// contiguous token range. Its weight fragments (bf16, 128 VGPRs per lane) are
+// loaded once; 32-token tiles of the token-major operands stream through a
+// ring of LDS buffers with global_load_lds, steps ahead of the multiply, and
+// each lane stores 4 consecutive output channels of one token (8 bytes).
 // dW kernel: K runs over tokens, so 32-token slabs of x and of the gate
 // gradient stream into a ring of LDS buffers (global_load_lds) and the MFMA
 // operands come out with the gfx950 transpose read; each workgroup owns one
@@ -38,12 +38,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBS = 256;          // block size (in = out = 256)
-constexpr int kHalf = 128;        // staged rows per workgroup
-constexpr int kPad = 264;         // LDS row stride in elements (528 B: conflict-free 16 B reads)
-constexpr int kWaves = 4;
-constexpr int kNT = 32;           // tokens per wave per tile
-constexpr int kTileT = kWaves * kNT;
-constexpr int kKSteps = kBS / 32;
+constexpr int kKT = 32;           // tokens per step
+constexpr int kWaves8 = 8;        // waves per workgroup of every kernel here
+constexpr uint32_t kSlabBytes = kKT * kBS * 2;   // one 32-row x 256-column bf16 slab
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -57,58 +54,180 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return f32x2_to_
 
 __device__ __forceinline__ float bf(uint16_t v) { return bf16_bits_to_f32(v); }
 
-// token fragments of one tile: [n-tile 0..1][k-step 0..7]
-struct TokFrags {
-  u32x4 f[2][kKSteps];
+// 16 bytes per lane from global memory straight into LDS (lane l writes
+// dst + 16 * l). The 16-byte form exists only on gfx950, so the host pass does
+// not see it.
+__device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#endif
+}
+
+// waits until at most N of this wave's vector-memory operations and none of
+// its LDS accesses are outstanding. gfx9 s_waitcnt layout: vmcnt[3:0] and
+// [15:14], expcnt[6:4], lgkmcnt[11:8]. Vector-memory operations (loads into
+// LDS and stores alike) retire in issue order on this architecture.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0070);
+}
+
+// wait_vm_lds<ns * S + nd * D>() for runtime ns <= NS, nd <= ND: a step
+// issues D loads and S stores per wave, and the loads of the step about to be
+// read are followed by ns steps of stores and nd steps of loads
+template <int S, int D, int NS, int ND>
+__device__ __forceinline__ void wait_ring_nd(int nd) {
+  if constexpr (ND > 0) {
+    if (nd == ND) {
+      wait_vm_lds<NS * S + ND * D>();
+      return;
+    }
+    wait_ring_nd<S, D, NS, ND - 1>(nd);
+  } else {
+    wait_vm_lds<NS * S>();
+  }
+}
+
+template <int S, int D, int NS, int ND>
+__device__ __forceinline__ void wait_ring(int ns, int nd) {
+  if constexpr (NS > 0) {
+    if (ns == NS) {
+      wait_ring_nd<S, D, NS, ND>(nd);
+      return;
+    }
+    wait_ring<S, D, NS - 1, ND>(ns, nd);
+  } else {
+    wait_ring_nd<S, D, 0, ND>(nd);
+  }
+}
+
+// LDS reads issued as inline assembly: the compiler would otherwise make each
+// of them wait for every LDS-bound global load in flight (it cannot tell
+// which ring buffer those land in). Completion is waited for with lds_wait,
+// whose operands tie the values read so that no use moves above the wait.
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 d;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(d) : "v"(addr));
+  return d;
+}
+
+__device__ __forceinline__ u32x2 lds_read8(uint32_t addr) {
+  u32x2 d;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(d) : "v"(addr));
+  return d;
+}
+
+// Transpose read ds_read_b64_tr_b16 (gfx950): in each group of 16 lanes, lane
+// i receives element (i & 3) of the 8 bytes addressed by lanes (i >> 2) + 4m,
+// m = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
+  u32x2 d;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(d) : "v"(addr));
+  return d;
+}
+
+// waits until at most N LDS operations of this wave are outstanding (they
+// complete in order; the counter holds at most 15)
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4& x, u32x4& y) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2& x, u32x2& y) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "n"(N));
+}
+
+__device__ __forceinline__ bf16x8 frag_of(u32x2 lo, u32x2 hi) {
+  return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const char lds_char;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(p)));   // generic -> LDS offset
+}
+
+// Slab layouts in LDS: 32 rows of 512 bytes; the 16-byte granules of a row
+// are permuted so that the reads of one operand fall on distinct banks.
+//   kSwz16: granule g of row r at position g ^ (r % 8)   (16-byte row reads)
+//   kSwz32: 32-byte chunk c of row r at position c ^ (r % 16), granules
+//           within a chunk in order                      (transpose reads)
+// The map is an involution: it gives the source granule of a position too.
+constexpr int kSwz16 = 0;
+constexpr int kSwz32 = 1;
+
+template <int SWZ>
+__device__ __forceinline__ int swz_gran(int g, int r) {
+  if constexpr (SWZ == kSwz16) {
+    return g ^ (r & 7);
+  } else {
+    return (((g >> 1) ^ (r & 15)) << 1) | (g & 1);
+  }
+}
+
+// A row of zeros in device memory: slab rows past the end of a token range
+// are loaded from it, so that every load instruction of a step is issued by
+// every lane (the waits count issued instructions).
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[kBS];
+
+// Piece j (rows 2j and 2j + 1, 1 KiB) of a slab whose row r is
+// src + r * ld (256 bf16): one LDS-bound load of 16 bytes per lane; rows at
+// or past `valid` read zeros.
+template <int SWZ>
+__device__ __forceinline__ void slab_piece(const uint16_t* src, long long ld, int j, int valid, uint16_t* slab,
+                                           int lane) {
+  const int r = 2 * j + (lane >> 5);
+  const uint16_t* row = r < valid ? src + r * ld : g_zero_row;
+  lds_dma16(row + swz_gran<SWZ>(lane & 31, r) * 8, slab + j * 2 * kBS);
+}
+
+// LDS byte offset, within a kSwz32 slab, of one of the two transpose reads
+// that give a lane its MFMA operand for columns col0 .. col0+15 of 8
+// consecutive rows (lane l: column col0 + l % 16, rows (l / 16) * 8 .. +7):
+// source lane s of each 16-lane group addresses row (s / 4) (+4 for the
+// second read) at columns col0 + 4 * (s % 4) .. +3.
+__device__ __forceinline__ uint32_t frag_off(int col0, int lane, int half) {
+  const int g = lane >> 4;
+  const int sl = lane & 15;
+  const int r = g * 8 + (sl >> 2) + half * 4;
+  const int chunk = col0 >> 4;
+  return static_cast<uint32_t>(r * (kBS * 2) + ((chunk ^ (r & 15)) << 5) + (sl & 3) * 8);
+}
+
+// LDS byte offset, within a kSwz16 slab, of the 16 bytes at row r, columns
+// 8 * g .. +7
+__device__ __forceinline__ uint32_t row_off16(int r, int g) {
+  return static_cast<uint32_t>(r * (kBS * 2) + (swz_gran<kSwz16>(g, r) << 4));
+}
+
+// token range of a workgroup: [tbeg, tend) and its step count
+struct Range {
+  long long tbeg;
+  long long tend;
+  int n_steps;
 };
 
-// Loads the B fragments of 32 tokens: row (token) t0 + nt*16 + l%16, columns
-// col0 + ks*32 + (l/16)*8 .. +7 of a [T, ld] bf16 matrix (zeros past T).
-__device__ __forceinline__ void load_tok_frags(TokFrags& fr, const uint16_t* m, long long ld, long long T,
-                                               long long t0, int col0, int lane) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const long long t = t0 + nt * 16 + (lane & 15);
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      if (t < T) {
-        fr.f[nt][ks] = load16(m + t * ld + col0 + ks * 32 + (lane >> 4) * 8);
-      } else {
-        fr.f[nt][ks] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
+__device__ __forceinline__ Range token_range(int idx, long long per, long long T) {
+  Range r;
+  r.tbeg = static_cast<long long>(idx) * per;
+  r.tend = r.tbeg + per < T ? r.tbeg + per : T;
+  r.n_steps = r.tend > r.tbeg ? static_cast<int>((r.tend - r.tbeg + kKT - 1) / kKT) : 0;
+  return r;
 }
 
-// acc[mt][nt] += Wst[mt-tile rows][k] * frags over the 8 k-steps. The A
-// fragments of the next k-step are read from LDS while the current one
-// multiplies; the scheduling barrier keeps the compiler from hoisting every
-// LDS read of the tile at once (which would exhaust the register file).
-__device__ __forceinline__ void mma_tile(f32x4 (&acc)[8][2], const uint16_t (*w)[kPad], const TokFrags& fr,
-                                         int lane) {
-  bf16x8 a[2][8];
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    a[0][mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(&w[mt * 16 + (lane & 15)][(lane >> 4) * 8]));
-  }
-#pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) {
-    const int c = ks & 1;
-    if (ks + 1 < kKSteps) {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        a[c ^ 1][mt] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(&w[mt * 16 + (lane & 15)][(ks + 1) * 32 + (lane >> 4) * 8]));
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      acc[mt][0] = mfma(a[c][mt], as_bf16x8(fr.f[0][ks]), acc[mt][0]);
-      acc[mt][1] = mfma(a[c][mt], as_bf16x8(fr.f[1][ks]), acc[mt][1]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
+// ---------------------------------------------------------------- forward
+//
+// gate_g[t, kb*256 + o] = b_g[o] + sum_i x[t, kb*256 + i] w_g[kb][i][o].
+// MFMA with A = w_g^T (rows o, k = i) held in registers and B = x^T (k = i,
+// columns t) from the LDS ring, so that D holds 4 consecutive outputs of one
+// token per lane. Wave w computes gate w / 4, outputs 64 * (w % 4) .. +63:
+// 4 m-tiles x 8 k-steps of weights. The weights reach registers through the
+// same LDS buffers (kSwz32 slabs of 32 input rows) and transpose reads.
+
+constexpr int kFwdBufs = 4;                   // ring of x slabs (16 KiB each)
+constexpr int kFwdDma = 2;                    // 1 KiB loads per wave per step
+constexpr int kFwdStores = 8;                 // 8-byte stores per wave per step (2 token tiles x 4 m-tiles)
 
 struct ProjFwdArgs {
   const uint16_t* x;
@@ -116,84 +235,164 @@ struct ProjFwdArgs {
   const uint16_t* bias[2];
   uint16_t* out[2];
   long long T;
+  long long per;   // tokens per range (a multiple of kKT)
   int Wd;
-  int splits;
+  int nb;
+  int ranges;
 };
 
-__global__ __launch_bounds__(256) void proj_fwd_kernel(ProjFwdArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kHalf][kPad];   // [gate][out][in]
-  __shared__ float s_bias[2][kHalf];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kb = blockIdx.y >> 1;
-  const int half = blockIdx.y & 1;
-  const int col0 = kb * kBS;                 // first column of this block in x and the outputs
-  const int out0 = half * kHalf;             // first output column (within the block) owned here
+__global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_ring[kFwdBufs][kKT][kBS];
+  const int id = blockIdx.x;
+  const int range = id / p.nb;
+  const int kb = id - range * p.nb;
+  if (range >= p.ranges) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = wave >> 2;                 // gate of this wave
+  const int ob = (wave & 3) * 64;           // first output (within the block) of this wave
+  const Range rg = token_range(range, p.per, p.T);
+  const uint32_t ring0 = lds_addr(&s_ring[0][0][0]);
 
-  // stage w_g[kb][in][out0 .. out0+127] transposed: s_w[g][out][in]
+  // weights: 16 slabs (gate, 32 input rows) in 4 rounds of 4 ring buffers
+  bf16x8 wr[4][8];                          // [m-tile][k-step]
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const uint16_t* wb = p.w[g] + static_cast<long long>(kb) * kBS * kBS;
-    for (int it = tid; it < (kBS / 2) * (kHalf / 8); it += 256) {
-      const int in = (it / (kHalf / 8)) * 2;
-      const int o = (it % (kHalf / 8)) * 8;
-      const u32x4 r0 = load16(wb + in * kBS + out0 + o);
-      const u32x4 r1 = load16(wb + (in + 1) * kBS + out0 + o);
+  for (int round = 0; round < 4; ++round) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t lo = (r0[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-        const uint32_t hi = (r1[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(&s_w[g][o + j][in]) = lo | (hi << 16);
-      }
+    for (int b = 0; b < 4; ++b) {
+      const int sl = round * 4 + b;         // gate sl / 8, input rows (sl % 8) * 32 .. +31
+      const uint16_t* src = p.w[sl >> 3] + static_cast<long long>(kb) * kBS * kBS + (sl & 7) * kKT * kBS;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) slab_piece<kSwz32>(src, kBS, wave * 2 + u, kKT, &s_ring[b][0][0], lane);
     }
-  }
-  // bias of the 128 output columns owned here
-  for (int it = tid; it < 2 * kHalf; it += 256) {
-    const int g = it / kHalf;
-    const int o = it % kHalf;
-    s_bias[g][o] = p.bias[g] != nullptr ? bf(p.bias[g][col0 + out0 + o]) : 0.0f;
-  }
-  __syncthreads();
-
-  const long long n_tiles = (p.T + kTileT - 1) / kTileT;
-  long long tile = blockIdx.x;
-  if (tile >= n_tiles) return;
-  TokFrags cur;
-  load_tok_frags(cur, p.x, p.Wd, p.T, tile * kTileT + wave * kNT, col0, lane);
-  for (; tile < n_tiles; tile += p.splits) {
-    const long long t0 = tile * kTileT + wave * kNT;
-    TokFrags nxt;
-    const long long ntile = tile + p.splits;
-    if (ntile < n_tiles) load_tok_frags(nxt, p.x, p.Wd, p.T, ntile * kTileT + wave * kNT, col0, lane);
+    wait_vm_lds<0>();
+    __syncthreads();
+    if (gw == (round >> 1)) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      f32x4 acc[8][2];
+      for (int b = 0; b < 4; ++b) {
+        const int ks = (round & 1) * 4 + b;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      mma_tile(acc, s_w[g], cur, lane);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const long long t = t0 + nt * 16 + (lane & 15);
-        if (t < p.T) {
-          uint16_t* orow = p.out[g] + t * p.Wd + col0 + out0 + (lane >> 4) * 4;
-#pragma unroll
-          for (int mt = 0; mt < 8; ++mt) {
-            const float* bb = &s_bias[g][mt * 16 + (lane >> 4) * 4];
-            u32x2 v;
-            v[0] = pack2(acc[mt][nt][0] + bb[0], acc[mt][nt][1] + bb[1]);
-            v[1] = pack2(acc[mt][nt][2] + bb[2], acc[mt][nt][3] + bb[3]);
-            *reinterpret_cast<u32x2*>(orow + mt * 16) = v;
-          }
+        for (int mt = 0; mt < 4; ++mt) {
+          u32x2 lo = lds_read_tr(ring0 + b * kSlabBytes + frag_off(ob + mt * 16, lane, 0));
+          u32x2 hi = lds_read_tr(ring0 + b * kSlabBytes + frag_off(ob + mt * 16, lane, 1));
+          lds_wait<0>(lo, hi);
+          wr[mt][ks] = frag_of(lo, hi);
         }
       }
     }
-    if (ntile < n_tiles) cur = nxt;
+    __syncthreads();
+  }
+
+  // bias of this lane's outputs: ob + mt*16 + (lane/16)*4 + j
+  f32x4 bias[4];
+  const uint16_t* bsrc = p.bias[gw];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bias[mt][j] = bsrc != nullptr ? bf(bsrc[kb * kBS + ob + mt * 16 + (lane >> 4) * 4 + j]) : 0.0f;
+    }
+  }
+
+  // x slabs: piece wave * 2 + u of each step
+  const uint16_t* xsrc = p.x + kb * kBS;
+  auto issue = [=](int st) {
+    const long long t0 = rg.tbeg + static_cast<long long>(st) * kKT;
+    const int valid = rg.tend - t0 < kKT ? static_cast<int>(rg.tend - t0) : kKT;
+#pragma unroll
+    for (int u = 0; u < kFwdDma; ++u) {
+      slab_piece<kSwz16>(xsrc + t0 * p.Wd, p.Wd, wave * kFwdDma + u, valid, &s_ring[st % kFwdBufs][0][0], lane);
+    }
+  };
+  // B operand of k-step ks, token tile tt: row tt*16 + lane%16, columns ks*32 + (lane/16)*8 .. +7
+  uint32_t xoff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) xoff[ks] = row_off16(lane & 15, ks * 4 + (lane >> 4));
+  uint16_t* obase = p.out[gw] + kb * kBS + ob + (lane >> 4) * 4;
+
+#pragma unroll
+  for (int d = 0; d < kFwdBufs - 1; ++d) {
+    if (d < rg.n_steps) issue(d);
+  }
+  for (int st = 0; st < rg.n_steps; ++st) {
+    const int ahead = rg.n_steps - 1 - st;
+    wait_ring<kFwdStores, kFwdDma, kFwdBufs - 1, kFwdBufs - 2>(st < kFwdBufs - 1 ? st : kFwdBufs - 1,
+                                                              ahead < kFwdBufs - 2 ? ahead : kFwdBufs - 2);
+    // every wave's loads of this step are in LDS, and every wave is done
+    // reading the buffer the next issue overwrites (read in step st - 1)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ahead >= kFwdBufs - 1) issue(st + kFwdBufs - 1);
+    const uint32_t sb = ring0 + static_cast<uint32_t>(st % kFwdBufs) * kSlabBytes;
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc[mt][0] = bias[mt];
+      acc[mt][1] = bias[mt];
+    }
+    // token operands of both tiles, at most 8 reads in flight
+    u32x4 xb[8][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      xb[ks][0] = lds_read16(sb + xoff[ks]);
+      xb[ks][1] = lds_read16(sb + xoff[ks] + 16 * kBS * 2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      // in flight: k-steps ks .. min(ks + 3, 7), two reads each
+      if (ks <= 4) {
+        lds_wait<6>(xb[ks][0], xb[ks][1]);
+      } else if (ks == 5) {
+        lds_wait<4>(xb[ks][0], xb[ks][1]);
+      } else if (ks == 6) {
+        lds_wait<2>(xb[ks][0], xb[ks][1]);
+      } else {
+        lds_wait<0>(xb[ks][0], xb[ks][1]);
+      }
+      if (ks + 4 < 8) {
+        xb[ks + 4][0] = lds_read16(sb + xoff[ks + 4]);
+        xb[ks + 4][1] = lds_read16(sb + xoff[ks + 4] + 16 * kBS * 2);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][tt] = mfma(wr[mt][ks], as_bf16x8(xb[ks][tt]), acc[mt][tt]);
+      }
+    }
+    asm volatile("" ::: "memory");
+    const long long t0 = rg.tbeg + static_cast<long long>(st) * kKT;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const long long t = t0 + tt * 16 + (lane & 15);
+      if (ahead > 0 || t < rg.tend) {
+        uint16_t* orow = obase + t * p.Wd;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          u32x2 v;
+          v[0] = pack2(acc[mt][tt][0], acc[mt][tt][1]);
+          v[1] = pack2(acc[mt][tt][2], acc[mt][tt][3]);
+          *reinterpret_cast<u32x2*>(orow + mt * 16) = v;
+        }
+      }
+    }
+    // the stores are issued before the next step's wait counts them
+    asm volatile("" ::: "memory");
   }
 }
+
+// ---------------------------------------------------------------- dx
+//
+// dx[t, kb*256 + i] = dx_in[t, kb*256 + i]
+//                     + sum_g sum_o dgate_g[t, kb*256 + o] w_g[kb][i][o].
+// MFMA with A = w_g (rows i, k = o: contiguous in memory, loaded straight
+// into registers) and B = dgate_g^T (k = o, columns t) from the LDS ring; D
+// holds 4 consecutive dx channels of one token per lane. Wave w computes
+// inputs 32 * w .. +31 (2 m-tiles) over K = 512 (both gates, 16 k-steps).
+// dx_in, when given, rides in the ring as a third slab and initialises the
+// accumulators.
+
+constexpr int kDxBufs = 3;       // ring of (dgate_x, dgate_a[, dx_in]) slab groups
+constexpr int kDxStores = 4;     // 8-byte stores per wave per step (2 token tiles x 2 m-tiles)
 
 struct ProjDxArgs {
   const uint16_t* w[2];
@@ -201,68 +400,150 @@ struct ProjDxArgs {
   const uint16_t* dx_in;
   uint16_t* dx_out;
   long long T;
+  long long per;   // tokens per range (a multiple of kKT)
   int Wd;
-  int splits;
+  int nb;
+  int ranges;
 };
 
-// dx rows in0 .. in0+127 of block kb: A = w_g[kb][in][out] (natural layout), B = dgate_g tokens.
-__global__ __launch_bounds__(256) void proj_dx_kernel(ProjDxArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kHalf][kPad];   // [gate][in][out]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kb = blockIdx.y >> 1;
-  const int half = blockIdx.y & 1;
-  const int col0 = kb * kBS;
-  const int in0 = half * kHalf;
+template <bool RES>
+__global__ __launch_bounds__(kWaves8 * 64) void proj_dx_kernel(ProjDxArgs p) {
+  constexpr int kQ = RES ? 3 : 2;                 // slabs per step
+  constexpr int kDma = kQ * 16 / kWaves8;         // 1 KiB loads per wave per step
+  __shared__ __attribute__((aligned(16))) uint16_t s_ring[kDxBufs][kQ][kKT][kBS];
+  const int id = blockIdx.x;
+  const int range = id / p.nb;
+  const int kb = id - range * p.nb;
+  if (range >= p.ranges) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ib = wave * 32;                       // first input channel (within the block) of this wave
+  const Range rg = token_range(range, p.per, p.T);
+  const uint32_t ring0 = lds_addr(&s_ring[0][0][0][0]);
 
+  // weights: lane l holds w_g[kb][ib + mt*16 + l%16][(ks%8)*32 + (l/16)*8 .. +7], g = ks / 8
+  bf16x8 wr[2][16];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const uint16_t* wb = p.w[g] + static_cast<long long>(kb) * kBS * kBS;
-    for (int it = tid; it < kHalf * (kBS / 8); it += 256) {
-      const int r = it / (kBS / 8);
-      const int o = (it % (kBS / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&s_w[g][r][o]) = load16(wb + (in0 + r) * kBS + o);
-    }
+  for (int ks = 0; ks < 16; ++ks) {
+    const uint16_t* wb = p.w[ks >> 3] + static_cast<long long>(kb) * kBS * kBS + (ks & 7) * 32 + (lane >> 4) * 8;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) wr[mt][ks] = as_bf16x8(load16(wb + (ib + mt * 16 + (lane & 15)) * kBS));
   }
-  __syncthreads();
 
-  const long long n_tiles = (p.T + kTileT - 1) / kTileT;
-  for (long long tile = blockIdx.x; tile < n_tiles; tile += p.splits) {
-    const long long t0 = tile * kTileT + wave * kNT;
-    f32x4 acc[8][2];
+  // loads of step st: pieces 2 * wave and 2 * wave + 1 of each slab
+  const uint16_t* src0 = p.dg[0] + kb * kBS;
+  const uint16_t* src1 = p.dg[1] + kb * kBS;
+  const uint16_t* src2 = RES ? p.dx_in + kb * kBS : nullptr;
+  const int Wd = p.Wd;
+  auto issue = [=](int st) {
+    const long long t0 = rg.tbeg + static_cast<long long>(st) * kKT;
+    const int valid = rg.tend - t0 < kKT ? static_cast<int>(rg.tend - t0) : kKT;
+    const int buf = st % kDxBufs;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u) {
+      slab_piece<kSwz16>(src0 + t0 * Wd, Wd, wave * 2 + u, valid, &s_ring[buf][0][0][0], lane);
+      slab_piece<kSwz16>(src1 + t0 * Wd, Wd, wave * 2 + u, valid, &s_ring[buf][1][0][0], lane);
+      if constexpr (RES) slab_piece<kSwz16>(src2 + t0 * Wd, Wd, wave * 2 + u, valid, &s_ring[buf][kQ - 1][0][0], lane);
     }
-    TokFrags fr[2];
-    load_tok_frags(fr[0], p.dg[0], p.Wd, p.T, t0, col0, lane);
-    load_tok_frags(fr[1], p.dg[1], p.Wd, p.T, t0, col0, lane);
-    mma_tile(acc, s_w[0], fr[0], lane);
-    mma_tile(acc, s_w[1], fr[1], lane);
+  };
+  // B operand of k-step ks, token tile tt: slab ks / 8, row tt*16 + lane%16,
+  // columns (ks%8)*32 + (lane/16)*8 .. +7
+  uint32_t xoff[8];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const long long t = t0 + nt * 16 + (lane & 15);
-      if (t < p.T) {
-        const long long rowoff = t * p.Wd + col0 + in0 + (lane >> 4) * 4;
+  for (int k = 0; k < 8; ++k) xoff[k] = row_off16(lane & 15, k * 4 + (lane >> 4));
+  uint16_t* obase = p.dx_out + kb * kBS + ib + (lane >> 4) * 4;
+
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          float add[4] = {0.f, 0.f, 0.f, 0.f};
-          if (p.dx_in != nullptr) {
-            const u32x2 d = *reinterpret_cast<const u32x2*>(p.dx_in + rowoff + mt * 16);
-            add[0] = bf(static_cast<uint16_t>(d[0] & 0xFFFFu));
-            add[1] = bf(static_cast<uint16_t>(d[0] >> 16));
-            add[2] = bf(static_cast<uint16_t>(d[1] & 0xFFFFu));
-            add[3] = bf(static_cast<uint16_t>(d[1] >> 16));
-          }
+  for (int d = 0; d < kDxBufs - 1; ++d) {
+    if (d < rg.n_steps) issue(d);
+  }
+  for (int st = 0; st < rg.n_steps; ++st) {
+    const int ahead = rg.n_steps - 1 - st;
+    wait_ring<kDxStores, kDma, kDxBufs - 1, kDxBufs - 2>(st < kDxBufs - 1 ? st : kDxBufs - 1,
+                                                         ahead < kDxBufs - 2 ? ahead : kDxBufs - 2);
+    // every wave's loads of this step are in LDS, and every wave is done
+    // reading the buffer the next issue overwrites (read in step st - 1)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ahead >= kDxBufs - 1) issue(st + kDxBufs - 1);
+    const uint32_t sb = ring0 + static_cast<uint32_t>(st % kDxBufs) * (kQ * kSlabBytes);
+    f32x4 acc[2][2];
+    if constexpr (RES) {
+      // dx_in at row tt*16 + lane%16, channels ib + mt*16 + (lane/16)*4 .. +3
+      u32x2 r[2][2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int row = tt * 16 + (lane & 15);
+          const int g = (ib + mt * 16) / 8 + (lane >> 5);
+          r[mt][tt] = lds_read8(sb + 2 * kSlabBytes + row_off16(row, g) + ((lane >> 4) & 1) * 8);
+        }
+      }
+      lds_wait<0>(r[0][0], r[0][1]);
+      lds_wait<0>(r[1][0], r[1][1]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          acc[mt][tt] = f32x4{__uint_as_float(r[mt][tt][0] << 16), __uint_as_float(r[mt][tt][0] & 0xFFFF0000u),
+                              __uint_as_float(r[mt][tt][1] << 16), __uint_as_float(r[mt][tt][1] & 0xFFFF0000u)};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    // gate-gradient operands of both tiles, at most 8 reads in flight
+    u32x4 xb[16][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      xb[ks][0] = lds_read16(sb + xoff[ks & 7] + (ks >> 3) * kSlabBytes);
+      xb[ks][1] = lds_read16(sb + xoff[ks & 7] + (ks >> 3) * kSlabBytes + 16 * kBS * 2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      // in flight: k-steps ks .. min(ks + 3, 15), two reads each
+      if (ks <= 12) {
+        lds_wait<6>(xb[ks][0], xb[ks][1]);
+      } else if (ks == 13) {
+        lds_wait<4>(xb[ks][0], xb[ks][1]);
+      } else if (ks == 14) {
+        lds_wait<2>(xb[ks][0], xb[ks][1]);
+      } else {
+        lds_wait<0>(xb[ks][0], xb[ks][1]);
+      }
+      if (ks + 4 < 16) {
+        xb[ks + 4][0] = lds_read16(sb + xoff[(ks + 4) & 7] + ((ks + 4) >> 3) * kSlabBytes);
+        xb[ks + 4][1] = lds_read16(sb + xoff[(ks + 4) & 7] + ((ks + 4) >> 3) * kSlabBytes + 16 * kBS * 2);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[mt][tt] = mfma(wr[mt][ks], as_bf16x8(xb[ks][tt]), acc[mt][tt]);
+      }
+    }
+    asm volatile("" ::: "memory");
+    const long long t0 = rg.tbeg + static_cast<long long>(st) * kKT;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const long long t = t0 + tt * 16 + (lane & 15);
+      if (ahead > 0 || t < rg.tend) {
+        uint16_t* orow = obase + t * p.Wd;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
           u32x2 v;
-          v[0] = pack2(acc[mt][nt][0] + add[0], acc[mt][nt][1] + add[1]);
-          v[1] = pack2(acc[mt][nt][2] + add[2], acc[mt][nt][3] + add[3]);
-          *reinterpret_cast<u32x2*>(p.dx_out + rowoff + mt * 16) = v;
+          v[0] = pack2(acc[mt][tt][0], acc[mt][tt][1]);
+          v[1] = pack2(acc[mt][tt][2], acc[mt][tt][3]);
+          *reinterpret_cast<u32x2*>(orow + mt * 16) = v;
         }
       }
     }
+    // the stores are issued before the next step's wait counts them
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -285,47 +566,8 @@ __global__ __launch_bounds__(256) void proj_dx_kernel(ProjDxArgs p) {
 // in the accumulators' own layout (16 contiguous bytes per lane) and
 // proj_dw_reduce_kernel sums the partials of all ranges in a fixed order.
 
-constexpr int kKT = 32;               // tokens per step
 constexpr int kDwBufs = 4;            // LDS ring depth (32 KiB per step)
-constexpr int kDwWaves = 8;
 constexpr int kDwIns = 4;             // 1 KiB loads per wave per step (32 KiB / 8 waves)
-
-// 16 bytes per lane from global memory straight into LDS (lane l writes
-// dst + 16 * l). The 16-byte form exists only on gfx950, so the host pass does
-// not see it.
-__device__ __forceinline__ void lds_dma16(const void* src, void* dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-#endif
-}
-
-// waits until at most N of this wave's global loads and none of its LDS
-// accesses are outstanding (gfx9 s_waitcnt layout: vmcnt[3:0], expcnt[6:4],
-// lgkmcnt[11:8])
-template <int N>
-__device__ __forceinline__ void wait_vm_lds() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);
-}
-
-// Transpose read ds_read_b64_tr_b16 at LDS byte address `addr`: in each group
-// of 16 lanes, lane i receives element (i & 3) of the 8 bytes addressed by
-// lanes (i >> 2) + 4m, m = 0..3. Issued as inline assembly: the compiler
-// would otherwise make every such read wait for all LDS-bound global loads in
-// flight (it cannot tell which ring buffer they land in). Completion is
-// waited for explicitly with lds_wait.
-__device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
-  u32x2 d;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(d) : "v"(addr));
-  return d;
-}
-
-// waits until at most N LDS reads are outstanding; the operands tie the
-// values read so that no use moves above the wait
-template <int N>
-__device__ __forceinline__ void lds_wait(u32x2& x, u32x2& y) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "n"(N));
-}
 
 struct ProjDwArgs {
   const uint16_t* x;
@@ -339,28 +581,9 @@ struct ProjDwArgs {
   int splits;
 };
 
-// LDS byte offsets, within one slab, of the two transpose reads that give a
-// lane its MFMA operand for columns col0 .. col0+15 (lane l: column
-// col0 + l % 16, tokens (l / 16) * 8 .. +7). Source lane s of each 16-lane
-// group addresses token row (s / 4) (+4 for the second read) at columns
-// col0 + 4 * (s % 4) .. +3; row r stores 32-byte chunk c at position
-// c ^ (r % 16).
-__device__ __forceinline__ uint32_t frag_off(int col0, int lane, int half) {
-  const int g = lane >> 4;
-  const int sl = lane & 15;
-  const int r = g * 8 + (sl >> 2) + half * 4;
-  const int chunk = col0 >> 4;
-  return static_cast<uint32_t>(r * (kBS * 2) + ((chunk ^ (r & 15)) << 5) + (sl & 3) * 8);
-}
-
-__device__ __forceinline__ bf16x8 frag_of(u32x2 lo, u32x2 hi) {
-  return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
-__global__ __launch_bounds__(kDwWaves * 64) void proj_dw_kernel(ProjDwArgs p) {
+__global__ __launch_bounds__(kWaves8 * 64) void proj_dw_kernel(ProjDwArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_slab[kDwBufs][2][kKT][kBS];   // [buf][x, dgate][token][col]
   __shared__ float s_cs[4][kBS];
-  constexpr uint32_t kSlabBytes = kKT * kBS * 2;
   // workgroup id -> (gate, range, block): ids 8 apart run on the same XCD, so
   // the two gates of one (range, block) are paired that way
   const int id = blockIdx.x;
@@ -383,19 +606,19 @@ __global__ __launch_bounds__(kDwWaves * 64) void proj_dw_kernel(ProjDwArgs p) {
   // 2 * (ins % 16) and the next. Byte offsets from the step's first token.
   const uint16_t* base_x = p.x + kb * kBS;
   const uint16_t* base_g = p.dg[gate] + kb * kBS;
-  uint32_t voff[kDwIns];
+  uint32_t roff[kDwIns];                // byte offset of this lane's row from the step's first token
+  uint32_t goff[kDwIns];                // byte offset of this lane's granule within the row
   int row[kDwIns];
 #pragma unroll
   for (int u = 0; u < kDwIns; ++u) {
     const int ins = wave * kDwIns + u;
     const int r = (ins & 15) * 2 + (lane >> 5);
     const int pos = lane & 31;           // 16-byte granule position in the LDS row
-    const int gran = (((pos >> 1) ^ (r & 15)) << 1) | (pos & 1);
-    voff[u] = static_cast<uint32_t>(r) * static_cast<uint32_t>(p.Wd) * 2u + gran * 16u;
+    roff[u] = static_cast<uint32_t>(r) * static_cast<uint32_t>(p.Wd) * 2u;
+    goff[u] = static_cast<uint32_t>(((((pos >> 1) ^ (r & 15)) << 1) | (pos & 1)) * 16);
     row[u] = r;
   }
-  // loads of step `st`; in the range's last step, rows past its end are
-  // zero-filled instead (LDS stores, waited for with the loads)
+  // loads of step `st`; rows past the range's end read zeros
   auto issue = [=](int st) {
     const long long t0 = tbeg + static_cast<long long>(st) * kKT;
     const int valid = tend - t0 < kKT ? static_cast<int>(tend - t0) : kKT;
@@ -403,18 +626,13 @@ __global__ __launch_bounds__(kDwWaves * 64) void proj_dw_kernel(ProjDwArgs p) {
     for (int u = 0; u < kDwIns; ++u) {
       const int ins = wave * kDwIns + u;
       const char* sb = reinterpret_cast<const char*>(((ins >> 4) == 0 ? base_x : base_g) + t0 * p.Wd);
-      uint16_t* dst = &s_slab[st % kDwBufs][ins >> 4][(ins & 15) * 2][0];
-      if (valid == kKT || row[u] < valid) {
-        lds_dma16(sb + voff[u], dst);
-      } else {
-        *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-      }
+      const char* rp = row[u] < valid ? sb + roff[u] : reinterpret_cast<const char*>(g_zero_row);
+      lds_dma16(rp + goff[u], &s_slab[st % kDwBufs][ins >> 4][(ins & 15) * 2][0]);
     }
   };
 
   // LDS byte addresses of this lane's operand reads in ring buffer 0
-  typedef __attribute__((address_space(3))) uint16_t lds_u16;
-  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)(&s_slab[0][0][0][0])));
+  const uint32_t ring0 = lds_addr(&s_slab[0][0][0][0]);
   uint32_t a_off[4][2];
   uint32_t b_off[8][2];
 #pragma unroll
@@ -571,29 +789,23 @@ __global__ __launch_bounds__(256) void proj_dw_reduce_kernel(const float* part_w
   }
 }
 
-int token_splits(long long T, int nb) {
-  const long long tiles = (T + kTileT - 1) / kTileT;
-  long long s = (256 * 2 + 2 * nb - 1) / (2 * nb);   // about two waves of workgroups over 256 CUs
-  if (s < 1) s = 1;
-  if (s > tiles) s = tiles;
-  return static_cast<int>(s);
-}
-
-// token ranges of the weight-gradient kernel: about one workgroup per CU
-// (each holds a whole CU's worth of registers), no empty range
-int dw_splits(long long T, int nb) {
+// token ranges for a kernel with `wgs` workgroups per range: about one
+// workgroup per CU (each holds a whole CU's worth of registers), no empty range
+int range_count(long long T, int wgs) {
   const long long steps = (T + kKT - 1) / kKT;
-  long long s = 256 / (2 * nb);
+  long long s = 256 / wgs;
   if (s < 1) s = 1;
   if (s > steps) s = steps;
   const long long per = (steps + s - 1) / s;
   return static_cast<int>((steps + per - 1) / per);
 }
 
-long long dw_per(long long T, int splits) {
+long long range_per(long long T, int ranges) {
   const long long steps = (T + kKT - 1) / kKT;
-  return ((steps + splits - 1) / splits) * kKT;
+  return ((steps + ranges - 1) / ranges) * kKT;
 }
+
+int dw_splits(long long T, int nb) { return range_count(T, 2 * nb); }
 
 rglru_status_t check_proj(int64_t tokens, int64_t width, int64_t block) {
   if (tokens < 1 || width < 1 || block < 1) return RGLRU_ERR_INVALID_ARGUMENT;
@@ -646,8 +858,11 @@ rglru_status_t rglru_blockdiag_gate_proj_fwd(int64_t tokens, int64_t width, int6
   a.out[1] = static_cast<uint16_t*>(gate_a);
   a.T = tokens;
   a.Wd = static_cast<int>(width);
-  a.splits = token_splits(tokens, nb);
-  hipLaunchKernelGGL(proj_fwd_kernel, dim3(a.splits, nb * 2), dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  a.nb = nb;
+  a.ranges = range_count(tokens, nb);
+  a.per = range_per(tokens, a.ranges);
+  hipLaunchKernelGGL(proj_fwd_kernel, dim3(static_cast<unsigned>(a.ranges) * nb), dim3(kWaves8 * 64), 0,
+                     static_cast<hipStream_t>(stream), a);
   return launch_status();
 }
 
@@ -676,7 +891,7 @@ rglru_status_t rglru_blockdiag_gate_proj_bwd(int64_t tokens, int64_t width, int6
   w.dg[0] = static_cast<const uint16_t*>(dgate_x);
   w.dg[1] = static_cast<const uint16_t*>(dgate_a);
   const int sw = dw_splits(tokens, nb);
-  w.per = dw_per(tokens, sw);
+  w.per = range_per(tokens, sw);
   w.part_w = static_cast<float*>(workspace);
   w.part_b = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                       round_up(static_cast<size_t>(sw) * nb * 2 * kBS * kBS * sizeof(float), 256));
@@ -685,7 +900,7 @@ rglru_status_t rglru_blockdiag_gate_proj_bwd(int64_t tokens, int64_t width, int6
   w.nb = nb;
   w.splits = sw;
   const long long pairs = static_cast<long long>(sw) * nb;
-  hipLaunchKernelGGL(proj_dw_kernel, dim3(static_cast<unsigned>(((pairs + 7) / 8) * 16)), dim3(kDwWaves * 64), 0,
+  hipLaunchKernelGGL(proj_dw_kernel, dim3(static_cast<unsigned>(((pairs + 7) / 8) * 16)), dim3(kWaves8 * 64), 0,
                      st, w);
   rglru_status_t s1 = launch_status();
   if (s1 != RGLRU_OK) return s1;
@@ -705,8 +920,16 @@ rglru_status_t rglru_blockdiag_gate_proj_bwd(int64_t tokens, int64_t width, int6
   d.dx_out = static_cast<uint16_t*>(dx_out);
   d.T = tokens;
   d.Wd = static_cast<int>(width);
-  d.splits = token_splits(tokens, nb);
-  hipLaunchKernelGGL(proj_dx_kernel, dim3(d.splits, nb * 2), dim3(256), 0, st, d);
+  d.nb = nb;
+  d.ranges = range_count(tokens, nb);
+  d.per = range_per(tokens, d.ranges);
+  if (dx_in != nullptr) {
+    hipLaunchKernelGGL(proj_dx_kernel<true>, dim3(static_cast<unsigned>(d.ranges) * nb), dim3(kWaves8 * 64), 0, st,
+                       d);
+  } else {
+    hipLaunchKernelGGL(proj_dx_kernel<false>, dim3(static_cast<unsigned>(d.ranges) * nb), dim3(kWaves8 * 64), 0, st,
+                       d);
+  }
   return launch_status();
 }
 
