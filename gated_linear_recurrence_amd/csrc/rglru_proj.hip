@@ -118,6 +118,10 @@ __device__ __forceinline__ u32x2 lds_read8(uint32_t addr) {
   return d;
 }
 
+__device__ __forceinline__ void lds_write8(uint32_t addr, u32x2 v) {
+  asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v));
+}
+
 // Transpose read ds_read_b64_tr_b16 (gfx950): in each group of 16 lanes, lane
 // i receives element (i & 3) of the 8 bytes addressed by lanes (i >> 2) + 4m,
 // m = 0..3.
@@ -227,7 +231,8 @@ __device__ __forceinline__ Range token_range(int idx, long long per, long long T
 
 constexpr int kFwdBufs = 4;                   // ring of x slabs (16 KiB each)
 constexpr int kFwdDma = 2;                    // 1 KiB loads per wave per step
-constexpr int kFwdStores = 8;                 // 8-byte stores per wave per step (2 token tiles x 4 m-tiles)
+constexpr int kFwdStores = 4;                 // 16-byte stores per wave per step (2 token tiles x 2)
+constexpr int kStagePitch = 144;              // bytes per staged output row (128 + 16: conflict-free)
 
 struct ProjFwdArgs {
   const uint16_t* x;
@@ -243,6 +248,9 @@ struct ProjFwdArgs {
 
 __global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_ring[kFwdBufs][kKT][kBS];
+  // per-wave output staging: 2 token tiles x 16 tokens x 64 outputs, so that
+  // each store writes whole 128-byte row segments
+  __shared__ __attribute__((aligned(16))) char s_stage[kWaves8][2][16][kStagePitch];
   const int id = blockIdx.x;
   const int range = id / p.nb;
   const int kb = id - range * p.nb;
@@ -308,7 +316,9 @@ __global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
   uint32_t xoff[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) xoff[ks] = row_off16(lane & 15, ks * 4 + (lane >> 4));
-  uint16_t* obase = p.out[gw] + kb * kBS + ob + (lane >> 4) * 4;
+  uint16_t* obase = p.out[gw] + kb * kBS + ob + (lane & 7) * 8;   // lane's 16 bytes of a staged row
+  const uint32_t stage_w = lds_addr(&s_stage[wave][0][lane & 15][(lane >> 4) * 8]);
+  const uint32_t stage_r = lds_addr(&s_stage[wave][0][lane >> 3][(lane & 7) * 16]);
 
 #pragma unroll
   for (int d = 0; d < kFwdBufs - 1; ++d) {
@@ -360,19 +370,34 @@ __global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
       }
     }
     asm volatile("" ::: "memory");
+    // D lane l: token tt*16 + l%16, outputs mt*16 + (l/16)*4 .. +3 -> staging
+    // (LDS accesses of one wave complete in order)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        u32x2 v;
+        v[0] = pack2(acc[mt][tt][0], acc[mt][tt][1]);
+        v[1] = pack2(acc[mt][tt][2], acc[mt][tt][3]);
+        lds_write8(stage_w + tt * 16 * kStagePitch + mt * 32, v);
+      }
+    }
+    // staged rows -> global: lane l stores bytes 16 * (l % 8) .. +15 of row (l / 8) (+8)
+    u32x4 sv[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sv[tt][h] = lds_read16(stage_r + (tt * 16 + h * 8) * kStagePitch);
+    }
+    lds_wait<0>(sv[0][0], sv[0][1]);
+    lds_wait<0>(sv[1][0], sv[1][1]);
     const long long t0 = rg.tbeg + static_cast<long long>(st) * kKT;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const long long t = t0 + tt * 16 + (lane & 15);
-      if (ahead > 0 || t < rg.tend) {
-        uint16_t* orow = obase + t * p.Wd;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          u32x2 v;
-          v[0] = pack2(acc[mt][tt][0], acc[mt][tt][1]);
-          v[1] = pack2(acc[mt][tt][2], acc[mt][tt][3]);
-          *reinterpret_cast<u32x2*>(orow + mt * 16) = v;
-        }
+      for (int h = 0; h < 2; ++h) {
+        const long long t = t0 + tt * 16 + h * 8 + (lane >> 3);
+        if (ahead > 0 || t < rg.tend) *reinterpret_cast<u32x4*>(obase + t * p.Wd) = sv[tt][h];
       }
     }
     // the stores are issued before the next step's wait counts them
