@@ -82,7 +82,7 @@ typedef struct {
   int32_t chunk;    /* time tile of the parallel scan: 0 = library default (64),
                        or one of 8, 16, 32, 64, 128, 256. Results depend on it
                        only through floating-point rounding. The forward uses
-                       min(chunk, 64), the backward min(chunk, 128). */
+                       min(chunk, 64), the backward min(chunk, 32). */
   float c;          /* decay scale of a = exp(-c * softplus(lambda) * r); 8 in the method */
   int32_t reserved; /* must be 0 */
 } rglru_shape_t;
