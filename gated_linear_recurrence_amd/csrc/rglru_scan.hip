@@ -417,13 +417,14 @@ constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 // workgroup:
 //   control waves : run the look-back of t_{i-1}, whose map went out during
 //                   the previous iteration, publish its outgoing carry and hand
-//                   the incoming one to the data waves through LDS; take
-//                   ticket t_{i+2}; once every data wave has reduced its steps
-//                   of t_i, publish the map of t_i; evaluate the per-channel
-//                   decay constants of t_{i+1};
-//   load wave     : once the look-back polls are on their way, stream the raw
-//                   words (and reset flags) of t_{i+1} from HBM straight into
-//                   LDS (global_load_lds) and wait for them;
+//                   the incoming one to the data waves through LDS; once every
+//                   data wave has reduced its steps of t_i, publish the map of
+//                   t_i;
+//   load wave     : take ticket t_{i+2}; once the look-back polls are on their
+//                   way, stream the raw words (and reset flags) of t_{i+1} from
+//                   HBM straight into LDS (global_load_lds), evaluate the
+//                   per-channel decay constants of t_{i+1} while they land,
+//                   and wait for them;
 //   data waves    : evaluate the gates of t_i from LDS into registers as
 //                   (alpha, write) pairs, reduce their steps to an affine map
 //                   and report it, then wait for the carry of t_{i-1} and replay
@@ -513,19 +514,23 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     return t;
   };
 
-  // control wave cj: decay constants of channel lane*V + cj of a tile, from
-  // the lambda value `lam` of that channel
-  auto tile_consts = [=](unsigned tile, int buf, float lam) {
+  // load wave: decay constants of channels lane*V .. +V-1 of a tile, from
+  // their lambda values
+  auto tile_consts = [=](unsigned tile, int buf, const float (&lam)[V]) {
     const Tile t = tile_of(tile, 0);
     if (!t.valid) return;
-    float cs = 0.0f, k2 = 0.0f;
-    if (t.active) channel_consts(lam, p.c, cs, k2);
-    s_cs[buf][lane * V + cj] = cs;
-    s_k2[buf][lane * V + cj] = k2;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      float cs = 0.0f, k2 = 0.0f;
+      if (t.active) channel_consts(lam[j], p.c, cs, k2);
+      s_cs[buf][lane * V + j] = cs;
+      s_k2[buf][lane * V + j] = k2;
+    }
   };
-  auto tile_lam = [=](unsigned tile) -> float {
+  auto tile_lam = [=](unsigned tile, float (&lam)[V]) {
     const Tile t = tile_of(tile, 0);
-    return (t.valid && t.active) ? p.lam[t.ch + cj] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < V; ++j) lam[j] = (t.valid && t.active) ? p.lam[t.ch + j] : 0.0f;
   };
 
   // load wave: every data wave's raw words of a tile, and the tile's reset
@@ -614,8 +619,10 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
   const unsigned tag = __builtin_amdgcn_readfirstlane(s_tag);
   {
     const unsigned t0 = __builtin_amdgcn_readfirstlane(s_tk[0]);
-    if (ctrl) tile_consts(t0, 0, tile_lam(t0));
     if (loader) {
+      float lam[V];
+      tile_lam(t0, lam);
+      tile_consts(t0, 0, lam);
       if (t0 < p.n_tiles) load_tile(t0, 0);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
@@ -668,11 +675,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
 
     if (ctrl) {
       clear();
-      // Issued first, used after the look-back: the next ticket and the
-      // lambda values of t_{i+1} (their round trips overlap the polls').
-      unsigned long long ticket = 0;
-      if (cj == 0 && lane == 0 && cur_ok) ticket = atomicAdd(&p.hdr->counter, 1ull);
-      const float lam_nxt = nxt_ok ? tile_lam(t_nxt) : 0.0f;
       // the carry entering t_{i-1}
       {
         const Tile t = tile_of(t_prv, 0);
@@ -704,10 +706,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
       // s_carry is written before the flag that releases the data waves
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (lane == 0) lds_flag_set(&s_carry_ready[cj], i);
-      // every slot read later is written: a ticket while this workgroup
-      // still draws them, past the last tile once it has stopped
-      if (cj == 0 && lane == 0) s_tk[(i + 2) & 7] = cur_ok ? static_cast<unsigned>(ticket) : p.n_tiles;
-      if (nxt_ok) tile_consts(t_nxt, pb, lam_nxt);
       // once every data wave has reported its map of t_i: the prefixes the
       // data waves replay from, and the published map (a first chunk
       // publishes its outgoing carry instead)
@@ -743,11 +741,21 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
       }
     } else if (loader) {
       clear();
+      // the lambda values of t_{i+1} and the next ticket first: their round
+      // trips overlap the wait for the polls and the tile's loads
+      float lam[V];
+      if (nxt_ok) tile_lam(t_nxt, lam);
+      unsigned long long ticket = 0;
+      if (lane == 0 && cur_ok) ticket = atomicAdd(&p.hdr->counter, 1ull);
       if (nxt_ok) {
         lds_flag_wait(&s_polls_out, i);
         load_tile(t_nxt, pb);
+        tile_consts(t_nxt, pb, lam);
       }
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      // every slot read later is written: a ticket while this workgroup
+      // still draws them, past the last tile once it has stopped
+      if (lane == 0) s_tk[(i + 2) & 7] = cur_ok ? static_cast<unsigned>(ticket) : p.n_tiles;
     } else {
       if (cur_ok) {
         const Tile t = tile_of(t_cur, wave);
