@@ -420,11 +420,10 @@ constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 //                   the incoming one to the data waves through LDS; once every
 //                   data wave has reduced its steps of t_i, publish the map of
 //                   t_i;
-//   load wave     : take ticket t_{i+2}; once the look-back polls are on their
-//                   way, stream the raw words (and reset flags) of t_{i+1} from
-//                   HBM straight into LDS (global_load_lds), evaluate the
-//                   per-channel decay constants of t_{i+1} while they land,
-//                   and wait for them;
+//   load wave     : take ticket t_{i+2}, stream the raw words (and reset
+//                   flags) of t_{i+1} from HBM straight into LDS
+//                   (global_load_lds), evaluate the per-channel decay
+//                   constants of t_{i+1} while they land, and wait for them;
 //   data waves    : evaluate the gates of t_i from LDS into registers as
 //                   (alpha, write) pairs, reduce their steps to an affine map
 //                   and report it, then wait for the carry of t_{i-1} and replay
@@ -434,10 +433,9 @@ constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 // looked back from at the start of the next, so the predecessors' words are
 // mostly visible by then. The data waves issue no loads and the control waves
 // only their polls, so no wave waits on memory traffic it does not need (the
-// vector memory counter retires in order), and the polls are not queued
-// behind a tile of loads. The only waits between waves inside an iteration
-// are one-directional LDS flags (data -> control for the maps, control ->
-// data and load for the carry and the polls), so they cannot deadlock.
+// vector memory counter retires in order). The only waits between waves
+// inside an iteration are one-directional LDS flags (data -> control for the
+// maps, control -> data for the carry), so they cannot deadlock.
 //
 // A staged step row is 256 bytes (64 lanes, 4 bytes each). WIDE loads move 16
 // bytes per lane, so one instruction fills 4 step rows and a tile takes
@@ -475,7 +473,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
   __shared__ unsigned s_tk[8];
   __shared__ unsigned s_tag;
   __shared__ int s_carry_ready[V];   // iteration whose carry (channel j) is in s_carry
-  __shared__ int s_polls_out;        // iteration whose look-back polls have been issued
   __shared__ int s_maps_in;          // data-wave maps reported so far (NW per iteration)
 
   const int lane = threadIdx.x & 63;
@@ -612,7 +609,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     s_tag = static_cast<unsigned>(v0 >> 32) + 1u;
 #pragma unroll
     for (int j = 0; j < V; ++j) s_carry_ready[j] = -1;
-    s_polls_out = -1;
     s_maps_in = 0;
   }
   __syncthreads();
@@ -622,8 +618,8 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     if (loader) {
       float lam[V];
       tile_lam(t0, lam);
-      tile_consts(t0, 0, lam);
       if (t0 < p.n_tiles) load_tile(t0, 0);
+      tile_consts(t0, 0, lam);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
   }
@@ -658,18 +654,24 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
       }
     };
     // composite map of a whole tile, channel lane*V + cj, from its waves' maps
+    // (every LDS read is issued before the first use: one wait, not NW)
     auto tile_map = [=](int mb, float& GA, float& GB, bool& GR) {
+      float Aw[NW], Bw[NW];
+      unsigned Rw[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        Rw[w] = s_R[mb][w];
+        Aw[w] = s_A[mb][w][lane * V + cj];
+        Bw[w] = s_B[mb][w][lane * V + cj];
+      }
       GA = 1.0f;
       GB = 0.0f;
       GR = false;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const bool Rw = s_R[mb][w] != 0u;
-        const float Aw = s_A[mb][w][lane * V + cj];
-        const float Bw = s_B[mb][w][lane * V + cj];
-        GB = Rw ? Bw : fmaf(Aw, GB, Bw);
-        GA *= Aw;
-        GR = GR || Rw;
+        GB = Rw[w] != 0u ? Bw[w] : fmaf(Aw[w], GB, Bw[w]);
+        GA *= Aw[w];
+        GR = GR || Rw[w] != 0u;
       }
     };
 
@@ -682,7 +684,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
           const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch + cj] : 0.0f;
           float carry = init;
           if (t.chunk > 0) {
-            if (cj == 0 && lane == 0) lds_flag_set(&s_polls_out, i);
             float in[1] = {init}, out[1];
             if (!look_back_wave<1, K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(t_prv) * SW,
                                       static_cast<unsigned>(lane * V + cj), static_cast<long long>(rows) * SW,
@@ -701,8 +702,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
           s_carry[pb][lane * V + cj] = carry;
         }
       }
-      // the load wave starts once the polls are out (or there are none)
-      if (cj == 0 && lane == 0) lds_flag_set(&s_polls_out, i);
       // s_carry is written before the flag that releases the data waves
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (lane == 0) lds_flag_set(&s_carry_ready[cj], i);
@@ -713,6 +712,15 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
         const Tile t = tile_of(t_cur, 0);
         if (cur_ok) {
           lds_count_wait(&s_maps_in, NW * (i + 1));
+          // every map read first (one wait), then the prefixes written
+          float Aw[NW], Bw[NW];
+          unsigned Rw[NW];
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            Rw[w] = s_R[cb][w];
+            Aw[w] = s_A[cb][w][lane * V + cj];
+            Bw[w] = s_B[cb][w][lane * V + cj];
+          }
           float GA = 1.0f, GB = 0.0f;
           bool GR = false;
 #pragma unroll
@@ -720,12 +728,9 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
             s_PA[cb][w][lane * V + cj] = GA;
             s_PB[cb][w][lane * V + cj] = GB;
             if (cj == 0 && lane == 0) s_PR[cb][w] = GR ? 1u : 0u;
-            const bool Rw = s_R[cb][w] != 0u;
-            const float Aw = s_A[cb][w][lane * V + cj];
-            const float Bw = s_B[cb][w][lane * V + cj];
-            GB = Rw ? Bw : fmaf(Aw, GB, Bw);
-            GA *= Aw;
-            GR = GR || Rw;
+            GB = Rw[w] != 0u ? Bw[w] : fmaf(Aw[w], GB, Bw[w]);
+            GA *= Aw[w];
+            GR = GR || Rw[w] != 0u;
           }
           if (t.active && t.chunk < p.n_chunks - 1) {
             const size_t sidx = static_cast<size_t>(t_cur) * SW + static_cast<size_t>(lane) * V + cj;
@@ -748,7 +753,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
       unsigned long long ticket = 0;
       if (lane == 0 && cur_ok) ticket = atomicAdd(&p.hdr->counter, 1ull);
       if (nxt_ok) {
-        lds_flag_wait(&s_polls_out, i);
         load_tile(t_nxt, pb);
         tile_consts(t_nxt, pb, lam);
       }
