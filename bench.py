@@ -25,6 +25,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "RG-LRU fwd & fwd+bwd ms + % HBM peak, B=4 L=2048 W=2048 bf16"
 FWD_BYTES_PER_ELEM = {"bf16": 8, "f32": 16}    # read x, gate_x, gate_a; write h
@@ -201,15 +202,19 @@ def main():
     fwd_gbs = fb / (fwd_avg * 1e-3) / 1e9
     bwd_gbs = bb / (bwd_avg * 1e-3) / 1e9
     fb_gbs = (fb + bb) / (ms_per_step * 1e-3) / 1e9
-    traffic = fwd_traffic = None
+    tr = {}
     prof = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(prof):
-        with open(prof) as f:
-            tr = json.load(f)
         # bytes per call from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)
         # scaled by a copy of known size; refreshed whenever the kernels change
-        traffic = (tr.get(f"{wl.name}:bwd") or {}).get("bytes")
-        fwd_traffic = (tr.get(f"{wl.name}:fwd") or {}).get("bytes")
+        with open(prof) as f:
+            tr = json.load(f)
+
+    def measured(group):
+        return (tr.get(f"{wl.name}:{group}") or {}).get("bytes")
+
+    traffic = measured("bwd")
+    fwd_traffic = measured("fwd")
     out = {
         "metric": METRIC,
         "value": round(ms_per_step, 5),
@@ -268,11 +273,19 @@ def main():
         flops = 2 * 2 * T * W * wl.proj_block
         pf = float(np.mean(pfwd_ms))
         pbk = float(np.mean(pbwd_ms))
+        fwd_tf = flops / (pf * 1e-3) / 1e12
+        bwd_tf = 2 * flops / (pbk * 1e-3) / 1e12
         out["projection"] = {
             "fwd_ms": round(pf, 5), "bwd_ms": round(pbk, 5),
             "fwd_gbs": round(pf_bytes / (pf * 1e-3) / 1e9, 1), "bwd_gbs": round(pb_bytes / (pbk * 1e-3) / 1e9, 1),
-            "fwd_tflops": round(flops / (pf * 1e-3) / 1e12, 1), "bwd_tflops": round(2 * flops / (pbk * 1e-3) / 1e12, 1),
-            "mfma_peak_tflops": 2500.0,
+            "fwd_hbm_frac": round(pf_bytes / (pf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_hbm_frac": round(pb_bytes / (pbk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "fwd_tflops": round(fwd_tf, 1), "bwd_tflops": round(bwd_tf, 1),
+            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "fwd_mfma_frac": round(fwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "bwd_mfma_frac": round(bwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "fwd_algorithmic_bytes": pf_bytes, "bwd_algorithmic_bytes": pb_bytes,
+            "fwd_traffic": measured("proj_fwd"), "bwd_traffic": measured("proj_bwd"),
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp)

@@ -9,6 +9,12 @@
         (__amd_rocclr_copyBuffer) of CALIB_MIB MiB in the same run; prints a
         markdown table and a JSON object of bytes per dispatch
 
+    python -m gated_linear_recurrence_amd.rocpd_summary traffic-json FETCH.db WRITE.db CALIB_MIB WORKLOAD OUT.json SOURCE
+        the same figures summed per library call (forward scan, backward scan,
+        projection forward, projection backward) and merged into OUT.json
+        under "WORKLOAD:fwd", ":bwd", ":proj_fwd", ":proj_bwd" (the file
+        bench.py reads); SOURCE names the summary the figures come from
+
 Only the standard library is used; nothing here runs on the GPU.
 """
 from __future__ import annotations
@@ -56,7 +62,7 @@ def traffic(fetch_db: str, write_db: str, calib_mib: float):
            "|---|---|---|---|---|---|"]
     per = {}
     for name in sorted(set(fetch) | set(write), key=lambda n: -(fetch.get(n, (0, 0))[1] or 0)):
-        if name == COPY_KERNEL or not name.startswith("void rglru::"):
+        if name == COPY_KERNEL or "rglru::" not in name:
             continue
         fc, fv = fetch.get(name, (0, 0.0))
         wc, wv = write.get(name, (0, 0.0))
@@ -67,6 +73,36 @@ def traffic(fetch_db: str, write_db: str, calib_mib: float):
     return "\n".join(out), per
 
 
+# kernels of each library call (matched on the kernel name)
+GROUPS = {
+    "fwd": ("fwd_kernel<",),
+    "bwd": ("bwd_map_kernel<", "bwd_carry_kernel<", "bwd_main_kernel<", "bwd_dlam_kernel<"),
+    "proj_fwd": ("proj_fwd_kernel(",),
+    "proj_bwd": ("proj_dw_kernel(", "proj_dw_reduce_kernel(", "proj_dx_kernel<"),
+}
+
+
+def traffic_json(fetch_db: str, write_db: str, calib_mib: float, workload: str, out: str, source: str):
+    _, per = traffic(fetch_db, write_db, calib_mib)
+    try:
+        with open(out) as f:
+            doc = json.load(f)
+    except FileNotFoundError:
+        doc = {}
+    for group, keys in GROUPS.items():
+        names = [n for n in per if any(k in n for k in keys)]
+        if not names:
+            continue
+        rb = sum(per[n]["read_bytes"] for n in names)
+        wb = sum(per[n]["write_bytes"] for n in names)
+        doc[f"{workload}:{group}"] = {"bytes": rb + wb, "read_bytes": rb, "write_bytes": wb,
+                                      "kernels": sorted(names), "source": source}
+    with open(out, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    return doc
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "kernels":
         print(kernels(argv[1]))
@@ -75,6 +111,9 @@ def main(argv):
         print(table)
         print()
         print(json.dumps(per, indent=1))
+    elif len(argv) >= 7 and argv[0] == "traffic-json":
+        doc = traffic_json(argv[1], argv[2], float(argv[3]), argv[4], argv[5], argv[6])
+        print(json.dumps(doc, indent=1))
     else:
         print(__doc__)
         return 2
