@@ -33,8 +33,9 @@
 // The tag is 1 + the call counter kept in the workspace header; the workgroup
 // that finishes last advances it, so stale words of earlier calls can never
 // look ready and the workspace never needs clearing between calls. Tiles are
-// handed out by an atomic ticket in chunk order, so every tile a workgroup
-// waits on belongs to a workgroup that is already running.
+// taken in chunk order (a workgroup's first tile is its index, later ones come
+// from an atomic ticket), so every tile a workgroup waits on belongs to a
+// workgroup that is running or done.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -56,12 +57,6 @@ constexpr int kMaxStrip = 512;   // widest channel strip of any variant (64 lane
 
 // Widest vector (channels per lane) the forward and backward may use; the
 // host picks the widest one that divides W and matches the pointers' alignment.
-#ifndef RGLRU_FWD_DEPTH
-#define RGLRU_FWD_DEPTH 2
-#endif
-#ifndef RGLRU_FWD_GATE_GROUP
-#define RGLRU_FWD_GATE_GROUP 2
-#endif
 #ifndef RGLRU_FWD_LOOKBACK
 #define RGLRU_FWD_LOOKBACK 4
 #endif
@@ -599,11 +594,17 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     }
   };
 
+  // The first tile of workgroup g is tile g (the grid never exceeds the tile
+  // count; workgroups are dispatched in index order and are all resident, so
+  // every tile a look-back waits on still belongs to a running or finished
+  // workgroup), so its loads start at once, overlapping the first ticket's
+  // round trip. Later tickets come from the counter: ticket value k is tile
+  // gridDim.x + k.
+  const unsigned t_first = blockIdx.x;
   if (ctrl && cj == 0 && lane == 0) {
     const u64 v0 = atomicAdd(&p.hdr->counter, 1ull);
-    const u64 v1 = atomicAdd(&p.hdr->counter, 1ull);
-    s_tk[0] = static_cast<unsigned>(v0);
-    s_tk[1] = static_cast<unsigned>(v1);
+    s_tk[0] = t_first;
+    s_tk[1] = gridDim.x + static_cast<unsigned>(v0);
 #pragma unroll
     for (int q = 2; q < 8; ++q) s_tk[q] = p.n_tiles;
     s_tag = static_cast<unsigned>(v0 >> 32) + 1u;
@@ -611,19 +612,15 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     for (int j = 0; j < V; ++j) s_carry_ready[j] = -1;
     s_maps_in = 0;
   }
-  __syncthreads();
-  const unsigned tag = __builtin_amdgcn_readfirstlane(s_tag);
-  {
-    const unsigned t0 = __builtin_amdgcn_readfirstlane(s_tk[0]);
-    if (loader) {
-      float lam[V];
-      tile_lam(t0, lam);
-      if (t0 < p.n_tiles) load_tile(t0, 0);
-      tile_consts(t0, 0, lam);
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
+  if (loader) {
+    float lam[V];
+    tile_lam(t_first, lam);
+    if (t_first < p.n_tiles) load_tile(t_first, 0);
+    tile_consts(t_first, 0, lam);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
   __syncthreads();
+  const unsigned tag = __builtin_amdgcn_readfirstlane(s_tag);
 
   // One pipeline iteration. (cal, cu) receive t_i's (alpha, write) pairs,
   // (pal, pu) hold t_{i-1}'s. Tickets of a workgroup increase, so once t_{i-1}
@@ -759,7 +756,7 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       // every slot read later is written: a ticket while this workgroup
       // still draws them, past the last tile once it has stopped
-      if (lane == 0) s_tk[(i + 2) & 7] = cur_ok ? static_cast<unsigned>(ticket) : p.n_tiles;
+      if (lane == 0) s_tk[(i + 2) & 7] = cur_ok ? gridDim.x + static_cast<unsigned>(ticket) : p.n_tiles;
     } else {
       if (cur_ok) {
         const Tile t = tile_of(t_cur, wave);
@@ -896,9 +893,10 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     if (!iteration(i + 1, al1, u1, al0, u0)) break;
   }
   if (ctrl && cj == 0 && lane == 0) {
-    // every workgroup took 2 tickets past the last tile; the last one to
-    // finish re-arms the counter and advances the call tag
-    const unsigned taken = p.n_tiles + 2u * gridDim.x;
+    // every workgroup drew one ticket in its prologue and one per tile it
+    // processed; the last one to finish re-arms the counter and advances the
+    // call tag
+    const unsigned taken = p.n_tiles + gridDim.x;
     const unsigned prev = atomicAdd(&p.hdr->done, 1u);
     if (prev == gridDim.x - 1) {
       atomicExch(&p.hdr->done, 0u);
