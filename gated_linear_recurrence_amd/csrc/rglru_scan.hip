@@ -1503,9 +1503,9 @@ int pick_vec(int vmax, long long W, int io_bytes, std::initializer_list<const vo
 }
 
 
-// Number of workgroups of a persistent kernel: as many as fit on the device at once.
+// Workgroups of `kernel` that fit on the device at once (0 on a HIP error).
 template <typename Kern>
-unsigned persistent_grid(Kern kernel, int threads, unsigned n_tiles) {
+unsigned resident_blocks(Kern kernel, int threads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   int cus = 0;
@@ -1513,7 +1513,13 @@ unsigned persistent_grid(Kern kernel, int threads, unsigned n_tiles) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
   if (per_cu < 1) per_cu = 1;
-  const unsigned g = static_cast<unsigned>(cus) * static_cast<unsigned>(per_cu);
+  return static_cast<unsigned>(cus) * static_cast<unsigned>(per_cu);
+}
+
+// Number of workgroups of a persistent kernel: as many as fit on the device at once.
+template <typename Kern>
+unsigned persistent_grid(Kern kernel, int threads, unsigned n_tiles) {
+  const unsigned g = resident_blocks(kernel, threads);
   return g < n_tiles ? g : n_tiles;
 }
 
@@ -1559,19 +1565,22 @@ rglru_status_t dispatch_fwd(int T, int V, bool wide, FwdArgs a, hipStream_t stre
 
 template <typename IO, int V, int NW>
 rglru_status_t launch_bwd(BwdArgs a, hipStream_t stream) {
-  // chunks per workgroup: the main pass evaluates a row's decay constants once
-  // for four; the map pass, whose arithmetic and loads are both short, keeps
-  // more workgroups in different phases with two (measured: 17.5 us against
-  // 19.3 us with four and 20.3 us with one at B=4, L=2048, W=2048)
-  constexpr int CPB = 4;
+  // Chunks of one row per workgroup (the decay constants are evaluated once
+  // for them). The map pass takes two: more workgroups in different phases
+  // than with four, while one evaluates the constants for every chunk
+  // (B=4 L=2048 W=2048: 17.5 us, 19.3 with four, 20.3 with one; equal at
+  // B=8 L=4096 W=2560). The main pass takes four, or two when four would
+  // leave fewer than four rounds of resident workgroups, whose last round
+  // would run mostly empty (B=4 L=2048 W=2048: 1.3 rounds with four; 54.0 us
+  // with two against 57.8 with four, 58.3 with three, 62.0 with one; at
+  // B=8 L=4096 W=2560, 6.7 rounds: 245 us with four, 257 with two).
   constexpr int CPB_MAP = 2;
   a.n_strips = static_cast<int>(ceil_div(a.W, 64 * V));
   a.n_chunks = static_cast<int>(ceil_div(a.L, kCkpt * NW));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  const unsigned strips_rows = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  const dim3 map_grid(strips_rows, static_cast<unsigned>(ceil_div(a.n_chunks, CPB_MAP)));
-  const dim3 tiles_grid(strips_rows, static_cast<unsigned>(ceil_div(a.n_chunks, CPB)));
-  hipLaunchKernelGGL((bwd_map_kernel<IO, V, NW, CPB_MAP>), map_grid, dim3(NW * 64), 0, stream, a);
+  const unsigned rows = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
+  hipLaunchKernelGGL((bwd_map_kernel<IO, V, NW, CPB_MAP>), dim3(rows, static_cast<unsigned>(ceil_div(a.n_chunks, CPB_MAP))),
+                     dim3(NW * 64), 0, stream, a);
   rglru_status_t st = launch_status();
   if (st != RGLRU_OK) return st;
   const unsigned groups = static_cast<unsigned>(ceil_div(a.W, 64)) * static_cast<unsigned>(a.B);
@@ -1579,7 +1588,17 @@ rglru_status_t launch_bwd(BwdArgs a, hipStream_t stream) {
   st = launch_status();
   if (st != RGLRU_OK) return st;
   // three waves per SIMD: room for the per-step coefficients without spills
-  hipLaunchKernelGGL((bwd_main_kernel<IO, V, NW, 3, CPB>), tiles_grid, dim3(NW * 64), 0, stream, a);
+  auto main4 = bwd_main_kernel<IO, V, NW, 3, 4>;
+  const unsigned slots = resident_blocks(main4, NW * 64);
+  if (slots == 0) return RGLRU_ERR_HIP;
+  const unsigned groups4 = rows * static_cast<unsigned>(ceil_div(a.n_chunks, 4));
+  if (groups4 >= 4u * slots) {
+    hipLaunchKernelGGL(main4, dim3(rows, static_cast<unsigned>(ceil_div(a.n_chunks, 4))), dim3(NW * 64), 0, stream,
+                       a);
+  } else {
+    hipLaunchKernelGGL((bwd_main_kernel<IO, V, NW, 3, 2>), dim3(rows, static_cast<unsigned>(ceil_div(a.n_chunks, 2))),
+                       dim3(NW * 64), 0, stream, a);
+  }
   st = launch_status();
   if (st != RGLRU_OK) return st;
   hipLaunchKernelGGL((bwd_dlam_kernel<V>), dim3(static_cast<unsigned>(ceil_div(a.W, 64))), dim3(1024), 0,
