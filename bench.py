@@ -91,7 +91,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the scan shards by channel or batch with no exchange in the forward; see DESIGN.md)",
+              "(the scan shards by channel or batch with no exchange in the forward)",
               file=sys.stderr)
         sys.exit(2)
 
