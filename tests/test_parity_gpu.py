@@ -103,6 +103,17 @@ def test_full_size_pages_shape(gpu_lib, wid):
     _case(gpu_lib, wl, chans=ch)
 
 
+@pytest.mark.parametrize("chunk", [8, 16, 32])
+def test_full_size_short_chunks(gpu_lib, chunk):
+    # shorter forward tiles run several workgroups per CU, which take every
+    # tile from the ticket counter (a look-back must never wait on a tile of a
+    # workgroup that has not started); no wait may reach its spin limit
+    wl = W[1]
+    ch = sample_channels(wl.width, n=16)
+    _case(gpu_lib, wl, chunk=chunk, chans=ch, label=f"{wl.name} chunk {chunk}")
+    assert max(ws.error_bits() for ws in gpu_lib.ops._default_ws.values()) == 0
+
+
 @pytest.mark.parametrize("length", [32768, 32768 + 37])
 def test_full_size_long_sequence(gpu_lib, length):
     wl = W[3].resized(length=length)
