@@ -33,9 +33,8 @@
 // The tag is 1 + the call counter kept in the workspace header; the workgroup
 // that finishes last advances it, so stale words of earlier calls can never
 // look ready and the workspace never needs clearing between calls. Tiles are
-// taken in chunk order (a workgroup's first tile is its index, later ones come
-// from an atomic ticket), so every tile a workgroup waits on belongs to a
-// workgroup that is running or done.
+// taken in chunk order from an atomic ticket, so every tile a workgroup waits
+// on belongs to a workgroup that is running or done.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -382,7 +381,6 @@ struct FwdArgs {
   int n_chunks;
   unsigned n_tiles;
   float c;
-  int static_first;      // 1: a workgroup's first tile is its index (one workgroup per CU)
 };
 
 // Flags in LDS between the waves of a workgroup. Workgroup-scope relaxed
@@ -595,23 +593,14 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     }
   };
 
-  // Tiles come from the ticket counter, so every tile a look-back waits on
-  // belongs to a workgroup that is running or finished, whatever the
-  // residency. With one workgroup per CU (static_first), every workgroup of
-  // the grid is resident and the first tile of workgroup g is tile g: its
-  // loads start at once, overlapping the first ticket's round trip, and
-  // ticket value k is tile gridDim.x + k. Otherwise the load wave draws the
-  // first two tickets at once and ticket value k is tile k (the occupancy
-  // query can promise more workgroups per CU than the hardware places).
-  const bool sfirst = p.static_first != 0;
-  const unsigned tk_base = sfirst ? gridDim.x : 0u;
+  // Every tile comes from the ticket counter (ticket value k is tile k), so
+  // every tile a look-back waits on belongs to a workgroup that is running or
+  // finished, whatever the residency: no workgroup has to be resident for
+  // another to make progress (a static first tile per workgroup index would
+  // save about 0.6 us, but the occupancy query can promise more workgroups
+  // per CU than the hardware places, and other work may hold CUs). The load
+  // wave draws the first two tickets at once.
   if (ctrl && cj == 0 && lane == 0) {
-    if (sfirst) {
-      const u64 v0 = atomicAdd(&p.hdr->counter, 1ull);
-      s_tk[0] = blockIdx.x;
-      s_tk[1] = gridDim.x + static_cast<unsigned>(v0);
-      s_tag = static_cast<unsigned>(v0 >> 32) + 1u;
-    }
 #pragma unroll
     for (int q = 2; q < 8; ++q) s_tk[q] = p.n_tiles;
 #pragma unroll
@@ -619,17 +608,14 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     s_maps_in = 0;
   }
   if (loader) {
-    unsigned t_first = blockIdx.x;
-    if (!sfirst) {
-      u64 v0 = 0;
-      if (lane == 0) {
-        v0 = atomicAdd(&p.hdr->counter, 2ull);
-        s_tk[0] = static_cast<unsigned>(v0);
-        s_tk[1] = static_cast<unsigned>(v0) + 1u;
-        s_tag = static_cast<unsigned>(v0 >> 32) + 1u;
-      }
-      t_first = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v0));
+    u64 v0 = 0;
+    if (lane == 0) {
+      v0 = atomicAdd(&p.hdr->counter, 2ull);
+      s_tk[0] = static_cast<unsigned>(v0);
+      s_tk[1] = static_cast<unsigned>(v0) + 1u;
+      s_tag = static_cast<unsigned>(v0 >> 32) + 1u;
     }
+    const unsigned t_first = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v0));
     float lam[V];
     tile_lam(t_first, lam);
     if (t_first < p.n_tiles) load_tile(t_first, 0);
@@ -773,7 +759,7 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       // every slot read later is written: a ticket while this workgroup
       // still draws them, past the last tile once it has stopped
-      if (lane == 0) s_tk[(i + 2) & 7] = cur_ok ? tk_base + static_cast<unsigned>(ticket) : p.n_tiles;
+      if (lane == 0) s_tk[(i + 2) & 7] = cur_ok ? static_cast<unsigned>(ticket) : p.n_tiles;
     } else {
       if (cur_ok) {
         const Tile t = tile_of(t_cur, wave);
@@ -910,10 +896,10 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     if (!iteration(i + 1, al1, u1, al0, u0)) break;
   }
   if (ctrl && cj == 0 && lane == 0) {
-    // every workgroup drew one ticket in its prologue (two without a static
-    // first tile) and one per tile it processed; the last one to finish
-    // re-arms the counter and advances the call tag
-    const unsigned taken = p.n_tiles + (sfirst ? 1u : 2u) * gridDim.x;
+    // every workgroup drew two tickets in its prologue and one per tile it
+    // processed; the last one to finish re-arms the counter and advances the
+    // call tag
+    const unsigned taken = p.n_tiles + 2u * gridDim.x;
     const unsigned prev = atomicAdd(&p.hdr->done, 1u);
     if (prev == gridDim.x - 1) {
       atomicExch(&p.hdr->done, 0u);
@@ -1520,10 +1506,9 @@ int pick_vec(int vmax, long long W, int io_bytes, std::initializer_list<const vo
 }
 
 
-// Workgroups of `kernel` that fit on the device at once (0 on a HIP error),
-// and how many of them per CU.
+// Workgroups of `kernel` that fit on the device at once (0 on a HIP error).
 template <typename Kern>
-unsigned resident_blocks(Kern kernel, int threads, int* per_cu_out = nullptr) {
+unsigned resident_blocks(Kern kernel, int threads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   int cus = 0;
@@ -1531,7 +1516,6 @@ unsigned resident_blocks(Kern kernel, int threads, int* per_cu_out = nullptr) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
   if (per_cu < 1) per_cu = 1;
-  if (per_cu_out != nullptr) *per_cu_out = per_cu;
   return static_cast<unsigned>(cus) * static_cast<unsigned>(per_cu);
 }
 
@@ -1549,12 +1533,8 @@ rglru_status_t launch_fwd(FwdArgs a, hipStream_t stream) {
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
   auto kernel = fwd_kernel<IO, V, TS, NW, WIDE>;
   constexpr int threads = (NW + V + 1) * 64;
-  int per_cu = 0;
-  const unsigned slots = resident_blocks(kernel, threads, &per_cu);
-  if (slots == 0) return RGLRU_ERR_HIP;
-  const unsigned grid = slots < a.n_tiles ? slots : a.n_tiles;
-  // a static first tile needs every workgroup resident: one per CU
-  a.static_first = per_cu == 1 ? 1 : 0;
+  const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
+  if (grid == 0) return RGLRU_ERR_HIP;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
   return launch_status();
 }
