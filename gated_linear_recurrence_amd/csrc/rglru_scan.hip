@@ -212,19 +212,22 @@ __device__ __forceinline__ float sigmoid_f(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * z));
 }
 
-// 1 - e^l for l <= 0, given a = e^l. For l > ln 0.9 (a > 0.9, where 1 - a
-// would cancel) it is the Taylor series of -expm1(l) through l^5: the next
-// term is below 2e-8 relative for |l| < 0.106. Elsewhere 1 - a >= 0.1, so
-// the rounding of a costs at most about 1e-6 relative. The stationary factor
-// sqrt(1 - a^2) thus keeps float32 precision when a is close to 1.
-__device__ __forceinline__ float one_minus_exp(float l, float a) {
-  float q = 1.0f / 120.0f;
-  q = fmaf(q, l, 1.0f / 24.0f);
-  q = fmaf(q, l, 1.0f / 6.0f);
-  q = fmaf(q, l, 0.5f);
-  q = fmaf(q, l, 1.0f);
-  const float near0 = -l * q;
-  return (l > -0.10536052f) ? near0 : 1.0f - a;
+// 1 - 2^y for y <= 0, given a = 2^y. For y > log2 0.9 (a > 0.9, where 1 - a
+// would cancel) it is the Taylor series of -expm1(y ln 2) through y^5, with
+// the powers of ln 2 folded into the coefficients: the next term is below
+// 2e-8 relative for |y ln 2| < 0.106. Elsewhere 1 - a >= 0.1, so the rounding
+// of a costs at most about 1e-6 relative. The stationary factor sqrt(1 - a^2)
+// thus keeps float32 precision when a is close to 1. Taking the exponent in
+// base 2 (the argument exp2 already gets) saves a multiply per element.
+__device__ __forceinline__ float one_minus_exp2(float y, float a) {
+  constexpr double kLn2 = 0.6931471805599453;
+  float q = static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 * kLn2 / 120.0);
+  q = fmaf(q, y, static_cast<float>(kLn2 * kLn2 * kLn2 * kLn2 / 24.0));
+  q = fmaf(q, y, static_cast<float>(kLn2 * kLn2 * kLn2 / 6.0));
+  q = fmaf(q, y, static_cast<float>(kLn2 * kLn2 / 2.0));
+  q = fmaf(q, y, static_cast<float>(kLn2));
+  const float near0 = -y * q;
+  return (y > -0.15200309f) ? near0 : 1.0f - a;
 }
 
 // Per-channel decay constants: cs = -c * softplus(lambda), k2 = cs * log2 e.
@@ -458,7 +461,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
   __shared__ float s_B[2][NW][SW];
   __shared__ unsigned s_R[2][NW];
   __shared__ unsigned s_rmask[2][NW];
-  __shared__ float s_cs[2][SW];
   __shared__ float s_k2[2][SW];
   __shared__ float s_carry[2][SW];
   __shared__ float s_PA[2][NW][SW];  // composite of the maps of the waves before each wave
@@ -514,7 +516,6 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     for (int j = 0; j < V; ++j) {
       float cs = 0.0f, k2 = 0.0f;
       if (t.active) channel_consts(lam[j], p.c, cs, k2);
-      s_cs[buf][lane * V + j] = cs;
       s_k2[buf][lane * V + j] = k2;
     }
   };
@@ -769,12 +770,9 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
 #pragma unroll
           for (int k = 0; k < TS; ++k) rmask |= (k < t.nvalid && fl[k] != 0u) ? (1u << k) : 0u;
         }
-        float cs[V], k2[V];
+        float k2[V];
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-          cs[j] = s_cs[cb][lane * V + j];
-          k2[j] = s_k2[cb][lane * V + j];
-        }
+        for (int j = 0; j < V; ++j) k2[j] = s_k2[cb][lane * V + j];
         float A[V], Bv[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) {
@@ -795,8 +793,9 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
           for (int j = 0; j < V; ++j) {
             const float ig = sigmoid_f(gxv[j]);
             const float r = sigmoid_f(gav[j]);
-            const float a = __builtin_amdgcn_exp2f(k2[j] * r);
-            const float m = __builtin_amdgcn_sqrtf(one_minus_exp(cs[j] * r, a) * (1.0f + a));
+            const float y = k2[j] * r;
+            const float a = __builtin_amdgcn_exp2f(y);
+            const float m = __builtin_amdgcn_sqrtf(one_minus_exp2(y, a) * (1.0f + a));
             if (FULL) {
               cal[k][j] = a;
               cu[k][j] = m * ig * xv[j];
@@ -1266,9 +1265,9 @@ void bwd_main_kernel(BwdArgs p) {
     for (int j = 0; j < V; ++j) {
       const float i = sigmoid_f(gxv[j]);
       const float r = sigmoid_f(gav[j]);
-      const float l = cs[j] * r;
-      const float a = __builtin_amdgcn_exp2f(k2[j] * r);
-      const float w = one_minus_exp(l, a) * (1.0f + a);   // 1 - a^2
+      const float y = k2[j] * r;
+      const float a = __builtin_amdgcn_exp2f(y);
+      const float w = one_minus_exp2(y, a) * (1.0f + a);  // 1 - a^2
       const float rsq = __builtin_amdgcn_rsqf(w);          // 1 / m
       const float m = w * rsq;
       const float mult = rs ? 1.0f : m;
