@@ -1000,6 +1000,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_map_kernel(BwdArgs p) {
   constexpr int SW = 64 * V;
   using io = Io<IO, V>;
   using R_t = typename io::R;
+  using elem = typename io::elem;
   __shared__ float s_A[NW][SW];
   __shared__ float s_B[NW][SW];
   __shared__ unsigned s_R[NW];
@@ -1022,15 +1023,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_map_kernel(BwdArgs p) {
     const unsigned tile = static_cast<unsigned>(c) * rows + blockIdx.x;
     const BwdTile t = bwd_tile<V, NW>(p, tile, wave, lane);
     const unsigned rmask = reset_mask<NW>(p, t.rowbase, t.t0, t.nvalid, lane);
+    // wave-uniform row base plus the lane's 32-bit channel offset
+    const long long row0 = t.rowbase + t.t0;
     R_t rga[TS], rdh[TS];
 #pragma unroll
     for (int k = 0; k < TS; ++k) {
       rga[k] = R_t{};
       rdh[k] = R_t{};
       if (t.active && k < t.nvalid) {
-        const long long off = (t.rowbase + t.t0 + k) * W + t.ch;
-        rga[k] = io::load_nt(p.ga, off);
-        rdh[k] = io::load_nt(p.dh, off);
+        const long long ro = (row0 + k) * W;
+        rga[k] = io::load_nt32(static_cast<const elem*>(p.ga) + ro, static_cast<unsigned>(t.ch));
+        rdh[k] = io::load_nt32(static_cast<const elem*>(p.dh) + ro, static_cast<unsigned>(t.ch));
       }
     }
     float A[V], Bv[V];
@@ -1189,6 +1192,7 @@ void bwd_main_kernel(BwdArgs p) {
   constexpr int SW = 64 * V;
   using io = Io<IO, V>;
   using R_t = typename io::R;
+  using elem = typename io::elem;
 
   __shared__ float s_A[NW][SW];
   __shared__ float s_B[NW][SW];
@@ -1218,6 +1222,10 @@ void bwd_main_kernel(BwdArgs p) {
   const unsigned rmask = reset_mask<NW>(p, t.rowbase, t.t0, nvalid, lane);
   const size_t idx = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
 
+  // A step row is addressed as a wave-uniform base (scalar registers) plus
+  // the lane's 32-bit channel offset, so no per-lane 64-bit address math.
+  const long long row0 = t.rowbase + t.t0;
+  const unsigned lane_off = static_cast<unsigned>(t.ch);
   R_t rx[TS], rgx[TS], rga[TS], rdh[TS];
 #pragma unroll
   for (int k = 0; k < TS; ++k) {
@@ -1226,11 +1234,11 @@ void bwd_main_kernel(BwdArgs p) {
     rga[k] = R_t{};
     rdh[k] = R_t{};
     if (active && k < nvalid) {
-      const long long off = (t.rowbase + t.t0 + k) * W + t.ch;
-      rx[k] = io::load_nt(p.x, off);
-      rgx[k] = io::load_nt(p.gx, off);
-      rga[k] = io::load_nt(p.ga, off);
-      rdh[k] = io::load_nt(p.dh, off);
+      const long long ro = (row0 + k) * W;
+      rx[k] = io::load_nt32(static_cast<const elem*>(p.x) + ro, lane_off);
+      rgx[k] = io::load_nt32(static_cast<const elem*>(p.gx) + ro, lane_off);
+      rga[k] = io::load_nt32(static_cast<const elem*>(p.ga) + ro, lane_off);
+      rdh[k] = io::load_nt32(static_cast<const elem*>(p.dh) + ro, lane_off);
     }
   }
   float h[V], cin[V];
@@ -1251,7 +1259,10 @@ void bwd_main_kernel(BwdArgs p) {
   // the coefficients the reverse pass needs:
   //   g = G + dh;  dx = g*cx;  dgate_x = g*cgx;  dgate_a = g*cga;
   //   lambda-gradient partial += g*cl;  G <- alpha*g  (0 after a reset token)
-  // with dl = g * a*(h_prev - a*i*x/m) off reset tokens (0 on them).
+  // with dl = g * a*(h_prev - a*i*x/m) off reset tokens (0 on them), and
+  // dgate_a = dl * c_s * (1 - r) with dl = g*cl. (A copy of this arithmetic
+  // without the reset selects, for tiles without reset tokens, measured
+  // slower: the kernel is not bound by its arithmetic, and twice the code.)
   float cx[TS][V], cgx[TS][V], cga[TS][V], cl[TS][V], al[TS][V], dhv[TS][V];
 #pragma unroll
   for (int k = 0; k < TS; ++k) {
@@ -1276,10 +1287,9 @@ void bwd_main_kernel(BwdArgs p) {
       const float uw = mult * ix;
       h[j] = rs ? uw : fmaf(a, h[j], uw);
       cx[k][j] = mult * i;
-      cgx[k][j] = mult * ix * (1.0f - i);
-      const float rr = r * (1.0f - r);
-      cga[k][j] = z * cs[j] * rr;
+      cgx[k][j] = uw * (1.0f - i);
       cl[k][j] = z * r;
+      cga[k][j] = cl[k][j] * fmaf(-cs[j], r, cs[j]);
       al[k][j] = rs ? 0.0f : a;
     }
   }
@@ -1341,10 +1351,10 @@ void bwd_main_kernel(BwdArgs p) {
           dl_acc[j] = fmaf(g, cl[k][j], dl_acc[j]);
           G[j] = rs ? 0.0f : al[k][j] * g;
         }
-        const long long off = (t.rowbase + t.t0 + k) * W + t.ch;
-        io::store_nt(p.dx, off, io::pack(ox));
-        io::store_nt(p.dgx, off, io::pack(ogx));
-        io::store_nt(p.dga, off, io::pack(oga));
+        const long long ro = (row0 + k) * W;
+        io::store_nt32(static_cast<elem*>(p.dx) + ro, lane_off, io::pack(ox));
+        io::store_nt32(static_cast<elem*>(p.dgx) + ro, lane_off, io::pack(ogx));
+        io::store_nt32(static_cast<elem*>(p.dga) + ro, lane_off, io::pack(oga));
       }
     }
     if (t.chunk == 0 && wave == 0 && p.dh0 != nullptr) store_f32v<V>(p.dh0 + t.b * W + t.ch, G);
