@@ -1279,7 +1279,12 @@ void bwd_main_kernel(BwdArgs p) {
       const float y = k2[j] * r;
       const float a = __builtin_amdgcn_exp2f(y);
       const float w = one_minus_exp2(y, a) * (1.0f + a);  // 1 - a^2
-      const float rsq = __builtin_amdgcn_rsqf(w);          // 1 / m
+      // 1 / m. Below the smallest normal float, w comes from a logit under
+      // about -87 (r = 0 or subnormal, a = 1): m is then under 1e-19, every
+      // gradient through m vanishes in the limit, and v_rsq_f32 would read a
+      // subnormal w as 0 and return inf. Taking 1/m as 0 there keeps inf
+      // and inf * 0 out of the gradients.
+      const float rsq = w >= 1.17549435e-38f ? __builtin_amdgcn_rsqf(w) : 0.0f;
       const float m = w * rsq;
       const float mult = rs ? 1.0f : m;
       const float ix = i * xv[j];

@@ -94,6 +94,40 @@ def test_reset_at_t0_zeroes_dh0_and_ignores_h0(gpu_lib):
     compare(wl.io, gpu, run_oracle(inp))
 
 
+# ------------------------------------------------------------------ decay regimes and extreme logits
+
+@pytest.mark.parametrize("io,lo,hi", [("f32", 0.01, 0.999), ("bf16", 0.01, 0.999), ("f32", 1e-6, 0.5)])
+def test_wide_decay_range(gpu_lib, io, lo, hi):
+    # per-step decays a = u^r with u = exp(-8 softplus(lambda)) ~ U[lo, hi] fall
+    # on both sides of 0.9, where the kernels switch from the series for
+    # 1 - a to 1 - a itself; the default workloads keep every a above 0.9
+    wl = synth.dataclasses.replace(W[2].resized(batch=2, length=700, width=320), io=io, decay_lo=lo, decay_hi=hi)
+    _case(gpu_lib, wl, label=f"decays U[{lo}, {hi}] {io}")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_extreme_gate_logits(gpu_lib, io):
+    # logits far enough out that the float32 sigmoid saturates to exactly 0
+    # or 1: r = 0 gives a = 1 and 1 - a^2 = 0, where the backward's 1/m must
+    # not turn into inf * 0; the float64 oracle stays finite down to -700
+    wl = synth.dataclasses.replace(W[2].resized(batch=2, length=300, width=256), io=io)
+    inp = synth.make_inputs(wl)
+    rng = np.random.default_rng(7)
+    extremes = np.array([-600.0, -200.0, -100.0, -89.0, -88.0, -87.0, -86.0, -80.0, -40.0, -20.0,
+                         20.0, 40.0, 80.0, 100.0, 200.0, 600.0])
+    for name in ("gx", "ga"):
+        v = getattr(inp, name).value.copy()
+        mask = rng.random(v.shape) < 0.3
+        v[mask] = rng.choice(extremes, size=int(mask.sum()))
+        setattr(inp, name, synth.store(v, io))
+    d = DevInputs(inp)
+    gpu = run_gpu(gpu_lib, d)
+    for k in ("h", "dx", "dgx", "dga", "dlam", "dh0"):
+        assert torch.isfinite(gpu[k]).all(), k
+    ref = run_oracle(inp)
+    compare(io, gpu, ref, label=f"extreme logits {io}")
+
+
 # ------------------------------------------------------------------ full sizes, sampled channels
 
 @pytest.mark.parametrize("wid", [1, 2])
