@@ -128,6 +128,24 @@ def test_extreme_gate_logits(gpu_lib, io):
     compare(io, gpu, ref, label=f"extreme logits {io}")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_extreme_decay_parameters(gpu_lib, io):
+    # lambda far out on both sides: softplus(lambda) underflows (a = 1 at
+    # every step, m = 0: the state never moves from h0) or is large enough
+    # that a underflows to 0 (m = 1: the state is the latest write)
+    wl = synth.dataclasses.replace(W[2].resized(batch=2, length=260, width=192), io=io)
+    inp = synth.make_inputs(wl)
+    vals = np.array([-200.0, -100.0, -90.0, -60.0, -30.0, -12.0, 12.0, 30.0, 80.0, 200.0], dtype=np.float32)
+    idx = np.arange(0, wl.width, 7)[: 3 * len(vals)]
+    lam = inp.lam.copy()
+    lam[idx] = np.resize(vals, idx.size)
+    inp.lam = lam
+    gpu = run_gpu(gpu_lib, DevInputs(inp))
+    for k in ("h", "dx", "dgx", "dga", "dlam", "dh0"):
+        assert torch.isfinite(gpu[k]).all(), k
+    compare(io, gpu, run_oracle(inp), label=f"extreme lambda {io}")
+
+
 # ------------------------------------------------------------------ full sizes, sampled channels
 
 @pytest.mark.parametrize("wid", [1, 2])
