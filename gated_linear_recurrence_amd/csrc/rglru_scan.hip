@@ -272,6 +272,19 @@ struct Header {
   unsigned err;    // sticky error bits
 };
 
+// The high half of Header::counter counts calls; a forward tags the words it
+// publishes with that count + 1. The backward's words carry 0 in their high
+// half, so the count skips 0xFFFFFFFF: every tag lies in [1, 0xFFFFFFFF] and
+// repeats only after 2^32 - 1 calls. Run by the last workgroup of a call,
+// when no other workgroup of the call touches the header: the next call
+// starts with no tickets handed out.
+__device__ __forceinline__ void advance_call(Header* hdr) {
+  const u64 c = __hip_atomic_load(&hdr->counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned next = static_cast<unsigned>(c >> 32) + 1u;
+  if (next == 0xFFFFFFFFu) next = 0u;
+  __hip_atomic_store(&hdr->counter, static_cast<u64>(next) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Carry entering a tile, computed by one wave (the workgroup's control
 // wave). Each round polls the published words of the K nearest predecessors
 // (tiles of earlier chunks of the same row in the forward, later chunks in the
@@ -895,14 +908,12 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     if (!iteration(i + 1, al1, u1, al0, u0)) break;
   }
   if (ctrl && cj == 0 && lane == 0) {
-    // every workgroup drew two tickets in its prologue and one per tile it
-    // processed; the last one to finish re-arms the counter and advances the
-    // call tag
-    const unsigned taken = p.n_tiles + 2u * gridDim.x;
+    // every workgroup draws its last ticket before it counts itself done; the
+    // last one to finish re-arms the tickets and advances the call tag
     const unsigned prev = atomicAdd(&p.hdr->done, 1u);
     if (prev == gridDim.x - 1) {
       atomicExch(&p.hdr->done, 0u);
-      atomicAdd(&p.hdr->counter, (1ull << 32) - static_cast<u64>(taken));
+      advance_call(p.hdr);
     }
   }
 }
@@ -1385,7 +1396,7 @@ void bwd_main_kernel(BwdArgs p) {
     const unsigned prev = atomicAdd(&p.hdr->done, 1u);
     if (prev == gridDim.x * gridDim.y - 1) {
       atomicExch(&p.hdr->done, 0u);
-      atomicAdd(&p.hdr->counter, 1ull << 32);
+      advance_call(p.hdr);
     }
   }
 }

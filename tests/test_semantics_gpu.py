@@ -125,6 +125,35 @@ def test_shared_workspace_across_shapes_and_directions(gpu_lib):
     assert hdr[1] == 8                           # one call-counter step per launch
 
 
+def test_call_counter_wraps_without_tag_zero(gpu_lib):
+    # The forward tags its published words with the call count + 1 and the
+    # backward's words carry 0 in that half, so the count must never make a
+    # tag of 0. Start the count just below 2^32 and cross the wrap: every call
+    # must match a fresh workspace bitwise, and the count skips 0xFFFFFFFF.
+    inp = _inputs(B=2, L=700, W=256, doc=300.0)
+    d = DevInputs(inp)
+
+    def step(ws):
+        h, hl, ck = gpu_lib.rglru_fwd(d.x, d.gx, d.ga, d.lam, d.reset, d.h0, chunk=64, workspace=ws)
+        grads = gpu_lib.rglru_bwd(d.x, d.gx, d.ga, d.lam, d.reset, ck, d.dh, d.dh_last, chunk=64, workspace=ws)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (h, hl) + tuple(grads) if t is not None]
+
+    ref = step(gpu_lib.Workspace("cuda"))
+    ws = gpu_lib.Workspace("cuda")
+    ws.get(gpu_lib.rglru_workspace_bytes(gpu_lib.make_shape(2, 700, 256, torch.bfloat16, 64)))
+    ws.buf[4:8].view(torch.int32).fill_(np.int32(np.uint32(0xFFFFFFFB).view(np.int32)))
+    counts = []
+    for _ in range(4):
+        got = step(ws)
+        assert len(got) == len(ref) == 7
+        for g, r in zip(got, ref):
+            assert torch.equal(g, r)
+        counts.append(int(ws.buf[4:8].cpu().numpy().view(np.uint32)[0]))
+    assert counts == [0xFFFFFFFD, 0, 2, 4]
+    assert ws.error_bits() == 0
+
+
 def test_autograd_function(gpu_lib):
     inp = _inputs(B=2, L=130, W=128)
     d = DevInputs(inp)
