@@ -930,10 +930,10 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
 //                      entering every tile;
 //   bwd_main_kernel  : every tile independently recomputes the forward from
 //                      its checkpoints, runs the reverse pass from its carry
-//                      and writes dx, dgate_x, dgate_a and its lambda-gradient
-//                      partial;
-//   bwd_dlam_kernel  : sums each channel's partials over (chunk, batch row)
-//                      in a fixed order.
+//                      and writes dx, dgate_x and dgate_a; a workgroup (a few
+//                      chunks of one row) writes one lambda-gradient partial;
+//   bwd_dlam_kernel  : sums each channel's partials over (workgroup, batch
+//                      row) in a fixed order.
 // No workgroup waits for another, so the main pass streams at full occupancy.
 // The maps, carries and partials are stored as 64-bit slot words whose high
 // half is 0, a tag the forward never uses, so a forward sharing the workspace
@@ -957,13 +957,14 @@ struct BwdArgs {
   u64* map_a;            // per tile and channel: A of the reverse map (a reset in the sign bit)
   u64* map_b;            // B of the reverse map
   u64* carry;            // carry entering the tile's last step from the later chunks
-  u64* part;             // the tile's lambda-gradient partial
+  u64* part;             // a main-pass workgroup's lambda-gradient partial
   long long L;
   long long n_ckpt;
   int B;
   int W;
   int n_strips;
   int n_chunks;
+  int n_groups;          // main-pass workgroups per (batch row, strip): one partial each
   unsigned n_tiles;
   float c;
 };
@@ -1216,8 +1217,10 @@ void bwd_main_kernel(BwdArgs p) {
   const int c_begin = blockIdx.y * CPB;
   const int c_end = c_begin + CPB < p.n_chunks ? c_begin + CPB : p.n_chunks;
   float cs[V], k2[V];
+  bool lane_active;
   {
     const BwdTile t0 = bwd_tile<V, NW>(p, static_cast<unsigned>(c_begin) * rows + blockIdx.x, wave, lane);
+    lane_active = t0.active;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       cs[j] = 0.0f;
@@ -1225,6 +1228,10 @@ void bwd_main_kernel(BwdArgs p) {
       if (t0.active) channel_consts(p.lam[t0.ch + j], p.c, cs[j], k2[j]);
     }
   }
+  // this lane's lambda-gradient partial over all chunks of the workgroup
+  float dl_acc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) dl_acc[j] = 0.0f;
   for (int chunk = c_begin; chunk < c_end; ++chunk) {
   const unsigned tile = static_cast<unsigned>(chunk) * rows + blockIdx.x;
   const BwdTile t = bwd_tile<V, NW>(p, tile, wave, lane);
@@ -1329,7 +1336,7 @@ void bwd_main_kernel(BwdArgs p) {
       }
     }
   }
-  __syncthreads();   // the previous chunk's partials have been summed
+  __syncthreads();   // every wave is done with the previous chunk's maps
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     s_A[wave][lane * V + j] = A[j];
@@ -1338,9 +1345,6 @@ void bwd_main_kernel(BwdArgs p) {
   if (lane == 0) s_R[wave] = rmask != 0u ? 1u : 0u;
   __syncthreads();
 
-  float dl_acc[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) dl_acc[j] = 0.0f;
   if (active) {
     // carry at this wave's last step: the tile's carry through the later waves
     float G[V];
@@ -1376,20 +1380,23 @@ void bwd_main_kernel(BwdArgs p) {
     if (t.chunk == 0 && wave == 0 && p.dh0 != nullptr) store_f32v<V>(p.dh0 + t.b * W + t.ch, G);
   }
 
-  // the tile's lambda-gradient partial: fixed-order sum over the waves
+  }   // chunks
+
+  // the workgroup's lambda-gradient partial: each wave's sum over its
+  // chunks in order, then the waves in order (fixed order: deterministic)
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < V; ++j) s_A[wave][lane * V + j] = dl_acc[j];
   __syncthreads();
-  if (wave == 0 && active) {
+  if (wave == 0 && lane_active) {
+    const size_t gidx = (static_cast<size_t>(blockIdx.y) * rows + blockIdx.x) * SW + static_cast<size_t>(lane) * V;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       float s = 0.0f;
       for (int w = 0; w < NW; ++w) s += s_A[w][lane * V + j];
-      p.part[idx + j] = untagged(s);
+      p.part[gidx + j] = untagged(s);
     }
   }
-  }   // chunks
 
   // the last workgroup of the call advances the call counter
   if (threadIdx.x == 0) {
@@ -1402,7 +1409,8 @@ void bwd_main_kernel(BwdArgs p) {
 }
 
 // Lambda gradient: 64 channels per workgroup, NWR waves each summing a
-// contiguous run of (chunk, batch row) partials, then the runs in wave order.
+// contiguous run of (main-pass workgroup, batch row) partials, then the runs
+// in wave order.
 template <int V>
 __global__ __launch_bounds__(1024) void bwd_dlam_kernel(BwdArgs p) {
   constexpr int SW = 64 * V;
@@ -1414,7 +1422,7 @@ __global__ __launch_bounds__(1024) void bwd_dlam_kernel(BwdArgs p) {
   const bool active = ch < p.W;
   const int strip = ch / SW;
   const int cin = ch - strip * SW;
-  const int n_parts = p.n_chunks * p.B;
+  const int n_parts = p.n_groups * p.B;
   const int per = (n_parts + NWR - 1) / NWR;
   const int k0 = wave * per;
   const int k1 = k0 + per < n_parts ? k0 + per : n_parts;
@@ -1422,7 +1430,7 @@ __global__ __launch_bounds__(1024) void bwd_dlam_kernel(BwdArgs p) {
   if (active) {
 #pragma unroll 8
     for (int k = k0; k < k1; ++k) {
-      // k = chunk * B + b: tile (chunk, b, strip)
+      // k = group * B + b: main-pass workgroup (group, b, strip)
       const size_t q = (static_cast<size_t>(k) * p.n_strips + strip) * SW + cin;
       s += word_value(p.part[q]);
     }
@@ -1621,10 +1629,11 @@ rglru_status_t launch_bwd(BwdArgs a, hipStream_t stream) {
   if (slots == 0) return RGLRU_ERR_HIP;
   const unsigned groups4 = rows * static_cast<unsigned>(ceil_div(a.n_chunks, 4));
   if (groups4 >= 4u * slots) {
-    hipLaunchKernelGGL(main4, dim3(rows, static_cast<unsigned>(ceil_div(a.n_chunks, 4))), dim3(NW * 64), 0, stream,
-                       a);
+    a.n_groups = static_cast<int>(ceil_div(a.n_chunks, 4));
+    hipLaunchKernelGGL(main4, dim3(rows, static_cast<unsigned>(a.n_groups)), dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((bwd_main_kernel<IO, V, NW, 3, 2>), dim3(rows, static_cast<unsigned>(ceil_div(a.n_chunks, 2))),
+    a.n_groups = static_cast<int>(ceil_div(a.n_chunks, 2));
+    hipLaunchKernelGGL((bwd_main_kernel<IO, V, NW, 3, 2>), dim3(rows, static_cast<unsigned>(a.n_groups)),
                        dim3(NW * 64), 0, stream, a);
   }
   st = launch_status();
