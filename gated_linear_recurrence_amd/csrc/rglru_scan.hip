@@ -244,10 +244,6 @@ __device__ __forceinline__ void publish(u64* slot, size_t idx, unsigned tag, uin
   __hip_atomic_store(slot + idx, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ u64 poll(const u64* slot, size_t idx) {
-  return __hip_atomic_load(slot + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // poll at a wave-uniform slot pointer plus a per-lane byte offset
 __device__ __forceinline__ u64 poll_at(const u64* uniform_slot, unsigned lane_bytes) {
   gbyte* b = uniform_gptr(uniform_slot);
