@@ -154,7 +154,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Slab layouts in LDS: 32 rows of 512 bytes; the 16-byte granules of a row
 // are permuted so that the reads of one operand fall on distinct banks.
-//   kSwz16: granule g of row r at position g ^ (r % 8)   (16-byte row reads)
+//   kSwz16: granule g of row r at position g ^ (r % 16)  (16-byte row reads:
+//           16 rows at one granule, 512 bytes apart, fall on 16 distinct
+//           groups of 4 banks)
 //   kSwz32: 32-byte chunk c of row r at position c ^ (r % 16), granules
 //           within a chunk in order                      (transpose reads)
 // The map is an involution: it gives the source granule of a position too.
@@ -164,7 +166,7 @@ constexpr int kSwz32 = 1;
 template <int SWZ>
 __device__ __forceinline__ int swz_gran(int g, int r) {
   if constexpr (SWZ == kSwz16) {
-    return g ^ (r & 7);
+    return g ^ (r & 15);
   } else {
     return (((g >> 1) ^ (r & 15)) << 1) | (g & 1);
   }
