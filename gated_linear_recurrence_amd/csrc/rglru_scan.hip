@@ -927,7 +927,7 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
 // ------------------------------------------------------------------ backward
 //
 // The reverse recurrence g_t = dh_t + alpha_{t+1} g_{t+1} needs only the
-// decays and dh, not x or gate_x, so the backward runs as three launches:
+// decays and dh, not x or gate_x, so the backward runs as four launches:
 //   bwd_map_kernel   : each tile's reverse map G_out = A*G_in + B (carry
 //                      entering its first step from the carry entering its
 //                      last), from gate_a, lambda, the reset flags and dh;

@@ -40,8 +40,10 @@
  *    needed. One workspace may serve forward and backward calls of any shape
  *    (size it for the largest), but calls that use the same workspace must not
  *    overlap in time (same stream, or ordered by events).
- *    Layout of its first 16 bytes (read-only for callers): a 64-bit call
- *    counter, a 32-bit counter, and a 32-bit sticky error word whose bit 0 is
+ *    Layout of its first 16 bytes (read-only for callers): a 64-bit counter
+ *    (high half: completed calls, which skips 0xFFFFFFFF; low half: tiles
+ *    handed out during a forward), a 32-bit count of finished workgroups, and
+ *    a 32-bit sticky error word whose bit 0 is
  *    set if a look-back wait ever exceeded its spin limit (the outputs of that
  *    call are then invalid; it cannot happen while every launched workgroup
  *    makes progress).
