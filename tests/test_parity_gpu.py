@@ -94,6 +94,33 @@ def test_reset_at_t0_zeroes_dh0_and_ignores_h0(gpu_lib):
     compare(wl.io, gpu, run_oracle(inp))
 
 
+# ------------------------------------------------------------------ randomised small shapes
+
+def _random_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    io = ("f32", "bf16")[seed % 2]
+    B = int(rng.integers(1, 4))
+    L = int(rng.choice([1, 2, 7, 8, 9, 63, 64, 65, 257, int(rng.integers(10, 600)), int(rng.integers(600, 2000))]))
+    Wd = int(rng.choice([1, 2, 5, 64, 96, 127, 129, 200, int(rng.integers(1, 700))]))
+    chunk = int(rng.choice([0, 8, 16, 32, 64, 128, 256]))
+    doc = None if rng.random() < 0.3 else float(rng.choice([1.0, 3.0, 40.0, 500.0]))
+    lo = float(rng.choice([1e-3, 0.5, 0.9, 0.99]))
+    wl = synth.dataclasses.replace(W[2].resized(batch=B, length=L, width=Wd), io=io, doc_mean=doc,
+                                   h0=bool(rng.random() < 0.5), decay_lo=lo, decay_hi=min(0.9999, lo + 0.099))
+    return wl, chunk, bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_small_shapes(gpu_lib, seed):
+    # shapes, chunk lengths, io types, reset densities, decay ranges and the
+    # optional inputs drawn at random (fixed seeds), every case against the
+    # oracle on all channels
+    wl, chunk, dh_last = _random_case(seed)
+    _case(gpu_lib, wl, chunk=chunk, variant=seed, with_dh_last=dh_last,
+          label=f"seed {seed}: B={wl.batch} L={wl.length} W={wl.width} {wl.io} chunk {chunk} "
+                f"docs {wl.doc_mean} h0 {wl.h0} decays [{wl.decay_lo}, {wl.decay_hi}]")
+
+
 # ------------------------------------------------------------------ decay regimes and extreme logits
 
 @pytest.mark.parametrize("io,lo,hi", [("f32", 0.01, 0.999), ("bf16", 0.01, 0.999), ("f32", 1e-6, 0.5)])
