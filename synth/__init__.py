@@ -68,6 +68,10 @@ WORKLOADS = {
                 chunk=256),
     4: Workload(4, "blockdiag_b8_l4096_w2560", 8, 4096, 2560, "bf16", 0.9, 0.999, 1024.0, True,
                 proj_blocks=10, proj_block=256),
+    # the pages' measured scope at their shape: both gate projections (8
+    # blocks of 256, an assumed block count) and the scan, restricted contract
+    5: Workload(5, "restricted_proj_b4_l2048_w2048", 4, 2048, 2048, "bf16", 0.9, 0.999, None, False,
+                proj_blocks=8, proj_block=256),
 }
 
 

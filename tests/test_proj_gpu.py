@@ -95,9 +95,11 @@ def test_projection_full_size_sampled(gpu_lib):
             assert grad_err(host64(db[sl]), dg.value[:, sl].sum(0)) <= GRAD_TOL["bf16"], kb
 
 
-def test_projection_feeding_scan_end_to_end(gpu_lib):
-    """Projection -> scan -> scan backward -> projection backward, against the oracle composed the same way."""
-    wl = synth.WORKLOADS[4].resized(batch=2, length=300)
+@pytest.mark.parametrize("wid", [4, 5])
+def test_projection_feeding_scan_end_to_end(gpu_lib, wid):
+    """Projection -> scan -> scan backward -> projection backward, against the oracle composed the same way
+    (workload 4: resets and an initial state; 5: the restricted contract at width 2048)."""
+    wl = synth.WORKLOADS[wid].resized(batch=2, length=300)
     inp = synth.make_inputs(wl, with_dh_last=True)
     B, L, W = wl.batch, wl.length, wl.width
     d = DevInputs(inp)

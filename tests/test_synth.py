@@ -75,6 +75,7 @@ def test_workload_table_matches_the_stated_shapes():
     assert (w[2].doc_mean, w[2].h0) == (512.0, True)
     assert (w[3].batch, w[3].length, w[3].width, w[3].chunk, w[3].doc_mean) == (1, 32768, 4096, 256, 4096.0)
     assert (w[4].batch, w[4].length, w[4].width, w[4].proj_blocks, w[4].proj_block) == (8, 4096, 2560, 10, 256)
+    assert (w[5].batch, w[5].length, w[5].width, w[5].doc_mean, w[5].h0, w[5].proj_blocks) == (4, 2048, 2048, None, False, 8)
 
 
 def test_projection_weights_scale():
