@@ -924,6 +924,73 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
   }
 }
 
+// Short sequences (L <= kSerialMaxL, e.g. a decode step: L = 1 with h0 in
+// and h_last out): one thread per (batch row, V channels) runs the steps in
+// order. All of a thread's loads go out in one round trip and there is no
+// look-back, barrier or map composition, so the call costs about a launch
+// and one memory round trip. Same arithmetic as the tiled kernel; for these
+// lengths the tiled kernel also runs the steps as one serial fma chain from
+// h0, so the results are bitwise the same.
+constexpr int kSerialMaxL = 8;
+template <typename IO, int V>
+__global__ __launch_bounds__(256) void fwd_serial_kernel(FwdArgs p) {
+  using io = Io<IO, V>;
+  using R_t = typename io::R;
+  const long long groups = p.W / V;
+  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<long long>(p.B) * groups) return;
+  const int b = static_cast<int>(idx / groups);
+  const long long W = p.W;
+  const long long ch = (idx - static_cast<long long>(b) * groups) * V;
+  const long long rowbase = static_cast<long long>(b) * p.L;
+  R_t rx[kSerialMaxL], rgx[kSerialMaxL], rga[kSerialMaxL];
+  bool rs[kSerialMaxL];
+#pragma unroll
+  for (int k = 0; k < kSerialMaxL; ++k) {
+    rx[k] = R_t{};
+    rgx[k] = R_t{};
+    rga[k] = R_t{};
+    rs[k] = false;
+    if (k < p.L) {
+      const long long off = (rowbase + k) * W + ch;
+      rx[k] = io::load_nt(p.x, off);
+      rgx[k] = io::load_nt(p.gx, off);
+      rga[k] = io::load_nt(p.ga, off);
+      rs[k] = p.reset != nullptr && p.reset[rowbase + k] != 0;
+    }
+  }
+  float k2[V], h[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    float cs;
+    channel_consts(p.lam[ch + j], p.c, cs, k2[j]);
+    h[j] = p.h0 != nullptr ? p.h0[static_cast<long long>(b) * W + ch + j] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < kSerialMaxL; ++k) {
+    if (k < p.L) {
+      if (p.ckpt != nullptr && k % kCkpt == 0) {
+        store_f32v<V>(p.ckpt + (static_cast<long long>(b) * p.n_ckpt + k / kCkpt) * W + ch, h);
+      }
+      float xv[V], gxv[V], gav[V];
+      io::unpack(rx[k], xv);
+      io::unpack(rgx[k], gxv);
+      io::unpack(rga[k], gav);
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const float ig = sigmoid_f(gxv[j]);
+        const float r = sigmoid_f(gav[j]);
+        const float y = k2[j] * r;
+        const float a = __builtin_amdgcn_exp2f(y);
+        const float m = __builtin_amdgcn_sqrtf(one_minus_exp2(y, a) * (1.0f + a));
+        h[j] = rs[k] ? ig * xv[j] : fmaf(a, h[j], m * ig * xv[j]);
+      }
+      io::store_nt(p.h, (rowbase + k) * W + ch, io::pack(h));
+    }
+  }
+  if (p.h_last != nullptr) store_f32v<V>(p.h_last + static_cast<long long>(b) * W + ch, h);
+}
+
 // ------------------------------------------------------------------ backward
 //
 // The reverse recurrence g_t = dh_t + alpha_{t+1} g_{t+1} needs only the
@@ -1732,6 +1799,20 @@ rglru_status_t rglru_fwd(const rglru_shape_t* s, const void* x, const void* gate
                     aligned_to(gate_a, 16) && (s->io_dtype == RGLRU_IO_F32 || V >= 2) &&
                     static_cast<long long>(g.T) * s->width * g.io_bytes < (1ll << 31);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s->length <= kSerialMaxL) {
+    const unsigned grid = static_cast<unsigned>(ceil_div(s->batch * (s->width / V), 256));
+    if (s->io_dtype == RGLRU_IO_F32) {
+      hipLaunchKernelGGL((fwd_serial_kernel<F32, 1>), dim3(static_cast<unsigned>(ceil_div(s->batch * s->width, 256))),
+                         dim3(256), 0, st, a);
+    } else if (V >= 4) {
+      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 4>), dim3(grid), dim3(256), 0, st, a);
+    } else if (V == 2) {
+      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 2>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 1>), dim3(grid), dim3(256), 0, st, a);
+    }
+    return launch_status();
+  }
   if (s->io_dtype == RGLRU_IO_F32) return dispatch_fwd<F32>(g.T, 1, wide, a, st);
   return dispatch_fwd<BF16>(g.T, V, wide, a, st);
 }
