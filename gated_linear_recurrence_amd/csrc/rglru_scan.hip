@@ -403,113 +403,155 @@ struct FwdArgs {
   int n_chunks;
   unsigned n_tiles;
   float c;
+  bool h_wide;           // h rows start 16-byte aligned (W * sizeof(io) % 16 == 0, h aligned)
 };
 
-// Flags in LDS between the waves of a workgroup. Workgroup-scope relaxed
-// atomics on the LDS variable itself compile to plain ds_write / ds_read:
-// no wait on the issuing wave's global memory traffic.
-__device__ __forceinline__ void lds_flag_set(int* flag, int v) {
-  __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Flags in LDS between the waves of a workgroup: workgroup-scope relaxed
+// atomics on the LDS word itself, which compile to plain ds_write / ds_read
+// (no wait on the issuing wave's global memory traffic). A writer makes its
+// data visible first (lds_release: its LDS operations have completed, and the
+// compiler keeps them before the flag); a reader keeps its data reads after
+// the flag (lds_acquire).
+__device__ __forceinline__ int lds_load(const int* f) {
+  return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_flag_wait(int* flag, int v) {
-  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != v) __builtin_amdgcn_s_sleep(1);
+__device__ __forceinline__ void lds_store(int* f, int v) {
+  __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_count_add(int* count) {
-  __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+__device__ __forceinline__ void lds_add(int* f, int v) {
+  __hip_atomic_fetch_add(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void lds_count_wait(int* count, int v) {
-  while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < v) __builtin_amdgcn_s_sleep(1);
+__device__ __forceinline__ void lds_release() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_acquire() { asm volatile("" ::: "memory"); }
+
+// Bounded wait for an LDS word to reach v (EQ: equal; otherwise at least v).
+// A wait that reaches the spin limit sets bit 1 of the sticky error word and
+// the workgroup's abort word; once that is set every wait returns at once, so
+// the workgroup always drains and exits (the call's outputs are then invalid,
+// as the error word says).
+template <bool EQ>
+__device__ __forceinline__ void lds_wait(const int* f, int v, int* abort, Header* hdr) {
+  for (unsigned n = 0; n < kSpinLimit; ++n) {
+    const int c = lds_load(f);
+    if (EQ ? c == v : c >= v) {
+      lds_acquire();
+      return;
+    }
+    if (lds_load(abort) != 0) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  lds_store(abort, 1);
+  if ((threadIdx.x & 63) == 0) atomicOr(&hdr->err, 2u);
 }
 
 // s_waitcnt immediates (gfx9 layout: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 
-// Persistent, software-pipelined forward with a producer wave.
+// Persistent, software-pipelined forward.
 //
-// Waves 0 .. NW-1 are data waves: each owns TS steps of a tile for 64*V
-// channels. Waves NW .. NW+V-1 are control waves, one per channel of a lane
-// (control wave j handles channel lane*V + j), and wave NW+V is the load wave.
-// One barrier per iteration. In iteration i, with t_i the i-th ticket of this
-// workgroup:
-//   control waves : run the look-back of t_{i-1}, whose map went out during
-//                   the previous iteration, publish its outgoing carry and hand
-//                   the incoming one to the data waves through LDS; once every
-//                   data wave has reduced its steps of t_i, publish the map of
-//                   t_i;
-//   load wave     : take ticket t_{i+2}, stream the raw words (and reset
-//                   flags) of t_{i+1} from HBM straight into LDS
-//                   (global_load_lds), evaluate the per-channel decay
-//                   constants of t_{i+1} while they land, and wait for them;
-//   data waves    : evaluate the gates of t_i from LDS into registers as
-//                   (alpha, write) pairs, reduce their steps to an affine map
-//                   and report it, then wait for the carry of t_{i-1} and replay
-//                   it from the pairs kept since the previous iteration,
-//                   storing h.
-// A map is published part-way through the iteration that evaluates it and
-// looked back from at the start of the next, so the predecessors' words are
-// mostly visible by then. The data waves issue no loads and the control waves
-// only their polls, so no wave waits on memory traffic it does not need (the
-// vector memory counter retires in order). The only waits between waves
-// inside an iteration are one-directional LDS flags (data -> control for the
-// maps, control -> data for the carry), so they cannot deadlock.
+// A tile is one batch row b, a strip of 64 channels (one channel per lane) and
+// T = NW * TS steps. Tiles are handed out in chunk order by an atomic ticket,
+// so every tile a look-back waits on belongs to a workgroup that is running or
+// done. A workgroup has NW data waves (wave w owns steps w*TS .. w*TS+TS-1 of
+// every tile), two control waves and two load waves; there is no barrier
+// inside the pipeline, only one-directional LDS flags. With t_i the
+// workgroup's i-th tile:
+//   load wave i%2    : once every data wave has finished with LDS buffer i%2
+//                      (tile t_{i-2}), streams the raw words of t_i (x, gate_x,
+//                      gate_a and the reset flags) from HBM into it with
+//                      global_load_lds and evaluates the tile's decay
+//                      constants, so two tiles of loads are in flight while
+//                      the data waves compute a third. Load wave 0 draws the
+//                      tickets, two at a time and two iterations ahead, so a
+//                      workgroup's tiles come in ticket order;
+//   data waves       : in iteration i, evaluate the gates of t_i as (alpha,
+//                      write) pairs, reduce their steps to an affine map
+//                      h -> R ? B : A*h + B and report it, and in the same
+//                      straight-line block replay t_{i-2} from the pairs kept
+//                      since then (a ring of three tiles in registers) and its
+//                      incoming carry, storing h and the checkpoint. The
+//                      replay's serial fma chain hides in the gate arithmetic,
+//                      and the carry of t_{i-2} has had a whole iteration to
+//                      arrive;
+//   control wave i%2 : once every data wave has reported t_i, writes the
+//                      per-wave prefix maps the replay starts from, publishes
+//                      the tile's map, runs its look-back, publishes its
+//                      outgoing carry and hands the incoming one to the data
+//                      waves. Two control waves give each tile's publish and
+//                      look-back two iterations.
+// The data waves issue no global loads and the control waves only their
+// polls, so no wave waits behind memory traffic it does not need (the vector
+// memory counter retires in order).
 //
-// A staged step row is 256 bytes (64 lanes, 4 bytes each). WIDE loads move 16
-// bytes per lane, so one instruction fills 4 step rows and a tile takes
-// 3 * TS * NW / 4 of them (a wave can have at most 63 in flight); otherwise
-// each instruction fills one row with 2 or 4 bytes per lane (every lane still
-// gets its own 4-byte slot, the value zero-extended).
-template <typename IO, int V, int TS, int NW, bool WIDE>
-__global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
-  static_assert((TS * NW) % kCkpt == 0 && (TS % kCkpt == 0 || kCkpt % TS == 0),
-                "checkpoint steps fall on wave boundaries");
-  static_assert(TS <= 32, "reset flags of a wave's steps fit one mask word");
-  using io = Io<IO, V>;
-  using R_t = typename io::R;
-  using elem = typename io::elem;
-  constexpr int SW = 64 * V;
-  constexpr int T = TS * NW;
+// LDS rows: WIDE loads move 16 bytes per lane, so one instruction fills 1 KiB
+// of consecutive step rows (8 rows of 64 bf16 channels, 4 of 64 float32); a
+// row in LDS is then 64 * sizeof(io) bytes. Otherwise each instruction fills
+// one row with 2 or 4 bytes per lane, each lane's value zero-extended into its
+// own 4-byte slot (rows of 256 bytes).
+template <typename IO, int NW, int TS, bool WIDE>
+__global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
+  using elem = typename IO::elem;
+  using io = Io<IO, 1>;
+  constexpr bool BF = std::is_same<IO, BF16>::value;
+  constexpr int ES = static_cast<int>(sizeof(elem));
+  constexpr int T = NW * TS;
+  constexpr int ROWB = WIDE ? 64 * ES : 256;
+  constexpr int SEG = ROWB / 16;           // 16-byte segments per row (WIDE)
+  constexpr int RPI = 64 / SEG;            // rows per 16-byte-per-lane instruction (WIDE)
   constexpr int K = RGLRU_FWD_LOOKBACK;
-  constexpr int LOAD_BYTES = static_cast<int>(sizeof(R_t));
-  static_assert(LOAD_BYTES == 2 || LOAD_BYTES == 4, "one or two channels of 2 or 4 bytes per lane");
-  static_assert(!WIDE || (LOAD_BYTES == 4 && TS % 4 == 0), "wide loads fill 4 rows of 64 four-byte slots");
-  static_assert(!WIDE || 3 * T / 4 + (T + 63) / 64 <= 63, "a tile's wide loads fit the vector memory counter");
+  constexpr int RING = 16;
+  constexpr int NFL = T < 64 ? 64 : T;     // reset-flag slots per buffer (one instruction fills 64)
+  constexpr int CTRL0 = NW, LOAD0 = NW + 2;
+  static_assert(TS % kCkpt == 0, "checkpoints fall on wave boundaries, at compile-time steps of a wave");
+  static_assert(TS <= 32 && NW <= 32, "reset flags of a wave's steps, and of the waves, fit one mask word");
+  static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
+  static_assert(NFL % 64 == 0 && NFL <= 128, "reset flags: at most two instructions");
 
-  __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][3][NW][TS][256];
-  __shared__ __attribute__((aligned(16))) unsigned char s_flag[2][(T < 64 ? 64 : T) * 4];
-  __shared__ float s_A[2][NW][SW];
-  __shared__ float s_B[2][NW][SW];
-  __shared__ unsigned s_R[2][NW];
-  __shared__ unsigned s_rmask[2][NW];
-  __shared__ float s_k2[2][SW];
-  __shared__ float s_carry[2][SW];
-  __shared__ float s_PA[2][NW][SW];  // composite of the maps of the waves before each wave
-  __shared__ float s_PB[2][NW][SW];
-  __shared__ unsigned s_PR[2][NW];
-  __shared__ unsigned s_tk[8];
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][3][T][ROWB];
+  __shared__ unsigned s_rflag[2][NFL];
+  __shared__ float s_k2[2][64];
+  // per map slot (iteration % 3): the data waves' maps, the prefixes the
+  // replay starts from and the tile's incoming carry
+  __shared__ float s_A[3][NW][64];
+  __shared__ float s_B[3][NW][64];
+  __shared__ unsigned s_R[3][NW];
+  __shared__ float s_PA[3][NW][64];   // composite of the maps of the waves before each wave
+  __shared__ float s_PB[3][NW][64];
+  __shared__ unsigned s_PRm[3];       // bit w: a reset inside the waves before wave w
+  __shared__ float s_carry[3][64];
+  __shared__ __attribute__((aligned(16))) elem s_hst[NW][TS * 64];   // a wave's h rows, staged for 16-byte stores
+  __shared__ unsigned s_tk[RING];     // tile of iteration i in s_tk[i % RING]
   __shared__ unsigned s_tag;
-  __shared__ int s_carry_ready[V];   // iteration whose carry (channel j) is in s_carry
-  __shared__ int s_maps_in;          // data-wave maps reported so far (NW per iteration)
+  __shared__ int s_tk_valid;          // highest iteration whose ticket is in s_tk
+  __shared__ int s_full[2];           // iteration whose raw words buffer j holds
+  __shared__ int s_cons[2];           // data waves done with buffer j so far
+  __shared__ int s_maps_in[3];        // data-wave maps reported for iterations of each slot so far
+  __shared__ int s_carry_ok[3];       // iteration whose incoming carry slot s holds
+  __shared__ int s_abort;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool ctrl = wave >= NW && wave < NW + V;
-  const int cj = ctrl ? wave - NW : 0;           // channel of a lane a control wave handles
-  const bool loader = wave == NW + V;
   const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
   const long long W = p.W;
-  // The control and load waves do little arithmetic but sit on the critical
-  // path (look-back, loads); each shares a SIMD with two data waves whose
-  // gate arithmetic would otherwise take nearly all of its issue slots.
-  if (ctrl || loader) __builtin_amdgcn_s_setprio(3);
+
+  if (threadIdx.x == 0) {
+    s_tk_valid = -1;
+    s_full[0] = s_full[1] = -1;
+    s_cons[0] = s_cons[1] = 0;
+    s_maps_in[0] = s_maps_in[1] = s_maps_in[2] = 0;
+    s_carry_ok[0] = s_carry_ok[1] = s_carry_ok[2] = -1;
+    s_abort = 0;
+  }
+  __syncthreads();
 
   struct Tile {
-    int chunk, b, strip, ch, nvalid;
-    long long t0, rowbase;
     bool valid, active;
+    int chunk, b, strip, ch;
+    long long t0, rowbase;
   };
   // Lambdas capture by value: a by-reference capture of the kernel arguments
   // takes their address and moves them to scratch memory.
-  auto tile_of = [=](unsigned tile, int w) {
+  auto tile_of = [=](unsigned tile) {
     Tile t;
     t.valid = tile < p.n_tiles;
     const unsigned tt = t.valid ? tile : 0u;
@@ -517,405 +559,412 @@ __global__ __launch_bounds__((NW + V + 1) * 64) void fwd_kernel(FwdArgs p) {
     const int row = static_cast<int>(tt - static_cast<unsigned>(t.chunk) * rows);
     t.b = row / p.n_strips;
     t.strip = row - t.b * p.n_strips;
-    t.ch = t.strip * SW + lane * V;
+    t.ch = t.strip * 64 + lane;
     t.active = t.ch < p.W;
-    t.t0 = static_cast<long long>(t.chunk) * T + static_cast<long long>(w) * TS;
-    const long long rem = p.L - t.t0;
-    t.nvalid = rem <= 0 ? 0 : (rem >= TS ? TS : static_cast<int>(rem));
+    t.t0 = static_cast<long long>(t.chunk) * T;
     t.rowbase = static_cast<long long>(t.b) * p.L;
     return t;
   };
+  auto ticket_tile = [=](u64 v, unsigned k) {
+    const unsigned q = static_cast<unsigned>(v) + k;
+    return q < p.n_tiles ? q : p.n_tiles;
+  };
 
-  // load wave: decay constants of channels lane*V .. +V-1 of a tile, from
-  // their lambda values
-  auto tile_consts = [=](unsigned tile, int buf, const float (&lam)[V]) {
-    const Tile t = tile_of(tile, 0);
-    if (!t.valid) return;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      float cs = 0.0f, k2 = 0.0f;
-      if (t.active) channel_consts(lam[j], p.c, cs, k2);
-      s_k2[buf][lane * V + j] = k2;
+  if (wave >= LOAD0) {
+    // ------------------------------------------------------------ load waves
+    __builtin_amdgcn_s_setprio(3);
+    const int j = wave - LOAD0;
+    if (j == 0) {
+      u64 v = 0;
+      if (lane == 0) v = atomicAdd(&p.hdr->counter, 2ull);
+      v = uniform_u64(v);
+      if (lane == 0) {
+        s_tk[0] = ticket_tile(v, 0);
+        s_tk[1] = ticket_tile(v, 1);
+        s_tag = static_cast<unsigned>(v >> 32) + 1u;
+      }
+      lds_release();
+      if (lane == 0) lds_store(&s_tk_valid, 1);
     }
-  };
-  auto tile_lam = [=](unsigned tile, float (&lam)[V]) {
-    const Tile t = tile_of(tile, 0);
-#pragma unroll
-    for (int j = 0; j < V; ++j) lam[j] = (t.valid && t.active) ? p.lam[t.ch + j] : 0.0f;
-  };
-
-  // load wave: every data wave's raw words of a tile, and the tile's reset
-  // flags, into LDS buffer `buf`. Words past W (last strip only) re-read the
-  // strip's first word and steps past L re-read row L-1; those words are never
-  // used, so every source address stays in bounds.
-  auto load_tile = [=](unsigned tile, int buf) {
-    const Tile t = tile_of(tile, 0);
     const unsigned char* src[3] = {static_cast<const unsigned char*>(p.x), static_cast<const unsigned char*>(p.gx),
                                    static_cast<const unsigned char*>(p.ga)};
-    const long long row_bytes = W * static_cast<long long>(sizeof(elem));
-    const long long strip_b = static_cast<long long>(t.strip) * 256;
-    if constexpr (WIDE) {
-      // lane l: step row l / 16 of a group of 4, bytes (l % 16) * 16 .. +15 of
-      // it. The per-lane offset from the tile's first word is fixed; a group's
-      // row offset is wave-uniform and goes into the scalar base (the host
-      // keeps a tile's rows under 2 GiB).
-      const unsigned col = strip_b + (lane & 15) * 16 < row_bytes ? static_cast<unsigned>((lane & 15) * 16) : 0u;
+    const long long row_bytes = W * ES;
+    for (int i = j;; i += 2) {
+      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      const Tile t = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
+      // buffer j is free once every data wave is done with iteration i - 2
+      lds_wait<false>(&s_cons[j], NW * (i / 2), &s_abort, p.hdr);
+      if (lds_load(&s_abort) != 0) break;
+      if (!t.valid) {
+        if (lane == 0) lds_store(&s_full[j], i);
+        break;
+      }
+      const float lam = t.active ? p.lam[t.ch] : 0.0f;
+      const long long strip_b = static_cast<long long>(t.strip) * 64 * ES;
       const long long tile_off = (t.rowbase + t.t0) * row_bytes + strip_b;
-      if (t.t0 + T <= p.L) {
-        const unsigned lane_off = static_cast<unsigned>(lane >> 4) * static_cast<unsigned>(row_bytes) + col;
+      const long long lim = p.L - 1 - t.t0;   // last step row of the tile inside the sequence
+      if constexpr (WIDE) {
+        // lane l: row l / SEG of each group of RPI rows, bytes (l % SEG) * 16
+        // .. +15 of it. Segments past W (last strip only) re-read the strip's
+        // first segment and rows past L re-read row L - 1; those words are
+        // never used, so every source address stays in bounds.
+        const int r = lane / SEG;
+        const unsigned seg = static_cast<unsigned>(lane % SEG) * 16u;
+        const unsigned col = strip_b + seg < row_bytes ? seg : 0u;
+        if (t.t0 + T <= p.L) {
+          // one scalar base per input, the lane's row and segment as a 32-bit
+          // offset that steps by RPI rows per instruction (the host keeps a
+          // tile's rows under 2 GiB)
+          const unsigned step = static_cast<unsigned>(RPI) * static_cast<unsigned>(row_bytes);
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          for (int w = 0; w < NW; ++w) {
+          for (int q = 0; q < 3; ++q) {
+            gbyte* base = uniform_gptr(src[q] + tile_off);
+            unsigned off = static_cast<unsigned>(r) * static_cast<unsigned>(row_bytes) + col;
+            unsigned char* dst = &s_raw[j][q][0][0];
+#pragma unroll 4
+            for (int g = 0; g < T / RPI; ++g) {
+              lds_dma16(base + off, dst);
+              off += step;
+              dst += 1024;
+            }
+          }
+        } else {
 #pragma unroll
-            for (int k = 0; k < TS; k += 4) {
-              const long long grp = tile_off + static_cast<long long>(w * TS + k) * row_bytes;
-              lds_dma16(uniform_gptr(src[q] + grp) + lane_off, &s_raw[buf][q][w][k][0]);
+          for (int q = 0; q < 3; ++q) {
+            gbyte* base = uniform_gptr(src[q] + tile_off);
+            for (int g = 0; g < T / RPI; ++g) {
+              const long long row = g * RPI + r;
+              const long long off = (row < lim ? row : lim) * row_bytes + col;
+              lds_dma16(base + off, &s_raw[j][q][g * RPI][0]);
             }
           }
         }
       } else {
-        const long long lim = p.L - 1 - t.t0;
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          gbyte* base = uniform_gptr(src[q] + tile_off);
-          for (int w = 0; w < NW; ++w) {
-#pragma unroll
-            for (int k = 0; k < TS; k += 4) {
-              const int sr = w * TS + k + (lane >> 4);
-              const unsigned off = static_cast<unsigned>(sr < lim ? sr : lim) * static_cast<unsigned>(row_bytes) + col;
-              lds_dma16(base + off, &s_raw[buf][q][w][k][0]);
-            }
-          }
-        }
-      }
-    } else {
-      const long long col = strip_b / (4 / LOAD_BYTES) + (t.active ? lane * LOAD_BYTES : 0);
-      for (int w = 0; w < NW; ++w) {
-#pragma unroll
-        for (int k = 0; k < TS; ++k) {
-          const long long st = t.t0 + w * TS + k;
-          const long long tk = st < p.L ? st : p.L - 1;
-          const long long off = (t.rowbase + tk) * row_bytes + col;
+        const unsigned col = t.active ? static_cast<unsigned>(lane * ES) : 0u;
+#pragma unroll 4
+        for (int k = 0; k < T; ++k) {
+          const long long row = k < lim ? k : lim;
 #pragma unroll
           for (int q = 0; q < 3; ++q) {
-            __builtin_amdgcn_global_load_lds(src[q] + off, &s_raw[buf][q][w][k][0], LOAD_BYTES, 0, 0);
+            gbyte* base = uniform_gptr(src[q] + tile_off + row * row_bytes);
+            __builtin_amdgcn_global_load_lds(const_cast<gbyte_w*>(base + col), &s_raw[j][q][k][0], ES, 0, 0);
           }
         }
       }
-    }
-    if (p.reset != nullptr) {
+      if (p.reset != nullptr) {
 #pragma unroll
-      for (int h = 0; h < (T + 63) / 64; ++h) {
-        const long long st = t.t0 + h * 64 + lane;
-        const long long tk = st < p.L ? st : p.L - 1;
-        __builtin_amdgcn_global_load_lds(p.reset + t.rowbase + tk, &s_flag[buf][h * 256], 1, 0, 0);
-      }
-    }
-  };
-
-  // Every tile comes from the ticket counter (ticket value k is tile k), so
-  // every tile a look-back waits on belongs to a workgroup that is running or
-  // finished, whatever the residency: no workgroup has to be resident for
-  // another to make progress (a static first tile per workgroup index would
-  // save about 0.6 us, but the occupancy query can promise more workgroups
-  // per CU than the hardware places, and other work may hold CUs). The load
-  // wave draws the first two tickets at once.
-  if (ctrl && cj == 0 && lane == 0) {
-#pragma unroll
-    for (int q = 2; q < 8; ++q) s_tk[q] = p.n_tiles;
-#pragma unroll
-    for (int j = 0; j < V; ++j) s_carry_ready[j] = -1;
-    s_maps_in = 0;
-  }
-  if (loader) {
-    u64 v0 = 0;
-    if (lane == 0) {
-      v0 = atomicAdd(&p.hdr->counter, 2ull);
-      s_tk[0] = static_cast<unsigned>(v0);
-      s_tk[1] = static_cast<unsigned>(v0) + 1u;
-      s_tag = static_cast<unsigned>(v0 >> 32) + 1u;
-    }
-    const unsigned t_first = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v0));
-    float lam[V];
-    tile_lam(t_first, lam);
-    if (t_first < p.n_tiles) load_tile(t_first, 0);
-    tile_consts(t_first, 0, lam);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  }
-  __syncthreads();
-  const unsigned tag = __builtin_amdgcn_readfirstlane(s_tag);
-
-  // One pipeline iteration. (cal, cu) receive t_i's (alpha, write) pairs,
-  // (pal, pu) hold t_{i-1}'s. Tickets of a workgroup increase, so once t_{i-1}
-  // is past the last tile every later one is too; t_{i+1} was taken in the
-  // previous iteration whenever t_i is a tile.
-  auto iteration = [=](int i, float (&cal)[TS][V], float (&cu)[TS][V], float (&pal)[TS][V],
-                       float (&pu)[TS][V]) -> bool {
-    const unsigned t_cur = __builtin_amdgcn_readfirstlane(s_tk[i & 7]);
-    const unsigned t_nxt = __builtin_amdgcn_readfirstlane(s_tk[(i + 1) & 7]);
-    const unsigned t_prv = i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i + 7) & 7]) : p.n_tiles;
-    const bool cur_ok = t_cur < p.n_tiles;
-    const bool prv_ok = t_prv < p.n_tiles;
-    if (!cur_ok && !prv_ok) return false;
-    const bool nxt_ok = cur_ok && t_nxt < p.n_tiles;
-    const int cb = i & 1;    // raw words, constants, maps and carry of t_i
-    const int pb = cb ^ 1;   // maps and carry of t_{i-1}; raw words and constants of t_{i+1}
-    // Waves that evaluate no gates still define (cal, cu): their previous
-    // contents are dead, and leaving them undefined on some paths would keep
-    // them alive and cost whole-array register copies.
-    auto clear = [&cal, &cu]() {
-#pragma unroll
-      for (int k = 0; k < TS; ++k) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          cal[k][j] = 0.0f;
-          cu[k][j] = 0.0f;
+        for (int h = 0; h < NFL / 64; ++h) {
+          const long long st = h * 64 + lane;
+          const long long tk = t.t0 + (st < lim ? st : lim);
+          __builtin_amdgcn_global_load_lds(p.reset + t.rowbase + tk, &s_rflag[j][h * 64], 1, 0, 0);
         }
       }
-    };
-    // composite map of a whole tile, channel lane*V + cj, from its waves' maps
-    // (every LDS read is issued before the first use: one wait, not NW)
-    auto tile_map = [=](int mb, float& GA, float& GB, bool& GR) {
+      // the next two tickets, two iterations ahead (load wave 0 draws them all,
+      // so a workgroup's tiles come in ticket order)
+      u64 nxt = 0;
+      if (j == 0 && lane == 0) nxt = atomicAdd(&p.hdr->counter, 2ull);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      {
+        float cs = 0.0f, k2 = 0.0f;
+        if (t.active) channel_consts(lam, p.c, cs, k2);
+        s_k2[j][lane] = k2;
+      }
+      if (j == 0) {
+        nxt = uniform_u64(nxt);
+        if (lane == 0) {
+          s_tk[(i + 2) % RING] = ticket_tile(nxt, 0);
+          s_tk[(i + 3) % RING] = ticket_tile(nxt, 1);
+        }
+      }
+      lds_release();
+      if (lane == 0) {
+        if (j == 0) lds_store(&s_tk_valid, i + 3);
+        lds_store(&s_full[j], i);
+      }
+    }
+  } else if (wave >= CTRL0) {
+    // ------------------------------------------------------------ control waves
+    __builtin_amdgcn_s_setprio(3);
+    const int c = wave - CTRL0;
+    unsigned tag = 0;
+    for (int i = c;; i += 2) {
+      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      if (lds_load(&s_abort) != 0) break;
+      if (i == c) tag = __builtin_amdgcn_readfirstlane(s_tag);
+      const unsigned tile = __builtin_amdgcn_readfirstlane(s_tk[i % RING]);
+      if (tile >= p.n_tiles) break;
+      const int ms = i % 3;
+      // once every data wave has reported its map of t_i: the prefixes the
+      // replay starts from and the tile's map. A data wave may report up to
+      // two iterations ahead of another (its replay of t_{i-2} waits for the
+      // carry of t_{i-2}), so the reports are counted per slot of three.
+      lds_wait<false>(&s_maps_in[ms], NW * (i / 3 + 1), &s_abort, p.hdr);
+      if (lds_load(&s_abort) != 0) break;
       float Aw[NW], Bw[NW];
       unsigned Rw[NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        Rw[w] = s_R[mb][w];
-        Aw[w] = s_A[mb][w][lane * V + cj];
-        Bw[w] = s_B[mb][w][lane * V + cj];
+        Rw[w] = s_R[ms][w];
+        Aw[w] = s_A[ms][w][lane];
+        Bw[w] = s_B[ms][w][lane];
       }
-      GA = 1.0f;
-      GB = 0.0f;
-      GR = false;
+      float GA = 1.0f, GB = 0.0f;
+      bool GR = false;
+      unsigned prbits = 0u;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
+        s_PA[ms][w][lane] = GA;
+        s_PB[ms][w][lane] = GB;
+        prbits |= GR ? (1u << w) : 0u;
         GB = Rw[w] != 0u ? Bw[w] : fmaf(Aw[w], GB, Bw[w]);
         GA *= Aw[w];
         GR = GR || Rw[w] != 0u;
       }
+      if (lane == 0) s_PRm[ms] = prbits;
+      // publish the map (a first chunk publishes its outgoing carry instead),
+      // run the look-back, publish the outgoing carry
+      const Tile t = tile_of(tile);
+      float carry = 0.0f;
+      if (t.active) {
+        const size_t sidx = static_cast<size_t>(tile) * 64 + lane;
+        const bool last = t.chunk == p.n_chunks - 1;
+        const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch] : 0.0f;
+        carry = init;
+        if (t.chunk == 0) {
+          if (!last) publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, init, GB)));
+        } else {
+          if (!last) {
+            publish(p.slot_a, sidx, tag, encode_a(GA, GR));
+            publish(p.slot_b, sidx, tag, __float_as_uint(GB));
+          }
+          float in[1] = {init}, out[1];
+          if (!look_back_wave<1, K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tile) * 64,
+                                    static_cast<unsigned>(lane), static_cast<long long>(rows) * 64, t.chunk, tag, in,
+                                    out)) {
+            atomicOr(&p.hdr->err, 1u);
+          }
+          carry = out[0];
+          if (!last) publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, carry, GB)));
+        }
+      }
+      s_carry[ms][lane] = carry;
+      lds_release();
+      if (lane == 0) lds_store(&s_carry_ok[ms], i);
+    }
+  } else {
+    // ------------------------------------------------------------ data waves
+    // A raw word as float32. Rows of 2-byte elements are read a dword at a
+    // time (the pair of channels holding the lane's) and the lane's half is
+    // moved to the high half with one byte permute: bytes 1:0 (even lanes) or
+    // 3:2 (odd lanes) above two zero bytes. Otherwise the 4-byte slot holds
+    // the element zero-extended.
+    const unsigned perm_sel = (lane & 1) ? 0x03020c0cu : 0x01000c0cu;
+    auto lds_raw = [=](int b, int q, int row) -> uint32_t {
+      if constexpr (ROWB == 128) {
+        return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][row][(lane & ~1) * 2]);
+      } else {
+        return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][row][lane * 4]);
+      }
     };
-
-    if (ctrl) {
-      clear();
-      // the carry entering t_{i-1}
-      {
-        const Tile t = tile_of(t_prv, 0);
-        if (prv_ok && t.active) {
-          const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch + cj] : 0.0f;
-          float carry = init;
-          if (t.chunk > 0) {
-            float in[1] = {init}, out[1];
-            if (!look_back_wave<1, K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(t_prv) * SW,
-                                      static_cast<unsigned>(lane * V + cj), static_cast<long long>(rows) * SW,
-                                      t.chunk, tag, in, out)) {
-              atomicOr(&p.hdr->err, 1u);
-            }
-            carry = out[0];
-            if (t.chunk < p.n_chunks - 1) {
-              float GA, GB;
-              bool GR;
-              tile_map(pb, GA, GB, GR);
-              const size_t sidx = static_cast<size_t>(t_prv) * SW + static_cast<size_t>(lane) * V + cj;
-              publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, carry, GB)));
-            }
-          }
-          s_carry[pb][lane * V + cj] = carry;
-        }
+    auto to_f32 = [=](uint32_t r) {
+      if constexpr (ROWB == 128) return __uint_as_float(__builtin_amdgcn_perm(0u, r, perm_sel));
+      else return BF ? __uint_as_float(r << 16) : __uint_as_float(r);
+    };
+    auto wave_steps = [=](const Tile& t) {
+      const long long rem = p.L - (t.t0 + wave * TS);
+      return rem <= 0 ? 0 : (rem >= TS ? TS : static_cast<int>(rem));
+    };
+    // One iteration: the gates of t_i into (cal, cu, crm), and the replay of
+    // t_{i-2} from (ral, ru, rrm). Returns false once t_{i-1} is past the last
+    // tile (the next iteration would have nothing to replay).
+    auto iteration = [=](int i, float (&cal)[TS], float (&cu)[TS], unsigned& crm, const float (&ral)[TS],
+                         const float (&ru)[TS], unsigned rrm) -> bool {
+      const int cb = i & 1;
+      const int ms = i % 3;
+      const int rs_slot = (i + 1) % 3;     // slot of iteration i - 2
+      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      if (lds_load(&s_abort) != 0) return false;
+      const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
+      const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 1) % RING]) : p.n_tiles);
+      const Tile tr = tile_of(i > 1 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 2) % RING]) : p.n_tiles);
+      // the replay's incoming state (ready since the previous iteration in
+      // steady state)
+      float hc = 0.0f;
+      int rn = 0;
+      if (tr.valid) {
+        lds_wait<true>(&s_carry_ok[rs_slot], i - 2, &s_abort, p.hdr);
+        const float c0 = s_carry[rs_slot][lane];
+        const float PA = s_PA[rs_slot][wave][lane];
+        const float PB = s_PB[rs_slot][wave][lane];
+        const bool PR = ((s_PRm[rs_slot] >> wave) & 1u) != 0u;
+        hc = PR ? PB : fmaf(PA, c0, PB);
+        rn = wave_steps(tr);
       }
-      // s_carry is written before the flag that releases the data waves
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (lane == 0) lds_flag_set(&s_carry_ready[cj], i);
-      // once every data wave has reported its map of t_i: the prefixes the
-      // data waves replay from, and the published map (a first chunk
-      // publishes its outgoing carry instead)
-      {
-        const Tile t = tile_of(t_cur, 0);
-        if (cur_ok) {
-          lds_count_wait(&s_maps_in, NW * (i + 1));
-          // every map read first (one wait), then the prefixes written
-          float Aw[NW], Bw[NW];
-          unsigned Rw[NW];
-#pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            Rw[w] = s_R[cb][w];
-            Aw[w] = s_A[cb][w][lane * V + cj];
-            Bw[w] = s_B[cb][w][lane * V + cj];
-          }
-          float GA = 1.0f, GB = 0.0f;
-          bool GR = false;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            s_PA[cb][w][lane * V + cj] = GA;
-            s_PB[cb][w][lane * V + cj] = GB;
-            if (cj == 0 && lane == 0) s_PR[cb][w] = GR ? 1u : 0u;
-            GB = Rw[w] != 0u ? Bw[w] : fmaf(Aw[w], GB, Bw[w]);
-            GA *= Aw[w];
-            GR = GR || Rw[w] != 0u;
-          }
-          if (t.active && t.chunk < p.n_chunks - 1) {
-            const size_t sidx = static_cast<size_t>(t_cur) * SW + static_cast<size_t>(lane) * V + cj;
-            if (t.chunk == 0) {
-              const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch + cj] : 0.0f;
-              publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, init, GB)));
-            } else {
-              publish(p.slot_a, sidx, tag, encode_a(GA, GR));
-              publish(p.slot_b, sidx, tag, __float_as_uint(GB));
-            }
-          }
-        }
-      }
-    } else if (loader) {
-      clear();
-      // the lambda values of t_{i+1} and the next ticket first: their round
-      // trips overlap the wait for the polls and the tile's loads
-      float lam[V];
-      if (nxt_ok) tile_lam(t_nxt, lam);
-      unsigned long long ticket = 0;
-      if (lane == 0 && cur_ok) ticket = atomicAdd(&p.hdr->counter, 1ull);
-      if (nxt_ok) {
-        load_tile(t_nxt, pb);
-        tile_consts(t_nxt, pb, lam);
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      // every slot read later is written: a ticket while this workgroup
-      // still draws them, past the last tile once it has stopped
-      if (lane == 0) s_tk[(i + 2) & 7] = cur_ok ? static_cast<unsigned>(ticket) : p.n_tiles;
-    } else {
-      if (cur_ok) {
-        const Tile t = tile_of(t_cur, wave);
+      float ck[TS / kCkpt];
+      float hv[TS];
+      if (tc.valid) {
+        lds_wait<true>(&s_full[cb], i, &s_abort, p.hdr);
+        const int nvalid = wave_steps(tc);
+        // reset flags of the wave's steps: lane k reads step k, one ballot
         unsigned rmask = 0;
         if (p.reset != nullptr) {
-          const unsigned* fl = reinterpret_cast<const unsigned*>(&s_flag[cb][wave * TS * 4]);
-#pragma unroll
-          for (int k = 0; k < TS; ++k) rmask |= (k < t.nvalid && fl[k] != 0u) ? (1u << k) : 0u;
+          const bool f = lane < nvalid && s_rflag[cb][wave * TS + (lane < TS ? lane : 0)] != 0u;
+          rmask = static_cast<unsigned>(__ballot(f));
         }
-        float k2[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) k2[j] = s_k2[cb][lane * V + j];
-        float A[V], Bv[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          A[j] = 1.0f;
-          Bv[j] = 0.0f;
-        }
-        // One step: (alpha, write) of both channels, and the wave's map
-        // extended by it. FULL: every step in range and no reset token, so
-        // no selects.
+        const float k2 = s_k2[cb][lane];
+        float A = 1.0f, Bv = 0.0f;
+        // one step of the gates: (alpha, write) and the wave's map extended by
+        // it. FULL: every step in range and no reset token, so no selects.
         auto gate_step = [&](int k, bool FULL) {
-          float xv[V], gxv[V], gav[V];
-          io::unpack(*reinterpret_cast<const R_t*>(&s_raw[cb][0][wave][k][lane * 4]), xv);
-          io::unpack(*reinterpret_cast<const R_t*>(&s_raw[cb][1][wave][k][lane * 4]), gxv);
-          io::unpack(*reinterpret_cast<const R_t*>(&s_raw[cb][2][wave][k][lane * 4]), gav);
-          const bool rs = FULL ? false : ((rmask >> k) & 1u) != 0u;
-          const bool in = FULL ? true : k < t.nvalid;
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            const float ig = sigmoid_f(gxv[j]);
-            const float r = sigmoid_f(gav[j]);
-            const float y = k2[j] * r;
-            const float a = __builtin_amdgcn_exp2f(y);
-            const float m = __builtin_amdgcn_sqrtf(one_minus_exp2(y, a) * (1.0f + a));
-            if (FULL) {
-              cal[k][j] = a;
-              cu[k][j] = m * ig * xv[j];
-              Bv[j] = fmaf(a, Bv[j], cu[k][j]);
-              A[j] *= a;
-            } else {
-              cal[k][j] = rs ? 0.0f : a;
-              cu[k][j] = (rs ? 1.0f : m) * ig * xv[j];
-              if (in) {
-                Bv[j] = rs ? cu[k][j] : fmaf(cal[k][j], Bv[j], cu[k][j]);
-                A[j] *= cal[k][j];
-              }
+          const float xv = to_f32(lds_raw(cb, 0, wave * TS + k));
+          const float ig = sigmoid_f(to_f32(lds_raw(cb, 1, wave * TS + k)));
+          const float r = sigmoid_f(to_f32(lds_raw(cb, 2, wave * TS + k)));
+          const float y = k2 * r;
+          const float a = __builtin_amdgcn_exp2f(y);
+          const float m = __builtin_amdgcn_sqrtf(one_minus_exp2(y, a) * (1.0f + a));
+          if (FULL) {
+            cal[k] = a;
+            cu[k] = m * ig * xv;
+            Bv = fmaf(a, Bv, cu[k]);
+            A *= a;
+          } else {
+            const bool rs = ((rmask >> k) & 1u) != 0u;
+            cal[k] = rs ? 0.0f : a;
+            cu[k] = (rs ? 1.0f : m) * ig * xv;
+            if (k < nvalid) {
+              Bv = rs ? cu[k] : fmaf(cal[k], Bv, cu[k]);
+              A *= cal[k];
             }
           }
         };
-        if (rmask == 0u && t.nvalid == TS) {
+        if (rmask == 0u && nvalid == TS && rrm == 0u && rn == TS) {
+          // common case: both tiles whole and free of reset tokens, one
+          // straight-line block the scheduler can interleave
 #pragma unroll
-          for (int k = 0; k < TS; ++k) gate_step(k, true);
-        } else {
-#pragma unroll
-          for (int k = 0; k < TS; ++k) gate_step(k, false);
-        }
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          s_A[cb][wave][lane * V + j] = A[j];
-          s_B[cb][wave][lane * V + j] = Bv[j];
-        }
-        if (lane == 0) {
-          s_R[cb][wave] = rmask != 0u ? 1u : 0u;
-          s_rmask[cb][wave] = rmask;
-        }
-      } else {
-        clear();
-      }
-      // report the map (every iteration, so the count stays NW per iteration)
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (lane == 0) lds_count_add(&s_maps_in);
-      if (prv_ok) {
-        // replay t_{i-1} from its carry and store h (and the checkpoint)
-        const Tile t = tile_of(t_prv, wave);
-        // the composite of the earlier waves' maps, from the control waves
-        float PA[V], PB[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          PA[j] = s_PA[pb][wave][lane * V + j];
-          PB[j] = s_PB[pb][wave][lane * V + j];
-        }
-        const bool PR = s_PR[pb][wave] != 0u;
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          lds_flag_wait(&s_carry_ready[j], i);
-        }
-        asm volatile("" ::: "memory");
-        if (t.active) {
-          float hc[V];
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            const float c0 = s_carry[pb][lane * V + j];
-            hc[j] = PR ? PB[j] : fmaf(PA[j], c0, PB[j]);
+          for (int k = 0; k < TS; ++k) {
+            gate_step(k, true);
+            if (k % kCkpt == 0) ck[k / kCkpt] = hc;
+            hc = fmaf(ral[k], hc, ru[k]);
+            hv[k] = hc;
           }
-          const unsigned rmask = s_rmask[pb][wave];
-          elem* hb = static_cast<elem*>(p.h) + (t.rowbase + t.t0) * W + static_cast<long long>(t.strip) * SW;
-          // FULL: every step in range and no reset token, so no selects
-          auto replay_step = [&](int k, bool FULL) {
-            if (FULL || k < t.nvalid) {
-              const long long tk = t.t0 + k;
-              if (p.ckpt != nullptr && ((wave * TS + k) % kCkpt) == 0) {
-                store_f32v<V>(p.ckpt + (static_cast<long long>(t.b) * p.n_ckpt + tk / kCkpt) * W + t.ch, hc);
-              }
-              const bool rs = FULL ? false : ((rmask >> k) & 1u) != 0u;
+        } else {
+          if (rmask == 0u && nvalid == TS) {
 #pragma unroll
-              for (int j = 0; j < V; ++j) hc[j] = rs ? pu[k][j] : fmaf(pal[k][j], hc[j], pu[k][j]);
-              io::store_nt32(hb + static_cast<long long>(k) * W, static_cast<unsigned>(lane * V), io::pack(hc));
-            }
-          };
-          if (rmask == 0u && t.nvalid == TS) {
-#pragma unroll
-            for (int k = 0; k < TS; ++k) replay_step(k, true);
+            for (int k = 0; k < TS; ++k) gate_step(k, true);
           } else {
 #pragma unroll
-            for (int k = 0; k < TS; ++k) replay_step(k, false);
+            for (int k = 0; k < TS; ++k) gate_step(k, false);
           }
-          if (p.h_last != nullptr && t.nvalid > 0 && t.t0 + t.nvalid == p.L) {
-            store_f32v<V>(p.h_last + t.b * W + t.ch, hc);
+#pragma unroll
+          for (int k = 0; k < TS; ++k) {
+            if (k % kCkpt == 0) ck[k / kCkpt] = hc;
+            const bool rs = ((rrm >> k) & 1u) != 0u;
+            const float nx = rs ? ru[k] : fmaf(ral[k], hc, ru[k]);
+            hc = k < rn ? nx : hc;   // steps past L leave the state as it is
+            hv[k] = hc;
           }
         }
+        crm = rmask;
+        s_A[ms][wave][lane] = A;
+        s_B[ms][wave][lane] = Bv;
+        if (lane == 0) s_R[ms][wave] = rmask != 0u ? 1u : 0u;
+        lds_release();
+        if (lane == 0) {
+          lds_add(&s_maps_in[ms], 1);
+          lds_add(&s_cons[cb], 1);
+        }
+      } else {
+        // past the last tile: the ring slot is still defined (its previous
+        // contents are dead, and leaving them undefined on some paths would
+        // keep them alive and cost whole-array register copies)
+#pragma unroll
+        for (int k = 0; k < TS; ++k) {
+          cal[k] = 0.0f;
+          cu[k] = 0.0f;
+        }
+        crm = 0u;
+#pragma unroll
+        for (int k = 0; k < TS; ++k) {
+          if (k % kCkpt == 0) ck[k / kCkpt] = hc;
+          const bool rs = ((rrm >> k) & 1u) != 0u;
+          const float nx = rs ? ru[k] : fmaf(ral[k], hc, ru[k]);
+          hc = k < rn ? nx : hc;
+          hv[k] = hc;
+        }
       }
+      if (tr.valid && tr.active) {
+        // stores of t_{i-2}: checkpoints, h, and the final state
+        const long long s0 = tr.t0 + wave * TS;
+        if (p.ckpt != nullptr) {
+#pragma unroll
+          for (int q = 0; q < TS / kCkpt; ++q) {
+            if (q * kCkpt < rn) p.ckpt[(static_cast<long long>(tr.b) * p.n_ckpt + s0 / kCkpt + q) * W + tr.ch] = ck[q];
+          }
+        }
+        elem* hb = static_cast<elem*>(p.h) + (tr.rowbase + s0) * W + static_cast<long long>(tr.strip) * 64;
+        if (p.h_wide && (tr.strip + 1) * 64 <= p.W) {
+          // Full strips with 16-byte aligned rows: the wave's rows go through
+          // LDS and out 16 bytes per lane (two instructions a wave). They are
+          // written as elements and read back as 16-byte vectors of other
+          // lanes' elements: the fence keeps the compiler from moving the
+          // reads above the writes (LDS itself executes a wave's operations
+          // in order).
+#pragma unroll
+          for (int k = 0; k < TS; ++k) {
+            float h1[1] = {hv[k]};
+            reinterpret_cast<typename io::R*>(&s_hst[wave][0])[k * 64 + lane] = io::pack(h1);
+          }
+          lds_acquire();
+          // lane l: row l / HSEG of each group of 64 / HSEG rows, 16 bytes at
+          // segment l % HSEG of it
+          constexpr int HSEG = 64 * ES / 16;
+          constexpr int HRPI = 64 / HSEG;
+          const int hr = lane / HSEG;
+          const int hs = lane % HSEG;
+#pragma unroll
+          for (int g = 0; g < TS / HRPI; ++g) {
+            const int row = g * HRPI + hr;
+            if (row < rn) {
+              // wave-uniform base (the group's first row), the lane's row and
+              // segment as a 32-bit element offset
+              const u32x4 v = *reinterpret_cast<const u32x4*>(&s_hst[wave][row * 64 + hs * (16 / ES)]);
+              Io<IO, 16 / ES>::store_nt32(hb + static_cast<long long>(g * HRPI) * W,
+                                          static_cast<unsigned>(hr) * static_cast<unsigned>(p.W) +
+                                              static_cast<unsigned>(hs * (16 / ES)),
+                                          v);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < TS; ++k) {
+            if (k < rn) {
+              float h1[1] = {hv[k]};
+              io::store_nt32(hb + static_cast<long long>(k) * W, static_cast<unsigned>(lane), io::pack(h1));
+            }
+          }
+        }
+        if (p.h_last != nullptr && rn > 0 && s0 + rn == p.L) p.h_last[tr.b * W + tr.ch] = hc;
+      }
+      return tc.valid || tp.valid;
+    };
+    // register ring of three tiles: iteration i writes slot i % 3 and replays
+    // slot (i - 2) % 3
+    float al0[TS], u0[TS], al1[TS], u1[TS], al2[TS], u2[TS];
+    unsigned rm0 = 0u, rm1 = 0u, rm2 = 0u;
+#pragma unroll
+    for (int k = 0; k < TS; ++k) {
+      al1[k] = u1[k] = al2[k] = u2[k] = 0.0f;
     }
-    __syncthreads();
-    return true;
-  };
-
-  // register ring: iteration i writes one set and replays the other
-  float al0[TS][V], u0[TS][V], al1[TS][V], u1[TS][V];
-  for (int i = 0;; i += 2) {
-    if (!iteration(i, al0, u0, al1, u1)) break;
-    if (!iteration(i + 1, al1, u1, al0, u0)) break;
+    for (int i = 0;; i += 3) {
+      if (!iteration(i, al0, u0, rm0, al1, u1, rm1)) break;
+      if (!iteration(i + 1, al1, u1, rm1, al2, u2, rm2)) break;
+      if (!iteration(i + 2, al2, u2, rm2, al0, u0, rm0)) break;
+    }
   }
-  if (ctrl && cj == 0 && lane == 0) {
-    // every workgroup draws its last ticket before it counts itself done; the
-    // last one to finish re-arms the tickets and advances the call tag
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // every workgroup has drawn its last ticket before it counts itself done;
+    // the last one to finish re-arms the tickets and advances the call tag
     const unsigned prev = atomicAdd(&p.hdr->done, 1u);
     if (prev == gridDim.x - 1) {
       atomicExch(&p.hdr->done, 0u);
@@ -1632,44 +1681,43 @@ unsigned persistent_grid(Kern kernel, int threads, unsigned n_tiles) {
   return g < n_tiles ? g : n_tiles;
 }
 
-template <typename IO, int V, int TS, int NW, bool WIDE>
+template <typename IO, int NW, int TS, bool WIDE>
 rglru_status_t launch_fwd(FwdArgs a, hipStream_t stream) {
-  a.n_strips = static_cast<int>(ceil_div(a.W, 64 * V));
-  a.n_chunks = static_cast<int>(ceil_div(a.L, TS * NW));
+  constexpr int T = NW * TS;
+  a.n_strips = static_cast<int>(ceil_div(a.W, 64));
+  a.n_chunks = static_cast<int>(ceil_div(a.L, T));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  auto kernel = fwd_kernel<IO, V, TS, NW, WIDE>;
-  constexpr int threads = (NW + V + 1) * 64;
+  auto kernel = fwd_kernel<IO, NW, TS, WIDE>;
+  constexpr int threads = (NW + 4) * 64;
   const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
   if (grid == 0) return RGLRU_ERR_HIP;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
   return launch_status();
 }
 
-template <typename IO, int V, bool WIDE>
-rglru_status_t dispatch_fwd_chunk(int T, FwdArgs a, hipStream_t stream) {
-  // up to 8 data waves (two per SIMD)
-  switch (T) {
-    case 8: return launch_fwd<IO, V, 8, 1, WIDE>(a, stream);
-    case 16: return launch_fwd<IO, V, 8, 2, WIDE>(a, stream);
-    case 32: return launch_fwd<IO, V, 8, 4, WIDE>(a, stream);
-    default: return launch_fwd<IO, V, 8, 8, WIDE>(a, stream);
-  }
+// Forward tile length for a requested chunk: at most 128 steps where 2-byte
+// rows are loaded 16 bytes per lane (a tile's raw words then fill 48 KiB of
+// LDS, and the pipeline holds two), at most 64 otherwise.
+int fwd_tile(int req, bool wide, int io_bytes) {
+  const int cap = (wide && io_bytes == 2) ? 128 : 64;
+  return req < cap ? req : cap;
 }
 
-// One lane covers 4 bytes of a step row: two bf16 channels or one float32
-// channel (one bf16 channel where the width or alignment rules out pairs).
-// Rows of 16-byte aligned words are loaded 16 bytes per lane.
-template <typename IO>
-rglru_status_t dispatch_fwd(int T, int V, bool wide, FwdArgs a, hipStream_t stream) {
-  constexpr bool f32 = std::is_same<IO, F32>::value;
-  if constexpr (f32) {
-    return wide ? dispatch_fwd_chunk<IO, 1, true>(T, a, stream) : dispatch_fwd_chunk<IO, 1, false>(T, a, stream);
-  } else {
-    if (V >= 2) {
-      return wide ? dispatch_fwd_chunk<IO, 2, true>(T, a, stream) : dispatch_fwd_chunk<IO, 2, false>(T, a, stream);
-    }
-    return dispatch_fwd_chunk<IO, 1, false>(T, a, stream);
+// Tiles of T steps: T / 8 data waves of 8 steps each up to 64 steps, 8 data
+// waves of 16 steps at 128.
+template <typename IO, bool WIDE>
+rglru_status_t dispatch_fwd(int T, FwdArgs a, hipStream_t stream) {
+  switch (T) {
+    case 8: return launch_fwd<IO, 1, 8, WIDE>(a, stream);
+    case 16: return launch_fwd<IO, 2, 8, WIDE>(a, stream);
+    case 32: return launch_fwd<IO, 4, 8, WIDE>(a, stream);
+    case 64: return launch_fwd<IO, 8, 8, WIDE>(a, stream);
+    default: break;
   }
+  if constexpr (WIDE && std::is_same<IO, BF16>::value) {
+    if (T == 128) return launch_fwd<IO, 8, 16, WIDE>(a, stream);
+  }
+  return RGLRU_ERR_UNSUPPORTED;
 }
 
 template <typename IO, int V, int NW>
@@ -1796,8 +1844,8 @@ rglru_status_t rglru_fwd(const rglru_shape_t* s, const void* x, const void* gate
   a.c = s->c;
   // 16-byte loads: rows a multiple of 16 bytes, the three inputs 16-byte aligned
   const bool wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(x, 16) && aligned_to(gate_x, 16) &&
-                    aligned_to(gate_a, 16) && (s->io_dtype == RGLRU_IO_F32 || V >= 2) &&
-                    static_cast<long long>(g.T) * s->width * g.io_bytes < (1ll << 31);
+                    aligned_to(gate_a, 16) && 128LL * s->width * g.io_bytes < (1LL << 31);
+  a.h_wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(h, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s->length <= kSerialMaxL) {
     const unsigned grid = static_cast<unsigned>(ceil_div(s->batch * (s->width / V), 256));
@@ -1813,8 +1861,12 @@ rglru_status_t rglru_fwd(const rglru_shape_t* s, const void* x, const void* gate
     }
     return launch_status();
   }
-  if (s->io_dtype == RGLRU_IO_F32) return dispatch_fwd<F32>(g.T, 1, wide, a, st);
-  return dispatch_fwd<BF16>(g.T, V, wide, a, st);
+  const int req = s->chunk == 0 ? 128 : s->chunk;
+  const int T = fwd_tile(req, wide, g.io_bytes);
+  if (s->io_dtype == RGLRU_IO_F32) {
+    return wide ? dispatch_fwd<F32, true>(T, a, st) : dispatch_fwd<F32, false>(T, a, st);
+  }
+  return wide ? dispatch_fwd<BF16, true>(T, a, st) : dispatch_fwd<BF16, false>(T, a, st);
 }
 
 rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate_x, const void* gate_a,
