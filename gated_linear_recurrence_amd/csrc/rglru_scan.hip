@@ -62,9 +62,6 @@ constexpr int kMaxStrip = 512;   // widest channel strip of any variant (64 lane
 #ifndef RGLRU_FWD_VMAX
 #define RGLRU_FWD_VMAX 4
 #endif
-#ifndef RGLRU_BWD_VMAX
-#define RGLRU_BWD_VMAX 2
-#endif
 
 // ------------------------------------------------------------------ io access
 
@@ -565,8 +562,8 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
     t.rowbase = static_cast<long long>(t.b) * p.L;
     return t;
   };
-  auto ticket_tile = [=](u64 v, unsigned k) {
-    const unsigned q = static_cast<unsigned>(v) + k;
+  auto ticket_tile = [=](u64 v, unsigned m) {
+    const unsigned q = static_cast<unsigned>(v) + m;
     return q < p.n_tiles ? q : p.n_tiles;
   };
 
@@ -626,6 +623,9 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
               lds_dma16(base + off, dst);
               off += step;
               dst += 1024;
+#ifdef RGLRU_DMA_THROTTLE
+              if ((g & 7) == 7) __builtin_amdgcn_s_waitcnt(RGLRU_DMA_THROTTLE);
+#endif
             }
           }
         } else {
@@ -774,11 +774,46 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
       const long long rem = p.L - (t.t0 + wave * TS);
       return rem <= 0 ? 0 : (rem >= TS ? TS : static_cast<int>(rem));
     };
+    // h rows staged in LDS by one iteration and stored 16 bytes per lane at
+    // the start of the next (two instructions a wave), so the read-back's LDS
+    // latency is not waited for. Lane l stores row l / HSEG of each group of
+    // 64 / HSEG rows, 16 bytes at segment l % HSEG of it.
+    constexpr int HSEG = 64 * ES / 16;
+    constexpr int HRPI = 64 / HSEG;
+    struct Pending {
+      elem* hb;   // h at the wave's first row of the staged tile
+      int rn;     // rows to store
+      bool on;
+    };
+    auto flush = [=](Pending& pd) {
+      if (!pd.on) return;
+      // the rows were written as elements and are read as 16-byte vectors of
+      // other lanes' elements: the fence keeps the compiler from moving the
+      // reads above the writes (LDS executes a wave's operations in order)
+      lds_acquire();
+      const int hr = lane / HSEG;
+      const int hs = lane % HSEG;
+#pragma unroll
+      for (int g = 0; g < TS / HRPI; ++g) {
+        const int row = g * HRPI + hr;
+        if (row < pd.rn) {
+          // wave-uniform base (the group's first row), the lane's row and
+          // segment as a 32-bit element offset
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&s_hst[wave][row * 64 + hs * (16 / ES)]);
+          Io<IO, 16 / ES>::store_nt32(pd.hb + static_cast<long long>(g * HRPI) * p.W,
+                                      static_cast<unsigned>(hr) * static_cast<unsigned>(p.W) +
+                                          static_cast<unsigned>(hs * (16 / ES)),
+                                      v);
+        }
+      }
+      pd.on = false;
+    };
     // One iteration: the gates of t_i into (cal, cu, crm), and the replay of
     // t_{i-2} from (ral, ru, rrm). Returns false once t_{i-1} is past the last
     // tile (the next iteration would have nothing to replay).
     auto iteration = [=](int i, float (&cal)[TS], float (&cu)[TS], unsigned& crm, const float (&ral)[TS],
-                         const float (&ru)[TS], unsigned rrm) -> bool {
+                         const float (&ru)[TS], unsigned rrm, Pending& pend) -> bool {
+      flush(pend);
       const int cb = i & 1;
       const int ms = i % 3;
       const int rs_slot = (i + 1) % 3;     // slot of iteration i - 2
@@ -903,37 +938,16 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
         }
         elem* hb = static_cast<elem*>(p.h) + (tr.rowbase + s0) * W + static_cast<long long>(tr.strip) * 64;
         if (p.h_wide && (tr.strip + 1) * 64 <= p.W) {
-          // Full strips with 16-byte aligned rows: the wave's rows go through
-          // LDS and out 16 bytes per lane (two instructions a wave). They are
-          // written as elements and read back as 16-byte vectors of other
-          // lanes' elements: the fence keeps the compiler from moving the
-          // reads above the writes (LDS itself executes a wave's operations
-          // in order).
+          // Full strips with 16-byte aligned rows: the wave's rows go to LDS
+          // now and out at the start of the next iteration
 #pragma unroll
           for (int k = 0; k < TS; ++k) {
             float h1[1] = {hv[k]};
             reinterpret_cast<typename io::R*>(&s_hst[wave][0])[k * 64 + lane] = io::pack(h1);
           }
-          lds_acquire();
-          // lane l: row l / HSEG of each group of 64 / HSEG rows, 16 bytes at
-          // segment l % HSEG of it
-          constexpr int HSEG = 64 * ES / 16;
-          constexpr int HRPI = 64 / HSEG;
-          const int hr = lane / HSEG;
-          const int hs = lane % HSEG;
-#pragma unroll
-          for (int g = 0; g < TS / HRPI; ++g) {
-            const int row = g * HRPI + hr;
-            if (row < rn) {
-              // wave-uniform base (the group's first row), the lane's row and
-              // segment as a 32-bit element offset
-              const u32x4 v = *reinterpret_cast<const u32x4*>(&s_hst[wave][row * 64 + hs * (16 / ES)]);
-              Io<IO, 16 / ES>::store_nt32(hb + static_cast<long long>(g * HRPI) * W,
-                                          static_cast<unsigned>(hr) * static_cast<unsigned>(p.W) +
-                                              static_cast<unsigned>(hs * (16 / ES)),
-                                          v);
-            }
-          }
+          pend.hb = hb;
+          pend.rn = rn;
+          pend.on = true;
         } else {
 #pragma unroll
           for (int k = 0; k < TS; ++k) {
@@ -955,11 +969,13 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
     for (int k = 0; k < TS; ++k) {
       al1[k] = u1[k] = al2[k] = u2[k] = 0.0f;
     }
+    Pending pend{nullptr, 0, false};
     for (int i = 0;; i += 3) {
-      if (!iteration(i, al0, u0, rm0, al1, u1, rm1)) break;
-      if (!iteration(i + 1, al1, u1, rm1, al2, u2, rm2)) break;
-      if (!iteration(i + 2, al2, u2, rm2, al0, u0, rm0)) break;
+      if (!iteration(i, al0, u0, rm0, al1, u1, rm1, pend)) break;
+      if (!iteration(i + 1, al1, u1, rm1, al2, u2, rm2, pend)) break;
+      if (!iteration(i + 2, al2, u2, rm2, al0, u0, rm0, pend)) break;
     }
+    flush(pend);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1042,24 +1058,37 @@ __global__ __launch_bounds__(256) void fwd_serial_kernel(FwdArgs p) {
 
 // ------------------------------------------------------------------ backward
 //
-// The reverse recurrence g_t = dh_t + alpha_{t+1} g_{t+1} needs only the
-// decays and dh, not x or gate_x, so the backward runs as four launches:
-//   bwd_map_kernel   : each tile's reverse map G_out = A*G_in + B (carry
-//                      entering its first step from the carry entering its
-//                      last), from gate_a, lambda, the reset flags and dh;
-//   bwd_carry_kernel : one thread per (batch row, channel) composes the maps
-//                      from the last chunk backwards and stores the carry
-//                      entering every tile;
-//   bwd_main_kernel  : every tile independently recomputes the forward from
-//                      its checkpoints, runs the reverse pass from its carry
-//                      and writes dx, dgate_x and dgate_a; a workgroup (a few
-//                      chunks of one row) writes one lambda-gradient partial;
-//   bwd_dlam_kernel  : sums each channel's partials over (workgroup, batch
-//                      row) in a fixed order.
-// No workgroup waits for another, so the main pass streams at full occupancy.
-// The maps, carries and partials are stored as 64-bit slot words whose high
-// half is 0, a tag the forward never uses, so a forward sharing the workspace
-// never mistakes them for its own published words.
+// The reverse recurrence g_t = dh_t + alpha_{t+1} g_{t+1} runs as a single
+// persistent pass over tiles in reverse chunk order, the mirror image of the
+// forward: a tile is one batch row, a strip of 64 channels (one per lane) and
+// T = NW * 8 steps, wave w owning steps 8w .. 8w+7 (one checkpoint interval,
+// whose entering state the forward stored). The carry a tile needs enters its
+// last step from the later chunks, so the look-back runs over later chunks.
+// A workgroup has NW data waves, one control wave and two load waves, joined
+// by one-directional LDS flags. With t_i the workgroup's i-th tile:
+//   load wave i%2 : once every data wave has finished with LDS buffer i%2,
+//                   streams the raw words of t_i (x, gate_x, gate_a, dh), the
+//                   checkpoint rows and the reset flags into it with
+//                   global_load_lds and evaluates the decay constants;
+//   data waves    : in iteration i, recompute the forward through their steps
+//                   of t_i from the checkpoint, keep six coefficients per step
+//                   (a register ring of two tiles), reduce their steps to the
+//                   reverse map G -> R ? B : A*G + B and report it; then wait
+//                   for the carry of t_{i-1} and run its reverse pass, writing
+//                   dx, dgate_x and dgate_a and reporting the wave's part of
+//                   the tile's lambda gradient;
+//   control wave  : runs the look-back of t_{i-1} and publishes its outgoing
+//                   carry; sums the lambda-gradient parts of t_{i-2} in wave
+//                   order into the tile's partial; once every data wave has
+//                   reported t_i, writes the suffix maps each wave's reverse
+//                   pass starts from and publishes the tile's map.
+// Per step, with G the carry arriving from the next step:
+//   g = G + dh;  dx = g*cx;  dgate_x = g*cgx;  dgate_a = g*cga;
+//   lambda partial += g*cl;  G <- alpha*g  (0 through a reset token)
+// where cx = mult*i, cgx = mult*i*x*(1-i), dl = g*a*(h_prev - a*i*x/m) off
+// reset tokens (0 on them), cl = dl/g * r, cga = cl * c_s * (1 - r). The
+// per-tile partials are summed per channel in a fixed order by
+// bwd_dlam_kernel, so the backward is deterministic run to run.
 
 struct BwdArgs {
   const void* x;
@@ -1076,475 +1105,536 @@ struct BwdArgs {
   float* dlam;
   float* dh0;
   Header* hdr;
-  u64* map_a;            // per tile and channel: A of the reverse map (a reset in the sign bit)
-  u64* map_b;            // B of the reverse map
-  u64* carry;            // carry entering the tile's last step from the later chunks
-  u64* part;             // a main-pass workgroup's lambda-gradient partial
+  u64* slot_a;           // published reverse map A (a reset in the sign bit)
+  u64* slot_b;           // published reverse map B
+  u64* slot_h;           // published carry leaving the tile's first step
+  float* part;           // lambda-gradient partial per tile and channel
   long long L;
   long long n_ckpt;
   int B;
   int W;
   int n_strips;
   int n_chunks;
-  int n_groups;          // main-pass workgroups per (batch row, strip): one partial each
   unsigned n_tiles;
   float c;
+  bool out_wide;         // output rows start 16-byte aligned
 };
 
-__device__ __forceinline__ u64 untagged(float v) { return static_cast<u64>(__float_as_uint(v)); }
-__device__ __forceinline__ float word_value(u64 w) { return __uint_as_float(static_cast<uint32_t>(w)); }
-
-// Geometry of a backward tile: chunk-major tile index, TS = 8 steps per wave
-// (one checkpoint interval), NW waves, 64*V channels.
-struct BwdTile {
-  int chunk, b, strip, ch, nvalid;
-  long long t0, rowbase;
-  bool active;
-};
-template <int V, int NW>
-__device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& p, unsigned tile, int wave, int lane) {
-  const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
-  BwdTile t;
-  t.chunk = static_cast<int>(tile / rows);
-  const int row = static_cast<int>(tile - static_cast<unsigned>(t.chunk) * rows);
-  t.b = row / p.n_strips;
-  t.strip = row - t.b * p.n_strips;
-  t.ch = t.strip * 64 * V + lane * V;
-  t.active = t.ch < p.W;
-  t.t0 = static_cast<long long>(t.chunk) * (kCkpt * NW) + static_cast<long long>(wave) * kCkpt;
-  const long long rem = p.L - t.t0;
-  t.nvalid = rem <= 0 ? 0 : (rem >= kCkpt ? kCkpt : static_cast<int>(rem));
-  t.rowbase = static_cast<long long>(t.b) * p.L;
-  return t;
-}
-
-template <int NW>
-__device__ __forceinline__ unsigned reset_mask(const BwdArgs& p, long long rowbase, long long t0, int nvalid,
-                                               int lane) {
-  if (p.reset == nullptr) return 0u;
-  const bool f = lane < nvalid && p.reset[rowbase + t0 + lane] != 0;
-  return static_cast<unsigned>(__ballot(f));
-}
-
-// Reverse maps of all tiles. Workgroup (row, y) covers chunks
-// y*CPB .. y*CPB+CPB-1 of one row, so the decay constants are evaluated once.
-template <typename IO, int V, int NW, int CPB>
-__global__ __launch_bounds__(NW * 64) void bwd_map_kernel(BwdArgs p) {
+template <typename IO, int NW, bool WIDE>
+__global__ __launch_bounds__((NW + 3) * 64) void bwd_kernel(BwdArgs p) {
+  using elem = typename IO::elem;
+  using io = Io<IO, 1>;
+  constexpr bool BF = std::is_same<IO, BF16>::value;
+  constexpr int ES = static_cast<int>(sizeof(elem));
   constexpr int TS = kCkpt;
-  constexpr int SW = 64 * V;
-  using io = Io<IO, V>;
-  using R_t = typename io::R;
-  using elem = typename io::elem;
-  __shared__ float s_A[NW][SW];
-  __shared__ float s_B[NW][SW];
-  __shared__ unsigned s_R[NW];
+  constexpr int T = NW * TS;
+  constexpr int ROWB = WIDE ? 64 * ES : 256;
+  constexpr int SEG = ROWB / 16;
+  constexpr int RPI = 64 / SEG;
+  constexpr int K = RGLRU_FWD_LOOKBACK;
+  constexpr int RING = 16;
+  constexpr int NFL = T < 64 ? 64 : T;
+  constexpr int CTRL = NW, LOAD0 = NW + 1;
+  constexpr int NQ = 4;                    // x, gate_x, gate_a, dh
+  constexpr bool STAGE = BF;               // bf16 outputs go out 16 bytes per lane through LDS
+  static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
+  static_assert(NFL % 64 == 0 && NFL <= 128, "reset flags: at most two instructions");
+  static_assert(NW <= 32, "reset flags of the waves fit one mask word");
+
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][NQ][T][ROWB];
+  __shared__ __attribute__((aligned(16))) float s_ck[2][NW][64];   // state entering each wave's first step
+  __shared__ unsigned s_rflag[2][NFL];
+  __shared__ float s_k2[2][64];
+  __shared__ float s_cs[2][64];
+  __shared__ float s_A[2][NW][64];
+  __shared__ float s_B[2][NW][64];
+  __shared__ unsigned s_R[2][NW];
+  __shared__ float s_SA[2][NW][64];   // composite of the maps of the waves after each wave
+  __shared__ float s_SB[2][NW][64];
+  __shared__ unsigned s_SRm[2];       // bit w: a reset inside the waves after wave w
+  __shared__ float s_carry[2][64];
+  __shared__ float s_dl[2][NW][64];   // each wave's part of a tile's lambda gradient
+  __shared__ __attribute__((aligned(16))) elem s_ost[STAGE ? NW : 1][3][TS * 64];
+  __shared__ unsigned s_tk[RING];
+  __shared__ unsigned s_tag;
+  __shared__ int s_tk_valid;
+  __shared__ int s_full[2];
+  __shared__ int s_cons[2];
+  __shared__ int s_maps_in[2];
+  __shared__ int s_dl_in[2];
+  __shared__ int s_carry_ready;
+  __shared__ int s_abort;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
   const long long W = p.W;
-  const int c_begin = blockIdx.y * CPB;
-  const int c_end = c_begin + CPB < p.n_chunks ? c_begin + CPB : p.n_chunks;
-  const BwdTile t0 = bwd_tile<V, NW>(p, static_cast<unsigned>(c_begin) * rows + blockIdx.x, wave, lane);
-  float cs[V], k2[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    cs[j] = 0.0f;
-    k2[j] = 0.0f;
-    if (t0.active) channel_consts(p.lam[t0.ch + j], p.c, cs[j], k2[j]);
+
+  if (threadIdx.x == 0) {
+    s_tk_valid = -1;
+    s_full[0] = s_full[1] = -1;
+    s_cons[0] = s_cons[1] = 0;
+    s_maps_in[0] = s_maps_in[1] = 0;
+    s_dl_in[0] = s_dl_in[1] = 0;
+    s_carry_ready = -1;
+    s_abort = 0;
   }
-  for (int c = c_begin; c < c_end; ++c) {
-    const unsigned tile = static_cast<unsigned>(c) * rows + blockIdx.x;
-    const BwdTile t = bwd_tile<V, NW>(p, tile, wave, lane);
-    const unsigned rmask = reset_mask<NW>(p, t.rowbase, t.t0, t.nvalid, lane);
-    // wave-uniform row base plus the lane's 32-bit channel offset
-    const long long row0 = t.rowbase + t.t0;
-    R_t rga[TS], rdh[TS];
+  __syncthreads();
+
+  struct Tile {
+    bool valid, active;
+    int chunk, b, strip, ch;
+    unsigned id;                // chunk-major index (slot and partial addressing)
+    long long t0, rowbase;
+  };
+  // ticket q -> chunk n_chunks - 1 - q / rows (latest chunk first)
+  auto tile_of = [=](unsigned q) {
+    Tile t;
+    t.valid = q < p.n_tiles;
+    const unsigned qq = t.valid ? q : 0u;
+    const unsigned cq = qq / rows;
+    const int row = static_cast<int>(qq - cq * rows);
+    t.chunk = p.n_chunks - 1 - static_cast<int>(cq);
+    t.id = static_cast<unsigned>(t.chunk) * rows + static_cast<unsigned>(row);
+    t.b = row / p.n_strips;
+    t.strip = row - t.b * p.n_strips;
+    t.ch = t.strip * 64 + lane;
+    t.active = t.ch < p.W;
+    t.t0 = static_cast<long long>(t.chunk) * T;
+    t.rowbase = static_cast<long long>(t.b) * p.L;
+    return t;
+  };
+  auto ticket_tile = [=](u64 v, unsigned k) {
+    const unsigned q = static_cast<unsigned>(v) + k;
+    return q < p.n_tiles ? q : p.n_tiles;
+  };
+  auto wave_steps = [=](const Tile& t, int w) {
+    const long long rem = p.L - (t.t0 + w * TS);
+    return rem <= 0 ? 0 : (rem >= TS ? TS : static_cast<int>(rem));
+  };
+
+  if (wave >= LOAD0) {
+    // ------------------------------------------------------------ load waves
+    __builtin_amdgcn_s_setprio(3);
+    const int j = wave - LOAD0;
+    if (j == 0) {
+      u64 v = 0;
+      if (lane == 0) v = atomicAdd(&p.hdr->counter, 2ull);
+      v = uniform_u64(v);
+      if (lane == 0) {
+        s_tk[0] = ticket_tile(v, 0);
+        s_tk[1] = ticket_tile(v, 1);
+        s_tag = static_cast<unsigned>(v >> 32) + 1u;
+      }
+      lds_release();
+      if (lane == 0) lds_store(&s_tk_valid, 1);
+    }
+    const unsigned char* src[NQ] = {
+        static_cast<const unsigned char*>(p.x), static_cast<const unsigned char*>(p.gx),
+        static_cast<const unsigned char*>(p.ga), static_cast<const unsigned char*>(p.dh)};
+    const long long row_bytes = W * ES;
+    for (int i = j;; i += 2) {
+      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      const Tile t = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
+      lds_wait<false>(&s_cons[j], NW * (i / 2), &s_abort, p.hdr);
+      if (lds_load(&s_abort) != 0) break;
+      if (!t.valid) {
+        if (lane == 0) lds_store(&s_full[j], i);
+        break;
+      }
+      float lam = 0.0f;
+      if (t.active) lam = p.lam[t.ch];
+      const long long strip_b = static_cast<long long>(t.strip) * 64 * ES;
+      const long long tile_off = (t.rowbase + t.t0) * row_bytes + strip_b;
+      const long long lim = p.L - 1 - t.t0;
+      if constexpr (WIDE) {
+        const int r = lane / SEG;
+        const unsigned seg = static_cast<unsigned>(lane % SEG) * 16u;
+        const unsigned col = strip_b + seg < row_bytes ? seg : 0u;
+        if (t.t0 + T <= p.L) {
+          const unsigned step = static_cast<unsigned>(RPI) * static_cast<unsigned>(row_bytes);
 #pragma unroll
-    for (int k = 0; k < TS; ++k) {
-      rga[k] = R_t{};
-      rdh[k] = R_t{};
-      if (t.active && k < t.nvalid) {
-        const long long ro = (row0 + k) * W;
-        rga[k] = io::load_nt32(static_cast<const elem*>(p.ga) + ro, static_cast<unsigned>(t.ch));
-        rdh[k] = io::load_nt32(static_cast<const elem*>(p.dh) + ro, static_cast<unsigned>(t.ch));
+          for (int q = 0; q < NQ; ++q) {
+            gbyte* base = uniform_gptr(src[q] + tile_off);
+            unsigned off = static_cast<unsigned>(r) * static_cast<unsigned>(row_bytes) + col;
+            unsigned char* dst = &s_raw[j][q][0][0];
+#pragma unroll 4
+            for (int g = 0; g < T / RPI; ++g) {
+              lds_dma16(base + off, dst);
+              off += step;
+              dst += 1024;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            gbyte* base = uniform_gptr(src[q] + tile_off);
+            for (int g = 0; g < T / RPI; ++g) {
+              const long long row = g * RPI + r;
+              const long long off = (row < lim ? row : lim) * row_bytes + col;
+              lds_dma16(base + off, &s_raw[j][q][g * RPI][0]);
+            }
+          }
+        }
+      } else {
+        const unsigned col = t.active ? static_cast<unsigned>(lane * ES) : 0u;
+#pragma unroll 2
+        for (int k = 0; k < T; ++k) {
+          const long long row = k < lim ? k : lim;
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            gbyte* base = uniform_gptr(src[q] + tile_off + row * row_bytes);
+            __builtin_amdgcn_global_load_lds(const_cast<gbyte_w*>(base + col), &s_raw[j][q][k][0], ES, 0, 0);
+          }
+        }
+      }
+      // checkpoint rows (float32, one per wave; waves past L re-read row 0 of
+      // the tile, never used) and reset flags
+      {
+        const unsigned col = t.active ? static_cast<unsigned>(lane * 4) : 0u;
+        const long long ck0 = static_cast<long long>(t.b) * p.n_ckpt + t.t0 / TS;
+        for (int w = 0; w < NW; ++w) {
+          const long long kr = t.t0 + w * TS < p.L ? w : 0;
+          gbyte* base = uniform_gptr(p.ckpt + (ck0 + kr) * W + static_cast<long long>(t.strip) * 64);
+          __builtin_amdgcn_global_load_lds(const_cast<gbyte_w*>(base + col), &s_ck[j][w][0], 4, 0, 0);
+        }
+      }
+      if (p.reset != nullptr) {
+#pragma unroll
+        for (int h = 0; h < NFL / 64; ++h) {
+          const long long st = h * 64 + lane;
+          const long long tk = t.t0 + (st < lim ? st : lim);
+          __builtin_amdgcn_global_load_lds(p.reset + t.rowbase + tk, &s_rflag[j][h * 64], 1, 0, 0);
+        }
+      }
+      u64 nxt = 0;
+      if (j == 0 && lane == 0) nxt = atomicAdd(&p.hdr->counter, 2ull);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      {
+        float cs = 0.0f, k2 = 0.0f;
+        if (t.active) channel_consts(lam, p.c, cs, k2);
+        s_k2[j][lane] = k2;
+        s_cs[j][lane] = cs;
+      }
+      if (j == 0) {
+        nxt = uniform_u64(nxt);
+        if (lane == 0) {
+          s_tk[(i + 2) % RING] = ticket_tile(nxt, 0);
+          s_tk[(i + 3) % RING] = ticket_tile(nxt, 1);
+        }
+      }
+      lds_release();
+      if (lane == 0) {
+        if (j == 0) lds_store(&s_tk_valid, i + 3);
+        lds_store(&s_full[j], i);
       }
     }
-    float A[V], Bv[V];
+  } else if (wave == CTRL) {
+    // ------------------------------------------------------------ control wave
+    __builtin_amdgcn_s_setprio(3);
+    float GA = 1.0f, GB = 0.0f;   // reverse map of the previous iteration's tile
+    bool GR = false;
+    unsigned tag = 0;
+    for (int i = 0;; ++i) {
+      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      if (lds_load(&s_abort) != 0) break;
+      if (i == 0) tag = __builtin_amdgcn_readfirstlane(s_tag);
+      const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
+      const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 1) % RING]) : p.n_tiles);
+      const Tile t2 = tile_of(i > 1 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 2) % RING]) : p.n_tiles);
+      // the carry entering the last step of t_{i-1}, and the carry leaving it
+      if (tp.valid) {
+        float carry = 0.0f;
+        if (tp.active) {
+          const float init = p.dh_last != nullptr ? p.dh_last[tp.b * W + tp.ch] : 0.0f;
+          carry = init;
+          if (tp.chunk < p.n_chunks - 1) {
+            float in[1] = {init}, out[1];
+            if (!look_back_wave<1, K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tp.id) * 64,
+                                      static_cast<unsigned>(lane), -static_cast<long long>(rows) * 64,
+                                      p.n_chunks - 1 - tp.chunk, tag, in, out)) {
+              atomicOr(&p.hdr->err, 1u);
+            }
+            carry = out[0];
+            if (tp.chunk > 0) {
+              publish(p.slot_h, static_cast<size_t>(tp.id) * 64 + lane, tag,
+                      __float_as_uint(GR ? GB : fmaf(GA, carry, GB)));
+            }
+          }
+        }
+        s_carry[(i - 1) & 1][lane] = carry;
+        lds_release();
+        if (lane == 0) lds_store(&s_carry_ready, i - 1);
+      }
+      // the lambda-gradient partial of t_{i-2}: the waves' parts in wave order
+      if (t2.valid) {
+        const int pb = (i - 2) & 1;
+        lds_wait<false>(&s_dl_in[pb], NW * ((i - 2) / 2 + 1), &s_abort, p.hdr);
+        float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      A[j] = 1.0f;
-      Bv[j] = 0.0f;
-    }
+        for (int w = 0; w < NW; ++w) s += s_dl[pb][w][lane];
+        p.part[static_cast<size_t>(t2.id) * 64 + lane] = s;
+      }
+      if (!tp.valid && !tc.valid) break;
+      if (tc.valid) {
+        // once every data wave has reported t_i: the suffix maps its reverse
+        // passes start from, the tile's map and its publication (the latest
+        // chunk publishes its outgoing carry instead)
+        const int cb = i & 1;
+        lds_wait<false>(&s_maps_in[cb], NW * (i / 2 + 1), &s_abort, p.hdr);
+        if (lds_load(&s_abort) != 0) break;
+        float Aw[NW], Bw[NW];
+        unsigned Rw[NW];
 #pragma unroll
-    for (int k = TS - 1; k >= 0; --k) {
-      if (k < t.nvalid) {
-        const bool rs = (rmask >> k) & 1u;
-        float gav[V], dhv[V];
-        io::unpack(rga[k], gav);
-        io::unpack(rdh[k], dhv);
+        for (int w = 0; w < NW; ++w) {
+          Rw[w] = s_R[cb][w];
+          Aw[w] = s_A[cb][w][lane];
+          Bw[w] = s_B[cb][w][lane];
+        }
+        GA = 1.0f;
+        GB = 0.0f;
+        GR = false;
+        unsigned srbits = 0u;
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const float a = __builtin_amdgcn_exp2f(k2[j] * sigmoid_f(gav[j]));
-          const float gB = Bv[j] + dhv[j];
-          Bv[j] = rs ? 0.0f : a * gB;
-          A[j] = rs ? 0.0f : a * A[j];
+        for (int w = NW - 1; w >= 0; --w) {
+          s_SA[cb][w][lane] = GA;
+          s_SB[cb][w][lane] = GB;
+          srbits |= GR ? (1u << w) : 0u;
+          GB = Rw[w] != 0u ? Bw[w] : fmaf(Aw[w], GB, Bw[w]);
+          GA *= Aw[w];
+          GR = GR || Rw[w] != 0u;
+        }
+        if (lane == 0) s_SRm[cb] = srbits;
+        if (tc.active && tc.chunk > 0) {
+          const size_t sidx = static_cast<size_t>(tc.id) * 64 + lane;
+          if (tc.chunk == p.n_chunks - 1) {
+            const float init = p.dh_last != nullptr ? p.dh_last[tc.b * W + tc.ch] : 0.0f;
+            publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, init, GB)));
+          } else {
+            publish(p.slot_a, sidx, tag, encode_a(GA, GR));
+            publish(p.slot_b, sidx, tag, __float_as_uint(GB));
+          }
         }
       }
     }
-    __syncthreads();   // the previous chunk's maps have been combined
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      s_A[wave][lane * V + j] = A[j];
-      s_B[wave][lane * V + j] = Bv[j];
-    }
-    if (lane == 0) s_R[wave] = rmask != 0u ? 1u : 0u;
-    __syncthreads();
-    if (wave == 0 && t.active) {
-      float GA[V], GB[V];
-      bool GR = false;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        GA[j] = 1.0f;
-        GB[j] = 0.0f;
+  } else {
+    // ------------------------------------------------------------ data waves
+    const unsigned perm_sel = (lane & 1) ? 0x03020c0cu : 0x01000c0cu;
+    auto lds_raw = [=](int b, int q, int row) -> uint32_t {
+      if constexpr (ROWB == 128) {
+        return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][row][(lane & ~1) * 2]);
+      } else {
+        return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][row][lane * 4]);
       }
+    };
+    auto to_f32 = [=](uint32_t r) {
+      if constexpr (ROWB == 128) return __uint_as_float(__builtin_amdgcn_perm(0u, r, perm_sel));
+      else return BF ? __uint_as_float(r << 16) : __uint_as_float(r);
+    };
+    // outputs staged in LDS by one iteration and stored 16 bytes per lane at
+    // the start of the next (lane l: row l / HSEG, segment l % HSEG)
+    constexpr int HSEG = 64 * ES / 16;
+    constexpr int HRPI = 64 / HSEG;
+    struct Pending {
+      long long base;   // element offset of the wave's first row in the outputs
+      int rn;
+      bool on;
+    };
+    auto flush = [=](Pending& pd) {
+      if constexpr (STAGE) {
+        if (!pd.on) return;
+        lds_acquire();
+        const int hr = lane / HSEG;
+        const int hs = lane % HSEG;
+        void* outs[3] = {p.dx, p.dgx, p.dga};
 #pragma unroll
-      for (int w = NW - 1; w >= 0; --w) {
-        const bool Rw = s_R[w] != 0u;
+        for (int q = 0; q < 3; ++q) {
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const float Aw = s_A[w][lane * V + j];
-          const float Bw = s_B[w][lane * V + j];
-          GB[j] = Rw ? Bw : fmaf(Aw, GB[j], Bw);
-          GA[j] *= Aw;
+          for (int g = 0; g < TS / HRPI; ++g) {
+            const int row = g * HRPI + hr;
+            if (row < pd.rn) {
+              const u32x4 v = *reinterpret_cast<const u32x4*>(&s_ost[wave][q][row * 64 + hs * (16 / ES)]);
+              Io<IO, 16 / ES>::store_nt32(static_cast<elem*>(outs[q]) + pd.base + static_cast<long long>(g * HRPI) * p.W,
+                                          static_cast<unsigned>(hr) * static_cast<unsigned>(p.W) +
+                                              static_cast<unsigned>(hs * (16 / ES)),
+                                          v);
+            }
+          }
         }
-        GR = GR || Rw;
+        pd.on = false;
       }
-      const size_t idx = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        p.map_a[idx + j] = static_cast<u64>(encode_a(GA[j], GR));
-        p.map_b[idx + j] = untagged(GB[j]);
-      }
-    }
-  }
-}
-
-// Carry entering every tile. Workgroup: 64 channels of one batch row, NWC
-// waves each covering a contiguous run of chunks. Each wave composes its
-// run's maps, the runs are combined from the last backwards through LDS, and
-// each wave then walks its run again from the carry entering it, storing the
-// carry entering every tile.
-template <int V>
-__global__ __launch_bounds__(1024) void bwd_carry_kernel(BwdArgs p) {
-  constexpr int SW = 64 * V;
-  constexpr int NWC = 16;
-  constexpr int U = 8;
-  __shared__ float s_a[NWC][64];
-  __shared__ float s_b[NWC][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int groups = (p.W + 63) / 64;
-  const int b = blockIdx.x / groups;
-  const int ch = (blockIdx.x - b * groups) * 64 + lane;
-  const bool active = ch < p.W;
-  const int strip = ch / SW;
-  const int cin = ch - strip * SW;
-  const size_t rows = static_cast<size_t>(p.B) * static_cast<size_t>(p.n_strips);
-  const size_t row = static_cast<size_t>(b) * p.n_strips + strip;
-  const int per = (p.n_chunks + NWC - 1) / NWC;
-  const int c_lo = wave * per;                                   // run: chunks [c_lo, c_hi)
-  const int c_hi = c_lo + per < p.n_chunks ? c_lo + per : p.n_chunks;
-  auto idx_of = [=](int c) { return (static_cast<size_t>(c) * rows + row) * SW + cin; };
-  // pass 1: the run's composite map, latest chunk first
-  float RA = 1.0f, RB = 0.0f;
-  bool RR = false;
-  for (int c0 = c_hi - 1; c0 >= c_lo; c0 -= U) {
-    u64 wa[U], wb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 - u;
-      const bool ok = active && c >= c_lo;
-      wa[u] = ok ? p.map_a[idx_of(c)] : 0ull;
-      wb[u] = ok ? p.map_b[idx_of(c)] : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c0 - u >= c_lo) {
-        const uint32_t a = static_cast<uint32_t>(wa[u]);
-        const float Am = __uint_as_float(a & 0x7FFFFFFFu);
-        const float Bm = word_value(wb[u]);
-        const bool Rm = (a >> 31) != 0;
-        RB = Rm ? Bm : fmaf(Am, RB, Bm);
-        RA *= Am;
-        RR = RR || Rm;
-      }
-    }
-  }
-  // A >= 0, so a reset inside the run is kept in the sign of A
-  s_a[wave][lane] = RR ? -0.0f : RA;
-  s_b[wave][lane] = RB;
-  __syncthreads();
-  // carry entering this run: dh_last through the later runs, latest first
-  float G = (active && p.dh_last != nullptr) ? p.dh_last[static_cast<long long>(b) * p.W + ch] : 0.0f;
-  for (int w = NWC - 1; w > wave; --w) {
-    const float Am = s_a[w][lane];
-    const float Bm = s_b[w][lane];
-    G = signbit(Am) ? Bm : fmaf(Am, G, Bm);
-  }
-  // pass 2: store the carry entering each tile of the run
-  for (int c0 = c_hi - 1; c0 >= c_lo; c0 -= U) {
-    u64 wa[U], wb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 - u;
-      const bool ok = active && c >= c_lo;
-      wa[u] = ok ? p.map_a[idx_of(c)] : 0ull;
-      wb[u] = ok ? p.map_b[idx_of(c)] : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 - u;
-      if (active && c >= c_lo) {
-        p.carry[idx_of(c)] = untagged(G);
-        const uint32_t a = static_cast<uint32_t>(wa[u]);
-        const float Bm = word_value(wb[u]);
-        G = (a >> 31) != 0 ? Bm : fmaf(__uint_as_float(a & 0x7FFFFFFFu), G, Bm);
-      }
-    }
-  }
-}
-
-// Every wave covers exactly one checkpoint interval, whose entering state the
-// forward stored; the tile's carry comes from bwd_carry_kernel. Workgroup
-// (row, y) covers chunks y*CPB .. y*CPB+CPB-1 of one row, so the decay
-// constants are evaluated once.
-template <typename IO, int V, int NW, int WPE, int CPB>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
-void bwd_main_kernel(BwdArgs p) {
-  constexpr int TS = kCkpt;
-  constexpr int SW = 64 * V;
-  using io = Io<IO, V>;
-  using R_t = typename io::R;
-  using elem = typename io::elem;
-
-  __shared__ float s_A[NW][SW];
-  __shared__ float s_B[NW][SW];
-  __shared__ unsigned s_R[NW];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const unsigned rows = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.n_strips);
-  const long long W = p.W;
-  const int c_begin = blockIdx.y * CPB;
-  const int c_end = c_begin + CPB < p.n_chunks ? c_begin + CPB : p.n_chunks;
-  float cs[V], k2[V];
-  bool lane_active;
-  {
-    const BwdTile t0 = bwd_tile<V, NW>(p, static_cast<unsigned>(c_begin) * rows + blockIdx.x, wave, lane);
-    lane_active = t0.active;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      cs[j] = 0.0f;
-      k2[j] = 0.0f;
-      if (t0.active) channel_consts(p.lam[t0.ch + j], p.c, cs[j], k2[j]);
-    }
-  }
-  // this lane's lambda-gradient partial over all chunks of the workgroup
-  float dl_acc[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) dl_acc[j] = 0.0f;
-  for (int chunk = c_begin; chunk < c_end; ++chunk) {
-  const unsigned tile = static_cast<unsigned>(chunk) * rows + blockIdx.x;
-  const BwdTile t = bwd_tile<V, NW>(p, tile, wave, lane);
-  const bool active = t.active;
-  const int nvalid = t.nvalid;
-  const unsigned rmask = reset_mask<NW>(p, t.rowbase, t.t0, nvalid, lane);
-  const size_t idx = static_cast<size_t>(tile) * SW + static_cast<size_t>(lane) * V;
-
-  // A step row is addressed as a wave-uniform base (scalar registers) plus
-  // the lane's 32-bit channel offset, so no per-lane 64-bit address math.
-  const long long row0 = t.rowbase + t.t0;
-  const unsigned lane_off = static_cast<unsigned>(t.ch);
-  R_t rx[TS], rgx[TS], rga[TS], rdh[TS];
-#pragma unroll
-  for (int k = 0; k < TS; ++k) {
-    rx[k] = R_t{};
-    rgx[k] = R_t{};
-    rga[k] = R_t{};
-    rdh[k] = R_t{};
-    if (active && k < nvalid) {
-      const long long ro = (row0 + k) * W;
-      rx[k] = io::load_nt32(static_cast<const elem*>(p.x) + ro, lane_off);
-      rgx[k] = io::load_nt32(static_cast<const elem*>(p.gx) + ro, lane_off);
-      rga[k] = io::load_nt32(static_cast<const elem*>(p.ga) + ro, lane_off);
-      rdh[k] = io::load_nt32(static_cast<const elem*>(p.dh) + ro, lane_off);
-    }
-  }
-  float h[V], cin[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    h[j] = 0.0f;
-    cin[j] = 0.0f;
-  }
-  if (active && nvalid > 0) {
-    load_f32v<V>(p.ckpt + (static_cast<long long>(t.b) * p.n_ckpt + t.t0 / kCkpt) * W + t.ch, h);
-  }
-  if (active) {
-#pragma unroll
-    for (int j = 0; j < V; ++j) cin[j] = word_value(p.carry[idx + j]);
-  }
-
-  // Recompute the forward through this wave's steps and turn every step into
-  // the coefficients the reverse pass needs:
-  //   g = G + dh;  dx = g*cx;  dgate_x = g*cgx;  dgate_a = g*cga;
-  //   lambda-gradient partial += g*cl;  G <- alpha*g  (0 after a reset token)
-  // with dl = g * a*(h_prev - a*i*x/m) off reset tokens (0 on them), and
-  // dgate_a = dl * c_s * (1 - r) with dl = g*cl. (A copy of this arithmetic
-  // without the reset selects, for tiles without reset tokens, measured
-  // slower: the kernel is not bound by its arithmetic, and twice the code.)
-  float cx[TS][V], cgx[TS][V], cga[TS][V], cl[TS][V], al[TS][V], dhv[TS][V];
-#pragma unroll
-  for (int k = 0; k < TS; ++k) {
-    float xv[V], gxv[V], gav[V];
-    io::unpack(rx[k], xv);
-    io::unpack(rgx[k], gxv);
-    io::unpack(rga[k], gav);
-    io::unpack(rdh[k], dhv[k]);
-    const bool rs = (rmask >> k) & 1u;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const float i = sigmoid_f(gxv[j]);
-      const float r = sigmoid_f(gav[j]);
-      const float y = k2[j] * r;
-      const float a = __builtin_amdgcn_exp2f(y);
-      const float w = one_minus_exp2(y, a) * (1.0f + a);  // 1 - a^2
-      // 1 / m. Below the smallest normal float, w comes from a logit under
-      // about -87 (r = 0 or subnormal, a = 1): m is then under 1e-19, every
-      // gradient through m vanishes in the limit, and v_rsq_f32 would read a
-      // subnormal w as 0 and return inf. Taking 1/m as 0 there keeps inf
-      // and inf * 0 out of the gradients.
-      const float rsq = w >= 1.17549435e-38f ? __builtin_amdgcn_rsqf(w) : 0.0f;
-      const float m = w * rsq;
-      const float mult = rs ? 1.0f : m;
-      const float ix = i * xv[j];
-      const float z = rs ? 0.0f : a * (h[j] - a * ix * rsq);
-      const float uw = mult * ix;
-      h[j] = rs ? uw : fmaf(a, h[j], uw);
-      cx[k][j] = mult * i;
-      cgx[k][j] = uw * (1.0f - i);
-      cl[k][j] = z * r;
-      cga[k][j] = cl[k][j] * fmaf(-cs[j], r, cs[j]);
-      al[k][j] = rs ? 0.0f : a;
-    }
-  }
-
-  // this wave's reverse map G_in -> G_out
-  float A[V], Bv[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    A[j] = 1.0f;
-    Bv[j] = 0.0f;
-  }
-#pragma unroll
-  for (int k = TS - 1; k >= 0; --k) {
-    if (k < nvalid) {
-      const bool rs = (rmask >> k) & 1u;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const float gB = Bv[j] + dhv[k][j];
-        Bv[j] = rs ? 0.0f : al[k][j] * gB;
-        A[j] = rs ? 0.0f : al[k][j] * A[j];
-      }
-    }
-  }
-  __syncthreads();   // every wave is done with the previous chunk's maps
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    s_A[wave][lane * V + j] = A[j];
-    s_B[wave][lane * V + j] = Bv[j];
-  }
-  if (lane == 0) s_R[wave] = rmask != 0u ? 1u : 0u;
-  __syncthreads();
-
-  if (active) {
-    // carry at this wave's last step: the tile's carry through the later waves
-    float G[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) G[j] = cin[j];
-    for (int w = NW - 1; w > wave; --w) {
-      const bool Rw = s_R[w] != 0u;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        G[j] = Rw ? s_B[w][lane * V + j] : fmaf(s_A[w][lane * V + j], G[j], s_B[w][lane * V + j]);
-      }
-    }
-#pragma unroll
-    for (int k = TS - 1; k >= 0; --k) {
-      if (k < nvalid) {
-        const bool rs = (rmask >> k) & 1u;
-        float ox[V], ogx[V], oga[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const float g = G[j] + dhv[k][j];
-          ox[j] = g * cx[k][j];
-          ogx[j] = g * cgx[k][j];
-          oga[j] = g * cga[k][j];
-          dl_acc[j] = fmaf(g, cl[k][j], dl_acc[j]);
-          G[j] = rs ? 0.0f : al[k][j] * g;
+    };
+    // One iteration: recompute t_i into the ring slot (ccx..cdh, crm), then
+    // the reverse pass of t_{i-1} from (pcx..pdh, prm). Returns false past
+    // the last tile.
+    auto iteration = [=](int i, float (&ccx)[TS], float (&ccgx)[TS], float (&ccga)[TS], float (&ccl)[TS],
+                         float (&cal)[TS], float (&cdh)[TS], unsigned& crm, const float (&pcx)[TS],
+                         const float (&pcgx)[TS], const float (&pcga)[TS], const float (&pcl)[TS],
+                         const float (&pal)[TS], const float (&pdh)[TS], unsigned prm, Pending& pend) -> bool {
+      const int cb = i & 1;
+      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      if (lds_load(&s_abort) != 0) return false;
+      const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
+      const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 1) % RING]) : p.n_tiles);
+      if (tc.valid) {
+        lds_wait<true>(&s_full[cb], i, &s_abort, p.hdr);
+        const int nvalid = wave_steps(tc, wave);
+        unsigned rmask = 0;
+        if (p.reset != nullptr) {
+          const bool f = lane < nvalid && s_rflag[cb][wave * TS + (lane < TS ? lane : 0)] != 0u;
+          rmask = static_cast<unsigned>(__ballot(f));
         }
-        const long long ro = (row0 + k) * W;
-        io::store_nt32(static_cast<elem*>(p.dx) + ro, lane_off, io::pack(ox));
-        io::store_nt32(static_cast<elem*>(p.dgx) + ro, lane_off, io::pack(ogx));
-        io::store_nt32(static_cast<elem*>(p.dga) + ro, lane_off, io::pack(oga));
+        const float k2 = s_k2[cb][lane];
+        const float cs = s_cs[cb][lane];
+        float h = s_ck[cb][wave][lane];
+        // recompute the forward through the wave's steps and turn every step
+        // into the coefficients of the reverse pass
+#pragma unroll
+        for (int k = 0; k < TS; ++k) {
+          const float xv = to_f32(lds_raw(cb, 0, wave * TS + k));
+          const float iv = sigmoid_f(to_f32(lds_raw(cb, 1, wave * TS + k)));
+          const float r = sigmoid_f(to_f32(lds_raw(cb, 2, wave * TS + k)));
+          cdh[k] = to_f32(lds_raw(cb, 3, wave * TS + k));
+          const bool rs = ((rmask >> k) & 1u) != 0u;
+          const float y = k2 * r;
+          const float a = __builtin_amdgcn_exp2f(y);
+          const float w1 = one_minus_exp2(y, a) * (1.0f + a);  // 1 - a^2
+          // 1 / m. Below the smallest normal float, 1 - a^2 comes from a
+          // logit under about -87 (r = 0 or subnormal, a = 1): m is then under
+          // 1e-19, every gradient through m vanishes in the limit, and
+          // v_rsq_f32 would read a subnormal as 0 and return inf. Taking 1/m
+          // as 0 there keeps inf and inf * 0 out of the gradients.
+          const float rsq = w1 >= 1.17549435e-38f ? __builtin_amdgcn_rsqf(w1) : 0.0f;
+          const float m = w1 * rsq;
+          const float mult = rs ? 1.0f : m;
+          const float ix = iv * xv;
+          const float z = rs ? 0.0f : a * (h - a * ix * rsq);
+          const float uw = mult * ix;
+          h = rs ? uw : fmaf(a, h, uw);
+          ccx[k] = mult * iv;
+          ccgx[k] = uw * (1.0f - iv);
+          ccl[k] = z * r;
+          ccga[k] = ccl[k] * fmaf(-cs, r, cs);
+          cal[k] = rs ? 0.0f : a;
+        }
+        // the wave's reverse map G_in -> G_out, latest step first
+        // (a reset token passes nothing on: a select, so not even a NaN
+        // arriving from a later step crosses it)
+        float A = 1.0f, Bv = 0.0f;
+#pragma unroll
+        for (int k = TS - 1; k >= 0; --k) {
+          if (k < nvalid) {
+            const bool rs = ((rmask >> k) & 1u) != 0u;
+            Bv = rs ? 0.0f : cal[k] * (Bv + cdh[k]);
+            A = rs ? 0.0f : cal[k] * A;
+          }
+        }
+        crm = rmask;
+        s_A[cb][wave][lane] = A;
+        s_B[cb][wave][lane] = Bv;
+        if (lane == 0) s_R[cb][wave] = rmask != 0u ? 1u : 0u;
+        lds_release();
+        if (lane == 0) {
+          lds_add(&s_maps_in[cb], 1);
+          lds_add(&s_cons[cb], 1);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < TS; ++k) ccx[k] = ccgx[k] = ccga[k] = ccl[k] = cal[k] = cdh[k] = 0.0f;
+        crm = 0u;
       }
-    }
-    if (t.chunk == 0 && wave == 0 && p.dh0 != nullptr) store_f32v<V>(p.dh0 + t.b * W + t.ch, G);
-  }
-
-  }   // chunks
-
-  // the workgroup's lambda-gradient partial: each wave's sum over its
-  // chunks in order, then the waves in order (fixed order: deterministic)
-  __syncthreads();
+      flush(pend);
+      if (tp.valid) {
+        // reverse pass of t_{i-1} from the carry entering its last step
+        const int pb = cb ^ 1;
+        lds_wait<false>(&s_carry_ready, i - 1, &s_abort, p.hdr);
+        const int rn = wave_steps(tp, wave);
+        const float c0 = s_carry[pb][lane];
+        const float SA = s_SA[pb][wave][lane];
+        const float SB = s_SB[pb][wave][lane];
+        const bool SR = ((s_SRm[pb] >> wave) & 1u) != 0u;
+        float G = SR ? SB : fmaf(SA, c0, SB);
+        float ox[TS], ogx[TS], oga[TS];
+        float dl = 0.0f;
 #pragma unroll
-  for (int j = 0; j < V; ++j) s_A[wave][lane * V + j] = dl_acc[j];
-  __syncthreads();
-  if (wave == 0 && lane_active) {
-    const size_t gidx = (static_cast<size_t>(blockIdx.y) * rows + blockIdx.x) * SW + static_cast<size_t>(lane) * V;
+        for (int k = TS - 1; k >= 0; --k) {
+          const float g = G + pdh[k];
+          ox[k] = g * pcx[k];
+          ogx[k] = g * pcgx[k];
+          oga[k] = g * pcga[k];
+          const bool in = k < rn;
+          const bool rs = ((prm >> k) & 1u) != 0u;
+          dl = in ? fmaf(g, pcl[k], dl) : dl;
+          G = in ? (rs ? 0.0f : pal[k] * g) : G;
+        }
+        s_dl[pb][wave][lane] = tp.active ? dl : 0.0f;
+        lds_release();
+        if (lane == 0) lds_add(&s_dl_in[pb], 1);
+        if (tp.active) {
+          if (tp.chunk == 0 && wave == 0 && p.dh0 != nullptr) p.dh0[tp.b * W + tp.ch] = G;
+          const long long s0 = tp.t0 + wave * TS;
+          const long long base = (tp.rowbase + s0) * W + static_cast<long long>(tp.strip) * 64;
+          if (STAGE && p.out_wide && (tp.strip + 1) * 64 <= p.W) {
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      float s = 0.0f;
-      for (int w = 0; w < NW; ++w) s += s_A[w][lane * V + j];
-      p.part[gidx + j] = untagged(s);
+            for (int k = 0; k < TS; ++k) {
+              float v0[1] = {ox[k]}, v1[1] = {ogx[k]}, v2[1] = {oga[k]};
+              reinterpret_cast<typename io::R*>(&s_ost[0][0][0])[(wave * 3 + 0) * TS * 64 + k * 64 + lane] = io::pack(v0);
+              reinterpret_cast<typename io::R*>(&s_ost[0][0][0])[(wave * 3 + 1) * TS * 64 + k * 64 + lane] = io::pack(v1);
+              reinterpret_cast<typename io::R*>(&s_ost[0][0][0])[(wave * 3 + 2) * TS * 64 + k * 64 + lane] = io::pack(v2);
+            }
+            pend.base = base;
+            pend.rn = rn;
+            pend.on = true;
+          } else {
+#pragma unroll
+            for (int k = 0; k < TS; ++k) {
+              if (k < rn) {
+                float v0[1] = {ox[k]}, v1[1] = {ogx[k]}, v2[1] = {oga[k]};
+                const long long ro = base + static_cast<long long>(k) * W;
+                io::store_nt32(static_cast<elem*>(p.dx) + ro, static_cast<unsigned>(lane), io::pack(v0));
+                io::store_nt32(static_cast<elem*>(p.dgx) + ro, static_cast<unsigned>(lane), io::pack(v1));
+                io::store_nt32(static_cast<elem*>(p.dga) + ro, static_cast<unsigned>(lane), io::pack(v2));
+              }
+            }
+          }
+        }
+      }
+      return tc.valid;
+    };
+    float cx0[TS], cgx0[TS], cga0[TS], cl0[TS], al0[TS], dh0r[TS];
+    float cx1[TS], cgx1[TS], cga1[TS], cl1[TS], al1[TS], dh1r[TS];
+    unsigned rm0 = 0u, rm1 = 0u;
+#pragma unroll
+    for (int k = 0; k < TS; ++k) cx1[k] = cgx1[k] = cga1[k] = cl1[k] = al1[k] = dh1r[k] = 0.0f;
+    Pending pend{0, 0, false};
+    for (int i = 0;; i += 2) {
+      if (!iteration(i, cx0, cgx0, cga0, cl0, al0, dh0r, rm0, cx1, cgx1, cga1, cl1, al1, dh1r, rm1, pend)) break;
+      if (!iteration(i + 1, cx1, cgx1, cga1, cl1, al1, dh1r, rm1, cx0, cgx0, cga0, cl0, al0, dh0r, rm0, pend)) break;
     }
+    flush(pend);
   }
-
-  // the last workgroup of the call advances the call counter
+  __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned prev = atomicAdd(&p.hdr->done, 1u);
-    if (prev == gridDim.x * gridDim.y - 1) {
+    if (prev == gridDim.x - 1) {
       atomicExch(&p.hdr->done, 0u);
       advance_call(p.hdr);
     }
   }
 }
 
-// Lambda gradient: 64 channels per workgroup, NWR waves each summing a
-// contiguous run of (main-pass workgroup, batch row) partials, then the runs
-// in wave order.
-template <int V>
+// Lambda gradient: each channel's per-tile partials summed over (chunk, batch
+// row) in a fixed order (16 waves take contiguous runs, then the runs in wave
+// order), times sigma(lambda) and -c.
 __global__ __launch_bounds__(1024) void bwd_dlam_kernel(BwdArgs p) {
-  constexpr int SW = 64 * V;
   constexpr int NWR = 16;
   __shared__ float s_sum[NWR][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ch = blockIdx.x * 64 + lane;
   const bool active = ch < p.W;
-  const int strip = ch / SW;
-  const int cin = ch - strip * SW;
-  const int n_parts = p.n_groups * p.B;
+  const int strip = blockIdx.x;
+  const int n_parts = p.n_chunks * p.B;
   const int per = (n_parts + NWR - 1) / NWR;
   const int k0 = wave * per;
   const int k1 = k0 + per < n_parts ? k0 + per : n_parts;
@@ -1552,9 +1642,9 @@ __global__ __launch_bounds__(1024) void bwd_dlam_kernel(BwdArgs p) {
   if (active) {
 #pragma unroll 8
     for (int k = k0; k < k1; ++k) {
-      // k = group * B + b: main-pass workgroup (group, b, strip)
-      const size_t q = (static_cast<size_t>(k) * p.n_strips + strip) * SW + cin;
-      s += word_value(p.part[q]);
+      // k = chunk * B + b: tile (chunk, b, strip)
+      const size_t tile = static_cast<size_t>(k) * p.n_strips + strip;
+      s += p.part[tile * 64 + lane];
     }
   }
   s_sum[wave][lane] = s;
@@ -1720,65 +1810,43 @@ rglru_status_t dispatch_fwd(int T, FwdArgs a, hipStream_t stream) {
   return RGLRU_ERR_UNSUPPORTED;
 }
 
-template <typename IO, int V, int NW>
+template <typename IO, int NW, bool WIDE>
 rglru_status_t launch_bwd(BwdArgs a, hipStream_t stream) {
-  // Chunks of one row per workgroup (the decay constants are evaluated once
-  // for them). The map pass takes two: more workgroups in different phases
-  // than with four, while one evaluates the constants for every chunk
-  // (B=4 L=2048 W=2048: 17.5 us, 19.3 with four, 20.3 with one; equal at
-  // B=8 L=4096 W=2560). The main pass takes four, or two when four would
-  // leave fewer than four rounds of resident workgroups, whose last round
-  // would run mostly empty (B=4 L=2048 W=2048: 1.3 rounds with four; 54.0 us
-  // with two against 57.8 with four, 58.3 with three, 62.0 with one; at
-  // B=8 L=4096 W=2560, 6.7 rounds: 245 us with four, 257 with two).
-  constexpr int CPB_MAP = 2;
-  a.n_strips = static_cast<int>(ceil_div(a.W, 64 * V));
-  a.n_chunks = static_cast<int>(ceil_div(a.L, kCkpt * NW));
+  constexpr int T = NW * kCkpt;
+  a.n_strips = static_cast<int>(ceil_div(a.W, 64));
+  a.n_chunks = static_cast<int>(ceil_div(a.L, T));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  const unsigned rows = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  hipLaunchKernelGGL((bwd_map_kernel<IO, V, NW, CPB_MAP>), dim3(rows, static_cast<unsigned>(ceil_div(a.n_chunks, CPB_MAP))),
-                     dim3(NW * 64), 0, stream, a);
+  auto kernel = bwd_kernel<IO, NW, WIDE>;
+  constexpr int threads = (NW + 3) * 64;
+  const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
+  if (grid == 0) return RGLRU_ERR_HIP;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
   rglru_status_t st = launch_status();
   if (st != RGLRU_OK) return st;
-  const unsigned groups = static_cast<unsigned>(ceil_div(a.W, 64)) * static_cast<unsigned>(a.B);
-  hipLaunchKernelGGL((bwd_carry_kernel<V>), dim3(groups), dim3(1024), 0, stream, a);
-  st = launch_status();
-  if (st != RGLRU_OK) return st;
-  // three waves per SIMD: room for the per-step coefficients without spills
-  auto main4 = bwd_main_kernel<IO, V, NW, 3, 4>;
-  const unsigned slots = resident_blocks(main4, NW * 64);
-  if (slots == 0) return RGLRU_ERR_HIP;
-  const unsigned groups4 = rows * static_cast<unsigned>(ceil_div(a.n_chunks, 4));
-  if (groups4 >= 4u * slots) {
-    a.n_groups = static_cast<int>(ceil_div(a.n_chunks, 4));
-    hipLaunchKernelGGL(main4, dim3(rows, static_cast<unsigned>(a.n_groups)), dim3(NW * 64), 0, stream, a);
-  } else {
-    a.n_groups = static_cast<int>(ceil_div(a.n_chunks, 2));
-    hipLaunchKernelGGL((bwd_main_kernel<IO, V, NW, 3, 2>), dim3(rows, static_cast<unsigned>(a.n_groups)),
-                       dim3(NW * 64), 0, stream, a);
-  }
-  st = launch_status();
-  if (st != RGLRU_OK) return st;
-  hipLaunchKernelGGL((bwd_dlam_kernel<V>), dim3(static_cast<unsigned>(ceil_div(a.W, 64))), dim3(1024), 0,
-                     stream, a);
+  hipLaunchKernelGGL(bwd_dlam_kernel, dim3(static_cast<unsigned>(a.n_strips)), dim3(1024), 0, stream, a);
   return launch_status();
 }
 
-template <typename IO, int V>
-rglru_status_t dispatch_bwd_chunk(int Tb, BwdArgs a, hipStream_t stream) {
-  switch (Tb) {
-    case 8: return launch_bwd<IO, V, 1>(a, stream);
-    case 16: return launch_bwd<IO, V, 2>(a, stream);
-    case 32: return launch_bwd<IO, V, 4>(a, stream);
-    default: break;
-  }
-  return RGLRU_ERR_UNSUPPORTED;
+// Backward tile length for a requested chunk: at most 64 steps where 2-byte
+// rows are loaded 16 bytes per lane (a tile's raw words then fill 32 KiB of
+// LDS and the pipeline holds two), at most 32 otherwise.
+int bwd_tile(int req, bool wide, int io_bytes) {
+  const int cap = (wide && io_bytes == 2) ? 64 : 32;
+  return req < cap ? req : cap;
 }
 
-template <typename IO>
-rglru_status_t dispatch_bwd(int Tb, int V, BwdArgs a, hipStream_t stream) {
-  if (V >= 2) return dispatch_bwd_chunk<IO, 2>(Tb, a, stream);
-  return dispatch_bwd_chunk<IO, 1>(Tb, a, stream);
+template <typename IO, bool WIDE>
+rglru_status_t dispatch_bwd(int T, BwdArgs a, hipStream_t stream) {
+  switch (T) {
+    case 8: return launch_bwd<IO, 1, WIDE>(a, stream);
+    case 16: return launch_bwd<IO, 2, WIDE>(a, stream);
+    case 32: return launch_bwd<IO, 4, WIDE>(a, stream);
+    default: break;
+  }
+  if constexpr (WIDE && std::is_same<IO, BF16>::value) {
+    if (T == 64) return launch_bwd<IO, 8, WIDE>(a, stream);
+  }
+  return RGLRU_ERR_UNSUPPORTED;
 }
 
 bool io_aligned(const void* p, int io_bytes) { return p == nullptr || aligned_to(p, io_bytes); }
@@ -1887,8 +1955,6 @@ rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate
   }
   if (workspace_bytes < bwd_ws(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
 
-  const int V = pick_vec(RGLRU_BWD_VMAX, s->width, g.io_bytes, {x, gate_x, gate_a, dh, dx, dgate_x, dgate_a},
-                         {ckpt, dh_last, dh0});
   const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_b));
   BwdArgs a;
   a.x = x;
@@ -1905,18 +1971,27 @@ rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate
   a.dlam = dlambda;
   a.dh0 = dh0;
   a.hdr = sl.hdr;
-  a.map_a = sl.a;
-  a.map_b = sl.b;
-  a.carry = sl.h;
-  a.part = sl.p;
+  a.slot_a = sl.a;
+  a.slot_b = sl.b;
+  a.slot_h = sl.h;
+  a.part = reinterpret_cast<float*>(sl.p);
   a.L = s->length;
   a.n_ckpt = g.n_ckpt;
   a.B = static_cast<int>(s->batch);
   a.W = static_cast<int>(s->width);
   a.c = s->c;
+  // 16-byte loads: rows a multiple of 16 bytes, the four inputs 16-byte aligned
+  const bool wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(x, 16) && aligned_to(gate_x, 16) &&
+                    aligned_to(gate_a, 16) && aligned_to(dh, 16) && 64LL * s->width * g.io_bytes < (1LL << 31);
+  a.out_wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(dx, 16) && aligned_to(dgate_x, 16) &&
+               aligned_to(dgate_a, 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (s->io_dtype == RGLRU_IO_F32) return dispatch_bwd<F32>(g.Tb, V, a, st);
-  return dispatch_bwd<BF16>(g.Tb, V, a, st);
+  const int req = s->chunk == 0 ? 64 : s->chunk;
+  const int T = bwd_tile(req, wide, g.io_bytes);
+  if (s->io_dtype == RGLRU_IO_F32) {
+    return wide ? dispatch_bwd<F32, true>(T, a, st) : dispatch_bwd<F32, false>(T, a, st);
+  }
+  return wide ? dispatch_bwd<BF16, true>(T, a, st) : dispatch_bwd<BF16, false>(T, a, st);
 }
 
 const char* rglru_status_string(rglru_status_t status) {
