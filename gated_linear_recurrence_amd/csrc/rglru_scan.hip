@@ -288,91 +288,82 @@ __device__ __forceinline__ void advance_call(Header* hdr) {
   __hip_atomic_store(&hdr->counter, static_cast<u64>(next) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Carry entering a tile, computed by one wave (the workgroup's control
-// wave). Each round polls the published words of the K nearest predecessors
+// Carry entering a tile, computed by one wave (a control wave), one channel
+// per lane. A round polls the published words of the K nearest predecessors
 // (tiles of earlier chunks of the same row in the forward, later chunks in the
 // backward) in one memory round trip, finds the nearest one whose outgoing
 // carry is known (published, fixed by a reset inside it, or the sequence
 // start) with every map between published, and applies those maps oldest
 // first with the very fma the predecessors use for their own outgoing
-// carries: the carry is bit-identical to the serial chain whatever the
-// timing. `self` is the slot index of this lane's first channel, `stride` the
-// slot distance between consecutive predecessors, `npred` how many exist.
-// `self` is split into a wave-uniform part and a per-lane part below 2^29 so
-// the polls address a scalar base plus one 32-bit lane offset.
-// Returns false if the spin limit was reached (the carry is then 0).
-template <int V, int K>
+// carries: the carry is bit-identical to the serial chain whatever the timing
+// (deterministic). `self` is the slot index of the lane's channel, split into
+// a wave-uniform part and the lane (the polls address a scalar base plus one
+// 32-bit lane offset); `stride` is the slot distance between consecutive
+// predecessors, `npred` how many exist. Returns whether this lane's carry was
+// found (it is then in `carry`).
+template <int K>
+__device__ __forceinline__ bool look_back_round(const u64* slot_a, const u64* slot_b, const u64* slot_h,
+                                                long long self_uniform, unsigned lane, long long stride, int npred,
+                                                unsigned tag, float init, float& carry) {
+  const unsigned lane_bytes = lane * 8u;
+  u64 wh[K], wa[K], wb[K];
+#pragma unroll
+  for (int d = 0; d < K; ++d) {
+    const long long q = self_uniform - static_cast<long long>(d + 1) * stride;
+    wh[d] = d < npred ? poll_at(slot_h + q, lane_bytes) : 0ull;
+    wa[d] = d < npred ? poll_at(slot_a + q, lane_bytes) : 0ull;
+    wb[d] = d < npred ? poll_at(slot_b + q, lane_bytes) : 0ull;
+  }
+  int start = -1;
+  int kind = 0;     // 1: published carry, 2: map with a reset, 3: sequence start
+  bool open = true; // every nearer map is published
+#pragma unroll
+  for (int d = 0; d < K; ++d) {
+    if (open && start < 0) {
+      if (d >= npred) {
+        start = d;
+        kind = 3;
+      } else if (tagged(wh[d], tag)) {
+        start = d;
+        kind = 1;
+      } else if (!(tagged(wa[d], tag) && tagged(wb[d], tag))) {
+        open = false;
+      } else if ((static_cast<uint32_t>(wa[d]) >> 31) != 0) {
+        start = d;
+        kind = 2;
+      }
+    }
+  }
+  if (start < 0) return false;
+  float hv = 0.0f;
+  bool have = false;
+#pragma unroll
+  for (int d = K - 1; d >= 0; --d) {
+    const float hd = __uint_as_float(static_cast<uint32_t>(wh[d]));
+    const float ad = __uint_as_float(static_cast<uint32_t>(wa[d]) & 0x7FFFFFFFu);
+    const float bd = __uint_as_float(static_cast<uint32_t>(wb[d]));
+    if (d == start) {
+      hv = kind == 1 ? hd : (kind == 2 ? bd : init);
+      have = true;
+    } else if (have) {
+      hv = fmaf(ad, hv, bd);
+    }
+  }
+  carry = hv;
+  return true;
+}
+
+// Rounds until the carry is found; false if the spin limit was reached (the
+// carry is then 0).
+template <int K>
 __device__ __forceinline__ bool look_back_wave(const u64* slot_a, const u64* slot_b, const u64* slot_h,
-                                               long long self_uniform, unsigned self_lane, long long stride,
-                                               int npred, unsigned tag, const float (&init)[V],
-                                               float (&carry)[V]) {
-  const unsigned lane_bytes = self_lane * 8u;
+                                               long long self_uniform, unsigned lane, long long stride, int npred,
+                                               unsigned tag, float init, float& carry) {
   for (unsigned round = 0; round < kSpinLimit; ++round) {
-    u64 wh[K][V], wa[K][V], wb[K][V];
-#pragma unroll
-    for (int d = 0; d < K; ++d) {
-      const long long q = self_uniform - static_cast<long long>(d + 1) * stride;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        wh[d][j] = d < npred ? poll_at(slot_h + q, lane_bytes + 8u * j) : 0ull;
-        wa[d][j] = d < npred ? poll_at(slot_a + q, lane_bytes + 8u * j) : 0ull;
-        wb[d][j] = d < npred ? poll_at(slot_b + q, lane_bytes + 8u * j) : 0ull;
-      }
-    }
-    int start = -1;
-    int kind = 0;     // 1: published carry, 2: map with a reset, 3: sequence start
-    bool open = true; // every nearer map is published
-#pragma unroll
-    for (int d = 0; d < K; ++d) {
-      if (open && start < 0) {
-        if (d >= npred) {
-          start = d;
-          kind = 3;
-        } else {
-          bool hr = true, ar = true;
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            hr = hr && tagged(wh[d][j], tag);
-            ar = ar && tagged(wa[d][j], tag) && tagged(wb[d][j], tag);
-          }
-          if (hr) {
-            start = d;
-            kind = 1;
-          } else if (!ar) {
-            open = false;
-          } else if ((static_cast<uint32_t>(wa[d][0]) >> 31) != 0) {
-            start = d;
-            kind = 2;
-          }
-        }
-      }
-    }
-    if (start >= 0) {
-      float hv[V];
-      bool have = false;
-#pragma unroll
-      for (int d = K - 1; d >= 0; --d) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const float hd = __uint_as_float(static_cast<uint32_t>(wh[d][j]));
-          const float ad = __uint_as_float(static_cast<uint32_t>(wa[d][j]) & 0x7FFFFFFFu);
-          const float bd = __uint_as_float(static_cast<uint32_t>(wb[d][j]));
-          if (d == start) {
-            hv[j] = kind == 1 ? hd : (kind == 2 ? bd : init[j]);
-          } else if (have) {
-            hv[j] = fmaf(ad, hv[j], bd);
-          }
-        }
-        if (d == start) have = true;
-      }
-#pragma unroll
-      for (int j = 0; j < V; ++j) carry[j] = hv[j];
-      return true;
-    }
+    if (look_back_round<K>(slot_a, slot_b, slot_h, self_uniform, lane, stride, npred, tag, init, carry)) return true;
     __builtin_amdgcn_s_sleep(1);
   }
-#pragma unroll
-  for (int j = 0; j < V; ++j) carry[j] = 0.0f;
+  carry = 0.0f;
   return false;
 }
 
@@ -694,6 +685,21 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
       const unsigned tile = __builtin_amdgcn_readfirstlane(s_tk[i % RING]);
       if (tile >= p.n_tiles) break;
       const int ms = i % 3;
+      const Tile t = tile_of(tile);
+      const size_t sidx = static_cast<size_t>(tile) * 64 + lane;
+      const bool last = t.chunk == p.n_chunks - 1;
+      const float init = (t.active && p.h0 != nullptr) ? p.h0[t.b * W + t.ch] : 0.0f;
+      // A look-back needs only the predecessors' words, so one round goes out
+      // before this tile's maps are in: its predecessors are usually far
+      // enough along that the carry is known by the time the maps are, and
+      // the tile then publishes its outgoing carry at once.
+      float carry = init;
+      bool found = true;
+      if (t.active && t.chunk > 0) {
+        found = look_back_round<K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tile) * 64,
+                                   static_cast<unsigned>(lane), static_cast<long long>(rows) * 64, t.chunk, tag, init,
+                                   carry);
+      }
       // once every data wave has reported its map of t_i: the prefixes the
       // replay starts from and the tile's map. A data wave may report up to
       // two iterations ahead of another (its replay of t_{i-2} waits for the
@@ -721,31 +727,23 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
         GR = GR || Rw[w] != 0u;
       }
       if (lane == 0) s_PRm[ms] = prbits;
-      // publish the map (a first chunk publishes its outgoing carry instead),
-      // run the look-back, publish the outgoing carry
-      const Tile t = tile_of(tile);
-      float carry = 0.0f;
+      // otherwise publish the map, finish the look-back; then publish the
+      // outgoing carry (not needed after the last chunk)
       if (t.active) {
-        const size_t sidx = static_cast<size_t>(tile) * 64 + lane;
-        const bool last = t.chunk == p.n_chunks - 1;
-        const float init = p.h0 != nullptr ? p.h0[t.b * W + t.ch] : 0.0f;
-        carry = init;
-        if (t.chunk == 0) {
-          if (!last) publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, init, GB)));
-        } else {
+        if (!found) {
           if (!last) {
             publish(p.slot_a, sidx, tag, encode_a(GA, GR));
             publish(p.slot_b, sidx, tag, __float_as_uint(GB));
           }
-          float in[1] = {init}, out[1];
-          if (!look_back_wave<1, K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tile) * 64,
-                                    static_cast<unsigned>(lane), static_cast<long long>(rows) * 64, t.chunk, tag, in,
-                                    out)) {
+          if (!look_back_wave<K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tile) * 64,
+                                 static_cast<unsigned>(lane), static_cast<long long>(rows) * 64, t.chunk, tag, init,
+                                 carry)) {
             atomicOr(&p.hdr->err, 1u);
           }
-          carry = out[0];
-          if (!last) publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, carry, GB)));
         }
+        if (!last) publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, carry, GB)));
+      } else {
+        carry = 0.0f;
       }
       s_carry[ms][lane] = carry;
       lds_release();
@@ -836,7 +834,24 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
         rn = wave_steps(tr);
       }
       float ck[TS / kCkpt];
-      float hv[TS];
+      // the state after each replayed step goes to the wave's LDS rows as it
+      // is computed (one element per lane and step); 8-step scheduling groups
+      // bound the registers the interleaved chains keep live
+      auto put_h = [=](int k, float v) {
+        float h1[1] = {v};
+        reinterpret_cast<typename io::R*>(&s_hst[wave][0])[k * 64 + lane] = io::pack(h1);
+      };
+      auto replay_step = [&](int k, bool FULL) {
+        if (k % kCkpt == 0) ck[k / kCkpt] = hc;
+        if (FULL) {
+          hc = fmaf(ral[k], hc, ru[k]);
+        } else {
+          const bool rs = ((rrm >> k) & 1u) != 0u;
+          const float nx = rs ? ru[k] : fmaf(ral[k], hc, ru[k]);
+          hc = k < rn ? nx : hc;   // steps past L leave the state as it is
+        }
+        put_h(k, hc);
+      };
       if (tc.valid) {
         lds_wait<true>(&s_full[cb], i, &s_abort, p.hdr);
         const int nvalid = wave_steps(tc);
@@ -878,26 +893,25 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
 #pragma unroll
           for (int k = 0; k < TS; ++k) {
             gate_step(k, true);
-            if (k % kCkpt == 0) ck[k / kCkpt] = hc;
-            hc = fmaf(ral[k], hc, ru[k]);
-            hv[k] = hc;
+            replay_step(k, true);
+            if (k % 8 == 7) __builtin_amdgcn_sched_barrier(0);
           }
         } else {
           if (rmask == 0u && nvalid == TS) {
 #pragma unroll
-            for (int k = 0; k < TS; ++k) gate_step(k, true);
+            for (int k = 0; k < TS; ++k) {
+              gate_step(k, true);
+              if (k % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+            }
           } else {
 #pragma unroll
-            for (int k = 0; k < TS; ++k) gate_step(k, false);
+            for (int k = 0; k < TS; ++k) {
+              gate_step(k, false);
+              if (k % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+            }
           }
 #pragma unroll
-          for (int k = 0; k < TS; ++k) {
-            if (k % kCkpt == 0) ck[k / kCkpt] = hc;
-            const bool rs = ((rrm >> k) & 1u) != 0u;
-            const float nx = rs ? ru[k] : fmaf(ral[k], hc, ru[k]);
-            hc = k < rn ? nx : hc;   // steps past L leave the state as it is
-            hv[k] = hc;
-          }
+          for (int k = 0; k < TS; ++k) replay_step(k, false);
         }
         crm = rmask;
         s_A[ms][wave][lane] = A;
@@ -919,13 +933,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
         }
         crm = 0u;
 #pragma unroll
-        for (int k = 0; k < TS; ++k) {
-          if (k % kCkpt == 0) ck[k / kCkpt] = hc;
-          const bool rs = ((rrm >> k) & 1u) != 0u;
-          const float nx = rs ? ru[k] : fmaf(ral[k], hc, ru[k]);
-          hc = k < rn ? nx : hc;
-          hv[k] = hc;
-        }
+        for (int k = 0; k < TS; ++k) replay_step(k, false);
       }
       if (tr.valid && tr.active) {
         // stores of t_{i-2}: checkpoints, h, and the final state
@@ -938,22 +946,19 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
         }
         elem* hb = static_cast<elem*>(p.h) + (tr.rowbase + s0) * W + static_cast<long long>(tr.strip) * 64;
         if (p.h_wide && (tr.strip + 1) * 64 <= p.W) {
-          // Full strips with 16-byte aligned rows: the wave's rows go to LDS
-          // now and out at the start of the next iteration
-#pragma unroll
-          for (int k = 0; k < TS; ++k) {
-            float h1[1] = {hv[k]};
-            reinterpret_cast<typename io::R*>(&s_hst[wave][0])[k * 64 + lane] = io::pack(h1);
-          }
+          // full strips with 16-byte aligned rows: out 16 bytes per lane at
+          // the start of the next iteration
           pend.hb = hb;
           pend.rn = rn;
           pend.on = true;
         } else {
+          // otherwise each lane stores its own elements, read back from LDS
+          lds_acquire();
 #pragma unroll
           for (int k = 0; k < TS; ++k) {
             if (k < rn) {
-              float h1[1] = {hv[k]};
-              io::store_nt32(hb + static_cast<long long>(k) * W, static_cast<unsigned>(lane), io::pack(h1));
+              const typename io::R v = reinterpret_cast<const typename io::R*>(&s_hst[wave][0])[k * 64 + lane];
+              io::store_nt32(hb + static_cast<long long>(k) * W, static_cast<unsigned>(lane), v);
             }
           }
         }
@@ -1121,7 +1126,7 @@ struct BwdArgs {
 };
 
 template <typename IO, int NW, bool WIDE>
-__global__ __launch_bounds__((NW + 3) * 64) void bwd_kernel(BwdArgs p) {
+__global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
   using elem = typename IO::elem;
   using io = Io<IO, 1>;
   constexpr bool BF = std::is_same<IO, BF16>::value;
@@ -1134,7 +1139,7 @@ __global__ __launch_bounds__((NW + 3) * 64) void bwd_kernel(BwdArgs p) {
   constexpr int K = RGLRU_FWD_LOOKBACK;
   constexpr int RING = 16;
   constexpr int NFL = T < 64 ? 64 : T;
-  constexpr int CTRL = NW, LOAD0 = NW + 1;
+  constexpr int CTRL0 = NW, LOAD0 = NW + 2;
   constexpr int NQ = 4;                    // x, gate_x, gate_a, dh
   constexpr bool STAGE = BF;               // bf16 outputs go out 16 bytes per lane through LDS
   static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
@@ -1162,7 +1167,7 @@ __global__ __launch_bounds__((NW + 3) * 64) void bwd_kernel(BwdArgs p) {
   __shared__ int s_cons[2];
   __shared__ int s_maps_in[2];
   __shared__ int s_dl_in[2];
-  __shared__ int s_carry_ready;
+  __shared__ int s_carry_ok[2];       // iteration whose incoming carry slot s holds
   __shared__ int s_abort;
 
   const int lane = threadIdx.x & 63;
@@ -1176,7 +1181,7 @@ __global__ __launch_bounds__((NW + 3) * 64) void bwd_kernel(BwdArgs p) {
     s_cons[0] = s_cons[1] = 0;
     s_maps_in[0] = s_maps_in[1] = 0;
     s_dl_in[0] = s_dl_in[1] = 0;
-    s_carry_ready = -1;
+    s_carry_ok[0] = s_carry_ok[1] = -1;
     s_abort = 0;
   }
   __syncthreads();
@@ -1329,93 +1334,86 @@ __global__ __launch_bounds__((NW + 3) * 64) void bwd_kernel(BwdArgs p) {
         lds_store(&s_full[j], i);
       }
     }
-  } else if (wave == CTRL) {
-    // ------------------------------------------------------------ control wave
+  } else if (wave >= CTRL0) {
+    // ------------------------------------------------------------ control waves
+    // Control wave c handles the tiles of iterations c, c + 2, ...: once every
+    // data wave has reported t_i, writes the suffix maps its reverse passes
+    // start from and publishes the tile's map (the latest chunk publishes its
+    // outgoing carry instead); runs the look-back and publishes the outgoing
+    // carry; once the data waves have run the reverse pass of t_i (next
+    // iteration), sums their lambda-gradient parts in wave order.
     __builtin_amdgcn_s_setprio(3);
-    float GA = 1.0f, GB = 0.0f;   // reverse map of the previous iteration's tile
-    bool GR = false;
+    const int c = wave - CTRL0;
     unsigned tag = 0;
-    for (int i = 0;; ++i) {
+    for (int i = c;; i += 2) {
       lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
-      if (i == 0) tag = __builtin_amdgcn_readfirstlane(s_tag);
+      if (i == c) tag = __builtin_amdgcn_readfirstlane(s_tag);
       const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
-      const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 1) % RING]) : p.n_tiles);
-      const Tile t2 = tile_of(i > 1 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 2) % RING]) : p.n_tiles);
-      // the carry entering the last step of t_{i-1}, and the carry leaving it
-      if (tp.valid) {
-        float carry = 0.0f;
-        if (tp.active) {
-          const float init = p.dh_last != nullptr ? p.dh_last[tp.b * W + tp.ch] : 0.0f;
-          carry = init;
-          if (tp.chunk < p.n_chunks - 1) {
-            float in[1] = {init}, out[1];
-            if (!look_back_wave<1, K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tp.id) * 64,
-                                      static_cast<unsigned>(lane), -static_cast<long long>(rows) * 64,
-                                      p.n_chunks - 1 - tp.chunk, tag, in, out)) {
-              atomicOr(&p.hdr->err, 1u);
-            }
-            carry = out[0];
-            if (tp.chunk > 0) {
-              publish(p.slot_h, static_cast<size_t>(tp.id) * 64 + lane, tag,
-                      __float_as_uint(GR ? GB : fmaf(GA, carry, GB)));
-            }
-          }
-        }
-        s_carry[(i - 1) & 1][lane] = carry;
-        lds_release();
-        if (lane == 0) lds_store(&s_carry_ready, i - 1);
+      if (!tc.valid) break;
+      const int cb = i & 1;
+      const size_t sidx = static_cast<size_t>(tc.id) * 64 + lane;
+      const bool latest = tc.chunk == p.n_chunks - 1;
+      const float init = (tc.active && p.dh_last != nullptr) ? p.dh_last[tc.b * W + tc.ch] : 0.0f;
+      // one look-back round before this tile's maps are in (it needs only the
+      // later chunks' words)
+      float carry = init;
+      bool found = true;
+      if (tc.active && !latest) {
+        found = look_back_round<K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tc.id) * 64,
+                                   static_cast<unsigned>(lane), -static_cast<long long>(rows) * 64,
+                                   p.n_chunks - 1 - tc.chunk, tag, init, carry);
       }
-      // the lambda-gradient partial of t_{i-2}: the waves' parts in wave order
-      if (t2.valid) {
-        const int pb = (i - 2) & 1;
-        lds_wait<false>(&s_dl_in[pb], NW * ((i - 2) / 2 + 1), &s_abort, p.hdr);
-        float s = 0.0f;
+      // a data wave may report t_{i+1} before another reports t_i (its
+      // reverse pass of t_i waits for this wave), so reports count per parity
+      lds_wait<false>(&s_maps_in[cb], NW * (i / 2 + 1), &s_abort, p.hdr);
+      if (lds_load(&s_abort) != 0) break;
+      float Aw[NW], Bw[NW];
+      unsigned Rw[NW];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) s += s_dl[pb][w][lane];
-        p.part[static_cast<size_t>(t2.id) * 64 + lane] = s;
+      for (int w = 0; w < NW; ++w) {
+        Rw[w] = s_R[cb][w];
+        Aw[w] = s_A[cb][w][lane];
+        Bw[w] = s_B[cb][w][lane];
       }
-      if (!tp.valid && !tc.valid) break;
-      if (tc.valid) {
-        // once every data wave has reported t_i: the suffix maps its reverse
-        // passes start from, the tile's map and its publication (the latest
-        // chunk publishes its outgoing carry instead)
-        const int cb = i & 1;
-        lds_wait<false>(&s_maps_in[cb], NW * (i / 2 + 1), &s_abort, p.hdr);
-        if (lds_load(&s_abort) != 0) break;
-        float Aw[NW], Bw[NW];
-        unsigned Rw[NW];
+      float GA = 1.0f, GB = 0.0f;
+      bool GR = false;
+      unsigned srbits = 0u;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          Rw[w] = s_R[cb][w];
-          Aw[w] = s_A[cb][w][lane];
-          Bw[w] = s_B[cb][w][lane];
-        }
-        GA = 1.0f;
-        GB = 0.0f;
-        GR = false;
-        unsigned srbits = 0u;
-#pragma unroll
-        for (int w = NW - 1; w >= 0; --w) {
-          s_SA[cb][w][lane] = GA;
-          s_SB[cb][w][lane] = GB;
-          srbits |= GR ? (1u << w) : 0u;
-          GB = Rw[w] != 0u ? Bw[w] : fmaf(Aw[w], GB, Bw[w]);
-          GA *= Aw[w];
-          GR = GR || Rw[w] != 0u;
-        }
-        if (lane == 0) s_SRm[cb] = srbits;
-        if (tc.active && tc.chunk > 0) {
-          const size_t sidx = static_cast<size_t>(tc.id) * 64 + lane;
-          if (tc.chunk == p.n_chunks - 1) {
-            const float init = p.dh_last != nullptr ? p.dh_last[tc.b * W + tc.ch] : 0.0f;
-            publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, init, GB)));
-          } else {
+      for (int w = NW - 1; w >= 0; --w) {
+        s_SA[cb][w][lane] = GA;
+        s_SB[cb][w][lane] = GB;
+        srbits |= GR ? (1u << w) : 0u;
+        GB = Rw[w] != 0u ? Bw[w] : fmaf(Aw[w], GB, Bw[w]);
+        GA *= Aw[w];
+        GR = GR || Rw[w] != 0u;
+      }
+      if (lane == 0) s_SRm[cb] = srbits;
+      if (tc.active) {
+        if (!found) {
+          if (tc.chunk > 0) {
             publish(p.slot_a, sidx, tag, encode_a(GA, GR));
             publish(p.slot_b, sidx, tag, __float_as_uint(GB));
           }
+          if (!look_back_wave<K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tc.id) * 64,
+                                 static_cast<unsigned>(lane), -static_cast<long long>(rows) * 64,
+                                 p.n_chunks - 1 - tc.chunk, tag, init, carry)) {
+            atomicOr(&p.hdr->err, 1u);
+          }
         }
+        if (tc.chunk > 0) publish(p.slot_h, sidx, tag, __float_as_uint(GR ? GB : fmaf(GA, carry, GB)));
+      } else {
+        carry = 0.0f;
       }
+      s_carry[cb][lane] = carry;
+      lds_release();
+      if (lane == 0) lds_store(&s_carry_ok[cb], i);
+      // the tile's lambda-gradient partial: the waves' parts in wave order
+      lds_wait<false>(&s_dl_in[cb], NW * (i / 2 + 1), &s_abort, p.hdr);
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += s_dl[cb][w][lane];
+      p.part[static_cast<size_t>(tc.id) * 64 + lane] = sum;
     }
   } else {
     // ------------------------------------------------------------ data waves
@@ -1547,7 +1545,7 @@ __global__ __launch_bounds__((NW + 3) * 64) void bwd_kernel(BwdArgs p) {
       if (tp.valid) {
         // reverse pass of t_{i-1} from the carry entering its last step
         const int pb = cb ^ 1;
-        lds_wait<false>(&s_carry_ready, i - 1, &s_abort, p.hdr);
+        lds_wait<true>(&s_carry_ok[pb], i - 1, &s_abort, p.hdr);
         const int rn = wave_steps(tp, wave);
         const float c0 = s_carry[pb][lane];
         const float SA = s_SA[pb][wave][lane];
@@ -1817,7 +1815,7 @@ rglru_status_t launch_bwd(BwdArgs a, hipStream_t stream) {
   a.n_chunks = static_cast<int>(ceil_div(a.L, T));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
   auto kernel = bwd_kernel<IO, NW, WIDE>;
-  constexpr int threads = (NW + 3) * 64;
+  constexpr int threads = (NW + 4) * 64;
   const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
   if (grid == 0) return RGLRU_ERR_HIP;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);

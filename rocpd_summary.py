@@ -1,15 +1,15 @@
 """Summaries of rocprofv3 databases (rocpd SQLite) for this library's kernels.
 
-    python -m gated_linear_recurrence_amd.rocpd_summary kernels RUN_results.db
+    python rocpd_summary.py kernels RUN_results.db
         per-kernel calls and durations of a --kernel-trace run (markdown table)
 
-    python -m gated_linear_recurrence_amd.rocpd_summary traffic FETCH.db WRITE.db CALIB_MIB
+    python rocpd_summary.py traffic FETCH.db WRITE.db CALIB_MIB
         per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of two --pmc runs,
         each scaled by what the same counter read for the largest plain copy
         (__amd_rocclr_copyBuffer) of CALIB_MIB MiB in the same run; prints a
         markdown table and a JSON object of bytes per dispatch
 
-    python -m gated_linear_recurrence_amd.rocpd_summary traffic-json FETCH.db WRITE.db CALIB_MIB WORKLOAD OUT.json SOURCE
+    python rocpd_summary.py traffic-json FETCH.db WRITE.db CALIB_MIB WORKLOAD OUT.json SOURCE
         the same figures summed per library call (forward scan, backward scan,
         projection forward, projection backward) and merged into OUT.json
         under "WORKLOAD:fwd", ":bwd", ":proj_fwd", ":proj_bwd" (the file
