@@ -3,6 +3,8 @@ from . import _lib
 from ._lib import RglruError, header_symbols  # noqa: F401
 from .ops import (  # noqa: F401
     Workspace,
+    WorkspaceError,
+    check_errors,
     make_shape,
     rglru,
     rglru_blockdiag_gate_proj_bwd,

@@ -614,9 +614,6 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
               lds_dma16(base + off, dst);
               off += step;
               dst += 1024;
-#ifdef RGLRU_DMA_THROTTLE
-              if ((g & 7) == 7) __builtin_amdgcn_s_waitcnt(RGLRU_DMA_THROTTLE);
-#endif
             }
           }
         } else {

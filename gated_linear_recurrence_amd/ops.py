@@ -8,6 +8,7 @@ HIP kernels; nothing here computes.
 from __future__ import annotations
 
 import ctypes
+import weakref
 from typing import Optional
 
 import torch
@@ -75,6 +76,7 @@ class Workspace:
     def __init__(self, device=None):
         self.device = torch.device(device if device is not None else "cuda")
         self.buf = None
+        _workspaces.add(self)
 
     def get(self, nbytes: int) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes:
@@ -82,10 +84,50 @@ class Workspace:
         return self.buf
 
     def error_bits(self) -> int:
-        """Sticky error word of the header (bit 0: a look-back wait hit its spin limit)."""
+        """Sticky error word of the header (synchronises with the device).
+
+        Bit 0: a wait for another workgroup's published prefix hit its spin
+        limit. Bit 1: a wait between the waves of one workgroup hit its spin
+        limit. Either invalidates the outputs of the call that set it.
+        """
         if self.buf is None:
             return 0
-        return int(self.buf[12:16].view(torch.int32).item())
+        return int(self.buf[12:16].view(torch.int32).item()) & 0xFFFFFFFF
+
+    def raise_if_error(self) -> None:
+        """Raises WorkspaceError if any call on this workspace set an error bit."""
+        bits = self.error_bits()
+        if bits:
+            raise WorkspaceError(bits)
+
+    def clear_errors(self) -> None:
+        """Zeroes the sticky error word (on the current stream)."""
+        if self.buf is not None:
+            self.buf[12:16].zero_()
+
+
+class WorkspaceError(RuntimeError):
+    """A scan's bounded wait ran out: the outputs of that call are invalid."""
+
+    def __init__(self, bits: int):
+        kinds = []
+        if bits & 1:
+            kinds.append("cross-workgroup look-back wait hit its spin limit")
+        if bits & 2:
+            kinds.append("wait between waves of a workgroup hit its spin limit")
+        if bits & ~3:
+            kinds.append(f"unknown bits {bits & ~3:#x}")
+        super().__init__("rglru workspace error word %#x: %s" % (bits, "; ".join(kinds)))
+        self.bits = bits
+
+
+_workspaces = weakref.WeakSet()
+
+
+def check_errors() -> None:
+    """Raises WorkspaceError if any live workspace (the defaults included) holds an error bit."""
+    for ws in list(_workspaces):
+        ws.raise_if_error()
 
 
 _default_ws = {}

@@ -43,10 +43,14 @@
  *    Layout of its first 16 bytes (read-only for callers): a 64-bit counter
  *    (high half: completed calls, which skips 0xFFFFFFFF; low half: tiles
  *    handed out during a forward), a 32-bit count of finished workgroups, and
- *    a 32-bit sticky error word whose bit 0 is
- *    set if a look-back wait ever exceeded its spin limit (the outputs of that
- *    call are then invalid; it cannot happen while every launched workgroup
- *    makes progress).
+ *    a 32-bit sticky error word. Bit 0 is set if a wait for another
+ *    workgroup's published prefix (the look-back across tiles) exceeded its
+ *    spin limit; bit 1 if a wait between the waves of one workgroup (on a
+ *    flag in LDS) exceeded its spin limit. Either makes the outputs of that
+ *    call invalid, and neither can happen while every launched workgroup
+ *    makes progress. The library never clears the word; the caller reads it
+ *    (after the call has completed) to check, and zero-fills the workspace to
+ *    clear it.
  */
 #ifndef RGLRU_H_
 #define RGLRU_H_
@@ -81,10 +85,21 @@ typedef struct {
   int64_t length;   /* L >= 1 */
   int64_t width;    /* W >= 1, any value */
   int32_t io_dtype; /* rglru_io_t */
-  int32_t chunk;    /* time tile of the parallel scan: 0 = library default (64),
-                       or one of 8, 16, 32, 64, 128, 256. Results depend on it
-                       only through floating-point rounding. The forward uses
-                       min(chunk, 64), the backward min(chunk, 32). */
+  int32_t chunk;    /* requested time tile of the parallel scan: 0 = library
+                       default, or one of 8, 16, 32, 64, 128, 256 (anything
+                       else is RGLRU_ERR_INVALID_ARGUMENT). Results depend on
+                       it only through floating-point rounding. The request is
+                       an upper bound that each direction clamps to the
+                       longest tile it implements for the call:
+                         forward : default 128; at most 128 for bf16 io whose
+                                   rows (W * 2 bytes) are a multiple of 16
+                                   bytes with x, gate_x, gate_a 16-byte aligned,
+                                   at most 64 otherwise.
+                         backward: default 64; at most 64 under the same
+                                   bf16 condition (dh aligned too), at most 32
+                                   otherwise.
+                       A clamped request is not an error: it runs the
+                       clamped tile and returns RGLRU_OK. */
   float c;          /* decay scale of a = exp(-c * softplus(lambda) * r); 8 in the method */
   int32_t reserved; /* must be 0 */
 } rglru_shape_t;

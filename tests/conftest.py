@@ -21,3 +21,18 @@ def gpu_lib():
     import gated_linear_recurrence_amd as glr
     glr.load_library()
     return glr
+
+
+@pytest.fixture(autouse=True)
+def _no_workspace_errors(request):
+    """After every GPU test: no scan call may have left an error bit in any live workspace.
+
+    The error word is sticky, so a bounded wait that ran out anywhere in the
+    test (a look-back across workgroups or a wait between the waves of one)
+    fails the test that caused it.
+    """
+    yield
+    if request.node.get_closest_marker("gpu") is None:
+        return
+    import gated_linear_recurrence_amd as glr
+    glr.check_errors()

@@ -135,6 +135,59 @@ def test_hand_built_resets_backward():
     assert out["dh0"][0, 0] == 0.0
 
 
+def _golden_half():
+    with open(os.path.join(GOLDEN, "half_gates_hand.json")) as f:
+        return json.load(f)
+
+
+def _half_inputs(g):
+    inp = g["inputs"]
+    L = len(inp["x"])
+    x = np.array(inp["x"]).reshape(1, L, 1)
+    gx = np.full((1, L, 1), inp["gate_x"])
+    ga = np.full((1, L, 1), inp["gate_a"])
+    lam = np.array([_expr(inp["lam_expr"])])
+    h0 = np.array([[inp["h0"]]])
+    dh = np.array(inp["dh"]).reshape(1, L, 1)
+    dh_last = np.array([[inp["dh_last"]]])
+    return x, gx, ga, lam, h0, dh, dh_last
+
+
+def test_half_gates_fixture_is_self_consistent():
+    g = _golden_half()
+    for e, v in zip(g["forward"]["h_expr"], g["forward"]["h"]):
+        assert abs(_expr(e) - v) <= 1e-15 * max(1.0, abs(v))
+    bw = g["backward"]
+    for k in ("dx", "dgx", "dga"):
+        for e, v in zip(bw[k + "_expr"], bw[k]):
+            assert abs(_expr(e) - v) <= 1e-15 * max(1.0, abs(v)), k
+    assert abs(_expr(bw["dlam_expr"]) - bw["dlam"]) <= 1e-15
+    assert _expr(bw["dh0_expr"]) == bw["dh0"]
+
+
+def test_half_gates_forward():
+    # gates at 0: the sigmoids give exactly 1/2 and a is exactly 1/2
+    g = _golden_half()
+    x, gx, ga, lam, h0, _, _ = _half_inputs(g)
+    h, h_last = oracle.rglru_forward(x, gx, ga, lam, None, h0, c=g["inputs"]["c"])
+    expect = [_expr(e) for e in g["forward"]["h_expr"]]
+    np.testing.assert_allclose(h[0, :, 0], expect, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(h_last[0], [_expr(g["forward"]["h_last_expr"])], rtol=1e-14)
+
+
+def test_half_gates_backward():
+    # every gradient of the hand derivation, nonzero gate derivatives included
+    g = _golden_half()
+    x, gx, ga, lam, h0, dh, dh_last = _half_inputs(g)
+    out = oracle.rglru_backward(x, gx, ga, lam, dh, None, h0, dh_last, c=g["inputs"]["c"])
+    bw = g["backward"]
+    for k in ("dx", "dgx", "dga"):
+        expect = [_expr(e) for e in bw[k + "_expr"]]
+        np.testing.assert_allclose(out[k][0, :, 0], expect, rtol=1e-14, atol=1e-14, err_msg=k)
+    np.testing.assert_allclose(out["dlam"], [_expr(bw["dlam_expr"])], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out["dh0"][0], [_expr(bw["dh0_expr"])], rtol=1e-14, atol=1e-14)
+
+
 # --------------------------------------------------------------- stationarity
 
 @pytest.mark.parametrize("with_h0", [False, True])
