@@ -9,11 +9,17 @@
         (__amd_rocclr_copyBuffer) of CALIB_MIB MiB in the same run; prints a
         markdown table and a JSON object of bytes per dispatch
 
-    python rocpd_summary.py traffic-json FETCH.db WRITE.db CALIB_MIB WORKLOAD OUT.json SOURCE
+    python rocpd_summary.py traffic-json FETCH.db WRITE.db CALIB_MIB WORKLOAD OUT.json SOURCE [COMMIT]
         the same figures summed per library call (forward scan, backward scan,
         projection forward, projection backward) and merged into OUT.json
         under "WORKLOAD:fwd", ":bwd", ":proj_fwd", ":proj_bwd" (the file
-        bench.py reads); SOURCE names the summary the figures come from
+        bench.py reads); SOURCE names the summary the figures come from and
+        COMMIT the source revision of the kernels that were counted
+
+    python rocpd_summary.py counters TRACE.db PMC.db [PMC.db ...]
+        per-kernel averages of every counter in the --pmc runs, with the
+        kernel's average duration from the --kernel-trace run and derived
+        ratios (VALU busy, wave time waiting, LDS bank conflicts)
 
 Only the standard library is used; nothing here runs on the GPU.
 """
@@ -76,13 +82,14 @@ def traffic(fetch_db: str, write_db: str, calib_mib: float):
 # kernels of each library call (matched on the kernel name)
 GROUPS = {
     "fwd": ("fwd_kernel<",),
-    "bwd": ("bwd_map_kernel<", "bwd_carry_kernel<", "bwd_main_kernel<", "bwd_dlam_kernel<"),
+    "bwd": ("bwd_kernel<", "bwd_dlam_kernel("),
     "proj_fwd": ("proj_fwd_kernel(",),
     "proj_bwd": ("proj_dw_kernel(", "proj_dw_reduce_kernel(", "proj_dx_kernel<"),
 }
 
 
-def traffic_json(fetch_db: str, write_db: str, calib_mib: float, workload: str, out: str, source: str):
+def traffic_json(fetch_db: str, write_db: str, calib_mib: float, workload: str, out: str, source: str,
+                 commit: str = None):
     _, per = traffic(fetch_db, write_db, calib_mib)
     try:
         with open(out) as f:
@@ -97,10 +104,53 @@ def traffic_json(fetch_db: str, write_db: str, calib_mib: float, workload: str, 
         wb = sum(per[n]["write_bytes"] for n in names)
         doc[f"{workload}:{group}"] = {"bytes": rb + wb, "read_bytes": rb, "write_bytes": wb,
                                       "kernels": sorted(names), "source": source}
+        if commit:
+            doc[f"{workload}:{group}"]["commit"] = commit
     with open(out, "w") as f:
         json.dump(doc, f, indent=1)
         f.write("\n")
     return doc
+
+
+N_SIMD = 1024    # 256 CUs x 4 SIMDs
+
+
+def counters(trace_db: str, pmc_dbs) -> str:
+    """Per-kernel counter averages and derived ratios (library kernels only)."""
+    con = sqlite3.connect(trace_db)
+    dur = {n: d for n, d in con.execute("select name, avg(duration) from kernels group by name")}
+    vals = {}
+    for db in pmc_dbs:
+        c = sqlite3.connect(db)
+        for n, cn, v in c.execute("""select kernel_name, counter_name, avg(value) from counters_collection
+                                     group by kernel_name, counter_name"""):
+            if "rglru::" in n:
+                vals.setdefault(n, {})[cn] = v
+    names = sorted(vals, key=lambda n: -(dur.get(n) or 0))
+    cols = sorted({k for v in vals.values() for k in v})
+    out = ["| kernel | us | " + " | ".join(cols) + " |", "|---|---|" + "---|" * len(cols)]
+    for n in names:
+        d = dur.get(n)
+        row = [f"`{_short(n)}`", f"{d / 1e3:.2f}" if d else "-"]
+        row += [f"{vals[n].get(k, float('nan')):.4g}" for k in cols]
+        out.append("| " + " | ".join(row) + " |")
+    out += ["", "| kernel | VALU busy | wave cycles waiting on a dependency | LDS bank-conflict cycles "
+            "per LDS instruction | SQ busy / GPU busy cycles | TA stalled by TC |", "|---|---|---|---|---|---|"]
+
+    def ratio(a, b):
+        return f"{a / b:.3f}" if a is not None and b else "-"
+
+    for n in names:
+        v = vals[n]
+        gui = v.get("GRBM_GUI_ACTIVE")
+        valu = v.get("SQ_ACTIVE_INST_VALU")
+        # VALU busy as rocprof has long defined it: 4 * SQ_ACTIVE_INST_VALU / SIMDs / GPU-busy cycles
+        vb = ratio(4 * valu / N_SIMD if valu is not None else None, gui)
+        out.append(f"| `{_short(n)}` | {vb} | {ratio(v.get('SQ_WAIT_INST_ANY'), v.get('SQ_WAVE_CYCLES'))} | "
+                   f"{ratio(v.get('SQ_LDS_BANK_CONFLICT'), v.get('SQ_INSTS_LDS'))} | "
+                   f"{ratio(v.get('SQ_BUSY_CYCLES'), gui)} | "
+                   f"{ratio(v.get('TA_ADDR_STALLED_BY_TC_CYCLES'), v.get('TA_BUSY'))} |")
+    return "\n".join(out)
 
 
 def main(argv):
@@ -112,8 +162,11 @@ def main(argv):
         print()
         print(json.dumps(per, indent=1))
     elif len(argv) >= 7 and argv[0] == "traffic-json":
-        doc = traffic_json(argv[1], argv[2], float(argv[3]), argv[4], argv[5], argv[6])
+        doc = traffic_json(argv[1], argv[2], float(argv[3]), argv[4], argv[5], argv[6],
+                           argv[7] if len(argv) >= 8 else None)
         print(json.dumps(doc, indent=1))
+    elif len(argv) >= 3 and argv[0] == "counters":
+        print(counters(argv[1], argv[2:]))
     else:
         print(__doc__)
         return 2
