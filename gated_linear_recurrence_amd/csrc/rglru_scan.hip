@@ -226,10 +226,12 @@ __device__ __forceinline__ float one_minus_exp2(float y, float a) {
 }
 
 // softplus(lambda) = max(lambda, 0) + log1p(e^-|lambda|) on the hardware exp2
-// and log2. log1p(z) is taken as ln(1 + z) * z / ((1 + z) - 1), which cancels
-// the rounding of 1 + z (the classic correction, a few ulp), and as z itself
-// where 1 + z rounds to 1. About a third of the instructions of the library
-// expf and log1pf, which the load wave runs for every tile.
+// and log2. log1p(z) uses Kahan's formulation, ln(1 + z) * z / ((1 + z) - 1),
+// which cancels the rounding of 1 + z (Goldberg, "What Every Computer
+// Scientist Should Know About Floating-Point Arithmetic", 1991, Theorem 4: a
+// few ulp), and z itself where 1 + z rounds to 1. About a third of the
+// instructions of the library expf and log1pf, which the load wave runs for
+// every tile.
 __device__ __forceinline__ float softplus_f(float lam) {
   const float z = __builtin_amdgcn_exp2f(-kLog2e * fabsf(lam));
   const float u = 1.0f + z;
@@ -1066,24 +1068,28 @@ __global__ __launch_bounds__(256) void fwd_serial_kernel(FwdArgs p) {
 // T = NW * 8 steps, wave w owning steps 8w .. 8w+7 (one checkpoint interval,
 // whose entering state the forward stored). The carry a tile needs enters its
 // last step from the later chunks, so the look-back runs over later chunks.
-// A workgroup has NW data waves, one control wave and two load waves, joined
+// A workgroup has NW data waves, two control waves and two load waves, joined
 // by one-directional LDS flags. With t_i the workgroup's i-th tile:
-//   load wave i%2 : once every data wave has finished with LDS buffer i%2,
-//                   streams the raw words of t_i (x, gate_x, gate_a, dh), the
-//                   checkpoint rows and the reset flags into it with
-//                   global_load_lds and evaluates the decay constants;
-//   data waves    : in iteration i, recompute the forward through their steps
-//                   of t_i from the checkpoint, keep six coefficients per step
-//                   (a register ring of two tiles), reduce their steps to the
-//                   reverse map G -> R ? B : A*G + B and report it; then wait
-//                   for the carry of t_{i-1} and run its reverse pass, writing
-//                   dx, dgate_x and dgate_a and reporting the wave's part of
-//                   the tile's lambda gradient;
-//   control wave  : runs the look-back of t_{i-1} and publishes its outgoing
-//                   carry; sums the lambda-gradient parts of t_{i-2} in wave
-//                   order into the tile's partial; once every data wave has
-//                   reported t_i, writes the suffix maps each wave's reverse
-//                   pass starts from and publishes the tile's map.
+//   load wave i%2 : once the data waves are done with the buffers t_i goes
+//                   to, streams its raw gate_a and dh words into buffer i%2,
+//                   its x and gate_x words and checkpoint rows into buffer
+//                   i%4, and the reset flags, with global_load_lds, and
+//                   evaluates the decay constants;
+//   data waves    : in iteration i, turn gate_a and dh of their steps of t_i
+//                   into the decays a and keep (a, r, dh) per step (a register
+//                   ring of three tiles), reduce their steps to the reverse
+//                   map G -> R ? B : A*G + B and report it; then wait for the
+//                   carry of t_{i-2}, recompute the forward through their
+//                   steps of it from the checkpoint and run its reverse pass,
+//                   writing dx, dgate_x and dgate_a; the last wave to finish
+//                   sums the waves' lambda-gradient parts in wave order into
+//                   the tile's partial;
+//   control wave i%2 : one look-back round ahead of the maps; once every data
+//                   wave has reported t_i, writes the suffix maps each wave's
+//                   reverse pass starts from, publishes the tile's map, runs
+//                   the look-back and publishes the outgoing carry.
+// The carry of t_i is needed two iterations after its maps are in, which
+// hides the look-back's latency behind the work of a whole iteration.
 // Per step, with G the carry arriving from the next step:
 //   g = G + dh;  dx = g*cx;  dgate_x = g*cgx;  dgate_a = g*cga;
 //   lambda partial += g*cl;  G <- alpha*g  (0 through a reset token)
@@ -1137,34 +1143,41 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
   constexpr int RING = 16;
   constexpr int NFL = T < 64 ? 64 : T;
   constexpr int CTRL0 = NW, LOAD0 = NW + 2;
-  constexpr int NQ = 4;                    // x, gate_x, gate_a, dh
   constexpr bool STAGE = BF;               // bf16 outputs go out 16 bytes per lane through LDS
   static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
   static_assert(NFL % 64 == 0 && NFL <= 128, "reset flags: at most two instructions");
   static_assert(NW <= 32, "reset flags of the waves fit one mask word");
 
-  __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][NQ][T][ROWB];
-  __shared__ __attribute__((aligned(16))) float s_ck[2][NW][64];   // state entering each wave's first step
+  // raw words: gate_a and dh feed a tile's maps (buffer i % 2), x and gate_x
+  // its reverse pass two iterations later (buffer i % 4, with the checkpoint
+  // rows and the decay constants)
+  __shared__ __attribute__((aligned(16))) unsigned char s_rm[2][2][T][ROWB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_rx[4][2][T][ROWB];
+  __shared__ __attribute__((aligned(16))) float s_ck[4][NW][64];   // state entering each wave's first step
   __shared__ unsigned s_rflag[2][NFL];
-  __shared__ float s_k2[2][64];
-  __shared__ float s_cs[2][64];
-  __shared__ float s_A[2][NW][64];
-  __shared__ float s_B[2][NW][64];
-  __shared__ unsigned s_R[2][NW];
-  __shared__ float s_SA[2][NW][64];   // composite of the maps of the waves after each wave
-  __shared__ float s_SB[2][NW][64];
-  __shared__ unsigned s_SRm[2];       // bit w: a reset inside the waves after wave w
-  __shared__ float s_carry[2][64];
-  __shared__ float s_dl[2][NW][64];   // each wave's part of a tile's lambda gradient
+  __shared__ float s_k2[4][64];
+  __shared__ float s_cs[4][64];
+  // a wave's reverse map; the control wave overwrites it with the composite
+  // of the maps of the waves after that wave (what the wave's reverse pass
+  // starts from)
+  __shared__ float s_A[3][NW][64];
+  __shared__ float s_B[3][NW][64];
+  __shared__ unsigned s_R[3][NW];
+  __shared__ unsigned s_SRm[3];       // bit w: a reset inside the waves after wave w
+  __shared__ float s_carry[3][64];
+  __shared__ float s_dl[3][NW][64];   // each wave's part of a tile's lambda gradient
   __shared__ __attribute__((aligned(16))) elem s_ost[STAGE ? NW : 1][3][TS * 64];
   __shared__ unsigned s_tk[RING];
   __shared__ unsigned s_tag;
   __shared__ int s_tk_valid;
   __shared__ int s_full[2];
-  __shared__ int s_cons[2];
-  __shared__ int s_maps_in[2];
-  __shared__ int s_dl_in[2];
-  __shared__ int s_carry_ok[2];       // iteration whose incoming carry slot s holds
+  __shared__ int s_cons_m[2];         // data-wave maps done on gate_a/dh buffer b
+  __shared__ int s_cons_x[4];         // data-wave reverse passes done on x/gate_x buffer b
+  __shared__ int s_maps_in[3];
+  __shared__ int s_dl_in[3];
+  __shared__ int s_dl_done[3];        // tile (iteration) whose parts slot s last summed
+  __shared__ int s_carry_ok[3];       // iteration whose incoming carry slot s holds
+  __shared__ int s_prog[NW];          // iteration each data wave is in
   __shared__ int s_abort;
 
   const int lane = threadIdx.x & 63;
@@ -1175,10 +1188,17 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
   if (threadIdx.x == 0) {
     s_tk_valid = -1;
     s_full[0] = s_full[1] = -1;
-    s_cons[0] = s_cons[1] = 0;
-    s_maps_in[0] = s_maps_in[1] = 0;
-    s_dl_in[0] = s_dl_in[1] = 0;
-    s_carry_ok[0] = s_carry_ok[1] = -1;
+    s_cons_m[0] = s_cons_m[1] = 0;
+    s_cons_x[0] = s_cons_x[1] = s_cons_x[2] = s_cons_x[3] = 0;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      s_maps_in[s] = 0;
+      s_dl_in[s] = 0;
+      s_dl_done[s] = s - 3;
+      s_carry_ok[s] = -1;
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s_prog[w] = -1;
     s_abort = 0;
   }
   __syncthreads();
@@ -1231,19 +1251,26 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       lds_release();
       if (lane == 0) lds_store(&s_tk_valid, 1);
     }
-    const unsigned char* src[NQ] = {
-        static_cast<const unsigned char*>(p.x), static_cast<const unsigned char*>(p.gx),
-        static_cast<const unsigned char*>(p.ga), static_cast<const unsigned char*>(p.dh)};
+    const unsigned char* src[4] = {
+        static_cast<const unsigned char*>(p.ga), static_cast<const unsigned char*>(p.dh),
+        static_cast<const unsigned char*>(p.x), static_cast<const unsigned char*>(p.gx)};
     const long long row_bytes = W * ES;
     for (int i = j;; i += 2) {
+      const int xb = i & 3;
       lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
       const Tile t = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
-      lds_wait<false>(&s_cons[j], NW * (i / 2), &s_abort, p.hdr);
+      // the maps of t_{i-2} and the reverse pass of t_{i-4} are done with
+      // the buffers t_i goes to
+      lds_wait<false>(&s_cons_m[j], NW * (i / 2), &s_abort, p.hdr);
+      lds_wait<false>(&s_cons_x[xb], NW * (i / 4), &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
       if (!t.valid) {
         if (lane == 0) lds_store(&s_full[j], i);
         break;
       }
+      auto dst_of = [&](int q, int row) -> unsigned char* {
+        return q < 2 ? &s_rm[j][q][row][0] : &s_rx[xb][q - 2][row][0];
+      };
       float lam = 0.0f;
       if (t.active) lam = p.lam[t.ch];
       const long long strip_b = static_cast<long long>(t.strip) * 64 * ES;
@@ -1256,10 +1283,10 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
         if (t.t0 + T <= p.L) {
           const unsigned step = static_cast<unsigned>(RPI) * static_cast<unsigned>(row_bytes);
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
+          for (int q = 0; q < 4; ++q) {
             gbyte* base = uniform_gptr(src[q] + tile_off);
             unsigned off = static_cast<unsigned>(r) * static_cast<unsigned>(row_bytes) + col;
-            unsigned char* dst = &s_raw[j][q][0][0];
+            unsigned char* dst = dst_of(q, 0);
 #pragma unroll 4
             for (int g = 0; g < T / RPI; ++g) {
               lds_dma16(base + off, dst);
@@ -1269,12 +1296,12 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
           }
         } else {
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
+          for (int q = 0; q < 4; ++q) {
             gbyte* base = uniform_gptr(src[q] + tile_off);
             for (int g = 0; g < T / RPI; ++g) {
               const long long row = g * RPI + r;
               const long long off = (row < lim ? row : lim) * row_bytes + col;
-              lds_dma16(base + off, &s_raw[j][q][g * RPI][0]);
+              lds_dma16(base + off, dst_of(q, g * RPI));
             }
           }
         }
@@ -1284,9 +1311,9 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
         for (int k = 0; k < T; ++k) {
           const long long row = k < lim ? k : lim;
 #pragma unroll
-          for (int q = 0; q < NQ; ++q) {
+          for (int q = 0; q < 4; ++q) {
             gbyte* base = uniform_gptr(src[q] + tile_off + row * row_bytes);
-            __builtin_amdgcn_global_load_lds(const_cast<gbyte_w*>(base + col), &s_raw[j][q][k][0], ES, 0, 0);
+            __builtin_amdgcn_global_load_lds(const_cast<gbyte_w*>(base + col), dst_of(q, k), ES, 0, 0);
           }
         }
       }
@@ -1298,7 +1325,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
         for (int w = 0; w < NW; ++w) {
           const long long kr = t.t0 + w * TS < p.L ? w : 0;
           gbyte* base = uniform_gptr(p.ckpt + (ck0 + kr) * W + static_cast<long long>(t.strip) * 64);
-          __builtin_amdgcn_global_load_lds(const_cast<gbyte_w*>(base + col), &s_ck[j][w][0], 4, 0, 0);
+          __builtin_amdgcn_global_load_lds(const_cast<gbyte_w*>(base + col), &s_ck[xb][w][0], 4, 0, 0);
         }
       }
       if (p.reset != nullptr) {
@@ -1315,8 +1342,8 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       {
         float cs = 0.0f, k2 = 0.0f;
         if (t.active) channel_consts(lam, p.c, cs, k2);
-        s_k2[j][lane] = k2;
-        s_cs[j][lane] = cs;
+        s_k2[xb][lane] = k2;
+        s_cs[xb][lane] = cs;
       }
       if (j == 0) {
         nxt = uniform_u64(nxt);
@@ -1333,12 +1360,11 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
     }
   } else if (wave >= CTRL0) {
     // ------------------------------------------------------------ control waves
-    // Control wave c handles the tiles of iterations c, c + 2, ...: once every
-    // data wave has reported t_i, writes the suffix maps its reverse passes
-    // start from and publishes the tile's map (the latest chunk publishes its
-    // outgoing carry instead); runs the look-back and publishes the outgoing
-    // carry; once the data waves have run the reverse pass of t_i (next
-    // iteration), sums their lambda-gradient parts in wave order.
+    // Control wave c handles the tiles of iterations c, c + 2, ...: one
+    // speculative look-back round; once every data wave has reported t_i,
+    // the suffix maps each wave's reverse pass starts from; publishes the
+    // tile's map (the latest chunk publishes its outgoing carry instead), runs
+    // the look-back and publishes the outgoing carry.
     __builtin_amdgcn_s_setprio(3);
     const int c = wave - CTRL0;
     unsigned tag = 0;
@@ -1348,7 +1374,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       if (i == c) tag = __builtin_amdgcn_readfirstlane(s_tag);
       const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
       if (!tc.valid) break;
-      const int cb = i & 1;
+      const int ms = i % 3;
       const size_t sidx = static_cast<size_t>(tc.id) * 64 + lane;
       const bool latest = tc.chunk == p.n_chunks - 1;
       const float init = (tc.active && p.dh_last != nullptr) ? p.dh_last[tc.b * W + tc.ch] : 0.0f;
@@ -1361,31 +1387,31 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
                                    static_cast<unsigned>(lane), -static_cast<long long>(rows) * 64,
                                    p.n_chunks - 1 - tc.chunk, tag, init, carry);
       }
-      // a data wave may report t_{i+1} before another reports t_i (its
-      // reverse pass of t_i waits for this wave), so reports count per parity
-      lds_wait<false>(&s_maps_in[cb], NW * (i / 2 + 1), &s_abort, p.hdr);
+      // reports count per ring slot: a data wave may report t_{i+1} or t_{i+2}
+      // before another reports t_i
+      lds_wait<false>(&s_maps_in[ms], NW * (i / 3 + 1), &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
       float Aw[NW], Bw[NW];
       unsigned Rw[NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        Rw[w] = s_R[cb][w];
-        Aw[w] = s_A[cb][w][lane];
-        Bw[w] = s_B[cb][w][lane];
+        Rw[w] = s_R[ms][w];
+        Aw[w] = s_A[ms][w][lane];
+        Bw[w] = s_B[ms][w][lane];
       }
       float GA = 1.0f, GB = 0.0f;
       bool GR = false;
       unsigned srbits = 0u;
 #pragma unroll
       for (int w = NW - 1; w >= 0; --w) {
-        s_SA[cb][w][lane] = GA;
-        s_SB[cb][w][lane] = GB;
+        s_A[ms][w][lane] = GA;
+        s_B[ms][w][lane] = GB;
         srbits |= GR ? (1u << w) : 0u;
         GB = Rw[w] != 0u ? Bw[w] : fmaf(Aw[w], GB, Bw[w]);
         GA *= Aw[w];
         GR = GR || Rw[w] != 0u;
       }
-      if (lane == 0) s_SRm[cb] = srbits;
+      if (lane == 0) s_SRm[ms] = srbits;
       if (tc.active) {
         if (!found) {
           if (tc.chunk > 0) {
@@ -1402,24 +1428,18 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       } else {
         carry = 0.0f;
       }
-      s_carry[cb][lane] = carry;
+      s_carry[ms][lane] = carry;
       lds_release();
-      if (lane == 0) lds_store(&s_carry_ok[cb], i);
-      // the tile's lambda-gradient partial: the waves' parts in wave order
-      lds_wait<false>(&s_dl_in[cb], NW * (i / 2 + 1), &s_abort, p.hdr);
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) sum += s_dl[cb][w][lane];
-      p.part[static_cast<size_t>(tc.id) * 64 + lane] = sum;
+      if (lane == 0) lds_store(&s_carry_ok[ms], i);
     }
   } else {
     // ------------------------------------------------------------ data waves
     const unsigned perm_sel = (lane & 1) ? 0x03020c0cu : 0x01000c0cu;
-    auto lds_raw = [=](int b, int q, int row) -> uint32_t {
+    auto lds_word = [=](const unsigned char (&buf)[T][ROWB], int row) -> uint32_t {
       if constexpr (ROWB == 128) {
-        return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][row][(lane & ~1) * 2]);
+        return *reinterpret_cast<const uint32_t*>(&buf[row][(lane & ~1) * 2]);
       } else {
-        return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][row][lane * 4]);
+        return *reinterpret_cast<const uint32_t*>(&buf[row][lane * 4]);
       }
     };
     auto to_f32 = [=](uint32_t r) {
@@ -1459,117 +1479,194 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
         pd.on = false;
       }
     };
-    // One iteration: recompute t_i into the ring slot (ccx..cdh, crm), then
-    // the reverse pass of t_{i-1} from (pcx..pdh, prm). Returns false past
-    // the last tile.
-    auto iteration = [=](int i, float (&ccx)[TS], float (&ccgx)[TS], float (&ccga)[TS], float (&ccl)[TS],
-                         float (&cal)[TS], float (&cdh)[TS], unsigned& crm, const float (&pcx)[TS],
-                         const float (&pcgx)[TS], const float (&pcga)[TS], const float (&pcl)[TS],
-                         const float (&pal)[TS], const float (&pdh)[TS], unsigned prm, Pending& pend) -> bool {
-      const int cb = i & 1;
-      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
-      if (lds_load(&s_abort) != 0) return false;
+    // Waves w and w + 4 share a SIMD, whose issue arbiter prefers the older
+    // wave: left alone, wave w runs ahead and wave w + 4 trails it by most of
+    // an iteration, so the tile's maps (and with them the buffers and the
+    // carry) wait for the trailing wave while the SIMD runs one wave at a
+    // time. A wave that is ahead of its partner drops to the lower priority.
+    auto pace = [=](int i, int other) {
+      if constexpr (NW == 8) {
+        if (lane == 0) lds_store(&s_prog[wave], i);
+        if (other < i) {
+          __builtin_amdgcn_s_setprio(0);
+        } else {
+          __builtin_amdgcn_s_setprio(1);
+        }
+      }
+    };
+    // One iteration: the maps of t_i from gate_a and dh, keeping (a, r, dh)
+    // per step in the ring slot (ca, cr, cd, cm); then the reverse pass of
+    // t_{i-2} from its slot (pa, pr, pd, pm), the recomputed forward through
+    // its steps and its incoming carry. Returns false once t_{i-1} is past
+    // the last tile (the next iteration would have nothing to reverse).
+    auto iteration = [=](int i, float (&ca)[TS], float (&cr)[TS], float (&cd)[TS], unsigned& cm,
+                         const float (&pa)[TS], const float (&pr)[TS], const float (&pd)[TS], unsigned pm,
+                         Pending& pend) -> bool {
+      const int mb = i & 1;
+      const int rs3 = (i + 1) % 3;       // ring slot of t_{i-2}
+      // every flag the iteration checks, read in one LDS round trip; a flag
+      // not yet where it must be is then waited for
+      const int f_tk = __builtin_amdgcn_readfirstlane(lds_load(&s_tk_valid));
+      const int f_abort = __builtin_amdgcn_readfirstlane(lds_load(&s_abort));
+      const int f_full = __builtin_amdgcn_readfirstlane(lds_load(&s_full[mb]));
+      const int f_carry = __builtin_amdgcn_readfirstlane(lds_load(&s_carry_ok[rs3]));
+      const int f_dl = __builtin_amdgcn_readfirstlane(lds_load(&s_dl_done[rs3]));
+      const int f_other = NW == 8 ? __builtin_amdgcn_readfirstlane(lds_load(&s_prog[wave ^ 4])) : i;
+      lds_acquire();
+      pace(i, f_other);
+      flush(pend);
+      if (f_tk < i) {
+        lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+        if (lds_load(&s_abort) != 0) return false;
+      } else if (f_abort != 0) {
+        return false;
+      }
       const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
       const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 1) % RING]) : p.n_tiles);
+      const Tile tr = tile_of(i > 1 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 2) % RING]) : p.n_tiles);
       if (tc.valid) {
-        lds_wait<true>(&s_full[cb], i, &s_abort, p.hdr);
+        const int ms = i % 3;
+        if (f_full != i) lds_wait<true>(&s_full[mb], i, &s_abort, p.hdr);
         const int nvalid = wave_steps(tc, wave);
         unsigned rmask = 0;
         if (p.reset != nullptr) {
-          const bool f = lane < nvalid && s_rflag[cb][wave * TS + (lane < TS ? lane : 0)] != 0u;
+          const bool f = lane < nvalid && s_rflag[mb][wave * TS + (lane < TS ? lane : 0)] != 0u;
           rmask = static_cast<unsigned>(__ballot(f));
         }
-        const float k2 = s_k2[cb][lane];
-        const float cs = s_cs[cb][lane];
-        float h = s_ck[cb][wave][lane];
-        // recompute the forward through the wave's steps and turn every step
-        // into the coefficients of the reverse pass
+        const float k2 = s_k2[i & 3][lane];
 #pragma unroll
         for (int k = 0; k < TS; ++k) {
-          const float xv = to_f32(lds_raw(cb, 0, wave * TS + k));
-          const float iv = sigmoid_f(to_f32(lds_raw(cb, 1, wave * TS + k)));
-          const float r = sigmoid_f(to_f32(lds_raw(cb, 2, wave * TS + k)));
-          cdh[k] = to_f32(lds_raw(cb, 3, wave * TS + k));
-          const bool rs = ((rmask >> k) & 1u) != 0u;
-          const float y = k2 * r;
-          const float a = __builtin_amdgcn_exp2f(y);
-          const float w1 = one_minus_exp2(y, a) * (1.0f + a);  // 1 - a^2
-          // 1 / m. Below the smallest normal float, 1 - a^2 comes from a
-          // logit under about -87 (r = 0 or subnormal, a = 1): m is then under
-          // 1e-19, every gradient through m vanishes in the limit, and
-          // v_rsq_f32 would read a subnormal as 0 and return inf. Taking 1/m
-          // as 0 there keeps inf and inf * 0 out of the gradients.
-          const float rsq = w1 >= 1.17549435e-38f ? __builtin_amdgcn_rsqf(w1) : 0.0f;
-          const float m = w1 * rsq;
-          const float mult = rs ? 1.0f : m;
-          const float ix = iv * xv;
-          const float z = rs ? 0.0f : a * (h - a * ix * rsq);
-          const float uw = mult * ix;
-          h = rs ? uw : fmaf(a, h, uw);
-          ccx[k] = mult * iv;
-          ccgx[k] = uw * (1.0f - iv);
-          ccl[k] = z * r;
-          ccga[k] = ccl[k] * fmaf(-cs, r, cs);
-          cal[k] = rs ? 0.0f : a;
+          const float r = sigmoid_f(to_f32(lds_word(s_rm[mb][0], wave * TS + k)));
+          cd[k] = to_f32(lds_word(s_rm[mb][1], wave * TS + k));
+          cr[k] = r;
+          ca[k] = __builtin_amdgcn_exp2f(k2 * r);
         }
+        lds_release();
+        if (lane == 0) lds_add(&s_cons_m[mb], 1);
         // the wave's reverse map G_in -> G_out, latest step first
         // (a reset token passes nothing on: a select, so not even a NaN
         // arriving from a later step crosses it)
         float A = 1.0f, Bv = 0.0f;
+        if (rmask == 0u && nvalid == TS) {
 #pragma unroll
-        for (int k = TS - 1; k >= 0; --k) {
-          if (k < nvalid) {
-            const bool rs = ((rmask >> k) & 1u) != 0u;
-            Bv = rs ? 0.0f : cal[k] * (Bv + cdh[k]);
-            A = rs ? 0.0f : cal[k] * A;
+          for (int k = TS - 1; k >= 0; --k) {
+            Bv = ca[k] * (Bv + cd[k]);
+            A = ca[k] * A;
+          }
+        } else {
+#pragma unroll
+          for (int k = TS - 1; k >= 0; --k) {
+            if (k < nvalid) {
+              const bool rs = ((rmask >> k) & 1u) != 0u;
+              Bv = rs ? 0.0f : ca[k] * (Bv + cd[k]);
+              A = rs ? 0.0f : ca[k] * A;
+            }
           }
         }
-        crm = rmask;
-        s_A[cb][wave][lane] = A;
-        s_B[cb][wave][lane] = Bv;
-        if (lane == 0) s_R[cb][wave] = rmask != 0u ? 1u : 0u;
+        cm = rmask;
+        s_A[ms][wave][lane] = A;
+        s_B[ms][wave][lane] = Bv;
+        if (lane == 0) s_R[ms][wave] = rmask != 0u ? 1u : 0u;
         lds_release();
-        if (lane == 0) {
-          lds_add(&s_maps_in[cb], 1);
-          lds_add(&s_cons[cb], 1);
-        }
+        if (lane == 0) lds_add(&s_maps_in[ms], 1);
       } else {
 #pragma unroll
-        for (int k = 0; k < TS; ++k) ccx[k] = ccgx[k] = ccga[k] = ccl[k] = cal[k] = cdh[k] = 0.0f;
-        crm = 0u;
+        for (int k = 0; k < TS; ++k) ca[k] = cr[k] = cd[k] = 0.0f;
+        cm = 0u;
       }
-      flush(pend);
-      if (tp.valid) {
-        // reverse pass of t_{i-1} from the carry entering its last step
-        const int pb = cb ^ 1;
-        lds_wait<true>(&s_carry_ok[pb], i - 1, &s_abort, p.hdr);
-        const int rn = wave_steps(tp, wave);
-        const float c0 = s_carry[pb][lane];
-        const float SA = s_SA[pb][wave][lane];
-        const float SB = s_SB[pb][wave][lane];
-        const bool SR = ((s_SRm[pb] >> wave) & 1u) != 0u;
+      if (tr.valid) {
+        // reverse pass of t_{i-2} from the carry entering its last step
+        const int xb = (i - 2) & 3;
+        if (f_carry != i - 2) lds_wait<true>(&s_carry_ok[rs3], i - 2, &s_abort, p.hdr);
+        const int rn = wave_steps(tr, wave);
+        const float c0 = s_carry[rs3][lane];
+        const float SA = s_A[rs3][wave][lane];
+        const float SB = s_B[rs3][wave][lane];
+        const bool SR = ((s_SRm[rs3] >> wave) & 1u) != 0u;
         float G = SR ? SB : fmaf(SA, c0, SB);
+        const float k2 = s_k2[xb][lane];
+        const float cs = s_cs[xb][lane];
+        float h = s_ck[xb][wave][lane];
+        // recompute the forward through the wave's steps, per step the
+        // coefficients of the reverse pass, then the reverse pass itself.
+        // FULL: every step in range and no reset token, so no selects.
         float ox[TS], ogx[TS], oga[TS];
         float dl = 0.0f;
+        auto reverse = [&](auto full_tag) {
+          constexpr bool FULL = decltype(full_tag)::value;
+          float cx[TS], cgx[TS], cga[TS], cl[TS];
 #pragma unroll
-        for (int k = TS - 1; k >= 0; --k) {
-          const float g = G + pdh[k];
-          ox[k] = g * pcx[k];
-          ogx[k] = g * pcgx[k];
-          oga[k] = g * pcga[k];
-          const bool in = k < rn;
-          const bool rs = ((prm >> k) & 1u) != 0u;
-          dl = in ? fmaf(g, pcl[k], dl) : dl;
-          G = in ? (rs ? 0.0f : pal[k] * g) : G;
+          for (int k = 0; k < TS; ++k) {
+            const float xv = to_f32(lds_word(s_rx[xb][0], wave * TS + k));
+            const float iv = sigmoid_f(to_f32(lds_word(s_rx[xb][1], wave * TS + k)));
+            const float r = pr[k];
+            const float a = pa[k];
+            const bool rs = FULL ? false : ((pm >> k) & 1u) != 0u;
+            const float y = k2 * r;
+            const float w1 = one_minus_exp2(y, a) * (1.0f + a);  // 1 - a^2
+            // 1 / m. Below the smallest normal float, 1 - a^2 comes from a
+            // logit under about -87 (r = 0 or subnormal, a = 1): m is then
+            // under 1e-19, every gradient through m vanishes in the limit, and
+            // v_rsq_f32 would read a subnormal as 0 and return inf. Taking
+            // 1/m as 0 there keeps inf and inf * 0 out of the gradients.
+            const float rsq = w1 >= 1.17549435e-38f ? __builtin_amdgcn_rsqf(w1) : 0.0f;
+            const float m = w1 * rsq;
+            const float mult = rs ? 1.0f : m;
+            const float ix = iv * xv;
+            const float z = rs ? 0.0f : a * (h - a * ix * rsq);
+            const float uw = mult * ix;
+            h = rs ? uw : fmaf(a, h, uw);
+            cx[k] = mult * iv;
+            cgx[k] = uw * (1.0f - iv);
+            cl[k] = z * r;
+            cga[k] = cl[k] * fmaf(-cs, r, cs);
+          }
+          lds_release();
+          if (lane == 0) lds_add(&s_cons_x[xb], 1);
+#pragma unroll
+          for (int k = TS - 1; k >= 0; --k) {
+            const float g = G + pd[k];
+            ox[k] = g * cx[k];
+            ogx[k] = g * cgx[k];
+            oga[k] = g * cga[k];
+            if (FULL) {
+              dl = fmaf(g, cl[k], dl);
+              G = pa[k] * g;
+            } else {
+              const bool in = k < rn;
+              const bool rs = ((pm >> k) & 1u) != 0u;
+              dl = in ? fmaf(g, cl[k], dl) : dl;
+              G = in ? (rs ? 0.0f : pa[k] * g) : G;
+            }
+          }
+        };
+        if (pm == 0u && rn == TS) {
+          reverse(std::true_type{});
+        } else {
+          reverse(std::false_type{});
         }
-        s_dl[pb][wave][lane] = tp.active ? dl : 0.0f;
+        // the tile's lambda-gradient partial: the last wave to report sums
+        // the waves' parts in wave order
+        if (f_dl != i - 5) lds_wait<true>(&s_dl_done[rs3], i - 5, &s_abort, p.hdr);
+        s_dl[rs3][wave][lane] = tr.active ? dl : 0.0f;
         lds_release();
-        if (lane == 0) lds_add(&s_dl_in[pb], 1);
-        if (tp.active) {
-          if (tp.chunk == 0 && wave == 0 && p.dh0 != nullptr) p.dh0[tp.b * W + tp.ch] = G;
-          const long long s0 = tp.t0 + wave * TS;
-          const long long base = (tp.rowbase + s0) * W + static_cast<long long>(tp.strip) * 64;
-          if (STAGE && p.out_wide && (tp.strip + 1) * 64 <= p.W) {
+        int prev = 0;
+        if (lane == 0) prev = __hip_atomic_fetch_add(&s_dl_in[rs3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        prev = __builtin_amdgcn_readfirstlane(prev);
+        if (prev + 1 == NW * ((i - 2) / 3 + 1)) {
+          lds_acquire();
+          float sum = 0.0f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) sum += s_dl[rs3][w][lane];
+          p.part[static_cast<size_t>(tr.id) * 64 + lane] = sum;
+          lds_release();
+          if (lane == 0) lds_store(&s_dl_done[rs3], i - 2);
+        }
+        if (tr.active) {
+          if (tr.chunk == 0 && wave == 0 && p.dh0 != nullptr) p.dh0[tr.b * W + tr.ch] = G;
+          const long long s0 = tr.t0 + wave * TS;
+          const long long base = (tr.rowbase + s0) * W + static_cast<long long>(tr.strip) * 64;
+          if (STAGE && p.out_wide && (tr.strip + 1) * 64 <= p.W) {
 #pragma unroll
             for (int k = 0; k < TS; ++k) {
               float v0[1] = {ox[k]}, v1[1] = {ogx[k]}, v2[1] = {oga[k]};
@@ -1594,17 +1691,17 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
           }
         }
       }
-      return tc.valid;
+      return tc.valid || tp.valid;
     };
-    float cx0[TS], cgx0[TS], cga0[TS], cl0[TS], al0[TS], dh0r[TS];
-    float cx1[TS], cgx1[TS], cga1[TS], cl1[TS], al1[TS], dh1r[TS];
-    unsigned rm0 = 0u, rm1 = 0u;
+    float a0[TS], r0[TS], d0[TS], a1[TS], r1[TS], d1[TS], a2[TS], r2[TS], d2[TS];
+    unsigned m0 = 0u, m1 = 0u, m2 = 0u;
 #pragma unroll
-    for (int k = 0; k < TS; ++k) cx1[k] = cgx1[k] = cga1[k] = cl1[k] = al1[k] = dh1r[k] = 0.0f;
+    for (int k = 0; k < TS; ++k) a1[k] = r1[k] = d1[k] = a2[k] = r2[k] = d2[k] = 0.0f;
     Pending pend{0, 0, false};
-    for (int i = 0;; i += 2) {
-      if (!iteration(i, cx0, cgx0, cga0, cl0, al0, dh0r, rm0, cx1, cgx1, cga1, cl1, al1, dh1r, rm1, pend)) break;
-      if (!iteration(i + 1, cx1, cgx1, cga1, cl1, al1, dh1r, rm1, cx0, cgx0, cga0, cl0, al0, dh0r, rm0, pend)) break;
+    for (int i = 0;; i += 3) {
+      if (!iteration(i, a0, r0, d0, m0, a1, r1, d1, m1, pend)) break;
+      if (!iteration(i + 1, a1, r1, d1, m1, a2, r2, d2, m2, pend)) break;
+      if (!iteration(i + 2, a2, r2, d2, m2, a0, r0, d0, m0, pend)) break;
     }
     flush(pend);
   }

@@ -3,7 +3,12 @@
 Tolerances (stated for the hot path): outputs pass elementwise when
 |got - ref| <= tol * max(1, |ref|), tol = 1e-5 for float32 io and 4e-3 for bf16
 io; gradients pass per tensor when max|got - ref| <= tol * max(1, max|ref|),
-tol = 1e-5 for float32 io and 1e-2 for bf16 io.
+tol = 1e-5 for float32 io and 1e-2 for bf16 io. The per-position gradients
+(dx, dgate_x, dgate_a) must also pass elementwise, |got - ref| <=
+tol * max(1, |ref|) with tol = 1e-4 for float32 io (the float32 reverse carry
+accumulates up to L terms) and 1e-2 for bf16 io (one bf16 rounding of the
+stored value is 2^-9 relative), so a small gradient next to a large one in the
+same tensor is checked too.
 """
 from __future__ import annotations
 
@@ -15,6 +20,7 @@ import synth
 
 OUT_TOL = {"f32": 1e-5, "bf16": 4e-3}
 GRAD_TOL = {"f32": 1e-5, "bf16": 1e-2}
+GRAD_EL_TOL = {"f32": 1e-4, "bf16": 1e-2}
 
 
 def to_dev(stored: synth.Stored, device="cuda") -> torch.Tensor:
@@ -99,9 +105,12 @@ def compare(io: str, gpu: dict, ref: dict, chans=None, label=""):
     errs["h"] = out_err(host64(gpu["h"])[:, :, sl], ref["h"])
     if gpu.get("h_last") is not None:
         errs["h_last"] = out_err(host64(gpu["h_last"])[:, sl], ref["h_last"])
+    el = {}
     for k, rk in (("dx", "dx"), ("dgx", "dgx"), ("dga", "dga")):
         if k in gpu:
-            errs[k] = grad_err(host64(gpu[k])[:, :, sl], ref[rk])
+            g = host64(gpu[k])[:, :, sl]
+            errs[k] = grad_err(g, ref[rk])
+            el[k] = out_err(g, ref[rk])
     if "dlam" in gpu:
         errs["dlam"] = grad_err(host64(gpu["dlam"])[sl], ref["dlam"])
     if gpu.get("dh0") is not None:
@@ -111,7 +120,10 @@ def compare(io: str, gpu: dict, ref: dict, chans=None, label=""):
         tol = OUT_TOL[io] if k in ("h", "h_last") else GRAD_TOL[io]
         if not (e <= tol):
             bad[k] = (e, tol)
-    assert not bad, f"{label} out of tolerance: {bad} (all errors: {errs})"
+    for k, e in el.items():
+        if not (e <= GRAD_EL_TOL[io]):
+            bad[k + " (elementwise)"] = (e, GRAD_EL_TOL[io])
+    assert not bad, f"{label} out of tolerance: {bad} (all errors: {errs}, elementwise: {el})"
     return errs
 
 

@@ -134,12 +134,33 @@ def test_projection_feeding_scan_end_to_end(gpu_lib, wid):
     assert grad_err(host64(dx), rdx) <= GRAD_TOL["bf16"]
     for got, want in ((dwx, rdw_x), (dwa, rdw_a), (dbx, rdb_x), (dba, rdb_a)):
         assert grad_err(host64(got), want) <= GRAD_TOL["bf16"]
-    # End to end: float64 logits (never rounded) through the float64 scan. The
-    # path rounds to bf16 twice in sequence (the logits it hands the scan, then
-    # h), and each rounding contributes up to 2^-8 relative, so the composed
-    # bound is twice the single-stage output tolerance.
-    e2e_in = synth.Inputs(wl, inp.x, synth.Stored("bf16", None, rgx.reshape(B, L, W)),
-                          synth.Stored("bf16", None, rga.reshape(B, L, W)), inp.lam, inp.dh, inp.reset,
+    # End to end: the float64 projection, rounded once to bf16 (as the path
+    # stores its logits), through the float64 scan. The GPU's logits are those
+    # rounded values up to the float32 accumulation: a bf16 rounding of the
+    # float32 sum can land one spacing away, and the sum itself is within
+    # bs * 2^-24 * sum|x w| of the exact one (the usual bound for a float32
+    # dot product of bs terms). h is then held to the single-stage output
+    # tolerance.
+    bs = wl.proj_block
+    rq = {}
+    for name, got, ref64, w, b in (("gate_x", gx, rgx, inp.wx.value, inp.bx.value),
+                                   ("gate_a", ga, rga, inp.wa.value, inp.ba.value)):
+        q = synth.store(ref64, "bf16").value
+        g = host64(got)
+        absdot = oracle.blockdiag_proj_forward(np.abs(xv), np.abs(w), None if b is None else np.abs(b))
+
+        def spacing(v):
+            return np.exp2(np.floor(np.log2(np.maximum(np.abs(v), 1e-30))) - 7)
+
+        bound = np.maximum(spacing(q), spacing(g)) + bs * 2.0 ** -24 * absdot
+        diff = g != q
+        assert diff.mean() <= 1e-2, (name, diff.mean())
+        assert np.all(np.abs(g - q) <= bound), (name, float(np.max(np.abs(g - q) / bound)))
+        rq[name] = q.reshape(B, L, W)
+    e2e_in = synth.Inputs(wl, inp.x, synth.Stored("bf16", None, rq["gate_x"]),
+                          synth.Stored("bf16", None, rq["gate_a"]), inp.lam, inp.dh, inp.reset,
                           inp.h0, inp.dh_last)
     e2e = run_oracle(e2e_in, want_bwd=False)
-    assert out_err(host64(h), e2e["h"]) <= 2 * OUT_TOL["bf16"]
+    err = out_err(host64(h), e2e["h"])
+    print(f"end-to-end h error vs bf16-rounded oracle logits: {err:.3e}")
+    assert err <= OUT_TOL["bf16"]
