@@ -51,6 +51,12 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kCkpt = RGLRU_CKPT_STEPS;
 constexpr unsigned kSpinLimit = 1u << 20;
+// Sleep between polls (units of 64 clocks). The load and control waves share
+// their SIMDs with data waves and poll at high priority, so they poll less
+// often: their waits have an iteration of slack. The data waves' waits are on
+// the critical path and poll at the shortest interval.
+constexpr int kHelperSleep = 8;
+constexpr int kLookBackSleep = 4;
 constexpr size_t kHeaderBytes = 256;
 constexpr int kMaxStrip = 512;   // widest channel strip of any variant (64 lanes * 8)
 
@@ -363,7 +369,7 @@ __device__ __forceinline__ bool look_back_wave(const u64* slot_a, const u64* slo
                                                unsigned tag, float init, float& carry) {
   for (unsigned round = 0; round < kSpinLimit; ++round) {
     if (look_back_round<K>(slot_a, slot_b, slot_h, self_uniform, lane, stride, npred, tag, init, carry)) return true;
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(kLookBackSleep);
   }
   carry = 0.0f;
   return false;
@@ -419,7 +425,7 @@ __device__ __forceinline__ void lds_acquire() { asm volatile("" ::: "memory"); }
 // the workgroup's abort word; once that is set every wait returns at once, so
 // the workgroup always drains and exits (the call's outputs are then invalid,
 // as the error word says).
-template <bool EQ>
+template <bool EQ, int SLEEP = 1>
 __device__ __forceinline__ void lds_wait(const int* f, int v, int* abort, Header* hdr) {
   for (unsigned n = 0; n < kSpinLimit; ++n) {
     const int c = lds_load(f);
@@ -428,7 +434,7 @@ __device__ __forceinline__ void lds_wait(const int* f, int v, int* abort, Header
       return;
     }
     if (lds_load(abort) != 0) return;
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(SLEEP);
   }
   lds_store(abort, 1);
   if ((threadIdx.x & 63) == 0) atomicOr(&hdr->err, 2u);
@@ -517,6 +523,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   __shared__ int s_cons[2];           // data waves done with buffer j so far
   __shared__ int s_maps_in[3];        // data-wave maps reported for iterations of each slot so far
   __shared__ int s_carry_ok[3];       // iteration whose incoming carry slot s holds
+  __shared__ int s_prog[NW];          // iteration each data wave is in
   __shared__ int s_abort;
 
   const int lane = threadIdx.x & 63;
@@ -530,6 +537,8 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
     s_cons[0] = s_cons[1] = 0;
     s_maps_in[0] = s_maps_in[1] = s_maps_in[2] = 0;
     s_carry_ok[0] = s_carry_ok[1] = s_carry_ok[2] = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s_prog[w] = -1;
     s_abort = 0;
   }
   __syncthreads();
@@ -580,10 +589,10 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
                                    static_cast<const unsigned char*>(p.ga)};
     const long long row_bytes = W * ES;
     for (int i = j;; i += 2) {
-      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_tk_valid, i, &s_abort, p.hdr);
       const Tile t = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
       // buffer j is free once every data wave is done with iteration i - 2
-      lds_wait<false>(&s_cons[j], NW * (i / 2), &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_cons[j], NW * (i / 2), &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
       if (!t.valid) {
         if (lane == 0) lds_store(&s_full[j], i);
@@ -678,7 +687,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
     const int c = wave - CTRL0;
     unsigned tag = 0;
     for (int i = c;; i += 2) {
-      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_tk_valid, i, &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
       if (i == c) tag = __builtin_amdgcn_readfirstlane(s_tag);
       const unsigned tile = __builtin_amdgcn_readfirstlane(s_tk[i % RING]);
@@ -703,7 +712,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
       // replay starts from and the tile's map. A data wave may report up to
       // two iterations ahead of another (its replay of t_{i-2} waits for the
       // carry of t_{i-2}), so the reports are counted per slot of three.
-      lds_wait<false>(&s_maps_in[ms], NW * (i / 3 + 1), &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_maps_in[ms], NW * (i / 3 + 1), &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
       float Aw[NW], Bw[NW];
       unsigned Rw[NW];
@@ -805,30 +814,77 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
       }
       pd.on = false;
     };
+    // Waves w and w + 4 share a SIMD, whose issue arbiter prefers the older
+    // wave: left alone, wave w runs ahead and wave w + 4 trails it, and the
+    // tile's maps (and with them the buffers and the carry) wait for the
+    // trailing wave. A wave that is ahead of its partner drops to the lower
+    // priority.
+    auto pace = [=](int i, int other) {
+      if constexpr (NW == 8) {
+        if (lane == 0) lds_store(&s_prog[wave], i);
+        if (other < i) {
+          __builtin_amdgcn_s_setprio(0);
+        } else {
+          __builtin_amdgcn_s_setprio(1);
+        }
+      }
+    };
     // One iteration: the gates of t_i into (cal, cu, crm), and the replay of
     // t_{i-2} from (ral, ru, rrm). Returns false once t_{i-1} is past the last
     // tile (the next iteration would have nothing to replay).
     auto iteration = [=](int i, float (&cal)[TS], float (&cu)[TS], unsigned& crm, const float (&ral)[TS],
                          const float (&ru)[TS], unsigned rrm, Pending& pend) -> bool {
-      flush(pend);
       const int cb = i & 1;
       const int ms = i % 3;
       const int rs_slot = (i + 1) % 3;     // slot of iteration i - 2
-      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
-      if (lds_load(&s_abort) != 0) return false;
-      const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
-      const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 1) % RING]) : p.n_tiles);
-      const Tile tr = tile_of(i > 1 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 2) % RING]) : p.n_tiles);
+      // One LDS round trip for the flags the iteration checks and the data
+      // they guard (tickets, the replay's carry and prefix map, the tile's
+      // decay constants and reset flags): the data is read right behind its
+      // flag, and read again only if the flag was not yet set (then waited
+      // for). LDS runs a wave's operations in order, so data read after a
+      // flag that was set is the data the flag published.
+      const int f_tk = __builtin_amdgcn_readfirstlane(lds_load(&s_tk_valid));
+      const int f_abort = __builtin_amdgcn_readfirstlane(lds_load(&s_abort));
+      const int f_full = __builtin_amdgcn_readfirstlane(lds_load(&s_full[cb]));
+      const int f_carry = __builtin_amdgcn_readfirstlane(lds_load(&s_carry_ok[rs_slot]));
+      const int f_other = NW == 8 ? __builtin_amdgcn_readfirstlane(lds_load(&s_prog[wave ^ 4])) : i;
+      lds_acquire();
+      unsigned q_c = s_tk[i % RING];
+      unsigned q_p = s_tk[(i + RING - 1) % RING];
+      unsigned q_r = s_tk[(i + RING - 2) % RING];
+      float c0 = s_carry[rs_slot][lane];
+      float PA = s_PA[rs_slot][wave][lane];
+      float PB = s_PB[rs_slot][wave][lane];
+      unsigned PRm = s_PRm[rs_slot];
+      unsigned rfl = s_rflag[cb][wave * TS + (lane < TS ? lane : 0)];
+      float k2 = s_k2[cb][lane];
+      pace(i, f_other);
+      flush(pend);
+      if (f_tk < i) {
+        lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+        if (lds_load(&s_abort) != 0) return false;
+        q_c = s_tk[i % RING];
+        q_p = s_tk[(i + RING - 1) % RING];
+        q_r = s_tk[(i + RING - 2) % RING];
+      } else if (f_abort != 0) {
+        return false;
+      }
+      const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(q_c));
+      const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(q_p) : p.n_tiles);
+      const Tile tr = tile_of(i > 1 ? __builtin_amdgcn_readfirstlane(q_r) : p.n_tiles);
       // the replay's incoming state (ready since the previous iteration in
       // steady state)
       float hc = 0.0f;
       int rn = 0;
       if (tr.valid) {
-        lds_wait<true>(&s_carry_ok[rs_slot], i - 2, &s_abort, p.hdr);
-        const float c0 = s_carry[rs_slot][lane];
-        const float PA = s_PA[rs_slot][wave][lane];
-        const float PB = s_PB[rs_slot][wave][lane];
-        const bool PR = ((s_PRm[rs_slot] >> wave) & 1u) != 0u;
+        if (f_carry != i - 2) {
+          lds_wait<true>(&s_carry_ok[rs_slot], i - 2, &s_abort, p.hdr);
+          c0 = s_carry[rs_slot][lane];
+          PA = s_PA[rs_slot][wave][lane];
+          PB = s_PB[rs_slot][wave][lane];
+          PRm = s_PRm[rs_slot];
+        }
+        const bool PR = ((PRm >> wave) & 1u) != 0u;
         hc = PR ? PB : fmaf(PA, c0, PB);
         rn = wave_steps(tr);
       }
@@ -852,15 +908,18 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
         put_h(k, hc);
       };
       if (tc.valid) {
-        lds_wait<true>(&s_full[cb], i, &s_abort, p.hdr);
+        if (f_full != i) {
+          lds_wait<true>(&s_full[cb], i, &s_abort, p.hdr);
+          rfl = s_rflag[cb][wave * TS + (lane < TS ? lane : 0)];
+          k2 = s_k2[cb][lane];
+        }
         const int nvalid = wave_steps(tc);
         // reset flags of the wave's steps: lane k reads step k, one ballot
         unsigned rmask = 0;
         if (p.reset != nullptr) {
-          const bool f = lane < nvalid && s_rflag[cb][wave * TS + (lane < TS ? lane : 0)] != 0u;
+          const bool f = lane < nvalid && rfl != 0u;
           rmask = static_cast<unsigned>(__ballot(f));
         }
-        const float k2 = s_k2[cb][lane];
         float A = 1.0f, Bv = 0.0f;
         // one step of the gates: (alpha, write) and the wave's map extended by
         // it. FULL: every step in range and no reset token, so no selects.
@@ -1257,12 +1316,12 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
     const long long row_bytes = W * ES;
     for (int i = j;; i += 2) {
       const int xb = i & 3;
-      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_tk_valid, i, &s_abort, p.hdr);
       const Tile t = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
       // the maps of t_{i-2} and the reverse pass of t_{i-4} are done with
       // the buffers t_i goes to
-      lds_wait<false>(&s_cons_m[j], NW * (i / 2), &s_abort, p.hdr);
-      lds_wait<false>(&s_cons_x[xb], NW * (i / 4), &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_cons_m[j], NW * (i / 2), &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_cons_x[xb], NW * (i / 4), &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
       if (!t.valid) {
         if (lane == 0) lds_store(&s_full[j], i);
@@ -1369,7 +1428,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
     const int c = wave - CTRL0;
     unsigned tag = 0;
     for (int i = c;; i += 2) {
-      lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_tk_valid, i, &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
       if (i == c) tag = __builtin_amdgcn_readfirstlane(s_tag);
       const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
@@ -1389,7 +1448,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       }
       // reports count per ring slot: a data wave may report t_{i+1} or t_{i+2}
       // before another reports t_i
-      lds_wait<false>(&s_maps_in[ms], NW * (i / 3 + 1), &s_abort, p.hdr);
+      lds_wait<false, kHelperSleep>(&s_maps_in[ms], NW * (i / 3 + 1), &s_abort, p.hdr);
       if (lds_load(&s_abort) != 0) break;
       float Aw[NW], Bw[NW];
       unsigned Rw[NW];
@@ -1504,8 +1563,12 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
                          Pending& pend) -> bool {
       const int mb = i & 1;
       const int rs3 = (i + 1) % 3;       // ring slot of t_{i-2}
-      // every flag the iteration checks, read in one LDS round trip; a flag
-      // not yet where it must be is then waited for
+      // One LDS round trip for the flags the iteration checks and the data
+      // they guard (tickets, the tile's reset flags and decay constants, the
+      // reverse pass's carry and suffix map): the data is read right behind
+      // its flag, and read again only if the flag was not yet set (then
+      // waited for). LDS runs a wave's operations in order, so data read
+      // after a flag that was set is the data the flag published.
       const int f_tk = __builtin_amdgcn_readfirstlane(lds_load(&s_tk_valid));
       const int f_abort = __builtin_amdgcn_readfirstlane(lds_load(&s_abort));
       const int f_full = __builtin_amdgcn_readfirstlane(lds_load(&s_full[mb]));
@@ -1513,27 +1576,43 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       const int f_dl = __builtin_amdgcn_readfirstlane(lds_load(&s_dl_done[rs3]));
       const int f_other = NW == 8 ? __builtin_amdgcn_readfirstlane(lds_load(&s_prog[wave ^ 4])) : i;
       lds_acquire();
+      unsigned q_c = s_tk[i % RING];
+      unsigned q_p = s_tk[(i + RING - 1) % RING];
+      unsigned q_r = s_tk[(i + RING - 2) % RING];
+      unsigned rfl = s_rflag[mb][wave * TS + (lane < TS ? lane : 0)];
+      float k2m = s_k2[i & 3][lane];
+      float c0 = s_carry[rs3][lane];
+      float SA = s_A[rs3][wave][lane];
+      float SB = s_B[rs3][wave][lane];
+      unsigned SRm = s_SRm[rs3];
       pace(i, f_other);
       flush(pend);
       if (f_tk < i) {
         lds_wait<false>(&s_tk_valid, i, &s_abort, p.hdr);
         if (lds_load(&s_abort) != 0) return false;
+        q_c = s_tk[i % RING];
+        q_p = s_tk[(i + RING - 1) % RING];
+        q_r = s_tk[(i + RING - 2) % RING];
       } else if (f_abort != 0) {
         return false;
       }
-      const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
-      const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 1) % RING]) : p.n_tiles);
-      const Tile tr = tile_of(i > 1 ? __builtin_amdgcn_readfirstlane(s_tk[(i - 2) % RING]) : p.n_tiles);
+      const Tile tc = tile_of(__builtin_amdgcn_readfirstlane(q_c));
+      const Tile tp = tile_of(i > 0 ? __builtin_amdgcn_readfirstlane(q_p) : p.n_tiles);
+      const Tile tr = tile_of(i > 1 ? __builtin_amdgcn_readfirstlane(q_r) : p.n_tiles);
       if (tc.valid) {
         const int ms = i % 3;
-        if (f_full != i) lds_wait<true>(&s_full[mb], i, &s_abort, p.hdr);
+        if (f_full != i) {
+          lds_wait<true>(&s_full[mb], i, &s_abort, p.hdr);
+          rfl = s_rflag[mb][wave * TS + (lane < TS ? lane : 0)];
+          k2m = s_k2[i & 3][lane];
+        }
         const int nvalid = wave_steps(tc, wave);
         unsigned rmask = 0;
         if (p.reset != nullptr) {
-          const bool f = lane < nvalid && s_rflag[mb][wave * TS + (lane < TS ? lane : 0)] != 0u;
+          const bool f = lane < nvalid && rfl != 0u;
           rmask = static_cast<unsigned>(__ballot(f));
         }
-        const float k2 = s_k2[i & 3][lane];
+        const float k2 = k2m;
 #pragma unroll
         for (int k = 0; k < TS; ++k) {
           const float r = sigmoid_f(to_f32(lds_word(s_rm[mb][0], wave * TS + k)));
@@ -1577,12 +1656,15 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       if (tr.valid) {
         // reverse pass of t_{i-2} from the carry entering its last step
         const int xb = (i - 2) & 3;
-        if (f_carry != i - 2) lds_wait<true>(&s_carry_ok[rs3], i - 2, &s_abort, p.hdr);
+        if (f_carry != i - 2) {
+          lds_wait<true>(&s_carry_ok[rs3], i - 2, &s_abort, p.hdr);
+          c0 = s_carry[rs3][lane];
+          SA = s_A[rs3][wave][lane];
+          SB = s_B[rs3][wave][lane];
+          SRm = s_SRm[rs3];
+        }
         const int rn = wave_steps(tr, wave);
-        const float c0 = s_carry[rs3][lane];
-        const float SA = s_A[rs3][wave][lane];
-        const float SB = s_B[rs3][wave][lane];
-        const bool SR = ((s_SRm[rs3] >> wave) & 1u) != 0u;
+        const bool SR = ((SRm >> wave) & 1u) != 0u;
         float G = SR ? SB : fmaf(SA, c0, SB);
         const float k2 = s_k2[xb][lane];
         const float cs = s_cs[xb][lane];
