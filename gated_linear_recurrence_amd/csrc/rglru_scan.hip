@@ -1865,8 +1865,9 @@ Geometry geometry(const rglru_shape_t* s) {
   Geometry g;
   g.io_bytes = s->io_dtype == RGLRU_IO_F32 ? 4 : 2;
   const int req = s->chunk == 0 ? 64 : s->chunk;
-  // the forward keeps the (alpha, write) pairs of two tiles in registers: at
-  // most 64 steps; the backward keeps six coefficients per step: at most 32
+  // the shortest tile a request can run with in each direction (the tile
+  // also depends on pointer alignment, unknown here), so the chunk counts
+  // below bound those of any launch
   g.T = req > 64 ? 64 : req;
   g.Tb = req > 32 ? 32 : req;
   g.n_ckpt = ceil_div(s->length, kCkpt);
@@ -1881,14 +1882,13 @@ size_t slot_words(const rglru_shape_t* s, int n_chunks) {
          round_up(static_cast<size_t>(s->width), kMaxStrip);
 }
 
-constexpr int kSlotKinds = 4;   // forward: map A, map B, carry; backward: map A, map B, carry, partial
-
-size_t ws_bytes(const rglru_shape_t* s, int n_chunks) {
-  return kHeaderBytes + kSlotKinds * round_up(slot_words(s, n_chunks) * 8, 256);
+// slot kinds: forward map A, map B, carry; the backward adds the partials
+size_t ws_bytes(const rglru_shape_t* s, int n_chunks, int kinds) {
+  return kHeaderBytes + static_cast<size_t>(kinds) * round_up(slot_words(s, n_chunks) * 8, 256);
 }
 
-size_t fwd_ws(const rglru_shape_t* s) { return ws_bytes(s, geometry(s).n_chunks_f); }
-size_t bwd_ws(const rglru_shape_t* s) { return ws_bytes(s, geometry(s).n_chunks_b); }
+size_t fwd_ws(const rglru_shape_t* s) { return ws_bytes(s, geometry(s).n_chunks_f, 3); }
+size_t bwd_ws(const rglru_shape_t* s) { return ws_bytes(s, geometry(s).n_chunks_b, 4); }
 
 struct Slots {
   Header* hdr;
