@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     rglru_bwd_workspace_bytes,
     rglru_ckpt_elems,
     rglru_fwd,
+    rglru_fwd_scratch,
     rglru_fwd_workspace_bytes,
     rglru_workspace_bytes,
 )

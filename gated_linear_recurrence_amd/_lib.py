@@ -18,6 +18,7 @@ RGLRU_IO_F32 = 0
 RGLRU_IO_BF16 = 1
 RGLRU_CKPT_STEPS = 8
 HEADER_BYTES = 256   # workspace header: u64 call counter, u32 done counter, u32 error bits
+RGLRU_SCRATCH_BYTES = 64 << 20   # the static workspace rglru_fwd_scratch uses, per GPU
 
 
 class rglru_shape_t(ctypes.Structure):
@@ -47,6 +48,7 @@ _SIGNATURES = {
     "rglru_blockdiag_gate_proj_bwd_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int64]),
     "rglru_blockdiag_gate_proj_bwd": (c_int, [c_int64, c_int64, c_int64, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _vp, _vp, c_size_t, _vp]),
+    "rglru_fwd_scratch": (c_int, [POINTER(rglru_shape_t), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "rglru_status_string": (ctypes.c_char_p, [c_int]),
     "rglru_abi_version": (c_int, []),
 }

@@ -40,7 +40,9 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -2031,6 +2033,39 @@ bool f32_aligned(const void* p) { return p == nullptr || aligned_to(p, 4); }
 
 using namespace rglru;
 
+// ------------------------------------------------------------------ allocation-free forward
+//
+// rglru_fwd_scratch runs rglru_fwd with this array as its workspace. Each GPU
+// the library runs on holds its own copy (zero when the code object loads)
+// until the process ends. Like a caller's workspace it is left ready for the
+// next call by every completed call, so it is never cleared. In host code the
+// array's name is not a device address: the address of the current device's
+// copy is looked up once per device and kept.
+constexpr size_t kScratchBytes = RGLRU_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of the scratch array, or nullptr if the runtime
+// cannot give its address.
+void* scratch_addr(int dev) {
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    g_scratch_addr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+}  // namespace
+
 extern "C" {
 
 size_t rglru_ckpt_elems(const rglru_shape_t* s) {
@@ -2168,6 +2203,18 @@ rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate
   return wide ? dispatch_bwd<BF16, true>(T, a, st) : dispatch_bwd<BF16, false>(T, a, st);
 }
 
+rglru_status_t rglru_fwd_scratch(const rglru_shape_t* s, const void* x, const void* gate_x, const void* gate_a,
+                                 const float* lambda, const uint8_t* reset, const float* h0, void* h,
+                                 float* h_last, float* ckpt, void* stream) {
+  if (!shape_ok(s)) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (fwd_ws(s) > kScratchBytes) return RGLRU_ERR_SCRATCH_TOO_SMALL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RGLRU_ERR_HIP;
+  void* ws = scratch_addr(dev);
+  if (ws == nullptr) return RGLRU_ERR_HIP;
+  return rglru_fwd(s, x, gate_x, gate_a, lambda, reset, h0, h, h_last, ckpt, ws, kScratchBytes, stream);
+}
+
 const char* rglru_status_string(rglru_status_t status) {
   switch (status) {
     case RGLRU_OK: return "RGLRU_OK";
@@ -2176,6 +2223,8 @@ const char* rglru_status_string(rglru_status_t status) {
     case RGLRU_ERR_WORKSPACE_TOO_SMALL: return "RGLRU_ERR_WORKSPACE_TOO_SMALL";
     case RGLRU_ERR_UNSUPPORTED: return "RGLRU_ERR_UNSUPPORTED: valid request not implemented in this build";
     case RGLRU_ERR_HIP: return "RGLRU_ERR_HIP: the HIP runtime refused a launch";
+    case RGLRU_ERR_SCRATCH_TOO_SMALL:
+      return "RGLRU_ERR_SCRATCH_TOO_SMALL: the shape needs more workspace than RGLRU_SCRATCH_BYTES";
   }
   return "RGLRU_ERR_UNKNOWN";
 }

@@ -181,6 +181,36 @@ def rglru_fwd(x: torch.Tensor, gate_x: torch.Tensor, gate_a: torch.Tensor, lam: 
     return h, h_last, ckpt
 
 
+def rglru_fwd_scratch(x: torch.Tensor, gate_x: torch.Tensor, gate_a: torch.Tensor, lam: torch.Tensor,
+                      reset: Optional[torch.Tensor] = None, h0: Optional[torch.Tensor] = None, *,
+                      h: torch.Tensor, h_last: Optional[torch.Tensor] = None, ckpt: Optional[torch.Tensor] = None,
+                      chunk: int = 0, c: float = 8.0):
+    """Forward scan through the allocation-free entry point: no workspace, and
+    every output passed in (nothing is allocated here either). Returns (h,
+    h_last, ckpt)."""
+    lib = _lib.load()
+    dev = x.device
+    B, L, W = x.shape
+    io = x.dtype
+    if io not in _IO:
+        raise ValueError(f"unsupported io dtype {io}")
+    _need(x, "x", (B, L, W), io, dev)
+    _need(gate_x, "gate_x", (B, L, W), io, dev)
+    _need(gate_a, "gate_a", (B, L, W), io, dev)
+    _need(lam, "lambda", (W,), torch.float32, dev)
+    _opt(reset, "reset", (B, L), torch.uint8, dev)
+    _opt(h0, "h0", (B, W), torch.float32, dev)
+    _need(h, "h", (B, L, W), io, dev)
+    _opt(h_last, "h_last", (B, W), torch.float32, dev)
+    shape = make_shape(B, L, W, io, chunk, c)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", (rglru_ckpt_elems(shape),), torch.float32, dev)
+    st = lib.rglru_fwd_scratch(ctypes.byref(shape), _ptr(x), _ptr(gate_x), _ptr(gate_a), _ptr(lam), _ptr(reset),
+                               _ptr(h0), _ptr(h), _ptr(h_last), _ptr(ckpt), _stream(dev))
+    _lib.check(st, "rglru_fwd_scratch")
+    return h, h_last, ckpt
+
+
 def rglru_bwd(x: torch.Tensor, gate_x: torch.Tensor, gate_a: torch.Tensor, lam: torch.Tensor,
               reset: Optional[torch.Tensor], ckpt: torch.Tensor, dh: torch.Tensor,
               dh_last: Optional[torch.Tensor] = None, *, chunk: int = 0, c: float = 8.0,

@@ -77,7 +77,8 @@ typedef enum {
   RGLRU_ERR_MISALIGNED = 2,        /* a pointer not aligned to its element size */
   RGLRU_ERR_WORKSPACE_TOO_SMALL = 3,
   RGLRU_ERR_UNSUPPORTED = 4,       /* a valid request this build does not implement */
-  RGLRU_ERR_HIP = 5                /* the HIP runtime refused a launch */
+  RGLRU_ERR_HIP = 5,               /* the HIP runtime refused a launch */
+  RGLRU_ERR_SCRATCH_TOO_SMALL = 6  /* rglru_fwd_scratch: the shape needs more than RGLRU_SCRATCH_BYTES */
 } rglru_status_t;
 
 typedef struct {
@@ -199,6 +200,28 @@ rglru_status_t rglru_blockdiag_gate_proj_bwd(int64_t tokens, int64_t width, int6
                                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status. Never NULL. */
+/* Forward scan without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * results (bitwise) and errors as rglru_fwd, minus the workspace: the library
+ * uses a static device array of RGLRU_SCRATCH_BYTES in its place, one per GPU,
+ * which it holds from the first call on that GPU until the process ends
+ * (zero-filled when the library's code object loads; every completed call
+ * leaves it ready for the next one). Returns RGLRU_ERR_SCRATCH_TOO_SMALL,
+ * writing nothing, when rglru_fwd_workspace_bytes(shape) exceeds
+ * RGLRU_SCRATCH_BYTES: B * ceil(L / T) * W' must stay under about 2.79e6,
+ * with T = min(chunk, 64) (64 for the default chunk) and W' = W rounded up to
+ * a multiple of 512 (B=1, L=32768, W=4096 needs 2097152). Returns
+ * RGLRU_ERR_HIP if the runtime cannot give the array's address.
+ * Runs on the current device. Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller. */
+#define RGLRU_SCRATCH_BYTES (((size_t)64) << 20)
+rglru_status_t rglru_fwd_scratch(const rglru_shape_t* shape,
+                                 const void* x, const void* gate_x, const void* gate_a,
+                                 const float* lambda, const uint8_t* reset, const float* h0,
+                                 void* h, float* h_last, float* ckpt, void* stream);
+
 const char* rglru_status_string(rglru_status_t status);
 
 /* RGLRU_ABI_VERSION of the loaded library. */
