@@ -10,8 +10,10 @@ from .rglru import (  # noqa: F401
     blockdiag_proj_forward,
     gates,
     rglru_backward,
+    rglru_backward_varlen,
     rglru_forward,
     rglru_forward_chunked,
+    rglru_forward_varlen,
     sigmoid,
     softplus,
 )

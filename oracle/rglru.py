@@ -137,6 +137,63 @@ def rglru_backward(x, gx, ga, lam, dh, reset=None, h0=None, dh_last=None, c=C_DE
     return {"dx": dx, "dgx": dgx, "dga": dga, "dlam": dlam, "dh0": carry}
 
 
+def rglru_forward_varlen(x, gx, ga, lam, cu_seqlens, reset=None, h0=None, c=C_DEFAULT):
+    """Packed sequences (the cu_seqlens convention of the linear-attention
+    reference oracles, recurrent_delta_rule_reference: offsets into one packed
+    row, one initial and one final state per sequence).
+
+    x, gx, ga [T, W]; cu_seqlens [n + 1] offsets, sequence s holding tokens
+    cu[s] .. cu[s+1]-1; reset [T] or None; h0 [n, W] or None. Each sequence is
+    its own row of rglru_forward from h0[s]. Returns (h [T, W], h_last [n, W]);
+    a sequence without tokens has h_last = h0[s] (zero without h0).
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = cu.size - 1
+    T, W = np.shape(x)
+    h = np.zeros((T, W))
+    h_last = np.zeros((n, W)) if h0 is None else _f64(h0).copy()
+    for k in range(n):
+        lo, hi = int(cu[k]), int(cu[k + 1])
+        if hi <= lo:
+            continue
+        sl = slice(lo, hi)
+        hk, hl = rglru_forward(_f64(x)[None, sl], _f64(gx)[None, sl], _f64(ga)[None, sl], lam,
+                               None if reset is None else np.asarray(reset)[None, sl],
+                               None if h0 is None else _f64(h0)[k][None], c)
+        h[sl] = hk[0]
+        h_last[k] = hl[0]
+    return h, h_last
+
+
+def rglru_backward_varlen(x, gx, ga, lam, dh, cu_seqlens, reset=None, h0=None, dh_last=None, c=C_DEFAULT):
+    """Backward of rglru_forward_varlen for the loss <dh, h> + <dh_last, h_last>.
+
+    Returns dx, dgx, dga [T, W], dlam [W] (summed over every sequence and
+    token) and dh0 [n, W]; a sequence without tokens passes dh_last[s] to
+    dh0[s] unchanged.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = cu.size - 1
+    T, W = np.shape(x)
+    out = {k: np.zeros((T, W)) for k in ("dx", "dgx", "dga")}
+    out["dlam"] = np.zeros(W)
+    out["dh0"] = np.zeros((n, W)) if dh_last is None else _f64(dh_last).copy()
+    for k in range(n):
+        lo, hi = int(cu[k]), int(cu[k + 1])
+        if hi <= lo:
+            continue
+        sl = slice(lo, hi)
+        g = rglru_backward(_f64(x)[None, sl], _f64(gx)[None, sl], _f64(ga)[None, sl], lam, _f64(dh)[None, sl],
+                           None if reset is None else np.asarray(reset)[None, sl],
+                           None if h0 is None else _f64(h0)[k][None],
+                           None if dh_last is None else _f64(dh_last)[k][None], c)
+        for name in ("dx", "dgx", "dga"):
+            out[name][sl] = g[name][0]
+        out["dlam"] += g["dlam"]
+        out["dh0"][k] = g["dh0"][0]
+    return out
+
+
 def rglru_forward_chunked(x, gx, ga, lam, reset=None, h0=None, c=C_DEFAULT, chunk=64):
     """The same forward, composed from per-chunk affine maps (exact, not approximate).
 

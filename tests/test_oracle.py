@@ -188,6 +188,64 @@ def test_half_gates_backward():
     np.testing.assert_allclose(out["dh0"][0], [_expr(bw["dh0_expr"])], rtol=1e-14, atol=1e-14)
 
 
+def _golden_varlen():
+    with open(os.path.join(GOLDEN, "varlen_hand.json")) as f:
+        return json.load(f)
+
+
+def test_varlen_hand_built():
+    # three packed sequences, one of them empty, a reset token in the last:
+    # every state, final state and gradient of the hand derivation
+    g = _golden_varlen()
+    inp = g["inputs"]
+    T, n = len(inp["x"]), len(inp["cu_seqlens"]) - 1
+    x = np.array(inp["x"]).reshape(T, 1)
+    gx = np.full((T, 1), inp["gate_x"])
+    ga = np.full((T, 1), inp["gate_a"])
+    lam = np.array([_expr(inp["lam_expr"])])
+    reset = np.array(inp["reset"], dtype=np.uint8)
+    h0 = np.array(inp["h0"]).reshape(n, 1)
+    dh = np.array(inp["dh"]).reshape(T, 1)
+    dh_last = np.array(inp["dh_last"]).reshape(n, 1)
+    h, h_last = oracle.rglru_forward_varlen(x, gx, ga, lam, inp["cu_seqlens"], reset, h0, c=inp["c"])
+    np.testing.assert_allclose(h[:, 0], [_expr(e) for e in g["forward"]["h_expr"]], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(h_last[:, 0], [_expr(e) for e in g["forward"]["h_last_expr"]], rtol=1e-14)
+    out = oracle.rglru_backward_varlen(x, gx, ga, lam, dh, inp["cu_seqlens"], reset, h0, dh_last, c=inp["c"])
+    for k in ("dx", "dgx"):
+        np.testing.assert_allclose(out[k][:, 0], [_expr(e) for e in g["backward"][k + "_expr"]], rtol=1e-14,
+                                   atol=1e-14, err_msg=k)
+    np.testing.assert_allclose(out["dh0"][:, 0], [_expr(e) for e in g["backward"]["dh0_expr"]], rtol=1e-14)
+    assert out["dga"][3, 0] == 0.0   # reset token
+
+
+def test_varlen_with_a_reset_at_every_start_is_one_row():
+    # Zero initial states and a reset token on every sequence's first token:
+    # no state crosses a boundary either way, so the packed sequences are the
+    # one-row recurrence with those resets (an independent route through the
+    # row oracle's reset handling).
+    rng = np.random.default_rng(11)
+    lens = [5, 1, 0, 9, 3, 0, 12]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, W = int(cu[-1]), 4
+    x, gx, ga, dh = (rng.standard_normal((T, W)) for _ in range(4))
+    lam = rng.uniform(-6, 1, W)
+    user = (rng.random(T) < 0.15).astype(np.uint8)
+    starts = np.zeros(T, dtype=np.uint8)
+    starts[cu[:-1][np.array(lens) > 0]] = 1
+    reset = np.maximum(user, starts)
+    h, h_last = oracle.rglru_forward_varlen(x, gx, ga, lam, cu, reset)
+    hr, _ = oracle.rglru_forward(x[None], gx[None], ga[None], lam, reset[None])
+    np.testing.assert_array_equal(h, hr[0])
+    for k, (lo, hi) in enumerate(zip(cu[:-1], cu[1:])):
+        np.testing.assert_array_equal(h_last[k], hr[0, hi - 1] if hi > lo else 0.0)
+    out = oracle.rglru_backward_varlen(x, gx, ga, lam, dh, cu, reset)
+    ref = oracle.rglru_backward(x[None], gx[None], ga[None], lam, dh[None], reset[None])
+    for k in ("dx", "dgx", "dga"):
+        np.testing.assert_array_equal(out[k], ref[k][0])
+    np.testing.assert_allclose(out["dlam"], ref["dlam"], rtol=1e-13)
+    np.testing.assert_array_equal(out["dh0"], 0.0)
+
+
 # --------------------------------------------------------------- stationarity
 
 @pytest.mark.parametrize("with_h0", [False, True])
