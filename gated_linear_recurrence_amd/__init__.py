@@ -14,6 +14,9 @@ from .ops import (  # noqa: F401
     rglru_ckpt_elems,
     rglru_fwd,
     rglru_fwd_scratch,
+    rglru_fwd_varlen,
+    rglru_bwd_varlen,
+    rglru_varlen_workspace_bytes,
     rglru_fwd_workspace_bytes,
     rglru_workspace_bytes,
 )

@@ -49,6 +49,11 @@ _SIGNATURES = {
     "rglru_blockdiag_gate_proj_bwd": (c_int, [c_int64, c_int64, c_int64, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _vp, _vp, c_size_t, _vp]),
     "rglru_fwd_scratch": (c_int, [POINTER(rglru_shape_t), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "rglru_varlen_workspace_bytes": (c_size_t, [POINTER(rglru_shape_t), c_int64]),
+    "rglru_fwd_varlen": (c_int, [POINTER(rglru_shape_t), _vp, c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, c_size_t, _vp]),
+    "rglru_bwd_varlen": (c_int, [POINTER(rglru_shape_t), _vp, c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, c_size_t, _vp]),
     "rglru_status_string": (ctypes.c_char_p, [c_int]),
     "rglru_abi_version": (c_int, []),
 }

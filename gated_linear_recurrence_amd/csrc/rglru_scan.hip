@@ -52,6 +52,11 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kCkpt = RGLRU_CKPT_STEPS;
+// Segment word of a token of packed sequences: the segment's index in the low
+// 30 bits, bit 30 set on its first token, bit 31 on its last.
+constexpr uint32_t kSegId = 0x3FFFFFFFu;
+constexpr uint32_t kSegStart = 1u << 30;
+constexpr uint32_t kSegEnd = 1u << 31;
 constexpr unsigned kSpinLimit = 1u << 20;
 // Sleep between polls (units of 64 clocks). The load and control waves share
 // their SIMDs with data waves and poll at high priority, so they poll less
@@ -389,6 +394,12 @@ struct FwdArgs {
   void* h;
   float* h_last;
   float* ckpt;
+  // packed sequences (batch row 0 only; nullptr otherwise): per-token
+  // segment word (segment id, start and end bits), the segments' initial and
+  // final states [n_segments, W]
+  const uint32_t* seg;
+  const float* h0s;
+  float* h_last_s;
   Header* hdr;
   u64* slot_a;
   u64* slot_b;
@@ -486,7 +497,7 @@ constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 // row in LDS is then 64 * sizeof(io) bytes. Otherwise each instruction fills
 // one row with 2 or 4 bytes per lane, each lane's value zero-extended into its
 // own 4-byte slot (rows of 256 bytes).
-template <typename IO, int NW, int TS, bool WIDE>
+template <typename IO, int NW, int TS, bool WIDE, bool PACKED>
 __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   using elem = typename IO::elem;
   using io = Io<IO, 1>;
@@ -501,12 +512,14 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   constexpr int NFL = T < 64 ? 64 : T;     // reset-flag slots per buffer (one instruction fills 64)
   constexpr int CTRL0 = NW, LOAD0 = NW + 2;
   static_assert(TS % kCkpt == 0, "checkpoints fall on wave boundaries, at compile-time steps of a wave");
-  static_assert(TS <= 32 && NW <= 32, "reset flags of a wave's steps, and of the waves, fit one mask word");
+  static_assert(TS <= 16 && NW <= 32, "a wave's cut and end flags share one mask word; the waves' flags fit one");
   static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
   static_assert(NFL % 64 == 0 && NFL <= 128, "reset flags: at most two instructions");
 
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][3][T][ROWB];
   __shared__ unsigned s_rflag[2][NFL];
+  __shared__ uint32_t s_seg[2][NFL];  // segment words (packed sequences)
+  __shared__ uint32_t s_endseg[3][NW][TS];   // a wave's segment ends, per ring slot
   __shared__ float s_k2[2][64];
   // per map slot (iteration % 3): the data waves' maps, the prefixes the
   // replay starts from and the tile's incoming carry
@@ -658,6 +671,14 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
           const long long st = h * 64 + lane;
           const long long tk = t.t0 + (st < lim ? st : lim);
           __builtin_amdgcn_global_load_lds(p.reset + t.rowbase + tk, &s_rflag[j][h * 64], 1, 0, 0);
+        }
+      }
+      if constexpr (PACKED) {
+#pragma unroll
+        for (int h = 0; h < NFL / 64; ++h) {
+          const long long st = h * 64 + lane;
+          const long long tk = t.t0 + (st < lim ? st : lim);
+          __builtin_amdgcn_global_load_lds(const_cast<uint32_t*>(p.seg) + t.rowbase + tk, &s_seg[j][h * 64], 4, 0, 0);
         }
       }
       // the next two tickets, two iterations ahead (load wave 0 draws them all,
@@ -859,6 +880,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
       float PB = s_PB[rs_slot][wave][lane];
       unsigned PRm = s_PRm[rs_slot];
       unsigned rfl = s_rflag[cb][wave * TS + (lane < TS ? lane : 0)];
+      uint32_t sgw = PACKED ? s_seg[cb][wave * TS + (lane < TS ? lane : 0)] : 0u;
       float k2 = s_k2[cb][lane];
       pace(i, f_other);
       flush(pend);
@@ -906,6 +928,10 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
           const bool rs = ((rrm >> k) & 1u) != 0u;
           const float nx = rs ? ru[k] : fmaf(ral[k], hc, ru[k]);
           hc = k < rn ? nx : hc;   // steps past L leave the state as it is
+          if (PACKED && ((rrm >> (16 + k)) & 1u) != 0u && tr.active) {
+            // a packed segment's last token: its final state
+            p.h_last_s[static_cast<long long>(s_endseg[rs_slot][wave][k]) * W + tr.ch] = hc;
+          }
         }
         put_h(k, hc);
       };
@@ -913,15 +939,25 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
         if (f_full != i) {
           lds_wait<true>(&s_full[cb], i, &s_abort, p.hdr);
           rfl = s_rflag[cb][wave * TS + (lane < TS ? lane : 0)];
+          if constexpr (PACKED) sgw = s_seg[cb][wave * TS + (lane < TS ? lane : 0)];
           k2 = s_k2[cb][lane];
         }
         const int nvalid = wave_steps(tc);
-        // reset flags of the wave's steps: lane k reads step k, one ballot
-        unsigned rmask = 0;
+        // reset flags of the wave's steps: lane k reads step k, one ballot;
+        // likewise the starts and ends of packed segments
+        unsigned rmask = 0, smask = 0, emask = 0;
         if (p.reset != nullptr) {
           const bool f = lane < nvalid && rfl != 0u;
           rmask = static_cast<unsigned>(__ballot(f));
         }
+        if constexpr (PACKED) {
+          smask = static_cast<unsigned>(__ballot(lane < nvalid && (sgw & kSegStart) != 0u));
+          emask = static_cast<unsigned>(__ballot(lane < nvalid && (sgw & kSegEnd) != 0u));
+          // the segments ending here, for the replay two iterations on
+          if (lane < TS && ((emask >> lane) & 1u) != 0u) s_endseg[ms][wave][lane] = sgw & kSegId;
+        }
+        // steps that take no carry in: reset tokens and segment starts
+        const unsigned cutm = rmask | smask;
         float A = 1.0f, Bv = 0.0f;
         // one step of the gates: (alpha, write) and the wave's map extended by
         // it. FULL: every step in range and no reset token, so no selects.
@@ -939,15 +975,23 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
             A *= a;
           } else {
             const bool rs = ((rmask >> k) & 1u) != 0u;
-            cal[k] = rs ? 0.0f : a;
-            cu[k] = (rs ? 1.0f : m) * ig * xv;
+            const bool cut = ((cutm >> k) & 1u) != 0u;
+            float u = (rs ? 1.0f : m) * ig * xv;
+            if (PACKED && ((smask >> k) & 1u) != 0u && !rs && p.h0s != nullptr) {
+              // a segment's first token: its initial state decays in
+              const uint32_t sg = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sgw), k)) & kSegId;
+              const float h0v = tc.active ? p.h0s[static_cast<long long>(sg) * W + tc.ch] : 0.0f;
+              u = fmaf(a, h0v, u);
+            }
+            cal[k] = cut ? 0.0f : a;
+            cu[k] = u;
             if (k < nvalid) {
-              Bv = rs ? cu[k] : fmaf(cal[k], Bv, cu[k]);
+              Bv = cut ? cu[k] : fmaf(cal[k], Bv, cu[k]);
               A *= cal[k];
             }
           }
         };
-        if (rmask == 0u && nvalid == TS && rrm == 0u && rn == TS) {
+        if (cutm == 0u && nvalid == TS && rrm == 0u && rn == TS) {
           // common case: both tiles whole and free of reset tokens, one
           // straight-line block the scheduler can interleave
 #pragma unroll
@@ -957,7 +1001,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
             if (k % 8 == 7) __builtin_amdgcn_sched_barrier(0);
           }
         } else {
-          if (rmask == 0u && nvalid == TS) {
+          if (cutm == 0u && nvalid == TS) {
 #pragma unroll
             for (int k = 0; k < TS; ++k) {
               gate_step(k, true);
@@ -973,10 +1017,10 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
 #pragma unroll
           for (int k = 0; k < TS; ++k) replay_step(k, false);
         }
-        crm = rmask;
+        crm = cutm | (emask << 16);
         s_A[ms][wave][lane] = A;
         s_B[ms][wave][lane] = Bv;
-        if (lane == 0) s_R[ms][wave] = rmask != 0u ? 1u : 0u;
+        if (lane == 0) s_R[ms][wave] = cutm != 0u ? 1u : 0u;
         lds_release();
         if (lane == 0) {
           lds_add(&s_maps_in[ms], 1);
@@ -1075,18 +1119,21 @@ __global__ __launch_bounds__(256) void fwd_serial_kernel(FwdArgs p) {
   const long long rowbase = static_cast<long long>(b) * p.L;
   R_t rx[kSerialMaxL], rgx[kSerialMaxL], rga[kSerialMaxL];
   bool rs[kSerialMaxL];
+  uint32_t sgw[kSerialMaxL];
 #pragma unroll
   for (int k = 0; k < kSerialMaxL; ++k) {
     rx[k] = R_t{};
     rgx[k] = R_t{};
     rga[k] = R_t{};
     rs[k] = false;
+    sgw[k] = 0u;
     if (k < p.L) {
       const long long off = (rowbase + k) * W + ch;
       rx[k] = io::load_nt(p.x, off);
       rgx[k] = io::load_nt(p.gx, off);
       rga[k] = io::load_nt(p.ga, off);
       rs[k] = p.reset != nullptr && p.reset[rowbase + k] != 0;
+      if (p.seg != nullptr) sgw[k] = p.seg[rowbase + k];
     }
   }
   float k2[V], h[V];
@@ -1106,6 +1153,10 @@ __global__ __launch_bounds__(256) void fwd_serial_kernel(FwdArgs p) {
       io::unpack(rx[k], xv);
       io::unpack(rgx[k], gxv);
       io::unpack(rga[k], gav);
+      // a packed segment's first token starts from the segment's initial
+      // state (zero without h0s)
+      const bool start = (sgw[k] & kSegStart) != 0u;
+      const long long sg = static_cast<long long>(sgw[k] & kSegId);
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         const float ig = sigmoid_f(gxv[j]);
@@ -1113,9 +1164,11 @@ __global__ __launch_bounds__(256) void fwd_serial_kernel(FwdArgs p) {
         const float y = k2[j] * r;
         const float a = __builtin_amdgcn_exp2f(y);
         const float m = __builtin_amdgcn_sqrtf(one_minus_exp2(y, a) * (1.0f + a));
-        h[j] = rs[k] ? ig * xv[j] : fmaf(a, h[j], m * ig * xv[j]);
+        const float hp = start ? (p.h0s != nullptr ? p.h0s[sg * W + ch + j] : 0.0f) : h[j];
+        h[j] = rs[k] ? ig * xv[j] : fmaf(a, hp, m * ig * xv[j]);
       }
       io::store_nt(p.h, (rowbase + k) * W + ch, io::pack(h));
+      if ((sgw[k] & kSegEnd) != 0u && p.h_last_s != nullptr) store_f32v<V>(p.h_last_s + sg * W + ch, h);
     }
   }
   if (p.h_last != nullptr) store_f32v<V>(p.h_last + static_cast<long long>(b) * W + ch, h);
@@ -1173,6 +1226,13 @@ struct BwdArgs {
   void* dga;
   float* dlam;
   float* dh0;
+  // packed sequences (batch row 0 only; nullptr otherwise): per-token
+  // segment word, the segments' initial states and the gradients on their
+  // final states in, the gradients on their initial states out [n_segments, W]
+  const uint32_t* seg;
+  const float* h0s;
+  const float* dh_last_s;
+  float* dh0s;
   Header* hdr;
   u64* slot_a;           // published reverse map A (a reset in the sign bit)
   u64* slot_b;           // published reverse map B
@@ -1189,7 +1249,7 @@ struct BwdArgs {
   bool out_wide;         // output rows start 16-byte aligned
 };
 
-template <typename IO, int NW, bool WIDE>
+template <typename IO, int NW, bool WIDE, bool PACKED>
 __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
   using elem = typename IO::elem;
   using io = Io<IO, 1>;
@@ -1216,6 +1276,8 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) unsigned char s_rx[4][2][T][ROWB];
   __shared__ __attribute__((aligned(16))) float s_ck[4][NW][64];   // state entering each wave's first step
   __shared__ unsigned s_rflag[2][NFL];
+  __shared__ uint32_t s_seg[2][NFL];  // segment words (packed sequences)
+  __shared__ uint32_t s_sseg[3][NW][TS];     // a wave's segment starts, per ring slot
   __shared__ float s_k2[4][64];
   __shared__ float s_cs[4][64];
   // a wave's reverse map; the control wave overwrites it with the composite
@@ -1395,6 +1457,14 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
           const long long st = h * 64 + lane;
           const long long tk = t.t0 + (st < lim ? st : lim);
           __builtin_amdgcn_global_load_lds(p.reset + t.rowbase + tk, &s_rflag[j][h * 64], 1, 0, 0);
+        }
+      }
+      if constexpr (PACKED) {
+#pragma unroll
+        for (int h = 0; h < NFL / 64; ++h) {
+          const long long st = h * 64 + lane;
+          const long long tk = t.t0 + (st < lim ? st : lim);
+          __builtin_amdgcn_global_load_lds(const_cast<uint32_t*>(p.seg) + t.rowbase + tk, &s_seg[j][h * 64], 4, 0, 0);
         }
       }
       u64 nxt = 0;
@@ -1582,6 +1652,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       unsigned q_p = s_tk[(i + RING - 1) % RING];
       unsigned q_r = s_tk[(i + RING - 2) % RING];
       unsigned rfl = s_rflag[mb][wave * TS + (lane < TS ? lane : 0)];
+      uint32_t sgw = PACKED ? s_seg[mb][wave * TS + (lane < TS ? lane : 0)] : 0u;
       float k2m = s_k2[i & 3][lane];
       float c0 = s_carry[rs3][lane];
       float SA = s_A[rs3][wave][lane];
@@ -1606,14 +1677,23 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
         if (f_full != i) {
           lds_wait<true>(&s_full[mb], i, &s_abort, p.hdr);
           rfl = s_rflag[mb][wave * TS + (lane < TS ? lane : 0)];
+          if constexpr (PACKED) sgw = s_seg[mb][wave * TS + (lane < TS ? lane : 0)];
           k2m = s_k2[i & 3][lane];
         }
         const int nvalid = wave_steps(tc, wave);
-        unsigned rmask = 0;
+        unsigned rmask = 0, smask = 0, emask = 0;
         if (p.reset != nullptr) {
           const bool f = lane < nvalid && rfl != 0u;
           rmask = static_cast<unsigned>(__ballot(f));
         }
+        if constexpr (PACKED) {
+          smask = static_cast<unsigned>(__ballot(lane < nvalid && (sgw & kSegStart) != 0u));
+          emask = static_cast<unsigned>(__ballot(lane < nvalid && (sgw & kSegEnd) != 0u));
+          // the segments starting here, for the reverse pass two iterations on
+          if (lane < TS && ((smask >> lane) & 1u) != 0u) s_sseg[ms][wave][lane] = sgw & kSegId;
+        }
+        // steps that pass no gradient back: reset tokens and segment starts
+        const unsigned cutm = rmask | smask;
         const float k2 = k2m;
 #pragma unroll
         for (int k = 0; k < TS; ++k) {
@@ -1624,11 +1704,22 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
         }
         lds_release();
         if (lane == 0) lds_add(&s_cons_m[mb], 1);
+        if (PACKED && emask != 0u && p.dh_last_s != nullptr) {
+          // a packed segment's last token also carries the gradient on the
+          // segment's final state
+#pragma unroll
+          for (int k = 0; k < TS; ++k) {
+            if (((emask >> k) & 1u) != 0u && tc.active) {
+              const uint32_t sg = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sgw), k)) & kSegId;
+              cd[k] += p.dh_last_s[static_cast<long long>(sg) * W + tc.ch];
+            }
+          }
+        }
         // the wave's reverse map G_in -> G_out, latest step first
         // (a reset token passes nothing on: a select, so not even a NaN
         // arriving from a later step crosses it)
         float A = 1.0f, Bv = 0.0f;
-        if (rmask == 0u && nvalid == TS) {
+        if (cutm == 0u && nvalid == TS) {
 #pragma unroll
           for (int k = TS - 1; k >= 0; --k) {
             Bv = ca[k] * (Bv + cd[k]);
@@ -1638,16 +1729,16 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
 #pragma unroll
           for (int k = TS - 1; k >= 0; --k) {
             if (k < nvalid) {
-              const bool rs = ((rmask >> k) & 1u) != 0u;
-              Bv = rs ? 0.0f : ca[k] * (Bv + cd[k]);
-              A = rs ? 0.0f : ca[k] * A;
+              const bool cut = ((cutm >> k) & 1u) != 0u;
+              Bv = cut ? 0.0f : ca[k] * (Bv + cd[k]);
+              A = cut ? 0.0f : ca[k] * A;
             }
           }
         }
-        cm = rmask;
+        cm = rmask | (smask << 16);
         s_A[ms][wave][lane] = A;
         s_B[ms][wave][lane] = Bv;
-        if (lane == 0) s_R[ms][wave] = rmask != 0u ? 1u : 0u;
+        if (lane == 0) s_R[ms][wave] = cutm != 0u ? 1u : 0u;
         lds_release();
         if (lane == 0) lds_add(&s_maps_in[ms], 1);
       } else {
@@ -1686,6 +1777,14 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
             const float r = pr[k];
             const float a = pa[k];
             const bool rs = FULL ? false : ((pm >> k) & 1u) != 0u;
+            // a packed segment's first token starts from the segment's
+            // initial state (zero without h0s), not the carry
+            float hp = h;
+            if (PACKED && !FULL && ((pm >> (16 + k)) & 1u) != 0u) {
+              hp = (tr.active && p.h0s != nullptr)
+                       ? p.h0s[static_cast<long long>(s_sseg[rs3][wave][k]) * W + tr.ch]
+                       : 0.0f;
+            }
             const float y = k2 * r;
             const float w1 = one_minus_exp2(y, a) * (1.0f + a);  // 1 - a^2
             // 1 / m. Below the smallest normal float, 1 - a^2 comes from a
@@ -1697,9 +1796,9 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
             const float m = w1 * rsq;
             const float mult = rs ? 1.0f : m;
             const float ix = iv * xv;
-            const float z = rs ? 0.0f : a * (h - a * ix * rsq);
+            const float z = rs ? 0.0f : a * (hp - a * ix * rsq);
             const float uw = mult * ix;
-            h = rs ? uw : fmaf(a, h, uw);
+            h = rs ? uw : fmaf(a, hp, uw);
             cx[k] = mult * iv;
             cgx[k] = uw * (1.0f - iv);
             cl[k] = z * r;
@@ -1719,8 +1818,14 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
             } else {
               const bool in = k < rn;
               const bool rs = ((pm >> k) & 1u) != 0u;
+              const bool ss = PACKED && ((pm >> (16 + k)) & 1u) != 0u;
               dl = in ? fmaf(g, cl[k], dl) : dl;
-              G = in ? (rs ? 0.0f : pa[k] * g) : G;
+              if (ss && in && tr.active && p.dh0s != nullptr) {
+                // what would pass to the previous token goes to the
+                // segment's initial state instead
+                p.dh0s[static_cast<long long>(s_sseg[rs3][wave][k]) * W + tr.ch] = rs ? 0.0f : pa[k] * g;
+              }
+              G = in ? ((rs || ss) ? 0.0f : pa[k] * g) : G;
             }
           }
         };
@@ -1953,7 +2058,9 @@ rglru_status_t launch_fwd(FwdArgs a, hipStream_t stream) {
   a.n_strips = static_cast<int>(ceil_div(a.W, 64));
   a.n_chunks = static_cast<int>(ceil_div(a.L, T));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  auto kernel = fwd_kernel<IO, NW, TS, WIDE>;
+  // packed sequences run their own instantiation, so the plain kernel carries
+  // none of their registers
+  auto kernel = a.seg != nullptr ? fwd_kernel<IO, NW, TS, WIDE, true> : fwd_kernel<IO, NW, TS, WIDE, false>;
   constexpr int threads = (NW + 4) * 64;
   const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
   if (grid == 0) return RGLRU_ERR_HIP;
@@ -1992,7 +2099,7 @@ rglru_status_t launch_bwd(BwdArgs a, hipStream_t stream) {
   a.n_strips = static_cast<int>(ceil_div(a.W, 64));
   a.n_chunks = static_cast<int>(ceil_div(a.L, T));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
-  auto kernel = bwd_kernel<IO, NW, WIDE>;
+  auto kernel = a.seg != nullptr ? bwd_kernel<IO, NW, WIDE, true> : bwd_kernel<IO, NW, WIDE, false>;
   constexpr int threads = (NW + 4) * 64;
   const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
   if (grid == 0) return RGLRU_ERR_HIP;
@@ -2032,6 +2139,233 @@ bool f32_aligned(const void* p) { return p == nullptr || aligned_to(p, 4); }
 }  // namespace rglru
 
 using namespace rglru;
+
+// ------------------------------------------------------------------ calls
+
+namespace {
+
+// Packed sequences on top of a call: per-token segment words (in the
+// workspace) and the per-segment states and gradients. All null for a plain
+// call.
+struct Packed {
+  const int32_t* cu = nullptr;     // segment offsets [n + 1]
+  long long n = 0;
+  uint32_t* seg = nullptr;         // segment words, written by the call
+  const float* h0s = nullptr;
+  float* h_last_s = nullptr;
+  const float* dh_last_s = nullptr;
+  float* dh0s = nullptr;
+};
+
+// ------------------------------------------------------------------ packed sequences
+//
+// n segments packed end to end in one row of T tokens, segment s holding
+// tokens [cu[s], cu[s+1]). Each segment is its own sequence: its first token
+// starts from the segment's initial state (zero without one) and its last
+// token's state is the segment's final state; reset tokens inside keep their
+// meaning. The scan kernels read one segment word per token.
+
+// Segment word of every token; error bit 2 if the offsets are not
+// 0 = cu[0] <= cu[1] <= ... <= cu[n] = T. Invalid offsets still give every
+// token a segment index below n, so nothing is addressed out of bounds.
+__global__ __launch_bounds__(256) void varlen_seg_kernel(const int32_t* cu, long long n, long long T, uint32_t* seg,
+                                                        Header* hdr) {
+  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t < n && cu[t] > cu[t + 1]) atomicOr(&hdr->err, 4u);
+  if (t == 0 && (cu[0] != 0 || static_cast<long long>(cu[n]) != T)) atomicOr(&hdr->err, 4u);
+  if (t >= T) return;
+  // the last segment starting at or before t (empty segments are skipped
+  // over: a later segment with the same start wins)
+  long long lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const long long mid = (lo + hi + 1) >> 1;
+    if (static_cast<long long>(cu[mid]) <= t) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  uint32_t w = static_cast<uint32_t>(lo) & kSegId;
+  if (static_cast<long long>(cu[lo]) == t) w |= kSegStart;
+  if (static_cast<long long>(cu[lo + 1]) - 1 == t) w |= kSegEnd;
+  seg[t] = w;
+}
+
+// Segments without tokens: final state = initial state (forward), gradient on
+// the initial state = gradient on the final state (backward).
+__global__ __launch_bounds__(256) void varlen_empty_kernel(const int32_t* cu, long long n, int W, const float* src,
+                                                          float* dst) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n * W) return;
+  const long long sgi = i / W;
+  if (cu[sgi] >= cu[sgi + 1]) dst[i] = src != nullptr ? src[i] : 0.0f;
+}
+
+size_t varlen_ws(const rglru_shape_t* s) {
+  const size_t f = fwd_ws(s), b = bwd_ws(s);
+  return (f > b ? f : b) + round_up(static_cast<size_t>(s->length) * 4, 256);
+}
+
+// Checks shared by both directions; the segment words go after the slots.
+rglru_status_t varlen_check(const rglru_shape_t* s, const int32_t* cu, long long n, void* workspace,
+                            size_t workspace_bytes, Packed* pk) {
+  if (!shape_ok(s) || s->batch != 1 || n < 1 || n > static_cast<long long>(kSegId) || cu == nullptr ||
+      workspace == nullptr) {
+    return RGLRU_ERR_INVALID_ARGUMENT;
+  }
+  if (!aligned_to(cu, 4) || !aligned_to(workspace, 256)) return RGLRU_ERR_MISALIGNED;
+  if (workspace_bytes < varlen_ws(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
+  const size_t f = fwd_ws(s), b = bwd_ws(s);
+  pk->cu = cu;
+  pk->n = n;
+  pk->seg = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + (f > b ? f : b));
+  return RGLRU_OK;
+}
+
+rglru_status_t launch_seg(const rglru_shape_t* s, const Packed& pk, void* workspace, hipStream_t st) {
+  const long long threads = s->length > pk.n ? s->length : pk.n;
+  hipLaunchKernelGGL(varlen_seg_kernel, dim3(static_cast<unsigned>(ceil_div(threads, 256))), dim3(256), 0, st,
+                     pk.cu, pk.n, static_cast<long long>(s->length), pk.seg, static_cast<Header*>(workspace));
+  return launch_status();
+}
+
+rglru_status_t fwd_call(const rglru_shape_t* s, const void* x, const void* gate_x, const void* gate_a,
+                        const float* lambda, const uint8_t* reset, const float* h0, void* h,
+                        float* h_last, float* ckpt, void* workspace, size_t workspace_bytes,
+                        void* stream, const Packed& pk) {
+  if (!shape_ok(s)) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (!x || !gate_x || !gate_a || !lambda || !h || !workspace) return RGLRU_ERR_INVALID_ARGUMENT;
+  const Geometry g = geometry(s);
+  if (!io_aligned(x, g.io_bytes) || !io_aligned(gate_x, g.io_bytes) || !io_aligned(gate_a, g.io_bytes) ||
+      !io_aligned(h, g.io_bytes) || !f32_aligned(lambda) || !f32_aligned(h0) || !f32_aligned(h_last) ||
+      !f32_aligned(ckpt) || !aligned_to(workspace, 256)) {
+    return RGLRU_ERR_MISALIGNED;
+  }
+  if (workspace_bytes < fwd_ws(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
+  if (!f32_aligned(pk.h0s) || !f32_aligned(pk.h_last_s)) return RGLRU_ERR_MISALIGNED;
+
+  if (pk.cu != nullptr) {
+    const rglru_status_t r = launch_seg(s, pk, workspace, static_cast<hipStream_t>(stream));
+    if (r != RGLRU_OK) return r;
+  }
+  const int V = pick_vec(RGLRU_FWD_VMAX, s->width, g.io_bytes, {x, gate_x, gate_a, h}, {h0, h_last, ckpt});
+  const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_f));
+  FwdArgs a;
+  a.x = x;
+  a.gx = gate_x;
+  a.ga = gate_a;
+  a.lam = lambda;
+  a.reset = reset;
+  a.h0 = h0;
+  a.h = h;
+  a.h_last = h_last;
+  a.ckpt = ckpt;
+  a.seg = pk.seg;
+  a.h0s = pk.h0s;
+  a.h_last_s = pk.h_last_s;
+  a.hdr = sl.hdr;
+  a.slot_a = sl.a;
+  a.slot_b = sl.b;
+  a.slot_h = sl.h;
+  a.L = s->length;
+  a.n_ckpt = g.n_ckpt;
+  a.B = static_cast<int>(s->batch);
+  a.W = static_cast<int>(s->width);
+  a.c = s->c;
+  // 16-byte loads: rows a multiple of 16 bytes, the three inputs 16-byte aligned
+  const bool wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(x, 16) && aligned_to(gate_x, 16) &&
+                    aligned_to(gate_a, 16) && 128LL * s->width * g.io_bytes < (1LL << 31);
+  a.h_wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(h, 16);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s->length <= kSerialMaxL) {
+    const unsigned grid = static_cast<unsigned>(ceil_div(s->batch * (s->width / V), 256));
+    if (s->io_dtype == RGLRU_IO_F32) {
+      hipLaunchKernelGGL((fwd_serial_kernel<F32, 1>), dim3(static_cast<unsigned>(ceil_div(s->batch * s->width, 256))),
+                         dim3(256), 0, st, a);
+    } else if (V >= 4) {
+      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 4>), dim3(grid), dim3(256), 0, st, a);
+    } else if (V == 2) {
+      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 2>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 1>), dim3(grid), dim3(256), 0, st, a);
+    }
+    return launch_status();
+  }
+  const int req = s->chunk == 0 ? 128 : s->chunk;
+  const int T = fwd_tile(req, wide, g.io_bytes);
+  if (s->io_dtype == RGLRU_IO_F32) {
+    return wide ? dispatch_fwd<F32, true>(T, a, st) : dispatch_fwd<F32, false>(T, a, st);
+  }
+  return wide ? dispatch_fwd<BF16, true>(T, a, st) : dispatch_fwd<BF16, false>(T, a, st);
+}
+
+rglru_status_t bwd_call(const rglru_shape_t* s, const void* x, const void* gate_x, const void* gate_a,
+                        const float* lambda, const uint8_t* reset, const float* ckpt, const void* dh,
+                        const float* dh_last, void* dx, void* dgate_x, void* dgate_a, float* dlambda,
+                        float* dh0, void* workspace, size_t workspace_bytes, void* stream, const Packed& pk) {
+  if (!shape_ok(s)) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (!x || !gate_x || !gate_a || !lambda || !ckpt || !dh || !dx || !dgate_x || !dgate_a || !dlambda ||
+      !workspace) {
+    return RGLRU_ERR_INVALID_ARGUMENT;
+  }
+  const Geometry g = geometry(s);
+  if (!io_aligned(x, g.io_bytes) || !io_aligned(gate_x, g.io_bytes) || !io_aligned(gate_a, g.io_bytes) ||
+      !io_aligned(dh, g.io_bytes) || !io_aligned(dx, g.io_bytes) || !io_aligned(dgate_x, g.io_bytes) ||
+      !io_aligned(dgate_a, g.io_bytes) || !f32_aligned(lambda) || !f32_aligned(ckpt) ||
+      !f32_aligned(dh_last) || !f32_aligned(dlambda) || !f32_aligned(dh0) || !aligned_to(workspace, 256)) {
+    return RGLRU_ERR_MISALIGNED;
+  }
+  if (workspace_bytes < bwd_ws(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
+  if (!f32_aligned(pk.h0s) || !f32_aligned(pk.dh_last_s) || !f32_aligned(pk.dh0s)) return RGLRU_ERR_MISALIGNED;
+  if (pk.cu != nullptr) {
+    const rglru_status_t r = launch_seg(s, pk, workspace, static_cast<hipStream_t>(stream));
+    if (r != RGLRU_OK) return r;
+  }
+
+  const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_b));
+  BwdArgs a;
+  a.x = x;
+  a.gx = gate_x;
+  a.ga = gate_a;
+  a.lam = lambda;
+  a.reset = reset;
+  a.ckpt = ckpt;
+  a.dh = dh;
+  a.dh_last = dh_last;
+  a.dx = dx;
+  a.dgx = dgate_x;
+  a.dga = dgate_a;
+  a.dlam = dlambda;
+  a.dh0 = dh0;
+  a.seg = pk.seg;
+  a.h0s = pk.h0s;
+  a.dh_last_s = pk.dh_last_s;
+  a.dh0s = pk.dh0s;
+  a.hdr = sl.hdr;
+  a.slot_a = sl.a;
+  a.slot_b = sl.b;
+  a.slot_h = sl.h;
+  a.part = reinterpret_cast<float*>(sl.p);
+  a.L = s->length;
+  a.n_ckpt = g.n_ckpt;
+  a.B = static_cast<int>(s->batch);
+  a.W = static_cast<int>(s->width);
+  a.c = s->c;
+  // 16-byte loads: rows a multiple of 16 bytes, the four inputs 16-byte aligned
+  const bool wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(x, 16) && aligned_to(gate_x, 16) &&
+                    aligned_to(gate_a, 16) && aligned_to(dh, 16) && 64LL * s->width * g.io_bytes < (1LL << 31);
+  a.out_wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(dx, 16) && aligned_to(dgate_x, 16) &&
+               aligned_to(dgate_a, 16);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int req = s->chunk == 0 ? 64 : s->chunk;
+  const int T = bwd_tile(req, wide, g.io_bytes);
+  if (s->io_dtype == RGLRU_IO_F32) {
+    return wide ? dispatch_bwd<F32, true>(T, a, st) : dispatch_bwd<F32, false>(T, a, st);
+  }
+  return wide ? dispatch_bwd<BF16, true>(T, a, st) : dispatch_bwd<BF16, false>(T, a, st);
+}
+
+}  // namespace
 
 // ------------------------------------------------------------------ allocation-free forward
 //
@@ -2088,119 +2422,16 @@ rglru_status_t rglru_fwd(const rglru_shape_t* s, const void* x, const void* gate
                          const float* lambda, const uint8_t* reset, const float* h0, void* h,
                          float* h_last, float* ckpt, void* workspace, size_t workspace_bytes,
                          void* stream) {
-  if (!shape_ok(s)) return RGLRU_ERR_INVALID_ARGUMENT;
-  if (!x || !gate_x || !gate_a || !lambda || !h || !workspace) return RGLRU_ERR_INVALID_ARGUMENT;
-  const Geometry g = geometry(s);
-  if (!io_aligned(x, g.io_bytes) || !io_aligned(gate_x, g.io_bytes) || !io_aligned(gate_a, g.io_bytes) ||
-      !io_aligned(h, g.io_bytes) || !f32_aligned(lambda) || !f32_aligned(h0) || !f32_aligned(h_last) ||
-      !f32_aligned(ckpt) || !aligned_to(workspace, 256)) {
-    return RGLRU_ERR_MISALIGNED;
-  }
-  if (workspace_bytes < fwd_ws(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
-
-  const int V = pick_vec(RGLRU_FWD_VMAX, s->width, g.io_bytes, {x, gate_x, gate_a, h}, {h0, h_last, ckpt});
-  const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_f));
-  FwdArgs a;
-  a.x = x;
-  a.gx = gate_x;
-  a.ga = gate_a;
-  a.lam = lambda;
-  a.reset = reset;
-  a.h0 = h0;
-  a.h = h;
-  a.h_last = h_last;
-  a.ckpt = ckpt;
-  a.hdr = sl.hdr;
-  a.slot_a = sl.a;
-  a.slot_b = sl.b;
-  a.slot_h = sl.h;
-  a.L = s->length;
-  a.n_ckpt = g.n_ckpt;
-  a.B = static_cast<int>(s->batch);
-  a.W = static_cast<int>(s->width);
-  a.c = s->c;
-  // 16-byte loads: rows a multiple of 16 bytes, the three inputs 16-byte aligned
-  const bool wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(x, 16) && aligned_to(gate_x, 16) &&
-                    aligned_to(gate_a, 16) && 128LL * s->width * g.io_bytes < (1LL << 31);
-  a.h_wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(h, 16);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (s->length <= kSerialMaxL) {
-    const unsigned grid = static_cast<unsigned>(ceil_div(s->batch * (s->width / V), 256));
-    if (s->io_dtype == RGLRU_IO_F32) {
-      hipLaunchKernelGGL((fwd_serial_kernel<F32, 1>), dim3(static_cast<unsigned>(ceil_div(s->batch * s->width, 256))),
-                         dim3(256), 0, st, a);
-    } else if (V >= 4) {
-      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 4>), dim3(grid), dim3(256), 0, st, a);
-    } else if (V == 2) {
-      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 2>), dim3(grid), dim3(256), 0, st, a);
-    } else {
-      hipLaunchKernelGGL((fwd_serial_kernel<BF16, 1>), dim3(grid), dim3(256), 0, st, a);
-    }
-    return launch_status();
-  }
-  const int req = s->chunk == 0 ? 128 : s->chunk;
-  const int T = fwd_tile(req, wide, g.io_bytes);
-  if (s->io_dtype == RGLRU_IO_F32) {
-    return wide ? dispatch_fwd<F32, true>(T, a, st) : dispatch_fwd<F32, false>(T, a, st);
-  }
-  return wide ? dispatch_fwd<BF16, true>(T, a, st) : dispatch_fwd<BF16, false>(T, a, st);
+  return fwd_call(s, x, gate_x, gate_a, lambda, reset, h0, h, h_last, ckpt, workspace, workspace_bytes, stream,
+                  Packed{});
 }
 
 rglru_status_t rglru_bwd(const rglru_shape_t* s, const void* x, const void* gate_x, const void* gate_a,
                          const float* lambda, const uint8_t* reset, const float* ckpt, const void* dh,
                          const float* dh_last, void* dx, void* dgate_x, void* dgate_a, float* dlambda,
                          float* dh0, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!shape_ok(s)) return RGLRU_ERR_INVALID_ARGUMENT;
-  if (!x || !gate_x || !gate_a || !lambda || !ckpt || !dh || !dx || !dgate_x || !dgate_a || !dlambda ||
-      !workspace) {
-    return RGLRU_ERR_INVALID_ARGUMENT;
-  }
-  const Geometry g = geometry(s);
-  if (!io_aligned(x, g.io_bytes) || !io_aligned(gate_x, g.io_bytes) || !io_aligned(gate_a, g.io_bytes) ||
-      !io_aligned(dh, g.io_bytes) || !io_aligned(dx, g.io_bytes) || !io_aligned(dgate_x, g.io_bytes) ||
-      !io_aligned(dgate_a, g.io_bytes) || !f32_aligned(lambda) || !f32_aligned(ckpt) ||
-      !f32_aligned(dh_last) || !f32_aligned(dlambda) || !f32_aligned(dh0) || !aligned_to(workspace, 256)) {
-    return RGLRU_ERR_MISALIGNED;
-  }
-  if (workspace_bytes < bwd_ws(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
-
-  const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_b));
-  BwdArgs a;
-  a.x = x;
-  a.gx = gate_x;
-  a.ga = gate_a;
-  a.lam = lambda;
-  a.reset = reset;
-  a.ckpt = ckpt;
-  a.dh = dh;
-  a.dh_last = dh_last;
-  a.dx = dx;
-  a.dgx = dgate_x;
-  a.dga = dgate_a;
-  a.dlam = dlambda;
-  a.dh0 = dh0;
-  a.hdr = sl.hdr;
-  a.slot_a = sl.a;
-  a.slot_b = sl.b;
-  a.slot_h = sl.h;
-  a.part = reinterpret_cast<float*>(sl.p);
-  a.L = s->length;
-  a.n_ckpt = g.n_ckpt;
-  a.B = static_cast<int>(s->batch);
-  a.W = static_cast<int>(s->width);
-  a.c = s->c;
-  // 16-byte loads: rows a multiple of 16 bytes, the four inputs 16-byte aligned
-  const bool wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(x, 16) && aligned_to(gate_x, 16) &&
-                    aligned_to(gate_a, 16) && aligned_to(dh, 16) && 64LL * s->width * g.io_bytes < (1LL << 31);
-  a.out_wide = (s->width * g.io_bytes) % 16 == 0 && aligned_to(dx, 16) && aligned_to(dgate_x, 16) &&
-               aligned_to(dgate_a, 16);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int req = s->chunk == 0 ? 64 : s->chunk;
-  const int T = bwd_tile(req, wide, g.io_bytes);
-  if (s->io_dtype == RGLRU_IO_F32) {
-    return wide ? dispatch_bwd<F32, true>(T, a, st) : dispatch_bwd<F32, false>(T, a, st);
-  }
-  return wide ? dispatch_bwd<BF16, true>(T, a, st) : dispatch_bwd<BF16, false>(T, a, st);
+  return bwd_call(s, x, gate_x, gate_a, lambda, reset, ckpt, dh, dh_last, dx, dgate_x, dgate_a, dlambda, dh0,
+                  workspace, workspace_bytes, stream, Packed{});
 }
 
 rglru_status_t rglru_fwd_scratch(const rglru_shape_t* s, const void* x, const void* gate_x, const void* gate_a,
@@ -2213,6 +2444,56 @@ rglru_status_t rglru_fwd_scratch(const rglru_shape_t* s, const void* x, const vo
   void* ws = scratch_addr(dev);
   if (ws == nullptr) return RGLRU_ERR_HIP;
   return rglru_fwd(s, x, gate_x, gate_a, lambda, reset, h0, h, h_last, ckpt, ws, kScratchBytes, stream);
+}
+
+size_t rglru_varlen_workspace_bytes(const rglru_shape_t* s, int64_t n_seqs) {
+  if (!shape_ok(s) || s->batch != 1 || n_seqs < 1 || n_seqs > static_cast<int64_t>(kSegId)) return 0;
+  return varlen_ws(s);
+}
+
+rglru_status_t rglru_fwd_varlen(const rglru_shape_t* s, const int32_t* cu_seqlens, int64_t n_seqs, const void* x,
+                                const void* gate_x, const void* gate_a, const float* lambda, const uint8_t* reset,
+                                const float* h0, void* h, float* h_last, float* ckpt, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!x || !gate_x || !gate_a || !lambda || !h) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (!f32_aligned(h0) || !f32_aligned(h_last)) return RGLRU_ERR_MISALIGNED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Packed pk;
+  rglru_status_t r = varlen_check(s, cu_seqlens, n_seqs, workspace, workspace_bytes, &pk);
+  if (r != RGLRU_OK) return r;
+  pk.h0s = h0;
+  pk.h_last_s = h_last;
+  r = fwd_call(s, x, gate_x, gate_a, lambda, reset, nullptr, h, nullptr, ckpt, workspace, workspace_bytes, st, pk);
+  if (r != RGLRU_OK || h_last == nullptr) return r;
+  const long long n = n_seqs * s->width;
+  hipLaunchKernelGGL(varlen_empty_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, st,
+                     cu_seqlens, static_cast<long long>(n_seqs), static_cast<int>(s->width), h0, h_last);
+  return launch_status();
+}
+
+rglru_status_t rglru_bwd_varlen(const rglru_shape_t* s, const int32_t* cu_seqlens, int64_t n_seqs, const void* x,
+                                const void* gate_x, const void* gate_a, const float* lambda, const uint8_t* reset,
+                                const float* h0, const float* ckpt, const void* dh, const float* dh_last, void* dx,
+                                void* dgate_x, void* dgate_a, float* dlambda, float* dh0, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!x || !gate_x || !gate_a || !lambda || !ckpt || !dh || !dx || !dgate_x || !dgate_a || !dlambda) {
+    return RGLRU_ERR_INVALID_ARGUMENT;
+  }
+  if (!f32_aligned(h0) || !f32_aligned(dh_last) || !f32_aligned(dh0)) return RGLRU_ERR_MISALIGNED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Packed pk;
+  rglru_status_t r = varlen_check(s, cu_seqlens, n_seqs, workspace, workspace_bytes, &pk);
+  if (r != RGLRU_OK) return r;
+  pk.h0s = h0;
+  pk.dh_last_s = dh_last;
+  pk.dh0s = dh0;
+  r = bwd_call(s, x, gate_x, gate_a, lambda, reset, ckpt, dh, nullptr, dx, dgate_x, dgate_a, dlambda, nullptr,
+               workspace, workspace_bytes, st, pk);
+  if (r != RGLRU_OK || dh0 == nullptr) return r;
+  const long long n = n_seqs * s->width;
+  hipLaunchKernelGGL(varlen_empty_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, st,
+                     cu_seqlens, static_cast<long long>(n_seqs), static_cast<int>(s->width), dh_last, dh0);
+  return launch_status();
 }
 
 const char* rglru_status_string(rglru_status_t status) {

@@ -88,7 +88,8 @@ class Workspace:
 
         Bit 0: a wait for another workgroup's published prefix hit its spin
         limit. Bit 1: a wait between the waves of one workgroup hit its spin
-        limit. Either invalidates the outputs of the call that set it.
+        limit. Bit 2: the offsets of a packed-sequence call were not valid.
+        Each invalidates the outputs of the call that set it.
         """
         if self.buf is None:
             return 0
@@ -115,8 +116,10 @@ class WorkspaceError(RuntimeError):
             kinds.append("cross-workgroup look-back wait hit its spin limit")
         if bits & 2:
             kinds.append("wait between waves of a workgroup hit its spin limit")
-        if bits & ~3:
-            kinds.append(f"unknown bits {bits & ~3:#x}")
+        if bits & 4:
+            kinds.append("packed-sequence offsets (cu_seqlens) were not valid")
+        if bits & ~7:
+            kinds.append(f"unknown bits {bits & ~7:#x}")
         super().__init__("rglru workspace error word %#x: %s" % (bits, "; ".join(kinds)))
         self.bits = bits
 
@@ -246,6 +249,88 @@ def rglru_bwd(x: torch.Tensor, gate_x: torch.Tensor, gate_a: torch.Tensor, lam: 
                        _ptr(ckpt), _ptr(dh), _ptr(dh_last), _ptr(dx), _ptr(dgate_x), _ptr(dgate_a),
                        _ptr(dlam), _ptr(dh0), _ptr(buf), buf.numel(), _stream(dev))
     _lib.check(st, "rglru_bwd")
+    return dx, dgate_x, dgate_a, dlam, dh0
+
+
+def rglru_varlen_workspace_bytes(shape: _lib.rglru_shape_t, n_seqs: int) -> int:
+    return int(_lib.load().rglru_varlen_workspace_bytes(ctypes.byref(shape), int(n_seqs)))
+
+
+def _varlen_common(x, gate_x, gate_a, lam, cu_seqlens, reset, h0):
+    dev = x.device
+    if x.dim() != 2:
+        raise ValueError("packed x must be [T, W]")
+    T, W = x.shape
+    io = x.dtype
+    if io not in _IO:
+        raise ValueError(f"unsupported io dtype {io}")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [n + 1] with n >= 1")
+    n = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (n + 1,), torch.int32, dev)
+    _need(x, "x", (T, W), io, dev)
+    _need(gate_x, "gate_x", (T, W), io, dev)
+    _need(gate_a, "gate_a", (T, W), io, dev)
+    _need(lam, "lambda", (W,), torch.float32, dev)
+    _opt(reset, "reset", (T,), torch.uint8, dev)
+    _opt(h0, "h0", (n, W), torch.float32, dev)
+    return dev, T, W, io, n
+
+
+def rglru_fwd_varlen(x: torch.Tensor, gate_x: torch.Tensor, gate_a: torch.Tensor, lam: torch.Tensor,
+                     cu_seqlens: torch.Tensor, reset: Optional[torch.Tensor] = None,
+                     h0: Optional[torch.Tensor] = None, *, chunk: int = 0, c: float = 8.0, training: bool = True,
+                     want_h_last: bool = True, h: Optional[torch.Tensor] = None,
+                     h_last: Optional[torch.Tensor] = None, ckpt: Optional[torch.Tensor] = None,
+                     workspace: Optional[Workspace] = None):
+    """Forward scan of packed sequences: x [T, W], cu_seqlens [n + 1] int32 on the device.
+    Returns (h [T, W], h_last [n, W] or None, ckpt or None)."""
+    lib = _lib.load()
+    dev, T, W, io, n = _varlen_common(x, gate_x, gate_a, lam, cu_seqlens, reset, h0)
+    shape = make_shape(1, T, W, io, chunk, c)
+    if h is None:
+        h = torch.empty((T, W), dtype=io, device=dev)
+    _need(h, "h", (T, W), io, dev)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((n, W), dtype=torch.float32, device=dev)
+    _opt(h_last, "h_last", (n, W), torch.float32, dev)
+    if ckpt is None and training:
+        ckpt = torch.empty(rglru_ckpt_elems(shape), dtype=torch.float32, device=dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", (rglru_ckpt_elems(shape),), torch.float32, dev)
+    ws = workspace if workspace is not None else default_workspace(dev)
+    buf = ws.get(rglru_varlen_workspace_bytes(shape, n))
+    st = lib.rglru_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), n, _ptr(x), _ptr(gate_x), _ptr(gate_a),
+                              _ptr(lam), _ptr(reset), _ptr(h0), _ptr(h), _ptr(h_last), _ptr(ckpt), _ptr(buf),
+                              buf.numel(), _stream(dev))
+    _lib.check(st, "rglru_fwd_varlen")
+    return h, h_last, ckpt
+
+
+def rglru_bwd_varlen(x: torch.Tensor, gate_x: torch.Tensor, gate_a: torch.Tensor, lam: torch.Tensor,
+                     cu_seqlens: torch.Tensor, reset: Optional[torch.Tensor], h0: Optional[torch.Tensor],
+                     ckpt: torch.Tensor, dh: torch.Tensor, dh_last: Optional[torch.Tensor] = None, *,
+                     chunk: int = 0, c: float = 8.0, want_dh0: bool = True,
+                     workspace: Optional[Workspace] = None):
+    """Backward of rglru_fwd_varlen. Returns (dx, dgate_x, dgate_a, dlambda, dh0 [n, W] or None)."""
+    lib = _lib.load()
+    dev, T, W, io, n = _varlen_common(x, gate_x, gate_a, lam, cu_seqlens, reset, h0)
+    shape = make_shape(1, T, W, io, chunk, c)
+    _need(dh, "dh", (T, W), io, dev)
+    _opt(dh_last, "dh_last", (n, W), torch.float32, dev)
+    _need(ckpt, "ckpt", (rglru_ckpt_elems(shape),), torch.float32, dev)
+    dx = torch.empty_like(x)
+    dgate_x = torch.empty_like(x)
+    dgate_a = torch.empty_like(x)
+    dlam = torch.empty((W,), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((n, W), dtype=torch.float32, device=dev) if want_dh0 else None
+    ws = workspace if workspace is not None else default_workspace(dev)
+    buf = ws.get(rglru_varlen_workspace_bytes(shape, n))
+    st = lib.rglru_bwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), n, _ptr(x), _ptr(gate_x), _ptr(gate_a),
+                              _ptr(lam), _ptr(reset), _ptr(h0), _ptr(ckpt), _ptr(dh), _ptr(dh_last), _ptr(dx),
+                              _ptr(dgate_x), _ptr(dgate_a), _ptr(dlam), _ptr(dh0), _ptr(buf), buf.numel(),
+                              _stream(dev))
+    _lib.check(st, "rglru_bwd_varlen")
     return dx, dgate_x, dgate_a, dlam, dh0
 
 

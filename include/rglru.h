@@ -46,8 +46,9 @@
  *    a 32-bit sticky error word. Bit 0 is set if a wait for another
  *    workgroup's published prefix (the look-back across tiles) exceeded its
  *    spin limit; bit 1 if a wait between the waves of one workgroup (on a
- *    flag in LDS) exceeded its spin limit. Either makes the outputs of that
- *    call invalid, and neither can happen while every launched workgroup
+ *    flag in LDS) exceeded its spin limit; bit 2 if the segment offsets of a
+ *    packed-sequence call were invalid. Any of them makes the outputs of that
+ *    call invalid; bits 0 and 1 cannot happen while every launched workgroup
  *    makes progress. The library never clears the word; the caller reads it
  *    (after the call has completed) to check, and zero-fills the workspace to
  *    clear it.
@@ -200,6 +201,47 @@ rglru_status_t rglru_blockdiag_gate_proj_bwd(int64_t tokens, int64_t width, int6
                                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status. Never NULL. */
+/* Packed variable-length sequences (the cu_seqlens convention of the
+ * linear-attention reference oracles, recurrent_delta_rule_reference and
+ * chunk_gdn_reference: offsets into one packed row, per-sequence initial and
+ * final states, gradients through the initial states). n_seqs sequences lie end to end in one row of T tokens, sequence s
+ * holding tokens [cu_seqlens[s], cu_seqlens[s+1]). Each sequence is computed
+ * exactly as its own batch row would be: its first token starts from h0[s]
+ * (zero if h0 is NULL) with the ordinary write, its last token's float32
+ * state is h_last[s]; reset tokens inside a sequence keep their meaning (a
+ * reset on a sequence's first token ignores h0[s]). A sequence with no
+ * tokens has h_last[s] = h0[s] and dh0[s] = dh_last[s].
+ *
+ *   shape       : batch = 1, length = T >= 1 (all tokens), width, io_dtype,
+ *                 chunk, c as for rglru_fwd.
+ *   cu_seqlens  : [n_seqs + 1] int32, device, 0 = cu[0] <= cu[1] <= ... <=
+ *                 cu[n_seqs] = T. Not checked on the host (that would need a
+ *                 synchronisation); invalid offsets set bit 2 of the
+ *                 workspace error word and give unspecified (but in-bounds)
+ *                 results.
+ *   n_seqs      : 1 <= n_seqs < 2^30.
+ *   x, gate_x, gate_a, h, dh, dx, dgate_x, dgate_a : [T, W] io.
+ *   reset       : [T] uint8 or NULL.
+ *   h0, h_last, dh_last, dh0 : [n_seqs, W] float32 or NULL.
+ *   ckpt        : rglru_ckpt_elems() of the shape, as for rglru_fwd.
+ *   workspace   : rglru_varlen_workspace_bytes() bytes (serves both
+ *                 directions), zero-filled before its first use, as for
+ *                 rglru_fwd; it also holds the per-token segment words,
+ *                 rebuilt by every call.
+ * The backward takes h0 again (segment starts inside the row need it). */
+size_t rglru_varlen_workspace_bytes(const rglru_shape_t* shape, int64_t n_seqs);
+rglru_status_t rglru_fwd_varlen(const rglru_shape_t* shape, const int32_t* cu_seqlens, int64_t n_seqs,
+                                const void* x, const void* gate_x, const void* gate_a,
+                                const float* lambda, const uint8_t* reset, const float* h0,
+                                void* h, float* h_last, float* ckpt,
+                                void* workspace, size_t workspace_bytes, void* stream);
+rglru_status_t rglru_bwd_varlen(const rglru_shape_t* shape, const int32_t* cu_seqlens, int64_t n_seqs,
+                                const void* x, const void* gate_x, const void* gate_a,
+                                const float* lambda, const uint8_t* reset, const float* h0,
+                                const float* ckpt, const void* dh, const float* dh_last,
+                                void* dx, void* dgate_x, void* dgate_a, float* dlambda, float* dh0,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Forward scan without a workspace argument and without any allocation, for
  * callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc. Same arguments,

@@ -23,7 +23,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids inside a seed sequence
-T_X, T_GX, T_GA, T_LAM, T_DH, T_H0, T_RESET, T_WX, T_WA, T_DHLAST = range(10)
+T_X, T_GX, T_GA, T_LAM, T_DH, T_H0, T_RESET, T_WX, T_WA, T_DHLAST, T_SEQLEN = range(11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -206,3 +206,48 @@ def make_inputs(wl: Workload, variant: int = 0, with_dh_last: bool = False,
         inp.bx = store(np.zeros(W), "bf16")
         inp.ba = store(np.zeros(W), "bf16")
     return inp
+
+
+# ---------------------------------------------------------------- packed sequences
+
+@dataclasses.dataclass
+class VarlenInputs:
+    """Packed sequences: [T, W] tensors, offsets cu [n + 1], per-sequence states [n, W]."""
+    io: str
+    cu: np.ndarray                  # int32 [n + 1]
+    x: Stored
+    gx: Stored
+    ga: Stored
+    lam: np.ndarray                 # float32 [W]
+    dh: Stored
+    reset: Optional[np.ndarray]     # uint8 [T] or None
+    h0: Optional[np.ndarray]        # float32 [n, W] or None
+    dh_last: Optional[np.ndarray]   # float32 [n, W] or None
+
+
+def seq_lengths(n, mean, variant=0, empty_p=0.0) -> np.ndarray:
+    """n sequence lengths, Geometric(1/mean) (support 1, 2, ...), each made empty with probability empty_p."""
+    g = generator(90, T_SEQLEN, variant)
+    lens = g.geometric(1.0 / mean, size=n).astype(np.int64)
+    lens[g.random(n) < empty_p] = 0
+    return lens
+
+
+def make_varlen_inputs(lengths, width, io, variant=0, decay=(0.9, 0.999), reset_mean=None,
+                       with_h0=True, with_dh_last=True) -> VarlenInputs:
+    """Inputs of packed sequences with the given lengths (total at least 1 token)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, n, W = int(cu[-1]), lengths.size, width
+    wid = 91
+    x = normal(wid, T_X, (T, W), io, variant)
+    gx = normal(wid, T_GX, (T, W), io, variant)
+    ga = normal(wid, T_GA, (T, W), io, variant)
+    dh = normal(wid, T_DH, (T, W), io, variant)
+    lam = decay_param(wid, W, decay[0], decay[1], variant)
+    reset = None
+    if reset_mean is not None:
+        reset = reset_flags(wid, 1, T, reset_mean, variant)[0]
+    h0 = generator(wid, T_H0, variant).standard_normal((n, W)).astype(np.float32) if with_h0 else None
+    dhl = generator(wid, T_DHLAST, variant).standard_normal((n, W)).astype(np.float32) if with_dh_last else None
+    return VarlenInputs(io, cu, x, gx, ga, lam, dh, reset, h0, dhl)
