@@ -103,6 +103,87 @@ def cpu_baseline(wl, inp, seconds_target=12.0):
     }
 
 
+DECODE_SHAPES = ((1, 1, 2048), (4, 1, 2048), (16, 1, 4096), (4, 8, 2048))
+
+
+def decode(args):
+    """Decode-step latency: B rows, L = 1 (or up to 8) new tokens, h0 in, h_last out.
+
+    Each shape runs `steps` calls of rglru_fwd_scratch (no workspace, nothing
+    allocated) back to back, first eagerly (host launch rate included), then
+    captured once into a HIP graph and replayed, which leaves the GPU time per
+    step; the graph's result is checked bitwise against the eager call.
+    """
+    import numpy as np
+    import torch
+
+    import gated_linear_recurrence_amd as glr
+    import synth
+
+    glr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps = max(args.steps, 20)
+    rows = []
+    for B, L, W in DECODE_SHAPES:
+        wl = synth.dataclasses.replace(synth.WORKLOADS[2].resized(batch=B, length=L, width=W), doc_mean=None)
+        inp = synth.make_inputs(wl)
+
+        def io(st):
+            return torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        x, gx, ga = io(inp.x), io(inp.gx), io(inp.ga)
+        lam = torch.from_numpy(inp.lam).to(dev)
+        h0 = torch.from_numpy(inp.h0).to(dev)
+        h = torch.empty_like(x)
+        h_last = torch.empty((B, W), dtype=torch.float32, device=dev)
+
+        def call():
+            glr.rglru_fwd_scratch(x, gx, ga, lam, None, h0, h=h, h_last=h_last)
+
+        for _ in range(args.warmup + 5):
+            call()
+        torch.cuda.synchronize()
+        ref_h, ref_hl = h.clone(), h_last.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / steps
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                for _ in range(steps):
+                    call()
+        torch.cuda.synchronize()
+        h.zero_()
+        h_last.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(h, ref_h) and torch.equal(h_last, ref_hl)):
+            print(f"graph replay differs from the eager call at B={B} L={L} W={W}", file=sys.stderr)
+            sys.exit(3)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / steps
+        if not (torch.equal(h, ref_h) and torch.equal(h_last, ref_hl)):
+            print(f"second graph replay differs at B={B} L={L} W={W}", file=sys.stderr)
+            sys.exit(3)
+        del graph
+        rows.append({"batch": B, "length": L, "width": W, "eager_us_per_step": round(eager_us, 2),
+                     "graph_us_per_step": round(graph_us, 2),
+                     "bytes_per_step": B * L * W * 2 * 4 + B * W * 4 * 2})
+    print(json.dumps({"metric": "RG-LRU decode step latency (graph replay)", "unit": "us",
+                      "higher_is_better": False, "n_gpus": 1, "steps": steps, "dtype": "bf16",
+                      "data": "synthetic", "entry_point": "rglru_fwd_scratch", "shapes": rows}), flush=True)
+
+
 def main():
     """Fields: metric, value (fwd+bwd ms per step), unit, n_gpus, steps, warmup, ms_per_step,
     higher_is_better, scaling, vs_baseline, dtype, data, config, fwd_ms, bwd_ms, elements_per_s,
@@ -118,7 +199,17 @@ def main():
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a known-size "
                          "reference for hardware traffic counters)")
+    ap.add_argument("--decode", action="store_true",
+                    help="instead: decode-step latency (L = 1, h0 in, h_last out) through the "
+                         "allocation-free forward, eager and replayed from a HIP graph")
     args = ap.parse_args()
+
+    if args.decode:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        decode(args)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
