@@ -113,6 +113,7 @@ def traffic_json(fetch_db: str, write_db: str, calib_mib: float, workload: str, 
 
 
 N_SIMD = 1024    # 256 CUs x 4 SIMDs
+N_XCD = 8
 
 
 def counters(trace_db: str, pmc_dbs) -> str:
@@ -134,22 +135,28 @@ def counters(trace_db: str, pmc_dbs) -> str:
         row = [f"`{_short(n)}`", f"{d / 1e3:.2f}" if d else "-"]
         row += [f"{vals[n].get(k, float('nan')):.4g}" for k in cols]
         out.append("| " + " | ".join(row) + " |")
-    out += ["", "| kernel | VALU busy | wave cycles waiting on a dependency | LDS bank-conflict cycles "
-            "per LDS instruction | SQ busy / GPU busy cycles | TA stalled by TC |", "|---|---|---|---|---|---|"]
+    out += ["", "| kernel | kernel cycles per XCD | VALU busy per SIMD | VALU instructions per SIMD | "
+            "wave time waiting (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) | of it on LDS (SQ_WAIT_INST_LDS) | "
+            "LDS bank-conflict cycles per LDS instruction |", "|---|---|---|---|---|---|---|"]
 
-    def ratio(a, b):
-        return f"{a / b:.3f}" if a is not None and b else "-"
+    def ratio(a, b, fmt="{:.3f}"):
+        return fmt.format(a / b) if a is not None and b else "-"
 
     for n in names:
         v = vals[n]
         gui = v.get("GRBM_GUI_ACTIVE")
+        xcd = gui / N_XCD if gui else None
         valu = v.get("SQ_ACTIVE_INST_VALU")
-        # VALU busy as rocprof has long defined it: 4 * SQ_ACTIVE_INST_VALU / SIMDs / GPU-busy cycles
-        vb = ratio(4 * valu / N_SIMD if valu is not None else None, gui)
-        out.append(f"| `{_short(n)}` | {vb} | {ratio(v.get('SQ_WAIT_INST_ANY'), v.get('SQ_WAVE_CYCLES'))} | "
-                   f"{ratio(v.get('SQ_LDS_BANK_CONFLICT'), v.get('SQ_INSTS_LDS'))} | "
-                   f"{ratio(v.get('SQ_BUSY_CYCLES'), gui)} | "
-                   f"{ratio(v.get('TA_ADDR_STALLED_BY_TC_CYCLES'), v.get('TA_BUSY'))} |")
+        # GRBM_GUI_ACTIVE sums the 8 XCDs; SQ_ACTIVE_INST_VALU counts in
+        # 4-cycle units, summed over every wave
+        busy = ratio(4 * valu / N_SIMD if valu is not None else None, xcd)
+        insts = v.get("SQ_INSTS_VALU")
+        cyc = f"{xcd:.0f}" if xcd else "-"
+        per_simd = f"{insts / N_SIMD:.0f}" if insts is not None else "-"
+        out.append(f"| `{_short(n)}` | {cyc} | {busy} | {per_simd} | "
+                   f"{ratio(v.get('SQ_WAIT_INST_ANY'), v.get('SQ_WAVE_CYCLES'))} | "
+                   f"{ratio(v.get('SQ_WAIT_INST_LDS'), v.get('SQ_WAVE_CYCLES'))} | "
+                   f"{ratio(v.get('SQ_LDS_BANK_CONFLICT'), v.get('SQ_INSTS_LDS'))} |")
     return "\n".join(out)
 
 
