@@ -7,6 +7,7 @@ from .ops import (  # noqa: F401
     check_errors,
     make_shape,
     rglru,
+    rglru_blockdiag_fused_fwd,
     rglru_blockdiag_gate_proj_bwd,
     rglru_blockdiag_gate_proj_fwd,
     rglru_bwd,

@@ -50,6 +50,8 @@ _SIGNATURES = {
                                               _vp, _vp, _vp, _vp, _vp, _vp, c_size_t, _vp]),
     "rglru_fwd_scratch": (c_int, [POINTER(rglru_shape_t), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "rglru_varlen_workspace_bytes": (c_size_t, [POINTER(rglru_shape_t), c_int64]),
+    "rglru_blockdiag_fused_fwd_workspace_bytes": (c_size_t, [POINTER(rglru_shape_t)]),
+    "rglru_blockdiag_fused_fwd": (c_int, [POINTER(rglru_shape_t)] + [_vp] * 14 + [c_size_t, _vp]),
     "rglru_fwd_varlen": (c_int, [POINTER(rglru_shape_t), _vp, c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, c_size_t, _vp]),
     "rglru_bwd_varlen": (c_int, [POINTER(rglru_shape_t), _vp, c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,

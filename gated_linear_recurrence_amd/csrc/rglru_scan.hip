@@ -87,6 +87,8 @@ struct BF16 {
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 template <int BYTES> struct Raw;
 template <> struct Raw<2> { using T = uint16_t; };
@@ -400,6 +402,12 @@ struct FwdArgs {
   const uint32_t* seg;
   const float* h0s;
   float* h_last_s;
+  // gate projections computed inside the forward (256-wide blocks): the
+  // transposed weights [nb][256 out][256 in] bf16 of each gate, the biases
+  // [W] bf16 (or nullptr), and where the logits also go [B*L, W] (or nullptr)
+  const uint16_t* wt[2];
+  const uint16_t* pbias[2];
+  uint16_t* gout[2];
   Header* hdr;
   u64* slot_a;
   u64* slot_b;
@@ -497,7 +505,7 @@ constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 // row in LDS is then 64 * sizeof(io) bytes. Otherwise each instruction fills
 // one row with 2 or 4 bytes per lane, each lane's value zero-extended into its
 // own 4-byte slot (rows of 256 bytes).
-template <typename IO, int NW, int TS, bool WIDE, bool PACKED>
+template <typename IO, int NW, int TS, bool WIDE, bool PACKED, bool FUSED>
 __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   using elem = typename IO::elem;
   using io = Io<IO, 1>;
@@ -515,8 +523,14 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   static_assert(TS <= 16 && NW <= 32, "a wave's cut and end flags share one mask word; the waves' flags fit one");
   static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
   static_assert(NFL % 64 == 0 && NFL <= 128, "reset flags: at most two instructions");
+  static_assert(!FUSED || (std::is_same<IO, BF16>::value && WIDE && T % 16 == 0 && !PACKED),
+                "the fused projection runs bf16 tiles of 16-row blocks");
 
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][3][T][ROWB];
+  // fused projection: the tile's rows of x across its whole 256-wide block
+  // (16-byte granules XOR-swizzled by row, so the MFMA operand reads of 16
+  // rows fall on distinct banks)
+  __shared__ __attribute__((aligned(16))) uint16_t s_xb[FUSED ? 2 : 1][FUSED ? T : 1][256];
   __shared__ unsigned s_rflag[2][NFL];
   __shared__ uint32_t s_seg[2][NFL];  // segment words (packed sequences)
   __shared__ uint32_t s_endseg[3][NW][TS];   // a wave's segment ends, per ring slot
@@ -583,6 +597,58 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
     const unsigned q = static_cast<unsigned>(v) + m;
     return q < p.n_tiles ? q : p.n_tiles;
   };
+  // Both gate projections of tile t from its block rows in s_xb[jb], into the
+  // gate_x and gate_a rows of raw buffer jb (bf16, rounded once) and, when
+  // asked, to the logit outputs: gate_g = x[:, blk] w_g[blk] + b_g[blk] as
+  // D = w_g^T x^T on v_mfma_f32_16x16x32_bf16 (A: lane l holds output l%16,
+  // inputs (l/16)*8 .. +7 of a 32-input step; B: token l%16, the same inputs;
+  // D: token l%16, outputs (l/16)*4 .. +3), accumulators started at the bias
+  // and the eight input steps in order, as the projection kernel does, so
+  // the logits are bitwise those of rglru_blockdiag_gate_proj_fwd.
+  auto project = [=](int jb, const Tile& t, long long lim) {
+    if constexpr (FUSED) {
+      const int kb = t.strip >> 2;
+      const int sub = t.strip & 3;
+      const int valid = lim + 1 < T ? static_cast<int>(lim + 1) : T;
+      const int lr = lane & 15;
+      const int lg = lane >> 4;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint16_t* wt = p.wt[g] + (static_cast<long long>(kb) * 256 + sub * 64) * 256;
+        const uint16_t* bias = p.pbias[g];
+        uint16_t* gout = p.gout[g];
+#pragma unroll 1
+        for (int ob = 0; ob < 4; ++ob) {
+          bf16x8 a[8];
+          const uint16_t* wrow = wt + (ob * 16 + lr) * 256 + lg * 8;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) a[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wrow + ks * 32));
+          const int o = kb * 256 + sub * 64 + ob * 16 + lg * 4;
+          f32x4 b0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) b0[q] = bias != nullptr ? bf16_bits_to_f32(bias[o + q]) : 0.0f;
+#pragma unroll 1
+          for (int tb = 0; tb < T / 16; ++tb) {
+            const int tr = tb * 16 + lr;
+            f32x4 acc = b0;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+              const int gr = ks * 4 + lg;
+              const u32x4 bv = *reinterpret_cast<const u32x4*>(&s_xb[jb][tr][(gr ^ (tr & 15)) * 8]);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            }
+            uint2 v;
+            v.x = f32x2_to_bf16x2(acc[0], acc[1]);
+            v.y = f32x2_to_bf16x2(acc[2], acc[3]);
+            *reinterpret_cast<uint2*>(&s_raw[jb][1 + g][tr][(ob * 16 + lg * 4) * 2]) = v;
+            if (gout != nullptr && tr < valid) {
+              *reinterpret_cast<uint2*>(gout + (t.rowbase + t.t0 + tr) * W + o) = v;
+            }
+          }
+        }
+      }
+    }
+  };
 
   if (wave >= LOAD0) {
     // ------------------------------------------------------------ load waves
@@ -631,7 +697,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
           // tile's rows under 2 GiB)
           const unsigned step = static_cast<unsigned>(RPI) * static_cast<unsigned>(row_bytes);
 #pragma unroll
-          for (int q = 0; q < 3; ++q) {
+          for (int q = 0; q < (FUSED ? 1 : 3); ++q) {
             gbyte* base = uniform_gptr(src[q] + tile_off);
             unsigned off = static_cast<unsigned>(r) * static_cast<unsigned>(row_bytes) + col;
             unsigned char* dst = &s_raw[j][q][0][0];
@@ -644,7 +710,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
           }
         } else {
 #pragma unroll
-          for (int q = 0; q < 3; ++q) {
+          for (int q = 0; q < (FUSED ? 1 : 3); ++q) {
             gbyte* base = uniform_gptr(src[q] + tile_off);
             for (int g = 0; g < T / RPI; ++g) {
               const long long row = g * RPI + r;
@@ -681,11 +747,30 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
           __builtin_amdgcn_global_load_lds(const_cast<uint32_t*>(p.seg) + t.rowbase + tk, &s_seg[j][h * 64], 4, 0, 0);
         }
       }
+      if constexpr (FUSED) {
+        // the tile's rows across the whole block: 2 rows of 512 bytes per
+        // instruction, lane l at row l / 32, LDS granule l % 32, which holds
+        // source granule (l % 32) ^ (row % 16)
+        const int kb = t.strip >> 2;
+        gbyte* base = uniform_gptr(static_cast<const unsigned char*>(p.x) + (t.rowbase + t.t0) * row_bytes +
+                                   static_cast<long long>(kb) * 512);
+        const int rr = lane >> 5;
+        const int gq = lane & 31;
+#pragma unroll 4
+        for (int g = 0; g < T / 2; ++g) {
+          const long long row = 2 * g + rr;
+          const long long rw = row < lim ? row : lim;
+          const unsigned off = static_cast<unsigned>(rw) * static_cast<unsigned>(row_bytes) +
+                               static_cast<unsigned>((gq ^ (static_cast<int>(row) & 15)) * 16);
+          lds_dma16(base + off, &s_xb[j][2 * g][0]);
+        }
+      }
       // the next two tickets, two iterations ahead (load wave 0 draws them all,
       // so a workgroup's tiles come in ticket order)
       u64 nxt = 0;
       if (j == 0 && lane == 0) nxt = atomicAdd(&p.hdr->counter, 2ull);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if constexpr (FUSED) project(j, t, lim);
       {
         float cs = 0.0f, k2 = 0.0f;
         if (t.active) channel_consts(lam, p.c, cs, k2);
@@ -2060,12 +2145,43 @@ rglru_status_t launch_fwd(FwdArgs a, hipStream_t stream) {
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
   // packed sequences run their own instantiation, so the plain kernel carries
   // none of their registers
-  auto kernel = a.seg != nullptr ? fwd_kernel<IO, NW, TS, WIDE, true> : fwd_kernel<IO, NW, TS, WIDE, false>;
+  auto kernel = a.seg != nullptr ? fwd_kernel<IO, NW, TS, WIDE, true, false> : fwd_kernel<IO, NW, TS, WIDE, false, false>;
   constexpr int threads = (NW + 4) * 64;
   const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
   if (grid == 0) return RGLRU_ERR_HIP;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
   return launch_status();
+}
+
+// The forward with both gate projections computed inside it: bf16, 64-step
+// tiles of 8 data waves (the projection's block rows of a 128-step tile would
+// not fit LDS twice).
+rglru_status_t launch_fused(FwdArgs a, hipStream_t stream) {
+  constexpr int NW = 8, TS = 8, T = NW * TS;
+  a.n_strips = static_cast<int>(ceil_div(a.W, 64));
+  a.n_chunks = static_cast<int>(ceil_div(a.L, T));
+  a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
+  auto kernel = fwd_kernel<BF16, NW, TS, true, false, true>;
+  constexpr int threads = (NW + 4) * 64;
+  const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
+  if (grid == 0) return RGLRU_ERR_HIP;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
+  return launch_status();
+}
+
+// Both gates' weights [nb][256 in][256 out] -> [nb][256 out][256 in], 32 x 32
+// tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_w_kernel(const uint16_t* w0, const uint16_t* w1, uint16_t* t0,
+                                                         uint16_t* t1) {
+  __shared__ uint16_t tile[32][33];
+  const int g = blockIdx.z & 1;
+  const long long kb = blockIdx.z >> 1;
+  const uint16_t* src = (g ? w1 : w0) + kb * 65536;
+  uint16_t* dst = (g ? t1 : t0) + kb * 65536;
+  const int i0 = blockIdx.y * 32, o0 = blockIdx.x * 32;
+  for (int r = threadIdx.y; r < 32; r += 8) tile[r][threadIdx.x] = src[(i0 + r) * 256 + o0 + threadIdx.x];
+  __syncthreads();
+  for (int r = threadIdx.y; r < 32; r += 8) dst[(o0 + r) * 256 + i0 + threadIdx.x] = tile[threadIdx.x][r];
 }
 
 // Forward tile length for a requested chunk: at most 128 steps where 2-byte
@@ -2263,6 +2379,9 @@ rglru_status_t fwd_call(const rglru_shape_t* s, const void* x, const void* gate_
   a.seg = pk.seg;
   a.h0s = pk.h0s;
   a.h_last_s = pk.h_last_s;
+  a.wt[0] = a.wt[1] = nullptr;
+  a.pbias[0] = a.pbias[1] = nullptr;
+  a.gout[0] = a.gout[1] = nullptr;
   a.hdr = sl.hdr;
   a.slot_a = sl.a;
   a.slot_b = sl.b;
@@ -2494,6 +2613,70 @@ rglru_status_t rglru_bwd_varlen(const rglru_shape_t* s, const int32_t* cu_seqlen
   hipLaunchKernelGGL(varlen_empty_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, st,
                      cu_seqlens, static_cast<long long>(n_seqs), static_cast<int>(s->width), dh_last, dh0);
   return launch_status();
+}
+
+size_t rglru_blockdiag_fused_fwd_workspace_bytes(const rglru_shape_t* s) {
+  if (!shape_ok(s) || s->io_dtype != RGLRU_IO_BF16 || s->width % 256 != 0) return 0;
+  return fwd_ws(s) + round_up(static_cast<size_t>(s->width) * 256 * 2 * 2, 256);
+}
+
+rglru_status_t rglru_blockdiag_fused_fwd(const rglru_shape_t* s, const void* x, const void* w_x, const void* b_x,
+                                         const void* w_a, const void* b_a, const float* lambda, const uint8_t* reset,
+                                         const float* h0, void* h, float* h_last, float* ckpt, void* gate_x,
+                                         void* gate_a, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape_ok(s)) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (!x || !w_x || !w_a || !lambda || !h || !workspace) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (s->io_dtype != RGLRU_IO_BF16 || s->width % 256 != 0 || (s->chunk != 0 && s->chunk != 64) ||
+      64LL * s->width * 2 >= (1LL << 31)) {
+    return RGLRU_ERR_UNSUPPORTED;
+  }
+  const Geometry g = geometry(s);
+  if (!aligned_to(x, 16) || !aligned_to(h, 16) || !aligned_to(w_x, 2) || !aligned_to(w_a, 2) ||
+      !aligned_to(b_x, 2) || !aligned_to(b_a, 2) || !aligned_to(gate_x, 8) || !aligned_to(gate_a, 8) ||
+      !f32_aligned(lambda) || !f32_aligned(h0) || !f32_aligned(h_last) || !f32_aligned(ckpt) ||
+      !aligned_to(workspace, 256)) {
+    return RGLRU_ERR_MISALIGNED;
+  }
+  if (workspace_bytes < rglru_blockdiag_fused_fwd_workspace_bytes(s)) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long nb = s->width / 256;
+  uint16_t* wt0 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + fwd_ws(s));
+  uint16_t* wt1 = wt0 + nb * 65536;
+  hipLaunchKernelGGL(transpose_w_kernel, dim3(8, 8, static_cast<unsigned>(2 * nb)), dim3(32, 8), 0, st,
+                     static_cast<const uint16_t*>(w_x), static_cast<const uint16_t*>(w_a), wt0, wt1);
+  rglru_status_t r = launch_status();
+  if (r != RGLRU_OK) return r;
+  const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_f));
+  FwdArgs a;
+  a.x = x;
+  a.gx = nullptr;
+  a.ga = nullptr;
+  a.lam = lambda;
+  a.reset = reset;
+  a.h0 = h0;
+  a.h = h;
+  a.h_last = h_last;
+  a.ckpt = ckpt;
+  a.seg = nullptr;
+  a.h0s = nullptr;
+  a.h_last_s = nullptr;
+  a.wt[0] = wt0;
+  a.wt[1] = wt1;
+  a.pbias[0] = static_cast<const uint16_t*>(b_x);
+  a.pbias[1] = static_cast<const uint16_t*>(b_a);
+  a.gout[0] = static_cast<uint16_t*>(gate_x);
+  a.gout[1] = static_cast<uint16_t*>(gate_a);
+  a.hdr = sl.hdr;
+  a.slot_a = sl.a;
+  a.slot_b = sl.b;
+  a.slot_h = sl.h;
+  a.L = s->length;
+  a.n_ckpt = g.n_ckpt;
+  a.B = static_cast<int>(s->batch);
+  a.W = static_cast<int>(s->width);
+  a.c = s->c;
+  a.h_wide = true;
+  return launch_fused(a, st);
 }
 
 const char* rglru_status_string(rglru_status_t status) {

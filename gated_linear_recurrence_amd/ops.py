@@ -355,6 +355,53 @@ def rglru_blockdiag_gate_proj_fwd(x: torch.Tensor, w_x: torch.Tensor, b_x: Optio
     return gate_x, gate_a
 
 
+def rglru_blockdiag_fused_fwd(x: torch.Tensor, w_x: torch.Tensor, b_x: Optional[torch.Tensor], w_a: torch.Tensor,
+                              b_a: Optional[torch.Tensor], lam: torch.Tensor, reset: Optional[torch.Tensor] = None,
+                              h0: Optional[torch.Tensor] = None, *, c: float = 8.0, training: bool = True,
+                              want_h_last: bool = True, want_gates: bool = False,
+                              h: Optional[torch.Tensor] = None, h_last: Optional[torch.Tensor] = None,
+                              ckpt: Optional[torch.Tensor] = None, gate_x: Optional[torch.Tensor] = None,
+                              gate_a: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None):
+    """Both gate projections and the forward scan in one call (x [B, L, W] bf16, W a multiple of 256).
+    Returns (h, h_last or None, ckpt or None, gate_x or None, gate_a or None)."""
+    lib = _lib.load()
+    dev = x.device
+    B, L, W = x.shape
+    nb = W // 256
+    _need(x, "x", (B, L, W), torch.bfloat16, dev)
+    _need(w_x, "w_x", (nb, 256, 256), torch.bfloat16, dev)
+    _need(w_a, "w_a", (nb, 256, 256), torch.bfloat16, dev)
+    _opt(b_x, "b_x", (W,), torch.bfloat16, dev)
+    _opt(b_a, "b_a", (W,), torch.bfloat16, dev)
+    _need(lam, "lambda", (W,), torch.float32, dev)
+    _opt(reset, "reset", (B, L), torch.uint8, dev)
+    _opt(h0, "h0", (B, W), torch.float32, dev)
+    shape = make_shape(B, L, W, torch.bfloat16, 0, c)
+    if h is None:
+        h = torch.empty((B, L, W), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", (B, L, W), torch.bfloat16, dev)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((B, W), dtype=torch.float32, device=dev)
+    _opt(h_last, "h_last", (B, W), torch.float32, dev)
+    if ckpt is None and training:
+        ckpt = torch.empty(rglru_ckpt_elems(shape), dtype=torch.float32, device=dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", (rglru_ckpt_elems(shape),), torch.float32, dev)
+    if want_gates:
+        gate_x = torch.empty_like(x) if gate_x is None else gate_x
+        gate_a = torch.empty_like(x) if gate_a is None else gate_a
+    _opt(gate_x, "gate_x", (B, L, W), torch.bfloat16, dev)
+    _opt(gate_a, "gate_a", (B, L, W), torch.bfloat16, dev)
+    ws = workspace if workspace is not None else default_workspace(dev)
+    nbytes = int(lib.rglru_blockdiag_fused_fwd_workspace_bytes(ctypes.byref(shape)))
+    buf = ws.get(max(nbytes, rglru_workspace_bytes(shape)))
+    st = lib.rglru_blockdiag_fused_fwd(ctypes.byref(shape), _ptr(x), _ptr(w_x), _ptr(b_x), _ptr(w_a), _ptr(b_a),
+                                       _ptr(lam), _ptr(reset), _ptr(h0), _ptr(h), _ptr(h_last), _ptr(ckpt),
+                                       _ptr(gate_x), _ptr(gate_a), _ptr(buf), buf.numel(), _stream(dev))
+    _lib.check(st, "rglru_blockdiag_fused_fwd")
+    return h, h_last, ckpt, gate_x, gate_a
+
+
 def rglru_blockdiag_gate_proj_bwd(x: torch.Tensor, w_x: torch.Tensor, w_a: torch.Tensor,
                                   dgate_x: torch.Tensor, dgate_a: torch.Tensor,
                                   dx_in: Optional[torch.Tensor] = None, *, want_db: bool = True,

@@ -201,6 +201,33 @@ rglru_status_t rglru_blockdiag_gate_proj_bwd(int64_t tokens, int64_t width, int6
                                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status. Never NULL. */
+/* Forward scan with both block-diagonal gate projections computed inside it
+ * (the step the Fattori comparison page says prior art leaves to the caller:
+ * two BlockDiagonalLinear projections of x ahead of the fused operator), so
+ * the logits need not pass through HBM. The result is bitwise that of
+ * rglru_blockdiag_gate_proj_fwd followed by rglru_fwd with chunk 64 on its
+ * logits; the logits themselves are written too when gate_x / gate_a are
+ * given (training: rglru_bwd and rglru_blockdiag_gate_proj_bwd take them).
+ *
+ *   shape          : io_dtype bf16, width a multiple of 256, chunk 0 or 64
+ *                    (the call runs 64-step tiles); anything else is
+ *                    RGLRU_ERR_UNSUPPORTED.
+ *   x              : [B, L, W] bf16, 16-byte aligned.
+ *   w_x, w_a       : [W/256, 256, 256] bf16 weights, read as [block, in, out].
+ *   b_x, b_a       : [W] bf16 or NULL (zero bias).
+ *   lambda, reset, h0, h, h_last, ckpt : as for rglru_fwd (h 16-byte aligned).
+ *   gate_x, gate_a : [B, L, W] bf16 (8-byte aligned) or NULL.
+ *   workspace      : rglru_blockdiag_fused_fwd_workspace_bytes() bytes,
+ *                    zero-filled before its first use, as for rglru_fwd; it
+ *                    also holds a transposed copy of both weights, rebuilt by
+ *                    every call. */
+size_t rglru_blockdiag_fused_fwd_workspace_bytes(const rglru_shape_t* shape);
+rglru_status_t rglru_blockdiag_fused_fwd(const rglru_shape_t* shape, const void* x,
+                                         const void* w_x, const void* b_x, const void* w_a, const void* b_a,
+                                         const float* lambda, const uint8_t* reset, const float* h0,
+                                         void* h, float* h_last, float* ckpt, void* gate_x, void* gate_a,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Packed variable-length sequences (the cu_seqlens convention of the
  * linear-attention reference oracles, recurrent_delta_rule_reference and
  * chunk_gdn_reference: offsets into one packed row, per-sequence initial and
