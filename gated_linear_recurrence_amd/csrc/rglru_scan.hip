@@ -464,6 +464,55 @@ __device__ __forceinline__ void lds_wait(const int* f, int v, int* abort, Header
 // s_waitcnt immediates (gfx9 layout: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 
+// Fused projection helpers. A pass works on one gate and two 16-output tiles
+// (outputs sub*64 + op*32 + u*16 + lane%16 of block kb): its weights are MFMA
+// A operands, inputs ks*32 + (lane/16)*8 .. +7 of each of the 8 input steps,
+// read from the transposed copy [block][out][in].
+__device__ __forceinline__ bf16x8 fused_w_frag(const uint16_t* wt, int kb, int sub, int op, int u, int ks, int lane) {
+  const uint16_t* w = wt + (static_cast<long long>(kb) * 256 + sub * 64 + op * 32 + u * 16 + (lane & 15)) * 256 +
+                      ks * 32 + (lane >> 4) * 8;
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(w));
+}
+
+// The bias of a lane's accumulator rows (4 consecutive outputs per output
+// tile), as raw bf16; zeros without a bias.
+struct FusedBias {
+  uint32_t v[2][2];   // [output tile][pair]: outputs 2k (low half) and 2k + 1
+};
+__device__ __forceinline__ FusedBias fused_bias(const uint16_t* bias, int o) {
+  FusedBias r;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      r.v[u][k] = bias != nullptr ? (static_cast<uint32_t>(bias[o + u * 16 + 2 * k]) |
+                                     (static_cast<uint32_t>(bias[o + u * 16 + 2 * k + 1]) << 16))
+                                  : 0u;
+    }
+  }
+  return r;
+}
+
+// LDS reads of the token operands, issued as inline assembly so that they
+// stay the written distance ahead of their MFMAs (compiled reads are placed
+// one step ahead). fused_lds_wait waits until at most N LDS operations of the
+// wave are outstanding (they complete in order) and ties the two values read,
+// so that no use of them moves above it.
+__device__ __forceinline__ uint32_t lds_off(const void* ptr) {
+  typedef __attribute__((address_space(3))) const char lds_char;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(ptr)));
+}
+__device__ __forceinline__ u32x4 fused_lds_read16(uint32_t addr) {
+  u32x4 d;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(d) : "v"(addr));
+  return d;
+}
+constexpr int kFusedAhead = 2;   // input steps of token operands read ahead
+template <int N>
+__device__ __forceinline__ void fused_lds_wait(u32x4& x, u32x4& y) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "n"(N));
+}
+
 // Persistent, software-pipelined forward.
 //
 // A tile is one batch row b, a strip of 64 channels (one channel per lane) and
@@ -506,7 +555,7 @@ constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 // one row with 2 or 4 bytes per lane, each lane's value zero-extended into its
 // own 4-byte slot (rows of 256 bytes).
 template <typename IO, int NW, int TS, bool WIDE, bool PACKED, bool FUSED>
-__global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
+__global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArgs p) {
   using elem = typename IO::elem;
   using io = Io<IO, 1>;
   constexpr bool BF = std::is_same<IO, BF16>::value;
@@ -518,7 +567,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   constexpr int K = RGLRU_FWD_LOOKBACK;
   constexpr int RING = 16;
   constexpr int NFL = T < 64 ? 64 : T;     // reset-flag slots per buffer (one instruction fills 64)
-  constexpr int CTRL0 = NW, LOAD0 = NW + 2;
+  constexpr int CTRL0 = NW, LOAD0 = NW + 2, PROJ0 = NW + 4;
   static_assert(TS % kCkpt == 0, "checkpoints fall on wave boundaries, at compile-time steps of a wave");
   static_assert(TS <= 16 && NW <= 32, "a wave's cut and end flags share one mask word; the waves' flags fit one");
   static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
@@ -553,6 +602,8 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   __shared__ int s_maps_in[3];        // data-wave maps reported for iterations of each slot so far
   __shared__ int s_carry_ok[3];       // iteration whose incoming carry slot s holds
   __shared__ int s_prog[NW];          // iteration each data wave is in
+  __shared__ int s_xb_full[2];        // fused: iteration whose block rows s_xb[j] holds
+  __shared__ int s_proj_done[2];      // fused: projection passes finished on buffer j so far
   __shared__ int s_abort;
 
   const int lane = threadIdx.x & 63;
@@ -563,6 +614,8 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   if (threadIdx.x == 0) {
     s_tk_valid = -1;
     s_full[0] = s_full[1] = -1;
+    s_xb_full[0] = s_xb_full[1] = -1;
+    s_proj_done[0] = s_proj_done[1] = 0;
     s_cons[0] = s_cons[1] = 0;
     s_maps_in[0] = s_maps_in[1] = s_maps_in[2] = 0;
     s_carry_ok[0] = s_carry_ok[1] = s_carry_ok[2] = -1;
@@ -605,44 +658,92 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
   // D: token l%16, outputs (l/16)*4 .. +3), accumulators started at the bias
   // and the eight input steps in order, as the projection kernel does, so
   // the logits are bitwise those of rglru_blockdiag_gate_proj_fwd.
-  auto project = [=](int jb, const Tile& t, long long lim) {
+  //
+  // Work of one pass: one gate, two 16-output tiles (weights in registers)
+  // against two 16-token tiles at a time, so four independent accumulator
+  // chains hide the MFMA latency and each token operand read from LDS feeds
+  // two products. A pass's weights come from the pre-transposed copy
+  // ([out][in], L2-resident: every tile of a strip reads the same 64 KiB).
+  auto project_pass = [=](int jb, const Tile& t, long long lim, int g, int op, const bf16x8 (&a)[2][8],
+                          FusedBias bias) {
     if constexpr (FUSED) {
       const int kb = t.strip >> 2;
       const int sub = t.strip & 3;
       const int valid = lim + 1 < T ? static_cast<int>(lim + 1) : T;
       const int lr = lane & 15;
       const int lg = lane >> 4;
+      // (a select, not indexing by g: a dynamic index into the argument
+      // struct's arrays would move the struct to scratch memory)
+      uint16_t* gout = g ? p.gout[1] : p.gout[0];
+      const int o = kb * 256 + sub * 64 + op * 32 + lg * 4;   // output of u = 0, q = 0
+      f32x4 b0[2];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const uint16_t* wt = p.wt[g] + (static_cast<long long>(kb) * 256 + sub * 64) * 256;
-        const uint16_t* bias = p.pbias[g];
-        uint16_t* gout = p.gout[g];
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          b0[u][q] = __uint_as_float((q & 1) ? (bias.v[u][q >> 1] & 0xFFFF0000u) : (bias.v[u][q >> 1] << 16));
+        }
+      }
+      // token operand of input step ks, token tile tb: row tb*16 + lr, source
+      // granule ks*4 + lg, stored at granule (ks*4 + lg) ^ lr
+      // (the swizzle acts on the offset within the buffer, which starts at
+      // xbase)
+      const uint32_t xbase = lds_off(&s_xb[jb][0][0]);
+      const uint32_t xrow = static_cast<uint32_t>(lr * 512 + ((lg ^ lr) << 4));
 #pragma unroll 1
-        for (int ob = 0; ob < 4; ++ob) {
-          bf16x8 a[8];
-          const uint16_t* wrow = wt + (ob * 16 + lr) * 256 + lg * 8;
+      for (int tp = 0; tp < T / 32; ++tp) {
+        f32x4 acc[2][2];   // [token tile][output tile]
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) a[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wrow + ks * 32));
-          const int o = kb * 256 + sub * 64 + ob * 16 + lg * 4;
-          f32x4 b0;
+        for (int v = 0; v < 2; ++v) {
+          acc[v][0] = b0[0];
+          acc[v][1] = b0[1];
+        }
+        const uint32_t x0 = xrow + static_cast<uint32_t>(tp * 32 * 512);
+        u32x4 xv[8][2];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) b0[q] = bias != nullptr ? bf16_bits_to_f32(bias[o + q]) : 0.0f;
-#pragma unroll 1
-          for (int tb = 0; tb < T / 16; ++tb) {
-            const int tr = tb * 16 + lr;
-            f32x4 acc = b0;
+        for (int ks = 0; ks < kFusedAhead; ++ks) {
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-              const int gr = ks * 4 + lg;
-              const u32x4 bv = *reinterpret_cast<const u32x4*>(&s_xb[jb][tr][(gr ^ (tr & 15)) * 8]);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+          for (int v = 0; v < 2; ++v) xv[ks][v] = fused_lds_read16(xbase + ((x0 + v * 16 * 512) ^ (ks << 6)));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          // in flight: steps ks .. min(ks + kFusedAhead - 1, 7), two reads each
+          constexpr int kLast = 8 - kFusedAhead;
+          if (ks <= kLast) {
+            fused_lds_wait<2 * (kFusedAhead - 1)>(xv[ks][0], xv[ks][1]);
+          } else if (ks == kLast + 1) {
+            fused_lds_wait<(2 * (kFusedAhead - 2) > 0 ? 2 * (kFusedAhead - 2) : 0)>(xv[ks][0], xv[ks][1]);
+          } else if (ks == kLast + 2) {
+            fused_lds_wait<(2 * (kFusedAhead - 3) > 0 ? 2 * (kFusedAhead - 3) : 0)>(xv[ks][0], xv[ks][1]);
+          } else {
+            fused_lds_wait<0>(xv[ks][0], xv[ks][1]);
+          }
+          if (ks + kFusedAhead < 8) {
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+              xv[ks + kFusedAhead][v] = fused_lds_read16(xbase + ((x0 + v * 16 * 512) ^ ((ks + kFusedAhead) << 6)));
             }
-            uint2 v;
-            v.x = f32x2_to_bf16x2(acc[0], acc[1]);
-            v.y = f32x2_to_bf16x2(acc[2], acc[3]);
-            *reinterpret_cast<uint2*>(&s_raw[jb][1 + g][tr][(ob * 16 + lg * 4) * 2]) = v;
+          }
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              acc[v][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][ks], __builtin_bit_cast(bf16x8, xv[ks][v]),
+                                                                  acc[v][u], 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int tr = (tp * 2 + v) * 16 + lr;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            uint2 w2;
+            w2.x = f32x2_to_bf16x2(acc[v][u][0], acc[v][u][1]);
+            w2.y = f32x2_to_bf16x2(acc[v][u][2], acc[v][u][3]);
+            *reinterpret_cast<uint2*>(&s_raw[jb][1 + g][tr][(op * 32 + u * 16 + lg * 4) * 2]) = w2;
             if (gout != nullptr && tr < valid) {
-              *reinterpret_cast<uint2*>(gout + (t.rowbase + t.t0 + tr) * W + o) = v;
+              *reinterpret_cast<uint2*>(gout + (t.rowbase + t.t0 + tr) * W + o + u * 16) = w2;
             }
           }
         }
@@ -650,7 +751,39 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
     }
   };
 
-  if (wave >= LOAD0) {
+  if (FUSED && wave >= PROJ0) {
+    // ------------------------------------------------------------ projection waves
+    // Wave PROJ0 + q computes pass q of every tile: gate q / 2, outputs
+    // (q % 2) * 32 .. +31 of the strip, once the tile's block rows have
+    // landed and its raw buffer is free (s_xb_full), and counts it done.
+    if constexpr (FUSED) {
+      __builtin_amdgcn_s_setprio(3);
+      const int q = wave - PROJ0;
+      const int g = q >> 1, op = q & 1;
+      for (int i = 0;; ++i) {
+        lds_wait<false, kHelperSleep>(&s_tk_valid, i, &s_abort, p.hdr);
+        if (lds_load(&s_abort) != 0) break;
+        const unsigned tile = __builtin_amdgcn_readfirstlane(s_tk[i % RING]);
+        if (tile >= p.n_tiles) break;
+        const Tile t = tile_of(tile);
+        const int jb = i & 1;
+        const int kb = t.strip >> 2, sub = t.strip & 3;
+        // this pass's weights and bias (L2-resident) while the rows land
+        bf16x8 a[2][8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) a[u][ks] = fused_w_frag(g ? p.wt[1] : p.wt[0], kb, sub, op, u, ks, lane);
+        }
+        const FusedBias fb = fused_bias(g ? p.pbias[1] : p.pbias[0], kb * 256 + sub * 64 + op * 32 + (lane >> 4) * 4);
+        lds_wait<false, kHelperSleep>(&s_xb_full[jb], i, &s_abort, p.hdr);
+        if (lds_load(&s_abort) != 0) break;
+        project_pass(jb, t, p.L - 1 - t.t0, g, op, a, fb);
+        lds_release();
+        if (lane == 0) lds_add(&s_proj_done[jb], 1);
+      }
+    }
+  } else   if (wave >= LOAD0) {
     // ------------------------------------------------------------ load waves
     __builtin_amdgcn_s_setprio(3);
     const int j = wave - LOAD0;
@@ -672,9 +805,36 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
     for (int i = j;; i += 2) {
       lds_wait<false, kHelperSleep>(&s_tk_valid, i, &s_abort, p.hdr);
       const Tile t = tile_of(__builtin_amdgcn_readfirstlane(s_tk[i % RING]));
+      const long long lim = p.L - 1 - t.t0;   // last step row of the tile inside the sequence
+      if constexpr (FUSED) {
+        // The tile's rows across its whole block go to this wave's own block
+        // buffer, free once the projection waves are done with tile t_{i-2},
+        // so they are in flight before the raw buffer is: 2 rows of 512 bytes
+        // per instruction, lane l at row l / 32, LDS granule l % 32, which
+        // holds source granule (l % 32) ^ (row % 16).
+        lds_wait<false, kHelperSleep>(&s_proj_done[j], 4 * (i / 2), &s_abort, p.hdr);
+        if (t.valid && lds_load(&s_abort) == 0) {
+          const int kb = t.strip >> 2;
+          gbyte* base = uniform_gptr(static_cast<const unsigned char*>(p.x) + (t.rowbase + t.t0) * row_bytes +
+                                     static_cast<long long>(kb) * 512);
+          const int rr = lane >> 5;
+          const int gq = lane & 31;
+#pragma unroll 4
+          for (int g = 0; g < T / 2; ++g) {
+            const long long row = 2 * g + rr;
+            const long long rw = row < lim ? row : lim;
+            const unsigned off = static_cast<unsigned>(rw) * static_cast<unsigned>(row_bytes) +
+                                 static_cast<unsigned>((gq ^ (static_cast<int>(row) & 15)) * 16);
+            lds_dma16(base + off, &s_xb[j][2 * g][0]);
+          }
+        }
+      }
       // buffer j is free once every data wave is done with iteration i - 2
       lds_wait<false, kHelperSleep>(&s_cons[j], NW * (i / 2), &s_abort, p.hdr);
-      if (lds_load(&s_abort) != 0) break;
+      if (lds_load(&s_abort) != 0) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // no LDS-bound load outlives the wave
+        break;
+      }
       if (!t.valid) {
         if (lane == 0) lds_store(&s_full[j], i);
         break;
@@ -682,7 +842,6 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
       const float lam = t.active ? p.lam[t.ch] : 0.0f;
       const long long strip_b = static_cast<long long>(t.strip) * 64 * ES;
       const long long tile_off = (t.rowbase + t.t0) * row_bytes + strip_b;
-      const long long lim = p.L - 1 - t.t0;   // last step row of the tile inside the sequence
       if constexpr (WIDE) {
         // lane l: row l / SEG of each group of RPI rows, bytes (l % SEG) * 16
         // .. +15 of it. Segments past W (last strip only) re-read the strip's
@@ -697,7 +856,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
           // tile's rows under 2 GiB)
           const unsigned step = static_cast<unsigned>(RPI) * static_cast<unsigned>(row_bytes);
 #pragma unroll
-          for (int q = 0; q < (FUSED ? 1 : 3); ++q) {
+          for (int q = 0; q < (FUSED ? 0 : 3); ++q) {
             gbyte* base = uniform_gptr(src[q] + tile_off);
             unsigned off = static_cast<unsigned>(r) * static_cast<unsigned>(row_bytes) + col;
             unsigned char* dst = &s_raw[j][q][0][0];
@@ -710,7 +869,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
           }
         } else {
 #pragma unroll
-          for (int q = 0; q < (FUSED ? 1 : 3); ++q) {
+          for (int q = 0; q < (FUSED ? 0 : 3); ++q) {
             gbyte* base = uniform_gptr(src[q] + tile_off);
             for (int g = 0; g < T / RPI; ++g) {
               const long long row = g * RPI + r;
@@ -747,30 +906,24 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
           __builtin_amdgcn_global_load_lds(const_cast<uint32_t*>(p.seg) + t.rowbase + tk, &s_seg[j][h * 64], 4, 0, 0);
         }
       }
-      if constexpr (FUSED) {
-        // the tile's rows across the whole block: 2 rows of 512 bytes per
-        // instruction, lane l at row l / 32, LDS granule l % 32, which holds
-        // source granule (l % 32) ^ (row % 16)
-        const int kb = t.strip >> 2;
-        gbyte* base = uniform_gptr(static_cast<const unsigned char*>(p.x) + (t.rowbase + t.t0) * row_bytes +
-                                   static_cast<long long>(kb) * 512);
-        const int rr = lane >> 5;
-        const int gq = lane & 31;
-#pragma unroll 4
-        for (int g = 0; g < T / 2; ++g) {
-          const long long row = 2 * g + rr;
-          const long long rw = row < lim ? row : lim;
-          const unsigned off = static_cast<unsigned>(rw) * static_cast<unsigned>(row_bytes) +
-                               static_cast<unsigned>((gq ^ (static_cast<int>(row) & 15)) * 16);
-          lds_dma16(base + off, &s_xb[j][2 * g][0]);
-        }
-      }
       // the next two tickets, two iterations ahead (load wave 0 draws them all,
       // so a workgroup's tiles come in ticket order)
       u64 nxt = 0;
       if (j == 0 && lane == 0) nxt = atomicAdd(&p.hdr->counter, 2ull);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      if constexpr (FUSED) project(j, t, lim);
+      if constexpr (FUSED) {
+        // the tile's x strip, from its block rows, into the raw x rows the
+        // data waves read (row r at r * 128 bytes, granule gg of the strip at
+        // gg * 16)
+        const int sub = t.strip & 3;
+        const int gg = lane & 7;
+#pragma unroll
+        for (int k = 0; k < T / 8; ++k) {
+          const int row = k * 8 + (lane >> 3);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&s_xb[j][row][((sub * 8 + gg) ^ (row & 15)) * 8]);
+          *reinterpret_cast<u32x4*>(&s_raw[j][0][row][gg * 16]) = v;
+        }
+      }
       {
         float cs = 0.0f, k2 = 0.0f;
         if (t.active) channel_consts(lam, p.c, cs, k2);
@@ -784,9 +937,21 @@ __global__ __launch_bounds__((NW + 4) * 64) void fwd_kernel(FwdArgs p) {
         }
       }
       lds_release();
-      if (lane == 0) {
-        if (j == 0) lds_store(&s_tk_valid, i + 3);
-        lds_store(&s_full[j], i);
+      if constexpr (FUSED) {
+        // the block rows are in and the raw buffer is free: the projection
+        // waves fill its gate rows, and the tile is full once all four passes
+        // are (each released its writes before counting)
+        if (lane == 0) {
+          if (j == 0) lds_store(&s_tk_valid, i + 3);
+          lds_store(&s_xb_full[j], i);
+        }
+        lds_wait<false, kHelperSleep>(&s_proj_done[j], 4 * (i / 2 + 1), &s_abort, p.hdr);
+        if (lane == 0) lds_store(&s_full[j], i);
+      } else {
+        if (lane == 0) {
+          if (j == 0) lds_store(&s_tk_valid, i + 3);
+          lds_store(&s_full[j], i);
+        }
       }
     }
   } else if (wave >= CTRL0) {
@@ -2162,7 +2327,7 @@ rglru_status_t launch_fused(FwdArgs a, hipStream_t stream) {
   a.n_chunks = static_cast<int>(ceil_div(a.L, T));
   a.n_tiles = static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.B) * static_cast<unsigned>(a.n_strips);
   auto kernel = fwd_kernel<BF16, NW, TS, true, false, true>;
-  constexpr int threads = (NW + 4) * 64;
+  constexpr int threads = (NW + 8) * 64;
   const unsigned grid = persistent_grid(kernel, threads, a.n_tiles);
   if (grid == 0) return RGLRU_ERR_HIP;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, a);
