@@ -8,15 +8,16 @@
 //   dx[:, blk]     = dx_in[:, blk] + sum_g dgate_g[:, blk] @ w_g[blk]^T
 //   dw_g[blk]      = x[:, blk]^T @ dgate_g[:, blk]
 //   db_g[blk]      = column sums of dgate_g[:, blk]
-// bf16 operands, float32 accumulation (v_mfma_f32_16x16x32_bf16: A 16x32,
-// B 32x16; lane l holds row/column l%16 and k = (l/16)*8 .. +7; D lane l holds
-// column l%16, rows (l/16)*4 .. +3).
+// bf16 operands, float32 accumulation: v_mfma_f32_32x32x16_bf16 in the
+// forward, v_mfma_f32_16x16x32_bf16 in the backward (A 16x32, B 32x16; lane l
+// holds row/column l%16 and k = (l/16)*8 .. +7; D lane l holds column l%16,
+// rows (l/16)*4 .. +3).
 //
 // Forward and dx kernels: a workgroup of 8 waves owns one block and a
 // contiguous token range. Its weight fragments (bf16, 128 VGPRs per lane) are
 // loaded once; 32-token tiles of the token-major operands stream through a
 // ring of LDS buffers with global_load_lds, steps ahead of the multiply, and
-// each lane stores 4 consecutive output channels of one token (8 bytes).
+// the outputs leave through a per-wave LDS staging area as whole row segments.
 // dW kernel: K runs over tokens, so 32-token slabs of x and of the gate
 // gradient stream into a ring of LDS buffers (global_load_lds) and the MFMA
 // operands come out with the gfx950 transpose read; each workgroup owns one
@@ -42,8 +43,18 @@ constexpr int kKT = 32;           // tokens per step
 constexpr int kWaves8 = 8;        // waves per workgroup of every kernel here
 constexpr uint32_t kSlabBytes = kKT * kBS * 2;   // one 32-row x 256-column bf16 slab
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: A 32x16, B 16x32; lane l holds row/column l%32
+// and k = (l/32)*8 .. +7; D lane l holds column l%32, register r row
+// (r/4)*8 + (l/32)*4 + r%4. One wave sustains about 2.4 times the rate of the
+// 16x16x32 form, which needs several waves per SIMD to approach its peak.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -143,6 +154,11 @@ __device__ __forceinline__ void lds_wait(u32x2& x, u32x2& y) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "n"(N));
 }
 
+template <int N>
+__device__ __forceinline__ void lds_wait1(u32x4& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
+}
+
 __device__ __forceinline__ bf16x8 frag_of(u32x2 lo, u32x2 hi) {
   return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
@@ -201,6 +217,18 @@ __device__ __forceinline__ uint32_t frag_off(int col0, int lane, int half) {
   return static_cast<uint32_t>(r * (kBS * 2) + ((chunk ^ (r & 15)) << 5) + (sl & 3) * 8);
 }
 
+// The same for a 32x32x16 A operand: rows h*16 .. +15 of the slab are the
+// k-step; lane l takes column col0 + l % 32, rows (l / 32) * 8 .. +7 of it, the
+// two reads giving rows +0 .. 3 and +4 .. 7 (source lane s of each 16-lane
+// group addresses row (s / 4) at columns 4 * (s % 4) .. +3 of its 16 columns).
+__device__ __forceinline__ uint32_t frag_off32(int col0, int lane, int h, int half) {
+  const int g = lane >> 4;
+  const int sl = lane & 15;
+  const int r = h * 16 + (g >> 1) * 8 + half * 4 + (sl >> 2);
+  const int chunk = (col0 >> 4) + (g & 1);
+  return static_cast<uint32_t>(r * (kBS * 2) + ((chunk ^ (r & 15)) << 5) + (sl & 3) * 8);
+}
+
 // LDS byte offset, within a kSwz16 slab, of the 16 bytes at row r, columns
 // 8 * g .. +7
 __device__ __forceinline__ uint32_t row_off16(int r, int g) {
@@ -225,16 +253,20 @@ __device__ __forceinline__ Range token_range(int idx, long long per, long long T
 // ---------------------------------------------------------------- forward
 //
 // gate_g[t, kb*256 + o] = b_g[o] + sum_i x[t, kb*256 + i] w_g[kb][i][o].
-// MFMA with A = w_g^T (rows o, k = i) held in registers and B = x^T (k = i,
-// columns t) from the LDS ring, so that D holds 4 consecutive outputs of one
-// token per lane. Wave w computes gate w / 4, outputs 64 * (w % 4) .. +63:
-// 4 m-tiles x 8 k-steps of weights. The weights reach registers through the
-// same LDS buffers (kSwz32 slabs of 32 input rows) and transpose reads.
+// v_mfma_f32_32x32x16_bf16 with A = w_g^T (rows o, k = i) held in registers
+// and B = x^T (k = i, columns t) from the LDS ring, so that D holds, per lane,
+// one token and 4 groups of 4 consecutive outputs. Wave w computes gate w / 4,
+// outputs 64 * (w % 4) .. +63: 2 m-tiles of 32 outputs x 16 k-steps of 16
+// inputs, accumulated from the bias in input order. The weights reach
+// registers through the same LDS buffers (kSwz32 slabs of 32 input rows) and
+// transpose reads.
 
 constexpr int kFwdBufs = 4;                   // ring of x slabs (16 KiB each)
 constexpr int kFwdDma = 2;                    // 1 KiB loads per wave per step
-constexpr int kFwdStores = 4;                 // 16-byte stores per wave per step (2 token tiles x 2)
+constexpr int kFwdStores = 4;                 // 16-byte stores per wave per step
 constexpr int kStagePitch = 144;              // bytes per staged output row (128 + 16: conflict-free)
+constexpr int kFwdAhead = 4;                  // k-steps of token operands read ahead
+static_assert(kFwdAhead == 4, "the wait ladder in proj_fwd_kernel assumes 4 reads in flight");
 
 struct ProjFwdArgs {
   const uint16_t* x;
@@ -250,9 +282,9 @@ struct ProjFwdArgs {
 
 __global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_ring[kFwdBufs][kKT][kBS];
-  // per-wave output staging: 2 token tiles x 16 tokens x 64 outputs, so that
-  // each store writes whole 128-byte row segments
-  __shared__ __attribute__((aligned(16))) char s_stage[kWaves8][2][16][kStagePitch];
+  // per-wave output staging: 32 tokens x 64 outputs, so that each store
+  // writes whole 128-byte row segments
+  __shared__ __attribute__((aligned(16))) char s_stage[kWaves8][kKT][kStagePitch];
   const int id = blockIdx.x;
   const int range = id / p.nb;
   const int kb = id - range * p.nb;
@@ -264,8 +296,8 @@ __global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
   const Range rg = token_range(range, p.per, p.T);
   const uint32_t ring0 = lds_addr(&s_ring[0][0][0]);
 
-  // weights: 16 slabs (gate, 32 input rows) in 4 rounds of 4 ring buffers
-  bf16x8 wr[4][8];                          // [m-tile][k-step]
+  // weights: 16 slabs (gate, 32 input rows = 2 k-steps) in 4 rounds of 4 ring buffers
+  bf16x8 wr[2][16];                         // [m-tile][k-step]
 #pragma unroll
   for (int round = 0; round < 4; ++round) {
 #pragma unroll
@@ -280,27 +312,37 @@ __global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
     if (gw == (round >> 1)) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int ks = (round & 1) * 4 + b;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          u32x2 lo = lds_read_tr(ring0 + b * kSlabBytes + frag_off(ob + mt * 16, lane, 0));
-          u32x2 hi = lds_read_tr(ring0 + b * kSlabBytes + frag_off(ob + mt * 16, lane, 1));
-          lds_wait<0>(lo, hi);
-          wr[mt][ks] = frag_of(lo, hi);
+        for (int h = 0; h < 2; ++h) {
+          const int ks = ((round & 1) * 4 + b) * 2 + h;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            u32x2 lo = lds_read_tr(ring0 + b * kSlabBytes + frag_off32(ob + mt * 32, lane, h, 0));
+            u32x2 hi = lds_read_tr(ring0 + b * kSlabBytes + frag_off32(ob + mt * 32, lane, h, 1));
+            lds_wait<0>(lo, hi);
+            wr[mt][ks] = frag_of(lo, hi);
+          }
         }
       }
     }
     __syncthreads();
   }
 
-  // bias of this lane's outputs: ob + mt*16 + (lane/16)*4 + j
-  f32x4 bias[4];
+  // bias of this lane's outputs ob + mt*32 + 8j + (lane/32)*4 + i, as bf16
+  // pairs (i = 0, 1 and 2, 3)
+  uint32_t bias2[2][4][2];
   const uint16_t* bsrc = p.bias[gw];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bias[mt][j] = bsrc != nullptr ? bf(bsrc[kb * kBS + ob + mt * 16 + (lane >> 4) * 4 + j]) : 0.0f;
+      const int o = kb * kBS + ob + mt * 32 + j * 8 + (lane >> 5) * 4;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        bias2[mt][j][k] = bsrc != nullptr ? (static_cast<uint32_t>(bsrc[o + 2 * k]) |
+                                             (static_cast<uint32_t>(bsrc[o + 2 * k + 1]) << 16))
+                                          : 0u;
+      }
     }
   }
 
@@ -314,13 +356,13 @@ __global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
       slab_piece<kSwz16>(xsrc + t0 * p.Wd, p.Wd, wave * kFwdDma + u, valid, &s_ring[st % kFwdBufs][0][0], lane);
     }
   };
-  // B operand of k-step ks, token tile tt: row tt*16 + lane%16, columns ks*32 + (lane/16)*8 .. +7
-  uint32_t xoff[8];
+  // B operand of k-step ks: row lane%32, columns ks*16 + (lane/32)*8 .. +7
+  uint32_t xoff[16];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) xoff[ks] = row_off16(lane & 15, ks * 4 + (lane >> 4));
+  for (int ks = 0; ks < 16; ++ks) xoff[ks] = row_off16(lane & 31, ks * 2 + (lane >> 5));
   uint16_t* obase = p.out[gw] + kb * kBS + ob + (lane & 7) * 8;   // lane's 16 bytes of a staged row
-  const uint32_t stage_w = lds_addr(&s_stage[wave][0][lane & 15][(lane >> 4) * 8]);
-  const uint32_t stage_r = lds_addr(&s_stage[wave][0][lane >> 3][(lane & 7) * 16]);
+  const uint32_t stage_w = lds_addr(&s_stage[wave][lane & 31][(lane >> 5) * 8]);
+  const uint32_t stage_r = lds_addr(&s_stage[wave][lane >> 3][(lane & 7) * 16]);
 
 #pragma unroll
   for (int d = 0; d < kFwdBufs - 1; ++d) {
@@ -336,71 +378,63 @@ __global__ __launch_bounds__(kWaves8 * 64) void proj_fwd_kernel(ProjFwdArgs p) {
     asm volatile("" ::: "memory");
     if (ahead >= kFwdBufs - 1) issue(st + kFwdBufs - 1);
     const uint32_t sb = ring0 + static_cast<uint32_t>(st % kFwdBufs) * kSlabBytes;
-    f32x4 acc[4][2];
+    f32x16 acc[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      acc[mt][0] = bias[mt];
-      acc[mt][1] = bias[mt];
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          acc[mt][j * 4 + 2 * k] = __uint_as_float(bias2[mt][j][k] << 16);
+          acc[mt][j * 4 + 2 * k + 1] = __uint_as_float(bias2[mt][j][k] & 0xFFFF0000u);
+        }
+      }
     }
-    // token operands of both tiles, at most 8 reads in flight
-    u32x4 xb[8][2];
+    // token operands, kFwdAhead k-steps in flight
+    u32x4 xb[16];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      xb[ks][0] = lds_read16(sb + xoff[ks]);
-      xb[ks][1] = lds_read16(sb + xoff[ks] + 16 * kBS * 2);
-    }
+    for (int ks = 0; ks < kFwdAhead; ++ks) xb[ks] = lds_read16(sb + xoff[ks]);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      // in flight: k-steps ks .. min(ks + 3, 7), two reads each
-      if (ks <= 4) {
-        lds_wait<6>(xb[ks][0], xb[ks][1]);
-      } else if (ks == 5) {
-        lds_wait<4>(xb[ks][0], xb[ks][1]);
-      } else if (ks == 6) {
-        lds_wait<2>(xb[ks][0], xb[ks][1]);
+    for (int ks = 0; ks < 16; ++ks) {
+      // in flight: k-steps ks .. min(ks + kFwdAhead - 1, 15)
+      if (ks <= 16 - kFwdAhead) {
+        lds_wait1<kFwdAhead - 1>(xb[ks]);
+      } else if (ks == 17 - kFwdAhead) {
+        lds_wait1<kFwdAhead - 2>(xb[ks]);
+      } else if (ks == 18 - kFwdAhead) {
+        lds_wait1<kFwdAhead - 3>(xb[ks]);
       } else {
-        lds_wait<0>(xb[ks][0], xb[ks][1]);
+        lds_wait1<0>(xb[ks]);
       }
-      if (ks + 4 < 8) {
-        xb[ks + 4][0] = lds_read16(sb + xoff[ks + 4]);
-        xb[ks + 4][1] = lds_read16(sb + xoff[ks + 4] + 16 * kBS * 2);
-      }
+      if (ks + kFwdAhead < 16) xb[ks + kFwdAhead] = lds_read16(sb + xoff[ks + kFwdAhead]);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt][tt] = mfma(wr[mt][ks], as_bf16x8(xb[ks][tt]), acc[mt][tt]);
-      }
+      for (int mt = 0; mt < 2; ++mt) acc[mt] = mfma32(wr[mt][ks], as_bf16x8(xb[ks]), acc[mt]);
     }
     asm volatile("" ::: "memory");
-    // D lane l: token tt*16 + l%16, outputs mt*16 + (l/16)*4 .. +3 -> staging
+    // D lane l: token l%32, outputs mt*32 + 8j + (l/32)*4 .. +3 -> staging
     // (LDS accesses of one wave complete in order)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int j = 0; j < 4; ++j) {
         u32x2 v;
-        v[0] = pack2(acc[mt][tt][0], acc[mt][tt][1]);
-        v[1] = pack2(acc[mt][tt][2], acc[mt][tt][3]);
-        lds_write8(stage_w + tt * 16 * kStagePitch + mt * 32, v);
+        v[0] = pack2(acc[mt][j * 4 + 0], acc[mt][j * 4 + 1]);
+        v[1] = pack2(acc[mt][j * 4 + 2], acc[mt][j * 4 + 3]);
+        lds_write8(stage_w + mt * 64 + j * 16, v);
       }
     }
-    // staged rows -> global: lane l stores bytes 16 * (l % 8) .. +15 of row (l / 8) (+8)
-    u32x4 sv[2][2];
+    // staged rows -> global: lane l stores bytes 16 * (l % 8) .. +15 of rows
+    // l / 8 + 8 * q
+    u32x4 sv[4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) sv[tt][h] = lds_read16(stage_r + (tt * 16 + h * 8) * kStagePitch);
-    }
-    lds_wait<0>(sv[0][0], sv[0][1]);
-    lds_wait<0>(sv[1][0], sv[1][1]);
+    for (int q = 0; q < 4; ++q) sv[q] = lds_read16(stage_r + q * 8 * kStagePitch);
+    lds_wait<0>(sv[0], sv[1]);
+    lds_wait<0>(sv[2], sv[3]);
     const long long t0 = rg.tbeg + static_cast<long long>(st) * kKT;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const long long t = t0 + tt * 16 + h * 8 + (lane >> 3);
-        if (ahead > 0 || t < rg.tend) *reinterpret_cast<u32x4*>(obase + t * p.Wd) = sv[tt][h];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const long long t = t0 + q * 8 + (lane >> 3);
+      if (ahead > 0 || t < rg.tend) *reinterpret_cast<u32x4*>(obase + t * p.Wd) = sv[q];
     }
     // the stores are issued before the next step's wait counts them
     asm volatile("" ::: "memory");

@@ -88,6 +88,7 @@ struct BF16 {
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 template <int BYTES> struct Raw;
@@ -403,8 +404,9 @@ struct FwdArgs {
   const float* h0s;
   float* h_last_s;
   // gate projections computed inside the forward (256-wide blocks): the
-  // transposed weights [nb][256 out][256 in] bf16 of each gate, the biases
-  // [W] bf16 (or nullptr), and where the logits also go [B*L, W] (or nullptr)
+  // weights of each gate in MFMA fragment order (one 1 KiB fragment per
+  // block, 32-output tile and 16-input step), the biases [W] bf16 (or
+  // nullptr), and where the logits also go [B*L, W] (or nullptr)
   const uint16_t* wt[2];
   const uint16_t* pbias[2];
   uint16_t* gout[2];
@@ -464,29 +466,32 @@ __device__ __forceinline__ void lds_wait(const int* f, int v, int* abort, Header
 // s_waitcnt immediates (gfx9 layout: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), other counters unconstrained
 
-// Fused projection helpers. A pass works on one gate and two 16-output tiles
-// (outputs sub*64 + op*32 + u*16 + lane%16 of block kb): its weights are MFMA
-// A operands, inputs ks*32 + (lane/16)*8 .. +7 of each of the 8 input steps,
-// read from the transposed copy [block][out][in].
-__device__ __forceinline__ bf16x8 fused_w_frag(const uint16_t* wt, int kb, int sub, int op, int u, int ks, int lane) {
-  const uint16_t* w = wt + (static_cast<long long>(kb) * 256 + sub * 64 + op * 32 + u * 16 + (lane & 15)) * 256 +
-                      ks * 32 + (lane >> 4) * 8;
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(w));
+// Fused projection helpers. A pass works on one gate and one 32-output tile
+// (outputs sub*64 + op*32 + lane%32 of block kb) with
+// v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32; lane l holds row/column l%32
+// and k = (l/32)*8 .. +7; D lane l holds column l%32, register r row
+// (r/4)*8 + (l/32)*4 + r%4): its weights are the A operands of the 16 input
+// steps of 16. The call lays them out beforehand in fragment order, so that
+// each is one contiguous 1 KiB load: fragment (kb, ot, ks) holds, for lane l,
+// inputs ks*16 + (l/32)*8 .. +7 of output ot*32 + l%32.
+__device__ __forceinline__ bf16x8 fused_w_frag(const uint16_t* wf, int kb, int sub, int op, int ks, int lane) {
+  const long long frag = (static_cast<long long>(kb) * 8 + sub * 2 + op) * 16 + ks;
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wf + (frag * 64 + lane) * 8));
 }
 
-// The bias of a lane's accumulator rows (4 consecutive outputs per output
-// tile), as raw bf16; zeros without a bias.
+// The bias of a lane's accumulator rows (outputs 8j + (lane/32)*4 + i of the
+// tile, i = 0..3, for j = 0..3), as raw bf16 pairs; zeros without a bias.
 struct FusedBias {
-  uint32_t v[2][2];   // [output tile][pair]: outputs 2k (low half) and 2k + 1
+  uint32_t v[4][2];   // [j][pair]: outputs i = 2k (low half) and 2k + 1
 };
 __device__ __forceinline__ FusedBias fused_bias(const uint16_t* bias, int o) {
   FusedBias r;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      r.v[u][k] = bias != nullptr ? (static_cast<uint32_t>(bias[o + u * 16 + 2 * k]) |
-                                     (static_cast<uint32_t>(bias[o + u * 16 + 2 * k + 1]) << 16))
+      r.v[j][k] = bias != nullptr ? (static_cast<uint32_t>(bias[o + j * 8 + 2 * k]) |
+                                     (static_cast<uint32_t>(bias[o + j * 8 + 2 * k + 1]) << 16))
                                   : 0u;
     }
   }
@@ -502,9 +507,10 @@ __device__ __forceinline__ uint32_t lds_off(const void* ptr) {
   typedef __attribute__((address_space(3))) const char lds_char;
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(ptr)));
 }
+template <int OFF = 0>
 __device__ __forceinline__ u32x4 fused_lds_read16(uint32_t addr) {
   u32x4 d;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(d) : "v"(addr));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
   return d;
 }
 constexpr int kFusedAhead = 2;   // input steps of token operands read ahead
@@ -572,8 +578,8 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
   static_assert(TS <= 16 && NW <= 32, "a wave's cut and end flags share one mask word; the waves' flags fit one");
   static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
   static_assert(NFL % 64 == 0 && NFL <= 128, "reset flags: at most two instructions");
-  static_assert(!FUSED || (std::is_same<IO, BF16>::value && WIDE && T % 16 == 0 && !PACKED),
-                "the fused projection runs bf16 tiles of 16-row blocks");
+  static_assert(!FUSED || (std::is_same<IO, BF16>::value && WIDE && T == 64 && !PACKED),
+                "the fused projection runs bf16 tiles of two 32-token MFMA tiles");
 
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][3][T][ROWB];
   // fused projection: the tile's rows of x across its whole 256-wide block
@@ -664,87 +670,75 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
   // chains hide the MFMA latency and each token operand read from LDS feeds
   // two products. A pass's weights come from the pre-transposed copy
   // ([out][in], L2-resident: every tile of a strip reads the same 64 KiB).
-  auto project_pass = [=](int jb, const Tile& t, long long lim, int g, int op, const bf16x8 (&a)[2][8],
-                          FusedBias bias) {
+  auto project_pass = [=](int jb, const Tile& t, long long lim, int g, int op, const bf16x8 (&a)[16],
+                          const FusedBias& bias) {
     if constexpr (FUSED) {
       const int kb = t.strip >> 2;
       const int sub = t.strip & 3;
       const int valid = lim + 1 < T ? static_cast<int>(lim + 1) : T;
-      const int lr = lane & 15;
-      const int lg = lane >> 4;
+      const int lr = lane & 31;
+      const int hi = lane >> 5;
       // (a select, not indexing by g: a dynamic index into the argument
       // struct's arrays would move the struct to scratch memory)
       uint16_t* gout = g ? p.gout[1] : p.gout[0];
-      const int o = kb * 256 + sub * 64 + op * 32 + lg * 4;   // output of u = 0, q = 0
-      f32x4 b0[2];
+      const int o = kb * 256 + sub * 64 + op * 32 + hi * 4;   // output of j = 0, i = 0
+      // token operand of input step ks, token tile tp: row tp*32 + lr, source
+      // granule ks*2 + hi, stored at granule (ks*2 + hi) ^ (lr % 16); the
+      // swizzle acts on the offset within the buffer, which starts at xbase
+      const uint32_t xbase = lds_off(&s_xb[jb][0][0]);
+      // (from a lane index opaque here, so that the read addresses are formed
+      // as they are used instead of being kept in registers across tiles)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const uint32_t xrow = static_cast<uint32_t>((ln & 31) * 512 + (((ln >> 5) ^ (ln & 15)) << 4));
+      // token tile 1 is 32 rows (16 KiB) further: an immediate offset
+      auto xread = [&](int ks, u32x4 (&dst)[2]) {
+        const uint32_t ad = xbase + (xrow ^ static_cast<uint32_t>(ks << 5));
+        dst[0] = fused_lds_read16<0>(ad);
+        dst[1] = fused_lds_read16<32 * 512>(ad);
+      };
+      f32x16 acc[2];   // [token tile]
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int v = 0; v < 2; ++v) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          b0[u][q] = __uint_as_float((q & 1) ? (bias.v[u][q >> 1] & 0xFFFF0000u) : (bias.v[u][q >> 1] << 16));
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            acc[v][j * 4 + 2 * k] = __uint_as_float(bias.v[j][k] << 16);
+            acc[v][j * 4 + 2 * k + 1] = __uint_as_float(bias.v[j][k] & 0xFFFF0000u);
+          }
         }
       }
-      // token operand of input step ks, token tile tb: row tb*16 + lr, source
-      // granule ks*4 + lg, stored at granule (ks*4 + lg) ^ lr
-      // (the swizzle acts on the offset within the buffer, which starts at
-      // xbase)
-      const uint32_t xbase = lds_off(&s_xb[jb][0][0]);
-      const uint32_t xrow = static_cast<uint32_t>(lr * 512 + ((lg ^ lr) << 4));
-#pragma unroll 1
-      for (int tp = 0; tp < T / 32; ++tp) {
-        f32x4 acc[2][2];   // [token tile][output tile]
+      u32x4 xv[16][2];
+#pragma unroll
+      for (int ks = 0; ks < kFusedAhead; ++ks) xread(ks, xv[ks]);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        // in flight: steps ks .. min(ks + kFusedAhead - 1, 15), two reads each
+        constexpr int kLast = 16 - kFusedAhead;
+        if (ks <= kLast) {
+          fused_lds_wait<2 * (kFusedAhead - 1)>(xv[ks][0], xv[ks][1]);
+        } else {
+          fused_lds_wait<0>(xv[ks][0], xv[ks][1]);
+        }
+        if (ks + kFusedAhead < 16) xread(ks + kFusedAhead, xv[ks + kFusedAhead]);
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
-          acc[v][0] = b0[0];
-          acc[v][1] = b0[1];
+          acc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], __builtin_bit_cast(bf16x8, xv[ks][v]), acc[v], 0, 0,
+                                                           0);
         }
-        const uint32_t x0 = xrow + static_cast<uint32_t>(tp * 32 * 512);
-        u32x4 xv[8][2];
+      }
 #pragma unroll
-        for (int ks = 0; ks < kFusedAhead; ++ks) {
+      for (int v = 0; v < 2; ++v) {
+        const int tr = v * 32 + lr;
 #pragma unroll
-          for (int v = 0; v < 2; ++v) xv[ks][v] = fused_lds_read16(xbase + ((x0 + v * 16 * 512) ^ (ks << 6)));
-        }
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          // in flight: steps ks .. min(ks + kFusedAhead - 1, 7), two reads each
-          constexpr int kLast = 8 - kFusedAhead;
-          if (ks <= kLast) {
-            fused_lds_wait<2 * (kFusedAhead - 1)>(xv[ks][0], xv[ks][1]);
-          } else if (ks == kLast + 1) {
-            fused_lds_wait<(2 * (kFusedAhead - 2) > 0 ? 2 * (kFusedAhead - 2) : 0)>(xv[ks][0], xv[ks][1]);
-          } else if (ks == kLast + 2) {
-            fused_lds_wait<(2 * (kFusedAhead - 3) > 0 ? 2 * (kFusedAhead - 3) : 0)>(xv[ks][0], xv[ks][1]);
-          } else {
-            fused_lds_wait<0>(xv[ks][0], xv[ks][1]);
-          }
-          if (ks + kFusedAhead < 8) {
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-              xv[ks + kFusedAhead][v] = fused_lds_read16(xbase + ((x0 + v * 16 * 512) ^ ((ks + kFusedAhead) << 6)));
-            }
-          }
-#pragma unroll
-          for (int v = 0; v < 2; ++v) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              acc[v][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][ks], __builtin_bit_cast(bf16x8, xv[ks][v]),
-                                                                  acc[v][u], 0, 0, 0);
-            }
-          }
-        }
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          const int tr = (tp * 2 + v) * 16 + lr;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            uint2 w2;
-            w2.x = f32x2_to_bf16x2(acc[v][u][0], acc[v][u][1]);
-            w2.y = f32x2_to_bf16x2(acc[v][u][2], acc[v][u][3]);
-            *reinterpret_cast<uint2*>(&s_raw[jb][1 + g][tr][(op * 32 + u * 16 + lg * 4) * 2]) = w2;
-            if (gout != nullptr && tr < valid) {
-              *reinterpret_cast<uint2*>(gout + (t.rowbase + t.t0 + tr) * W + o + u * 16) = w2;
-            }
+        for (int j = 0; j < 4; ++j) {
+          uint2 w2;
+          w2.x = f32x2_to_bf16x2(acc[v][j * 4 + 0], acc[v][j * 4 + 1]);
+          w2.y = f32x2_to_bf16x2(acc[v][j * 4 + 2], acc[v][j * 4 + 3]);
+          *reinterpret_cast<uint2*>(&s_raw[jb][1 + g][tr][(op * 32 + j * 8 + hi * 4) * 2]) = w2;
+          if (gout != nullptr && tr < valid) {
+            *reinterpret_cast<uint2*>(gout + (t.rowbase + t.t0 + tr) * W + o + j * 8) = w2;
           }
         }
       }
@@ -769,13 +763,10 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
         const int jb = i & 1;
         const int kb = t.strip >> 2, sub = t.strip & 3;
         // this pass's weights and bias (L2-resident) while the rows land
-        bf16x8 a[2][8];
+        bf16x8 a[16];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks) a[u][ks] = fused_w_frag(g ? p.wt[1] : p.wt[0], kb, sub, op, u, ks, lane);
-        }
-        const FusedBias fb = fused_bias(g ? p.pbias[1] : p.pbias[0], kb * 256 + sub * 64 + op * 32 + (lane >> 4) * 4);
+        for (int ks = 0; ks < 16; ++ks) a[ks] = fused_w_frag(g ? p.wt[1] : p.wt[0], kb, sub, op, ks, lane);
+        const FusedBias fb = fused_bias(g ? p.pbias[1] : p.pbias[0], kb * 256 + sub * 64 + op * 32 + (lane >> 5) * 4);
         lds_wait<false, kHelperSleep>(&s_xb_full[jb], i, &s_abort, p.hdr);
         if (lds_load(&s_abort) != 0) break;
         project_pass(jb, t, p.L - 1 - t.t0, g, op, a, fb);
@@ -2334,19 +2325,27 @@ rglru_status_t launch_fused(FwdArgs a, hipStream_t stream) {
   return launch_status();
 }
 
-// Both gates' weights [nb][256 in][256 out] -> [nb][256 out][256 in], 32 x 32
-// tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_w_kernel(const uint16_t* w0, const uint16_t* w1, uint16_t* t0,
-                                                         uint16_t* t1) {
-  __shared__ uint16_t tile[32][33];
-  const int g = blockIdx.z & 1;
-  const long long kb = blockIdx.z >> 1;
-  const uint16_t* src = (g ? w1 : w0) + kb * 65536;
-  uint16_t* dst = (g ? t1 : t0) + kb * 65536;
-  const int i0 = blockIdx.y * 32, o0 = blockIdx.x * 32;
-  for (int r = threadIdx.y; r < 32; r += 8) tile[r][threadIdx.x] = src[(i0 + r) * 256 + o0 + threadIdx.x];
-  __syncthreads();
-  for (int r = threadIdx.y; r < 32; r += 8) dst[(o0 + r) * 256 + i0 + threadIdx.x] = tile[threadIdx.x][r];
+// Both gates' weights [nb][256 in][256 out] into the fused projection's
+// fragment order (see fused_w_frag): thread (fragment, lane) gathers its 8
+// inputs of one output; a wave's reads of one input row are 32 consecutive
+// outputs.
+__global__ __launch_bounds__(256) void w_frag_kernel(const uint16_t* w0, const uint16_t* w1, uint16_t* f0, uint16_t* f1,
+                                                     long long n_frag) {
+  const long long id = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const long long frag = id >> 6;
+  if (frag >= 2 * n_frag) return;
+  const int g = frag >= n_frag ? 1 : 0;
+  const long long fr = frag - g * n_frag;
+  const int lane = static_cast<int>(id & 63);
+  const int ks = static_cast<int>(fr & 15);
+  const int ot = static_cast<int>((fr >> 4) & 7);
+  const long long kb = fr >> 7;
+  const uint16_t* src = (g ? w1 : w0) + kb * 65536 + (ks * 16 + (lane >> 5) * 8) * 256 + ot * 32 + (lane & 31);
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = src[e * 256];
+  uint16_t* dst = (g ? f1 : f0) + (fr * 64 + lane) * 8;
+  *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, v);
 }
 
 // Forward tile length for a requested chunk: at most 128 steps where 2-byte
@@ -2807,8 +2806,9 @@ rglru_status_t rglru_blockdiag_fused_fwd(const rglru_shape_t* s, const void* x, 
   const long long nb = s->width / 256;
   uint16_t* wt0 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + fwd_ws(s));
   uint16_t* wt1 = wt0 + nb * 65536;
-  hipLaunchKernelGGL(transpose_w_kernel, dim3(8, 8, static_cast<unsigned>(2 * nb)), dim3(32, 8), 0, st,
-                     static_cast<const uint16_t*>(w_x), static_cast<const uint16_t*>(w_a), wt0, wt1);
+  const long long n_frag = nb * 128;   // per gate: 8 output tiles x 16 input steps per block
+  hipLaunchKernelGGL(w_frag_kernel, dim3(static_cast<unsigned>(ceil_div(2 * n_frag * 64, 256))), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(w_x), static_cast<const uint16_t*>(w_a), wt0, wt1, n_frag);
   rglru_status_t r = launch_status();
   if (r != RGLRU_OK) return r;
   const Slots sl = slots_in(workspace, slot_words(s, g.n_chunks_f));
