@@ -479,25 +479,6 @@ __device__ __forceinline__ bf16x8 fused_w_frag(const uint16_t* wf, int kb, int s
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wf + (frag * 64 + lane) * 8));
 }
 
-// The bias of a lane's accumulator rows (outputs 8j + (lane/32)*4 + i of the
-// tile, i = 0..3, for j = 0..3), as raw bf16 pairs; zeros without a bias.
-struct FusedBias {
-  uint32_t v[4][2];   // [j][pair]: outputs i = 2k (low half) and 2k + 1
-};
-__device__ __forceinline__ FusedBias fused_bias(const uint16_t* bias, int o) {
-  FusedBias r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      r.v[j][k] = bias != nullptr ? (static_cast<uint32_t>(bias[o + j * 8 + 2 * k]) |
-                                     (static_cast<uint32_t>(bias[o + j * 8 + 2 * k + 1]) << 16))
-                                  : 0u;
-    }
-  }
-  return r;
-}
-
 // LDS reads of the token operands, issued as inline assembly so that they
 // stay the written distance ahead of their MFMAs (compiled reads are placed
 // one step ahead). fused_lds_wait waits until at most N LDS operations of the
@@ -513,7 +494,7 @@ __device__ __forceinline__ u32x4 fused_lds_read16(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
   return d;
 }
-constexpr int kFusedAhead = 2;   // input steps of token operands read ahead
+constexpr int kFusedAhead = 1;   // input steps of token operands read ahead
 template <int N>
 __device__ __forceinline__ void fused_lds_wait(u32x4& x, u32x4& y) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "n"(N));
@@ -578,7 +559,7 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
   static_assert(TS <= 16 && NW <= 32, "a wave's cut and end flags share one mask word; the waves' flags fit one");
   static_assert(!WIDE || T % RPI == 0, "a tile is a whole number of 16-byte-per-lane instructions");
   static_assert(NFL % 64 == 0 && NFL <= 128, "reset flags: at most two instructions");
-  static_assert(!FUSED || (std::is_same<IO, BF16>::value && WIDE && T == 64 && !PACKED),
+  static_assert(!FUSED || (std::is_same<IO, BF16>::value && WIDE && T == 64 && TS == 8 && !PACKED),
                 "the fused projection runs bf16 tiles of two 32-token MFMA tiles");
 
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[2][3][T][ROWB];
@@ -608,6 +589,7 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
   __shared__ int s_maps_in[3];        // data-wave maps reported for iterations of each slot so far
   __shared__ int s_carry_ok[3];       // iteration whose incoming carry slot s holds
   __shared__ int s_prog[NW];          // iteration each data wave is in
+  __shared__ __attribute__((aligned(16))) float s_fbias[FUSED ? 2 : 1][2][64];   // fused: the strip's biases per gate
   __shared__ int s_xb_full[2];        // fused: iteration whose block rows s_xb[j] holds
   __shared__ int s_proj_done[2];      // fused: projection passes finished on buffer j so far
   __shared__ int s_abort;
@@ -670,18 +652,18 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
   // chains hide the MFMA latency and each token operand read from LDS feeds
   // two products. A pass's weights come from the pre-transposed copy
   // ([out][in], L2-resident: every tile of a strip reads the same 64 KiB).
-  auto project_pass = [=](int jb, const Tile& t, long long lim, int g, int op, const bf16x8 (&a)[16],
-                          const FusedBias& bias) {
+  // The gate rows the passes write are swizzled: 8-byte chunk c of row r
+  // (channels 4c .. 4c+3) sits at chunk c ^ ((r >> 1) & 15), so that the 32
+  // rows one write instruction covers fall on distinct banks; the data waves
+  // read them through the same map.
+  //
+  // a holds the pass's weights; the biases come from s_fbias[jb][g].
+  auto project_pass = [=](int jb, const Tile& t, long long lim, int g, int op, const bf16x8 (&a)[16]) {
     if constexpr (FUSED) {
       const int kb = t.strip >> 2;
       const int sub = t.strip & 3;
-      const int valid = lim + 1 < T ? static_cast<int>(lim + 1) : T;
       const int lr = lane & 31;
       const int hi = lane >> 5;
-      // (a select, not indexing by g: a dynamic index into the argument
-      // struct's arrays would move the struct to scratch memory)
-      uint16_t* gout = g ? p.gout[1] : p.gout[0];
-      const int o = kb * 256 + sub * 64 + op * 32 + hi * 4;   // output of j = 0, i = 0
       // token operand of input step ks, token tile tp: row tp*32 + lr, source
       // granule ks*2 + hi, stored at granule (ks*2 + hi) ^ (lr % 16); the
       // swizzle acts on the offset within the buffer, which starts at xbase
@@ -699,15 +681,10 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
       };
       f32x16 acc[2];   // [token tile]
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_fbias[jb][g][op * 32 + j * 8 + hi * 4]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            acc[v][j * 4 + 2 * k] = __uint_as_float(bias.v[j][k] << 16);
-            acc[v][j * 4 + 2 * k + 1] = __uint_as_float(bias.v[j][k] & 0xFFFF0000u);
-          }
-        }
+        for (int q = 0; q < 4; ++q) acc[0][j * 4 + q] = acc[1][j * 4 + q] = b4[q];
       }
       u32x4 xv[16][2];
 #pragma unroll
@@ -736,10 +713,7 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
           uint2 w2;
           w2.x = f32x2_to_bf16x2(acc[v][j * 4 + 0], acc[v][j * 4 + 1]);
           w2.y = f32x2_to_bf16x2(acc[v][j * 4 + 2], acc[v][j * 4 + 3]);
-          *reinterpret_cast<uint2*>(&s_raw[jb][1 + g][tr][(op * 32 + j * 8 + hi * 4) * 2]) = w2;
-          if (gout != nullptr && tr < valid) {
-            *reinterpret_cast<uint2*>(gout + (t.rowbase + t.t0 + tr) * W + o + j * 8) = w2;
-          }
+          *reinterpret_cast<uint2*>(&s_raw[jb][1 + g][tr][((op * 8 + j * 2 + hi) ^ ((tr >> 1) & 15)) * 8]) = w2;
         }
       }
     }
@@ -754,6 +728,7 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
       __builtin_amdgcn_s_setprio(3);
       const int q = wave - PROJ0;
       const int g = q >> 1, op = q & 1;
+      const uint16_t* wf = g ? p.wt[1] : p.wt[0];
       for (int i = 0;; ++i) {
         lds_wait<false, kHelperSleep>(&s_tk_valid, i, &s_abort, p.hdr);
         if (lds_load(&s_abort) != 0) break;
@@ -762,19 +737,18 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
         const Tile t = tile_of(tile);
         const int jb = i & 1;
         const int kb = t.strip >> 2, sub = t.strip & 3;
-        // this pass's weights and bias (L2-resident) while the rows land
+        // this pass's weights (L2-resident) while the rows land
         bf16x8 a[16];
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) a[ks] = fused_w_frag(g ? p.wt[1] : p.wt[0], kb, sub, op, ks, lane);
-        const FusedBias fb = fused_bias(g ? p.pbias[1] : p.pbias[0], kb * 256 + sub * 64 + op * 32 + (lane >> 5) * 4);
+        for (int ks = 0; ks < 16; ++ks) a[ks] = fused_w_frag(wf, kb, sub, op, ks, lane);
         lds_wait<false, kHelperSleep>(&s_xb_full[jb], i, &s_abort, p.hdr);
         if (lds_load(&s_abort) != 0) break;
-        project_pass(jb, t, p.L - 1 - t.t0, g, op, a, fb);
+        project_pass(jb, t, p.L - 1 - t.t0, g, op, a);
         lds_release();
         if (lane == 0) lds_add(&s_proj_done[jb], 1);
       }
     }
-  } else   if (wave >= LOAD0) {
+  } else if (wave >= LOAD0) {
     // ------------------------------------------------------------ load waves
     __builtin_amdgcn_s_setprio(3);
     const int j = wave - LOAD0;
@@ -914,6 +888,12 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
           const u32x4 v = *reinterpret_cast<const u32x4*>(&s_xb[j][row][((sub * 8 + gg) ^ (row & 15)) * 8]);
           *reinterpret_cast<u32x4*>(&s_raw[j][0][row][gg * 16]) = v;
         }
+        // and the strip's biases of both gates (zeros without)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const uint16_t* bsrc = g ? p.pbias[1] : p.pbias[0];
+          s_fbias[j][g][lane] = bsrc != nullptr ? bf16_bits_to_f32(bsrc[t.strip * 64 + lane]) : 0.0f;
+        }
       }
       {
         float cs = 0.0f, k2 = 0.0f;
@@ -1034,6 +1014,21 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
         return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][row][(lane & ~1) * 2]);
       } else {
         return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][row][lane * 4]);
+      }
+    };
+    // fused: the lane's dword of gate row wave*TS + k, through the swizzle of
+    // the projection's writes (chunk c of row r at c ^ ((r >> 1) & 15));
+    // row r >> 1 is wave*TS/2 + k/2, so a wave needs TS/2 lane offsets
+    uint32_t gsw[FUSED ? TS / 2 : 1];
+#pragma unroll
+    for (int m = 0; m < (FUSED ? TS / 2 : 1); ++m) {
+      gsw[m] = static_cast<uint32_t>(((lane & ~1) * 2) ^ ((((wave * TS) / 2 + m) & 15) << 3));
+    }
+    auto lds_gate = [=](int b, int q, int k) -> uint32_t {
+      if constexpr (FUSED) {
+        return *reinterpret_cast<const uint32_t*>(&s_raw[b][q][wave * TS + k][0] + gsw[k >> 1]);
+      } else {
+        return lds_raw(b, q, wave * TS + k);
       }
     };
     auto to_f32 = [=](uint32_t r) {
@@ -1204,8 +1199,8 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
         // it. FULL: every step in range and no reset token, so no selects.
         auto gate_step = [&](int k, bool FULL) {
           const float xv = to_f32(lds_raw(cb, 0, wave * TS + k));
-          const float ig = sigmoid_f(to_f32(lds_raw(cb, 1, wave * TS + k)));
-          const float r = sigmoid_f(to_f32(lds_raw(cb, 2, wave * TS + k)));
+          const float ig = sigmoid_f(to_f32(lds_gate(cb, 1, k)));
+          const float r = sigmoid_f(to_f32(lds_gate(cb, 2, k)));
           const float y = k2 * r;
           const float a = __builtin_amdgcn_exp2f(y);
           const float m = __builtin_amdgcn_sqrtf(one_minus_exp2(y, a) * (1.0f + a));
@@ -1257,6 +1252,23 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
           }
 #pragma unroll
           for (int k = 0; k < TS; ++k) replay_step(k, false);
+        }
+        if constexpr (FUSED) {
+          // the logits, when asked for, leave from the wave's own gate rows
+          // before the buffer is released: lane l takes row wave*TS + l/8,
+          // channels 8*(l%8) .. +7 (chunks 2m and 2m + 1, which the rows'
+          // swizzle keeps in one aligned pair, swapped when it is odd)
+          const int rr = lane >> 3, m = lane & 7;
+          const int row = wave * TS + rr;
+          const int f = (row >> 1) & 15;
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            uint16_t* go = g ? p.gout[1] : p.gout[0];
+            if (go == nullptr) continue;
+            u32x4 v = *reinterpret_cast<const u32x4*>(&s_raw[cb][1 + g][row][((2 * m) ^ (f & 14)) * 8]);
+            if (f & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+            if (rr < nvalid) *reinterpret_cast<u32x4*>(go + (tc.rowbase + tc.t0 + row) * W + tc.strip * 64 + m * 8) = v;
+          }
         }
         crm = cutm | (emask << 16);
         s_A[ms][wave][lane] = A;
