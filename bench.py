@@ -187,7 +187,8 @@ def decode(args):
 def main():
     """Fields: metric, value (fwd+bwd ms per step), unit, n_gpus, steps, warmup, ms_per_step,
     higher_is_better, scaling, vs_baseline, dtype, data, config, fwd_ms, bwd_ms, elements_per_s,
-    hbm_frac_fwd, hbm_frac_fwd_bwd, roofline, cpu_baseline."""
+    hbm_frac_fwd, hbm_frac_fwd_bwd, roofline, roofline_fwd, cpu_baseline; with the projections
+    (workloads 4 and 5) also projection and fused_forward."""
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -331,6 +332,28 @@ def main():
     fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
     bwd_ms = [e[2].elapsed_time(e[3]) for e in evs]
     pbwd_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    fused = None
+    if proj:
+        # The fused forward (both projections inside the scan), with and
+        # without the logits as outputs, timed the same way. Its result is
+        # bitwise that of the projection followed by the scan with 64-step tiles.
+        def fused_call(d, gates):
+            glr.rglru_blockdiag_fused_fwd(d["x"], wx, bx, wa, ba, lam, reset, h0, h=d["h"], h_last=d["h_last"],
+                                          ckpt=d["ckpt"], gate_x=d["gxp"] if gates else None,
+                                          gate_a=d["gap"] if gates else None, workspace=d["ws"])
+        fused = {}
+        for gates in (False, True):
+            for i in range(args.warmup):
+                fused_call(sets[i % len(sets)], gates)
+            fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                fev[i][0].record(stream)
+                fused_call(sets[i % len(sets)], gates)
+                fev[i][1].record(stream)
+            torch.cuda.synchronize()
+            fused[gates] = float(np.mean([a.elapsed_time(b) for a, b in fev]))
     err = max(d["ws"].error_bits() for d in sets)
     if err:
         print(f"look-back spin limit reported (error bits {err}); timings invalid", file=sys.stderr)
@@ -429,6 +452,21 @@ def main():
             "bwd_mfma_frac": round(bwd_tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "fwd_algorithmic_bytes": pf_bytes, "bwd_algorithmic_bytes": pb_bytes,
             "fwd_traffic": measured("proj_fwd"), "bwd_traffic": measured("proj_bwd"),
+        }
+        # x read and h written (2 + 2 bytes per element), plus both logits
+        # written when they are outputs
+        fz = fused[False]
+        fzg = fused[True]
+        out["fused_forward"] = {
+            "call": "rglru_blockdiag_fused_fwd (64-step tiles)",
+            "ms": round(fz, 5),
+            "with_logits_ms": round(fzg, 5),
+            "two_call_ms": round(pf + fwd_avg, 5),
+            "algorithmic_bytes": 2 * 2 * N,
+            "with_logits_algorithmic_bytes": 4 * 2 * N,
+            "hbm_frac": round(2 * 2 * N / (fz * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "with_logits_hbm_frac": round(4 * 2 * N / (fzg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(flops / (fz * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         }
     out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
