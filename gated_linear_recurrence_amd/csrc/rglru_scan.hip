@@ -325,6 +325,15 @@ __device__ __forceinline__ bool look_back_round(const u64* slot_a, const u64* sl
                                                 unsigned tag, float init, float& carry) {
   const unsigned lane_bytes = lane * 8u;
   u64 wh[K], wa[K], wb[K];
+  // the nearest predecessor's published carry first: once every channel of
+  // the strip has it, the round needs none of the other words
+  if (npred > 0) {
+    const u64 h1 = poll_at(slot_h + (self_uniform - stride), lane_bytes);
+    if (__builtin_amdgcn_ballot_w64(!tagged(h1, tag)) == 0ull) {
+      carry = __uint_as_float(static_cast<uint32_t>(h1));
+      return true;
+    }
+  }
 #pragma unroll
   for (int d = 0; d < K; ++d) {
     const long long q = self_uniform - static_cast<long long>(d + 1) * stride;
