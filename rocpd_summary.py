@@ -79,12 +79,14 @@ def traffic(fetch_db: str, write_db: str, calib_mib: float):
     return "\n".join(out), per
 
 
-# kernels of each library call (matched on the kernel name)
+# kernels of each library call (matched on the kernel name; the forward's
+# last template argument tells the fused instantiation from the plain scan)
 GROUPS = {
-    "fwd": ("fwd_kernel<",),
-    "bwd": ("bwd_kernel<", "bwd_dlam_kernel("),
-    "proj_fwd": ("proj_fwd_kernel(",),
-    "proj_bwd": ("proj_dw_kernel(", "proj_dw_reduce_kernel(", "proj_dx_kernel<"),
+    "fwd": lambda n: "fwd_kernel<" in n and not n.endswith(", true>(FwdArgs)"),
+    "bwd": lambda n: "bwd_kernel<" in n or "bwd_dlam_kernel(" in n,
+    "proj_fwd": lambda n: "proj_fwd_kernel(" in n,
+    "proj_bwd": lambda n: any(k in n for k in ("proj_dw_kernel(", "proj_dw_reduce_kernel(", "proj_dx_kernel<")),
+    "fused_fwd": lambda n: ("fwd_kernel<" in n and n.endswith(", true>(FwdArgs)")) or "w_frag_kernel(" in n,
 }
 
 
@@ -96,8 +98,8 @@ def traffic_json(fetch_db: str, write_db: str, calib_mib: float, workload: str, 
             doc = json.load(f)
     except FileNotFoundError:
         doc = {}
-    for group, keys in GROUPS.items():
-        names = [n for n in per if any(k in n for k in keys)]
+    for group, match in GROUPS.items():
+        names = [n for n in per if match(n)]
         if not names:
             continue
         rb = sum(per[n]["read_bytes"] for n in names)
