@@ -36,6 +36,8 @@
 // taken in chunk order from an atomic ticket, so every tile a workgroup waits
 // on belongs to a workgroup that is running or done.
 #include <hip/hip_runtime.h>
+
+#include <cstring>
 #include <stddef.h>
 #include <stdint.h>
 #include <math.h>
@@ -2223,9 +2225,11 @@ bool shape_ok(const rglru_shape_t* s) {
     default: return false;
   }
   // index arithmetic limits: batch and width fit int, tile counts fit 32 bits
-  if (s->batch > (1LL << 24) || s->width > (1LL << 24)) return false;
-  const long long strips = ceil_div(s->width, 64);
-  const long long tiles = strips * s->batch * ceil_div(s->length, 8);
+  // (each factor bounded before the product, so none of it can overflow)
+  if (s->batch > (1LL << 24) || s->width > (1LL << 24) || s->length > (1LL << 34)) return false;
+  const long long rows = ceil_div(s->width, 64) * s->batch;   // < 2^43
+  if (rows >= (1LL << 31)) return false;
+  const long long tiles = rows * ceil_div(s->length, 8);       // < 2^62
   if (tiles >= (1LL << 31)) return false;
   return true;
 }
@@ -2866,7 +2870,13 @@ rglru_status_t rglru_blockdiag_fused_fwd(const rglru_shape_t* s, const void* x, 
 }
 
 const char* rglru_status_string(rglru_status_t status) {
-  switch (status) {
+  // A C caller may pass any int; in C++ an enum object holding a value
+  // outside its enumerators' range may not be read as the enum, so its
+  // bits are read as an int.
+  int v = 0;
+  static_assert(sizeof(status) == sizeof(v), "the status enum has the size of int");
+  std::memcpy(&v, &status, sizeof(v));
+  switch (v) {
     case RGLRU_OK: return "RGLRU_OK";
     case RGLRU_ERR_INVALID_ARGUMENT: return "RGLRU_ERR_INVALID_ARGUMENT: bad shape, NULL required pointer or bad enum";
     case RGLRU_ERR_MISALIGNED: return "RGLRU_ERR_MISALIGNED: a pointer is not aligned to its element size";
