@@ -82,6 +82,10 @@ typedef enum {
   RGLRU_ERR_SCRATCH_TOO_SMALL = 6  /* rglru_fwd_scratch: the shape needs more than RGLRU_SCRATCH_BYTES */
 } rglru_status_t;
 
+/* Size limits (beyond them RGLRU_ERR_INVALID_ARGUMENT, and size queries
+ * return 0): B <= 2^24, W <= 2^24, L <= 2^34, and ceil(W / 64) * B *
+ * ceil(L / 8) < 2^31 (the count of 64-channel, 8-step units indexed in 32
+ * bits). */
 typedef struct {
   int64_t batch;    /* B >= 1 */
   int64_t length;   /* L >= 1 */
