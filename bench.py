@@ -200,6 +200,9 @@ def main():
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a known-size "
                          "reference for hardware traffic counters)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="with the default workload, skip the long-sequence and projection workloads "
+                         "measured after it")
     ap.add_argument("--decode", action="store_true",
                     help="instead: decode-step latency (L = 1, h0 in, h_last out) through the "
                          "allocation-free forward, eager and replayed from a HIP graph")
@@ -218,15 +221,36 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    out = run_workload(args, args.workload, args.steps, args.warmup, True)
+    if args.workload == 1 and not args.no_other_workloads:
+        # The long-sequence shape and the pages' measured scope (projections
+        # in the step, and the fused forward), measured in the same run;
+        # reported beside the headline, which they do not change.
+        import torch
+        other = {}
+        for wid in (3, 5):
+            torch.cuda.empty_cache()
+            o = run_workload(args, wid, 20, 3, False)
+            keep = ("config", "value", "fwd_ms", "bwd_ms", "hbm_frac_fwd", "hbm_frac_fwd_bwd", "projection",
+                    "fused_forward")
+            other[o["config"]["workload"]] = {k: o[k] for k in keep if k in o}
+            other[o["config"]["workload"]]["roofline_frac_bwd"] = o["roofline"]["frac"]
+            other[o["config"]["workload"]]["roofline_frac_fwd"] = o["roofline_fwd"]["frac"]
+        out["other_workloads"] = other
+    print(json.dumps(out), flush=True)
+
+
+def run_workload(args, wid, steps, warmup, with_cpu):
+    """Measures one synth workload: its bench JSON object."""
     import numpy as np
 
     import synth
 
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[wid]
     chunk = wl.chunk if args.chunk is None else args.chunk
     inp = synth.make_inputs(wl)
     # the oracle's pool is forked, so it runs before the GPU is touched
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, inp)
+    cpu = None if (args.no_cpu_baseline or not with_cpu) else cpu_baseline(wl, inp)
 
     import torch
 
@@ -307,7 +331,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
@@ -317,15 +341,15 @@ def main():
     # out of this pass.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # Per-call durations (the roofline figures): the same steps again, each
     # library call bracketed by events recorded on the launch stream.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
     pfwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
@@ -343,12 +367,12 @@ def main():
                                           gate_a=d["gap"] if gates else None, workspace=d["ws"])
         fused = {}
         for gates in (False, True):
-            for i in range(args.warmup):
+            for i in range(warmup):
                 fused_call(sets[i % len(sets)], gates)
             fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.steps)]
+                   for _ in range(steps)]
             torch.cuda.synchronize()
-            for i in range(args.steps):
+            for i in range(steps):
                 fev[i][0].record(stream)
                 fused_call(sets[i % len(sets)], gates)
                 fev[i][1].record(stream)
@@ -359,7 +383,7 @@ def main():
         print(f"look-back spin limit reported (error bits {err}); timings invalid", file=sys.stderr)
         sys.exit(3)
 
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     fwd_avg = float(np.mean(fwd_ms))
     bwd_avg = float(np.mean(bwd_ms))
     fb = FWD_BYTES_PER_ELEM[wl.io] * N
@@ -385,8 +409,8 @@ def main():
         "value": round(ms_per_step, 5),
         "unit": "ms",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": False,
         "scaling": "weak",
@@ -395,7 +419,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs and logits, decay U[0.9,0.999]; no datasets)",
         "config": {"workload": wl.name, "batch": B, "length": L, "width": W, "io": wl.io,
                    "chunk": chunk or "library default (forward 128 steps, backward 64)", "resets": wl.doc_mean is not None, "h0": wl.h0,
-                   "step": "rglru_fwd + rglru_bwd"},
+                   "step": ("rglru_blockdiag_gate_proj_fwd + rglru_fwd + rglru_bwd + rglru_blockdiag_gate_proj_bwd"
+                            if proj else "rglru_fwd + rglru_bwd")},
         "fwd_ms": round(fwd_avg, 5),
         "bwd_ms": round(bwd_avg, 5),
         "fwd_plus_bwd_ms": round(fwd_avg + bwd_avg, 5),
@@ -441,6 +466,8 @@ def main():
         pbk = float(np.mean(pbwd_ms))
         fwd_tf = flops / (pf * 1e-3) / 1e12
         bwd_tf = 2 * flops / (pbk * 1e-3) / 1e12
+        # the whole step's algorithmic bytes (scan and projections) over its time
+        out["hbm_frac_fwd_bwd"] = round((fb + bb + pf_bytes + pb_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         out["projection"] = {
             "fwd_ms": round(pf, 5), "bwd_ms": round(pbk, 5),
             "fwd_gbs": round(pf_bytes / (pf * 1e-3) / 1e9, 1), "bwd_gbs": round(pb_bytes / (pbk * 1e-3) / 1e9, 1),
@@ -469,7 +496,9 @@ def main():
             "mfma_frac": round(flops / (fz * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         }
     out["cpu_baseline"] = cpu
-    print(json.dumps(out), flush=True)
+    return out
+
+
 
 
 if __name__ == "__main__":
