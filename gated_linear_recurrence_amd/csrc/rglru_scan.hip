@@ -321,27 +321,55 @@ __device__ __forceinline__ void advance_call(Header* hdr) {
 // 32-bit lane offset); `stride` is the slot distance between consecutive
 // predecessors, `npred` how many exist. Returns whether this lane's carry was
 // found (it is then in `carry`).
-template <int K>
+template <int K, bool EARLY_OUT>
 __device__ __forceinline__ bool look_back_round(const u64* slot_a, const u64* slot_b, const u64* slot_h,
                                                 long long self_uniform, unsigned lane, long long stride, int npred,
                                                 unsigned tag, float init, float& carry) {
   const unsigned lane_bytes = lane * 8u;
   u64 wh[K], wa[K], wb[K];
-  // the nearest predecessor's published carry first: once every channel of
-  // the strip has it, the round needs none of the other words
-  if (npred > 0) {
-    const u64 h1 = poll_at(slot_h + (self_uniform - stride), lane_bytes);
-    if (__builtin_amdgcn_ballot_w64(!tagged(h1, tag)) == 0ull) {
-      carry = __uint_as_float(static_cast<uint32_t>(h1));
-      return true;
+  if constexpr (!EARLY_OUT) {
+    // the nearest predecessor's published carry first: once every channel
+    // of the strip has it, the round needs none of the other words
+    if (npred > 0) {
+      const u64 h1 = poll_at(slot_h + (self_uniform - stride), lane_bytes);
+      if (__builtin_amdgcn_ballot_w64(!tagged(h1, tag)) == 0ull) {
+        carry = __uint_as_float(static_cast<uint32_t>(h1));
+        return true;
+      }
     }
-  }
 #pragma unroll
-  for (int d = 0; d < K; ++d) {
-    const long long q = self_uniform - static_cast<long long>(d + 1) * stride;
-    wh[d] = d < npred ? poll_at(slot_h + q, lane_bytes) : 0ull;
-    wa[d] = d < npred ? poll_at(slot_a + q, lane_bytes) : 0ull;
-    wb[d] = d < npred ? poll_at(slot_b + q, lane_bytes) : 0ull;
+    for (int d = 0; d < K; ++d) {
+      const long long q = self_uniform - static_cast<long long>(d + 1) * stride;
+      wh[d] = d < npred ? poll_at(slot_h + q, lane_bytes) : 0ull;
+      wa[d] = d < npred ? poll_at(slot_a + q, lane_bytes) : 0ull;
+      wb[d] = d < npred ? poll_at(slot_b + q, lane_bytes) : 0ull;
+    }
+  } else {
+    // The same first poll; then, without the nearest predecessor's carry and
+    // map no channel can get further this round, so the farther words are
+    // read only when some channel has that map (fewer words polled, one more
+    // round trip when the map is there but the carry is not).
+    if (npred > 0) {
+      const long long q0 = self_uniform - stride;
+      wh[0] = poll_at(slot_h + q0, lane_bytes);
+      if (__builtin_amdgcn_ballot_w64(!tagged(wh[0], tag)) == 0ull) {
+        carry = __uint_as_float(static_cast<uint32_t>(wh[0]));
+        return true;
+      }
+      wa[0] = poll_at(slot_a + q0, lane_bytes);
+      wb[0] = poll_at(slot_b + q0, lane_bytes);
+      const bool stuck = !tagged(wh[0], tag) && !(tagged(wa[0], tag) && tagged(wb[0], tag));
+      if (__builtin_amdgcn_ballot_w64(!stuck) == 0ull) return false;
+    } else {
+      wh[0] = wa[0] = wb[0] = 0ull;
+    }
+#pragma unroll
+    for (int d = 1; d < K; ++d) {
+      const long long q = self_uniform - static_cast<long long>(d + 1) * stride;
+      wh[d] = d < npred ? poll_at(slot_h + q, lane_bytes) : 0ull;
+      wa[d] = d < npred ? poll_at(slot_a + q, lane_bytes) : 0ull;
+      wb[d] = d < npred ? poll_at(slot_b + q, lane_bytes) : 0ull;
+    }
   }
   int start = -1;
   int kind = 0;     // 1: published carry, 2: map with a reset, 3: sequence start
@@ -384,12 +412,14 @@ __device__ __forceinline__ bool look_back_round(const u64* slot_a, const u64* sl
 
 // Rounds until the carry is found; false if the spin limit was reached (the
 // carry is then 0).
-template <int K>
+template <int K, bool EARLY_OUT>
 __device__ __forceinline__ bool look_back_wave(const u64* slot_a, const u64* slot_b, const u64* slot_h,
                                                long long self_uniform, unsigned lane, long long stride, int npred,
                                                unsigned tag, float init, float& carry) {
   for (unsigned round = 0; round < kSpinLimit; ++round) {
-    if (look_back_round<K>(slot_a, slot_b, slot_h, self_uniform, lane, stride, npred, tag, init, carry)) return true;
+    if (look_back_round<K, EARLY_OUT>(slot_a, slot_b, slot_h, self_uniform, lane, stride, npred, tag, init, carry)) {
+      return true;
+    }
     __builtin_amdgcn_s_sleep(kLookBackSleep);
   }
   carry = 0.0f;
@@ -959,7 +989,7 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
       float carry = init;
       bool found = true;
       if (t.active && t.chunk > 0) {
-        found = look_back_round<K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tile) * 64,
+        found = look_back_round<K, false>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tile) * 64,
                                    static_cast<unsigned>(lane), static_cast<long long>(rows) * 64, t.chunk, tag, init,
                                    carry);
       }
@@ -998,7 +1028,7 @@ __global__ __launch_bounds__((NW + (FUSED ? 8 : 4)) * 64) void fwd_kernel(FwdArg
             publish(p.slot_a, sidx, tag, encode_a(GA, GR));
             publish(p.slot_b, sidx, tag, __float_as_uint(GB));
           }
-          if (!look_back_wave<K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tile) * 64,
+          if (!look_back_wave<K, false>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tile) * 64,
                                  static_cast<unsigned>(lane), static_cast<long long>(rows) * 64, t.chunk, tag, init,
                                  carry)) {
             atomicOr(&p.hdr->err, 1u);
@@ -1778,7 +1808,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
       float carry = init;
       bool found = true;
       if (tc.active && !latest) {
-        found = look_back_round<K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tc.id) * 64,
+        found = look_back_round<K, true>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tc.id) * 64,
                                    static_cast<unsigned>(lane), -static_cast<long long>(rows) * 64,
                                    p.n_chunks - 1 - tc.chunk, tag, init, carry);
       }
@@ -1813,7 +1843,7 @@ __global__ __launch_bounds__((NW + 4) * 64) void bwd_kernel(BwdArgs p) {
             publish(p.slot_a, sidx, tag, encode_a(GA, GR));
             publish(p.slot_b, sidx, tag, __float_as_uint(GB));
           }
-          if (!look_back_wave<K>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tc.id) * 64,
+          if (!look_back_wave<K, true>(p.slot_a, p.slot_b, p.slot_h, static_cast<long long>(tc.id) * 64,
                                  static_cast<unsigned>(lane), -static_cast<long long>(rows) * 64,
                                  p.n_chunks - 1 - tc.chunk, tag, init, carry)) {
             atomicOr(&p.hdr->err, 1u);
