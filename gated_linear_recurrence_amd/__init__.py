@@ -1,4 +1,4 @@
-"""MI355X (gfx950) RG-LRU: HIP kernels behind a C ABI (include/rglru.h) and this thin binding."""
+"""MI355X (gfx950) RG-LRU and gated delta rule: HIP kernels behind a C ABI (include/*.h) and this thin binding."""
 from . import _lib
 from ._lib import RglruError, header_symbols  # noqa: F401
 from .ops import (  # noqa: F401
@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     rglru_blockdiag_gate_proj_fwd,
     rglru_bwd,
     rglru_bwd_workspace_bytes,
+    rglru_delta_rule_fwd,
     rglru_ckpt_elems,
     rglru_fwd,
     rglru_fwd_scratch,

@@ -1,4 +1,4 @@
-"""ctypes view of librglru.so: the C ABI of include/rglru.h, nothing more.
+"""ctypes view of librglru.so: the C ABI of include/*.h, nothing more.
 
 The library is loaded from this package directory only. If it is missing, every
 entry point raises: there is no fallback implementation.
@@ -12,7 +12,8 @@ from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_uint8,
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "librglru.so")
-HEADER_PATH = os.path.join(os.path.dirname(PKG), "include", "rglru.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(PKG), "include")
+HEADER_PATH = os.path.join(INCLUDE_DIR, "rglru.h")
 
 RGLRU_IO_F32 = 0
 RGLRU_IO_BF16 = 1
@@ -30,6 +31,25 @@ class rglru_shape_t(ctypes.Structure):
         ("chunk", c_int32),
         ("c", c_float),
         ("reserved", c_int32),
+    ]
+
+
+RGLRU_DELTA_GDN = 0
+RGLRU_DELTA_KDA = 1
+
+
+class rglru_delta_shape_t(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_int64),
+        ("length", c_int64),
+        ("k_heads", c_int32),
+        ("v_heads", c_int32),
+        ("k_dim", c_int32),
+        ("v_dim", c_int32),
+        ("io_dtype", c_int32),
+        ("decay", c_int32),
+        ("state_v_first", c_int32),
+        ("scale", c_float),
     ]
 
 
@@ -56,6 +76,7 @@ _SIGNATURES = {
                                  _vp, _vp, c_size_t, _vp]),
     "rglru_bwd_varlen": (c_int, [POINTER(rglru_shape_t), _vp, c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, c_size_t, _vp]),
+    "rglru_delta_rule_fwd": (c_int, [POINTER(rglru_delta_shape_t), _vp, c_int64] + [_vp] * 9),
     "rglru_status_string": (ctypes.c_char_p, [c_int]),
     "rglru_abi_version": (c_int, []),
 }
@@ -64,9 +85,12 @@ _lib = None
 
 
 def header_symbols() -> list:
-    """Names of the functions include/rglru.h declares."""
-    with open(HEADER_PATH) as f:
-        text = f.read()
+    """Names of the functions the headers under include/ declare."""
+    text = ""
+    for name in sorted(os.listdir(INCLUDE_DIR)):
+        if name.endswith(".h"):
+            with open(os.path.join(INCLUDE_DIR, name)) as f:
+                text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(rglru_[a-z0-9_]+)\s*\(", text)))
 

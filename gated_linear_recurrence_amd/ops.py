@@ -452,3 +452,55 @@ class _RGLRU(torch.autograd.Function):
 def rglru(x, gate_x, gate_a, lam, h0=None, reset=None, *, chunk: int = 0, c: float = 8.0):
     """Differentiable RG-LRU scan: returns (h, h_last). Gradients flow to x, gate_x, gate_a, lambda and h0."""
     return _RGLRU.apply(x, gate_x, gate_a, lam, h0, reset, chunk, c)
+
+
+def rglru_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
+                         scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
+                         cu_seqlens: Optional[torch.Tensor] = None, state_v_first: bool = False,
+                         output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                         final_state: Optional[torch.Tensor] = None):
+    """Gated delta rule forward, token recurrence (GDN when g is [B, T, Hv], KDA when [B, T, Hv, Dk]).
+
+    q, k [B, T, Hk, Dk] and v [B, T, Hv, Dv] in bfloat16 or float32 (one dtype);
+    g, beta float32; states float32 [N, Hv, Dk, Dv] ([N, Hv, Dv, Dk] with
+    state_v_first), N = B, or the number of sequences when cu_seqlens (int32
+    [N + 1], B = 1) packs them. scale defaults to 1 / sqrt(Dk).
+    Returns (o [B, T, Hv, Dv], final state or None).
+    """
+    lib = _lib.load()
+    dev = q.device
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, D]")
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    io = q.dtype
+    if io not in _IO:
+        raise ValueError(f"unsupported dtype {io}")
+    _need(q, "q", (B, T, Hk, Dk), io, dev)
+    _need(k, "k", (B, T, Hk, Dk), io, dev)
+    _need(v, "v", (B, T, Hv, Dv), io, dev)
+    kda = g.dim() == 4
+    _need(g, "g", (B, T, Hv, Dk) if kda else (B, T, Hv), torch.float32, dev)
+    _need(beta, "beta", (B, T, Hv), torch.float32, dev)
+    n = B
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be [N + 1]")
+        n = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", (n + 1,), torch.int32, dev)
+    sshape = (n, Hv, Dv, Dk) if state_v_first else (n, Hv, Dk, Dv)
+    _opt(initial_state, "initial_state", sshape, torch.float32, dev)
+    o = torch.empty_like(v) if o is None else _need(o, "o", (B, T, Hv, Dv), io, dev)
+    if output_final_state:
+        final_state = (torch.empty(sshape, dtype=torch.float32, device=dev) if final_state is None
+                       else _need(final_state, "final_state", sshape, torch.float32, dev))
+    else:
+        final_state = None
+    sc = (1.0 / float(Dk) ** 0.5) if scale is None else float(scale)
+    shape = _lib.rglru_delta_shape_t(B, T, Hk, Hv, Dk, Dv, _IO[io],
+                                     _lib.RGLRU_DELTA_KDA if kda else _lib.RGLRU_DELTA_GDN,
+                                     int(bool(state_v_first)), sc)
+    st = lib.rglru_delta_rule_fwd(ctypes.byref(shape), _ptr(cu_seqlens), n, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state), _stream(dev))
+    _lib.check(st, "rglru_delta_rule_fwd")
+    return o, final_state

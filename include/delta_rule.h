@@ -1,0 +1,81 @@
+/* Gated delta rule forward (GDN and KDA), token-recurrent form, on gfx950.
+ *
+ * The operation is the one the linear_attention reference page
+ * (modelopt.torch.quantization.linear_attention.reference) names
+ * recurrent_delta_rule_reference: GDN (one decay per value head) or KDA (one
+ * decay per key channel), natural-log gates, inputs already normalized, an
+ * optional initial state, packed sequences through cu_seqlens, and the output
+ * together with the final state. For value head h (key head h / (Hv / Hk))
+ * and each token t, with S the [Dk, Dv] state:
+ *
+ *     S   <- diag(exp(g_t)) S                  (GDN: exp(g_t) S)
+ *     S   <- S + k_t (beta_t (v_t - S^T k_t))^T
+ *     o_t  = scale S^T q_t
+ *
+ * The state is carried in float32; q, k, v and o are float32 or bf16.
+ */
+#ifndef RGLRU_DELTA_RULE_H_
+#define RGLRU_DELTA_RULE_H_
+
+#include "rglru.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RGLRU_DELTA_GDN = 0,  /* g [.., Hv]: one decay per value head and token */
+  RGLRU_DELTA_KDA = 1   /* g [.., Hv, Dk]: one decay per key channel, value head and token */
+} rglru_delta_decay_t;
+
+/* Limits beyond which the call returns RGLRU_ERR_INVALID_ARGUMENT:
+ * batch, length >= 0 with batch * length < 2^40; 1 <= k_heads <= v_heads <
+ * 2^16 with v_heads a multiple of k_heads; 1 <= k_dim, v_dim <= 2^16; finite
+ * scale; state_v_first 0 or 1; and n_seqs * v_heads * ceil(v_dim / 16) <
+ * 2^31 (the workgroups of one call). Within them, k_dim > 256, or k_dim or
+ * v_dim not a multiple of 8, is RGLRU_ERR_UNSUPPORTED. */
+typedef struct {
+  int64_t batch;          /* B; 1 with cu_seqlens */
+  int64_t length;         /* T tokens per batch row (with cu_seqlens: all tokens) */
+  int32_t k_heads;        /* Hk, heads of q and k */
+  int32_t v_heads;        /* Hv, heads of v, g, beta, o and the state */
+  int32_t k_dim;          /* Dk */
+  int32_t v_dim;          /* Dv */
+  int32_t io_dtype;       /* rglru_io_t of q, k, v and o */
+  int32_t decay;          /* rglru_delta_decay_t */
+  int32_t state_v_first;  /* 0: states [N, Hv, Dk, Dv]; 1: [N, Hv, Dv, Dk] */
+  float scale;            /* read-out scale (the reference's default is 1 / sqrt(Dk)) */
+} rglru_delta_shape_t;
+
+/* Forward of the gated delta rule over every token, on `stream` (a
+ * hipStream_t; NULL = the null stream). All pointers are device memory,
+ * owned by the caller, dense row-major:
+ *
+ *   cu_seqlens : NULL (B independent rows of T tokens, N = B) or [n_seqs + 1]
+ *                int32 with 0 = cu[0] <= ... <= cu[n_seqs] = T and B = 1
+ *                (N = n_seqs packed sequences, 1 <= n_seqs < 2^30). Offsets
+ *                are read on the device and clamped into [0, T], so invalid
+ *                offsets give unspecified but in-bounds results.
+ *   q, k       : [B, T, Hk, Dk] io, 16-byte aligned.
+ *   v, o       : [B, T, Hv, Dv] io, 16-byte aligned; o is written.
+ *   g          : float32 natural-log decays, [B, T, Hv] (GDN, 4-byte aligned)
+ *                or [B, T, Hv, Dk] (KDA, 16-byte aligned).
+ *   beta       : [B, T, Hv] float32 write strengths.
+ *   h0         : NULL (zero initial states) or [N, Hv, Dk, Dv] float32
+ *                ([N, Hv, Dv, Dk] with state_v_first).
+ *   h_last     : NULL or the final states, same layout as h0; a sequence with
+ *                no tokens gets its initial state.
+ * q, k, v, g, beta and o may be NULL only when B * T = 0. Returns
+ * RGLRU_ERR_INVALID_ARGUMENT, RGLRU_ERR_MISALIGNED or RGLRU_ERR_UNSUPPORTED
+ * without launching anything, RGLRU_ERR_HIP if the launch fails. Outputs
+ * must not overlap inputs. */
+rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* shape, const int32_t* cu_seqlens,
+                                    int64_t n_seqs, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const float* h0, void* o,
+                                    float* h_last, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* RGLRU_DELTA_RULE_H_ */
