@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (the published figure counts packed FMA)
 METRIC = "RG-LRU fwd & fwd+bwd ms + % HBM peak, B=4 L=2048 W=2048 bf16"
 FWD_BYTES_PER_ELEM = {"bf16": 8, "f32": 16}    # read x, gate_x, gate_a; write h
 BWD_BYTES_PER_ELEM = {"bf16": 14, "f32": 28}   # read x, gate_x, gate_a, dh; write dx, dgate_x, dgate_a
@@ -206,7 +207,17 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="instead: decode-step latency (L = 1, h0 in, h_last out) through the "
                          "allocation-free forward, eager and replayed from a HIP graph")
+    ap.add_argument("--delta-only", action="store_true",
+                    help="instead: only the gated delta rule workloads (one JSON object per workload)")
     args = ap.parse_args()
+
+    if args.delta_only:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        for w in (10, 11, 12):
+            print(json.dumps(run_delta(args, w, args.steps, args.warmup)), flush=True)
+        return
 
     if args.decode:
         if args.gpus != 1:
@@ -237,7 +248,118 @@ def main():
             other[o["config"]["workload"]]["roofline_frac_bwd"] = o["roofline"]["frac"]
             other[o["config"]["workload"]]["roofline_frac_fwd"] = o["roofline_fwd"]["frac"]
         out["other_workloads"] = other
+        torch.cuda.empty_cache()
+        out["delta_rule"] = {str(w): run_delta(args, w, 20, 3) for w in (10, 11, 12)}
     print(json.dumps(out), flush=True)
+
+
+def delta_cpu_baseline(inp, seconds_target=2.0):
+    """The float64 oracle (untuned, one thread) on a bounded sample of a delta-rule workload:
+    one (batch row, value head) pair over up to 256 tokens, repeated for about
+    seconds_target, scaled to the whole workload's (row, head, token) count."""
+    import numpy as np
+
+    import oracle
+
+    wl = inp.wl
+    T = min(wl.length, 256)
+    kh = 0
+    sl = lambda st: st.value[:1, :T, kh:kh + 1]
+    g = inp.g[:1, :T, :1].astype(np.float64)
+    beta = inp.beta[:1, :T, :1].astype(np.float64)
+    h0 = None if inp.h0 is None else inp.h0[:1, :1]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrent_delta_rule(sl(inp.q), sl(inp.k), inp.v.value[:1, :T, :1], g, beta, initial_state=h0)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds_target:
+            break
+    per_token_head = el / reps / T
+    total = per_token_head * wl.batch * wl.length * wl.v_heads
+    return {
+        "value": round(total * 1e3, 3), "unit": "ms", "cores": 1, "kind": "oracle",
+        "sample": f"one (row, head) pair over {T} tokens, {reps} passes in {el:.1f} s, scaled to "
+                  f"{wl.batch} x {wl.length} x {wl.v_heads} (row, token, head) steps",
+    }
+
+
+def run_delta(args, wid, steps, warmup):
+    """Gated delta rule forward (rglru_delta_rule_fwd) on one delta workload: its JSON object.
+
+    Rotates through enough copies of the inputs and outputs to exceed the
+    Infinity Cache; the events bracket `steps` back-to-back calls on the
+    launch stream (one kernel launch per call)."""
+    import numpy as np
+    import torch
+
+    import gated_linear_recurrence_amd as glr
+    from synth import delta as sd
+
+    wl = sd.DELTA_WORKLOADS[wid]
+    inp = sd.make_delta_inputs(wl)
+    cpu = None if args.no_cpu_baseline else delta_cpu_baseline(inp)
+    glr.load_library()
+    dev = torch.device("cuda:0")
+
+    def io(st):
+        t = torch.from_numpy(np.ascontiguousarray(st.raw)).to(dev)
+        return t.view(torch.bfloat16) if st.io == "bf16" else t
+
+    base = dict(q=io(inp.q), k=io(inp.k), v=io(inp.v), g=torch.from_numpy(inp.g).to(dev),
+                beta=torch.from_numpy(inp.beta).to(dev))
+    h0 = None if inp.h0 is None else torch.from_numpy(inp.h0).to(dev)
+    B, T, Hv, Dk, Dv = wl.batch, wl.length, wl.v_heads, wl.k_dim, wl.v_dim
+    es = 2 if wl.io == "bf16" else 4
+    state_bytes = B * Hv * Dk * Dv * 4
+    nbytes = (B * T * wl.k_heads * Dk * 2 * es + B * T * Hv * Dv * 2 * es
+              + B * T * Hv * (Dk if wl.kda else 1) * 4 + B * T * Hv * 4
+              + state_bytes * (2 if h0 is not None else 1))
+    n_sets = max(2, int(np.ceil(600e6 / max(nbytes, 1))))
+    n_sets = min(n_sets, 8)
+    sets = []
+    for _ in range(n_sets):
+        d = {kk: vv.clone() for kk, vv in base.items()}
+        d["o"] = torch.empty_like(d["v"])
+        d["fs"] = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev)
+        d["h0"] = None if h0 is None else h0.clone()
+        sets.append(d)
+    del base
+
+    def call(d):
+        glr.rglru_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
+                                 o=d["o"], final_state=d["fs"])
+
+    for i in range(warmup):
+        call(sets[i % n_sets])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(sets[i % n_sets])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 7 * B * T * Hv * Dk * Dv   # per state element and token: decay, two dot-product FMAs, one write FMA
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del sets
+    torch.cuda.empty_cache()
+    return {
+        "call": "rglru_delta_rule_fwd (token recurrence)",
+        "config": {"workload": wl.name, "batch": B, "length": T, "k_heads": wl.k_heads, "v_heads": Hv,
+                   "k_dim": Dk, "v_dim": Dv, "io": wl.io, "decay": "KDA" if wl.kda else "GDN",
+                   "h0": inp.h0 is not None},
+        "ms": round(ms, 5),
+        "tokens_per_s": B * T / (ms * 1e-3),
+        "roofline": {"kernel": "delta_fwd_kernel", "bound": "alu", "achieved": round(tf, 2),
+                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "launch_ms": round(ms, 5)},
+        "hbm": {"algorithmic_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": cpu,
+    }
 
 
 def run_workload(args, wid, steps, warmup, with_cpu):

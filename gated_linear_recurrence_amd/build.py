@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librglru.so"
 ARCH = "gfx950"
 
-SOURCES = ["rglru_scan.hip", "rglru_proj.hip", "delta_rule.hip"]
+SOURCES = ["rglru_scan.hip", "rglru_proj.hip", "delta_rule.hip", "delta_chunk.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -39,10 +39,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librglru)")
 
 
-def build(verbose: bool = False) -> str:
-    out = os.path.join(PKG, LIB_NAME)
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,6 +48,23 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"librglru build failed:\n{msg}")
     if verbose and msg.strip():
         print(msg)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object (in parallel), then links the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    out = os.path.join(PKG, LIB_NAME)
+    tmp = out + ".tmp"
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[hipcc(), *compile_flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, out)
     return out
 

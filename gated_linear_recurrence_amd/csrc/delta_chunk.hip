@@ -1,0 +1,567 @@
+// Gated delta rule forward, GDN chunk form, on bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+//
+// The chunk algebra of the linear_attention reference page's
+// chunk_gdn_reference (exact up to rounding, one unit-lower-triangular solve
+// per chunk). Within a chunk of C = 64 tokens with in-chunk cumulative log
+// decays Gc and the state S0 entering it:
+//
+//   A    = strictly lower part of diag(beta) (e^{Gc_i - Gc_j}) (K K^T)
+//   T    = (I + A)^{-1}
+//   W    = T diag(beta e^{Gc}) K,   Ut = T diag(beta) V           (the WY operands)
+//   U    = Ut - W S0                                              (corrected writes)
+//   P    = lower part (diagonal included) of (e^{Gc_i - Gc_j}) (Q K^T)
+//   O    = scale (diag(e^{Gc}) Q S0 + P U)
+//   S1   = e^{Gc_last} S0 + (diag(e^{Gc_last - Gc}) K)^T U
+//
+// Two launches. gdn_chunk_prep (one workgroup per chunk and value head, all
+// in parallel) computes Gc, K K^T and Q K^T on MFMA, T by forward
+// substitution in float32 on the vector ALUs, then W and Ut on MFMA, and
+// writes -W, Ut, P, Gc and the decayed K^T to the workspace, each in the
+// layout its consumer reads as MFMA fragments. gdn_chunk_state (one
+// workgroup per value head and 32-column tile of the state, every column of
+// S being independent) walks the chunks in order with its [Dk x 32] float32
+// state tile held in MFMA accumulators: U = Ut + (-W) S0 and Q S0 on MFMA,
+// then O and the state update. Its A operands come from global memory
+// straight into registers, one chunk ahead; only the bf16 copies of the
+// state tile and of U (the B operands) pass through LDS. MFMA operands are bf16 (q, k, v are bf16 already;
+// T, W, Ut, P, U and the state's operand copy are rounded to bf16), every
+// accumulation is float32, and the state itself stays float32.
+//
+// MFMA 32x32x16 lane layout used throughout (lane l, k-block kb = l / 32):
+// A supplies row l % 32, elements k = 8 kb .. 8 kb + 7; B supplies column
+// l % 32, the same k; accumulator register r holds row 8 (r / 4) + 4 kb +
+// r % 4, column l % 32.
+
+#include <hip/hip_runtime.h>
+#include <cmath>
+
+#include "common.h"
+#include "delta_rule.h"
+
+namespace rglru {
+namespace dchunk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kC = 64;  // chunk length
+constexpr int kThreads = 256;
+constexpr int kTP = kC + 8;  // padded row (bf16 elements) of token-indexed LDS tiles
+constexpr int kMaxDv = 256;
+
+struct ChunkArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* g;
+  const float* beta;
+  const float* h0;
+  uint16_t* o;
+  float* h_last;
+  uint16_t* w_ws;  // [B Hv][NC][64][Dk]      bf16, -W
+  uint16_t* u_ws;  // [B Hv][NC][Dv/32][2][64 lanes][16] bf16, Ut in accumulator order
+  uint16_t* p_ws;  // [B Hv][NC][64][64]      bf16, P
+  float* gc_ws;    // [B Hv][NC][64]          float32, Gc
+  uint16_t* kt_ws; // [B Hv][NC][Dk][64]      bf16, (diag(e^{Gc_last - Gc}) K)^T
+  int64_t T;
+  int Hk, Hv, grp, Dv, NC, NV;
+  int n_blocks;
+  int v_first;
+  float scale;
+};
+
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  const int q = n >> 3, r = n & 7, x = id & 7, pos = id >> 3;
+  return x < r ? x * (q + 1) + pos : r * (q + 1) + (x - r) * q + pos;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ uint16_t h16(u32x4 v, int e) {
+  return static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum_step(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// ------------------------------------------------------------------ prep
+
+// One workgroup per (chunk, value head). LDS region r1 holds K and Q (row-major) while K K^T
+// and Q K^T run, then A (for the solve) and the two scaled copies of T.
+template <int DK, int DVM>
+__global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
+  constexpr int KP = DK + 8;
+  constexpr int kKQ = 2 * kC * KP * 2;
+  constexpr int kAT = kC * kC * 4 + 2 * kC * kTP * 2;
+  constexpr int kR1 = kKQ > kAT ? kKQ : kAT;
+  __shared__ __align__(16) unsigned char r1[kR1];
+  __shared__ __align__(16) uint16_t sKt[DK][kTP];
+  __shared__ __align__(16) uint16_t sVt[DVM][kTP];
+  __shared__ float sG[kC], sGc[kC], sBeta[kC];
+  uint16_t(*sK)[KP] = reinterpret_cast<uint16_t(*)[KP]>(r1);
+  uint16_t(*sQ)[KP] = reinterpret_cast<uint16_t(*)[KP]>(r1 + kC * KP * 2);
+  float(*sA)[kC] = reinterpret_cast<float(*)[kC]>(r1);  // row i: A[i][4 t + s] at [s * 16 + t]
+  uint16_t(*sTw)[kTP] = reinterpret_cast<uint16_t(*)[kTP]>(r1 + kC * kC * 4);
+  uint16_t(*sTu)[kTP] = reinterpret_cast<uint16_t(*)[kTP]>(r1 + kC * kC * 4 + kC * kTP * 2);
+
+  const int bid = xcd_remap(blockIdx.x, p.n_blocks);
+  const int c = bid % p.NC;
+  const int bh = bid / p.NC;
+  const int h = bh % p.Hv, b = bh / p.Hv, kh = h / p.grp;
+  const int64_t t0 = (int64_t)c * kC;
+  const int n = (int)(p.T - t0 < kC ? p.T - t0 : kC);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t chunk_id = (int64_t)bh * p.NC + c;
+
+  // stage K and Q (row-major, K also transposed) and V (transposed), zero past the end; the
+  // token index runs fastest across lanes so each transposed 2-byte write fills one row
+  for (int idx = tid; idx < kC * (DK / 8); idx += kThreads) {
+    const int r = idx & (kC - 1), part = idx / kC;
+    u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+    if (r < n) {
+      const int64_t e = (((int64_t)b * p.T + t0 + r) * p.Hk + kh) * DK + part * 8;
+      kv = *reinterpret_cast<const u32x4*>(p.k + e);
+      qv = *reinterpret_cast<const u32x4*>(p.q + e);
+    }
+    *reinterpret_cast<u32x4*>(&sK[r][part * 8]) = kv;
+    *reinterpret_cast<u32x4*>(&sQ[r][part * 8]) = qv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sKt[part * 8 + e][r] = h16(kv, e);
+  }
+  for (int idx = tid; idx < kC * (p.Dv / 8); idx += kThreads) {
+    const int r = idx & (kC - 1), part = idx / kC;
+    u32x4 vv = {0u, 0u, 0u, 0u};
+    if (r < n) vv = *reinterpret_cast<const u32x4*>(p.v + (((int64_t)b * p.T + t0 + r) * p.Hv + h) * p.Dv + part * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sVt[part * 8 + e][r] = h16(vv, e);
+  }
+  if (tid < kC) {
+    const bool ok = tid < n;
+    const int64_t e = ((int64_t)b * p.T + t0 + tid) * p.Hv + h;
+    sBeta[tid] = ok ? p.beta[e] : 0.f;
+    sG[tid] = ok ? p.g[e] : 0.f;
+  }
+  __syncthreads();
+  if (tid < kC) {
+    float acc = 0.f;
+    for (int m = 0; m <= tid; ++m) acc += sG[m];  // in token order, as a running sum
+    sGc[tid] = acc;
+    p.gc_ws[chunk_id * kC + tid] = acc;
+  }
+  __syncthreads();
+
+  // K K^T and Q K^T, one 32x32 tile of each per wave
+  const int ti = wave >> 1, tj = wave & 1;
+  f32x16 akk = {}, aqk = {};
+#pragma unroll
+  for (int ks = 0; ks < DK / 16; ++ks) {
+    const int kof = ks * 16 + (lane >> 5) * 8;
+    const bf16x8 bk = ld8(&sK[tj * 32 + (lane & 31)][kof]);
+    akk = mfma32(ld8(&sK[ti * 32 + (lane & 31)][kof]), bk, akk);
+    aqk = mfma32(ld8(&sQ[ti * 32 + (lane & 31)][kof]), bk, aqk);
+  }
+  __syncthreads();  // K and Q are no longer read: A takes their place
+
+  // A (strictly lower, scaled) to LDS; P (lower with diagonal, scaled) to the workspace
+  {
+    const int j = tj * 32 + (lane & 31);
+    const float gj = sGc[j];
+    uint16_t* pw = p.p_ws + chunk_id * kC * kC;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = ti * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const float dec = expf(sGc[i] - gj);
+      const float a = (j < i) ? sBeta[i] * dec * akk[r] : 0.f;
+      sA[i][(j & 3) * 16 + (j >> 2)] = a;
+      const float pv = (j <= i) ? dec * aqk[r] : 0.f;
+      pw[i * kC + j] = f32_to_bf16(pv);
+    }
+  }
+  __syncthreads();
+
+  // T = (I + A)^{-1} by forward substitution, T[i][j] = [i == j] - sum_{m < i} A[i][m] T[m][j].
+  // Wave w solves columns 16 w .. 16 w + 15; the 4 lanes of a quad share column j, lane s of
+  // the quad holding T[4 t + s][j] (t = 0 .. 15) and summing those terms; a quad sum joins them.
+  {
+    const int j = wave * 16 + (lane >> 2), s = lane & 3;
+    float tr[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) tr[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+      const float4* ar = reinterpret_cast<const float4*>(&sA[i][s * 16]);
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 a = ar[q4];
+        a0 = fmaf(a.x, tr[4 * q4], a0);
+        a1 = fmaf(a.y, tr[4 * q4 + 1], a1);
+        a0 = fmaf(a.z, tr[4 * q4 + 2], a0);
+        a1 = fmaf(a.w, tr[4 * q4 + 3], a1);
+      }
+      float sum = dpp_sum_step<0xB1>(a0 + a1);
+      sum = dpp_sum_step<0x4E>(sum);
+      const float tij = (i == j ? 1.f : 0.f) - sum;
+      if (s == (i & 3)) tr[i >> 2] = tij;
+    }
+    const float bj = sBeta[j], ej = bj * expf(sGc[j]);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int m = 4 * t + s;
+      sTw[m][j] = f32_to_bf16(tr[t] * ej);
+      sTu[m][j] = f32_to_bf16(tr[t] * bj);
+    }
+  }
+  __syncthreads();
+
+  // -W = -(T diag(beta e^Gc)) K  -> w_ws row-major [64][DK]
+  {
+    uint16_t* ww = p.w_ws + chunk_id * kC * DK;
+    for (int tile = wave; tile < 2 * (DK / 32); tile += 4) {
+      const int mi = tile & 1, td = tile >> 1;
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < kC / 16; ++ks) {
+        const int kof = ks * 16 + (lane >> 5) * 8;
+        acc = mfma32(ld8(&sTw[mi * 32 + (lane & 31)][kof]), ld8(&sKt[td * 32 + (lane & 31)][kof]), acc);
+      }
+      const int d = td * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        ww[i * DK + d] = f32_to_bf16(-acc[r]);
+      }
+    }
+  }
+  // Ut = (T diag(beta)) V -> u_ws in accumulator order
+  for (int tile = wave; tile < 2 * p.NV; tile += 4) {
+    const int mi = tile & 1, tv = tile >> 1;
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < kC / 16; ++ks) {
+      const int kof = ks * 16 + (lane >> 5) * 8;
+      acc = mfma32(ld8(&sTu[mi * 32 + (lane & 31)][kof]), ld8(&sVt[tv * 32 + (lane & 31)][kof]), acc);
+    }
+    uint16_t* uw = p.u_ws + (((chunk_id * p.NV + tv) * 2 + mi) * 64 + lane) * 16;
+    u32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = f32x2_to_bf16x2(acc[2 * e], acc[2 * e + 1]);
+      hi[e] = f32x2_to_bf16x2(acc[8 + 2 * e], acc[8 + 2 * e + 1]);
+    }
+    *reinterpret_cast<u32x4*>(uw) = lo;
+    *reinterpret_cast<u32x4*>(uw + 8) = hi;
+  }
+  // (e^{Gc_last - Gc} K)^T -> kt_ws row-major [DK][64]
+  {
+    const float gl = sGc[kC - 1];
+    uint16_t* kw = p.kt_ws + chunk_id * DK * kC;
+    for (int idx = tid; idx < DK * 8; idx += kThreads) {
+      const int d = idx >> 3, part = idx & 7;
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(&sKt[d][part * 8]);
+      u32x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = part * 8 + 2 * e;
+        out[e] = f32x2_to_bf16x2(bf16_bits_to_f32(kv[e] & 0xFFFFu) * expf(gl - sGc[m]),
+                                 bf16_bits_to_f32(kv[e] >> 16) * expf(gl - sGc[m + 1]));
+      }
+      *reinterpret_cast<u32x4*>(kw + d * kC + part * 8) = out;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ state pass
+
+// Operands of one chunk for one wave, loaded from global memory straight into MFMA fragment
+// registers (lane l: row l % 32 of its tile, 8 consecutive k at 8 (l / 32)).
+template <int DK>
+struct ChunkOps {
+  u32x4 a[DK / 16];  // U waves: rows of -W; O waves: rows of Q
+  u32x4 pk[4];       // O waves: rows of P
+  u32x4 kt[4];       // state owners: rows of the decayed K^T
+  u32x4 u[2];        // U waves: U~ in accumulator order
+  float4 gc[4];      // O waves: Gc of the accumulator rows
+  float glast;
+};
+
+// One workgroup per (value head, 32-column tile of the state); waves 0 and 1 compute the
+// corrected writes U for token rows 0-31 and 32-63, waves 2 and 3 the outputs of those rows,
+// and wave w < Dk / 32 owns state rows 32 w .. 32 w + 31.
+template <int DK>
+__global__ __launch_bounds__(kThreads) void gdn_chunk_state(ChunkArgs p) {
+  constexpr int KP = DK + 8;
+  constexpr int ST = DK / 32;
+  constexpr int KS = DK / 16;
+  __shared__ __align__(16) uint16_t sS[32][KP];   // bf16 state tile, [column][key]
+  __shared__ __align__(16) uint16_t sU[32][kTP];  // bf16 U, [column][token]
+
+  const int bid = xcd_remap(blockIdx.x, p.n_blocks);
+  const int tv = bid % p.NV;
+  const int bh = bid / p.NV;
+  const int h = bh % p.Hv, b = bh / p.Hv, kh = h / p.grp;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = tv * 32 + (lane & 31);
+  const int kb8 = (lane >> 5) * 8;
+  const int ti = wave & 1;
+  const bool uwave = wave < 2;
+  const bool owns_s = wave < ST;
+  const int arow = ti * 32 + (lane & 31);
+  const int64_t st_base = (int64_t)bh * DK * p.Dv;
+
+  auto load = [&](int c, ChunkOps<DK>& o) {
+    const int64_t cid = (int64_t)bh * p.NC + c;
+    const int64_t t0 = (int64_t)c * kC;
+    if (uwave) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        o.a[ks] = *reinterpret_cast<const u32x4*>(p.w_ws + (cid * kC + arow) * DK + ks * 16 + kb8);
+      const uint16_t* uw = p.u_ws + (((cid * p.NV + tv) * 2 + ti) * 64 + lane) * 16;
+      o.u[0] = *reinterpret_cast<const u32x4*>(uw);
+      o.u[1] = *reinterpret_cast<const u32x4*>(uw + 8);
+    } else {
+      const bool ok = t0 + arow < p.T;
+      const uint16_t* qr = p.q + (((int64_t)b * p.T + t0 + arow) * p.Hk + kh) * DK + kb8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        o.a[ks] = ok ? *reinterpret_cast<const u32x4*>(qr + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        o.pk[ks] = *reinterpret_cast<const u32x4*>(p.p_ws + (cid * kC + arow) * kC + ks * 16 + kb8);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        o.gc[g4] = *reinterpret_cast<const float4*>(p.gc_ws + cid * kC + ti * 32 + g4 * 8 + (lane >> 5) * 4);
+    }
+    if (owns_s) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        o.kt[ks] = *reinterpret_cast<const u32x4*>(p.kt_ws + (cid * DK + wave * 32 + (lane & 31)) * kC + ks * 16 + kb8);
+    }
+    o.glast = p.gc_ws[cid * kC + kC - 1];
+  };
+
+  // state tile of this wave: keys 32 w .. 32 w + 31, columns col; key of register r
+  f32x16 s_acc = {};
+  auto srow = [&](int r) { return wave * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
+  auto sidx = [&](int d) -> int64_t {
+    return st_base + (p.v_first ? (int64_t)col * DK + d : (int64_t)d * p.Dv + col);
+  };
+  auto write_sS = [&]() {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = wave * 32 + g4 * 8 + (lane >> 5) * 4;
+      *reinterpret_cast<u32x2*>(&sS[lane & 31][d]) =
+          u32x2{f32x2_to_bf16x2(s_acc[4 * g4], s_acc[4 * g4 + 1]), f32x2_to_bf16x2(s_acc[4 * g4 + 2], s_acc[4 * g4 + 3])};
+    }
+  };
+  if (owns_s) {
+    if (p.h0 != nullptr) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_acc[r] = p.h0[sidx(srow(r))];
+    }
+    write_sS();
+  }
+
+  auto step = [&](int c, const ChunkOps<DK>& o) {
+    const int64_t t0 = (int64_t)c * kC;
+    const int n = (int)(p.T - t0 < kC ? p.T - t0 : kC);
+    f32x16 acc = {};
+    if (uwave) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = bf16_bits_to_f32(o.u[0][e] & 0xFFFFu);
+        acc[2 * e + 1] = bf16_bits_to_f32(o.u[0][e] >> 16);
+        acc[8 + 2 * e] = bf16_bits_to_f32(o.u[1][e] & 0xFFFFu);
+        acc[8 + 2 * e + 1] = bf16_bits_to_f32(o.u[1][e] >> 16);
+      }
+    }
+    // U = U~ + (-W) S0 (U waves); Q S0 (O waves)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = mfma32(__builtin_bit_cast(bf16x8, o.a[ks]), ld8(&sS[lane & 31][ks * 16 + kb8]), acc);
+    if (uwave) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int i = ti * 32 + g4 * 8 + (lane >> 5) * 4;
+        *reinterpret_cast<u32x2*>(&sU[lane & 31][i]) =
+            u32x2{f32x2_to_bf16x2(acc[4 * g4], acc[4 * g4 + 1]), f32x2_to_bf16x2(acc[4 * g4 + 2], acc[4 * g4 + 3])};
+      }
+    } else {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        acc[4 * g4] *= expf(o.gc[g4].x);
+        acc[4 * g4 + 1] *= expf(o.gc[g4].y);
+        acc[4 * g4 + 2] *= expf(o.gc[g4].z);
+        acc[4 * g4 + 3] *= expf(o.gc[g4].w);
+      }
+    }
+    __syncthreads();  // U complete; the state tile is no longer read
+
+    if (!uwave) {
+      // O = scale (e^Gc Q S0 + P U)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma32(__builtin_bit_cast(bf16x8, o.pk[ks]), ld8(&sU[lane & 31][ks * 16 + kb8]), acc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = ti * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (i < n) p.o[(((int64_t)b * p.T + t0 + i) * p.Hv + h) * p.Dv + col] = f32_to_bf16(p.scale * acc[r]);
+      }
+    }
+    if (owns_s) {
+      // S1 = e^{Gc_last} S0 + (e^{Gc_last - Gc} K)^T U
+      const float dl = expf(o.glast);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_acc[r] *= dl;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        s_acc = mfma32(__builtin_bit_cast(bf16x8, o.kt[ks]), ld8(&sU[lane & 31][ks * 16 + kb8]), s_acc);
+      write_sS();
+    }
+    __syncthreads();  // the new state tile is written; U is no longer read
+  };
+
+  ChunkOps<DK> o0, o1;
+  if (p.NC > 0) load(0, o0);
+  __syncthreads();
+  for (int c = 0; c < p.NC; c += 2) {
+    if (c + 1 < p.NC) load(c + 1, o1);
+    step(c, o0);
+    if (c + 1 >= p.NC) break;
+    if (c + 2 < p.NC) load(c + 2, o0);
+    step(c + 1, o1);
+  }
+
+  if (owns_s && p.h_last != nullptr) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p.h_last[sidx(srow(r))] = s_acc[r];
+  }
+}
+
+template <int DK>
+hipError_t launch(ChunkArgs a, int64_t prep_blocks, int64_t state_blocks, hipStream_t st) {
+  if (prep_blocks > 0) {
+    a.n_blocks = (int)prep_blocks;
+    if (a.Dv <= 128)
+      hipLaunchKernelGGL((gdn_chunk_prep<DK, 128>), dim3((unsigned)prep_blocks), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((gdn_chunk_prep<DK, kMaxDv>), dim3((unsigned)prep_blocks), dim3(kThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  a.n_blocks = (int)state_blocks;
+  hipLaunchKernelGGL(gdn_chunk_state<DK>, dim3((unsigned)state_blocks), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+struct Plan {
+  int64_t NC, NV, prep_blocks, state_blocks;
+  size_t w_off, u_off, p_off, g_off, kt_off, bytes;
+};
+
+// Validates the shape for the chunk form; fills the workspace plan.
+rglru_status_t plan(const rglru_delta_shape_t* sp, const int32_t* cu, Plan* pl) {
+  if (sp == nullptr) return RGLRU_ERR_INVALID_ARGUMENT;
+  const rglru_delta_shape_t s = *sp;
+  if (s.batch < 0 || s.length < 0 || s.batch > (int64_t(1) << 40) || s.length > (int64_t(1) << 40) ||
+      (s.batch > 0 && s.length >= (int64_t(1) << 40) / s.batch))
+    return RGLRU_ERR_INVALID_ARGUMENT;
+  if (s.k_heads < 1 || s.v_heads < s.k_heads || s.v_heads >= (1 << 16) || s.v_heads % s.k_heads != 0)
+    return RGLRU_ERR_INVALID_ARGUMENT;
+  if (s.k_dim < 1 || s.v_dim < 1 || s.k_dim > (1 << 16) || s.v_dim > (1 << 16)) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (s.io_dtype != RGLRU_IO_F32 && s.io_dtype != RGLRU_IO_BF16) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (s.decay != RGLRU_DELTA_GDN && s.decay != RGLRU_DELTA_KDA) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (s.state_v_first != 0 && s.state_v_first != 1) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(s.scale)) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (s.decay != RGLRU_DELTA_GDN || s.io_dtype != RGLRU_IO_BF16 || (s.k_dim != 64 && s.k_dim != 128) ||
+      s.v_dim % 32 != 0 || s.v_dim > kMaxDv || cu != nullptr)
+    return RGLRU_ERR_UNSUPPORTED;
+  const int64_t NC = ceil_div(s.length, kC), NV = s.v_dim / 32;
+  const int64_t BH = s.batch * s.v_heads;
+  if (BH * NC >= (int64_t(1) << 31) || BH * NV >= (int64_t(1) << 31)) return RGLRU_ERR_INVALID_ARGUMENT;
+  const size_t chunks = (size_t)(BH * NC);
+  pl->NC = NC;
+  pl->NV = NV;
+  pl->prep_blocks = BH * NC;
+  pl->state_blocks = BH * NV;
+  pl->w_off = 0;
+  pl->u_off = round_up(pl->w_off + chunks * kC * s.k_dim * 2, 256);
+  pl->p_off = round_up(pl->u_off + chunks * kC * s.v_dim * 2, 256);
+  pl->g_off = round_up(pl->p_off + chunks * kC * kC * 2, 256);
+  pl->kt_off = round_up(pl->g_off + chunks * kC * 4, 256);
+  pl->bytes = round_up(pl->kt_off + chunks * kC * s.k_dim * 2, 256);
+  return RGLRU_OK;
+}
+
+}  // namespace dchunk
+}  // namespace rglru
+
+using namespace rglru;
+
+extern "C" size_t rglru_delta_chunk_workspace_bytes(const rglru_delta_shape_t* shape) {
+  dchunk::Plan pl;
+  if (dchunk::plan(shape, nullptr, &pl) != RGLRU_OK) return 0;
+  return pl.bytes;
+}
+
+extern "C" rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape, const void* q, const void* k,
+                                                const void* v, const float* g, const float* beta, const float* h0,
+                                                void* o, float* h_last, void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  dchunk::Plan pl;
+  const rglru_status_t st = dchunk::plan(shape, nullptr, &pl);
+  if (st != RGLRU_OK) return st;
+  const rglru_delta_shape_t& s = *shape;
+  const int64_t tokens = s.batch * s.length;
+  if (tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
+                     o == nullptr || workspace == nullptr))
+    return RGLRU_ERR_INVALID_ARGUMENT;
+  if (tokens == 0) pl.prep_blocks = 0;
+  if (!aligned_to(q, 16) || !aligned_to(k, 16) || !aligned_to(v, 16) || !aligned_to(o, 2) ||
+      !aligned_to(g, 4) || !aligned_to(beta, 4) || !aligned_to(h0, 4) || !aligned_to(h_last, 4) ||
+      !aligned_to(workspace, 256))
+    return RGLRU_ERR_MISALIGNED;
+  if (s.batch * s.v_heads == 0 || (tokens == 0 && h_last == nullptr)) return RGLRU_OK;
+  // with no tokens there are no chunks: only the state pass runs (it copies h0 or zeros
+  // into h_last) and the workspace is not touched
+  if (tokens > 0 && workspace_bytes < pl.bytes) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  dchunk::ChunkArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.g = g;
+  a.beta = beta;
+  a.h0 = h0;
+  a.o = static_cast<uint16_t*>(o);
+  a.h_last = h_last;
+  a.w_ws = reinterpret_cast<uint16_t*>(ws + pl.w_off);
+  a.u_ws = reinterpret_cast<uint16_t*>(ws + pl.u_off);
+  a.p_ws = reinterpret_cast<uint16_t*>(ws + pl.p_off);
+  a.gc_ws = reinterpret_cast<float*>(ws + pl.g_off);
+  a.kt_ws = reinterpret_cast<uint16_t*>(ws + pl.kt_off);
+  a.T = s.length;
+  a.Hk = s.k_heads;
+  a.Hv = s.v_heads;
+  a.grp = s.v_heads / s.k_heads;
+  a.Dv = s.v_dim;
+  a.NC = (int)pl.NC;
+  a.NV = (int)pl.NV;
+  a.n_blocks = 0;
+  a.v_first = s.state_v_first;
+  a.scale = s.scale;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = s.k_dim == 64 ? dchunk::launch<64>(a, pl.prep_blocks, pl.state_blocks, hs)
+                                     : dchunk::launch<128>(a, pl.prep_blocks, pl.state_blocks, hs);
+  return e == hipSuccess ? RGLRU_OK : RGLRU_ERR_HIP;
+}

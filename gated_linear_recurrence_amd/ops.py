@@ -454,20 +454,8 @@ def rglru(x, gate_x, gate_a, lam, h0=None, reset=None, *, chunk: int = 0, c: flo
     return _RGLRU.apply(x, gate_x, gate_a, lam, h0, reset, chunk, c)
 
 
-def rglru_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
-                         scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
-                         cu_seqlens: Optional[torch.Tensor] = None, state_v_first: bool = False,
-                         output_final_state: bool = True, o: Optional[torch.Tensor] = None,
-                         final_state: Optional[torch.Tensor] = None):
-    """Gated delta rule forward, token recurrence (GDN when g is [B, T, Hv], KDA when [B, T, Hv, Dk]).
-
-    q, k [B, T, Hk, Dk] and v [B, T, Hv, Dv] in bfloat16 or float32 (one dtype);
-    g, beta float32; states float32 [N, Hv, Dk, Dv] ([N, Hv, Dv, Dk] with
-    state_v_first), N = B, or the number of sequences when cu_seqlens (int32
-    [N + 1], B = 1) packs them. scale defaults to 1 / sqrt(Dk).
-    Returns (o [B, T, Hv, Dv], final state or None).
-    """
-    lib = _lib.load()
+def _delta_common(q, k, v, g, beta, scale, initial_state, cu_seqlens, state_v_first, output_final_state, o,
+                  final_state):
     dev = q.device
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, T, H, D]")
@@ -500,7 +488,57 @@ def rglru_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
     shape = _lib.rglru_delta_shape_t(B, T, Hk, Hv, Dk, Dv, _IO[io],
                                      _lib.RGLRU_DELTA_KDA if kda else _lib.RGLRU_DELTA_GDN,
                                      int(bool(state_v_first)), sc)
+    return shape, n, o, final_state
+
+
+def rglru_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
+                         scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
+                         cu_seqlens: Optional[torch.Tensor] = None, state_v_first: bool = False,
+                         output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                         final_state: Optional[torch.Tensor] = None):
+    """Gated delta rule forward, token recurrence (GDN when g is [B, T, Hv], KDA when [B, T, Hv, Dk]).
+
+    q, k [B, T, Hk, Dk] and v [B, T, Hv, Dv] in bfloat16 or float32 (one dtype);
+    g, beta float32; states float32 [N, Hv, Dk, Dv] ([N, Hv, Dv, Dk] with
+    state_v_first), N = B, or the number of sequences when cu_seqlens (int32
+    [N + 1], B = 1) packs them. scale defaults to 1 / sqrt(Dk).
+    Returns (o [B, T, Hv, Dv], final state or None).
+    """
+    lib = _lib.load()
+    shape, n, o, final_state = _delta_common(q, k, v, g, beta, scale, initial_state, cu_seqlens, state_v_first,
+                                             output_final_state, o, final_state)
     st = lib.rglru_delta_rule_fwd(ctypes.byref(shape), _ptr(cu_seqlens), n, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                  _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state), _stream(dev))
+                                  _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                  _stream(q.device))
     _lib.check(st, "rglru_delta_rule_fwd")
+    return o, final_state
+
+
+def rglru_delta_chunk_workspace_bytes(shape: _lib.rglru_delta_shape_t) -> int:
+    return int(_lib.load().rglru_delta_chunk_workspace_bytes(ctypes.byref(shape)))
+
+
+def rglru_delta_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
+                          scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
+                          state_v_first: bool = False, output_final_state: bool = True,
+                          o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """Gated delta rule forward for GDN in chunk form (64-token chunks, bf16 MFMA, float32 state).
+
+    Same arguments and results as rglru_delta_rule_fwd without cu_seqlens; bf16
+    q, k, v, Dk 64 or 128, Dv a multiple of 32 up to 256. workspace: a uint8
+    device tensor of at least rglru_delta_chunk_workspace_bytes bytes (allocated
+    here when None)."""
+    lib = _lib.load()
+    if g.dim() != 3:
+        raise ValueError("the chunk form takes the GDN decay g [B, T, Hv]")
+    shape, n, o, final_state = _delta_common(q, k, v, g, beta, scale, initial_state, None, state_v_first,
+                                             output_final_state, o, final_state)
+    nbytes = int(lib.rglru_delta_chunk_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.rglru_delta_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
+                                   workspace.numel(), _stream(q.device))
+    _lib.check(st, "rglru_delta_chunk_fwd")
     return o, final_state
