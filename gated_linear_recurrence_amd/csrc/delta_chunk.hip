@@ -50,6 +50,7 @@ constexpr int kC = 64;  // chunk length
 constexpr int kThreads = 256;
 constexpr int kTP = kC + 8;  // padded row (bf16 elements) of token-indexed LDS tiles
 constexpr int kMaxDv = 256;
+constexpr int kGS = 68;  // floats per chunk in gc_ws (16-byte multiple)
 
 struct ChunkArgs {
   const uint16_t* q;
@@ -62,9 +63,10 @@ struct ChunkArgs {
   float* h_last;
   uint16_t* w_ws;  // [B Hv][NC][64][Dk]      bf16, -W
   uint16_t* u_ws;  // [B Hv][NC][Dv/32][2][64 lanes][16] bf16, Ut in accumulator order
-  uint16_t* p_ws;  // [B Hv][NC][64][64]      bf16, P
-  float* gc_ws;    // [B Hv][NC][64]          float32, Gc
+  uint16_t* p_ws;  // [B Hv][NC][64][64]      bf16, scale P
+  float* gc_ws;    // [B Hv][NC][kGS]         float32: scale e^{Gc_i} (i < 64), then e^{Gc_last}
   uint16_t* kt_ws; // [B Hv][NC][Dk][64]      bf16, (diag(e^{Gc_last - Gc}) K)^T
+  uint16_t* sink;  // 4 KiB that absorbs the output stores of rows past the end
   int64_t T;
   int Hk, Hv, grp, Dv, NC, NV;
   int n_blocks;
@@ -124,40 +126,62 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
   const int64_t chunk_id = (int64_t)bh * p.NC + c;
 
   // stage K and Q (row-major, K also transposed) and V (transposed), zero past the end; the
-  // token index runs fastest across lanes so each transposed 2-byte write fills one row
-  for (int idx = tid; idx < kC * (DK / 8); idx += kThreads) {
-    const int r = idx & (kC - 1), part = idx / kC;
-    u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-    if (r < n) {
-      const int64_t e = (((int64_t)b * p.T + t0 + r) * p.Hk + kh) * DK + part * 8;
-      kv = *reinterpret_cast<const u32x4*>(p.k + e);
-      qv = *reinterpret_cast<const u32x4*>(p.q + e);
-    }
+  // token index runs fastest across lanes so each transposed 2-byte write fills one row. Every
+  // load is issued (at an in-bounds address) before the first LDS write.
+  constexpr int NKG = kC * (DK / 8) / kThreads;
+  constexpr int NVG = kC * (DVM / 8) / kThreads;
+  const int r = tid & (kC - 1);
+  const bool rok = r < n;
+  const int64_t rowq = ((int64_t)b * p.T + t0 + (rok ? r : 0)) * p.Hk + kh;
+  const int64_t rowv = ((int64_t)b * p.T + t0 + (rok ? r : 0)) * p.Hv + h;
+  u32x4 kr[NKG], qr[NKG], vr[NVG];
+#pragma unroll
+  for (int j = 0; j < NKG; ++j) {
+    const int part = (tid + kThreads * j) / kC;
+    kr[j] = *reinterpret_cast<const u32x4*>(p.k + rowq * DK + part * 8);
+    qr[j] = *reinterpret_cast<const u32x4*>(p.q + rowq * DK + part * 8);
+  }
+  const int vparts = p.Dv / 8;
+#pragma unroll
+  for (int j = 0; j < NVG; ++j) {
+    const int part = (tid + kThreads * j) / kC;
+    vr[j] = *reinterpret_cast<const u32x4*>(p.v + rowv * p.Dv + (part < vparts ? part : 0) * 8);
+  }
+  const int64_t eg = ((int64_t)b * p.T + t0 + (tid < n ? tid : 0)) * p.Hv + h;
+  const float gv = p.g[eg], bv = p.beta[eg];
+#pragma unroll
+  for (int j = 0; j < NKG; ++j) {
+    const int part = (tid + kThreads * j) / kC;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 kv = rok ? kr[j] : z, qv = rok ? qr[j] : z;
     *reinterpret_cast<u32x4*>(&sK[r][part * 8]) = kv;
     *reinterpret_cast<u32x4*>(&sQ[r][part * 8]) = qv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) sKt[part * 8 + e][r] = h16(kv, e);
   }
-  for (int idx = tid; idx < kC * (p.Dv / 8); idx += kThreads) {
-    const int r = idx & (kC - 1), part = idx / kC;
-    u32x4 vv = {0u, 0u, 0u, 0u};
-    if (r < n) vv = *reinterpret_cast<const u32x4*>(p.v + (((int64_t)b * p.T + t0 + r) * p.Hv + h) * p.Dv + part * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sVt[part * 8 + e][r] = h16(vv, e);
+  for (int j = 0; j < NVG; ++j) {
+    const int part = (tid + kThreads * j) / kC;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 vv = rok ? vr[j] : z;
+    if (part < vparts) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sVt[part * 8 + e][r] = h16(vv, e);
+    }
   }
   if (tid < kC) {
-    const bool ok = tid < n;
-    const int64_t e = ((int64_t)b * p.T + t0 + tid) * p.Hv + h;
-    sBeta[tid] = ok ? p.beta[e] : 0.f;
-    sG[tid] = ok ? p.g[e] : 0.f;
+    sBeta[tid] = tid < n ? bv : 0.f;
+    sG[tid] = tid < n ? gv : 0.f;
   }
   __syncthreads();
   if (tid < kC) {
     float acc = 0.f;
     for (int m = 0; m <= tid; ++m) acc += sG[m];  // in token order, as a running sum
     sGc[tid] = acc;
-    p.gc_ws[chunk_id * kC + tid] = acc;
   }
+  __syncthreads();
+  if (tid < kC) p.gc_ws[chunk_id * kGS + tid] = p.scale * __expf(sGc[tid]);
+  if (tid == kC) p.gc_ws[chunk_id * kGS + kC] = __expf(sGc[kC - 1]);
   __syncthreads();
 
   // K K^T and Q K^T, one 32x32 tile of each per wave
@@ -180,10 +204,10 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = ti * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      const float dec = expf(sGc[i] - gj);
+      const float dec = __expf(sGc[i] - gj);
       const float a = (j < i) ? sBeta[i] * dec * akk[r] : 0.f;
       sA[i][(j & 3) * 16 + (j >> 2)] = a;
-      const float pv = (j <= i) ? dec * aqk[r] : 0.f;
+      const float pv = (j <= i) ? p.scale * dec * aqk[r] : 0.f;
       pw[i * kC + j] = f32_to_bf16(pv);
     }
   }
@@ -214,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
       const float tij = (i == j ? 1.f : 0.f) - sum;
       if (s == (i & 3)) tr[i >> 2] = tij;
     }
-    const float bj = sBeta[j], ej = bj * expf(sGc[j]);
+    const float bj = sBeta[j], ej = bj * __expf(sGc[j]);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int m = 4 * t + s;
@@ -273,8 +297,8 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = part * 8 + 2 * e;
-        out[e] = f32x2_to_bf16x2(bf16_bits_to_f32(kv[e] & 0xFFFFu) * expf(gl - sGc[m]),
-                                 bf16_bits_to_f32(kv[e] >> 16) * expf(gl - sGc[m + 1]));
+        out[e] = f32x2_to_bf16x2(bf16_bits_to_f32(kv[e] & 0xFFFFu) * __expf(gl - sGc[m]),
+                                 bf16_bits_to_f32(kv[e] >> 16) * __expf(gl - sGc[m + 1]));
       }
       *reinterpret_cast<u32x4*>(kw + d * kC + part * 8) = out;
     }
@@ -284,14 +308,16 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
 // ------------------------------------------------------------------ state pass
 
 // Operands of one chunk for one wave, loaded from global memory straight into MFMA fragment
-// registers (lane l: row l % 32 of its tile, 8 consecutive k at 8 (l / 32)).
+// registers (lane l: row l % 32 of its tile, 8 consecutive k at 8 (l / 32)). Every wave issues
+// the same loads in the same order (at in-bounds addresses, some unused by its role), so the
+// compiler's count of outstanding loads stays exact and the prefetch is never waited for early.
 template <int DK>
 struct ChunkOps {
   u32x4 a[DK / 16];  // U waves: rows of -W; O waves: rows of Q
-  u32x4 pk[4];       // O waves: rows of P
-  u32x4 kt[4];       // state owners: rows of the decayed K^T
-  u32x4 u[2];        // U waves: U~ in accumulator order
-  float4 gc[4];      // O waves: Gc of the accumulator rows
+  u32x4 pk[4];       // rows of P
+  u32x4 kt[4];       // rows of the decayed K^T
+  u32x4 u[2];        // U~ in accumulator order
+  float4 gc[4];      // scale e^{Gc} of the accumulator rows
   float glast;
 };
 
@@ -305,54 +331,49 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_state(ChunkArgs p) {
   constexpr int KS = DK / 16;
   __shared__ __align__(16) uint16_t sS[32][KP];   // bf16 state tile, [column][key]
   __shared__ __align__(16) uint16_t sU[32][kTP];  // bf16 U, [column][token]
+  __shared__ __align__(16) uint16_t sO[kC][40];   // bf16 outputs, [token][column]
 
   const int bid = xcd_remap(blockIdx.x, p.n_blocks);
   const int tv = bid % p.NV;
   const int bh = bid / p.NV;
   const int h = bh % p.Hv, b = bh / p.Hv, kh = h / p.grp;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = tv * 32 + (lane & 31);
   const int kb8 = (lane >> 5) * 8;
   const int ti = wave & 1;
   const bool uwave = wave < 2;
   const bool owns_s = wave < ST;
+  const int kw = wave % ST;  // state rows whose K^T this wave loads
   const int arow = ti * 32 + (lane & 31);
   const int64_t st_base = (int64_t)bh * DK * p.Dv;
 
   auto load = [&](int c, ChunkOps<DK>& o) {
     const int64_t cid = (int64_t)bh * p.NC + c;
     const int64_t t0 = (int64_t)c * kC;
-    if (uwave) {
+    const int64_t qrow = t0 + arow < p.T ? t0 + arow : t0;  // rows past the end: any valid row
+    const uint16_t* ab = uwave ? p.w_ws + (cid * kC + arow) * DK + kb8
+                               : p.q + (((int64_t)b * p.T + qrow) * p.Hk + kh) * DK + kb8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        o.a[ks] = *reinterpret_cast<const u32x4*>(p.w_ws + (cid * kC + arow) * DK + ks * 16 + kb8);
-      const uint16_t* uw = p.u_ws + (((cid * p.NV + tv) * 2 + ti) * 64 + lane) * 16;
-      o.u[0] = *reinterpret_cast<const u32x4*>(uw);
-      o.u[1] = *reinterpret_cast<const u32x4*>(uw + 8);
-    } else {
-      const bool ok = t0 + arow < p.T;
-      const uint16_t* qr = p.q + (((int64_t)b * p.T + t0 + arow) * p.Hk + kh) * DK + kb8;
+    for (int ks = 0; ks < KS; ++ks) o.a[ks] = *reinterpret_cast<const u32x4*>(ab + ks * 16);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        o.a[ks] = ok ? *reinterpret_cast<const u32x4*>(qr + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < 4; ++ks)
+      o.pk[ks] = *reinterpret_cast<const u32x4*>(p.p_ws + (cid * kC + arow) * kC + ks * 16 + kb8);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        o.pk[ks] = *reinterpret_cast<const u32x4*>(p.p_ws + (cid * kC + arow) * kC + ks * 16 + kb8);
+    for (int ks = 0; ks < 4; ++ks)
+      o.kt[ks] = *reinterpret_cast<const u32x4*>(p.kt_ws + (cid * DK + kw * 32 + (lane & 31)) * kC + ks * 16 + kb8);
+    const uint16_t* uw = p.u_ws + (((cid * p.NV + tv) * 2 + ti) * 64 + lane) * 16;
+    o.u[0] = *reinterpret_cast<const u32x4*>(uw);
+    o.u[1] = *reinterpret_cast<const u32x4*>(uw + 8);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        o.gc[g4] = *reinterpret_cast<const float4*>(p.gc_ws + cid * kC + ti * 32 + g4 * 8 + (lane >> 5) * 4);
-    }
-    if (owns_s) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        o.kt[ks] = *reinterpret_cast<const u32x4*>(p.kt_ws + (cid * DK + wave * 32 + (lane & 31)) * kC + ks * 16 + kb8);
-    }
-    o.glast = p.gc_ws[cid * kC + kC - 1];
+    for (int g4 = 0; g4 < 4; ++g4)
+      o.gc[g4] = *reinterpret_cast<const float4*>(p.gc_ws + cid * kGS + ti * 32 + g4 * 8 + (lane >> 5) * 4);
+    o.glast = p.gc_ws[cid * kGS + kC];
   };
 
   // state tile of this wave: keys 32 w .. 32 w + 31, columns col; key of register r
   f32x16 s_acc = {};
-  auto srow = [&](int r) { return wave * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
+  auto srow = [&](int r) { return kw * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
   auto sidx = [&](int d) -> int64_t {
     return st_base + (p.v_first ? (int64_t)col * DK + d : (int64_t)d * p.Dv + col);
   };
@@ -364,17 +385,23 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_state(ChunkArgs p) {
           u32x2{f32x2_to_bf16x2(s_acc[4 * g4], s_acc[4 * g4 + 1]), f32x2_to_bf16x2(s_acc[4 * g4 + 2], s_acc[4 * g4 + 3])};
     }
   };
-  if (owns_s) {
-    if (p.h0 != nullptr) {
+  if (p.h0 != nullptr) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_acc[r] = p.h0[sidx(srow(r))];
-    }
-    write_sS();
+    for (int r = 0; r < 16; ++r) s_acc[r] = p.h0[sidx(srow(r))];
   }
+  if (owns_s) write_sS();
+
+  // the output rows of one chunk, from LDS: thread -> token row tid / 4, 8 columns at 8 (tid % 4)
+  const int orow = tid >> 2, ocol = (tid & 3) * 8;
+  auto store_out = [&](int c) {
+    const int64_t t0 = (int64_t)c * kC;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(&sO[orow][ocol]);
+    uint16_t* dst = t0 + orow < p.T ? p.o + (((int64_t)b * p.T + t0 + orow) * p.Hv + h) * p.Dv + tv * 32 + ocol
+                                    : p.sink + tid * 8;
+    *reinterpret_cast<u32x4*>(dst) = val;
+  };
 
   auto step = [&](int c, const ChunkOps<DK>& o) {
-    const int64_t t0 = (int64_t)c * kC;
-    const int n = (int)(p.T - t0 < kC ? p.T - t0 : kC);
     f32x16 acc = {};
     if (uwave) {
 #pragma unroll
@@ -399,46 +426,46 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_state(ChunkArgs p) {
     } else {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        acc[4 * g4] *= expf(o.gc[g4].x);
-        acc[4 * g4 + 1] *= expf(o.gc[g4].y);
-        acc[4 * g4 + 2] *= expf(o.gc[g4].z);
-        acc[4 * g4 + 3] *= expf(o.gc[g4].w);
+        acc[4 * g4] *= o.gc[g4].x;
+        acc[4 * g4 + 1] *= o.gc[g4].y;
+        acc[4 * g4 + 2] *= o.gc[g4].z;
+        acc[4 * g4 + 3] *= o.gc[g4].w;
       }
     }
-    __syncthreads();  // U complete; the state tile is no longer read
+    __syncthreads();  // U complete; the state tile is no longer read; last chunk's outputs are out
 
     if (!uwave) {
-      // O = scale (e^Gc Q S0 + P U)
+      // O = scale (e^Gc Q S0 + P U), to LDS (scale is folded into e^Gc and P)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         acc = mfma32(__builtin_bit_cast(bf16x8, o.pk[ks]), ld8(&sU[lane & 31][ks * 16 + kb8]), acc);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = ti * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (i < n) p.o[(((int64_t)b * p.T + t0 + i) * p.Hv + h) * p.Dv + col] = f32_to_bf16(p.scale * acc[r]);
-      }
+      for (int r = 0; r < 16; ++r)
+        sO[ti * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)][lane & 31] = f32_to_bf16(acc[r]);
     }
     if (owns_s) {
       // S1 = e^{Gc_last} S0 + (e^{Gc_last - Gc} K)^T U
-      const float dl = expf(o.glast);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_acc[r] *= dl;
+      for (int r = 0; r < 16; ++r) s_acc[r] *= o.glast;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         s_acc = mfma32(__builtin_bit_cast(bf16x8, o.kt[ks]), ld8(&sU[lane & 31][ks * 16 + kb8]), s_acc);
       write_sS();
     }
-    __syncthreads();  // the new state tile is written; U is no longer read
+    __syncthreads();  // the new state tile and the outputs are written; U is no longer read
+    store_out(c);
   };
 
   ChunkOps<DK> o0, o1;
   if (p.NC > 0) load(0, o0);
   __syncthreads();
+  // the prefetch is unconditional (the last chunk reloads itself) so that every path issues
+  // the same loads
   for (int c = 0; c < p.NC; c += 2) {
-    if (c + 1 < p.NC) load(c + 1, o1);
+    load(c + 1 < p.NC ? c + 1 : c, o1);
     step(c, o0);
     if (c + 1 >= p.NC) break;
-    if (c + 2 < p.NC) load(c + 2, o0);
+    load(c + 2 < p.NC ? c + 2 : c + 1, o0);
     step(c + 1, o1);
   }
 
@@ -466,7 +493,7 @@ hipError_t launch(ChunkArgs a, int64_t prep_blocks, int64_t state_blocks, hipStr
 
 struct Plan {
   int64_t NC, NV, prep_blocks, state_blocks;
-  size_t w_off, u_off, p_off, g_off, kt_off, bytes;
+  size_t w_off, u_off, p_off, g_off, kt_off, sink_off, bytes;
 };
 
 // Validates the shape for the chunk form; fills the workspace plan.
@@ -498,8 +525,9 @@ rglru_status_t plan(const rglru_delta_shape_t* sp, const int32_t* cu, Plan* pl) 
   pl->u_off = round_up(pl->w_off + chunks * kC * s.k_dim * 2, 256);
   pl->p_off = round_up(pl->u_off + chunks * kC * s.v_dim * 2, 256);
   pl->g_off = round_up(pl->p_off + chunks * kC * kC * 2, 256);
-  pl->kt_off = round_up(pl->g_off + chunks * kC * 4, 256);
-  pl->bytes = round_up(pl->kt_off + chunks * kC * s.k_dim * 2, 256);
+  pl->kt_off = round_up(pl->g_off + chunks * kGS * 4, 256);
+  pl->sink_off = round_up(pl->kt_off + chunks * kC * s.k_dim * 2, 256);
+  pl->bytes = pl->sink_off + 4096;
   return RGLRU_OK;
 }
 
@@ -550,6 +578,7 @@ extern "C" rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape
   a.p_ws = reinterpret_cast<uint16_t*>(ws + pl.p_off);
   a.gc_ws = reinterpret_cast<float*>(ws + pl.g_off);
   a.kt_ws = reinterpret_cast<uint16_t*>(ws + pl.kt_off);
+  a.sink = reinterpret_cast<uint16_t*>(ws + pl.sink_off);
   a.T = s.length;
   a.Hk = s.k_heads;
   a.Hv = s.v_heads;
