@@ -330,20 +330,50 @@ def run_delta(args, wid, steps, warmup):
         glr.rglru_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
                                  o=d["o"], final_state=d["fs"])
 
-    for i in range(warmup):
-        call(sets[i % n_sets])
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        call(sets[i % n_sets])
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    def timed(fn):
+        for i in range(warmup):
+            fn(sets[i % n_sets])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(sets[i % n_sets])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(call)
     flops = 7 * B * T * Hv * Dk * Dv   # per state element and token: decay, two dot-product FMAs, one write FMA
     tf = flops / (ms * 1e-3) / 1e12
     gbs = nbytes / (ms * 1e-3) / 1e9
+    chunk = None
+    shape = glr.ops._lib.rglru_delta_shape_t(B, T, wl.k_heads, Hv, Dk, Dv, 1 if wl.io == "bf16" else 0,
+                                             1 if wl.kda else 0, 0, 1.0)
+    ws_bytes = glr.rglru_delta_chunk_workspace_bytes(shape)
+    if ws_bytes > 0 and T >= 64:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def chunk_call(d):
+            glr.rglru_delta_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
+                                      o=d["o"], final_state=d["fs"], workspace=ws)
+
+        cms = timed(chunk_call)
+        # dense products of the chunk form per (64-token chunk, head), as multiply-adds:
+        # K K^T, Q K^T and W (64 x 64 x Dk each), U~ and P U (64 x 64 x Dv each), and
+        # U = U~ - W S, Q S and the state update (64 x Dk x Dv each)
+        n_chunks = B * Hv * ((T + 63) // 64)
+        cflops = 2 * n_chunks * (3 * 64 * 64 * Dk + 2 * 64 * 64 * Dv + 3 * 64 * Dk * Dv)
+        ctf = cflops / (cms * 1e-3) / 1e12
+        chunk = {
+            "call": "rglru_delta_chunk_fwd (64-token chunks, bf16 MFMA)", "ms": round(cms, 5),
+            "tokens_per_s": B * T / (cms * 1e-3),
+            "roofline": {"kernel": "gdn_chunk_prep + gdn_chunk_state", "bound": "mfma", "achieved": round(ctf, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ctf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": cflops, "launch_ms": round(cms, 5)},
+            "speedup_vs_token_recurrence": round(ms / cms, 3),
+        }
     del sets
     torch.cuda.empty_cache()
     return {
@@ -358,6 +388,7 @@ def run_delta(args, wid, steps, warmup):
                      "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
                      "algorithmic_flops_per_launch": flops, "launch_ms": round(ms, 5)},
         "hbm": {"algorithmic_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "chunk_form": chunk,
         "cpu_baseline": cpu,
     }
 

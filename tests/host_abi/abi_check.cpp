@@ -9,6 +9,7 @@
 #include <cstring>
 #include <limits>
 
+#include "delta_rule.h"
 #include "rglru.h"
 
 extern "C" const char* host_abi_status_of_int(int v);
@@ -171,6 +172,65 @@ int main() {
   rglru_shape_t sf3 = shape(2, 100, 512, 1);
   EXPECT(rglru_blockdiag_fused_fwd(&sf3, p, p, nullptr, p, nullptr, fp, nullptr, nullptr, p, nullptr, nullptr, nullptr,
                                    nullptr, p, 16, nullptr) == RGLRU_ERR_WORKSPACE_TOO_SMALL);
+
+  // gated delta rule, token and chunk forms: validation paths only (nothing is launched)
+  auto dshape = [](int64_t b, int64_t t, int hk, int hv, int dk, int dv, int io, int decay) {
+    rglru_delta_shape_t d;
+    std::memset(&d, 0, sizeof(d));
+    d.batch = b;
+    d.length = t;
+    d.k_heads = hk;
+    d.v_heads = hv;
+    d.k_dim = dk;
+    d.v_dim = dv;
+    d.io_dtype = io;
+    d.decay = decay;
+    d.state_v_first = 0;
+    d.scale = 0.125f;
+    return d;
+  };
+  float* wf = (float*)p;
+  const int32_t* dcu = (const int32_t*)p;
+  auto dfwd = [&](const rglru_delta_shape_t& d, const void* q, const int32_t* c = nullptr, int64_t n = 0) {
+    return rglru_delta_rule_fwd(&d, c, n, q, p, p, fp, fp, nullptr, p, nullptr, nullptr);
+  };
+  rglru_delta_shape_t d = dshape(2, 64, 2, 3, 64, 64, 1, 0);
+  EXPECT(dfwd(d, p) == RGLRU_ERR_INVALID_ARGUMENT);  // Hv not a multiple of Hk
+  d = dshape(2, 64, 1, 1, 264, 64, 1, 0);
+  EXPECT(dfwd(d, p) == RGLRU_ERR_UNSUPPORTED);       // Dk > 256
+  d = dshape(2, 64, 1, 1, 64, 12, 1, 1);
+  EXPECT(dfwd(d, p) == RGLRU_ERR_UNSUPPORTED);       // Dv not a multiple of 8
+  d = dshape(2, 64, 1, 1, 64, 64, 1, 0);
+  EXPECT(dfwd(d, buf + 8) == RGLRU_ERR_MISALIGNED);
+  EXPECT(dfwd(d, nullptr) == RGLRU_ERR_INVALID_ARGUMENT);
+  EXPECT(dfwd(d, p, dcu, 3) == RGLRU_ERR_INVALID_ARGUMENT);  // packed sequences need B = 1
+  d.scale = std::numeric_limits<float>::quiet_NaN();
+  EXPECT(dfwd(d, p) == RGLRU_ERR_INVALID_ARGUMENT);
+  d = dshape(2, 64, 1, 1, 64, 64, 1, 2);
+  EXPECT(dfwd(d, p) == RGLRU_ERR_INVALID_ARGUMENT);  // decay kind
+  d = dshape(2, 64, 1, 1, 64, 64, 7, 0);
+  EXPECT(dfwd(d, p) == RGLRU_ERR_INVALID_ARGUMENT);  // io dtype
+  d = dshape(int64_t(1) << 30, int64_t(1) << 11, 1, 1, 64, 64, 1, 0);
+  EXPECT(dfwd(d, p) == RGLRU_ERR_INVALID_ARGUMENT);  // 2^41 tokens
+  d = dshape(1, 64, 1, 1, 64, 64, 1, 0);
+  EXPECT(dfwd(d, p, dcu, 0) == RGLRU_ERR_INVALID_ARGUMENT);  // no sequences
+  EXPECT(rglru_delta_rule_fwd(nullptr, nullptr, 0, p, p, p, fp, fp, nullptr, p, nullptr, nullptr) ==
+         RGLRU_ERR_INVALID_ARGUMENT);
+  rglru_delta_shape_t c1 = dshape(2, 100, 1, 2, 128, 128, 1, 0);
+  const size_t cws = rglru_delta_chunk_workspace_bytes(&c1);
+  EXPECT(cws > 0 && cws % 256 == 0);
+  auto cfwd = [&](const rglru_delta_shape_t& c, size_t bytes) {
+    return rglru_delta_chunk_fwd(&c, p, p, p, fp, fp, nullptr, p, wf, p, bytes, nullptr);
+  };
+  EXPECT(cfwd(c1, 16) == RGLRU_ERR_WORKSPACE_TOO_SMALL);
+  const rglru_delta_shape_t unsupported[] = {dshape(2, 100, 1, 2, 128, 128, 1, 1), dshape(2, 100, 1, 2, 96, 128, 1, 0),
+                                            dshape(2, 100, 1, 2, 128, 48, 1, 0), dshape(2, 100, 1, 2, 128, 288, 1, 0),
+                                            dshape(2, 100, 1, 2, 128, 128, 0, 0)};
+  for (const rglru_delta_shape_t& c : unsupported) {
+    EXPECT(rglru_delta_chunk_workspace_bytes(&c) == 0);
+    EXPECT(cfwd(c, cws) == RGLRU_ERR_UNSUPPORTED);
+  }
+  EXPECT(rglru_delta_chunk_workspace_bytes(nullptr) == 0);
 
   std::printf(g_fail ? "host ABI checks: %d failed\n" : "host ABI checks: all passed\n", g_fail);
   return g_fail ? 1 : 0;

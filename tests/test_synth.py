@@ -84,3 +84,18 @@ def test_projection_weights_scale():
     assert inp.wx.shape == (10, 256, 256)
     assert abs(inp.wx.value.std() - 1 / 16) < 0.002
     assert np.all(inp.bx.value == 0)
+
+
+def test_delta_inputs_are_seeded_and_shaped():
+    from synth import delta as sd
+    wl = sd.DELTA_WORKLOADS[11].resized(batch=2, length=9, k_heads=1, v_heads=2, k_dim=16, v_dim=8, h0=True)
+    a, b = sd.make_delta_inputs(wl), sd.make_delta_inputs(wl)
+    for x, y in ((a.q.raw, b.q.raw), (a.k.raw, b.k.raw), (a.v.raw, b.v.raw), (a.g, b.g), (a.beta, b.beta), (a.h0, b.h0)):
+        np.testing.assert_array_equal(x, y)
+    assert a.q.shape == (2, 9, 1, 16) and a.v.shape == (2, 9, 2, 8) and a.g.shape == (2, 9, 2, 16)
+    assert a.h0.shape == (2, 2, 16, 8)
+    np.testing.assert_allclose(np.linalg.norm(a.k.value, axis=-1), 1.0, atol=1e-2)   # unit keys up to bf16 rounding
+    assert np.all(a.g < 0) and np.all(np.exp(a.g) >= 0.9 - 1e-6) and np.all((a.beta > 0) & (a.beta < 1))
+    p = sd.make_delta_inputs(wl.resized(kda=False), lengths=[3, 0, 5])
+    assert p.cu.tolist() == [0, 3, 3, 8] and p.q.shape == (1, 8, 1, 16) and p.h0.shape == (3, 2, 16, 8)
+    assert p.g.shape == (1, 8, 2)
