@@ -67,6 +67,7 @@ struct ChunkArgs {
   float* gc_ws;    // [B Hv][NC][kGS]         float32: scale e^{Gc_i} (i < 64), then e^{Gc_last}
   uint16_t* kt_ws; // [B Hv][NC][Dk][64]      bf16, (diag(e^{Gc_last - Gc}) K)^T
   uint16_t* sink;  // 4 KiB that absorbs the output stores of rows past the end
+  uint16_t* qs_ws; // [B Hv][NC][64][Dk]      bf16, scale diag(e^Gc) Q
   int64_t T;
   int Hk, Hv, grp, Dv, NC, NV;
   int n_blocks;
@@ -104,17 +105,22 @@ template <int DK, int DVM>
 __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
   constexpr int KP = DK + 8;
   constexpr int kKQ = 2 * kC * KP * 2;
-  constexpr int kAT = kC * kC * 4 + 2 * kC * kTP * 2;
+  constexpr int kSTP = kC + 4;                    // padded row (floats) of the float32 T
+  constexpr int kTB = 2 * kC * kTP * 2;           // Tw and Tu (bf16); the float32 T uses the same bytes
+  static_assert(kC * kSTP * 4 <= kTB, "T in the Tw/Tu bytes");
+  constexpr int kAT = kC * kC * 4 + kTB + 3 * 16 * 16 * 4;  // A, T (or Tw/Tu), three 16x16 temporaries
   constexpr int kR1 = kKQ > kAT ? kKQ : kAT;
   __shared__ __align__(16) unsigned char r1[kR1];
   __shared__ __align__(16) uint16_t sKt[DK][kTP];
   __shared__ __align__(16) uint16_t sVt[DVM][kTP];
-  __shared__ float sG[kC], sGc[kC], sBeta[kC];
+  __shared__ float sG[kC], sGc[kC], sBeta[kC], sEg[kC], sEl[kC];
   uint16_t(*sK)[KP] = reinterpret_cast<uint16_t(*)[KP]>(r1);
   uint16_t(*sQ)[KP] = reinterpret_cast<uint16_t(*)[KP]>(r1 + kC * KP * 2);
   float(*sA)[kC] = reinterpret_cast<float(*)[kC]>(r1);  // row i: A[i][4 t + s] at [s * 16 + t]
   uint16_t(*sTw)[kTP] = reinterpret_cast<uint16_t(*)[kTP]>(r1 + kC * kC * 4);
   uint16_t(*sTu)[kTP] = reinterpret_cast<uint16_t(*)[kTP]>(r1 + kC * kC * 4 + kC * kTP * 2);
+  float(*sT)[kSTP] = reinterpret_cast<float(*)[kSTP]>(r1 + kC * kC * 4);
+  float(*sM)[16][16] = reinterpret_cast<float(*)[16][16]>(r1 + kC * kC * 4 + kTB);
 
   const int bid = xcd_remap(blockIdx.x, p.n_blocks);
   const int c = bid % p.NC;
@@ -175,13 +181,37 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
   }
   __syncthreads();
   if (tid < kC) {
-    float acc = 0.f;
-    for (int m = 0; m <= tid; ++m) acc += sG[m];  // in token order, as a running sum
+    // inclusive prefix sum over the 64 lanes of wave 0 (log-step shuffles)
+    float acc = sG[tid];
+#pragma unroll
+    for (int d = 1; d < kC; d <<= 1) {
+      const float up = __shfl_up(acc, d, kC);
+      if (tid >= d) acc += up;
+    }
     sGc[tid] = acc;
   }
   __syncthreads();
-  if (tid < kC) p.gc_ws[chunk_id * kGS + tid] = p.scale * __expf(sGc[tid]);
+  if (tid < kC) {
+    const float eg = __expf(sGc[tid]);
+    sEg[tid] = eg;
+    sEl[tid] = __expf(sGc[kC - 1] - sGc[tid]);
+    p.gc_ws[chunk_id * kGS + tid] = p.scale * eg;
+  }
   if (tid == kC) p.gc_ws[chunk_id * kGS + kC] = __expf(sGc[kC - 1]);
+  // scale diag(e^Gc) Q, from the staged registers, for the state pass's read-out
+  {
+    const float f = rok ? p.scale * __expf(sGc[r]) : 0.f;
+    uint16_t* qw = p.qs_ws + (chunk_id * kC + r) * DK;
+#pragma unroll
+    for (int j = 0; j < NKG; ++j) {
+      const int part = (tid + kThreads * j) / kC;
+      u32x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[e] = f32x2_to_bf16x2(bf16_bits_to_f32(qr[j][e] & 0xFFFFu) * f, bf16_bits_to_f32(qr[j][e] >> 16) * f);
+      *reinterpret_cast<u32x4*>(qw + part * 8) = out;
+    }
+  }
   __syncthreads();
 
   // K K^T and Q K^T, one 32x32 tile of each per wave
@@ -213,38 +243,84 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
   }
   __syncthreads();
 
-  // T = (I + A)^{-1} by forward substitution, T[i][j] = [i == j] - sum_{m < i} A[i][m] T[m][j].
-  // Wave w solves columns 16 w .. 16 w + 15; the 4 lanes of a quad share column j, lane s of
-  // the quad holding T[4 t + s][j] (t = 0 .. 15) and summing those terms; a quad sum joins them.
+  // T = (I + A)^{-1} in 16 x 16 blocks. Diagonal blocks by forward substitution, one per wave:
+  // T[i][j] = [i == j] - sum_{m < i} A[i][m] T[m][j] within the block; the 4 lanes of a quad
+  // share column j, lane s holding rows 4 t + s of the block (t = 0 .. 3), a quad sum joining
+  // their terms. Then the blocks below the diagonal by their distance d from it:
+  // T[I][J] = -T[I][I] sum_{K = J}^{I - 1} A[I][K] T[K][J], with I = J + d.
   {
-    const int j = wave * 16 + (lane >> 2), s = lane & 3;
-    float tr[16];
+    const int w16 = wave * 16;
+    const int j = w16 + (lane >> 2), s = lane & 3;
+    float tr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 16; ++t) tr[t] = 0.f;
-#pragma unroll
-    for (int i = 0; i < kC; ++i) {
-      const float4* ar = reinterpret_cast<const float4*>(&sA[i][s * 16]);
-      float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 a = ar[q4];
-        a0 = fmaf(a.x, tr[4 * q4], a0);
-        a1 = fmaf(a.y, tr[4 * q4 + 1], a1);
-        a0 = fmaf(a.z, tr[4 * q4 + 2], a0);
-        a1 = fmaf(a.w, tr[4 * q4 + 3], a1);
-      }
-      float sum = dpp_sum_step<0xB1>(a0 + a1);
+    for (int i = 0; i < 16; ++i) {
+      const float4 a = *reinterpret_cast<const float4*>(&sA[w16 + i][s * 16 + 4 * wave]);
+      float sum = fmaf(a.x, tr[0], a.y * tr[1]) + fmaf(a.z, tr[2], a.w * tr[3]);
+      sum = dpp_sum_step<0xB1>(sum);
       sum = dpp_sum_step<0x4E>(sum);
-      const float tij = (i == j ? 1.f : 0.f) - sum;
+      const float tij = (w16 + i == j ? 1.f : 0.f) - sum;
       if (s == (i & 3)) tr[i >> 2] = tij;
     }
-    const float bj = sBeta[j], ej = bj * __expf(sGc[j]);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int m = 4 * t + s;
-      sTw[m][j] = f32_to_bf16(tr[t] * ej);
-      sTu[m][j] = f32_to_bf16(tr[t] * bj);
+    for (int t = 0; t < 4; ++t) sT[w16 + 4 * t + s][j] = tr[t];
+  }
+  __syncthreads();
+  {
+    const int r = tid >> 4, cc = tid & 15;  // element (r, cc) of a 16 x 16 block
+    // A[row][16 K + x] for x = 0 .. 15, from A's permuted rows
+    auto arow = [&](int row, int K, float* x16) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float4 v = *reinterpret_cast<const float4*>(&sA[row][s4 * 16 + 4 * K]);
+        x16[s4] = v.x;
+        x16[s4 + 4] = v.y;
+        x16[s4 + 8] = v.z;
+        x16[s4 + 12] = v.w;
+      }
+    };
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      for (int J = 0; J + d < 4; ++J) {
+        const int I = J + d;
+        float m = 0.f;
+        for (int K = J; K < I; ++K) {
+          float x16[16];
+          arow(16 * I + r, K, x16);
+#pragma unroll
+          for (int x = 0; x < 16; ++x) m = fmaf(x16[x], sT[16 * K + x][16 * J + cc], m);
+        }
+        sM[J][r][cc] = m;
+      }
+      __syncthreads();
+      for (int J = 0; J + d < 4; ++J) {
+        const int I = J + d;
+        float t = 0.f;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) t = fmaf(sT[16 * I + r][16 * I + x], sM[J][x][cc], t);
+        sT[16 * I + r][16 * J + cc] = -t;
+      }
+      __syncthreads();
     }
+  }
+  // Tw = T diag(beta e^Gc), Tu = T diag(beta) in bf16, over the float32 T's bytes
+  {
+    const int m = tid >> 2, j0 = (tid & 3) * 16;
+    float tv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tv[e] = (j0 + e <= m) ? sT[m][j0 + e] : 0.f;  // T is lower triangular
+    __syncthreads();
+    u32x4 w2[2], u2[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ja = j0 + 2 * e, jb = ja + 1;
+      const float ba = sBeta[ja], bb = sBeta[jb];
+      w2[e >> 2][e & 3] = f32x2_to_bf16x2(tv[2 * e] * ba * sEg[ja], tv[2 * e + 1] * bb * sEg[jb]);
+      u2[e >> 2][e & 3] = f32x2_to_bf16x2(tv[2 * e] * ba, tv[2 * e + 1] * bb);
+    }
+    *reinterpret_cast<u32x4*>(&sTw[m][j0]) = w2[0];
+    *reinterpret_cast<u32x4*>(&sTw[m][j0 + 8]) = w2[1];
+    *reinterpret_cast<u32x4*>(&sTu[m][j0]) = u2[0];
+    *reinterpret_cast<u32x4*>(&sTu[m][j0 + 8]) = u2[1];
   }
   __syncthreads();
 
@@ -288,7 +364,6 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
   }
   // (e^{Gc_last - Gc} K)^T -> kt_ws row-major [DK][64]
   {
-    const float gl = sGc[kC - 1];
     uint16_t* kw = p.kt_ws + chunk_id * DK * kC;
     for (int idx = tid; idx < DK * 8; idx += kThreads) {
       const int d = idx >> 3, part = idx & 7;
@@ -297,8 +372,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = part * 8 + 2 * e;
-        out[e] = f32x2_to_bf16x2(bf16_bits_to_f32(kv[e] & 0xFFFFu) * __expf(gl - sGc[m]),
-                                 bf16_bits_to_f32(kv[e] >> 16) * __expf(gl - sGc[m + 1]));
+        out[e] = f32x2_to_bf16x2(bf16_bits_to_f32(kv[e] & 0xFFFFu) * sEl[m], bf16_bits_to_f32(kv[e] >> 16) * sEl[m + 1]);
       }
       *reinterpret_cast<u32x4*>(kw + d * kC + part * 8) = out;
     }
@@ -307,25 +381,21 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
 
 // ------------------------------------------------------------------ state pass
 
-// Operands of one chunk for one wave, loaded from global memory straight into MFMA fragment
-// registers (lane l: row l % 32 of its tile, 8 consecutive k at 8 (l / 32)). Every wave issues
-// the same loads in the same order (at in-bounds addresses, some unused by its role), so the
-// compiler's count of outstanding loads stays exact and the prefetch is never waited for early.
-template <int DK>
-struct ChunkOps {
-  u32x4 a[DK / 16];  // U waves: rows of -W; O waves: rows of Q
-  u32x4 pk[4];       // rows of P
-  u32x4 kt[4];       // rows of the decayed K^T
-  u32x4 u[2];        // U~ in accumulator order
-  float4 gc[4];      // scale e^{Gc} of the accumulator rows
-  float glast;
-};
+// The state pass: one workgroup of 8 waves per (value head, 32-column tile of the state),
+// walking the chunks in order. Roles, each in a loop of its own with the same two barriers
+// per chunk:
+//   waves 0, 1 (U): U = U~ + (-W) S for token rows 32 w .. 32 w + 31, to LDS as bf16;
+//   waves 2, 3 (O): scale e^Gc Q S, then + scale P U, for those rows, to LDS, then out;
+//   waves 4 .. 4 + Dk/32 - 1 (S): state rows 32 (w - 4) .. + 31 in MFMA accumulators,
+//     S = e^{Gc_last} S + (e^{Gc_last - Gc} K)^T U, and their bf16 copy in LDS.
+// A operands come from global memory straight into registers one chunk ahead; each role's
+// loop issues the same loads every chunk, so the compiler's count of outstanding loads is
+// exact and the prefetch is not waited for early. B operands (the state's and U's bf16
+// copies) pass through LDS.
+constexpr int kStateThreads = 512;
 
-// One workgroup per (value head, 32-column tile of the state); waves 0 and 1 compute the
-// corrected writes U for token rows 0-31 and 32-63, waves 2 and 3 the outputs of those rows,
-// and wave w < Dk / 32 owns state rows 32 w .. 32 w + 31.
 template <int DK>
-__global__ __launch_bounds__(kThreads) void gdn_chunk_state(ChunkArgs p) {
+__global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
   constexpr int KP = DK + 8;
   constexpr int ST = DK / 32;
   constexpr int KS = DK / 16;
@@ -336,142 +406,146 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_state(ChunkArgs p) {
   const int bid = xcd_remap(blockIdx.x, p.n_blocks);
   const int tv = bid % p.NV;
   const int bh = bid / p.NV;
-  const int h = bh % p.Hv, b = bh / p.Hv, kh = h / p.grp;
+  const int h = bh % p.Hv, b = bh / p.Hv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = tv * 32 + (lane & 31);
   const int kb8 = (lane >> 5) * 8;
-  const int ti = wave & 1;
-  const bool uwave = wave < 2;
-  const bool owns_s = wave < ST;
-  const int kw = wave % ST;  // state rows whose K^T this wave loads
-  const int arow = ti * 32 + (lane & 31);
   const int64_t st_base = (int64_t)bh * DK * p.Dv;
+  const int NC = p.NC;
 
-  auto load = [&](int c, ChunkOps<DK>& o) {
-    const int64_t cid = (int64_t)bh * p.NC + c;
-    const int64_t t0 = (int64_t)c * kC;
-    const int64_t qrow = t0 + arow < p.T ? t0 + arow : t0;  // rows past the end: any valid row
-    const uint16_t* ab = uwave ? p.w_ws + (cid * kC + arow) * DK + kb8
-                               : p.q + (((int64_t)b * p.T + qrow) * p.Hk + kh) * DK + kb8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) o.a[ks] = *reinterpret_cast<const u32x4*>(ab + ks * 16);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      o.pk[ks] = *reinterpret_cast<const u32x4*>(p.p_ws + (cid * kC + arow) * kC + ks * 16 + kb8);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      o.kt[ks] = *reinterpret_cast<const u32x4*>(p.kt_ws + (cid * DK + kw * 32 + (lane & 31)) * kC + ks * 16 + kb8);
-    const uint16_t* uw = p.u_ws + (((cid * p.NV + tv) * 2 + ti) * 64 + lane) * 16;
-    o.u[0] = *reinterpret_cast<const u32x4*>(uw);
-    o.u[1] = *reinterpret_cast<const u32x4*>(uw + 8);
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
-      o.gc[g4] = *reinterpret_cast<const float4*>(p.gc_ws + cid * kGS + ti * 32 + g4 * 8 + (lane >> 5) * 4);
-    o.glast = p.gc_ws[cid * kGS + kC];
-  };
-
-  // state tile of this wave: keys 32 w .. 32 w + 31, columns col; key of register r
-  f32x16 s_acc = {};
-  auto srow = [&](int r) { return kw * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
-  auto sidx = [&](int d) -> int64_t {
-    return st_base + (p.v_first ? (int64_t)col * DK + d : (int64_t)d * p.Dv + col);
-  };
-  auto write_sS = [&]() {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = wave * 32 + g4 * 8 + (lane >> 5) * 4;
-      *reinterpret_cast<u32x2*>(&sS[lane & 31][d]) =
-          u32x2{f32x2_to_bf16x2(s_acc[4 * g4], s_acc[4 * g4 + 1]), f32x2_to_bf16x2(s_acc[4 * g4 + 2], s_acc[4 * g4 + 3])};
-    }
-  };
-  if (p.h0 != nullptr) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s_acc[r] = p.h0[sidx(srow(r))];
-  }
-  if (owns_s) write_sS();
-
-  // the output rows of one chunk, from LDS: thread -> token row tid / 4, 8 columns at 8 (tid % 4)
-  const int orow = tid >> 2, ocol = (tid & 3) * 8;
+  // the output rows of one chunk, from LDS, by the U and O waves: thread -> token row tid / 4,
+  // 8 columns at 8 (tid % 4); rows past the end go to the sink
   auto store_out = [&](int c) {
+    const int orow = tid >> 2, ocol = (tid & 3) * 8;
     const int64_t t0 = (int64_t)c * kC;
     const u32x4 val = *reinterpret_cast<const u32x4*>(&sO[orow][ocol]);
     uint16_t* dst = t0 + orow < p.T ? p.o + (((int64_t)b * p.T + t0 + orow) * p.Hv + h) * p.Dv + tv * 32 + ocol
                                     : p.sink + tid * 8;
     *reinterpret_cast<u32x4*>(dst) = val;
   };
+  auto bsS = [&](int ks) { return ld8(&sS[lane & 31][ks * 16 + kb8]); };
+  auto bsU = [&](int ks) { return ld8(&sU[lane & 31][ks * 16 + kb8]); };
 
-  auto step = [&](int c, const ChunkOps<DK>& o) {
-    f32x16 acc = {};
-    if (uwave) {
+  if (wave < 4) {
+    const bool is_u = wave < 2;
+    const int ti = wave & 1;
+    const int arow = ti * 32 + (lane & 31);
+    struct Ops {
+      u32x4 a[KS];
+      u32x4 x[4];  // U waves: U~ (two registers used); O waves: rows of P
+    };
+    auto load = [&](int c, Ops& o) {
+      const int64_t cid = (int64_t)bh * NC + c;
+      const uint16_t* ab = (is_u ? p.w_ws : p.qs_ws) + (cid * kC + arow) * DK + kb8;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = bf16_bits_to_f32(o.u[0][e] & 0xFFFFu);
-        acc[2 * e + 1] = bf16_bits_to_f32(o.u[0][e] >> 16);
-        acc[8 + 2 * e] = bf16_bits_to_f32(o.u[1][e] & 0xFFFFu);
-        acc[8 + 2 * e + 1] = bf16_bits_to_f32(o.u[1][e] >> 16);
+      for (int ks = 0; ks < KS; ++ks) o.a[ks] = *reinterpret_cast<const u32x4*>(ab + ks * 16);
+      const uint16_t* xb = is_u ? p.u_ws + (((cid * p.NV + tv) * 2 + ti) * 64 + lane) * 16
+                                : p.p_ws + (cid * kC + arow) * kC + kb8;
+      const int xs = is_u ? 8 : 16;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) o.x[k4] = *reinterpret_cast<const u32x4*>(xb + (k4 & (is_u ? 1 : 3)) * xs);
+    };
+    auto step = [&](int c, const Ops& o) {
+      f32x16 acc = {};
+      if (is_u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = bf16_bits_to_f32(o.x[0][e] & 0xFFFFu);
+          acc[2 * e + 1] = bf16_bits_to_f32(o.x[0][e] >> 16);
+          acc[8 + 2 * e] = bf16_bits_to_f32(o.x[1][e] & 0xFFFFu);
+          acc[8 + 2 * e + 1] = bf16_bits_to_f32(o.x[1][e] >> 16);
+        }
       }
-    }
-    // U = U~ + (-W) S0 (U waves); Q S0 (O waves)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = mfma32(__builtin_bit_cast(bf16x8, o.a[ks]), ld8(&sS[lane & 31][ks * 16 + kb8]), acc);
-    if (uwave) {
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32(__builtin_bit_cast(bf16x8, o.a[ks]), bsS(ks), acc);
+      if (is_u) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int i = ti * 32 + g4 * 8 + (lane >> 5) * 4;
+          *reinterpret_cast<u32x2*>(&sU[lane & 31][i]) =
+              u32x2{f32x2_to_bf16x2(acc[4 * g4], acc[4 * g4 + 1]), f32x2_to_bf16x2(acc[4 * g4 + 2], acc[4 * g4 + 3])};
+        }
+      }
+      __syncthreads();  // (1) U complete; the state tile is no longer read
+      if (!is_u) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma32(__builtin_bit_cast(bf16x8, o.x[ks]), bsU(ks), acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sO[ti * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)][lane & 31] = f32_to_bf16(acc[r]);
+      }
+      __syncthreads();  // (2) outputs and the new state tile written; U no longer read
+      store_out(c);
+    };
+    Ops o0, o1;
+    if (NC > 0) load(0, o0);
+    __syncthreads();  // (0) initial state tile written
+    for (int c = 0; c < NC; c += 2) {
+      load(c + 1 < NC ? c + 1 : c, o1);
+      step(c, o0);
+      if (c + 1 >= NC) break;
+      load(c + 2 < NC ? c + 2 : c + 1, o0);
+      step(c + 1, o1);
+    }
+  } else {
+    const int sw = wave - 4;
+    const bool owns = sw < ST;
+    const int kw = owns ? sw : 0;
+    f32x16 s_acc = {};
+    auto srow = [&](int r) { return kw * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
+    auto sidx = [&](int d) -> int64_t {
+      return st_base + (p.v_first ? (int64_t)col * DK + d : (int64_t)d * p.Dv + col);
+    };
+    if (p.h0 != nullptr) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_acc[r] = p.h0[sidx(srow(r))];
+    }
+    auto write_sS = [&]() {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int i = ti * 32 + g4 * 8 + (lane >> 5) * 4;
-        *reinterpret_cast<u32x2*>(&sU[lane & 31][i]) =
-            u32x2{f32x2_to_bf16x2(acc[4 * g4], acc[4 * g4 + 1]), f32x2_to_bf16x2(acc[4 * g4 + 2], acc[4 * g4 + 3])};
+        const int d = kw * 32 + g4 * 8 + (lane >> 5) * 4;
+        *reinterpret_cast<u32x2*>(&sS[lane & 31][d]) = u32x2{f32x2_to_bf16x2(s_acc[4 * g4], s_acc[4 * g4 + 1]),
+                                                             f32x2_to_bf16x2(s_acc[4 * g4 + 2], s_acc[4 * g4 + 3])};
       }
-    } else {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        acc[4 * g4] *= o.gc[g4].x;
-        acc[4 * g4 + 1] *= o.gc[g4].y;
-        acc[4 * g4 + 2] *= o.gc[g4].z;
-        acc[4 * g4 + 3] *= o.gc[g4].w;
-      }
-    }
-    __syncthreads();  // U complete; the state tile is no longer read; last chunk's outputs are out
-
-    if (!uwave) {
-      // O = scale (e^Gc Q S0 + P U), to LDS (scale is folded into e^Gc and P)
+    };
+    if (owns) write_sS();
+    struct Ops {
+      u32x4 kt[4];
+      float el;
+    };
+    auto load = [&](int c, Ops& o) {
+      const int64_t cid = (int64_t)bh * NC + c;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = mfma32(__builtin_bit_cast(bf16x8, o.pk[ks]), ld8(&sU[lane & 31][ks * 16 + kb8]), acc);
+        o.kt[ks] = *reinterpret_cast<const u32x4*>(p.kt_ws + (cid * DK + kw * 32 + (lane & 31)) * kC + ks * 16 + kb8);
+      o.el = p.gc_ws[cid * kGS + kC];
+    };
+    auto step = [&](const Ops& o) {
+      __syncthreads();  // (1) U complete
+      if (owns) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sO[ti * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)][lane & 31] = f32_to_bf16(acc[r]);
+        for (int r = 0; r < 16; ++r) s_acc[r] *= o.el;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) s_acc = mfma32(__builtin_bit_cast(bf16x8, o.kt[ks]), bsU(ks), s_acc);
+        write_sS();
+      }
+      __syncthreads();  // (2)
+    };
+    Ops o0, o1;
+    if (NC > 0) load(0, o0);
+    __syncthreads();  // (0)
+    for (int c = 0; c < NC; c += 2) {
+      load(c + 1 < NC ? c + 1 : c, o1);
+      step(o0);
+      if (c + 1 >= NC) break;
+      load(c + 2 < NC ? c + 2 : c + 1, o0);
+      step(o1);
     }
-    if (owns_s) {
-      // S1 = e^{Gc_last} S0 + (e^{Gc_last - Gc} K)^T U
+    if (owns && p.h_last != nullptr) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_acc[r] *= o.glast;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        s_acc = mfma32(__builtin_bit_cast(bf16x8, o.kt[ks]), ld8(&sU[lane & 31][ks * 16 + kb8]), s_acc);
-      write_sS();
+      for (int r = 0; r < 16; ++r) p.h_last[sidx(srow(r))] = s_acc[r];
     }
-    __syncthreads();  // the new state tile and the outputs are written; U is no longer read
-    store_out(c);
-  };
-
-  ChunkOps<DK> o0, o1;
-  if (p.NC > 0) load(0, o0);
-  __syncthreads();
-  // the prefetch is unconditional (the last chunk reloads itself) so that every path issues
-  // the same loads
-  for (int c = 0; c < p.NC; c += 2) {
-    load(c + 1 < p.NC ? c + 1 : c, o1);
-    step(c, o0);
-    if (c + 1 >= p.NC) break;
-    load(c + 2 < p.NC ? c + 2 : c + 1, o0);
-    step(c + 1, o1);
-  }
-
-  if (owns_s && p.h_last != nullptr) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p.h_last[sidx(srow(r))] = s_acc[r];
   }
 }
 
@@ -487,13 +561,13 @@ hipError_t launch(ChunkArgs a, int64_t prep_blocks, int64_t state_blocks, hipStr
     if (e != hipSuccess) return e;
   }
   a.n_blocks = (int)state_blocks;
-  hipLaunchKernelGGL(gdn_chunk_state<DK>, dim3((unsigned)state_blocks), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(gdn_chunk_state<DK>, dim3((unsigned)state_blocks), dim3(kStateThreads), 0, st, a);
   return hipGetLastError();
 }
 
 struct Plan {
   int64_t NC, NV, prep_blocks, state_blocks;
-  size_t w_off, u_off, p_off, g_off, kt_off, sink_off, bytes;
+  size_t w_off, u_off, p_off, g_off, kt_off, qs_off, sink_off, bytes;
 };
 
 // Validates the shape for the chunk form; fills the workspace plan.
@@ -526,7 +600,8 @@ rglru_status_t plan(const rglru_delta_shape_t* sp, const int32_t* cu, Plan* pl) 
   pl->p_off = round_up(pl->u_off + chunks * kC * s.v_dim * 2, 256);
   pl->g_off = round_up(pl->p_off + chunks * kC * kC * 2, 256);
   pl->kt_off = round_up(pl->g_off + chunks * kGS * 4, 256);
-  pl->sink_off = round_up(pl->kt_off + chunks * kC * s.k_dim * 2, 256);
+  pl->qs_off = round_up(pl->kt_off + chunks * kC * s.k_dim * 2, 256);
+  pl->sink_off = round_up(pl->qs_off + chunks * kC * s.k_dim * 2, 256);
   pl->bytes = pl->sink_off + 4096;
   return RGLRU_OK;
 }
@@ -579,6 +654,7 @@ extern "C" rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape
   a.gc_ws = reinterpret_cast<float*>(ws + pl.g_off);
   a.kt_ws = reinterpret_cast<uint16_t*>(ws + pl.kt_off);
   a.sink = reinterpret_cast<uint16_t*>(ws + pl.sink_off);
+  a.qs_ws = reinterpret_cast<uint16_t*>(ws + pl.qs_off);
   a.T = s.length;
   a.Hk = s.k_heads;
   a.Hv = s.v_heads;
