@@ -64,7 +64,7 @@ struct ChunkArgs {
   uint16_t* w_ws;  // [B Hv][NC][64][Dk]      bf16, -W
   uint16_t* u_ws;  // [B Hv][NC][Dv/32][2][64 lanes][16] bf16, Ut in accumulator order
   uint16_t* p_ws;  // [B Hv][NC][64][64]      bf16, scale P
-  float* gc_ws;    // [B Hv][NC][kGS]         float32: scale e^{Gc_i} (i < 64), then e^{Gc_last}
+  float* gc_ws;    // [B Hv][NC][kGS]         float32: scale e^{Gc_i} (i < 64), then e^{Gc_last} twice
   uint16_t* kt_ws; // [B Hv][NC][Dk][64]      bf16, (diag(e^{Gc_last - Gc}) K)^T
   uint16_t* sink;  // 4 KiB that absorbs the output stores of rows past the end
   uint16_t* qs_ws; // [B Hv][NC][64][Dk]      bf16, scale diag(e^Gc) Q
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
     sEl[tid] = __expf(sGc[kC - 1] - sGc[tid]);
     p.gc_ws[chunk_id * kGS + tid] = p.scale * eg;
   }
-  if (tid == kC) p.gc_ws[chunk_id * kGS + kC] = __expf(sGc[kC - 1]);
+  if (tid == kC || tid == kC + 1) p.gc_ws[chunk_id * kGS + tid] = __expf(sGc[kC - 1]);  // two copies
   // scale diag(e^Gc) Q, from the staged registers, for the state pass's read-out
   {
     const float f = rok ? p.scale * __expf(sGc[r]) : 0.f;
@@ -414,14 +414,15 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
   const int64_t st_base = (int64_t)bh * DK * p.Dv;
   const int NC = p.NC;
 
-  // the output rows of one chunk, from LDS, by the U and O waves: thread -> token row tid / 4,
-  // 8 columns at 8 (tid % 4); rows past the end go to the sink
+  // the output rows of one chunk, from LDS, by the S waves (idle until U is complete):
+  // thread -> token row / 4, 8 columns at 8 (thread % 4); rows past the end go to the sink
   auto store_out = [&](int c) {
-    const int orow = tid >> 2, ocol = (tid & 3) * 8;
+    const int st = tid - 256;
+    const int orow = st >> 2, ocol = (st & 3) * 8;
     const int64_t t0 = (int64_t)c * kC;
     const u32x4 val = *reinterpret_cast<const u32x4*>(&sO[orow][ocol]);
     uint16_t* dst = t0 + orow < p.T ? p.o + (((int64_t)b * p.T + t0 + orow) * p.Hv + h) * p.Dv + tv * 32 + ocol
-                                    : p.sink + tid * 8;
+                                    : p.sink + st * 8;
     *reinterpret_cast<u32x4*>(dst) = val;
   };
   auto bsS = [&](int ks) { return ld8(&sS[lane & 31][ks * 16 + kb8]); };
@@ -446,7 +447,9 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) o.x[k4] = *reinterpret_cast<const u32x4*>(xb + (k4 & (is_u ? 1 : 3)) * xs);
     };
-    auto step = [&](int c, const Ops& o) {
+    // pf: the chunk whose operands are loaded into nx once this wave's part before barrier (1) is
+    // done (off the corrected writes' critical path)
+    auto step = [&](int c, const Ops& o, int pf, Ops& nx) {
       f32x16 acc = {};
       if (is_u) {
 #pragma unroll
@@ -467,6 +470,7 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
               u32x2{f32x2_to_bf16x2(acc[4 * g4], acc[4 * g4 + 1]), f32x2_to_bf16x2(acc[4 * g4 + 2], acc[4 * g4 + 3])};
         }
       }
+      load(pf, nx);
       __syncthreads();  // (1) U complete; the state tile is no longer read
       if (!is_u) {
 #pragma unroll
@@ -476,17 +480,14 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
           sO[ti * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)][lane & 31] = f32_to_bf16(acc[r]);
       }
       __syncthreads();  // (2) outputs and the new state tile written; U no longer read
-      store_out(c);
     };
     Ops o0, o1;
     if (NC > 0) load(0, o0);
     __syncthreads();  // (0) initial state tile written
     for (int c = 0; c < NC; c += 2) {
-      load(c + 1 < NC ? c + 1 : c, o1);
-      step(c, o0);
+      step(c, o0, c + 1 < NC ? c + 1 : c, o1);
       if (c + 1 >= NC) break;
-      load(c + 2 < NC ? c + 2 : c + 1, o0);
-      step(c + 1, o1);
+      step(c + 1, o1, c + 2 < NC ? c + 2 : c + 1, o0);
     }
   } else {
     const int sw = wave - 4;
@@ -501,6 +502,7 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_acc[r] = p.h0[sidx(srow(r))];
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the initial state is in registers before the loop
     auto write_sS = [&]() {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -512,16 +514,19 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
     if (owns) write_sS();
     struct Ops {
       u32x4 kt[4];
-      float el;
+      float el;  // e^{Gc_last}
     };
     auto load = [&](int c, Ops& o) {
       const int64_t cid = (int64_t)bh * NC + c;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         o.kt[ks] = *reinterpret_cast<const u32x4*>(p.kt_ws + (cid * DK + kw * 32 + (lane & 31)) * kC + ks * 16 + kb8);
-      o.el = p.gc_ws[cid * kGS + kC];
+      // a vector load (its address depends on the lane: either of the two copies), issued here with
+      // the other prefetches rather than reloaded at its use
+      o.el = p.gc_ws[cid * kGS + kC + (lane & 1)];
     };
-    auto step = [&](const Ops& o) {
+    auto step = [&](int c, const Ops& o) {
+      if (c > 0) store_out(c - 1);
       __syncthreads();  // (1) U complete
       if (owns) {
 #pragma unroll
@@ -537,11 +542,12 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
     __syncthreads();  // (0)
     for (int c = 0; c < NC; c += 2) {
       load(c + 1 < NC ? c + 1 : c, o1);
-      step(o0);
+      step(c, o0);
       if (c + 1 >= NC) break;
       load(c + 2 < NC ? c + 2 : c + 1, o0);
-      step(o1);
+      step(c + 1, o1);
     }
+    if (NC > 0) store_out(NC - 1);
     if (owns && p.h_last != nullptr) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) p.h_last[sidx(srow(r))] = s_acc[r];
