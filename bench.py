@@ -350,7 +350,7 @@ def run_delta(args, wid, steps, warmup):
     chunk = None
     shape = glr.ops._lib.rglru_delta_shape_t(B, T, wl.k_heads, Hv, Dk, Dv, 1 if wl.io == "bf16" else 0,
                                              1 if wl.kda else 0, 0, 1.0)
-    ws_bytes = glr.rglru_delta_chunk_workspace_bytes(shape)
+    ws_bytes = glr.rglru_delta_chunk_workspace_bytes(shape, 0)
     if ws_bytes > 0 and T >= 64:
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 

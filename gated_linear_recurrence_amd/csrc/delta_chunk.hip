@@ -61,15 +61,20 @@ struct ChunkArgs {
   const float* h0;
   uint16_t* o;
   float* h_last;
-  uint16_t* w_ws;  // [B Hv][NC][64][Dk]      bf16, -W
-  uint16_t* u_ws;  // [B Hv][NC][Dv/32][2][64 lanes][16] bf16, Ut in accumulator order
-  uint16_t* p_ws;  // [B Hv][NC][64][64]      bf16, scale P
-  float* gc_ws;    // [B Hv][NC][kGS]         float32: scale e^{Gc_i} (i < 64), then e^{Gc_last} twice
-  uint16_t* kt_ws; // [B Hv][NC][Dk][64]      bf16, (diag(e^{Gc_last - Gc}) K)^T
+  // per (value head, chunk) = h * NCW + g, g counting the chunks of all sequences in order:
+  uint16_t* w_ws;  // [64][Dk]                 bf16, -W
+  uint16_t* u_ws;  // [Dv/32][2][64 lanes][16] bf16, Ut in accumulator order
+  uint16_t* p_ws;  // [64][64]                 bf16, scale P
+  float* gc_ws;    // [kGS]                    float32: scale e^{Gc_i} (i < 64), then e^{Gc_last} twice
+  uint16_t* kt_ws; // [Dk][64]                 bf16, (diag(e^{Gc_last - Gc}) K)^T
   uint16_t* sink;  // 4 KiB that absorbs the output stores of rows past the end
-  uint16_t* qs_ws; // [B Hv][NC][64][Dk]      bf16, scale diag(e^Gc) Q
+  uint16_t* qs_ws; // [64][Dk]                 bf16, scale diag(e^Gc) Q
+  const int32_t* cu;  // packed sequence offsets (n_seqs + 1), or NULL: B rows of T tokens
+  int* cs;            // with cu: first chunk of each sequence (n_seqs + 1 entries), in the workspace
   int64_t T;
   int Hk, Hv, grp, Dv, NC, NV;
+  int NCW;            // chunks per value head in the workspace: B * NC, or ceil(T / 64) + n_seqs
+  int n_seqs;
   int n_blocks;
   int v_first;
   float scale;
@@ -95,6 +100,72 @@ __device__ __forceinline__ uint16_t h16(u32x4 v, int e) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_sum_step(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// A sequence's tokens [t0, t1) of the flattened [B * T] token axis and its chunks [c0, c1).
+struct Seq {
+  int64_t t0, t1;
+  int c0, c1;
+};
+
+__device__ __forceinline__ Seq seq_info(const ChunkArgs& p, int n) {
+  if (p.cu != nullptr) {
+    int64_t a = p.cu[n], b = p.cu[n + 1];
+    a = a < 0 ? 0 : (a > p.T ? p.T : a);
+    b = b < a ? a : (b > p.T ? p.T : b);
+    return {a, b, p.cs[n], p.cs[n + 1]};
+  }
+  return {(int64_t)n * p.T, (int64_t)(n + 1) * p.T, n * p.NC, (n + 1) * p.NC};
+}
+
+// The sequence holding chunk g (g below the total): the last n with cs[n] <= g.
+__device__ __forceinline__ int seq_of_chunk(const ChunkArgs& p, int g) {
+  if (p.cu == nullptr) return g / p.NC;
+  int lo = 0, hi = p.n_seqs;  // cs[lo] <= g < cs[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.cs[mid] <= g) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// cs[n] = sum over m < n of ceil(len_m / 64) with the offsets clamped as in seq_info, cs[n_seqs]
+// the total; each clamped to NCW (valid offsets never reach it; invalid ones, whose clamped
+// sequences may overlap, then get unspecified but in-bounds results). One workgroup, the
+// sequences in tiles of 1024 with a block-wide scan per tile, in 64-bit sums.
+__global__ __launch_bounds__(1024) void gdn_chunk_map(ChunkArgs p) {
+  __shared__ long long part[1024];
+  __shared__ long long carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < p.n_seqs; base += 1024) {
+    const int n = base + tid;
+    long long v = 0;
+    if (n < p.n_seqs) {
+      int64_t a = p.cu[n], b = p.cu[n + 1];
+      a = a < 0 ? 0 : (a > p.T ? p.T : a);
+      b = b < a ? a : (b > p.T ? p.T : b);
+      v = (b - a + kC - 1) / kC;
+    }
+    part[tid] = v;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const long long add = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    const long long c0 = carry;
+    if (n < p.n_seqs) {
+      const long long e = c0 + part[tid] - v;
+      p.cs[n] = (int)(e < p.NCW ? e : p.NCW);
+    }
+    __syncthreads();
+    if (tid == 1023) carry = c0 + part[1023];
+    __syncthreads();
+  }
+  if (tid == 0) p.cs[p.n_seqs] = (int)(carry < p.NCW ? carry : p.NCW);
 }
 
 // ------------------------------------------------------------------ prep
@@ -123,13 +194,14 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
   float(*sM)[16][16] = reinterpret_cast<float(*)[16][16]>(r1 + kC * kC * 4 + kTB);
 
   const int bid = xcd_remap(blockIdx.x, p.n_blocks);
-  const int c = bid % p.NC;
-  const int bh = bid / p.NC;
-  const int h = bh % p.Hv, b = bh / p.Hv, kh = h / p.grp;
-  const int64_t t0 = (int64_t)c * kC;
-  const int n = (int)(p.T - t0 < kC ? p.T - t0 : kC);
+  const int g = bid % p.NCW;
+  const int h = bid / p.NCW, kh = h / p.grp;
+  if (p.cu != nullptr && g >= p.cs[p.n_seqs]) return;  // the grid covers the most chunks any offsets give
+  const Seq sq = seq_info(p, seq_of_chunk(p, g));
+  const int64_t t0 = sq.t0 + (int64_t)(g - sq.c0) * kC;  // first token of the chunk (flattened)
+  const int n = (int)(sq.t1 - t0 < kC ? sq.t1 - t0 : kC);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t chunk_id = (int64_t)bh * p.NC + c;
+  const int64_t chunk_id = (int64_t)h * p.NCW + g;
 
   // stage K and Q (row-major, K also transposed) and V (transposed), zero past the end; the
   // token index runs fastest across lanes so each transposed 2-byte write fills one row. Every
@@ -138,8 +210,8 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
   constexpr int NVG = kC * (DVM / 8) / kThreads;
   const int r = tid & (kC - 1);
   const bool rok = r < n;
-  const int64_t rowq = ((int64_t)b * p.T + t0 + (rok ? r : 0)) * p.Hk + kh;
-  const int64_t rowv = ((int64_t)b * p.T + t0 + (rok ? r : 0)) * p.Hv + h;
+  const int64_t rowq = (t0 + (rok ? r : 0)) * p.Hk + kh;
+  const int64_t rowv = (t0 + (rok ? r : 0)) * p.Hv + h;
   u32x4 kr[NKG], qr[NKG], vr[NVG];
 #pragma unroll
   for (int j = 0; j < NKG; ++j) {
@@ -153,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep(ChunkArgs p) {
     const int part = (tid + kThreads * j) / kC;
     vr[j] = *reinterpret_cast<const u32x4*>(p.v + rowv * p.Dv + (part < vparts ? part : 0) * 8);
   }
-  const int64_t eg = ((int64_t)b * p.T + t0 + (tid < n ? tid : 0)) * p.Hv + h;
+  const int64_t eg = (t0 + (tid < n ? tid : 0)) * p.Hv + h;
   const float gv = p.g[eg], bv = p.beta[eg];
 #pragma unroll
   for (int j = 0; j < NKG; ++j) {
@@ -405,24 +477,25 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
 
   const int bid = xcd_remap(blockIdx.x, p.n_blocks);
   const int tv = bid % p.NV;
-  const int bh = bid / p.NV;
-  const int h = bh % p.Hv, b = bh / p.Hv;
+  const int bh = bid / p.NV;  // sequence * Hv + value head
+  const int h = bh % p.Hv, seq = bh / p.Hv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = tv * 32 + (lane & 31);
   const int kb8 = (lane >> 5) * 8;
   const int64_t st_base = (int64_t)bh * DK * p.Dv;
-  const int NC = p.NC;
+  const Seq sq = seq_info(p, seq);
+  const int NC = sq.c1 - sq.c0;                      // this sequence's chunks
+  const int64_t cid0 = (int64_t)h * p.NCW + sq.c0;   // workspace index of its first chunk
 
   // the output rows of one chunk, from LDS, by the S waves (idle until U is complete):
   // thread -> token row / 4, 8 columns at 8 (thread % 4); rows past the end go to the sink
   auto store_out = [&](int c) {
     const int st = tid - 256;
     const int orow = st >> 2, ocol = (st & 3) * 8;
-    const int64_t t0 = (int64_t)c * kC;
+    const int64_t t0 = sq.t0 + (int64_t)c * kC;
     const u32x4 val = *reinterpret_cast<const u32x4*>(&sO[orow][ocol]);
-    uint16_t* dst = t0 + orow < p.T ? p.o + (((int64_t)b * p.T + t0 + orow) * p.Hv + h) * p.Dv + tv * 32 + ocol
-                                    : p.sink + st * 8;
+    uint16_t* dst = t0 + orow < sq.t1 ? p.o + ((t0 + orow) * p.Hv + h) * p.Dv + tv * 32 + ocol : p.sink + st * 8;
     *reinterpret_cast<u32x4*>(dst) = val;
   };
   auto bsS = [&](int ks) { return ld8(&sS[lane & 31][ks * 16 + kb8]); };
@@ -437,7 +510,7 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
       u32x4 x[4];  // U waves: U~ (two registers used); O waves: rows of P
     };
     auto load = [&](int c, Ops& o) {
-      const int64_t cid = (int64_t)bh * NC + c;
+      const int64_t cid = cid0 + c;
       const uint16_t* ab = (is_u ? p.w_ws : p.qs_ws) + (cid * kC + arow) * DK + kb8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) o.a[ks] = *reinterpret_cast<const u32x4*>(ab + ks * 16);
@@ -517,7 +590,7 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
       float el;  // e^{Gc_last}
     };
     auto load = [&](int c, Ops& o) {
-      const int64_t cid = (int64_t)bh * NC + c;
+      const int64_t cid = cid0 + c;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         o.kt[ks] = *reinterpret_cast<const u32x4*>(p.kt_ws + (cid * DK + kw * 32 + (lane & 31)) * kC + ks * 16 + kb8);
@@ -557,6 +630,11 @@ __global__ __launch_bounds__(kStateThreads) void gdn_chunk_state(ChunkArgs p) {
 
 template <int DK>
 hipError_t launch(ChunkArgs a, int64_t prep_blocks, int64_t state_blocks, hipStream_t st) {
+  if (a.cu != nullptr) {
+    hipLaunchKernelGGL(gdn_chunk_map, dim3(1), dim3(1024), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (prep_blocks > 0) {
     a.n_blocks = (int)prep_blocks;
     if (a.Dv <= 128)
@@ -572,12 +650,13 @@ hipError_t launch(ChunkArgs a, int64_t prep_blocks, int64_t state_blocks, hipStr
 }
 
 struct Plan {
-  int64_t NC, NV, prep_blocks, state_blocks;
-  size_t w_off, u_off, p_off, g_off, kt_off, qs_off, sink_off, bytes;
+  int64_t NC, NV, NCW, N, prep_blocks, state_blocks;
+  size_t w_off, u_off, p_off, g_off, kt_off, qs_off, cs_off, sink_off, bytes;
 };
 
-// Validates the shape for the chunk form; fills the workspace plan.
-rglru_status_t plan(const rglru_delta_shape_t* sp, const int32_t* cu, Plan* pl) {
+// Validates the shape for the chunk form; fills the workspace plan. n_seqs = 0: B rows of T
+// tokens; n_seqs >= 1: that many packed sequences (B = 1).
+rglru_status_t plan(const rglru_delta_shape_t* sp, int64_t n_seqs, Plan* pl) {
   if (sp == nullptr) return RGLRU_ERR_INVALID_ARGUMENT;
   const rglru_delta_shape_t s = *sp;
   if (s.batch < 0 || s.length < 0 || s.batch > (int64_t(1) << 40) || s.length > (int64_t(1) << 40) ||
@@ -590,24 +669,30 @@ rglru_status_t plan(const rglru_delta_shape_t* sp, const int32_t* cu, Plan* pl) 
   if (s.decay != RGLRU_DELTA_GDN && s.decay != RGLRU_DELTA_KDA) return RGLRU_ERR_INVALID_ARGUMENT;
   if (s.state_v_first != 0 && s.state_v_first != 1) return RGLRU_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(s.scale)) return RGLRU_ERR_INVALID_ARGUMENT;
+  if (n_seqs < 0 || (n_seqs > 0 && (s.batch != 1 || n_seqs >= (int64_t(1) << 30)))) return RGLRU_ERR_INVALID_ARGUMENT;
   if (s.decay != RGLRU_DELTA_GDN || s.io_dtype != RGLRU_IO_BF16 || (s.k_dim != 64 && s.k_dim != 128) ||
-      s.v_dim % 32 != 0 || s.v_dim > kMaxDv || cu != nullptr)
+      s.v_dim % 32 != 0 || s.v_dim > kMaxDv)
     return RGLRU_ERR_UNSUPPORTED;
   const int64_t NC = ceil_div(s.length, kC), NV = s.v_dim / 32;
-  const int64_t BH = s.batch * s.v_heads;
-  if (BH * NC >= (int64_t(1) << 31) || BH * NV >= (int64_t(1) << 31)) return RGLRU_ERR_INVALID_ARGUMENT;
-  const size_t chunks = (size_t)(BH * NC);
+  const int64_t N = n_seqs > 0 ? n_seqs : s.batch;
+  const int64_t NCW = n_seqs > 0 ? NC + n_seqs : s.batch * NC;  // each sequence adds at most one partial chunk
+  if (NCW * s.v_heads >= (int64_t(1) << 31) || N * s.v_heads * NV >= (int64_t(1) << 31))
+    return RGLRU_ERR_INVALID_ARGUMENT;
+  const size_t chunks = (size_t)(NCW * s.v_heads);
   pl->NC = NC;
   pl->NV = NV;
-  pl->prep_blocks = BH * NC;
-  pl->state_blocks = BH * NV;
+  pl->NCW = NCW;
+  pl->N = N;
+  pl->prep_blocks = NCW * s.v_heads;
+  pl->state_blocks = N * s.v_heads * NV;
   pl->w_off = 0;
   pl->u_off = round_up(pl->w_off + chunks * kC * s.k_dim * 2, 256);
   pl->p_off = round_up(pl->u_off + chunks * kC * s.v_dim * 2, 256);
   pl->g_off = round_up(pl->p_off + chunks * kC * kC * 2, 256);
   pl->kt_off = round_up(pl->g_off + chunks * kGS * 4, 256);
   pl->qs_off = round_up(pl->kt_off + chunks * kC * s.k_dim * 2, 256);
-  pl->sink_off = round_up(pl->qs_off + chunks * kC * s.k_dim * 2, 256);
+  pl->cs_off = round_up(pl->qs_off + chunks * kC * s.k_dim * 2, 256);
+  pl->sink_off = round_up(pl->cs_off + (size_t)(n_seqs + 1) * 4, 256);
   pl->bytes = pl->sink_off + 4096;
   return RGLRU_OK;
 }
@@ -617,33 +702,38 @@ rglru_status_t plan(const rglru_delta_shape_t* sp, const int32_t* cu, Plan* pl) 
 
 using namespace rglru;
 
-extern "C" size_t rglru_delta_chunk_workspace_bytes(const rglru_delta_shape_t* shape) {
+extern "C" size_t rglru_delta_chunk_workspace_bytes(const rglru_delta_shape_t* shape, int64_t n_seqs) {
   dchunk::Plan pl;
-  if (dchunk::plan(shape, nullptr, &pl) != RGLRU_OK) return 0;
+  if (dchunk::plan(shape, n_seqs, &pl) != RGLRU_OK) return 0;
   return pl.bytes;
 }
 
-extern "C" rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape, const void* q, const void* k,
-                                                const void* v, const float* g, const float* beta, const float* h0,
-                                                void* o, float* h_last, void* workspace, size_t workspace_bytes,
+extern "C" rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape, const int32_t* cu_seqlens,
+                                                int64_t n_seqs, const void* q, const void* k, const void* v,
+                                                const float* g, const float* beta, const float* h0, void* o,
+                                                float* h_last, void* workspace, size_t workspace_bytes,
                                                 void* stream) {
+  if (cu_seqlens == nullptr) n_seqs = 0;
+  else if (n_seqs < 1) return RGLRU_ERR_INVALID_ARGUMENT;
   dchunk::Plan pl;
-  const rglru_status_t st = dchunk::plan(shape, nullptr, &pl);
+  const rglru_status_t st = dchunk::plan(shape, n_seqs, &pl);
   if (st != RGLRU_OK) return st;
   const rglru_delta_shape_t& s = *shape;
   const int64_t tokens = s.batch * s.length;
   if (tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
-                     o == nullptr || workspace == nullptr))
+                     o == nullptr))
     return RGLRU_ERR_INVALID_ARGUMENT;
-  if (tokens == 0) pl.prep_blocks = 0;
+  // the workspace holds the chunks' operands and, for packed sequences, the chunk map; with no
+  // tokens and no packed sequences there are no chunks and it is not touched
+  const bool needs_ws = tokens > 0 || cu_seqlens != nullptr;
+  if (needs_ws && workspace == nullptr) return RGLRU_ERR_INVALID_ARGUMENT;
   if (!aligned_to(q, 16) || !aligned_to(k, 16) || !aligned_to(v, 16) || !aligned_to(o, 2) ||
       !aligned_to(g, 4) || !aligned_to(beta, 4) || !aligned_to(h0, 4) || !aligned_to(h_last, 4) ||
-      !aligned_to(workspace, 256))
+      !aligned_to(workspace, 256) || !aligned_to(cu_seqlens, 4))
     return RGLRU_ERR_MISALIGNED;
-  if (s.batch * s.v_heads == 0 || (tokens == 0 && h_last == nullptr)) return RGLRU_OK;
-  // with no tokens there are no chunks: only the state pass runs (it copies h0 or zeros
-  // into h_last) and the workspace is not touched
-  if (tokens > 0 && workspace_bytes < pl.bytes) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
+  if (pl.N * s.v_heads == 0 || (tokens == 0 && h_last == nullptr)) return RGLRU_OK;
+  if (needs_ws && workspace_bytes < pl.bytes) return RGLRU_ERR_WORKSPACE_TOO_SMALL;
+  if (tokens == 0) pl.prep_blocks = 0;
   char* ws = static_cast<char*>(workspace);
   dchunk::ChunkArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -659,8 +749,10 @@ extern "C" rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape
   a.p_ws = reinterpret_cast<uint16_t*>(ws + pl.p_off);
   a.gc_ws = reinterpret_cast<float*>(ws + pl.g_off);
   a.kt_ws = reinterpret_cast<uint16_t*>(ws + pl.kt_off);
-  a.sink = reinterpret_cast<uint16_t*>(ws + pl.sink_off);
   a.qs_ws = reinterpret_cast<uint16_t*>(ws + pl.qs_off);
+  a.cs = reinterpret_cast<int*>(ws + pl.cs_off);
+  a.sink = reinterpret_cast<uint16_t*>(ws + pl.sink_off);
+  a.cu = cu_seqlens;
   a.T = s.length;
   a.Hk = s.k_heads;
   a.Hv = s.v_heads;
@@ -668,6 +760,8 @@ extern "C" rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape
   a.Dv = s.v_dim;
   a.NC = (int)pl.NC;
   a.NV = (int)pl.NV;
+  a.NCW = (int)pl.NCW;
+  a.n_seqs = (int)n_seqs;
   a.n_blocks = 0;
   a.v_first = s.state_v_first;
   a.scale = s.scale;

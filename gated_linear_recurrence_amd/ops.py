@@ -514,31 +514,33 @@ def rglru_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
     return o, final_state
 
 
-def rglru_delta_chunk_workspace_bytes(shape: _lib.rglru_delta_shape_t) -> int:
-    return int(_lib.load().rglru_delta_chunk_workspace_bytes(ctypes.byref(shape)))
+def rglru_delta_chunk_workspace_bytes(shape: _lib.rglru_delta_shape_t, n_seqs: int = 0) -> int:
+    """Workspace bytes of rglru_delta_chunk_fwd: n_seqs packed sequences, or 0 for B rows."""
+    return int(_lib.load().rglru_delta_chunk_workspace_bytes(ctypes.byref(shape), int(n_seqs)))
 
 
 def rglru_delta_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
                           scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
-                          state_v_first: bool = False, output_final_state: bool = True,
-                          o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                          workspace: Optional[torch.Tensor] = None):
+                          cu_seqlens: Optional[torch.Tensor] = None, state_v_first: bool = False,
+                          output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                          final_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Gated delta rule forward for GDN in chunk form (64-token chunks, bf16 MFMA, float32 state).
 
-    Same arguments and results as rglru_delta_rule_fwd without cu_seqlens; bf16
-    q, k, v, Dk 64 or 128, Dv a multiple of 32 up to 256. workspace: a uint8
-    device tensor of at least rglru_delta_chunk_workspace_bytes bytes (allocated
-    here when None)."""
+    Same arguments and results as rglru_delta_rule_fwd (packed sequences
+    included); bf16 q, k, v, Dk 64 or 128, Dv a multiple of 32 up to 256.
+    workspace: a uint8 device tensor of at least rglru_delta_chunk_workspace_bytes
+    bytes (allocated here when None)."""
     lib = _lib.load()
     if g.dim() != 3:
         raise ValueError("the chunk form takes the GDN decay g [B, T, Hv]")
-    shape, n, o, final_state = _delta_common(q, k, v, g, beta, scale, initial_state, None, state_v_first,
+    shape, n, o, final_state = _delta_common(q, k, v, g, beta, scale, initial_state, cu_seqlens, state_v_first,
                                              output_final_state, o, final_state)
-    nbytes = int(lib.rglru_delta_chunk_workspace_bytes(ctypes.byref(shape)))
+    n_packed = n if cu_seqlens is not None else 0
+    nbytes = int(lib.rglru_delta_chunk_workspace_bytes(ctypes.byref(shape), n_packed))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib.rglru_delta_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                   _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace),
-                                   workspace.numel(), _stream(q.device))
+    st = lib.rglru_delta_chunk_fwd(ctypes.byref(shape), _ptr(cu_seqlens), n_packed, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                   _ptr(workspace), workspace.numel(), _stream(q.device))
     _lib.check(st, "rglru_delta_chunk_fwd")
     return o, final_state

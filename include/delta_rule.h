@@ -78,25 +78,30 @@ rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* shape, const int3
  * page: within each chunk of 64 tokens, a unit-lower-triangular solve gives
  * the WY operands W = T diag(beta e^Gc) K and U~ = T diag(beta) V, with T the
  * inverse of I plus the strictly lower, decay-weighted beta K K^T; the state
- * then advances once per chunk). The dense products run on bf16 MFMA with
- * float32 accumulation: T, W, U~, the corrected writes, the masked Q K^T and
- * the state's operand copy are rounded to bf16 where they enter a product,
- * so results match the token recurrence to bf16-operand accuracy, not
- * bitwise; the state itself is float32 throughout.
+ * then advances once per chunk; packed sequences through cu_seqlens). The
+ * dense products run on bf16 MFMA with float32 accumulation: T, W, U~, the
+ * corrected writes, the masked Q K^T, the decayed and scaled K and Q and the
+ * state's operand copy are rounded to bf16 where they enter a product, so
+ * results match the token recurrence to bf16-operand accuracy, not bitwise;
+ * the state itself is float32 throughout.
  *
- * Arguments as for rglru_delta_rule_fwd without cu_seqlens, with these
- * restrictions (RGLRU_ERR_UNSUPPORTED otherwise): decay RGLRU_DELTA_GDN, io
- * bf16, k_dim 64 or 128, v_dim a multiple of 32 and at most 256. o needs
- * only 2-byte alignment here. workspace: device memory of at least
- * rglru_delta_chunk_workspace_bytes(shape) bytes, 256-byte aligned, owned by
- * the caller, no initial contents required; it holds the WY operands
- * between the two launches and is not needed when B * T = 0 (then only the
- * final state is written, from h0 or zeros). Size query returns 0 for an
- * invalid or unsupported shape. */
-size_t rglru_delta_chunk_workspace_bytes(const rglru_delta_shape_t* shape);
-rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape, const void* q, const void* k,
-                                     const void* v, const float* g, const float* beta, const float* h0,
-                                     void* o, float* h_last, void* workspace, size_t workspace_bytes,
+ * Arguments as for rglru_delta_rule_fwd (cu_seqlens NULL with n_seqs
+ * ignored, or n_seqs >= 1 packed sequences with B = 1; offsets read on the
+ * device and clamped into [0, T]), with these restrictions
+ * (RGLRU_ERR_UNSUPPORTED otherwise): decay RGLRU_DELTA_GDN, io bf16, k_dim
+ * 64 or 128, v_dim a multiple of 32 and at most 256. o needs only 2-byte
+ * alignment here. workspace: device memory of at least
+ * rglru_delta_chunk_workspace_bytes(shape, n) bytes (n = n_seqs with
+ * cu_seqlens, else 0), 256-byte aligned, owned by the caller, no initial
+ * contents required; it holds the WY operands between the launches (and
+ * the chunk map of packed sequences); it may be NULL when B * T = 0 without
+ * cu_seqlens (then only the final state is written, from h0 or zeros). The
+ * size query returns 0 for an invalid or unsupported shape. */
+size_t rglru_delta_chunk_workspace_bytes(const rglru_delta_shape_t* shape, int64_t n_seqs);
+rglru_status_t rglru_delta_chunk_fwd(const rglru_delta_shape_t* shape, const int32_t* cu_seqlens,
+                                     int64_t n_seqs, const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, const float* h0, void* o,
+                                     float* h_last, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
 #ifdef __cplusplus

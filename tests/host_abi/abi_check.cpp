@@ -217,20 +217,27 @@ int main() {
   EXPECT(rglru_delta_rule_fwd(nullptr, nullptr, 0, p, p, p, fp, fp, nullptr, p, nullptr, nullptr) ==
          RGLRU_ERR_INVALID_ARGUMENT);
   rglru_delta_shape_t c1 = dshape(2, 100, 1, 2, 128, 128, 1, 0);
-  const size_t cws = rglru_delta_chunk_workspace_bytes(&c1);
+  const size_t cws = rglru_delta_chunk_workspace_bytes(&c1, 0);
   EXPECT(cws > 0 && cws % 256 == 0);
-  auto cfwd = [&](const rglru_delta_shape_t& c, size_t bytes) {
-    return rglru_delta_chunk_fwd(&c, p, p, p, fp, fp, nullptr, p, wf, p, bytes, nullptr);
+  auto cfwd = [&](const rglru_delta_shape_t& c, size_t bytes, const int32_t* cu = nullptr, int64_t n = 0) {
+    return rglru_delta_chunk_fwd(&c, cu, n, p, p, p, fp, fp, nullptr, p, wf, p, bytes, nullptr);
   };
   EXPECT(cfwd(c1, 16) == RGLRU_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(cfwd(c1, cws, dcu, 3) == RGLRU_ERR_INVALID_ARGUMENT);  // packed sequences need B = 1
+  rglru_delta_shape_t c2 = dshape(1, 100, 1, 2, 128, 128, 1, 0);
+  const size_t pws = rglru_delta_chunk_workspace_bytes(&c2, 5);
+  EXPECT(pws > rglru_delta_chunk_workspace_bytes(&c2, 0));  // room for the extra partial chunks and the map
+  EXPECT(cfwd(c2, pws, dcu, 0) == RGLRU_ERR_INVALID_ARGUMENT);
+  EXPECT(cfwd(c2, pws - 256, dcu, 5) == RGLRU_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(rglru_delta_chunk_workspace_bytes(&c1, 3) == 0);
   const rglru_delta_shape_t unsupported[] = {dshape(2, 100, 1, 2, 128, 128, 1, 1), dshape(2, 100, 1, 2, 96, 128, 1, 0),
                                             dshape(2, 100, 1, 2, 128, 48, 1, 0), dshape(2, 100, 1, 2, 128, 288, 1, 0),
                                             dshape(2, 100, 1, 2, 128, 128, 0, 0)};
   for (const rglru_delta_shape_t& c : unsupported) {
-    EXPECT(rglru_delta_chunk_workspace_bytes(&c) == 0);
+    EXPECT(rglru_delta_chunk_workspace_bytes(&c, 0) == 0);
     EXPECT(cfwd(c, cws) == RGLRU_ERR_UNSUPPORTED);
   }
-  EXPECT(rglru_delta_chunk_workspace_bytes(nullptr) == 0);
+  EXPECT(rglru_delta_chunk_workspace_bytes(nullptr, 0) == 0);
 
   std::printf(g_fail ? "host ABI checks: %d failed\n" : "host ABI checks: all passed\n", g_fail);
   return g_fail ? 1 : 0;

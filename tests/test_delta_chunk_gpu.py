@@ -54,8 +54,9 @@ def _run(glr, inp, v_first=False, scale=None, fn="chunk"):
     if h0 is not None and v_first:
         h0 = h0.transpose(0, 1, 3, 2)
     f = glr.rglru_delta_chunk_fwd if fn == "chunk" else glr.rglru_delta_rule_fwd
+    cu = None if inp.cu is None else torch.from_numpy(inp.cu).cuda()
     o, s = f(_dev(inp.q), _dev(inp.k), _dev(inp.v), _f32(inp.g), _f32(inp.beta), scale=scale,
-             initial_state=_f32(h0), state_v_first=v_first)
+             initial_state=_f32(h0), cu_seqlens=cu, state_v_first=v_first)
     torch.cuda.synchronize()
     s = host64(s)
     if v_first:
@@ -65,7 +66,8 @@ def _run(glr, inp, v_first=False, scale=None, fn="chunk"):
 
 def _ref(inp, scale=None):
     return oracle.recurrent_delta_rule(inp.q.value, inp.k.value, inp.v.value, inp.g.astype(np.float64),
-                                       inp.beta.astype(np.float64), scale=scale, initial_state=inp.h0)
+                                       inp.beta.astype(np.float64), scale=scale, initial_state=inp.h0,
+                                       cu_seqlens=inp.cu)
 
 
 def _err(got, ref):
@@ -102,6 +104,44 @@ def test_value_first_state_and_scale(gpu_lib):
     wl = BASE.resized(wid=31, batch=2, length=150, k_heads=1, v_heads=2, k_dim=128, v_dim=64, h0=True)
     inp = sd.make_delta_inputs(wl)
     _check(_run(gpu_lib, inp, v_first=True, scale=0.29), _ref(inp, scale=0.29), "v_first")
+
+
+@pytest.mark.parametrize("Dk", [64, 128])
+def test_packed_sequences(gpu_lib, Dk):
+    lens = [0, 1, 17, 64, 65, 130, 0, 5]
+    wl = BASE.resized(wid=34, k_heads=1, v_heads=2, k_dim=Dk, v_dim=64, h0=True)
+    inp = sd.make_delta_inputs(wl, lengths=lens)
+    got = _run(gpu_lib, inp)
+    _check(got, _ref(inp), f"packed Dk{Dk}")
+    for n in (0, 6):   # empty sequences return their initial state bitwise
+        np.testing.assert_array_equal(got[1][n], inp.h0[n].astype(np.float64))
+    # each sequence alone, as a one-row call, gives the same bits
+    cu = inp.cu
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b == a:
+            continue
+        one = sd.DeltaInputs(wl.resized(batch=1, length=b - a),
+                             *(sd.Stored(st.io, st.raw[:, a:b].copy(), st.value[:, a:b]) for st in (inp.q, inp.k, inp.v)),
+                             inp.g[:, a:b].copy(), inp.beta[:, a:b].copy(), inp.h0[n:n + 1].copy())
+        o1, s1 = _run(gpu_lib, one)
+        np.testing.assert_array_equal(o1[0], got[0][0, a:b])
+        np.testing.assert_array_equal(s1[0], got[1][n])
+
+
+def test_packed_geometric_lengths(gpu_lib):
+    lens = sd.seq_lengths(24, 100.0, empty_p=0.1)
+    wl = BASE.resized(wid=35, k_heads=2, v_heads=4, h0=True)
+    inp = sd.make_delta_inputs(wl, lengths=lens)
+    _check(_run(gpu_lib, inp), _ref(inp), "packed geometric")
+
+
+def test_packed_all_empty(gpu_lib):
+    wl = BASE.resized(wid=36, k_heads=1, v_heads=2, k_dim=64, v_dim=32, h0=True)
+    inp = sd.make_delta_inputs(wl, lengths=[0, 0, 0])
+    o, s = _run(gpu_lib, inp)
+    assert o.shape == (1, 0, 2, 32)
+    np.testing.assert_array_equal(s, inp.h0.astype(np.float64))
 
 
 @pytest.mark.parametrize("with_h0", [False, True])
