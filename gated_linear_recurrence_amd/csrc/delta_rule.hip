@@ -133,6 +133,8 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
   __shared__ float sb[2][kTC];
   __shared__ __align__(16) float sv[2][kTC][CW];
   __shared__ __align__(16) float so[2][kTC][CW];
+  __shared__ float sst[DKP][CW + 1];  // the key-first state slice, for coalesced loads and stores
+  constexpr int GQ = CW / 4;          // 16-byte column groups of a state row
 
   const int bid = xcd_remap(blockIdx.x, p.n_blocks);
   const int cb = bid % p.n_cb;
@@ -166,10 +168,28 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
   };
 
   float s[R];
+  if (!p.v_first) {
+    // rows of CW contiguous columns, 16 bytes per load, through LDS
+    for (int idx = tid; idx < DKP * GQ; idx += kThreads) {
+      const int d = idx / GQ, gq = idx % GQ;
+      const int c0 = cb * CW + gq * 4;
+      float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p.h0 != nullptr && d < p.Dk && c0 < p.Dv)
+        v4 = *reinterpret_cast<const float4*>(p.h0 + st_base + (int64_t)d * p.Dv + c0);
+      sst[d][gq * 4] = v4.x;
+      sst[d][gq * 4 + 1] = v4.y;
+      sst[d][gq * 4 + 2] = v4.z;
+      sst[d][gq * 4 + 3] = v4.w;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int row = rb * R + i;
-    s[i] = (p.h0 != nullptr && col_ok && row < p.Dk) ? p.h0[st_index(row)] : 0.0f;
+    for (int i = 0; i < R; ++i) s[i] = sst[rb * R + i][cl];
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int row = rb * R + i;
+      s[i] = (p.h0 != nullptr && col_ok && row < p.Dk) ? p.h0[st_index(row)] : 0.0f;
+    }
   }
 
   const char* qb = static_cast<const char*>(p.q);
@@ -344,7 +364,19 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
     write_out((int)((nch - 1) & 1), nch - 1);
   }
 
-  if (p.h_last != nullptr && col_ok) {
+  if (p.h_last != nullptr && !p.v_first) {
+    __syncthreads();  // every lane has read its initial slice
+#pragma unroll
+    for (int i = 0; i < R; ++i) sst[rb * R + i][cl] = s[i];
+    __syncthreads();
+    for (int idx = tid; idx < DKP * GQ; idx += kThreads) {
+      const int d = idx / GQ, gq = idx % GQ;
+      const int c0 = cb * CW + gq * 4;
+      if (d < p.Dk && c0 < p.Dv)
+        *reinterpret_cast<float4*>(p.h_last + st_base + (int64_t)d * p.Dv + c0) =
+            make_float4(sst[d][gq * 4], sst[d][gq * 4 + 1], sst[d][gq * 4 + 2], sst[d][gq * 4 + 3]);
+    }
+  } else if (p.h_last != nullptr && col_ok) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int row = rb * R + i;
@@ -403,7 +435,7 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   if (blocks >= (int64_t(1) << 31)) return RGLRU_ERR_INVALID_ARGUMENT;
   if (s.k_dim > 256 || s.k_dim % 8 != 0 || s.v_dim % 8 != 0) return RGLRU_ERR_UNSUPPORTED;
   if (!aligned_to(q, 16) || !aligned_to(k, 16) || !aligned_to(v, 16) || !aligned_to(o, 16) ||
-      !aligned_to(g, kda ? 16 : 4) || !aligned_to(beta, 4) || !aligned_to(h0, 4) || !aligned_to(h_last, 4) ||
+      !aligned_to(g, kda ? 16 : 4) || !aligned_to(beta, 4) || !aligned_to(h0, 16) || !aligned_to(h_last, 16) ||
       !aligned_to(cu_seqlens, 4))
     return RGLRU_ERR_MISALIGNED;
   if (blocks == 0 || (tokens == 0 && h_last == nullptr)) return RGLRU_OK;

@@ -62,9 +62,9 @@ typedef struct {
  *                or [B, T, Hv, Dk] (KDA, 16-byte aligned).
  *   beta       : [B, T, Hv] float32 write strengths.
  *   h0         : NULL (zero initial states) or [N, Hv, Dk, Dv] float32
- *                ([N, Hv, Dv, Dk] with state_v_first).
- *   h_last     : NULL or the final states, same layout as h0; a sequence with
- *                no tokens gets its initial state.
+ *                ([N, Hv, Dv, Dk] with state_v_first), 16-byte aligned.
+ *   h_last     : NULL or the final states, same layout and alignment as h0; a
+ *                sequence with no tokens gets its initial state.
  * q, k, v, g, beta and o may be NULL only when B * T = 0. Returns
  * RGLRU_ERR_INVALID_ARGUMENT, RGLRU_ERR_MISALIGNED or RGLRU_ERR_UNSUPPORTED
  * without launching anything, RGLRU_ERR_HIP if the launch fails. Outputs
@@ -89,8 +89,8 @@ rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* shape, const int3
  * ignored, or n_seqs >= 1 packed sequences with B = 1; offsets read on the
  * device and clamped into [0, T]), with these restrictions
  * (RGLRU_ERR_UNSUPPORTED otherwise): decay RGLRU_DELTA_GDN, io bf16, k_dim
- * 64 or 128, v_dim a multiple of 32 and at most 256. o needs only 2-byte
- * alignment here. workspace: device memory of at least
+ * 64 or 128, v_dim a multiple of 32 and at most 256. o needs only 2-byte,
+ * h0 and h_last only 4-byte alignment here. workspace: device memory of at least
  * rglru_delta_chunk_workspace_bytes(shape, n) bytes (n = n_seqs with
  * cu_seqlens, else 0), 256-byte aligned, owned by the caller, no initial
  * contents required; it holds the WY operands between the launches (and
