@@ -209,13 +209,17 @@ def main():
                          "allocation-free forward, eager and replayed from a HIP graph")
     ap.add_argument("--delta-only", action="store_true",
                     help="instead: only the gated delta rule workloads (one JSON object per workload)")
+    ap.add_argument("--delta-workload", type=int, default=None, choices=(10, 11, 12),
+                    help="with --delta-only: that delta-rule workload alone")
     args = ap.parse_args()
 
     if args.delta_only:
         if args.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)
             sys.exit(2)
-        for w in (10, 11, 12):
+        if args.calibration_copy_mb > 0:
+            calibration_copy(args.calibration_copy_mb)
+        for w in ((10, 11, 12) if args.delta_workload is None else (args.delta_workload,)):
             print(json.dumps(run_delta(args, w, args.steps, args.warmup)), flush=True)
         return
 
@@ -251,6 +255,28 @@ def main():
         torch.cuda.empty_cache()
         out["delta_rule"] = {str(w): run_delta(args, w, 20, 3) for w in (10, 11, 12)}
     print(json.dumps(out), flush=True)
+
+
+def calibration_copy(mib):
+    """One device-to-device copy of `mib` MiB: a known-size reference for the hardware traffic counters."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def measured_traffic(key):
+    """Per-call HBM bytes of a library call from profiles/traffic.json (None when not measured)."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            return (json.load(f).get(key) or {}).get("bytes")
+    except (OSError, ValueError):
+        return None
 
 
 def delta_cpu_baseline(inp, seconds_target=2.0):
@@ -370,7 +396,8 @@ def run_delta(args, wid, steps, warmup):
             "tokens_per_s": B * T / (cms * 1e-3),
             "roofline": {"kernel": "gdn_chunk_prep + gdn_chunk_state", "bound": "mfma", "achieved": round(ctf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ctf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(ctf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic(f"{wl.name}:delta_chunk"),
                          "algorithmic_flops_per_launch": cflops, "launch_ms": round(cms, 5)},
             "speedup_vs_token_recurrence": round(ms / cms, 3),
         }
@@ -385,7 +412,8 @@ def run_delta(args, wid, steps, warmup):
         "tokens_per_s": B * T / (ms * 1e-3),
         "roofline": {"kernel": "delta_fwd_kernel", "bound": "alu", "achieved": round(tf, 2),
                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(f"{wl.name}:delta_token"),
                      "algorithmic_flops_per_launch": flops, "launch_ms": round(ms, 5)},
         "hbm": {"algorithmic_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)},
         "chunk_form": chunk,
@@ -477,13 +505,7 @@ def run_workload(args, wid, steps, warmup, with_cpu):
         mark(4)
 
     if args.calibration_copy_mb > 0:
-        n = args.calibration_copy_mb << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(args.calibration_copy_mb)
     for i in range(warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()

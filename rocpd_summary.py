@@ -82,11 +82,13 @@ def traffic(fetch_db: str, write_db: str, calib_mib: float):
 # kernels of each library call (matched on the kernel name; the forward's
 # last template argument tells the fused instantiation from the plain scan)
 GROUPS = {
-    "fwd": lambda n: "fwd_kernel<" in n and not n.endswith(", true>(FwdArgs)"),
+    "fwd": lambda n: "fwd_kernel<" in n and "delta_fwd_kernel<" not in n and not n.endswith(", true>(FwdArgs)"),
     "bwd": lambda n: "bwd_kernel<" in n or "bwd_dlam_kernel(" in n,
     "proj_fwd": lambda n: "proj_fwd_kernel(" in n,
     "proj_bwd": lambda n: any(k in n for k in ("proj_dw_kernel(", "proj_dw_reduce_kernel(", "proj_dx_kernel<")),
     "fused_fwd": lambda n: ("fwd_kernel<" in n and n.endswith(", true>(FwdArgs)")) or "w_frag_kernel(" in n,
+    "delta_token": lambda n: "delta_fwd_kernel<" in n,
+    "delta_chunk": lambda n: any(k in n for k in ("gdn_chunk_prep<", "gdn_chunk_state<", "gdn_chunk_map(")),
 }
 
 
