@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
 benchmark's CPU-baseline leg. The HIP library and its binding never import,
 call or link anything here.
 """
-from .delta import chunk_gdn, recurrent_delta_rule  # noqa: F401
+from .delta import chunk_gdn, recurrent_delta_rule, recurrent_delta_rule_backward  # noqa: F401
 from .rglru import (  # noqa: F401
     C_DEFAULT,
     blockdiag_proj_backward,

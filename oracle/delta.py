@@ -145,3 +145,69 @@ def chunk_gdn(q, k, v, g, beta, chunk_size=64, scale=None, initial_state=None, c
     if state_v_first:
         fin = fin.transpose(0, 1, 3, 2)
     return o, fin
+
+
+def recurrent_delta_rule_backward(q, k, v, g, beta, do, dh_last=None, scale=None, initial_state=None,
+                                  cu_seqlens=None, state_v_first=False):
+    """Gradients of the token recurrence above for the loss <do, o> + <dh_last, S_final>.
+
+    Reverse-mode differentiation of each step, written out (the page's oracles keep autograd
+    gradients, through the initial state included). With S~ = D S_prev (the decayed state),
+    e = v - S~^T k, u = beta e, S = S~ + k u^T, o = scale S^T q, and G the gradient of S:
+      G += scale q do^T;  dq = scale S do;  du = G^T k;  dv = beta du;  dbeta = e . du;
+      G~ = G - beta k du^T  (gradient of S~);  dk = G u - beta S~ du;
+      dg = <G~, S~> (GDN) or the row sums of G~ * S~ (KDA);  G <- D G~ for the step before.
+    Returns (dq, dk, dv, dg, dbeta, dh0) with the shapes of q, k, v, g, beta and the states.
+    """
+    q, k, v, g, beta, do = (_f64(a) for a in (q, k, v, g, beta, do))
+    B, T, Hk, Dk, Hv, Dv, grp = _heads(q, v)
+    kda = g.ndim == 4
+    sc = 1.0 / math.sqrt(Dk) if scale is None else float(scale)
+    seqs = _sequences(B, T, cu_seqlens)
+    h0 = _f64(initial_state)
+    dhl = _f64(dh_last)
+    dq, dk = np.zeros_like(q), np.zeros_like(k)
+    dv, dg, dbeta = np.zeros_like(v), np.zeros_like(g), np.zeros_like(beta)
+    dh0 = np.zeros((len(seqs), Hv, Dk, Dv))
+    for n, (b, s0, s1) in enumerate(seqs):
+        for h in range(Hv):
+            kh = h // grp
+            if h0 is None:
+                S = np.zeros((Dk, Dv))
+            else:
+                S = (h0[n, h].T if state_v_first else h0[n, h]).copy()
+            hist = []   # (S~, e, u) of every step, forward order
+            for t in range(s0, s1):
+                dec = np.exp(g[b, t, h])
+                St = (dec[:, None] if kda else dec) * S
+                kt = k[b, t, kh]
+                e = v[b, t, h] - St.T @ kt
+                u = beta[b, t, h] * e
+                S = St + np.outer(kt, u)
+                hist.append((St, e, u))
+            if dhl is None:
+                G = np.zeros((Dk, Dv))
+            else:
+                G = (dhl[n, h].T if state_v_first else dhl[n, h]).copy()
+            for t in range(s1 - 1, s0 - 1, -1):
+                St, e, u = hist[t - s0]
+                kt, qt, dot = k[b, t, kh], q[b, t, kh], do[b, t, h]
+                Sn = St + np.outer(kt, u)
+                G = G + sc * np.outer(qt, dot)
+                dq[b, t, kh] += sc * (Sn @ dot)
+                du = G.T @ kt
+                bt = beta[b, t, h]
+                dv[b, t, h] = bt * du
+                dbeta[b, t, h] = e @ du
+                dk[b, t, kh] += G @ u - bt * (St @ du)
+                Gt = G - bt * np.outer(kt, du)
+                if kda:
+                    dg[b, t, h] = np.sum(Gt * St, axis=1)
+                    G = np.exp(g[b, t, h])[:, None] * Gt
+                else:
+                    dg[b, t, h] = np.sum(Gt * St)
+                    G = np.exp(g[b, t, h]) * Gt
+            dh0[n, h] = G
+    if state_v_first:
+        dh0 = dh0.transpose(0, 1, 3, 2)
+    return dq, dk, dv, dg, dbeta, dh0

@@ -229,3 +229,83 @@ def test_rejects_bad_layouts():
         recurrent_delta_rule(q, k, v, g, beta, cu_seqlens=[0, 4])    # packed needs B = 1
     with pytest.raises(ValueError):
         chunk_gdn(q, k, v, np.zeros((2, 4, 1, 4)), beta)             # chunk form is GDN only
+
+
+# --------------------------------------------------------------- backward
+
+from oracle import recurrent_delta_rule_backward  # noqa: E402
+
+
+def _loss_fd(args, do, dhl, kw, i, idx, eps=1e-6):
+    def L(a):
+        o, s = recurrent_delta_rule(*a, **kw)
+        return np.sum(o * do) + (np.sum(s * dhl) if dhl is not None else 0.0)
+    ap = [x.copy() for x in args]
+    am = [x.copy() for x in args]
+    ap[i][idx] += eps
+    am[i][idx] -= eps
+    return (L(ap) - L(am)) / (2 * eps)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("layout", ["rows", "packed", "v_first"])
+def test_backward_matches_finite_differences(kda, layout):
+    """Every gradient, element by element, against central differences of <do, o> + <dh_last, S_final>."""
+    rng = np.random.default_rng(20 + kda)
+    B, T, Hk, Hv, Dk, Dv = (2, 5, 1, 2, 3, 2) if layout != "packed" else (1, 7, 1, 2, 3, 2)
+    q, k, v, g, beta = _rand(rng, B, T, Hk, Hv, Dk, Dv, kda)
+    cu = [0, 3, 3, 7] if layout == "packed" else None
+    N = 3 if layout == "packed" else B
+    vf = layout == "v_first"
+    sshape = (N, Hv, Dv, Dk) if vf else (N, Hv, Dk, Dv)
+    h0 = rng.standard_normal(sshape)
+    do = rng.standard_normal((B, T, Hv, Dv))
+    dhl = rng.standard_normal(sshape)
+    kw = dict(scale=0.7, initial_state=h0, cu_seqlens=cu, state_v_first=vf)
+    grads = recurrent_delta_rule_backward(q, k, v, g, beta, do, dhl, **kw)
+    args = [q, k, v, g, beta]
+    for i, gr in enumerate(grads[:5]):
+        fd = np.zeros_like(args[i])
+        for idx in np.ndindex(*args[i].shape):
+            fd[idx] = _loss_fd(args, do, dhl, kw, i, idx)
+        np.testing.assert_allclose(gr, fd, rtol=1e-6, atol=1e-7, err_msg=f"input {i}")
+    # initial state
+    def L0(h):
+        o, s = recurrent_delta_rule(q, k, v, g, beta, **dict(kw, initial_state=h))
+        return np.sum(o * do) + np.sum(s * dhl)
+    fd = np.zeros_like(h0)
+    for idx in np.ndindex(*h0.shape):
+        hp, hm = h0.copy(), h0.copy()
+        hp[idx] += 1e-6
+        hm[idx] -= 1e-6
+        fd[idx] = (L0(hp) - L0(hm)) / 2e-6
+    np.testing.assert_allclose(grads[5], fd, rtol=1e-6, atol=1e-7)
+
+
+def test_backward_without_writes_is_closed_form():
+    """beta = 0: S_t = Gamma_t S0, so dh0 = sum_t scale Gamma_t q_t do_t^T + Gamma_T dh_last, dv = 0."""
+    rng = np.random.default_rng(30)
+    T, Dk, Dv = 9, 4, 3
+    q, k, v, g, beta = _rand(rng, 1, T, 1, 1, Dk, Dv)
+    beta[:] = 0.0
+    do = rng.standard_normal((1, T, 1, Dv))
+    dhl = rng.standard_normal((1, 1, Dk, Dv))
+    dq, dk, dv, dg, db, dh0 = recurrent_delta_rule_backward(q, k, v, g, beta, do, dhl, scale=0.5)
+    Gam = np.exp(np.cumsum(g[0, :, 0]))
+    want = sum(0.5 * Gam[t] * np.outer(q[0, t, 0], do[0, t, 0]) for t in range(T)) + Gam[-1] * dhl[0, 0]
+    np.testing.assert_allclose(dh0[0, 0], want, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(dv, 0.0)
+    np.testing.assert_array_equal(dq, 0.0)   # zero state and no writes: o = 0 for any q
+
+
+def test_backward_is_linear_in_the_output_gradients():
+    rng = np.random.default_rng(31)
+    q, k, v, g, beta = _rand(rng, 1, 6, 1, 2, 4, 3, kda=True)
+    h0 = rng.standard_normal((1, 2, 4, 3))
+    d1, d2 = rng.standard_normal((2, 1, 6, 2, 3))
+    l1, l2 = rng.standard_normal((2, 1, 2, 4, 3))
+    a = recurrent_delta_rule_backward(q, k, v, g, beta, d1, l1, initial_state=h0)
+    b = recurrent_delta_rule_backward(q, k, v, g, beta, d2, l2, initial_state=h0)
+    c = recurrent_delta_rule_backward(q, k, v, g, beta, 2 * d1 - d2, 2 * l1 - l2, initial_state=h0)
+    for x, y, z in zip(a, b, c):
+        np.testing.assert_allclose(z, 2 * x - y, rtol=1e-10, atol=1e-12)
