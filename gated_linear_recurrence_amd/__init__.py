@@ -14,6 +14,8 @@ from .ops import (  # noqa: F401
     rglru_bwd_workspace_bytes,
     rglru_delta_chunk_fwd,
     rglru_delta_chunk_workspace_bytes,
+    rglru_delta_ckpt_elems,
+    rglru_delta_rule_bwd,
     rglru_delta_rule_fwd,
     rglru_ckpt_elems,
     rglru_fwd,

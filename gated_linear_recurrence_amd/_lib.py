@@ -76,7 +76,10 @@ _SIGNATURES = {
                                  _vp, _vp, c_size_t, _vp]),
     "rglru_bwd_varlen": (c_int, [POINTER(rglru_shape_t), _vp, c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, c_size_t, _vp]),
-    "rglru_delta_rule_fwd": (c_int, [POINTER(rglru_delta_shape_t), _vp, c_int64] + [_vp] * 9),
+    "rglru_delta_rule_fwd": (c_int, [POINTER(rglru_delta_shape_t), _vp, c_int64] + [_vp] * 10),
+    "rglru_delta_ckpt_elems": (c_size_t, [POINTER(rglru_delta_shape_t), c_int64]),
+    "rglru_delta_bwd_workspace_bytes": (c_size_t, [POINTER(rglru_delta_shape_t), c_int64]),
+    "rglru_delta_rule_bwd": (c_int, [POINTER(rglru_delta_shape_t), _vp, c_int64] + [_vp] * 15 + [c_size_t, _vp]),
     "rglru_delta_chunk_workspace_bytes": (c_size_t, [POINTER(rglru_delta_shape_t), c_int64]),
     "rglru_delta_chunk_fwd": (c_int, [POINTER(rglru_delta_shape_t), _vp, c_int64] + [_vp] * 9 + [c_size_t, _vp]),
     "rglru_status_string": (ctypes.c_char_p, [c_int]),

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librglru.so"
 ARCH = "gfx950"
 
-SOURCES = ["rglru_scan.hip", "rglru_proj.hip", "delta_rule.hip", "delta_chunk.hip"]
+SOURCES = ["rglru_scan.hip", "rglru_proj.hip", "delta_rule.hip", "delta_chunk.hip", "delta_bwd.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -51,6 +51,8 @@ struct DeltaArgs {
   int n_blocks;  // workgroups in the grid
   int v_first;
   float scale;
+  float* ckpt;        // NULL, or the state entering every 16-token chunk (for the backward)
+  int64_t ck_slots;   // checkpoint slots per value head
 };
 
 // Workgroup id -> logical block such that consecutive logical blocks share an
@@ -355,6 +357,15 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
     for (int64_t c = 0; c < nch; ++c) {
       const int b = (int)(c & 1);
       if (c + 1 < nch) load_chunk(c + 1);
+      if (p.ckpt != nullptr && col_ok) {
+        // the state entering chunk c, key-first [Dk][Dv] per slot
+        float* ck = p.ckpt + (((int64_t)h * p.ck_slots + delta_ckpt_base(p.cu != nullptr, p.T, n, tok0) + c) * p.Dk) * p.Dv;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int row = rb * R + i;
+          if (row < p.Dk) ck[(int64_t)row * p.Dv + col] = s[i];
+        }
+      }
       const int64_t rem = len - c * kTC;
       compute(b, rem < kTC ? (int)rem : kTC);
       if (c + 1 < nch) store_chunk(b ^ 1);
@@ -402,10 +413,19 @@ hipError_t launch_dt(const DeltaArgs& a, bool kda, bool bf, hipStream_t st) {
 
 using namespace rglru;
 
+extern "C" size_t rglru_delta_ckpt_elems(const rglru_delta_shape_t* sp, int64_t n_seqs) {
+  if (sp == nullptr || sp->batch < 0 || sp->length < 0 || sp->batch > (int64_t(1) << 40) ||
+      sp->length > (int64_t(1) << 40) || sp->v_heads < 1 || sp->k_dim < 1 || sp->v_dim < 1 || n_seqs < 0 ||
+      (n_seqs > 0 && sp->batch != 1))
+    return 0;
+  const int64_t slots = n_seqs > 0 ? (sp->length + 15) / 16 + n_seqs : sp->batch * ((sp->length + 15) / 16);
+  return (size_t)slots * sp->v_heads * sp->k_dim * sp->v_dim;
+}
+
 extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, const int32_t* cu_seqlens,
                                                int64_t n_seqs, const void* q, const void* k, const void* v,
                                                const float* g, const float* beta, const float* h0, void* o,
-                                               float* h_last, void* stream) {
+                                               float* h_last, float* ckpt, void* stream) {
   if (sp == nullptr) return RGLRU_ERR_INVALID_ARGUMENT;
   const rglru_delta_shape_t s = *sp;
   if (s.batch < 0 || s.length < 0 || s.batch > (int64_t(1) << 40) || s.length > (int64_t(1) << 40) ||
@@ -435,7 +455,7 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   if (blocks >= (int64_t(1) << 31)) return RGLRU_ERR_INVALID_ARGUMENT;
   if (s.k_dim > 256 || s.k_dim % 8 != 0 || s.v_dim % 8 != 0) return RGLRU_ERR_UNSUPPORTED;
   if (!aligned_to(q, 16) || !aligned_to(k, 16) || !aligned_to(v, 16) || !aligned_to(o, 16) ||
-      !aligned_to(g, kda ? 16 : 4) || !aligned_to(beta, 4) || !aligned_to(h0, 16) || !aligned_to(h_last, 16) ||
+      !aligned_to(g, kda ? 16 : 4) || !aligned_to(beta, 4) || !aligned_to(h0, 16) || !aligned_to(h_last, 16) || !aligned_to(ckpt, 4) ||
       !aligned_to(cu_seqlens, 4))
     return RGLRU_ERR_MISALIGNED;
   if (blocks == 0 || (tokens == 0 && h_last == nullptr)) return RGLRU_OK;
@@ -460,6 +480,8 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   a.n_blocks = (int)blocks;
   a.v_first = s.state_v_first;
   a.scale = s.scale;
+  a.ckpt = ckpt;
+  a.ck_slots = cu_seqlens != nullptr ? (s.length + 15) / 16 + n_seqs : s.batch * ((s.length + 15) / 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = s.io_dtype == RGLRU_IO_BF16;
   hipError_t e;

@@ -491,27 +491,78 @@ def _delta_common(q, k, v, g, beta, scale, initial_state, cu_seqlens, state_v_fi
     return shape, n, o, final_state
 
 
+def rglru_delta_ckpt_elems(shape: _lib.rglru_delta_shape_t, n_seqs: int = 0) -> int:
+    return int(_lib.load().rglru_delta_ckpt_elems(ctypes.byref(shape), int(n_seqs)))
+
+
 def rglru_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
                          scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
                          cu_seqlens: Optional[torch.Tensor] = None, state_v_first: bool = False,
                          output_final_state: bool = True, o: Optional[torch.Tensor] = None,
-                         final_state: Optional[torch.Tensor] = None):
+                         final_state: Optional[torch.Tensor] = None, training: bool = False,
+                         ckpt: Optional[torch.Tensor] = None):
     """Gated delta rule forward, token recurrence (GDN when g is [B, T, Hv], KDA when [B, T, Hv, Dk]).
 
     q, k [B, T, Hk, Dk] and v [B, T, Hv, Dv] in bfloat16 or float32 (one dtype);
     g, beta float32; states float32 [N, Hv, Dk, Dv] ([N, Hv, Dv, Dk] with
     state_v_first), N = B, or the number of sequences when cu_seqlens (int32
     [N + 1], B = 1) packs them. scale defaults to 1 / sqrt(Dk).
-    Returns (o [B, T, Hv, Dv], final state or None).
+    With training (or a ckpt tensor given), the forward also writes the
+    float32 checkpoint rglru_delta_rule_bwd needs. Returns (o [B, T, Hv, Dv],
+    final state or None), plus the checkpoint when training.
     """
     lib = _lib.load()
     shape, n, o, final_state = _delta_common(q, k, v, g, beta, scale, initial_state, cu_seqlens, state_v_first,
                                              output_final_state, o, final_state)
+    n_packed = n if cu_seqlens is not None else 0
+    if training or ckpt is not None:
+        ne = int(lib.rglru_delta_ckpt_elems(ctypes.byref(shape), n_packed))
+        ckpt = (torch.empty(max(ne, 1), dtype=torch.float32, device=q.device) if ckpt is None
+                else _need(ckpt, "ckpt", (ckpt.numel(),), torch.float32, q.device))
+        if ckpt.numel() < ne:
+            raise ValueError(f"ckpt needs {ne} elements")
     st = lib.rglru_delta_rule_fwd(ctypes.byref(shape), _ptr(cu_seqlens), n, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                  _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                  _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(ckpt),
                                   _stream(q.device))
     _lib.check(st, "rglru_delta_rule_fwd")
+    if training or ckpt is not None:
+        return o, final_state, ckpt
     return o, final_state
+
+
+def rglru_delta_rule_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                         ckpt: torch.Tensor, do: torch.Tensor, dh_last: Optional[torch.Tensor] = None, *,
+                         scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                         state_v_first: bool = False, want_dh0: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Backward of rglru_delta_rule_fwd (token form) from its checkpoint.
+
+    Returns (dq, dk, dv, dg, dbeta, dh0): dq, dk, dv in the io dtype, dg and
+    dbeta float32 in the shapes of g and beta, dh0 float32 in the layout of the
+    states (None unless want_dh0)."""
+    lib = _lib.load()
+    dev = q.device
+    shape, n, _, _ = _delta_common(q, k, v, g, beta, scale, None, cu_seqlens, state_v_first, False, do, None)
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    sshape = (n, Hv, Dv, Dk) if state_v_first else (n, Hv, Dk, Dv)
+    _opt(dh_last, "dh_last", sshape, torch.float32, dev)
+    n_packed = n if cu_seqlens is not None else 0
+    ne = int(lib.rglru_delta_ckpt_elems(ctypes.byref(shape), n_packed))
+    if not isinstance(ckpt, torch.Tensor) or ckpt.dtype != torch.float32 or ckpt.numel() < ne or ckpt.device != dev:
+        raise ValueError(f"ckpt must be a float32 tensor of at least {ne} elements on {dev}")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty(g.shape, dtype=torch.float32, device=dev)
+    dbeta = torch.empty(beta.shape, dtype=torch.float32, device=dev)
+    dh0 = torch.empty(sshape, dtype=torch.float32, device=dev) if want_dh0 else None
+    nbytes = int(lib.rglru_delta_bwd_workspace_bytes(ctypes.byref(shape), n_packed))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib.rglru_delta_rule_bwd(ctypes.byref(shape), _ptr(cu_seqlens), n, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), _ptr(ckpt), _ptr(do), _ptr(dh_last), _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(workspace), workspace.numel(),
+                                  _stream(dev))
+    _lib.check(st, "rglru_delta_rule_bwd")
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def rglru_delta_chunk_workspace_bytes(shape: _lib.rglru_delta_shape_t, n_seqs: int = 0) -> int:

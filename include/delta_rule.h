@@ -65,6 +65,9 @@ typedef struct {
  *                ([N, Hv, Dv, Dk] with state_v_first), 16-byte aligned.
  *   h_last     : NULL or the final states, same layout and alignment as h0; a
  *                sequence with no tokens gets its initial state.
+ *   ckpt       : NULL (inference) or rglru_delta_ckpt_elems(shape, n) float32
+ *                (n = n_seqs with cu_seqlens, else 0): the state entering
+ *                every 16-token chunk, which rglru_delta_rule_bwd needs.
  * q, k, v, g, beta and o may be NULL only when B * T = 0. Returns
  * RGLRU_ERR_INVALID_ARGUMENT, RGLRU_ERR_MISALIGNED or RGLRU_ERR_UNSUPPORTED
  * without launching anything, RGLRU_ERR_HIP if the launch fails. Outputs
@@ -72,7 +75,42 @@ typedef struct {
 rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* shape, const int32_t* cu_seqlens,
                                     int64_t n_seqs, const void* q, const void* k, const void* v,
                                     const float* g, const float* beta, const float* h0, void* o,
-                                    float* h_last, void* stream);
+                                    float* h_last, float* ckpt, void* stream);
+
+/* Float32 elements of the forward's checkpoint: per value head, ceil(T / 16)
+ * slots per batch row (B rows), or ceil(T / 16) + n_seqs slots for packed
+ * sequences, of Dk * Dv each. 0 for an invalid shape. */
+size_t rglru_delta_ckpt_elems(const rglru_delta_shape_t* shape, int64_t n_seqs);
+
+/* Backward of rglru_delta_rule_fwd (token form, GDN or KDA) for the loss
+ * <do, o> + <dh_last, final state>: the reverse-mode steps of the same
+ * recurrence (the page's recurrent oracle keeps gradients through every input
+ * and the initial state). The forward must have run with ckpt on the same
+ * inputs; h0 is not needed again (the checkpoint holds it).
+ *
+ *   q, k, v, g, beta, cu_seqlens, n_seqs : as for the forward.
+ *   ckpt       : the forward's checkpoint.
+ *   d_o        : [B, T, Hv, Dv] io, 16-byte aligned: the gradient of o.
+ *   dh_last    : NULL (zero) or the gradient of the final state, layout of h0.
+ *   dq, dk     : [B, T, Hk, Dk] io (summed over the value heads of each key head).
+ *   dv         : [B, T, Hv, Dv] io, 16-byte aligned.
+ *   dg         : float32, the shape of g.  dbeta : [B, T, Hv] float32.
+ *   dh0        : NULL or the gradient of the initial state, layout of h0.
+ *   workspace  : rglru_delta_bwd_workspace_bytes(shape, n) bytes (n as for
+ *                the checkpoint), 256-byte aligned, no initial contents
+ *                required: per-column-block partial sums, which a second
+ *                launch adds in a fixed order, so results are bitwise
+ *                reproducible.
+ * Restrictions (RGLRU_ERR_UNSUPPORTED otherwise): k_dim at most 128, k_dim
+ * and v_dim multiples of 8. Invalid offsets give unspecified (in-bounds)
+ * results. Returns as the forward does. */
+size_t rglru_delta_bwd_workspace_bytes(const rglru_delta_shape_t* shape, int64_t n_seqs);
+rglru_status_t rglru_delta_rule_bwd(const rglru_delta_shape_t* shape, const int32_t* cu_seqlens,
+                                    int64_t n_seqs, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const float* ckpt, const void* d_o,
+                                    const float* dh_last, void* dq, void* dk, void* dv, float* dg,
+                                    float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /* The same forward for GDN in chunk form (chunk_gdn_reference on the same
  * page: within each chunk of 64 tokens, a unit-lower-triangular solve gives

@@ -192,7 +192,7 @@ int main() {
   float* wf = (float*)p;
   const int32_t* dcu = (const int32_t*)p;
   auto dfwd = [&](const rglru_delta_shape_t& d, const void* q, const int32_t* c = nullptr, int64_t n = 0) {
-    return rglru_delta_rule_fwd(&d, c, n, q, p, p, fp, fp, nullptr, p, nullptr, nullptr);
+    return rglru_delta_rule_fwd(&d, c, n, q, p, p, fp, fp, nullptr, p, nullptr, nullptr, nullptr);
   };
   rglru_delta_shape_t d = dshape(2, 64, 2, 3, 64, 64, 1, 0);
   EXPECT(dfwd(d, p) == RGLRU_ERR_INVALID_ARGUMENT);  // Hv not a multiple of Hk
@@ -214,8 +214,25 @@ int main() {
   EXPECT(dfwd(d, p) == RGLRU_ERR_INVALID_ARGUMENT);  // 2^41 tokens
   d = dshape(1, 64, 1, 1, 64, 64, 1, 0);
   EXPECT(dfwd(d, p, dcu, 0) == RGLRU_ERR_INVALID_ARGUMENT);  // no sequences
-  EXPECT(rglru_delta_rule_fwd(nullptr, nullptr, 0, p, p, p, fp, fp, nullptr, p, nullptr, nullptr) ==
+  EXPECT(rglru_delta_rule_fwd(nullptr, nullptr, 0, p, p, p, fp, fp, nullptr, p, nullptr, nullptr, nullptr) ==
          RGLRU_ERR_INVALID_ARGUMENT);
+  // checkpoint and backward
+  rglru_delta_shape_t b1 = dshape(2, 100, 1, 2, 128, 64, 1, 0);
+  EXPECT(rglru_delta_ckpt_elems(&b1, 0) == (size_t)2 * 7 * 2 * 128 * 64);
+  rglru_delta_shape_t b2 = dshape(1, 100, 1, 2, 128, 64, 1, 0);
+  EXPECT(rglru_delta_ckpt_elems(&b2, 3) == (size_t)(7 + 3) * 2 * 128 * 64);
+  EXPECT(rglru_delta_ckpt_elems(&b1, 3) == 0);   // packed sequences need B = 1
+  const size_t bws = rglru_delta_bwd_workspace_bytes(&b1, 0);
+  EXPECT(bws > 0 && bws % 256 == 0);
+  auto bwd = [&](const rglru_delta_shape_t& d, size_t bytes, const void* dq) {
+    return rglru_delta_rule_bwd(&d, nullptr, 0, p, p, p, fp, fp, fp, p, nullptr, (void*)dq, p, p, wf, wf, nullptr, p,
+                                bytes, nullptr);
+  };
+  EXPECT(bwd(b1, 16, p) == RGLRU_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(bwd(b1, bws, nullptr) == RGLRU_ERR_INVALID_ARGUMENT);
+  rglru_delta_shape_t b3 = dshape(2, 100, 1, 2, 256, 64, 1, 0);
+  EXPECT(bwd(b3, bws, p) == RGLRU_ERR_UNSUPPORTED);   // the backward holds Dk <= 128
+  EXPECT(rglru_delta_bwd_workspace_bytes(&b3, 0) == 0);
   rglru_delta_shape_t c1 = dshape(2, 100, 1, 2, 128, 128, 1, 0);
   const size_t cws = rglru_delta_chunk_workspace_bytes(&c1, 0);
   EXPECT(cws > 0 && cws % 256 == 0);

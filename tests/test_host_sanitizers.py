@@ -45,7 +45,7 @@ def test_abi_host_code_under_sanitizers(tmp_path):
            str(empty), "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer", *HOST_SANITIZE, f"-I{inc}", f"-I{CSRC}",
            "-o", str(exe), os.path.join(HOST, "abi_check.cpp"), os.path.join(CSRC, "rglru_scan.hip"),
            os.path.join(CSRC, "rglru_proj.hip"), os.path.join(CSRC, "delta_rule.hip"),
-           os.path.join(CSRC, "delta_chunk.hip"), f"-Wl,{shim}"]
+           os.path.join(CSRC, "delta_chunk.hip"), os.path.join(CSRC, "delta_bwd.hip"), f"-Wl,{shim}"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
     env = dict(os.environ)
