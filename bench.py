@@ -401,9 +401,43 @@ def run_delta(args, wid, steps, warmup):
                          "algorithmic_flops_per_launch": cflops, "launch_ms": round(cms, 5)},
             "speedup_vs_token_recurrence": round(ms / cms, 3),
         }
+    backward = None
+    if T >= 16:
+        # training step of the token form: the forward writing its checkpoint, then the backward
+        n_ck = glr.rglru_delta_ckpt_elems(shape, 0)
+        for d in sets:
+            d["ck"] = torch.empty(n_ck, dtype=torch.float32, device=dev)
+            d["do"] = torch.randn_like(d["v"], dtype=torch.float32).to(d["v"].dtype)
+        bws = torch.empty(max(glr.rglru_delta_bwd_workspace_bytes(shape, 0), 1), dtype=torch.uint8, device=dev)
+
+        def fwd_train(d):
+            glr.rglru_delta_rule_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
+                                     o=d["o"], final_state=d["fs"], ckpt=d["ck"])
+
+        def bwd(d):
+            glr.rglru_delta_rule_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["ck"], d["do"], d["fs"],
+                                     workspace=bws)
+
+        ftm = timed(fwd_train)
+        for d in sets:
+            fwd_train(d)
+        btm = timed(bwd)
+        # per state element and token: recomputing the step (5 flops) and the reverse step
+        # (17: the read-out's gradient, dq, du, dk, the decayed gradient, dg and its decay)
+        bflops = 22 * B * T * Hv * Dk * Dv
+        btf = bflops / (btm * 1e-3) / 1e12
+        backward = {
+            "call": "rglru_delta_rule_fwd with its checkpoint + rglru_delta_rule_bwd (token form)",
+            "fwd_train_ms": round(ftm, 5), "bwd_ms": round(btm, 5), "step_ms": round(ftm + btm, 5),
+            "roofline": {"kernel": "delta_bwd_kernel + delta_bwd_reduce", "bound": "alu", "achieved": round(btf, 2),
+                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(btf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": bflops, "launch_ms": round(btm, 5)},
+        }
     del sets
     torch.cuda.empty_cache()
     return {
+        "backward": backward,
         "call": "rglru_delta_rule_fwd (token recurrence)",
         "config": {"workload": wl.name, "batch": B, "length": T, "k_heads": wl.k_heads, "v_heads": Hv,
                    "k_dim": Dk, "v_dim": Dv, "io": wl.io, "decay": "KDA" if wl.kda else "GDN",

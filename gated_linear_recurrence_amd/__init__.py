@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     rglru_blockdiag_gate_proj_fwd,
     rglru_bwd,
     rglru_bwd_workspace_bytes,
+    rglru_delta_bwd_workspace_bytes,
     rglru_delta_chunk_fwd,
     rglru_delta_chunk_workspace_bytes,
     rglru_delta_ckpt_elems,

@@ -14,11 +14,12 @@
 // lanes, R rows each, and the columns are independent, so each workgroup
 // walks its 256 / LPC columns of one head through the tokens in reverse,
 // 16-token chunk by chunk: it reloads the state entering the chunk from the
-// forward's checkpoint, recomputes the chunk's decayed states S~ (kept in
-// registers) forward, then runs the reverse steps. dv and the initial
+// forward's checkpoint, recomputes the chunk's decayed states S~ forward
+// (keeping those of one half chunk in registers, so each half's are
+// recomputed from the checkpoint), then runs the reverse steps. dv and the initial
 // state's gradient belong to single columns; dq, dk, dbeta and dg sum over
 // all columns of a head, so the workgroup sums its columns in a fixed order
-// (lane shuffles inside a wave, then the waves' LDS slots in wave order)
+// (DPP adds inside a wave, then the waves' LDS slots in wave order)
 // and writes per-column-block partials, which delta_bwd_reduce adds over the
 // column blocks and the value heads of a key head, again in a fixed order:
 // results are bitwise reproducible.
@@ -73,21 +74,27 @@ __device__ __forceinline__ float dpp_sum_step(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// sum over each group of LPC consecutive lanes (the rows of one column); every lane gets it
-template <int LPC>
-__device__ __forceinline__ float group_sum(float x) {
-  x = dpp_sum_step<0xB1>(x);
-  x = dpp_sum_step<0x4E>(x);
-  x = dpp_sum_step<0x141>(x);
-  if constexpr (LPC == 16) x = dpp_sum_step<0x140>(x);
+// Lane layout of the backward: lane = rb * CPW + ciw, the CPW = 64 / LPC columns of a wave
+// interleaved in the low lane bits, so that the sums over a wave's columns (18 per token) stay
+// inside a quad or half-row (DPP), and only the sums over a column's rows (3 per token) cross
+// DPP rows.
+
+// sum over the columns of a wave (lanes with the same rb), every lane gets it; fixed order
+template <int CPW>
+__device__ __forceinline__ float column_sum(float x) {
+  x = dpp_sum_step<0xB1>(x);                               // quad_perm [1,0,3,2]
+  x = dpp_sum_step<0x4E>(x);                               // quad_perm [2,3,0,1]
+  if constexpr (CPW == 8) x = dpp_sum_step<0x141>(x);      // row_half_mirror: the other quad of 8
   return x;
 }
 
-// sum over the columns of a wave (lanes LPC, 2 LPC, ... apart), in a fixed order
-template <int LPC>
-__device__ __forceinline__ float wave_column_sum(float x) {
-#pragma unroll
-  for (int m = LPC; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+// sum over the rows of a column (lanes with the same ciw), every lane gets it; fixed order
+template <int CPW>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (CPW == 4) x = dpp_sum_step<0x124>(x);      // row_ror 4
+  x = dpp_sum_step<0x128>(x);                              // row_ror 8
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
   return x;
 }
 
@@ -121,7 +128,7 @@ struct Io {
 };
 
 template <int LPC, int R, bool KDA, bool BF>
-__global__ __launch_bounds__(kThreads) void delta_bwd_kernel(BwdArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void delta_bwd_kernel(BwdArgs p) {
   using IO = Io<BF>;
   constexpr int VW = IO::VW;
   constexpr int DKP = LPC * R;
@@ -138,10 +145,12 @@ __global__ __launch_bounds__(kThreads) void delta_bwd_kernel(BwdArgs p) {
   __shared__ __align__(16) float sv[kTC][CW];
   __shared__ __align__(16) float sdo[kTC][CW];
   __shared__ __align__(16) float sdv[kTC][CW];
-  __shared__ float rq[NW][kTC][DKP];
-  __shared__ float rk[NW][kTC][DKP];
-  __shared__ float rg[NW][kTC][KDA ? DKP : 1];
-  __shared__ float rb_[NW][kTC];
+  // per-wave column sums of dq, dk (and dg, dbeta) for half a chunk, flushed every kTH tokens
+  constexpr int kTH = kTC / 2;
+  __shared__ float rq[NW][kTH][DKP];
+  __shared__ float rk[NW][kTH][DKP];
+  __shared__ float rg[NW][kTH][KDA ? DKP : 1];
+  __shared__ float rb_[NW][kTH];
 
   const int bid = xcd_remap(blockIdx.x, p.n_blocks);
   const int cb = bid % p.n_cb;
@@ -165,8 +174,9 @@ __global__ __launch_bounds__(kThreads) void delta_bwd_kernel(BwdArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rb = lane % LPC;
-  const int ciw = lane / LPC;  // column within the wave
+  constexpr int CPW = 64 / LPC;  // columns per wave
+  const int rb = lane / CPW;      // row block of the column
+  const int ciw = lane % CPW;     // column within the wave
   const int cl = wave * (64 / LPC) + ciw;
   const int col = cb * CW + cl;
   const bool col_ok = col < p.Dv;
@@ -241,49 +251,57 @@ __global__ __launch_bounds__(kThreads) void delta_bwd_kernel(BwdArgs p) {
       if constexpr (!KDA) sgs[tid] = ok ? expf(p.g[e0]) : 1.f;
     }
     // the state entering the chunk
-    float s[R];
+    float s0[R];
     {
       const float* ck = p.ckpt + (ck0 + c) * p.Dk * p.Dv;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int row = rb * R + i;
-        s[i] = (col_ok && row < p.Dk) ? ck[(int64_t)row * p.Dv + col] : 0.f;
+        s0[i] = (col_ok && row < p.Dk) ? ck[(int64_t)row * p.Dv + col] : 0.f;
       }
     }
     __syncthreads();
 
-    // recompute the chunk forward: decayed states S~, errors e and writes u
-    float hs[kTC][R], he[kTC], hu[kTC];
+    // decayed states S~, errors e and writes u of one half chunk, recomputed forward from the
+    // chunk's checkpoint (the steps before the half are run again and not kept): holding half
+    // a chunk is what lets two waves share a SIMD's registers
+    constexpr int kHS = kTH;
+    float hs[kHS][R], he[kHS], hu[kHS];
+    auto recompute = [&](const int lo) {
+      float s[R];
 #pragma unroll
-    for (int t = 0; t < kTC; ++t) {
-      if (t < nt) {
-        float kk[R];
+      for (int i = 0; i < R; ++i) s[i] = s0[i];
 #pragma unroll
-        for (int i = 0; i < R; ++i) kk[i] = sk[t][rb * R + i];
+      for (int t = 0; t < kTC; ++t) {
+        if (t < lo + kHS && t < nt) {
+          float kk[R];
 #pragma unroll
-        for (int i = 0; i < R; ++i) s[i] *= KDA ? sg[t][rb * R + i] : sgs[t];
-        float a0 = 0.f, a1 = 0.f;
+          for (int i = 0; i < R; ++i) kk[i] = sk[t][rb * R + i];
 #pragma unroll
-        for (int i = 0; i < R; i += 2) {
-          a0 = fmaf(s[i], kk[i], a0);
-          a1 = fmaf(s[i + 1], kk[i + 1], a1);
+          for (int i = 0; i < R; ++i) s[i] *= KDA ? sg[t][rb * R + i] : sgs[t];
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int i = 0; i < R; i += 2) {
+            a0 = fmaf(s[i], kk[i], a0);
+            a1 = fmaf(s[i + 1], kk[i + 1], a1);
+          }
+          const float e = (col_ok ? sv[t][cl] : 0.f) - row_sum<CPW>(a0 + a1);
+          const float u = sb[t] * e;
+          if (t >= lo) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) hs[t - lo][i] = s[i];
+            he[t - lo] = e;
+            hu[t - lo] = u;
+          }
+#pragma unroll
+          for (int i = 0; i < R; ++i) s[i] = fmaf(u, kk[i], s[i]);
         }
-        const float e = (col_ok ? sv[t][cl] : 0.f) - group_sum<LPC>(a0 + a1);
-        const float u = sb[t] * e;
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          hs[t][i] = s[i];
-          s[i] = fmaf(u, kk[i], s[i]);
-        }
-        he[t] = e;
-        hu[t] = u;
       }
-    }
+    };
 
-    // the reverse steps
-#pragma unroll
-    for (int t = kTC - 1; t >= 0; --t) {
-      if (t < nt) {
+    // the reverse steps, the per-wave sums flushed to this column block's partials (waves
+    // summed in order) after each half chunk
+    auto rev = [&](const int t) {
         float kk[R], qq[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -296,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void delta_bwd_kernel(BwdArgs p) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
           G[i] = fmaf(p.scale * qq[i], dov, G[i]);
-          dqv[i] = p.scale * fmaf(kk[i], hu[t], hs[t][i]) * dov;  // scale S do with S = S~ + k u
+          dqv[i] = p.scale * fmaf(kk[i], hu[t & (kHS - 1)], hs[t & (kHS - 1)][i]) * dov;  // scale S do with S = S~ + k u
         }
         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
@@ -304,81 +322,92 @@ __global__ __launch_bounds__(kThreads) void delta_bwd_kernel(BwdArgs p) {
           d0 = fmaf(G[i], kk[i], d0);
           d1 = fmaf(G[i + 1], kk[i + 1], d1);
         }
-        const float du = group_sum<LPC>(d0 + d1);
+        const float du = row_sum<CPW>(d0 + d1);
         const float da = -bt * du;
         float gs0 = 0.f;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          dkv[i] = fmaf(G[i], hu[t], hs[t][i] * da);
+          dkv[i] = fmaf(G[i], hu[t & (kHS - 1)], hs[t & (kHS - 1)][i] * da);
           const float gt = fmaf(kk[i], da, G[i]);  // G~ = G - beta k du^T
           if constexpr (KDA) {
-            dgv[i] = gt * hs[t][i];
+            dgv[i] = gt * hs[t & (kHS - 1)][i];
             G[i] = gt * sg[t][rb * R + i];
           } else {
-            gs0 = fmaf(gt, hs[t][i], gs0);
+            gs0 = fmaf(gt, hs[t & (kHS - 1)][i], gs0);
             G[i] = gt * sgs[t];
           }
         }
-        if constexpr (!KDA) dgv[0] = group_sum<LPC>(gs0);
-        float dbv = he[t] * du;  // the same on every lane of the column
+        if constexpr (!KDA) dgv[0] = row_sum<CPW>(gs0);
+        float dbv = he[t & (kHS - 1)] * du;  // the same on every lane of the column
         if (rb == 0 && col_ok) sdv[t][cl] = bt * du;
         // sum over the wave's columns (fixed order), then one slot per wave
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          dqv[i] = wave_column_sum<LPC>(col_ok ? dqv[i] : 0.f);
-          dkv[i] = wave_column_sum<LPC>(col_ok ? dkv[i] : 0.f);
+          dqv[i] = column_sum<CPW>(col_ok ? dqv[i] : 0.f);
+          dkv[i] = column_sum<CPW>(col_ok ? dkv[i] : 0.f);
         }
         if constexpr (KDA) {
 #pragma unroll
-          for (int i = 0; i < R; ++i) dgv[i] = wave_column_sum<LPC>(col_ok ? dgv[i] : 0.f);
+          for (int i = 0; i < R; ++i) dgv[i] = column_sum<CPW>(col_ok ? dgv[i] : 0.f);
         } else {
-          dgv[0] = wave_column_sum<LPC>(col_ok ? dgv[0] : 0.f);
+          dgv[0] = column_sum<CPW>(col_ok ? dgv[0] : 0.f);
         }
-        dbv = wave_column_sum<LPC>(col_ok ? dbv : 0.f);
+        dbv = column_sum<CPW>(col_ok ? dbv : 0.f);
         if (ciw == 0) {
 #pragma unroll
           for (int i = 0; i < R; ++i) {
-            rq[wave][t][rb * R + i] = dqv[i];
-            rk[wave][t][rb * R + i] = dkv[i];
-            if constexpr (KDA) rg[wave][t][rb * R + i] = dgv[i];
+            rq[wave][t & (kTH - 1)][rb * R + i] = dqv[i];
+            rk[wave][t & (kTH - 1)][rb * R + i] = dkv[i];
+            if constexpr (KDA) rg[wave][t & (kTH - 1)][rb * R + i] = dgv[i];
           }
           if (rb == 0) {
-            if constexpr (!KDA) rg[wave][t][0] = dgv[0];
-            rb_[wave][t] = dbv;
+            if constexpr (!KDA) rg[wave][t & (kTH - 1)][0] = dgv[0];
+            rb_[wave][t & (kTH - 1)] = dbv;
           }
         }
+    };
+    auto flush = [&](const int lo) {
+      __syncthreads();
+      for (int idx = tid; idx < kTH * DKP; idx += kThreads) {
+        const int tt = idx / DKP, d = idx % DKP;
+        if (lo + tt < nt && d < p.Dk) {
+          float aq = 0.f, ak = 0.f, ag = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            aq += rq[w][tt][d];
+            ak += rk[w][tt][d];
+            if constexpr (KDA) ag += rg[w][tt][d];
+          }
+          const int64_t e0 = (((int64_t)cb * p.tokens + t0 + lo + tt) * p.Hv + h) * p.Dk + d;
+          p.pdq[e0] = aq;
+          p.pdk[e0] = ak;
+          if constexpr (KDA) p.pdg[e0] = ag;
+        }
       }
-    }
-    __syncthreads();
-
-    // this column block's partials for the chunk (waves summed in order), and dv
-    for (int idx = tid; idx < nt * DKP; idx += kThreads) {
-      const int tt = idx / DKP, d = idx % DKP;
-      if (d < p.Dk) {
-        float aq = 0.f, ak = 0.f, ag = 0.f;
+      if (tid < kTH && lo + tid < nt) {
+        float ag = 0.f, ab = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          aq += rq[w][tt][d];
-          ak += rk[w][tt][d];
-          if constexpr (KDA) ag += rg[w][tt][d];
+          if constexpr (!KDA) ag += rg[w][tid][0];
+          ab += rb_[w][tid];
         }
-        const int64_t e0 = (((int64_t)cb * p.tokens + t0 + tt) * p.Hv + h) * p.Dk + d;
-        p.pdq[e0] = aq;
-        p.pdk[e0] = ak;
-        if constexpr (KDA) p.pdg[e0] = ag;
+        const int64_t e0 = ((int64_t)cb * p.tokens + t0 + lo + tid) * p.Hv + h;
+        if constexpr (!KDA) p.pdg[e0] = ag;
+        p.pdb[e0] = ab;
       }
-    }
-    if (tid < nt) {
-      float ag = 0.f, ab = 0.f;
+      __syncthreads();
+    };
+    recompute(kTC - kHS);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        if constexpr (!KDA) ag += rg[w][tid][0];
-        ab += rb_[w][tid];
-      }
-      const int64_t e0 = ((int64_t)cb * p.tokens + t0 + tid) * p.Hv + h;
-      if constexpr (!KDA) p.pdg[e0] = ag;
-      p.pdb[e0] = ab;
-    }
+    for (int t = kTC - 1; t >= kTH; --t)
+      if (t < nt) rev(t);
+    flush(kTH);
+    recompute(0);
+#pragma unroll
+    for (int t = kTH - 1; t >= 0; --t)
+      if (t < nt) rev(t);
+    flush(0);
+    // dv
     {
       const int tt = tid / VPT, part = tid % VPT;
       const int c0 = cb * CW + part * VW;

@@ -530,6 +530,11 @@ def rglru_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
     return o, final_state
 
 
+def rglru_delta_bwd_workspace_bytes(shape: _lib.rglru_delta_shape_t, n_seqs: int = 0) -> int:
+    """Workspace bytes of rglru_delta_rule_bwd: n_seqs packed sequences, or 0 for B rows."""
+    return int(_lib.load().rglru_delta_bwd_workspace_bytes(ctypes.byref(shape), int(n_seqs)))
+
+
 def rglru_delta_rule_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                          ckpt: torch.Tensor, do: torch.Tensor, dh_last: Optional[torch.Tensor] = None, *,
                          scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
