@@ -211,6 +211,9 @@ def main():
                     help="instead: only the gated delta rule workloads (one JSON object per workload)")
     ap.add_argument("--delta-workload", type=int, default=None, choices=(10, 11, 12),
                     help="with --delta-only: that delta-rule workload alone")
+    ap.add_argument("--delta-no-backward", action="store_true",
+                    help="with --delta-only: skip the delta rule's training step (forward with "
+                         "checkpoint + backward), so the forward kernels run in one configuration")
     args = ap.parse_args()
 
     if args.delta_only:
@@ -402,7 +405,7 @@ def run_delta(args, wid, steps, warmup):
             "speedup_vs_token_recurrence": round(ms / cms, 3),
         }
     backward = None
-    if T >= 16:
+    if T >= 16 and not getattr(args, "delta_no_backward", False):
         # training step of the token form: the forward writing its checkpoint, then the backward
         n_ck = glr.rglru_delta_ckpt_elems(shape, 0)
         for d in sets:
@@ -431,7 +434,8 @@ def run_delta(args, wid, steps, warmup):
             "fwd_train_ms": round(ftm, 5), "bwd_ms": round(btm, 5), "step_ms": round(ftm + btm, 5),
             "roofline": {"kernel": "delta_bwd_kernel + delta_bwd_reduce", "bound": "alu", "achieved": round(btf, 2),
                          "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(btf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(btf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic(f"{wl.name}:delta_bwd"),
                          "algorithmic_flops_per_launch": bflops, "launch_ms": round(btm, 5)},
         }
     del sets

@@ -9,12 +9,14 @@
         (__amd_rocclr_copyBuffer) of CALIB_MIB MiB in the same run; prints a
         markdown table and a JSON object of bytes per dispatch
 
-    python rocpd_summary.py traffic-json FETCH.db WRITE.db CALIB_MIB WORKLOAD OUT.json SOURCE [COMMIT]
+    python rocpd_summary.py traffic-json FETCH.db WRITE.db CALIB_MIB WORKLOAD OUT.json SOURCE [COMMIT] [--groups G,...]
         the same figures summed per library call (forward scan, backward scan,
-        projection forward, projection backward) and merged into OUT.json
-        under "WORKLOAD:fwd", ":bwd", ":proj_fwd", ":proj_bwd" (the file
-        bench.py reads); SOURCE names the summary the figures come from and
-        COMMIT the source revision of the kernels that were counted
+        projection forward, projection backward, the delta rule's token form,
+        chunk form and backward) and merged into OUT.json under
+        "WORKLOAD:fwd", ":bwd", ":proj_fwd", ":proj_bwd", ":delta_token",
+        ":delta_chunk", ":delta_bwd" (the file bench.py reads); SOURCE names
+        the summary the figures come from and COMMIT the source revision of
+        the kernels that were counted; --groups keeps only the named calls
 
     python rocpd_summary.py counters TRACE.db PMC.db [PMC.db ...]
         per-kernel averages of every counter in the --pmc runs, with the
@@ -83,17 +85,18 @@ def traffic(fetch_db: str, write_db: str, calib_mib: float):
 # last template argument tells the fused instantiation from the plain scan)
 GROUPS = {
     "fwd": lambda n: "fwd_kernel<" in n and "delta_fwd_kernel<" not in n and not n.endswith(", true>(FwdArgs)"),
-    "bwd": lambda n: "bwd_kernel<" in n or "bwd_dlam_kernel(" in n,
+    "bwd": lambda n: ("bwd_kernel<" in n and "delta_bwd_kernel<" not in n) or "bwd_dlam_kernel(" in n,
     "proj_fwd": lambda n: "proj_fwd_kernel(" in n,
     "proj_bwd": lambda n: any(k in n for k in ("proj_dw_kernel(", "proj_dw_reduce_kernel(", "proj_dx_kernel<")),
     "fused_fwd": lambda n: ("fwd_kernel<" in n and n.endswith(", true>(FwdArgs)")) or "w_frag_kernel(" in n,
     "delta_token": lambda n: "delta_fwd_kernel<" in n,
     "delta_chunk": lambda n: any(k in n for k in ("gdn_chunk_prep<", "gdn_chunk_state<", "gdn_chunk_map(")),
+    "delta_bwd": lambda n: any(k in n for k in ("delta_bwd_kernel<", "delta_bwd_reduce_qk<", "delta_bwd_reduce_gb(")),
 }
 
 
 def traffic_json(fetch_db: str, write_db: str, calib_mib: float, workload: str, out: str, source: str,
-                 commit: str = None):
+                 commit: str = None, groups=None):
     _, per = traffic(fetch_db, write_db, calib_mib)
     try:
         with open(out) as f:
@@ -102,7 +105,7 @@ def traffic_json(fetch_db: str, write_db: str, calib_mib: float, workload: str, 
         doc = {}
     for group, match in GROUPS.items():
         names = [n for n in per if match(n)]
-        if not names:
+        if not names or (groups is not None and group not in groups):
             continue
         rb = sum(per[n]["read_bytes"] for n in names)
         wb = sum(per[n]["write_bytes"] for n in names)
@@ -165,6 +168,11 @@ def counters(trace_db: str, pmc_dbs) -> str:
 
 
 def main(argv):
+    groups = None
+    if "--groups" in argv:
+        i = argv.index("--groups")
+        groups = set(argv[i + 1].split(","))
+        argv = argv[:i] + argv[i + 2:]
     if len(argv) >= 2 and argv[0] == "kernels":
         print(kernels(argv[1]))
     elif len(argv) >= 4 and argv[0] == "traffic":
@@ -174,7 +182,7 @@ def main(argv):
         print(json.dumps(per, indent=1))
     elif len(argv) >= 7 and argv[0] == "traffic-json":
         doc = traffic_json(argv[1], argv[2], float(argv[3]), argv[4], argv[5], argv[6],
-                           argv[7] if len(argv) >= 8 else None)
+                           argv[7] if len(argv) >= 8 else None, groups)
         print(json.dumps(doc, indent=1))
     elif len(argv) >= 3 and argv[0] == "counters":
         print(counters(argv[1], argv[2:]))
