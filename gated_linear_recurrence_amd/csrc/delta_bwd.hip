@@ -88,13 +88,28 @@ __device__ __forceinline__ float column_sum(float x) {
   return x;
 }
 
+// x[lane] + x[lane ^ 16] (ROWS = 16) or x[lane] + x[lane ^ 32] (ROWS = 32) on every lane: the
+// permlane swap of a register with a copy of itself leaves, in each lane, the pair of values the
+// xor partner and the lane hold (a VALU exchange; a shuffle would go through LDS)
+template <int ROWS>
+__device__ __forceinline__ float swap_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (ROWS == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 // sum over the rows of a column (lanes with the same ciw), every lane gets it; fixed order
 template <int CPW>
 __device__ __forceinline__ float row_sum(float x) {
   if constexpr (CPW == 4) x = dpp_sum_step<0x124>(x);      // row_ror 4
   x = dpp_sum_step<0x128>(x);                              // row_ror 8
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
+  x = swap_sum<16>(x);
+  x = swap_sum<32>(x);
   return x;
 }
 
