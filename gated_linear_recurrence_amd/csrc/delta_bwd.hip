@@ -194,6 +194,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int ciw = lane % CPW;     // column within the wave
   const int cl = wave * (64 / LPC) + ciw;
   const int col = cb * CW + cl;
+  // lanes of columns past Dv start from a zero state and gradient and read v and do staged as
+  // zero, so every term they add to the column sums is zero and needs no mask
   const bool col_ok = col < p.Dv;
   const int64_t st_base = ((int64_t)n * p.Hv + h) * p.Dk * p.Dv;
   auto st_index = [&](int row) -> int64_t {
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
         sk[tt][part * VW + e] = fk[e];
-        sq[tt][part * VW + e] = fq[e];
+        sq[tt][part * VW + e] = p.scale * fq[e];
       }
     }
     if constexpr (KDA) {
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             a0 = fmaf(s[i], kk[i], a0);
             a1 = fmaf(s[i + 1], kk[i + 1], a1);
           }
-          const float e = (col_ok ? sv[t][cl] : 0.f) - row_sum<CPW>(a0 + a1);
+          const float e = sv[t][cl] - row_sum<CPW>(a0 + a1);
           const float u = sb[t] * e;
           if (t >= lo) {
 #pragma unroll
@@ -323,13 +325,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           kk[i] = sk[t][rb * R + i];
           qq[i] = sq[t][rb * R + i];
         }
-        const float dov = col_ok ? sdo[t][cl] : 0.f;
+        const float dov = sdo[t][cl];
+        const float dovs = p.scale * dov;
         const float bt = sb[t];
         float dqv[R], dkv[R], dgv[KDA ? R : 1];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          G[i] = fmaf(p.scale * qq[i], dov, G[i]);
-          dqv[i] = p.scale * fmaf(kk[i], hu[t & (kHS - 1)], hs[t & (kHS - 1)][i]) * dov;  // scale S do with S = S~ + k u
+          G[i] = fmaf(qq[i], dov, G[i]);  // qq holds scale q
+          dqv[i] = fmaf(kk[i], hu[t & (kHS - 1)], hs[t & (kHS - 1)][i]) * dovs;  // scale S do with S = S~ + k u
         }
         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
@@ -358,16 +361,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // sum over the wave's columns (fixed order), then one slot per wave
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          dqv[i] = column_sum<CPW>(col_ok ? dqv[i] : 0.f);
-          dkv[i] = column_sum<CPW>(col_ok ? dkv[i] : 0.f);
+          dqv[i] = column_sum<CPW>(dqv[i]);
+          dkv[i] = column_sum<CPW>(dkv[i]);
         }
         if constexpr (KDA) {
 #pragma unroll
-          for (int i = 0; i < R; ++i) dgv[i] = column_sum<CPW>(col_ok ? dgv[i] : 0.f);
+          for (int i = 0; i < R; ++i) dgv[i] = column_sum<CPW>(dgv[i]);
         } else {
-          dgv[0] = column_sum<CPW>(col_ok ? dgv[0] : 0.f);
+          dgv[0] = column_sum<CPW>(dgv[0]);
         }
-        dbv = column_sum<CPW>(col_ok ? dbv : 0.f);
+        dbv = column_sum<CPW>(dbv);
         if (ciw == 0) {
 #pragma unroll
           for (int i = 0; i < R; ++i) {
