@@ -12,7 +12,7 @@
 //
 // Like the forward, a column of the [Dk, Dv] state (and of G) lives in LPC
 // lanes, R rows each, and the columns are independent, so each workgroup
-// walks its 256 / LPC columns of one head through the tokens in reverse,
+// walks its 512 / LPC columns of one head through the tokens in reverse,
 // 16-token chunk by chunk: it reloads the state entering the chunk from the
 // forward's checkpoint, recomputes the chunk's decayed states S~ forward
 // (keeping those of one half chunk in registers, so each half's are
@@ -33,7 +33,7 @@
 namespace rglru {
 namespace dbwd {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves: one workgroup per CU, two waves per SIMD
 constexpr int kTC = 16;  // tokens per chunk (the forward's checkpoint interval)
 
 struct BwdArgs {
