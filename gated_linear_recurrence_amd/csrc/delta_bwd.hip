@@ -71,7 +71,8 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_sum_step(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  // every control used here reads a valid lane, so no "old" value is needed (mov_dpp leaves it undefined)
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Lane layout of the backward: lane = rb * CPW + ciw, the CPW = 64 / LPC columns of a wave
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int i = 0; i < R; ++i) s[i] = s0[i];
 #pragma unroll
       for (int t = 0; t < kTC; ++t) {
-        if (t < lo + kHS && t < nt) {
+        if (t < lo + kHS) {
           float kk[R];
 #pragma unroll
           for (int i = 0; i < R; ++i) kk[i] = sk[t][rb * R + i];
@@ -415,15 +416,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       __syncthreads();
     };
+    // Every step runs, also over the tokens past nt in a sequence's last chunk: those are
+    // staged with k = q = v = do = beta = 0 and decay 1, so their steps leave the state and the
+    // gradient unchanged and their sums are never written; straight-line code keeps the
+    // recomputed states in place (no merges of the register history at every token).
     recompute(kTC - kHS);
 #pragma unroll
-    for (int t = kTC - 1; t >= kTH; --t)
-      if (t < nt) rev(t);
+    for (int t = kTC - 1; t >= kTH; --t) rev(t);
     flush(kTH);
     recompute(0);
 #pragma unroll
-    for (int t = kTH - 1; t >= 0; --t)
-      if (t < nt) rev(t);
+    for (int t = kTH - 1; t >= 0; --t) rev(t);
     flush(0);
     // dv
     {

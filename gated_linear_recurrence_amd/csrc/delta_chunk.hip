@@ -99,7 +99,8 @@ __device__ __forceinline__ uint16_t h16(u32x4 v, int e) {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_sum_step(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  // every control used here reads a valid lane, so no "old" value is needed (mov_dpp leaves it undefined)
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // A sequence's tokens [t0, t1) of the flattened [B * T] token axis and its chunks [c0, c1).

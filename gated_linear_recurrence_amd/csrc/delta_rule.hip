@@ -65,7 +65,8 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_sum_step(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  // every control used here reads a valid lane, so no "old" value is needed (mov_dpp leaves it undefined)
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over each group of LPC consecutive lanes (LPC = 8 or 16, groups aligned
