@@ -218,21 +218,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int64_t nch = (len + kTC - 1) / kTC;
   const int64_t ck0 = (int64_t)h * p.ck_slots + delta_ckpt_base(p.cu != nullptr, p.T, n, tok0);
-  for (int64_t c = nch - 1; c >= 0; --c) {
+
+  // A chunk's inputs are loaded into registers while the chunk after it is still being
+  // processed (after its last reverse step), then converted into LDS: at most one piece of k and
+  // q, one of v and do, NGK decays (KDA), beta and the decay (GDN) and the R checkpoint rows of
+  // the lane's column per thread. Entries past the chunk's end or the head's size load as zero:
+  // the staged k, q, v, do and beta are then zero and the decays exp(0) = 1.
+  constexpr int NGK = (kTC * DKP + kThreads - 1) / kThreads;
+  static_assert(kTC * KPT <= kThreads && kTC * VPT <= kThreads, "one staged piece per thread");
+  uint4 rk4, rq4, rv4, ro4;
+  float rgk[KDA ? NGK : 1], rbt, rgs, s0[R];
+  auto prefetch = [&](const int64_t c) {
     const int64_t t0 = tok0 + c * kTC;
     const int nt = (int)(len - c * kTC < kTC ? len - c * kTC : kTC);
-
-    // stage the chunk's inputs (zero past its end)
-    for (int idx = tid; idx < kTC * KPT; idx += kThreads) {
-      const int tt = idx / KPT, part = idx % KPT;
-      float fk[VW], fq[VW];
-#pragma unroll
-      for (int e = 0; e < VW; ++e) fk[e] = fq[e] = 0.f;
-      if (tt < nt && part * VW < p.Dk) {
+    rk4 = rq4 = rv4 = ro4 = make_uint4(0u, 0u, 0u, 0u);
+    {
+      const int tt = tid / KPT, part = tid % KPT;
+      if (tid < kTC * KPT && tt < nt && part * VW < p.Dk) {
         const int64_t e0 = ((t0 + tt) * p.Hk + kh) * p.Dk + part * VW;
-        IO::to_f32(*reinterpret_cast<const uint4*>(kb + e0 * IO::ES), fk);
-        IO::to_f32(*reinterpret_cast<const uint4*>(qb + e0 * IO::ES), fq);
+        rk4 = *reinterpret_cast<const uint4*>(kb + e0 * IO::ES);
+        rq4 = *reinterpret_cast<const uint4*>(qb + e0 * IO::ES);
       }
+    }
+    if constexpr (KDA) {
+#pragma unroll
+      for (int j = 0; j < NGK; ++j) {
+        const int idx = tid + j * kThreads;
+        const int tt = idx / DKP, d = idx % DKP;
+        rgk[j] = (idx < kTC * DKP && tt < nt && d < p.Dk) ? p.g[((t0 + tt) * p.Hv + h) * p.Dk + d] : 0.f;
+      }
+    }
+    {
+      const int tt = tid / VPT, part = tid % VPT;
+      const int c0 = cb * CW + part * VW;
+      if (tid < kTC * VPT && tt < nt && c0 < p.Dv) {
+        const int64_t e0 = ((t0 + tt) * p.Hv + h) * p.Dv + c0;
+        rv4 = *reinterpret_cast<const uint4*>(vb + e0 * IO::ES);
+        ro4 = *reinterpret_cast<const uint4*>(dob + e0 * IO::ES);
+      }
+    }
+    {
+      const bool ok = tid < nt;
+      const int64_t e0 = (t0 + tid) * p.Hv + h;
+      rbt = ok ? p.beta[e0] : 0.f;
+      rgs = (!KDA && ok) ? p.g[e0] : 0.f;
+    }
+    const float* ck = p.ckpt + (ck0 + c) * p.Dk * p.Dv;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int row = rb * R + i;
+      s0[i] = (col_ok && row < p.Dk) ? ck[(int64_t)row * p.Dv + col] : 0.f;
+    }
+  };
+  auto stage = [&]() {
+    if (tid < kTC * KPT) {
+      const int tt = tid / KPT, part = tid % KPT;
+      float fk[VW], fq[VW];
+      IO::to_f32(rk4, fk);
+      IO::to_f32(rq4, fq);
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
         sk[tt][part * VW + e] = fk[e];
@@ -240,22 +283,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     if constexpr (KDA) {
-      for (int idx = tid; idx < kTC * DKP; idx += kThreads) {
-        const int tt = idx / DKP, d = idx % DKP;
-        sg[tt][d] = (tt < nt && d < p.Dk) ? expf(p.g[((t0 + tt) * p.Hv + h) * p.Dk + d]) : 1.0f;
+#pragma unroll
+      for (int j = 0; j < NGK; ++j) {
+        const int idx = tid + j * kThreads;
+        if (idx < kTC * DKP) sg[idx / DKP][idx % DKP] = expf(rgk[j]);
       }
     }
-    for (int idx = tid; idx < kTC * VPT; idx += kThreads) {
-      const int tt = idx / VPT, part = idx % VPT;
-      const int c0 = cb * CW + part * VW;
+    if (tid < kTC * VPT) {
+      const int tt = tid / VPT, part = tid % VPT;
       float fv[VW], fo[VW];
-#pragma unroll
-      for (int e = 0; e < VW; ++e) fv[e] = fo[e] = 0.f;
-      if (tt < nt && c0 < p.Dv) {
-        const int64_t e0 = ((t0 + tt) * p.Hv + h) * p.Dv + c0;
-        IO::to_f32(*reinterpret_cast<const uint4*>(vb + e0 * IO::ES), fv);
-        IO::to_f32(*reinterpret_cast<const uint4*>(dob + e0 * IO::ES), fo);
-      }
+      IO::to_f32(rv4, fv);
+      IO::to_f32(ro4, fo);
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
         sv[tt][part * VW + e] = fv[e];
@@ -263,21 +301,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     if (tid < kTC) {
-      const bool ok = tid < nt;
-      const int64_t e0 = (t0 + tid) * p.Hv + h;
-      sb[tid] = ok ? p.beta[e0] : 0.f;
-      if constexpr (!KDA) sgs[tid] = ok ? expf(p.g[e0]) : 1.f;
+      sb[tid] = rbt;
+      if constexpr (!KDA) sgs[tid] = expf(rgs);
     }
-    // the state entering the chunk
-    float s0[R];
-    {
-      const float* ck = p.ckpt + (ck0 + c) * p.Dk * p.Dv;
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int row = rb * R + i;
-        s0[i] = (col_ok && row < p.Dk) ? ck[(int64_t)row * p.Dv + col] : 0.f;
-      }
-    }
+  };
+
+  // KDA's per-channel decays leave no registers for loads held across the flush: it loads
+  // each chunk's inputs at the top of that chunk's own iteration instead
+  constexpr bool kEarly = !KDA;
+  if (kEarly && nch > 0) prefetch(nch - 1);
+  for (int64_t c = nch - 1; c >= 0; --c) {
+    const int64_t t0 = tok0 + c * kTC;
+    const int nt = (int)(len - c * kTC < kTC ? len - c * kTC : kTC);
+    if (!kEarly) prefetch(c);
+    stage();
     __syncthreads();
 
     // decayed states S~, errors e and writes u of one half chunk, recomputed forward from the
@@ -427,6 +464,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     recompute(0);
 #pragma unroll
     for (int t = kTH - 1; t >= 0; --t) rev(t);
+    if (kEarly && c > 0) prefetch(c - 1);  // lands during the flush, the dv stores and the barrier
     flush(0);
     // dv
     {
