@@ -34,6 +34,7 @@ namespace delta {
 
 constexpr int kThreads = 256;
 constexpr int kTC = 16;  // tokens per staged chunk
+constexpr int kTCShort = 4;  // the same for calls of at most this many tokens per sequence
 
 struct DeltaArgs {
   const void* q;
@@ -113,29 +114,29 @@ struct Io {
   }
 };
 
-template <int LPC, int R, bool KDA, bool BF>
+template <int LPC, int R, bool KDA, bool BF, int TC>
 __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
   using IO = Io<BF>;
   constexpr int VW = IO::VW;
   constexpr int DKP = LPC * R;            // padded key dimension
   constexpr int CW = kThreads / LPC;      // columns per workgroup
   constexpr int KPT = DKP / VW;           // k granules per token
-  constexpr int KG = kTC * KPT;           // k (and q) granules per chunk
+  constexpr int KG = TC * KPT;           // k (and q) granules per chunk
   constexpr int NKG = (KG + kThreads - 1) / kThreads;
   constexpr int GPT = DKP / 4;            // KDA decay granules (float4) per token
-  constexpr int GG = KDA ? kTC * GPT : 0;
+  constexpr int GG = KDA ? TC * GPT : 0;
   constexpr int NGG = KDA ? (GG + kThreads - 1) / kThreads : 1;
   constexpr int VPT = CW / VW;            // v / o granules per token
-  constexpr int VG = kTC * VPT;
+  constexpr int VG = TC * VPT;
   static_assert(VG <= kThreads && DKP % VW == 0 && CW % VW == 0 && R % 4 == 0, "tiling");
 
-  __shared__ __align__(16) float sk[2][kTC][DKP];
-  __shared__ __align__(16) float sq[2][kTC][DKP];
-  __shared__ __align__(16) float sg[2][KDA ? kTC : 1][KDA ? DKP : 4];
-  __shared__ float sgs[2][kTC];
-  __shared__ float sb[2][kTC];
-  __shared__ __align__(16) float sv[2][kTC][CW];
-  __shared__ __align__(16) float so[2][kTC][CW];
+  __shared__ __align__(16) float sk[2][TC][DKP];
+  __shared__ __align__(16) float sq[2][TC][DKP];
+  __shared__ __align__(16) float sg[2][KDA ? TC : 1][KDA ? DKP : 4];
+  __shared__ float sgs[2][TC];
+  __shared__ float sb[2][TC];
+  __shared__ __align__(16) float sv[2][TC][CW];
+  __shared__ __align__(16) float so[2][TC][CW];
   __shared__ float sst[DKP][CW + 1];  // the key-first state slice, for coalesced loads and stores
   constexpr int GQ = CW / 4;          // 16-byte column groups of a state row
 
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
   float rbeta = 0.0f, rgs = 0.0f;
 
   auto load_chunk = [&](int64_t c) {
-    const int64_t t0 = c * kTC;
+    const int64_t t0 = c * TC;
 #pragma unroll
     for (int j = 0; j < NKG; ++j) {
       const int idx = tid + kThreads * j;
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
       if (tid < VG && c0 < p.Dv && t0 + tt < len)
         rv = *reinterpret_cast<const uint4*>(vb + (((tok0 + t0 + tt) * p.Hv + h) * p.Dv + c0) * IO::ES);
     }
-    if (tid < kTC) {
+    if (tid < TC) {
       const bool ok = t0 + tid < len;
       const int64_t e = (tok0 + t0 + tid) * p.Hv + h;
       rbeta = ok ? p.beta[e] : 0.0f;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
       for (int e = 0; e < VW; e += 4)
         *reinterpret_cast<float4*>(&sv[b][tt][part * VW + e]) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
     }
-    if (tid < kTC) {
+    if (tid < TC) {
       sb[b][tid] = rbeta;
       if constexpr (!KDA) sgs[b][tid] = expf(rgs);
     }
@@ -330,16 +331,16 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
   };
 
   auto compute = [&](int b, int nt) {
-    if (nt == kTC) {
+    if (nt == TC) {
 #pragma unroll
-      for (int t = 0; t < kTC; ++t) step(b, t);
+      for (int t = 0; t < TC; ++t) step(b, t);
     } else {
       for (int t = 0; t < nt; ++t) step(b, t);
     }
   };
 
   auto write_out = [&](int b, int64_t c) {
-    const int64_t t0 = c * kTC;
+    const int64_t t0 = c * TC;
     const int tt = tid / VPT, part = tid % VPT;
     const int c0 = cb * CW + part * VW;
     if (tid < VG && c0 < p.Dv && t0 + tt < len) {
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
     }
   };
 
-  const int64_t nch = (len + kTC - 1) / kTC;
+  const int64_t nch = (len + TC - 1) / TC;
   if (nch > 0) {
     load_chunk(0);
     store_chunk(0);
@@ -367,8 +368,8 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
           if (row < p.Dk) ck[(int64_t)row * p.Dv + col] = s[i];
         }
       }
-      const int64_t rem = len - c * kTC;
-      compute(b, rem < kTC ? (int)rem : kTC);
+      const int64_t rem = len - c * TC;
+      compute(b, rem < TC ? (int)rem : TC);
       if (c + 1 < nch) store_chunk(b ^ 1);
       if (c > 0) write_out(b ^ 1, c - 1);
       __syncthreads();
@@ -397,16 +398,23 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
   }
 }
 
-template <int LPC, int R, bool KDA, bool BF>
+template <int LPC, int R, bool KDA, bool BF, int TC>
 hipError_t launch(const DeltaArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((delta_fwd_kernel<LPC, R, KDA, BF>), dim3(a.n_blocks), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((delta_fwd_kernel<LPC, R, KDA, BF, TC>), dim3(a.n_blocks), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
+// Calls whose sequences are all at most kTCShort tokens long (decode steps) stage kTCShort
+// tokens instead of kTC: a quarter of the LDS, so more workgroups are resident. Each sequence is
+// then one chunk, whose checkpoint slot is the same under either chunk length.
 template <int LPC, int R>
 hipError_t launch_dt(const DeltaArgs& a, bool kda, bool bf, hipStream_t st) {
-  if (kda) return bf ? launch<LPC, R, true, true>(a, st) : launch<LPC, R, true, false>(a, st);
-  return bf ? launch<LPC, R, false, true>(a, st) : launch<LPC, R, false, false>(a, st);
+  if (a.T <= kTCShort) {
+    if (kda) return bf ? launch<LPC, R, true, true, kTCShort>(a, st) : launch<LPC, R, true, false, kTCShort>(a, st);
+    return bf ? launch<LPC, R, false, true, kTCShort>(a, st) : launch<LPC, R, false, false, kTCShort>(a, st);
+  }
+  if (kda) return bf ? launch<LPC, R, true, true, kTC>(a, st) : launch<LPC, R, true, false, kTC>(a, st);
+  return bf ? launch<LPC, R, false, true, kTC>(a, st) : launch<LPC, R, false, false, kTC>(a, st);
 }
 
 }  // namespace delta

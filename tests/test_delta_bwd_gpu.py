@@ -102,6 +102,8 @@ CASES = [
     (1, 50, 2, 4, 128, 136, "f32", True, False),
     (1, 33, 1, 1, 128, 128, "bf16", False, True),
     (3, 16, 1, 1, 8, 8, "f32", True, True),
+    (2, 3, 1, 2, 64, 40, "f32", True, True),        # the checkpoint of a short (4-token chunk) forward
+    (1, 4, 1, 1, 128, 128, "bf16", False, True),
 ]
 
 

@@ -4,7 +4,9 @@ Element by element against the float64 oracle on the same stored inputs, at
 sizes that span several 16-token chunks with a ragged tail and several
 column blocks with a partial last one, for each key-dimension tiling the
 library selects (Dk <= 64, <= 128, <= 256); packed sequences with empty and
-one-token members; zero-token calls; one decode step; the value-first state;
+one-token members; zero-token calls; one decode step; calls of at most 4
+tokens per sequence, which stage 4-token chunks (every tiling, packed, the
+value-first state); the value-first state;
 grouped key heads (bitwise against repeated heads); run-to-run determinism;
 and, at the full prefill workload (B=4, T=2048, 16 heads of 128 x 128),
 sampled (batch row, head) pairs.
@@ -100,6 +102,40 @@ def test_against_oracle(gpu_lib, case):
     wl = BASE.resized(wid=20, batch=B, length=T, k_heads=Hk, v_heads=Hv, k_dim=Dk, v_dim=Dv, io=io, kda=kda, h0=h0)
     inp = sd.make_delta_inputs(wl)
     _check(inp, _run(gpu_lib, inp), _ref(inp), str(case))
+
+
+SHORT_CASES = [
+    # calls of at most 4 tokens per sequence (decode-like) stage 4-token chunks
+    (3, 1, 1, 2, 64, 40, "bf16", True, True),
+    (2, 2, 2, 4, 128, 136, "bf16", False, True),
+    (2, 4, 1, 1, 128, 128, "f32", True, False),
+    (1, 3, 1, 2, 256, 64, "f32", False, True),
+    (1, 4, 1, 1, 200, 24, "bf16", True, True),
+    (2, 5, 1, 2, 128, 64, "bf16", False, True),     # one token past it: 16-token chunks again
+]
+
+
+@pytest.mark.parametrize("case", SHORT_CASES, ids=lambda c: "B{}T{}Hk{}Hv{}Dk{}Dv{}-{}-{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "kda" if c[7] else "gdn", "-h0" if c[8] else ""))
+def test_short_calls_against_oracle(gpu_lib, case):
+    B, T, Hk, Hv, Dk, Dv, io, kda, h0 = case
+    wl = BASE.resized(wid=27, batch=B, length=T, k_heads=Hk, v_heads=Hv, k_dim=Dk, v_dim=Dv, io=io, kda=kda, h0=h0)
+    inp = sd.make_delta_inputs(wl)
+    _check(inp, _run(gpu_lib, inp), _ref(inp), str(case))
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_short_packed_and_value_first(gpu_lib, kda):
+    lens = [1, 0, 2, 1]   # four tokens in all: the short chunks
+    wl = BASE.resized(wid=28, k_heads=1, v_heads=2, k_dim=128, v_dim=64, kda=kda, h0=True)
+    inp = sd.make_delta_inputs(wl, lengths=lens)
+    got = _run(gpu_lib, inp)
+    _check(inp, got, _ref(inp))
+    np.testing.assert_array_equal(got[1][1], inp.h0[1].astype(np.float64))
+    wl = BASE.resized(wid=29, batch=2, length=3, k_heads=1, v_heads=2, k_dim=64, v_dim=48, io="f32",
+                      kda=kda, h0=True)
+    inp = sd.make_delta_inputs(wl)
+    _check(inp, _run(gpu_lib, inp, v_first=True), _ref(inp))
 
 
 @pytest.mark.parametrize("kda", [False, True])
