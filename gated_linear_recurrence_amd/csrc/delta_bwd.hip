@@ -263,11 +263,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       rbt = ok ? p.beta[e0] : 0.f;
       rgs = (!KDA && ok) ? p.g[e0] : 0.f;
     }
-    const float* ck = p.ckpt + (ck0 + c) * p.Dk * p.Dv;
+    // column-major slot: the lane's R rows of its column are contiguous (16-byte loads; Dk is a
+    // multiple of 8, so a group of 4 rows is wholly inside it or wholly past it)
+    const float* ck = p.ckpt + (ck0 + c) * p.Dk * p.Dv + (int64_t)col * p.Dk;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int row = rb * R + i;
-      s0[i] = (col_ok && row < p.Dk) ? ck[(int64_t)row * p.Dv + col] : 0.f;
+    for (int i = 0; i < R; i += 4) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (col_ok && rb * R + i < p.Dk) x = *reinterpret_cast<const float4*>(ck + rb * R + i);
+      s0[i] = x.x;
+      s0[i + 1] = x.y;
+      s0[i + 2] = x.z;
+      s0[i + 3] = x.w;
     }
   };
   auto stage = [&]() {
@@ -632,7 +638,7 @@ extern "C" rglru_status_t rglru_delta_rule_bwd(const rglru_delta_shape_t* shape,
     return RGLRU_ERR_INVALID_ARGUMENT;
   if (!aligned_to(q, 16) || !aligned_to(k, 16) || !aligned_to(v, 16) || !aligned_to(d_o, 16) ||
       !aligned_to(dv, 16) || !aligned_to(dq, 4) || !aligned_to(dk, 4) || !aligned_to(g, 4) ||
-      !aligned_to(beta, 4) || !aligned_to(ckpt, 4) || !aligned_to(dh_last, 4) || !aligned_to(dg, 4) ||
+      !aligned_to(beta, 4) || !aligned_to(ckpt, 16) || !aligned_to(dh_last, 4) || !aligned_to(dg, 4) ||
       !aligned_to(dbeta, 4) || !aligned_to(dh0, 4) || !aligned_to(workspace, 256) || !aligned_to(cu_seqlens, 4))
     return RGLRU_ERR_MISALIGNED;
   if (pl.blocks == 0 || (pl.tokens == 0 && dh0 == nullptr)) return RGLRU_OK;

@@ -360,13 +360,15 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
       const int b = (int)(c & 1);
       if (c + 1 < nch) load_chunk(c + 1);
       if (p.ckpt != nullptr && col_ok) {
-        // the state entering chunk c, key-first [Dk][Dv] per slot
-        float* ck = p.ckpt + (((int64_t)h * p.ck_slots + delta_ckpt_base(p.cu != nullptr, p.T, n, tok0) + c) * p.Dk) * p.Dv;
+        // the state entering chunk c, column-major [Dv][Dk] per slot: a lane's R rows are
+        // contiguous, stored 16 bytes at a time (Dk is a multiple of 8, so a group of 4 rows is
+        // wholly inside it or wholly past it)
+        float* ck = p.ckpt + ((int64_t)h * p.ck_slots + delta_ckpt_base(p.cu != nullptr, p.T, n, tok0) + c) * p.Dk * p.Dv +
+                    (int64_t)col * p.Dk;
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const int row = rb * R + i;
-          if (row < p.Dk) ck[(int64_t)row * p.Dv + col] = s[i];
-        }
+        for (int i = 0; i < R; i += 4)
+          if (rb * R + i < p.Dk)
+            *reinterpret_cast<float4*>(ck + rb * R + i) = make_float4(s[i], s[i + 1], s[i + 2], s[i + 3]);
       }
       const int64_t rem = len - c * TC;
       compute(b, rem < TC ? (int)rem : TC);
@@ -464,7 +466,7 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   if (blocks >= (int64_t(1) << 31)) return RGLRU_ERR_INVALID_ARGUMENT;
   if (s.k_dim > 256 || s.k_dim % 8 != 0 || s.v_dim % 8 != 0) return RGLRU_ERR_UNSUPPORTED;
   if (!aligned_to(q, 16) || !aligned_to(k, 16) || !aligned_to(v, 16) || !aligned_to(o, 16) ||
-      !aligned_to(g, kda ? 16 : 4) || !aligned_to(beta, 4) || !aligned_to(h0, 16) || !aligned_to(h_last, 16) || !aligned_to(ckpt, 4) ||
+      !aligned_to(g, kda ? 16 : 4) || !aligned_to(beta, 4) || !aligned_to(h0, 16) || !aligned_to(h_last, 16) || !aligned_to(ckpt, 16) ||
       !aligned_to(cu_seqlens, 4))
     return RGLRU_ERR_MISALIGNED;
   if (blocks == 0 || (tokens == 0 && h_last == nullptr)) return RGLRU_OK;

@@ -66,8 +66,10 @@ typedef struct {
  *   h_last     : NULL or the final states, same layout and alignment as h0; a
  *                sequence with no tokens gets its initial state.
  *   ckpt       : NULL (inference) or rglru_delta_ckpt_elems(shape, n) float32
- *                (n = n_seqs with cu_seqlens, else 0): the state entering
- *                every 16-token chunk, which rglru_delta_rule_bwd needs.
+ *                (n = n_seqs with cu_seqlens, else 0), 16-byte aligned: the
+ *                state entering every 16-token chunk, which
+ *                rglru_delta_rule_bwd needs; each slot column-major (the Dk
+ *                values of a state column contiguous, whatever state_v_first).
  * q, k, v, g, beta and o may be NULL only when B * T = 0. Returns
  * RGLRU_ERR_INVALID_ARGUMENT, RGLRU_ERR_MISALIGNED or RGLRU_ERR_UNSUPPORTED
  * without launching anything, RGLRU_ERR_HIP if the launch fails. Outputs
@@ -89,7 +91,7 @@ size_t rglru_delta_ckpt_elems(const rglru_delta_shape_t* shape, int64_t n_seqs);
  * inputs; h0 is not needed again (the checkpoint holds it).
  *
  *   q, k, v, g, beta, cu_seqlens, n_seqs : as for the forward.
- *   ckpt       : the forward's checkpoint.
+ *   ckpt       : the forward's checkpoint (16-byte aligned).
  *   d_o        : [B, T, Hv, Dv] io, 16-byte aligned: the gradient of o.
  *   dh_last    : NULL (zero) or the gradient of the final state, layout of h0.
  *   dq, dk     : [B, T, Hk, Dk] io (summed over the value heads of each key head).
