@@ -312,14 +312,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // KDA's per-channel decays leave no registers for loads held across the flush: it loads
-  // each chunk's inputs at the top of that chunk's own iteration instead
-  constexpr bool kEarly = !KDA;
-  if (kEarly && nch > 0) prefetch(nch - 1);
+  if (nch > 0) prefetch(nch - 1);
   for (int64_t c = nch - 1; c >= 0; --c) {
     const int64_t t0 = tok0 + c * kTC;
     const int nt = (int)(len - c * kTC < kTC ? len - c * kTC : kTC);
-    if (!kEarly) prefetch(c);
     stage();
     __syncthreads();
 
@@ -470,7 +466,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     recompute(0);
 #pragma unroll
     for (int t = kTH - 1; t >= 0; --t) rev(t);
-    if (kEarly && c > 0) prefetch(c - 1);  // lands during the flush, the dv stores and the barrier
+    if (c > 0) prefetch(c - 1);  // lands during the flush, the dv stores and the barrier
     flush(0);
     // dv
     {
