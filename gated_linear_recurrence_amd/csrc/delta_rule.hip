@@ -406,17 +406,10 @@ hipError_t launch(const DeltaArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Calls whose sequences are all at most kTCShort tokens long (decode steps) stage kTCShort
-// tokens instead of kTC: a quarter of the LDS, so more workgroups are resident. Each sequence is
-// then one chunk, whose checkpoint slot is the same under either chunk length.
-template <int LPC, int R>
+template <int LPC, int R, int TC>
 hipError_t launch_dt(const DeltaArgs& a, bool kda, bool bf, hipStream_t st) {
-  if (a.T <= kTCShort) {
-    if (kda) return bf ? launch<LPC, R, true, true, kTCShort>(a, st) : launch<LPC, R, true, false, kTCShort>(a, st);
-    return bf ? launch<LPC, R, false, true, kTCShort>(a, st) : launch<LPC, R, false, false, kTCShort>(a, st);
-  }
-  if (kda) return bf ? launch<LPC, R, true, true, kTC>(a, st) : launch<LPC, R, true, false, kTC>(a, st);
-  return bf ? launch<LPC, R, false, true, kTC>(a, st) : launch<LPC, R, false, false, kTC>(a, st);
+  if (kda) return bf ? launch<LPC, R, true, true, TC>(a, st) : launch<LPC, R, true, false, TC>(a, st);
+  return bf ? launch<LPC, R, false, true, TC>(a, st) : launch<LPC, R, false, false, TC>(a, st);
 }
 
 }  // namespace delta
@@ -459,7 +452,8 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   if (tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
                      o == nullptr))
     return RGLRU_ERR_INVALID_ARGUMENT;
-  const int LPC = s.k_dim <= 64 ? 8 : 16;
+  const bool short_call = s.length <= delta::kTCShort;
+  const int LPC = (s.k_dim <= 64 || (s.k_dim <= 128 && short_call)) ? 8 : 16;
   const int cw = delta::kThreads / LPC;
   const int64_t n_cb = ceil_div(s.v_dim, cw);
   const int64_t blocks = N * s.v_heads * n_cb;
@@ -496,11 +490,23 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = s.io_dtype == RGLRU_IO_BF16;
   hipError_t e;
-  if (s.k_dim <= 64)
-    e = delta::launch_dt<8, 8>(a, kda, bf, st);
-  else if (s.k_dim <= 128)
-    e = delta::launch_dt<16, 8>(a, kda, bf, st);
-  else
-    e = delta::launch_dt<16, 16>(a, kda, bf, st);
+  if (short_call) {
+    // sequences of at most kTCShort tokens (decode steps): kTCShort-token staging, a quarter of
+    // the LDS, so more workgroups are resident, and for Dk <= 128 columns on 8 lanes of 16 rows,
+    // so each workgroup moves twice the state per memory round trip. Each sequence is then one
+    // chunk, whose checkpoint slot is the same under either chunk length.
+    if (s.k_dim <= 64)
+      e = delta::launch_dt<8, 8, delta::kTCShort>(a, kda, bf, st);
+    else if (s.k_dim <= 128)
+      e = delta::launch_dt<8, 16, delta::kTCShort>(a, kda, bf, st);
+    else
+      e = delta::launch_dt<16, 16, delta::kTCShort>(a, kda, bf, st);
+  } else if (s.k_dim <= 64) {
+    e = delta::launch_dt<8, 8, delta::kTC>(a, kda, bf, st);
+  } else if (s.k_dim <= 128) {
+    e = delta::launch_dt<16, 8, delta::kTC>(a, kda, bf, st);
+  } else {
+    e = delta::launch_dt<16, 16, delta::kTC>(a, kda, bf, st);
+  }
   return e == hipSuccess ? RGLRU_OK : RGLRU_ERR_HIP;
 }
