@@ -412,6 +412,28 @@ hipError_t launch_dt(const DeltaArgs& a, bool kda, bool bf, hipStream_t st) {
   return bf ? launch<LPC, R, false, true, TC>(a, st) : launch<LPC, R, false, false, TC>(a, st);
 }
 
+// The tiling of a call: lanes per state column (which sets the columns per workgroup and so the
+// grid) and the launcher of the matching instantiation, chosen in one place.
+struct Tiling {
+  int lpc;
+  hipError_t (*launch)(const DeltaArgs&, bool, bool, hipStream_t);
+};
+
+// Sequences of at most kTCShort tokens (decode steps) stage kTCShort tokens: a quarter of the
+// LDS, so more workgroups are resident; for Dk <= 128 their columns also sit on 8 lanes of 16
+// rows, so each workgroup moves twice the state per memory round trip. Each sequence is then one
+// chunk, whose checkpoint slot is the same under either chunk length.
+inline Tiling pick_tiling(int64_t k_dim, bool short_call) {
+  if (short_call) {
+    if (k_dim <= 64) return {8, launch_dt<8, 8, kTCShort>};
+    if (k_dim <= 128) return {8, launch_dt<8, 16, kTCShort>};
+    return {16, launch_dt<16, 16, kTCShort>};
+  }
+  if (k_dim <= 64) return {8, launch_dt<8, 8, kTC>};
+  if (k_dim <= 128) return {16, launch_dt<16, 8, kTC>};
+  return {16, launch_dt<16, 16, kTC>};
+}
+
 }  // namespace delta
 }  // namespace rglru
 
@@ -452,9 +474,8 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   if (tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr ||
                      o == nullptr))
     return RGLRU_ERR_INVALID_ARGUMENT;
-  const bool short_call = s.length <= delta::kTCShort;
-  const int LPC = (s.k_dim <= 64 || (s.k_dim <= 128 && short_call)) ? 8 : 16;
-  const int cw = delta::kThreads / LPC;
+  const delta::Tiling tl = delta::pick_tiling(s.k_dim, s.length <= delta::kTCShort);
+  const int cw = delta::kThreads / tl.lpc;
   const int64_t n_cb = ceil_div(s.v_dim, cw);
   const int64_t blocks = N * s.v_heads * n_cb;
   if (blocks >= (int64_t(1) << 31)) return RGLRU_ERR_INVALID_ARGUMENT;
@@ -489,24 +510,6 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   a.ck_slots = cu_seqlens != nullptr ? (s.length + 15) / 16 + n_seqs : s.batch * ((s.length + 15) / 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = s.io_dtype == RGLRU_IO_BF16;
-  hipError_t e;
-  if (short_call) {
-    // sequences of at most kTCShort tokens (decode steps): kTCShort-token staging, a quarter of
-    // the LDS, so more workgroups are resident, and for Dk <= 128 columns on 8 lanes of 16 rows,
-    // so each workgroup moves twice the state per memory round trip. Each sequence is then one
-    // chunk, whose checkpoint slot is the same under either chunk length.
-    if (s.k_dim <= 64)
-      e = delta::launch_dt<8, 8, delta::kTCShort>(a, kda, bf, st);
-    else if (s.k_dim <= 128)
-      e = delta::launch_dt<8, 16, delta::kTCShort>(a, kda, bf, st);
-    else
-      e = delta::launch_dt<16, 16, delta::kTCShort>(a, kda, bf, st);
-  } else if (s.k_dim <= 64) {
-    e = delta::launch_dt<8, 8, delta::kTC>(a, kda, bf, st);
-  } else if (s.k_dim <= 128) {
-    e = delta::launch_dt<16, 8, delta::kTC>(a, kda, bf, st);
-  } else {
-    e = delta::launch_dt<16, 16, delta::kTC>(a, kda, bf, st);
-  }
+  const hipError_t e = tl.launch(a, kda, bf, st);
   return e == hipSuccess ? RGLRU_OK : RGLRU_ERR_HIP;
 }
