@@ -13,16 +13,19 @@
 // Like the forward, a column of the [Dk, Dv] state (and of G) lives in LPC
 // lanes, R rows each, and the columns are independent, so each workgroup
 // walks its 512 / LPC columns of one head through the tokens in reverse,
-// 16-token chunk by chunk: it reloads the state entering the chunk from the
-// forward's checkpoint, recomputes the chunk's decayed states S~ forward
-// (keeping those of one half chunk in registers, so each half's are
-// recomputed from the checkpoint), then runs the reverse steps. dv and the initial
-// state's gradient belong to single columns; dq, dk, dbeta and dg sum over
-// all columns of a head, so the workgroup sums its columns in a fixed order
-// (DPP adds inside a wave, then the waves' LDS slots in wave order)
-// and writes per-column-block partials, which delta_bwd_reduce adds over the
-// column blocks and the value heads of a key head, again in a fixed order:
-// results are bitwise reproducible.
+// 16-token chunk by chunk: it takes the state entering the chunk from the
+// forward's checkpoint (column-major slots, so a lane's rows are contiguous),
+// recomputes the chunk's decayed states S~ forward (keeping those of one half
+// chunk in registers, so each half's are recomputed from the checkpoint),
+// then runs the reverse steps; the next chunk's inputs are loaded into
+// registers after the last reverse step, so they arrive while this chunk's
+// sums are flushed. dv and the initial state's gradient belong to single
+// columns; dq, dk, dbeta and dg sum over all columns of a head, so the
+// workgroup sums its columns in a fixed order (DPP adds and permlane swaps
+// inside a wave, then the waves' LDS slots in wave order) and writes
+// per-column-block partials, which delta_bwd_reduce_qk and
+// delta_bwd_reduce_gb add over the column blocks and the value heads of a
+// key head, again in a fixed order: results are bitwise reproducible.
 
 #include <hip/hip_runtime.h>
 #include <cmath>

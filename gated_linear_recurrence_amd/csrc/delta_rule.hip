@@ -18,10 +18,14 @@
 //
 // Per token every lane needs its R rows of k, q (and of the KDA decays), the
 // token's beta and decay, and its column of v. The workgroup stages them for
-// kTC tokens at a time in LDS as float32 (decays already exponentiated),
+// TC tokens at a time in LDS as float32 (decays already exponentiated),
 // double-buffered: the global loads of the next chunk are issued before the
 // current chunk's recurrence and written to LDS after it, with one barrier
-// per chunk. Outputs go through LDS too and leave as 16-byte stores.
+// per chunk. Outputs go through LDS too and leave as 16-byte stores. TC is
+// 16, or 4 for calls whose sequences are all that short (decode steps),
+// where the smaller LDS lets more workgroups be resident. In training mode
+// the state entering every 16-token chunk is stored to the checkpoint, each
+// slot column-major so a lane's R rows leave as 16-byte pieces.
 
 #include <hip/hip_runtime.h>
 #include <cmath>
