@@ -1,8 +1,9 @@
 """Gated delta rule entry points captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
 
-A decode step (the forward of one token per sequence from a nonzero state)
-and a training step (the forward writing its checkpoint, then the backward)
-are captured once and replayed several times. Between replays an eager call
+A decode step (the forward of one token per sequence from a nonzero state),
+a training step (the forward writing its checkpoint, then the backward) and
+the GDN chunk form on packed sequences are captured once and replayed
+several times. Between replays an eager call
 on other inputs overwrites the same outputs, checkpoint and workspace, so a
 replay only matches if the captured kernels rewrite everything they read.
 Every replay must equal the eager results bitwise; the kernels clear no
@@ -115,4 +116,33 @@ def test_training_step_graph_replay(gpu_lib, kda):
     torch.cuda.synchronize()
     names = ["o", "final_state", "dq", "dk", "dv", "dg", "dbeta", "dh0"]
     ref = {n: t.clone() for n, t in zip(names, (o, fs, *grads))}
+    _replays_match(step, live, other, ref)
+
+
+def test_chunk_form_graph_replay(gpu_lib):
+    """The GDN chunk form on packed sequences (its chunk map is rebuilt on the device each call)."""
+    glr = gpu_lib
+    lens = [70, 0, 1, 130, 64]
+    wl = sd.DELTA_WORKLOADS[10].resized(wid=52, k_heads=1, v_heads=2, k_dim=128, v_dim=64, h0=True)
+
+    def inputs(variant):
+        inp = sd.make_delta_inputs(wl, variant=variant, lengths=lens)
+        return {"q": _dev(inp.q), "k": _dev(inp.k), "v": _dev(inp.v), "g": _f32(inp.g), "beta": _f32(inp.beta),
+                "h0": _f32(inp.h0), "cu": torch.from_numpy(inp.cu).cuda()}
+
+    live, other = inputs(5), inputs(6)
+    o = torch.empty_like(live["v"])
+    fs = torch.empty_like(live["h0"])
+    shape = glr.ops._delta_common(live["q"], live["k"], live["v"], live["g"], live["beta"], None, live["h0"],
+                                  live["cu"], False, True, o, fs)[0]
+    ws = torch.empty(glr.rglru_delta_chunk_workspace_bytes(shape, len(lens)), dtype=torch.uint8, device="cuda")
+
+    def step(d):
+        glr.rglru_delta_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
+                                  cu_seqlens=d["cu"], o=o, final_state=fs, workspace=ws)
+        return o, fs
+
+    step(live)
+    torch.cuda.synchronize()
+    ref = {"o": o.clone(), "final_state": fs.clone()}
     _replays_match(step, live, other, ref)
