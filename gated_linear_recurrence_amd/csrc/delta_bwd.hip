@@ -495,29 +495,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // dq, dk [tokens][Hk][Dk] (io dtype): the partials of every column block and every value head
-// of the key head, in order.
+// of the key head, in order. A thread takes 4 consecutive key channels (Dk is a multiple of 8,
+// so they share a row and their partials are 16-byte aligned).
 template <bool BF>
 __global__ __launch_bounds__(256) void delta_bwd_reduce_qk(BwdArgs p) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = p.tokens * p.Hk * p.Dk;
-  if (i >= total) return;
-  const int d = (int)(i % p.Dk);
-  const int64_t r = i / p.Dk;
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nd4 = p.Dk / 4;
+  const int64_t total = p.tokens * p.Hk * nd4;
+  if (i4 >= total) return;
+  const int d = (int)(i4 % nd4) * 4;
+  const int64_t r = i4 / nd4;
   const int kh = (int)(r % p.Hk);
   const int64_t tok = r / p.Hk;
-  float aq = 0.f, ak = 0.f;
+  float4 aq = make_float4(0.f, 0.f, 0.f, 0.f), ak = aq;
   for (int hh = kh * p.grp; hh < (kh + 1) * p.grp; ++hh)
     for (int c = 0; c < p.n_cb; ++c) {
       const int64_t e0 = (((int64_t)c * p.tokens + tok) * p.Hv + hh) * p.Dk + d;
-      aq += p.pdq[e0];
-      ak += p.pdk[e0];
+      const float4 x = *reinterpret_cast<const float4*>(p.pdq + e0);
+      const float4 y = *reinterpret_cast<const float4*>(p.pdk + e0);
+      aq.x += x.x; aq.y += x.y; aq.z += x.z; aq.w += x.w;
+      ak.x += y.x; ak.y += y.y; ak.z += y.z; ak.w += y.w;
     }
+  const int64_t o = r * p.Dk + d;
   if constexpr (BF) {
-    static_cast<uint16_t*>(p.dq)[i] = f32_to_bf16(aq);
-    static_cast<uint16_t*>(p.dk)[i] = f32_to_bf16(ak);
+    // pairs of bf16 as 4-byte stores (dq and dk need only 4-byte alignment)
+    uint32_t* dq = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.dq) + o);
+    uint32_t* dk = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.dk) + o);
+    dq[0] = f32x2_to_bf16x2(aq.x, aq.y);
+    dq[1] = f32x2_to_bf16x2(aq.z, aq.w);
+    dk[0] = f32x2_to_bf16x2(ak.x, ak.y);
+    dk[1] = f32x2_to_bf16x2(ak.z, ak.w);
   } else {
-    static_cast<float*>(p.dq)[i] = aq;
-    static_cast<float*>(p.dk)[i] = ak;
+    float* dq = static_cast<float*>(p.dq) + o;
+    float* dk = static_cast<float*>(p.dk) + o;
+    dq[0] = aq.x; dq[1] = aq.y; dq[2] = aq.z; dq[3] = aq.w;
+    dk[0] = ak.x; dk[1] = ak.y; dk[2] = ak.z; dk[3] = ak.w;
   }
 }
 
@@ -543,7 +555,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((delta_bwd_kernel<LPC, R, KDA, BF>), dim3(a.n_blocks), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nqk = a.tokens * a.Hk * a.Dk;
+  const int64_t nqk = a.tokens * a.Hk * (a.Dk / 4);
   if (nqk > 0) {
     hipLaunchKernelGGL((delta_bwd_reduce_qk<BF>), dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, st, a);
     e = hipGetLastError();
