@@ -298,6 +298,31 @@ def test_backward_without_writes_is_closed_form():
     np.testing.assert_array_equal(dq, 0.0)   # zero state and no writes: o = 0 for any q
 
 
+@pytest.mark.parametrize("kda", [False, True])
+def test_backward_of_one_write_from_zero_is_closed_form(kda):
+    """One token from a zero state: S = beta k v^T and o = scale beta (k.q) v, so with
+    L = dh_last and G = scale q do^T + L (derived by hand):
+      dq = scale beta (v.do) k,  dk = scale beta (v.do) q + beta L v,
+      dv = scale beta (k.q) do + beta L^T k,  dbeta = scale (k.q)(v.do) + k^T L v,
+      dg = 0 (the decay only scales the zero state),  dh0 = D (I - beta k k^T) G."""
+    rng = np.random.default_rng(32)
+    Dk, Dv, sc = 4, 3, 0.7
+    q, k, v, g, beta = _rand(rng, 1, 1, 1, 1, Dk, Dv, kda=kda)
+    do = rng.standard_normal((1, 1, 1, Dv))
+    L = rng.standard_normal((1, 1, Dk, Dv))
+    dq, dk, dv, dg, db, dh0 = recurrent_delta_rule_backward(q, k, v, g, beta, do, L, scale=sc)
+    qv, kv, vv, dov, Lm, b = q[0, 0, 0], k[0, 0, 0], v[0, 0, 0], do[0, 0, 0], L[0, 0], beta[0, 0, 0]
+    kq, vdo = kv @ qv, vv @ dov
+    np.testing.assert_allclose(dq[0, 0, 0], sc * b * vdo * kv, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0, 0], sc * b * vdo * qv + b * (Lm @ vv), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dv[0, 0, 0], sc * b * kq * dov + b * (Lm.T @ kv), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(db[0, 0, 0], sc * kq * vdo + kv @ Lm @ vv, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dg, 0.0, atol=1e-15)
+    D = np.diag(np.exp(g[0, 0, 0])) if kda else np.exp(g[0, 0, 0]) * np.eye(Dk)
+    G = sc * np.outer(qv, dov) + Lm
+    np.testing.assert_allclose(dh0[0, 0], D @ (np.eye(Dk) - b * np.outer(kv, kv)) @ G, rtol=1e-12, atol=1e-14)
+
+
 def test_backward_is_linear_in_the_output_gradients():
     rng = np.random.default_rng(31)
     q, k, v, g, beta = _rand(rng, 1, 6, 1, 2, 4, 3, kda=True)
