@@ -43,12 +43,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(f32x2_to_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
-// Gated delta rule checkpoints (the state entering every 16-token chunk), per value head: the
-// first slot of sequence n is n ceil(T / 16) for B rows of T tokens, else floor(start / 16) + n
-// for packed sequences (each adds at most one partial chunk, so for ordered offsets the
-// sequences' slots do not overlap, and clamped offsets stay below ceil(T / 16) + N).
+// Gated delta rule checkpoints: the state entering every 8th token of each sequence, per value
+// head. The first slot of sequence n is n ceil(T / 8) for B rows of T tokens, else
+// floor(start / 8) + n for packed sequences (each adds at most one partial interval, so for
+// ordered offsets the sequences' slots do not overlap, and clamped offsets stay below
+// ceil(T / 8) + N).
+constexpr int kDeltaCkpt = 8;
 __host__ __device__ __forceinline__ int64_t delta_ckpt_base(bool packed, int64_t T, int n, int64_t start) {
-  return packed ? start / 16 + n : (int64_t)n * ((T + 15) / 16);
+  return packed ? start / kDeltaCkpt + n : (int64_t)n * ((T + kDeltaCkpt - 1) / kDeltaCkpt);
+}
+__host__ __device__ __forceinline__ int64_t delta_ckpt_slots(bool packed, int64_t T, int64_t B, int64_t n_seqs) {
+  return packed ? (T + kDeltaCkpt - 1) / kDeltaCkpt + n_seqs : B * ((T + kDeltaCkpt - 1) / kDeltaCkpt);
 }
 
 }  // namespace rglru

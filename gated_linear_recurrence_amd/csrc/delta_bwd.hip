@@ -13,10 +13,10 @@
 // Like the forward, a column of the [Dk, Dv] state (and of G) lives in LPC
 // lanes, R rows each, and the columns are independent, so each workgroup
 // walks its 512 / LPC columns of one head through the tokens in reverse,
-// 16-token chunk by chunk: it takes the state entering the chunk from the
+// 16-token chunk by chunk: it takes the states entering the chunk and its 9th token from the
 // forward's checkpoint (column-major slots, so a lane's rows are contiguous),
-// recomputes the chunk's decayed states S~ forward (keeping those of one half
-// chunk in registers, so each half's are recomputed from the checkpoint),
+// recomputes the chunk's decayed states S~ forward one half chunk at a time,
+// each from its own checkpoint (the forward stores one every 8 tokens),
 // then runs the reverse steps; the next chunk's inputs are loaded into
 // registers after the last reverse step, so they arrive while this chunk's
 // sums are flushed. dv and the initial state's gradient belong to single
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int NGK = (kTC * DKP + kThreads - 1) / kThreads;
   static_assert(kTC * KPT <= kThreads && kTC * VPT <= kThreads, "one staged piece per thread");
   uint4 rk4, rq4, rv4, ro4;
-  float rgk[KDA ? NGK : 1], rbt, rgs, s0[R];
+  float rgk[KDA ? NGK : 1], rbt, rgs, s0[R], s1[R];
   auto prefetch = [&](const int64_t c) {
     const int64_t t0 = tok0 + c * kTC;
     const int nt = (int)(len - c * kTC < kTC ? len - c * kTC : kTC);
@@ -266,17 +266,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       rbt = ok ? p.beta[e0] : 0.f;
       rgs = (!KDA && ok) ? p.g[e0] : 0.f;
     }
-    // column-major slot: the lane's R rows of its column are contiguous (16-byte loads; Dk is a
-    // multiple of 8, so a group of 4 rows is wholly inside it or wholly past it)
-    const float* ck = p.ckpt + (ck0 + c) * p.Dk * p.Dv + (int64_t)col * p.Dk;
+    // the states entering the chunk and its 9th token (checkpoint slots 2c and 2c + 1; the second
+    // exists when the chunk has more than 8 tokens, else the second half is all padding and starts
+    // from zero). Column-major slots: the lane's R rows of its column are contiguous (16-byte
+    // loads; Dk is a multiple of 8, so a group of 4 rows is wholly inside it or wholly past it).
+    static_assert(kTH == kDeltaCkpt, "one checkpoint per half chunk");
+    const float* ck = p.ckpt + (ck0 + 2 * c) * p.Dk * p.Dv + (int64_t)col * p.Dk;
+    const bool mid = nt > kTH;
 #pragma unroll
     for (int i = 0; i < R; i += 4) {
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (col_ok && rb * R + i < p.Dk) x = *reinterpret_cast<const float4*>(ck + rb * R + i);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+      if (col_ok && rb * R + i < p.Dk) {
+        x = *reinterpret_cast<const float4*>(ck + rb * R + i);
+        if (mid) y = *reinterpret_cast<const float4*>(ck + (int64_t)p.Dk * p.Dv + rb * R + i);
+      }
       s0[i] = x.x;
       s0[i + 1] = x.y;
       s0[i + 2] = x.z;
       s0[i + 3] = x.w;
+      s1[i] = y.x;
+      s1[i + 1] = y.y;
+      s1[i + 2] = y.z;
+      s1[i + 3] = y.w;
     }
   };
   auto stage = [&]() {
@@ -322,18 +333,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     stage();
     __syncthreads();
 
-    // decayed states S~, errors e and writes u of one half chunk, recomputed forward from the
-    // chunk's checkpoint (the steps before the half are run again and not kept): holding half
-    // a chunk is what lets two waves share a SIMD's registers
+    // decayed states S~, errors e and writes u of one half chunk, recomputed forward from that
+    // half's checkpoint: holding half a chunk is what lets two waves share a SIMD's registers
     constexpr int kHS = kTH;
     float hs[kHS][R], he[kHS], hu[kHS];
     auto recompute = [&](const int lo) {
       float s[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) s[i] = s0[i];
+      for (int i = 0; i < R; ++i) s[i] = lo == 0 ? s0[i] : s1[i];
 #pragma unroll
       for (int t = 0; t < kTC; ++t) {
-        if (t < lo + kHS) {
+        if (t >= lo && t < lo + kHS) {
           float kk[R];
 #pragma unroll
           for (int i = 0; i < R; ++i) kk[i] = sk[t][rb * R + i];
@@ -347,12 +357,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           }
           const float e = sv[t][cl] - row_sum<CPW>(a0 + a1);
           const float u = sb[t] * e;
-          if (t >= lo) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) hs[t - lo][i] = s[i];
-            he[t - lo] = e;
-            hu[t - lo] = u;
-          }
+          for (int i = 0; i < R; ++i) hs[t - lo][i] = s[i];
+          he[t - lo] = e;
+          hu[t - lo] = u;
 #pragma unroll
           for (int i = 0; i < R; ++i) s[i] = fmaf(u, kk[i], s[i]);
         }
@@ -611,7 +619,7 @@ rglru_status_t plan(const rglru_delta_shape_t* sp, const int32_t* cu, int64_t n_
   pl->n_cb = n_cb;
   pl->blocks = blocks;
   pl->tokens = tokens;
-  pl->ck_slots = cu != nullptr ? (s.length + 15) / 16 + n_seqs : s.batch * ((s.length + 15) / 16);
+  pl->ck_slots = delta_ckpt_slots(cu != nullptr, s.length, s.batch, n_seqs);
   pl->pdq_off = 0;
   pl->pdk_off = round_up(nqk * 4, 256);
   pl->pdg_off = pl->pdk_off + round_up(nqk * 4, 256);

@@ -24,7 +24,7 @@
 // per chunk. Outputs go through LDS too and leave as 16-byte stores. TC is
 // 16, or 4 for calls whose sequences are all that short (decode steps),
 // where the smaller LDS lets more workgroups be resident. In training mode
-// the state entering every 16-token chunk is stored to the checkpoint, each
+// the state entering every 8th token is stored to the checkpoint, each
 // slot column-major so a lane's R rows leave as 16-byte pieces.
 
 #include <hip/hip_runtime.h>
@@ -56,7 +56,7 @@ struct DeltaArgs {
   int n_blocks;  // workgroups in the grid
   int v_first;
   float scale;
-  float* ckpt;        // NULL, or the state entering every 16-token chunk (for the backward)
+  float* ckpt;        // NULL, or the state entering every 8th token (for the backward)
   int64_t ck_slots;   // checkpoint slots per value head
 };
 
@@ -334,12 +334,33 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
     if (rb == 0) so[b][t][cl] = p.scale * ov;
   };
 
-  auto compute = [&](int b, int nt) {
+  // the state entering the sequence's token 8 j into checkpoint slot j, column-major [Dv][Dk]: a
+  // lane's R rows are contiguous, stored 16 bytes at a time (Dk is a multiple of 8, so a group of
+  // 4 rows is wholly inside it or wholly past it)
+  const int64_t ck_first = (int64_t)h * p.ck_slots + delta_ckpt_base(p.cu != nullptr, p.T, n, tok0);
+  auto store_ckpt = [&](int64_t j) {
+    if (!col_ok) return;
+    float* ck = p.ckpt + (ck_first + j) * p.Dk * p.Dv + (int64_t)col * p.Dk;
+#pragma unroll
+    for (int i = 0; i < R; i += 4)
+      if (rb * R + i < p.Dk)
+        *reinterpret_cast<float4*>(ck + rb * R + i) = make_float4(s[i], s[i + 1], s[i + 2], s[i + 3]);
+  };
+  // chunk c's tokens; in training mode also the state after each of its 8-token intervals but the
+  // last (the one entering the chunk is stored before)
+  auto compute = [&](int b, int nt, int64_t c) {
+    const bool ck = p.ckpt != nullptr;
     if (nt == TC) {
 #pragma unroll
-      for (int t = 0; t < TC; ++t) step(b, t);
+      for (int t = 0; t < TC; ++t) {
+        step(b, t);
+        if ((t + 1) % kDeltaCkpt == 0 && t + 1 < TC && ck) store_ckpt((c * TC + t + 1) / kDeltaCkpt);
+      }
     } else {
-      for (int t = 0; t < nt; ++t) step(b, t);
+      for (int t = 0; t < nt; ++t) {
+        step(b, t);
+        if ((t + 1) % kDeltaCkpt == 0 && t + 1 < nt && ck) store_ckpt((c * TC + t + 1) / kDeltaCkpt);
+      }
     }
   };
 
@@ -363,19 +384,9 @@ __global__ __launch_bounds__(kThreads) void delta_fwd_kernel(DeltaArgs p) {
     for (int64_t c = 0; c < nch; ++c) {
       const int b = (int)(c & 1);
       if (c + 1 < nch) load_chunk(c + 1);
-      if (p.ckpt != nullptr && col_ok) {
-        // the state entering chunk c, column-major [Dv][Dk] per slot: a lane's R rows are
-        // contiguous, stored 16 bytes at a time (Dk is a multiple of 8, so a group of 4 rows is
-        // wholly inside it or wholly past it)
-        float* ck = p.ckpt + ((int64_t)h * p.ck_slots + delta_ckpt_base(p.cu != nullptr, p.T, n, tok0) + c) * p.Dk * p.Dv +
-                    (int64_t)col * p.Dk;
-#pragma unroll
-        for (int i = 0; i < R; i += 4)
-          if (rb * R + i < p.Dk)
-            *reinterpret_cast<float4*>(ck + rb * R + i) = make_float4(s[i], s[i + 1], s[i + 2], s[i + 3]);
-      }
+      if (p.ckpt != nullptr) store_ckpt(c * TC / kDeltaCkpt);
       const int64_t rem = len - c * TC;
-      compute(b, rem < TC ? (int)rem : TC);
+      compute(b, rem < TC ? (int)rem : TC, c);
       if (c + 1 < nch) store_chunk(b ^ 1);
       if (c > 0) write_out(b ^ 1, c - 1);
       __syncthreads();
@@ -448,7 +459,7 @@ extern "C" size_t rglru_delta_ckpt_elems(const rglru_delta_shape_t* sp, int64_t 
       sp->length > (int64_t(1) << 40) || sp->v_heads < 1 || sp->k_dim < 1 || sp->v_dim < 1 || n_seqs < 0 ||
       (n_seqs > 0 && sp->batch != 1))
     return 0;
-  const int64_t slots = n_seqs > 0 ? (sp->length + 15) / 16 + n_seqs : sp->batch * ((sp->length + 15) / 16);
+  const int64_t slots = delta_ckpt_slots(n_seqs > 0, sp->length, sp->batch, n_seqs);
   return (size_t)slots * sp->v_heads * sp->k_dim * sp->v_dim;
 }
 
@@ -511,7 +522,7 @@ extern "C" rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* sp, co
   a.v_first = s.state_v_first;
   a.scale = s.scale;
   a.ckpt = ckpt;
-  a.ck_slots = cu_seqlens != nullptr ? (s.length + 15) / 16 + n_seqs : s.batch * ((s.length + 15) / 16);
+  a.ck_slots = delta_ckpt_slots(cu_seqlens != nullptr, s.length, s.batch, n_seqs);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = s.io_dtype == RGLRU_IO_BF16;
   const hipError_t e = tl.launch(a, kda, bf, st);

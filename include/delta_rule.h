@@ -67,7 +67,7 @@ typedef struct {
  *                sequence with no tokens gets its initial state.
  *   ckpt       : NULL (inference) or rglru_delta_ckpt_elems(shape, n) float32
  *                (n = n_seqs with cu_seqlens, else 0), 16-byte aligned: the
- *                state entering every 16-token chunk, which
+ *                state entering every 8th token of each sequence, which
  *                rglru_delta_rule_bwd needs; each slot column-major (the Dk
  *                values of a state column contiguous, whatever state_v_first).
  * q, k, v, g, beta and o may be NULL only when B * T = 0. Returns
@@ -79,8 +79,8 @@ rglru_status_t rglru_delta_rule_fwd(const rglru_delta_shape_t* shape, const int3
                                     const float* g, const float* beta, const float* h0, void* o,
                                     float* h_last, float* ckpt, void* stream);
 
-/* Float32 elements of the forward's checkpoint: per value head, ceil(T / 16)
- * slots per batch row (B rows), or ceil(T / 16) + n_seqs slots for packed
+/* Float32 elements of the forward's checkpoint: per value head, ceil(T / 8)
+ * slots per batch row (B rows), or ceil(T / 8) + n_seqs slots for packed
  * sequences, of Dk * Dv each. 0 for an invalid shape. */
 size_t rglru_delta_ckpt_elems(const rglru_delta_shape_t* shape, int64_t n_seqs);
 

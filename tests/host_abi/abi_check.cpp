@@ -218,9 +218,9 @@ int main() {
          RGLRU_ERR_INVALID_ARGUMENT);
   // checkpoint and backward
   rglru_delta_shape_t b1 = dshape(2, 100, 1, 2, 128, 64, 1, 0);
-  EXPECT(rglru_delta_ckpt_elems(&b1, 0) == (size_t)2 * 7 * 2 * 128 * 64);
+  EXPECT(rglru_delta_ckpt_elems(&b1, 0) == (size_t)2 * 13 * 2 * 128 * 64);  // ceil(100 / 8) slots a row
   rglru_delta_shape_t b2 = dshape(1, 100, 1, 2, 128, 64, 1, 0);
-  EXPECT(rglru_delta_ckpt_elems(&b2, 3) == (size_t)(7 + 3) * 2 * 128 * 64);
+  EXPECT(rglru_delta_ckpt_elems(&b2, 3) == (size_t)(13 + 3) * 2 * 128 * 64);
   EXPECT(rglru_delta_ckpt_elems(&b1, 3) == 0);   // packed sequences need B = 1
   const size_t bws = rglru_delta_bwd_workspace_bytes(&b1, 0);
   EXPECT(bws > 0 && bws % 256 == 0);
